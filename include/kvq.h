@@ -1,0 +1,201 @@
+/*
+ * kvq.h — C ABI of libkvq: low-bit KV-cache quantization with RoPE-aware
+ * per-block bit allocation, and decode attention that reads the packed cache,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Sources.  The method is that of "RoPE-Aware Bit Allocation for KV-Cache
+ * Quantization" (Liang, Zhang, Jia; arXiv 2606.24033), abstract: a key's
+ * contribution to a future logit decomposes over two-dimensional RoPE
+ * frequency blocks; for each layer and KV head a label-free energy score is
+ * computed per block and integer bit widths are allocated greedily by marginal
+ * gain under a bits-per-dimension budget (KxVy); the quantizer is built on
+ * TQ-MSE; decode runs over a packed cache.  The comparison codec is NQKV's
+ * per-block Gaussian-quantile quantizer ("NQKV: A KV Cache Quantization Scheme
+ * Based on Normal Distribution Characteristics", Pith review: "What carries
+ * the argument", referee major comment 1; block size 256 from "Assumptions &
+ * free parameters"), with append-only encoding ("Assumptions", third item).
+ *
+ * Conventions shared by every call.
+ *  - head_dim is 128; each KV head has 64 RoPE blocks.
+ *  - Tensor arguments are device pointers owned by the caller, C-contiguous,
+ *    on the device that was current when the cache was created.  The library
+ *    never keeps them after the call returns (work already enqueued on
+ *    `stream` may still read them until it completes).
+ *  - The cache owns all of its own device memory; kvq_cache_destroy frees it.
+ *  - Calls validate their arguments synchronously on the host and return a
+ *    status without enqueuing anything when validation fails; a failed call
+ *    leaves the cache unchanged.  Valid calls enqueue kernels on `stream` and
+ *    return without waiting (except the calls documented as synchronizing).
+ *  - KVQ_EHIP reports a HIP runtime error seen at launch; a device-side fault
+ *    surfaces at the caller's next synchronization.
+ *  - A cache must not be mutated from two host threads at once.
+ *  - Every sequence of the batch has the same length; kvq_quantize_append
+ *    advances the length of one layer.
+ *  - The library never applies RoPE: keys and queries arrive rotated.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct kvq_cache kvq_cache;
+typedef void* kvq_stream; /* a hipStream_t; NULL is the default stream */
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_EINVAL = 1,    /* bad argument: null pointer, out-of-range layer/size/budget, bad config */
+  KVQ_ENOMEM = 2,    /* device or host allocation failed */
+  KVQ_ECAPACITY = 3, /* an append would exceed max_tokens */
+  KVQ_ESTATE = 4,    /* call out of order: append before alloc, re-alloc after append,
+                        decode of an empty layer */
+  KVQ_EHIP = 5       /* HIP runtime error (kvq_last_error() has the text) */
+} kvq_status;
+
+typedef enum { KVQ_F16 = 0, KVQ_F32 = 1 } kvq_dtype;
+
+typedef enum {
+  KVQ_CODEC_BGTQ = 0,       /* Block-GTQ: per-block widths from kvq_alloc_bits, per-block gains */
+  KVQ_CODEC_UNIFORM = 1,    /* uniform TQ-MSE-style baseline: every block k_bits, no gains */
+  KVQ_CODEC_NF16_B256 = 2   /* NQKV-style: 4-bit 16-level Gaussian quantiles, absmax scale per
+                               256 consecutive values of a token's [n_kv_heads*128] vector */
+} kvq_codec;
+
+typedef enum {
+  KVQ_ROPE_HALF = 0,        /* block j pairs dims (j, j+64) */
+  KVQ_ROPE_INTERLEAVED = 1  /* block j pairs dims (2j, 2j+1) */
+} kvq_pairing;
+
+typedef struct {
+  int32_t n_layers;    /* >= 1 */
+  int32_t n_kv_heads;  /* >= 1 */
+  int32_t n_q_heads;   /* multiple of n_kv_heads; group size n_q/n_kv in {1, 2, 4, 8} */
+  int32_t head_dim;    /* must be 128 */
+  int32_t batch;       /* sequences, >= 1 */
+  int64_t max_tokens;  /* capacity per sequence and layer, >= 1 */
+  int32_t k_bits;      /* K budget in bits per dim, in [max(1,b_min), b_max] */
+  int32_t v_bits;      /* V width in bits per dim, in [1, 8] */
+  int32_t b_min;       /* smallest per-block K width, >= 0 (default 0) */
+  int32_t b_max;       /* largest per-block K width, <= 8 (default 8) */
+  int32_t codec;       /* kvq_codec; NF16_B256 needs k_bits = v_bits = 4 and
+                          n_kv_heads*128 divisible by 256 */
+  int32_t pairing;     /* kvq_pairing */
+} kvq_config;
+
+/* Layout facts of one layer's packed storage, for parity dumps (see kvq_read_cache). */
+typedef struct {
+  int64_t capacity;        /* token capacity per sequence (max_tokens rounded up to 128) */
+  int64_t len;             /* tokens appended so far */
+  int32_t k_row_words;     /* 32-bit words per K row = 4*k_bits */
+  int32_t v_dim_words;     /* 32-bit words per dim per 128-token V tile = 4*v_bits */
+  int64_t k_codes_bytes;   /* bytes of one layer's K rows:   [batch][n_kv][capacity][k_row_words] */
+  int64_t v_codes_bytes;   /* bytes of one layer's V tiles:  [batch][n_kv][capacity/128][128][v_dim_words] */
+  int64_t k_scales_bytes;  /* fp16 K scales: BGTQ/UNIFORM [batch][n_kv][capacity];
+                              NF16 [batch][capacity][n_kv*128/256] */
+  int64_t v_scales_bytes;  /* fp16 V scales, same shapes as K scales */
+  int32_t plan_ready;      /* 1 once kvq_alloc_bits has run for this layer */
+} kvq_layer_info;
+
+typedef enum {
+  KVQ_PART_K_CODES = 0,
+  KVQ_PART_V_CODES = 1,
+  KVQ_PART_K_SCALES = 2,
+  KVQ_PART_V_SCALES = 3
+} kvq_part;
+
+/* Create a cache for cfg and allocate its full capacity on the current device.
+   Validates cfg before touching the GPU (KVQ_EINVAL).  *out is set only on KVQ_OK. */
+kvq_status kvq_cache_create(const kvq_config* cfg, kvq_cache** out);
+
+/* Free everything the cache owns; NULL is ignored.  Synchronizes the device. */
+void kvq_cache_destroy(kvq_cache* cache);
+
+/* Per-(layer, KV head) bit allocation (Block-GTQ; RoPE-aware bit allocation
+   page, abstract: each RoPE block gets an energy score computed from keys
+   alone, then integer widths are handed out one step at a time to the block
+   whose marginal gain is largest).
+   keys:   [n_tok][n_kv_heads][128] post-RoPE calibration keys (dtype), n_tok >= 1.
+           May be NULL for the UNIFORM and NF16 codecs, whose plans are fixed.
+   block_weight: NULL, or a device fp64 array [n_kv_heads][64] of per-block
+           weights multiplying the energy score before the greedy.
+   Computes m_j = sum over tokens of the block's squared norm / (2 n_tok) in fp64
+   (terms summed in token order inside 256-token chunks, then chunk totals in
+   order), widths b_j in [b_min, b_max] with sum_j 2 b_j = 128 k_bits by
+   repeatedly raising the block with the largest s_j * delta(b_j) (ties to the
+   smallest j), and per-block gains sqrt(m_j / mean m).  Writes the layer's plan.
+   Errors: KVQ_EINVAL (null cache/keys, bad layer, n_tok < 1, bad dtype),
+           KVQ_ESTATE (the layer already holds appended tokens). */
+kvq_status kvq_alloc_bits(kvq_cache* cache, int32_t layer, const void* keys, int32_t dtype,
+                          int64_t n_tok, const double* block_weight, kvq_stream stream);
+
+/* Copy one layer's plan to host memory.  Synchronizes the device.
+   bits:  host int8 [n_kv_heads][64] per-block widths (required).
+   gains: host fp32 [n_kv_heads][64] per-block gains g_j (nullable).
+   Errors: KVQ_EINVAL, KVQ_ESTATE (no plan yet), KVQ_EHIP. */
+kvq_status kvq_get_plan(const kvq_cache* cache, int32_t layer, int8_t* bits, float* gains);
+
+/* Quantize and append n_new tokens to every sequence of one layer
+   (per-token scale, codebook lookup and bit-packing; append-only).
+   k, v:  [batch][n_new][n_kv_heads][128] post-RoPE keys and values (dtype).
+   n_new = 0 is a no-op.  Row quantizer, in IEEE fp32/fp64 with no fused ops:
+   y = x * ig_j; s = fp16(fp32(sqrt(sum y^2 / 128))); u = y * fp32(1/s);
+   code = number of codebook boundaries below u.  NF16: s = fp16(absmax) per
+   256 values, u = x * fp32(1/s).
+   Errors: KVQ_EINVAL, KVQ_ESTATE (no plan for the layer), KVQ_ECAPACITY. */
+kvq_status kvq_quantize_append(kvq_cache* cache, int32_t layer, const void* k, const void* v,
+                               int32_t dtype, int64_t n_new, kvq_stream stream);
+
+/* Grouped-query decode attention of one query per sequence against the packed
+   cache of one layer: logits sigma * <q_h, x_hat^K> over every appended token,
+   softmax, weighted sum of x_hat^V; KV head of query head h is h / group.
+   q:     [batch][n_q_heads][128] (dtype).
+   softmax_scale: sigma; <= 0 selects 1/sqrt(128).
+   out:   [batch][n_q_heads][128] fp32 device buffer.
+   The context is split into chunks processed in parallel, each producing a
+   partial (max, sum, weighted sum) that a second pass combines in fixed order.
+   Errors: KVQ_EINVAL, KVQ_ESTATE (layer empty or without plan). */
+kvq_status kvq_decode_attn(kvq_cache* cache, int32_t layer, const void* q, int32_t dtype,
+                           float softmax_scale, float* out, kvq_stream stream);
+
+/* As kvq_decode_attn with an explicit number of context splits per (sequence,
+   KV head); n_splits <= 0 lets the library choose.  The result does not depend
+   on n_splits beyond fp32 rounding. */
+kvq_status kvq_decode_attn_splits(kvq_cache* cache, int32_t layer, const void* q, int32_t dtype,
+                                  float softmax_scale, float* out, int32_t n_splits,
+                                  kvq_stream stream);
+
+/* Tokens appended so far to `layer` (host bookkeeping; does not synchronize). */
+kvq_status kvq_seq_len(const kvq_cache* cache, int32_t layer, int64_t* len);
+
+/* Layout facts of one layer (host bookkeeping; does not synchronize). */
+kvq_status kvq_layer_info_get(const kvq_cache* cache, int32_t layer, kvq_layer_info* info);
+
+/* Copy nbytes of one layer's packed storage, starting at byte `offset` of the
+   part, to host memory dst.  Synchronizes the device.  Used by parity tests.
+   Errors: KVQ_EINVAL (bad part, range outside the part), KVQ_EHIP. */
+kvq_status kvq_read_cache(const kvq_cache* cache, int32_t layer, int32_t part, int64_t offset,
+                          int64_t nbytes, void* dst);
+
+/* Host copies of the library's own constant tables (no GPU needed).
+   kvq_codebook: bits in [1, 8]; centroids: 2^bits fp16 bit patterns;
+                 boundaries: 2^bits - 1 fp32 values (either pointer nullable).
+   kvq_delta:    8 fp32 greedy gains delta(b) = c(b) - c(b+1), b = 0..7.
+   kvq_nf16_codebook: 16 fp16 levels and 15 fp32 boundaries. */
+kvq_status kvq_codebook(int32_t bits, uint16_t* centroids, float* boundaries);
+kvq_status kvq_delta(float* delta);
+kvq_status kvq_nf16_codebook(uint16_t* levels, float* boundaries);
+
+/* Human-readable name of a status; never NULL. */
+const char* kvq_status_str(kvq_status status);
+
+/* Text of the last HIP error recorded by this thread ("" if none); never NULL. */
+const char* kvq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,10 +1,10 @@
 """RoPE-block energy score, per-block gains and greedy bit allocation (oracle).
 
-Source: "RoPE-Aware Bit Allocation for KV-Cache Quantization", abstract.  Under
-RoPE a key's contribution to a future logit is a position-dependent sum over
-two-dimensional frequency blocks; for each layer and KV head a label-free
-energy score is computed per RoPE block and integer bit widths are allocated
-greedily by marginal gain, high-energy blocks receiving more bits.
+Source: "RoPE-Aware Bit Allocation for KV-Cache Quantization", abstract.  With
+RoPE, the logit a cached key will contribute splits into one term per 2-D
+frequency block, each depending on the relative position; the method scores
+every block of every (layer, KV head) by its energy, without labels, and hands
+out integer widths greedily by marginal gain, so energetic blocks get more bits.
 
 Readings (the pages give no formulas):
   * score: m_j = sum_t (k_{t,p0(j)}^2 + k_{t,p1(j)}^2) / (2T) over the keys the

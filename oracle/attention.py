@@ -1,8 +1,8 @@
 """Dequantization and fp64 GQA decode attention (oracle; test infrastructure only).
 
 Decode attention over the packed cache (RoPE-Aware Bit Allocation for
-KV-Cache Quantization, abstract: the packed-cache serving path attends over
-the packed K3V3 cache at 128K context).  Readings:
+KV-Cache Quantization, abstract: its serving path decodes directly from a
+packed K3V3 cache at 128K context).  Readings:
 
   * the dequantized cache: K x_hat = s16 * g_{j(i)} * CB_{b_i}[code] (0 when
     b_i = 0); V x_hat = s16 * CB_{B_V}[code]; the 256-value absmax codec
@@ -12,9 +12,9 @@ the packed K3V3 cache at 128K context).  Readings:
     unless given, kv(h) = floor(h / G) (contiguous grouped-query mapping);
   * p = softmax over the cached tokens (max subtracted), o_h = sum_t p_t x_hat^V_t.
 
-RoPE block identity.  A key's contribution to a future logit decomposes into
-a position-dependent sum over two-dimensional frequency blocks (same abstract):
-with q = R(m) q0 and k = R(n) k0,  q . k = sum_j q0_j^T R((n - m) w_j) k0_j.
+RoPE block identity (same abstract: the logit splits into per-block terms
+that depend on the relative position): with q = R(m) q0 and k = R(n) k0,
+q . k = sum_j q0_j^T R((n - m) w_j) k0_j.
 """
 from __future__ import annotations
 

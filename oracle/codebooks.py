@@ -1,21 +1,22 @@
 """Scalar codebooks of the quantizers (oracle; test infrastructure only).
 
-TQ-MSE-style codebook (reading).  The method is "built on TurboQuant-MSE
-(TQ-MSE)" (RoPE-Aware Bit Allocation for KV-Cache Quantization, abstract), but
-the pages print no codebook.  The reading taken here is the MSE-optimal
+TQ-MSE-style codebook (reading).  The method's quantizer derives from
+TurboQuant-MSE (RoPE-Aware Bit Allocation for KV-Cache Quantization,
+abstract), but the pages print no codebook.  The reading taken here is the MSE-optimal
 (Lloyd-Max) 2^b-level scalar quantizer for a standard normal, with no random
 rotation; its centroids are rounded once to fp16 (round-to-nearest-even) and
 those fp16 values *are* the codebook.  Decision boundaries are the fp32
 rounding of the exact midpoint of neighbouring fp16 centroids.
 
-Greedy gains (reading).  The allocator moves bits "by marginal gain"; the gain
+Greedy gains (reading).  The allocator raises widths by marginal gain; the gain
 of raising a block from b to b+1 bits is taken as delta(b) = c(b) - c(b+1)
 rounded once to fp32, where c(b) is the exact N(0,1) mean squared error of the
 b-bit codebook above (c(0) = 1: a zero-width block reconstructs 0).
 
-16-level Gaussian-quantile codebook (reading).  The NQKV review describes "a
-fixed set of 16 quantiles of the standard normal" applied after absmax
-scaling ("What carries the argument"; referee major comment 1).  The level
+16-level Gaussian-quantile codebook (reading).  The NQKV review describes a
+fixed codebook of sixteen standard-normal quantiles, applied after each block
+is divided by its absolute maximum ("What carries the argument"; referee major
+comment 1).  The level
 values are not printed; the reading is the equal-mass bin midpoints
 Phi^-1((k + 1/2)/16), divided by Phi^-1(31/32) so the end levels are +-1,
 rounded to fp16, with fp32 midpoint boundaries.

@@ -1,9 +1,9 @@
 """Packed-cache bit layout (oracle; test infrastructure only).
 
-The pages state that the cache is packed (RoPE-Aware Bit Allocation for
-KV-Cache Quantization, abstract: "packed-cache serving path") and that the
-NQKV cache stores codebook indices plus block scales (Pith review, "What
-carries the argument"), but give no layout.  The layout used here:
+The pages state that the cache is stored packed (RoPE-Aware Bit Allocation
+for KV-Cache Quantization, abstract) and that the NQKV cache keeps codebook
+indices plus block scales (Pith review, "What carries the argument"), but give
+no layout.  The layout used here:
 
 K rows.  One row per (sequence, KV head, token): the stored fields in plan
 order (allocation.field_order), each field's code written least-significant
@@ -65,20 +65,18 @@ def pack_v_tiles(codes: np.ndarray, bits: int) -> np.ndarray:
     nt = (T + V_TILE - 1) // V_TILE
     padded = np.zeros((nt * V_TILE, d), dtype=np.uint8)
     padded[:T] = codes
-    out = np.zeros((nt, d, 4 * bits), dtype=np.uint32)
-    for t in range(nt):
-        blk = padded[t * V_TILE:(t + 1) * V_TILE].T            # [d, 128] dim-major
-        w = np.zeros((d, 4 * bits), dtype=np.uint32)
-        for tau in range(V_TILE):
-            _put(w, tau * bits, bits, blk[:, tau])
-        out[t] = w
-    return out
+    # [tile, dim, token-in-tile]: each (tile, dim) row is one dim's 128-token stream
+    streams = padded.reshape(nt, V_TILE, d).transpose(0, 2, 1).reshape(nt * d, V_TILE)
+    w = np.zeros((nt * d, 4 * bits), dtype=np.uint32)
+    for tau in range(V_TILE):
+        _put(w, tau * bits, bits, streams[:, tau])
+    return w.reshape(nt, d, 4 * bits)
 
 
 def unpack_v_tiles(words: np.ndarray, bits: int, T: int) -> np.ndarray:
-    nt, d, _ = words.shape
-    codes = np.zeros((nt * V_TILE, d), dtype=np.uint8)
-    for t in range(nt):
-        for tau in range(V_TILE):
-            codes[t * V_TILE + tau] = _get(words[t], tau * bits, bits)
-    return codes[:T]
+    nt, d, nw = words.shape
+    flat = words.reshape(nt * d, nw)
+    streams = np.zeros((nt * d, V_TILE), dtype=np.uint8)
+    for tau in range(V_TILE):
+        streams[:, tau] = _get(flat, tau * bits, bits)
+    return streams.reshape(nt, d, V_TILE).transpose(0, 2, 1).reshape(nt * V_TILE, d)[:T]

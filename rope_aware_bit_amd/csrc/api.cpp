@@ -1,0 +1,320 @@
+// Host side of the libkvq C ABI: validation, cache memory, bookkeeping, launches.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "kvq_internal.h"
+
+using kvq::kBlocks;
+using kvq::kHeadDim;
+using kvq::kMaxBits;
+using kvq::kVTile;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kvq_status hip_fail(hipError_t e, const char* what) {
+  g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+  return KVQ_EHIP;
+}
+
+bool config_valid(const kvq_config* c) {
+  if (!c) return false;
+  if (c->n_layers < 1 || c->n_kv_heads < 1 || c->n_q_heads < 1 || c->batch < 1) return false;
+  if (c->head_dim != kHeadDim) return false;
+  if (c->max_tokens < 1 || c->max_tokens > (int64_t(1) << 40)) return false;
+  if (c->n_q_heads % c->n_kv_heads != 0) return false;
+  const int G = c->n_q_heads / c->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return false;
+  if (c->codec < KVQ_CODEC_BGTQ || c->codec > KVQ_CODEC_NF16_B256) return false;
+  if (c->pairing != KVQ_ROPE_HALF && c->pairing != KVQ_ROPE_INTERLEAVED) return false;
+  if (c->v_bits < 1 || c->v_bits > kMaxBits) return false;
+  if (c->b_min < 0 || c->b_max > kMaxBits || c->b_min > c->b_max) return false;
+  if (c->k_bits < 1 || c->k_bits < c->b_min || c->k_bits > c->b_max) return false;
+  if (c->codec == KVQ_CODEC_NF16_B256) {
+    if (c->k_bits != 4 || c->v_bits != 4) return false;
+    if ((c->n_kv_heads * kHeadDim) % kvq::kNfBlock != 0) return false;
+  }
+  return true;
+}
+
+bool layer_ok(const kvq_cache* c, int32_t layer) {
+  return c && layer >= 0 && layer < c->cfg.n_layers;
+}
+
+void free_device(kvq_cache* c) {
+  void* ptrs[] = {c->k_codes, c->v_codes, c->k_scales, c->v_scales, c->plans,
+                  c->tables,  c->part_o,  c->part_ml,  c->energy_scratch};
+  for (void* p : ptrs)
+    if (p) (void)hipFree(p);
+}
+
+kvq_status dev_alloc(void** p, size_t bytes, const char* what) {
+  hipError_t e = hipMalloc(p, bytes);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    g_last_error = std::string("hipMalloc ") + what + ": " + hipGetErrorString(e);
+    *p = nullptr;
+    return e == hipErrorOutOfMemory ? KVQ_ENOMEM : KVQ_EHIP;
+  }
+  return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvq_status_str(kvq_status s) {
+  switch (s) {
+    case KVQ_OK: return "KVQ_OK";
+    case KVQ_EINVAL: return "KVQ_EINVAL";
+    case KVQ_ENOMEM: return "KVQ_ENOMEM";
+    case KVQ_ECAPACITY: return "KVQ_ECAPACITY";
+    case KVQ_ESTATE: return "KVQ_ESTATE";
+    case KVQ_EHIP: return "KVQ_EHIP";
+  }
+  return "KVQ_UNKNOWN";
+}
+
+const char* kvq_last_error(void) { return g_last_error.c_str(); }
+
+kvq_status kvq_codebook(int32_t bits, uint16_t* centroids, float* boundaries) {
+  if (bits < 1 || bits > kMaxBits) return KVQ_EINVAL;
+  kvq::Tables t;
+  kvq::build_tables(&t);
+  const int L = 1 << bits;
+  if (centroids) std::memcpy(centroids, t.cb[bits], sizeof(uint16_t) * L);
+  if (boundaries) std::memcpy(boundaries, t.bd[bits], sizeof(float) * (L - 1));
+  return KVQ_OK;
+}
+
+kvq_status kvq_delta(float* delta) {
+  if (!delta) return KVQ_EINVAL;
+  kvq::Tables t;
+  kvq::build_tables(&t);
+  std::memcpy(delta, t.delta, sizeof(t.delta));
+  return KVQ_OK;
+}
+
+kvq_status kvq_nf16_codebook(uint16_t* levels, float* boundaries) {
+  kvq::Tables t;
+  kvq::build_tables(&t);
+  if (levels) std::memcpy(levels, t.nf_cb, sizeof(t.nf_cb));
+  if (boundaries) std::memcpy(boundaries, t.nf_bd, sizeof(float) * 15);
+  return KVQ_OK;
+}
+
+kvq_status kvq_cache_create(const kvq_config* cfg, kvq_cache** out) {
+  if (!out || !config_valid(cfg)) return KVQ_EINVAL;
+  kvq_cache* c = new (std::nothrow) kvq_cache();
+  if (!c) return KVQ_ENOMEM;
+  std::memset(static_cast<void*>(c), 0, sizeof(kvq_cache));
+  c->cfg = *cfg;
+  c->group = cfg->n_q_heads / cfg->n_kv_heads;
+  c->cap = (cfg->max_tokens + kVTile - 1) / kVTile * kVTile;
+  const bool nf = cfg->codec == KVQ_CODEC_NF16_B256;
+  c->k_words = 4 * (nf ? 4 : cfg->k_bits);
+  c->v_words = 4 * (nf ? 4 : cfg->v_bits);
+  c->n_nf_blocks = cfg->n_kv_heads * kHeadDim / kvq::kNfBlock;
+  c->len = static_cast<int64_t*>(std::calloc(cfg->n_layers, sizeof(int64_t)));
+  c->plan_ready = static_cast<uint8_t*>(std::calloc(cfg->n_layers, 1));
+  if (!c->len || !c->plan_ready) {
+    std::free(c->len);
+    std::free(c->plan_ready);
+    delete c;
+    return KVQ_ENOMEM;
+  }
+  kvq::build_tables(&c->host_tables);
+
+  const int64_t B = cfg->batch, H = cfg->n_kv_heads, L = cfg->n_layers, cap = c->cap;
+  c->k_codes_layer = B * H * cap * c->k_words * 4;
+  c->v_codes_layer = B * H * cap * c->v_words * 4;  // (cap/128) tiles * 128 dims * v_words words
+  c->k_scales_layer = nf ? B * cap * c->n_nf_blocks * 2 : B * H * cap * 2;
+  c->v_scales_layer = c->k_scales_layer;
+  // split partials: at most 1024 splits per (sequence, head), at most 256 MiB of partials
+  int64_t per_split = B * H * c->group * (kHeadDim + 2) * 4;
+  int64_t ms = (int64_t(256) << 20) / per_split;
+  if (ms > 1024) ms = 1024;
+  if (ms < 1) ms = 1;
+  c->max_splits = static_cast<int>(ms);
+
+  hipError_t e = hipGetDevice(&c->device);
+  kvq_status st = e == hipSuccess ? KVQ_OK : hip_fail(e, "hipGetDevice");
+  if (st == KVQ_OK) st = dev_alloc(reinterpret_cast<void**>(&c->k_codes), c->k_codes_layer * L, "K codes");
+  if (st == KVQ_OK) st = dev_alloc(reinterpret_cast<void**>(&c->v_codes), c->v_codes_layer * L, "V codes");
+  if (st == KVQ_OK) st = dev_alloc(reinterpret_cast<void**>(&c->k_scales), c->k_scales_layer * L, "K scales");
+  if (st == KVQ_OK) st = dev_alloc(reinterpret_cast<void**>(&c->v_scales), c->v_scales_layer * L, "V scales");
+  if (st == KVQ_OK) st = dev_alloc(reinterpret_cast<void**>(&c->plans), sizeof(kvq::Plan) * L * H, "plans");
+  if (st == KVQ_OK) st = dev_alloc(reinterpret_cast<void**>(&c->tables), sizeof(kvq::Tables), "tables");
+  if (st == KVQ_OK)
+    st = dev_alloc(reinterpret_cast<void**>(&c->part_o), per_split / (kHeadDim + 2) * kHeadDim * ms, "partials");
+  if (st == KVQ_OK)
+    st = dev_alloc(reinterpret_cast<void**>(&c->part_ml), per_split / (kHeadDim + 2) * 2 * ms, "partials");
+  if (st == KVQ_OK) {
+    const hipError_t es[] = {
+        hipMemset(c->k_codes, 0, c->k_codes_layer * L),
+        hipMemset(c->v_codes, 0, c->v_codes_layer * L),
+        hipMemset(c->k_scales, 0, c->k_scales_layer * L),
+        hipMemset(c->v_scales, 0, c->v_scales_layer * L),
+        hipMemset(c->plans, 0, sizeof(kvq::Plan) * L * H),
+        hipMemcpy(c->tables, &c->host_tables, sizeof(kvq::Tables), hipMemcpyHostToDevice),
+        hipDeviceSynchronize()};
+    for (hipError_t x : es)
+      if (x != hipSuccess && st == KVQ_OK) st = hip_fail(x, "cache init");
+  }
+  if (st != KVQ_OK) {
+    free_device(c);
+    std::free(c->len);
+    std::free(c->plan_ready);
+    delete c;
+    return st;
+  }
+  *out = c;
+  return KVQ_OK;
+}
+
+void kvq_cache_destroy(kvq_cache* c) {
+  if (!c) return;
+  (void)hipDeviceSynchronize();
+  free_device(c);
+  std::free(c->len);
+  std::free(c->plan_ready);
+  delete c;
+}
+
+kvq_status kvq_alloc_bits(kvq_cache* c, int32_t layer, const void* keys, int32_t dtype,
+                          int64_t n_tok, const double* block_weight, kvq_stream stream) {
+  if (!layer_ok(c, layer)) return KVQ_EINVAL;
+  if (dtype != KVQ_F16 && dtype != KVQ_F32) return KVQ_EINVAL;
+  const bool bgtq = c->cfg.codec == KVQ_CODEC_BGTQ;
+  if (bgtq && (!keys || n_tok < 1)) return KVQ_EINVAL;
+  if (bgtq && n_tok > (int64_t(1) << 31)) return KVQ_EINVAL;
+  if (c->len[layer] > 0) return KVQ_ESTATE;
+  if (bgtq) {
+    const int64_t n_chunks = (n_tok + kvq::kEnergyChunk - 1) / kvq::kEnergyChunk;
+    if (n_chunks > c->energy_scratch_chunks) {
+      // the scratch grows to the largest calibration seen; earlier work on any stream may
+      // still read the old buffer, so wait for the device before freeing it
+      if (c->energy_scratch) {
+        hipError_t e = hipDeviceSynchronize();
+        if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+        (void)hipFree(c->energy_scratch);
+        c->energy_scratch = nullptr;
+        c->energy_scratch_chunks = 0;
+      }
+      kvq_status st = dev_alloc(reinterpret_cast<void**>(&c->energy_scratch),
+                                sizeof(double) * n_chunks * c->cfg.n_kv_heads * kBlocks, "energy scratch");
+      if (st != KVQ_OK) return st;
+      c->energy_scratch_chunks = n_chunks;
+    }
+  }
+  hipError_t e = kvq::launch_alloc(c, layer, keys, dtype, bgtq ? n_tok : 0, block_weight,
+                                   static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "alloc launch");
+  c->plan_ready[layer] = 1;
+  return KVQ_OK;
+}
+
+kvq_status kvq_get_plan(const kvq_cache* c, int32_t layer, int8_t* bits, float* gains) {
+  if (!layer_ok(c, layer) || !bits) return KVQ_EINVAL;
+  if (!c->plan_ready[layer]) return KVQ_ESTATE;
+  const int H = c->cfg.n_kv_heads;
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+  for (int h = 0; h < H; ++h) {
+    kvq::Plan p;
+    e = hipMemcpy(&p, c->plans + static_cast<int64_t>(layer) * H + h, sizeof(p), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "plan copy");
+    std::memcpy(bits + h * kBlocks, p.bwidth, kBlocks);
+    if (gains) {
+      for (int j = 0; j < kBlocks; ++j) {
+        const int d0 = c->cfg.pairing == KVQ_ROPE_HALF ? j : 2 * j;
+        gains[h * kBlocks + j] = p.g[d0];
+      }
+    }
+  }
+  return KVQ_OK;
+}
+
+kvq_status kvq_quantize_append(kvq_cache* c, int32_t layer, const void* k, const void* v,
+                               int32_t dtype, int64_t n_new, kvq_stream stream) {
+  if (!layer_ok(c, layer)) return KVQ_EINVAL;
+  if (dtype != KVQ_F16 && dtype != KVQ_F32) return KVQ_EINVAL;
+  if (n_new < 0) return KVQ_EINVAL;
+  if (n_new == 0) return KVQ_OK;
+  if (!k || !v) return KVQ_EINVAL;
+  if (!c->plan_ready[layer]) return KVQ_ESTATE;
+  if (c->len[layer] + n_new > c->cfg.max_tokens) return KVQ_ECAPACITY;
+  hipError_t e = kvq::launch_quantize(c, layer, k, v, dtype, n_new, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "quantize launch");
+  c->len[layer] += n_new;
+  return KVQ_OK;
+}
+
+kvq_status kvq_decode_attn_splits(kvq_cache* c, int32_t layer, const void* q, int32_t dtype,
+                                  float softmax_scale, float* out, int32_t n_splits,
+                                  kvq_stream stream) {
+  if (!layer_ok(c, layer) || !q || !out) return KVQ_EINVAL;
+  if (dtype != KVQ_F16 && dtype != KVQ_F32) return KVQ_EINVAL;
+  if (!(softmax_scale == softmax_scale)) return KVQ_EINVAL;  // NaN
+  if (!c->plan_ready[layer] || c->len[layer] == 0) return KVQ_ESTATE;
+  int S = n_splits > 0 ? n_splits : kvq::auto_splits(c, c->len[layer]);
+  if (S > c->max_splits) return KVQ_EINVAL;
+  hipError_t e = kvq::launch_decode(c, layer, q, dtype, softmax_scale, out, S,
+                                    static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return KVQ_OK;
+}
+
+kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, const void* q, int32_t dtype,
+                           float softmax_scale, float* out, kvq_stream stream) {
+  return kvq_decode_attn_splits(c, layer, q, dtype, softmax_scale, out, 0, stream);
+}
+
+kvq_status kvq_seq_len(const kvq_cache* c, int32_t layer, int64_t* len) {
+  if (!layer_ok(c, layer) || !len) return KVQ_EINVAL;
+  *len = c->len[layer];
+  return KVQ_OK;
+}
+
+kvq_status kvq_layer_info_get(const kvq_cache* c, int32_t layer, kvq_layer_info* info) {
+  if (!layer_ok(c, layer) || !info) return KVQ_EINVAL;
+  info->capacity = c->cap;
+  info->len = c->len[layer];
+  info->k_row_words = c->k_words;
+  info->v_dim_words = c->v_words;
+  info->k_codes_bytes = c->k_codes_layer;
+  info->v_codes_bytes = c->v_codes_layer;
+  info->k_scales_bytes = c->k_scales_layer;
+  info->v_scales_bytes = c->v_scales_layer;
+  info->plan_ready = c->plan_ready[layer];
+  return KVQ_OK;
+}
+
+kvq_status kvq_read_cache(const kvq_cache* c, int32_t layer, int32_t part, int64_t offset,
+                          int64_t nbytes, void* dst) {
+  if (!layer_ok(c, layer) || !dst || offset < 0 || nbytes < 0) return KVQ_EINVAL;
+  const char* base = nullptr;
+  int64_t size = 0;
+  kvq_cache* m = const_cast<kvq_cache*>(c);
+  switch (part) {
+    case KVQ_PART_K_CODES: base = reinterpret_cast<const char*>(kvq::layer_k_codes(m, layer)); size = c->k_codes_layer; break;
+    case KVQ_PART_V_CODES: base = reinterpret_cast<const char*>(kvq::layer_v_codes(m, layer)); size = c->v_codes_layer; break;
+    case KVQ_PART_K_SCALES: base = reinterpret_cast<const char*>(kvq::layer_k_scales(m, layer)); size = c->k_scales_layer; break;
+    case KVQ_PART_V_SCALES: base = reinterpret_cast<const char*>(kvq::layer_v_scales(m, layer)); size = c->v_scales_layer; break;
+    default: return KVQ_EINVAL;
+  }
+  if (offset + nbytes > size) return KVQ_EINVAL;
+  if (nbytes == 0) return KVQ_OK;
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(dst, base + offset, nbytes, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "read cache");
+  return KVQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,99 @@
+// Internal definitions shared by the libkvq host code and its gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kvq.h"
+
+namespace kvq {
+
+constexpr int kHeadDim = 128;
+constexpr int kBlocks = 64;          // 2-D RoPE blocks per head
+constexpr int kMaxBits = 8;
+constexpr int kVTile = 128;          // tokens per dim-major V tile
+constexpr int kEnergyChunk = 256;    // tokens per sequential energy partial sum
+constexpr int kMaxGroup = 8;         // query heads per KV head supported
+constexpr int kNfBlock = 256;        // values per absmax block of the NF16 codec
+
+// Constant tables, built on the host at cache creation and copied to the device.
+struct Tables {
+  uint16_t cb[kMaxBits + 1][256];    // fp16 bit patterns of CB_b[k], b = 1..8 (row 0 unused)
+  float bd[kMaxBits + 1][256];       // fp32 boundaries beta_b[k], k < 2^b - 1; +inf padding
+  float delta[kMaxBits];             // greedy gain delta(b) = c(b) - c(b+1), fp32
+  uint16_t nf_cb[16];                // fp16 levels of the 16-level Gaussian-quantile codebook
+  float nf_bd[16];                   // 15 boundaries; [15] = +inf
+};
+
+// Per-(layer, KV head) plan written by the allocation kernel.
+struct alignas(16) Plan {
+  float g[kHeadDim];                 // per-dim gain (its block's g_j)
+  float ig[kHeadDim];                // per-dim inverse gain
+  uint16_t foff[kHeadDim];           // bit offset of field f within the K row
+  uint8_t fdim[kHeadDim];            // dim of field f, plan order
+  uint8_t fwidth[kHeadDim];          // width of field f
+  uint8_t dwidth[kHeadDim];          // width of dim i
+  int8_t bwidth[kBlocks];            // width of block j
+  int32_t n_fields;                  // stored fields (2 x blocks with width > 0)
+  int32_t pad[3];
+};
+
+// Host-side tables builder (independent implementation of the codebook definitions).
+void build_tables(Tables* t);
+
+}  // namespace kvq
+
+struct kvq_cache {
+  kvq_config cfg;
+  int device;
+  int64_t cap;                 // token capacity per sequence, multiple of kVTile
+  int group;                   // n_q / n_kv
+  int k_words;                 // 32-bit words per K row
+  int v_words;                 // 32-bit words per dim per V tile
+  int n_nf_blocks;             // NF16 scale blocks per token (n_kv*128/256)
+  int64_t* len;                // per layer
+  uint8_t* plan_ready;         // per layer
+  // device memory
+  uint32_t* k_codes;           // [L][B][H][cap][k_words]
+  uint32_t* v_codes;           // [L][B][H][cap/128][128][v_words]
+  uint16_t* k_scales;          // BGTQ/UNI [L][B][H][cap]; NF16 [L][B][cap][nnf]
+  uint16_t* v_scales;
+  kvq::Plan* plans;            // [L][H]
+  kvq::Tables* tables;         // device copy
+  kvq::Tables host_tables;
+  float* part_o;               // split partials [B][H][max_splits][G][128]
+  float* part_ml;              // [B][H][max_splits][G][2]
+  int max_splits;
+  double* energy_scratch;      // [H][n_chunks][64]
+  int64_t energy_scratch_chunks;
+  // byte sizes per layer
+  int64_t k_codes_layer, v_codes_layer, k_scales_layer, v_scales_layer;
+};
+
+namespace kvq {
+
+// Kernel launchers (defined in the .hip sources).  All enqueue on `stream` and
+// return the launch status; arguments are validated by the caller.
+hipError_t launch_alloc(kvq_cache* c, int layer, const void* keys, int dtype, int64_t n_tok,
+                        const double* block_weight, hipStream_t stream);
+hipError_t launch_quantize(kvq_cache* c, int layer, const void* k, const void* v, int dtype,
+                           int64_t n_new, hipStream_t stream);
+hipError_t launch_decode(kvq_cache* c, int layer, const void* q, int dtype, float scale,
+                         float* out, int n_splits, hipStream_t stream);
+int auto_splits(const kvq_cache* c, int64_t len);
+
+// Offsets of one layer's storage.
+inline uint32_t* layer_k_codes(kvq_cache* c, int layer) {
+  return reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(c->k_codes) + c->k_codes_layer * layer);
+}
+inline uint32_t* layer_v_codes(kvq_cache* c, int layer) {
+  return reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(c->v_codes) + c->v_codes_layer * layer);
+}
+inline uint16_t* layer_k_scales(kvq_cache* c, int layer) {
+  return reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(c->k_scales) + c->k_scales_layer * layer);
+}
+inline uint16_t* layer_v_scales(kvq_cache* c, int layer) {
+  return reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(c->v_scales) + c->v_scales_layer * layer);
+}
+
+}  // namespace kvq

@@ -1,0 +1,254 @@
+"""Thin ctypes binding of libkvq (include/kvq.h): argument marshalling only.
+
+Every step of the hot path runs in the library's HIP kernels; this module only
+turns torch device tensors into pointers, picks torch's current HIP stream and
+maps status codes to exceptions.  It raises ImportError if the built library
+is missing: there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
+
+KVQ_OK, KVQ_EINVAL, KVQ_ENOMEM, KVQ_ECAPACITY, KVQ_ESTATE, KVQ_EHIP = range(6)
+KVQ_F16, KVQ_F32 = 0, 1
+CODEC_BGTQ, CODEC_UNIFORM, CODEC_NF16_B256 = 0, 1, 2
+ROPE_HALF, ROPE_INTERLEAVED = 0, 1
+PART_K_CODES, PART_V_CODES, PART_K_SCALES, PART_V_SCALES = range(4)
+
+EXPORTED = (
+    "kvq_cache_create", "kvq_cache_destroy", "kvq_alloc_bits", "kvq_get_plan",
+    "kvq_quantize_append", "kvq_decode_attn", "kvq_decode_attn_splits", "kvq_seq_len",
+    "kvq_layer_info_get", "kvq_read_cache", "kvq_codebook", "kvq_delta",
+    "kvq_nf16_codebook", "kvq_status_str", "kvq_last_error",
+)
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, what: str, detail: str = ""):
+        self.status = status
+        super().__init__(f"{what}: {_status_name(status)}" + (f" ({detail})" if detail else ""))
+
+
+class kvq_config(ctypes.Structure):
+    _fields_ = [
+        ("n_layers", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("batch", ctypes.c_int32), ("max_tokens", ctypes.c_int64),
+        ("k_bits", ctypes.c_int32), ("v_bits", ctypes.c_int32), ("b_min", ctypes.c_int32),
+        ("b_max", ctypes.c_int32), ("codec", ctypes.c_int32), ("pairing", ctypes.c_int32),
+    ]
+
+
+class kvq_layer_info(ctypes.Structure):
+    _fields_ = [
+        ("capacity", ctypes.c_int64), ("len", ctypes.c_int64), ("k_row_words", ctypes.c_int32),
+        ("v_dim_words", ctypes.c_int32), ("k_codes_bytes", ctypes.c_int64),
+        ("v_codes_bytes", ctypes.c_int64), ("k_scales_bytes", ctypes.c_int64),
+        ("v_scales_bytes", ctypes.c_int64), ("plan_ready", ctypes.c_int32),
+    ]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"libkvq.so not built at {_LIB_PATH}; run __graft_entry__.build()")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I32, I64, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    sig = {
+        "kvq_cache_create": (I32, [ctypes.POINTER(kvq_config), ctypes.POINTER(P)]),
+        "kvq_cache_destroy": (None, [P]),
+        "kvq_alloc_bits": (I32, [P, I32, P, I32, I64, P, P]),
+        "kvq_get_plan": (I32, [P, I32, P, P]),
+        "kvq_quantize_append": (I32, [P, I32, P, P, I32, I64, P]),
+        "kvq_decode_attn": (I32, [P, I32, P, I32, F32, P, P]),
+        "kvq_decode_attn_splits": (I32, [P, I32, P, I32, F32, P, I32, P]),
+        "kvq_seq_len": (I32, [P, I32, ctypes.POINTER(I64)]),
+        "kvq_layer_info_get": (I32, [P, I32, ctypes.POINTER(kvq_layer_info)]),
+        "kvq_read_cache": (I32, [P, I32, I32, I64, I64, P]),
+        "kvq_codebook": (I32, [I32, P, P]),
+        "kvq_delta": (I32, [P]),
+        "kvq_nf16_codebook": (I32, [P, P]),
+        "kvq_status_str": (ctypes.c_char_p, [I32]),
+        "kvq_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def _status_name(s: int) -> str:
+    return lib.kvq_status_str(s).decode()
+
+
+def _check(status: int, what: str):
+    if status != KVQ_OK:
+        detail = lib.kvq_last_error().decode() if status == KVQ_EHIP else ""
+        raise KvqError(status, what, detail)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float16:
+        return KVQ_F16
+    if t.dtype == torch.float32:
+        return KVQ_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t) -> int:
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream=None) -> Optional[int]:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+# ---- host-only constant tables --------------------------------------------------------------
+
+def codebook(bits: int):
+    """(fp16 centroids as np.float16[2^bits], fp32 boundaries[2^bits - 1]) from the library."""
+    cb = np.zeros(1 << bits, dtype=np.uint16)
+    bd = np.zeros((1 << bits) - 1, dtype=np.float32)
+    _check(lib.kvq_codebook(bits, cb.ctypes.data, bd.ctypes.data), "kvq_codebook")
+    return cb.view(np.float16), bd
+
+
+def delta():
+    d = np.zeros(8, dtype=np.float32)
+    _check(lib.kvq_delta(d.ctypes.data), "kvq_delta")
+    return d
+
+
+def nf16_codebook():
+    lv = np.zeros(16, dtype=np.uint16)
+    bd = np.zeros(15, dtype=np.float32)
+    _check(lib.kvq_nf16_codebook(lv.ctypes.data, bd.ctypes.data), "kvq_nf16_codebook")
+    return lv.view(np.float16), bd
+
+
+# ---- cache -----------------------------------------------------------------------------------
+
+@dataclass
+class Config:
+    n_layers: int
+    n_kv_heads: int
+    n_q_heads: int
+    batch: int
+    max_tokens: int
+    k_bits: int
+    v_bits: int
+    head_dim: int = 128
+    b_min: int = 0
+    b_max: int = 8
+    codec: int = CODEC_BGTQ
+    pairing: int = ROPE_HALF
+
+    def to_c(self) -> kvq_config:
+        return kvq_config(self.n_layers, self.n_kv_heads, self.n_q_heads, self.head_dim, self.batch,
+                          self.max_tokens, self.k_bits, self.v_bits, self.b_min, self.b_max,
+                          self.codec, self.pairing)
+
+
+def create_status(cfg: Config) -> int:
+    """Raw status of kvq_cache_create (the cache is destroyed right away on success)."""
+    h = ctypes.c_void_p()
+    c = cfg.to_c()
+    st = lib.kvq_cache_create(ctypes.byref(c), ctypes.byref(h))
+    if st == KVQ_OK:
+        lib.kvq_cache_destroy(h)
+    return st
+
+
+class Cache:
+    """Owns one kvq_cache; all tensor arguments are torch GPU tensors."""
+
+    def __init__(self, cfg: Config):
+        self.cfg = cfg
+        self._h = ctypes.c_void_p()
+        c = cfg.to_c()
+        _check(lib.kvq_cache_create(ctypes.byref(c), ctypes.byref(self._h)), "kvq_cache_create")
+
+    def close(self):
+        if self._h:
+            lib.kvq_cache_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def handle(self):
+        return self._h
+
+    def alloc_bits(self, layer: int, keys=None, block_weight=None, stream=None):
+        kp = _ptr(keys) if keys is not None else None
+        dt = _dtype_code(keys) if keys is not None else KVQ_F16
+        n = keys.shape[0] if keys is not None else 0
+        wp = _ptr(block_weight) if block_weight is not None else None
+        _check(lib.kvq_alloc_bits(self._h, layer, kp, dt, n, wp, _stream(stream)), "kvq_alloc_bits")
+
+    def get_plan(self, layer: int):
+        H = self.cfg.n_kv_heads
+        bits = np.zeros((H, 64), dtype=np.int8)
+        gains = np.zeros((H, 64), dtype=np.float32)
+        _check(lib.kvq_get_plan(self._h, layer, bits.ctypes.data, gains.ctypes.data), "kvq_get_plan")
+        return bits.astype(np.int64), gains
+
+    def quantize_append(self, layer: int, k, v, stream=None):
+        if k.shape != v.shape or k.dtype != v.dtype:
+            raise ValueError("k and v must have the same shape and dtype")
+        if k.dim() != 4 or k.shape[0] != self.cfg.batch or k.shape[2] != self.cfg.n_kv_heads \
+                or k.shape[3] != self.cfg.head_dim:
+            raise ValueError(f"k must be [batch, n_new, n_kv_heads, head_dim], got {tuple(k.shape)}")
+        _check(lib.kvq_quantize_append(self._h, layer, _ptr(k), _ptr(v), _dtype_code(k), k.shape[1],
+                                       _stream(stream)), "kvq_quantize_append")
+
+    def decode_attn(self, layer: int, q, out=None, scale: float = 0.0, n_splits: int = 0, stream=None):
+        import torch
+        if q.dim() != 3 or tuple(q.shape) != (self.cfg.batch, self.cfg.n_q_heads, self.cfg.head_dim):
+            raise ValueError(f"q must be [batch, n_q_heads, head_dim], got {tuple(q.shape)}")
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        if out.dtype != torch.float32 or tuple(out.shape) != tuple(q.shape):
+            raise ValueError("out must be fp32 with q's shape")
+        _check(lib.kvq_decode_attn_splits(self._h, layer, _ptr(q), _dtype_code(q), float(scale),
+                                          _ptr(out), int(n_splits), _stream(stream)), "kvq_decode_attn")
+        return out
+
+    def seq_len(self, layer: int) -> int:
+        n = ctypes.c_int64()
+        _check(lib.kvq_seq_len(self._h, layer, ctypes.byref(n)), "kvq_seq_len")
+        return n.value
+
+    def layer_info(self, layer: int) -> kvq_layer_info:
+        info = kvq_layer_info()
+        _check(lib.kvq_layer_info_get(self._h, layer, ctypes.byref(info)), "kvq_layer_info_get")
+        return info
+
+    def read(self, layer: int, part: int, dtype, offset: int = 0, nbytes: Optional[int] = None) -> np.ndarray:
+        info = self.layer_info(layer)
+        size = {PART_K_CODES: info.k_codes_bytes, PART_V_CODES: info.v_codes_bytes,
+                PART_K_SCALES: info.k_scales_bytes, PART_V_SCALES: info.v_scales_bytes}[part]
+        n = size - offset if nbytes is None else nbytes
+        buf = np.empty(n, dtype=np.uint8)
+        _check(lib.kvq_read_cache(self._h, layer, part, offset, n, buf.ctypes.data), "kvq_read_cache")
+        return buf.view(dtype)

@@ -1,0 +1,244 @@
+"""GPU (HIP, gfx950) vs oracle parity through the C ABI.
+
+Plans, codes, packed words and scales must be bit-exact; decode attention
+must match the oracle's fp64 attention over its own dequantized cache within
+max-abs 2e-3 and relative L2 1e-3.
+"""
+import numpy as np
+import pytest
+
+from oracle import attention as at
+from oracle import layout as lay
+from synth import WORKLOADS, gen_layer, gen_query
+from tests.parity import CODEC, PAIRING, OracleLayer, assert_attention_close, errors
+
+pytestmark = pytest.mark.gpu
+
+
+def _torch():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch
+
+
+def _kvq():
+    from rope_aware_bit_amd import kvq
+    return kvq
+
+
+def run_case(wname, T, k_bits, v_bits, codec="bgtq", pairing="half", batch=None, layer=0,
+             chunks=None, n_splits=0, noise="gauss", temper=False, check_codes=True, sample_rows=None,
+             b_min=0, b_max=8):
+    """Quantize T tokens of one layer on the GPU and in the oracle; compare everything."""
+    torch = _torch()
+    kvq = _kvq()
+    w = WORKLOADS[wname]
+    B = w.batch if batch is None else batch
+    H, Hq = w.n_kv, w.n_q
+    ks, vs, qs = [], [], []
+    for b in range(B):
+        k, v = gen_layer(w, layer, 0, T, seq=b, noise=noise, pairing=pairing)
+        ks.append(k)
+        vs.append(v)
+        qs.append(gen_query(w, layer, T, seq=b, noise=noise, pairing=pairing))
+    K = np.stack(ks)            # [B, T, H, d]
+    V = np.stack(vs)
+    Q = np.stack(qs)            # [B, Hq, d]
+    tc = min(T, w.calib_tokens)
+    calib = K[:, :tc].reshape(B * tc, H, 128)
+    ol = OracleLayer(calib if codec == "bgtq" else K[:, :1].reshape(B, H, 128), k_bits, v_bits,
+                     codec, pairing, b_min, b_max)
+
+    cfg = kvq.Config(n_layers=1, n_kv_heads=H, n_q_heads=Hq, batch=B, max_tokens=T, k_bits=k_bits,
+                     v_bits=v_bits, b_min=b_min, b_max=b_max, codec=CODEC[codec],
+                     pairing=PAIRING[pairing])
+    cache = kvq.Cache(cfg)
+    dev = torch.device("cuda:0")
+    cache.alloc_bits(0, torch.from_numpy(np.ascontiguousarray(calib)).to(dev) if codec == "bgtq" else None)
+    bits, gains = cache.get_plan(0)
+    assert np.array_equal(bits, ol.widths), "plan widths differ"
+    assert np.array_equal(gains.view(np.uint32), ol.g.astype(np.float32).view(np.uint32)), "gains differ"
+
+    bounds = [0, T] if chunks is None else [0, *np.cumsum(chunks).tolist()]
+    assert bounds[-1] == T
+    Kt = torch.from_numpy(K).to(dev)
+    Vt = torch.from_numpy(V).to(dev)
+    for a, z in zip(bounds[:-1], bounds[1:]):
+        cache.quantize_append(0, Kt[:, a:z].contiguous(), Vt[:, a:z].contiguous())
+    assert cache.seq_len(0) == T
+
+    sigma = 0.0
+    refs = []
+    for b in range(B):
+        kh_all, vh_all, qo = [], [], []
+        for h in range(H):
+            r = ol.quantize_head(K[b, :, h], V[b, :, h], h,
+                                 K[b].reshape(T, H * 128) if codec == "nf16" else None,
+                                 V[b].reshape(T, H * 128) if codec == "nf16" else None)
+            qo.append(r)
+            kh, vh = ol.dequant(r, h)
+            kh_all.append(kh)
+            vh_all.append(vh)
+        refs.append((qo, np.stack(kh_all), np.stack(vh_all)))
+    if temper:
+        # choose sigma so that the logits' standard deviation is about 2 (softmax blends)
+        qb = Q[0].astype(np.float64)
+        lg = np.concatenate([refs[0][1][h // w.group] @ qb[h] for h in range(Hq)])
+        sigma = float(2.0 / lg.std())
+
+    info = cache.layer_info(0)
+    cap = info.capacity
+    if check_codes:
+        kw = cache.read(0, kvq.PART_K_CODES, np.uint32).reshape(B, H, cap, info.k_row_words)
+        vw = cache.read(0, kvq.PART_V_CODES, np.uint32).reshape(B, H, cap // 128, 128, info.v_dim_words)
+        kscale = cache.read(0, kvq.PART_K_SCALES, np.uint16)
+        vscale = cache.read(0, kvq.PART_V_SCALES, np.uint16)
+        if codec == "nf16":
+            kscale = kscale.reshape(B, cap, -1)
+            vscale = vscale.reshape(B, cap, -1)
+        else:
+            kscale = kscale.reshape(B, H, cap)
+            vscale = vscale.reshape(B, H, cap)
+        nt = (T + 127) // 128
+        vb = 4 if codec == "nf16" else v_bits
+        for b in range(B):
+            for h in range(H):
+                r = refs[b][0][h]
+                rows = slice(None) if sample_rows is None else sample_rows
+                assert np.array_equal(kw[b, h, :T][rows], r["k_words"][rows]), f"K words differ b={b} h={h}"
+                assert np.array_equal(vw[b, h, :nt], lay.pack_v_tiles(r["v_codes"], vb)), f"V tiles differ b={b} h={h}"
+                if codec == "nf16":
+                    assert np.array_equal(kscale[b, :T], r["k_scale_blocks"].view(np.uint16))
+                    assert np.array_equal(vscale[b, :T], r["v_scale_blocks"].view(np.uint16))
+                else:
+                    assert np.array_equal(kscale[b, h, :T], r["k_s16"].view(np.uint16)), f"K scales b={b} h={h}"
+                    assert np.array_equal(vscale[b, h, :T], r["v_s16"].view(np.uint16)), f"V scales b={b} h={h}"
+
+    Qt = torch.from_numpy(Q).to(dev)
+    out = cache.decode_attn(0, Qt, scale=sigma, n_splits=n_splits)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    ref = np.stack([at.decode_attention(Q[b].astype(np.float64), refs[b][1], refs[b][2],
+                                        sigma if sigma > 0 else None) for b in range(B)])
+    res = assert_attention_close(got, ref, f"{wname} T={T} K{k_bits}V{v_bits} {codec}")
+    cache.close()
+    return res
+
+
+def test_tiny_end_to_end():
+    w = WORKLOADS["tiny"]
+    run_case("tiny", w.T, 4, 4)
+
+
+def test_tiny_tempered_softmax():
+    run_case("tiny", 1024, 4, 4, temper=True)
+
+
+@pytest.mark.parametrize("pairing", ["half", "interleaved"])
+def test_tiny_pairings(pairing):
+    run_case("tiny", 700, 3, 2, pairing=pairing)
+
+
+def test_single_token():
+    run_case("tiny", 1, 4, 4)
+
+
+def test_ragged_appends_cross_tiles():
+    run_case("tiny", 1000, 3, 3, chunks=[100, 200, 37, 1, 662])
+
+
+@pytest.mark.parametrize("kb,vb", [(2, 2), (3, 3), (4, 4)])
+def test_llama_layer_budgets(kb, vb):
+    run_case("llama8b_32k", 4096, kb, vb, temper=True)
+
+
+@pytest.mark.parametrize("kb", [1, 5, 8])
+def test_extreme_budgets(kb):
+    run_case("llama8b_32k", 1000, kb, 8 if kb == 8 else 1)
+
+
+def test_uniform_codec():
+    run_case("llama8b_32k", 3000, 3, 3, codec="uniform", temper=True)
+
+
+def test_nf16_codec_gauss_and_t5():
+    run_case("llama8b_b64", 1500, 4, 4, codec="nf16", batch=3, temper=True)
+    run_case("llama8b_b64", 1500, 4, 4, codec="nf16", batch=2, noise="t5", temper=True)
+
+
+def test_bgtq_batched_t5():
+    run_case("llama8b_b64", 2048, 4, 4, batch=4, noise="t5", temper=True)
+
+
+def test_b_min_b_max_limits():
+    run_case("llama8b_32k", 600, 3, 3, b_min=1, b_max=5)
+
+
+def test_split_count_invariance_and_determinism():
+    torch = _torch()
+    kvq = _kvq()
+    w = WORKLOADS["qwen3b_128k"]
+    T = 5000
+    k, v = gen_layer(w, 0, 0, T)
+    q = gen_query(w, 0, T)
+    cache = kvq.Cache(kvq.Config(1, w.n_kv, w.n_q, 1, T, 3, 3))
+    dev = torch.device("cuda:0")
+    cache.alloc_bits(0, torch.from_numpy(k[:2048]).to(dev))
+    cache.quantize_append(0, torch.from_numpy(k[None]).to(dev), torch.from_numpy(v[None]).to(dev))
+    qt = torch.from_numpy(q[None]).to(dev)
+    outs = [cache.decode_attn(0, qt, n_splits=s).cpu().numpy() for s in (1, 2, 7, 40)]
+    for o in outs[1:]:
+        assert np.allclose(o, outs[0], rtol=2e-6, atol=2e-6)
+    a = cache.decode_attn(0, qt).cpu().numpy()
+    b = cache.decode_attn(0, qt).cpu().numpy()
+    assert np.array_equal(a, b)
+    cache.close()
+
+
+def test_error_states():
+    torch = _torch()
+    kvq = _kvq()
+    dev = torch.device("cuda:0")
+    cache = kvq.Cache(kvq.Config(2, 2, 16, 1, 300, 3, 3))
+    x = torch.zeros(1, 10, 2, 128, dtype=torch.float16, device=dev)
+    q = torch.zeros(1, 16, 128, dtype=torch.float16, device=dev)
+    with pytest.raises(kvq.KvqError) as e:
+        cache.quantize_append(0, x, x)                       # no plan yet
+    assert e.value.status == kvq.KVQ_ESTATE
+    with pytest.raises(kvq.KvqError) as e:
+        cache.alloc_bits(0, torch.zeros(0, 2, 128, dtype=torch.float16, device=dev))
+    assert e.value.status == kvq.KVQ_EINVAL
+    cache.alloc_bits(0, torch.randn(64, 2, 128, device=dev).half())
+    with pytest.raises(kvq.KvqError) as e:
+        cache.decode_attn(0, q)                               # empty layer
+    assert e.value.status == kvq.KVQ_ESTATE
+    cache.quantize_append(0, x[:, :0].contiguous(), x[:, :0].contiguous())   # n_new = 0 is a no-op
+    assert cache.seq_len(0) == 0
+    cache.quantize_append(0, x, x)
+    with pytest.raises(kvq.KvqError) as e:
+        cache.alloc_bits(0, torch.randn(64, 2, 128, device=dev).half())   # re-alloc after append
+    assert e.value.status == kvq.KVQ_ESTATE
+    big = torch.zeros(1, 291, 2, 128, dtype=torch.float16, device=dev)
+    with pytest.raises(kvq.KvqError) as e:
+        cache.quantize_append(0, big, big)                    # 10 + 291 > 300
+    assert e.value.status == kvq.KVQ_ECAPACITY
+    assert cache.seq_len(0) == 10
+    with pytest.raises(kvq.KvqError) as e:
+        cache.decode_attn(5, q)
+    assert e.value.status == kvq.KVQ_EINVAL
+    out = cache.decode_attn(0, q)
+    assert torch.isfinite(out).all()
+    cache.close()
+
+
+def test_headline_layer_full_size():
+    """Qwen2.5-3B-shaped layer at 131072 tokens, K3V3: sampled K rows, all V tiles and
+    scales bit-exact; decode (auto split count, as benchmarked) vs fp64 oracle."""
+    rng = np.random.default_rng(0)
+    rows = np.sort(rng.choice(131072, 4096, replace=False))
+    run_case("qwen3b_128k", 131072, 3, 3, layer=5, sample_rows=rows)
+
+
+def test_longest_context_layer_full_size():
+    """512K context, K2V2, one layer; decode with the automatic split-K."""
+    run_case("qwen3b_512k", 524288, 2, 2, layer=0, check_codes=False)
