@@ -1,0 +1,216 @@
+#!/usr/bin/env python3
+"""Packed-KV decode attention benchmark on one MI355X.
+
+Workload (default): Qwen2.5-3B-shaped decode attention step, 36 layers, 2 KV
+heads, 16 query heads, head_dim 128, 131072 cached tokens per layer, batch 1,
+Block-GTQ K3V3 packed cache.  Synthetic RoPE'd Gaussian keys with per-block
+log-normal deviations (2 outlier blocks per head at 10x) and Gaussian values
+are drawn on the GPU; each layer is calibrated on its first 2048 tokens,
+then all tokens are appended.
+
+A step = one kvq_decode_attn call per layer (36 launches, one query each),
+inputs resident in HBM.  `value` is the step's algorithmic bytes over its time
+(effective GB/s); tokens/s and % of the 8 TB/s peak are reported beside it.
+The roofline entry times every decode launch with HIP events on the launch
+stream.  The CPU baseline times the fp64 oracle's decode (unpack, dequantize,
+attention) of one of the 36 layers on the host and scales it to a step.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+PLAN_BYTES_PER_HEAD = 1024   # field dims/widths/offsets and gains read by each decode launch
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(k0, v0, q0, calib, kb, vb, n_layers, bytes_per_step):
+    """Time the oracle's decode of one layer (host cores, BLAS limited to one thread)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import allocation as al
+    from oracle import attention as at
+    from oracle import layout as lay
+    from tests.parity import OracleLayer
+
+    H = k0.shape[1]
+    ol = OracleLayer(calib, kb, vb)
+    packed = []
+    for h in range(H):                      # quantize + pack (not timed: that is the append)
+        r = ol.quantize_head(k0[:, h], v0[:, h], h)
+        packed.append((r["k_words"], r["k_s16"], lay.pack_v_tiles(r["v_codes"], vb), r["v_s16"]))
+    T = k0.shape[0]
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        kh, vh = [], []
+        for h in range(H):
+            kw, ks, vw, vs = packed[h]
+            dims, ws = ol.fields(h)
+            kc = lay.unpack_k_rows(kw, dims, ws, 128)
+            kh.append(at.dequant_k(kc, ks, al.dim_widths(ol.widths[h], 128), al.dim_values(ol.g[h], 128)))
+            vh.append(at.dequant_v(lay.unpack_v_tiles(vw, vb, T), vs, vb))
+        out = at.decode_attention(q0.astype(np.float64), np.stack(kh), np.stack(vh))
+        dt = time.perf_counter() - t0
+    assert np.all(np.isfinite(out))
+    step_s = dt * n_layers
+    return {
+        "value": round(bytes_per_step / step_s / 1e9, 4),
+        "unit": "GB/s",
+        "tokens_per_s": round(1.0 / step_s, 5),
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"1 of {n_layers} layers ({H} KV heads x {T} tokens): unpack + fp64 dequantize + "
+                  f"fp64 attention took {dt:.2f} s; scaled x{n_layers} to one step",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3b_128k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the packed decode path "
+              "is single-GPU and has no multi-GPU mode.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from rope_aware_bit_amd import kvq
+    from synth import WORKLOADS
+    from synth.torch_gen import TorchLayerGen
+
+    w = WORKLOADS[args.workload]
+    kb, vb = w.budgets[0]
+    L, H, Hq, B, T = w.n_layers, w.n_kv, w.n_q, w.batch, w.T
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    cache = kvq.Cache(kvq.Config(L, H, Hq, B, T, kb, vb))
+    gen = TorchLayerGen(w, dev)
+    chunk = min(w.calib_tokens, T)
+    app_ms = []
+    keep = None
+    t_setup = time.perf_counter()
+    for layer in range(L):
+        k, v = gen.layer(layer)
+        cache.alloc_bits(layer, k[:chunk])
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        cache.quantize_append(layer, k[None, :chunk], v[None, :chunk])
+        e1.record(stream)
+        if T > chunk:
+            cache.quantize_append(layer, k[None, chunk:], v[None, chunk:])
+        torch.cuda.synchronize()
+        app_ms.append(e0.elapsed_time(e1))
+        if layer == 0:
+            keep = (k.cpu().numpy(), v.cpu().numpy(), k[:chunk].cpu().numpy())
+        del k, v
+    qs = [gen.query(layer)[None].contiguous() for layer in range(L)]
+    outs = [torch.empty(B, Hq, 128, dtype=torch.float32, device=dev) for _ in range(L)]
+    torch.cuda.synchronize()
+    log(f"setup {time.perf_counter() - t_setup:.1f} s")
+
+    bytes_cache_layer = B * H * T * ((kb + vb) * 128 / 8 + 4)
+    bytes_launch = bytes_cache_layer + B * Hq * 128 * 2 + B * Hq * 128 * 4 + H * PLAN_BYTES_PER_HEAD
+    bytes_step = bytes_launch * L
+
+    def step():
+        for layer in range(L):
+            cache.decode_attn(layer, qs[layer], out=outs[layer])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    for o in outs:
+        assert torch.isfinite(o).all()
+
+    # per-launch durations of the decode kernel (events around each launch, same stream)
+    pairs = []
+    for _ in range(args.steps):
+        for layer in range(L):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            cache.decode_attn(layer, qs[layer], out=outs[layer])
+            b.record(stream)
+            pairs.append((a, b))
+    torch.cuda.synchronize()
+    launch_us = float(np.mean([a.elapsed_time(b) for a, b in pairs])) * 1e3
+
+    value = bytes_step / (ms_step * 1e-3) / 1e9
+    achieved = bytes_launch / (launch_us * 1e-6) / 1e9
+    res = {
+        "metric": "packed-KV decode attn: effective HBM GB/s (% of peak) + tokens/s at 128K K3V3",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(B / (ms_step * 1e-3), 2),
+        "config": {
+            "workload": f"packed decode attention, Qwen2.5-3B shape: {L} layers x {H} KV heads, "
+                        f"{Hq} query heads, head_dim 128, {T} tokens, batch {B}, Block-GTQ K{kb}V{vb}",
+            "layers": L, "kv_heads": H, "q_heads": Hq, "head_dim": 128, "context": T, "batch": B,
+            "k_bits": kb, "v_bits": vb, "codec": "bgtq", "launches_per_step": L,
+            "bytes_per_step": int(bytes_step), "hip_graph": False,
+        },
+        "append": {
+            "tokens_per_layer": chunk,
+            "us_per_layer": round(float(np.mean(app_ms)) * 1e3, 2),
+            "GB/s": round((B * H * chunk * (2 * 128 * 2 + (kb + vb) * 16 + 4)) /
+                          (float(np.mean(app_ms)) * 1e-3) / 1e9, 2),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode_split",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "launch_us": round(launch_us, 3),
+            "bytes_per_launch": int(bytes_launch),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        k0, v0, calib = keep
+        res["cpu_baseline"] = cpu_baseline(k0, v0, qs[0][0].cpu().numpy(), calib, kb, vb, L, bytes_step)
+    cache.close()
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

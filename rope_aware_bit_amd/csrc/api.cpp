@@ -49,7 +49,7 @@ bool layer_ok(const kvq_cache* c, int32_t layer) {
 
 void free_device(kvq_cache* c) {
   void* ptrs[] = {c->k_codes, c->v_codes, c->k_scales, c->v_scales, c->plans,
-                  c->tables,  c->part_o,  c->part_ml,  c->energy_scratch};
+                  c->tables,  c->part_o,  c->part_ml,  c->energy_scratch, c->split_counters};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
 }
@@ -155,8 +155,11 @@ kvq_status kvq_cache_create(const kvq_config* cfg, kvq_cache** out) {
     st = dev_alloc(reinterpret_cast<void**>(&c->part_o), per_split / (kHeadDim + 2) * kHeadDim * ms, "partials");
   if (st == KVQ_OK)
     st = dev_alloc(reinterpret_cast<void**>(&c->part_ml), per_split / (kHeadDim + 2) * 2 * ms, "partials");
+  if (st == KVQ_OK)
+    st = dev_alloc(reinterpret_cast<void**>(&c->split_counters), sizeof(unsigned) * B * H, "counters");
   if (st == KVQ_OK) {
     const hipError_t es[] = {
+        hipMemset(c->split_counters, 0, sizeof(unsigned) * B * H),
         hipMemset(c->k_codes, 0, c->k_codes_layer * L),
         hipMemset(c->v_codes, 0, c->v_codes_layer * L),
         hipMemset(c->k_scales, 0, c->k_scales_layer * L),

@@ -13,8 +13,10 @@
 // per head updates the running max / sum, then lane i decodes dim i of the
 // tile's dim-major V stream (staged in LDS) and accumulates the G outputs.
 // Each split writes (m, l, unnormalised o) for its G heads.
-// Pass 2 (combine_splits): one workgroup per query head combines the splits in
-// split order: m* = max m_s, l = sum exp(m_s - m*) l_s, o = sum exp(m_s - m*) o_s / l.
+// The last workgroup of a (sequence, KV head) to finish (an agent-scope counter)
+// combines the splits in split order: m* = max m_s, l = sum exp(m_s - m*) l_s,
+// o = sum exp(m_s - m*) o_s / l, and resets the counter for the next call.  Calls
+// that overlap on one cache (two streams) would share the counters and must not.
 #include <hip/hip_fp16.h>
 
 #include "kvq_internal.h"
@@ -37,7 +39,7 @@ __global__ __launch_bounds__(256) void decode_split(
     const Plan* __restrict__ plans, const Tables* __restrict__ tab, const uint32_t* __restrict__ kc,
     const uint32_t* __restrict__ vc, const uint16_t* __restrict__ ks, const uint16_t* __restrict__ vs,
     int k_words, int v_bits, int n_nf, int n_splits, float* __restrict__ part_o,
-    float* __restrict__ part_ml) {
+    float* __restrict__ part_ml, unsigned* __restrict__ counters, float* __restrict__ out) {
   const int tid = threadIdx.x;
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int n_q = n_kv * G;
@@ -188,27 +190,37 @@ __global__ __launch_bounds__(256) void decode_split(
     part_ml[(pbase + tid) * 2 + 0] = m_run_s[tid];
     part_ml[(pbase + tid) * 2 + 1] = l_run_s[tid];
   }
-}
 
-__global__ __launch_bounds__(128) void combine_splits(const float* __restrict__ part_o,
-                                                      const float* __restrict__ part_ml, int n_kv,
-                                                      int G, int n_splits, float* __restrict__ out) {
-  const int i = threadIdx.x;
-  const int hq = blockIdx.x, b = blockIdx.y;
-  const int h = hq / G, g = hq % G;
-  const int64_t bh = static_cast<int64_t>(b) * n_kv + h;
-  float mstar = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) mstar = fmaxf(mstar, part_ml[((bh * n_splits + s) * G + g) * 2]);
-  float l = 0.0f, o = 0.0f;
-  for (int s = 0; s < n_splits; ++s) {
-    const int64_t p = (bh * n_splits + s) * G + g;
-    const float ms = part_ml[p * 2];
-    if (ms == -INFINITY) continue;
-    const float w = __expf(ms - mstar);
-    l += w * part_ml[p * 2 + 1];
-    o += w * part_o[p * kHeadDim + i];
+  // The last split of this (sequence, KV head) to finish combines all splits, in split
+  // order: release the partials at agent scope, count, and acquire before reading.
+  __shared__ bool last_s;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(counters + bh, 1u, __ATOMIC_ACQ_REL,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    last_s = prev == static_cast<unsigned>(n_splits - 1);
   }
-  out[(static_cast<int64_t>(b) * n_kv * G + hq) * kHeadDim + i] = o / l;
+  __syncthreads();
+  if (!last_s) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  for (int idx = tid; idx < G * kHeadDim; idx += blockDim.x) {
+    const int g = idx / kHeadDim, i = idx % kHeadDim;
+    const int64_t p0 = bh * n_splits * G + g;
+    float mstar = -INFINITY;
+    for (int sp = 0; sp < n_splits; ++sp) mstar = fmaxf(mstar, part_ml[(p0 + sp * G) * 2]);
+    float l = 0.0f, o = 0.0f;
+    for (int sp = 0; sp < n_splits; ++sp) {
+      const int64_t p = p0 + sp * G;
+      const float ms = part_ml[p * 2];
+      if (ms == -INFINITY) continue;
+      const float wgt = __expf(ms - mstar);
+      l += wgt * part_ml[p * 2 + 1];
+      o += wgt * part_o[p * kHeadDim + i];
+    }
+    out[(static_cast<int64_t>(b) * n_q + h * G + g) * kHeadDim + i] = o / l;
+  }
+  if (tid == 0) counters[bh] = 0u;  // ready for the next call on this stream
 }
 
 template <typename TQ, int G>
@@ -225,17 +237,13 @@ hipError_t launch_g(kvq_cache* c, int layer, const void* q, float sigma, float* 
                        static_cast<const TQ*>(q), sigma, len, cfg.n_kv_heads, c->cap, tps, plans,
                        c->tables, layer_k_codes(c, layer), layer_v_codes(c, layer),
                        layer_k_scales(c, layer), layer_v_scales(c, layer), c->k_words, cfg.v_bits,
-                       c->n_nf_blocks, S, c->part_o, c->part_ml);
+                       c->n_nf_blocks, S, c->part_o, c->part_ml, c->split_counters, out);
   else
     hipLaunchKernelGGL((decode_split<TQ, G, false>), grid, dim3(256), 0, stream,
                        static_cast<const TQ*>(q), sigma, len, cfg.n_kv_heads, c->cap, tps, plans,
                        c->tables, layer_k_codes(c, layer), layer_v_codes(c, layer),
                        layer_k_scales(c, layer), layer_v_scales(c, layer), c->k_words, cfg.v_bits,
-                       c->n_nf_blocks, S, c->part_o, c->part_ml);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(combine_splits, dim3(cfg.n_q_heads, cfg.batch), dim3(128), 0, stream,
-                     c->part_o, c->part_ml, cfg.n_kv_heads, G, S, out);
+                       c->n_nf_blocks, S, c->part_o, c->part_ml, c->split_counters, out);
   return hipGetLastError();
 }
 

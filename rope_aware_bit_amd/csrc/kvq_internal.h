@@ -63,6 +63,7 @@ struct kvq_cache {
   kvq::Tables host_tables;
   float* part_o;               // split partials [B][H][max_splits][G][128]
   float* part_ml;              // [B][H][max_splits][G][2]
+  unsigned* split_counters;    // [B][H] finished-split counters (zero between calls)
   int max_splits;
   double* energy_scratch;      // [H][n_chunks][64]
   int64_t energy_scratch_chunks;

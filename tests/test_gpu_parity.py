@@ -44,6 +44,7 @@ def run_case(wname, T, k_bits, v_bits, codec="bgtq", pairing="half", batch=None,
     K = np.stack(ks)            # [B, T, H, d]
     V = np.stack(vs)
     Q = np.stack(qs)            # [B, Hq, d]
+    print(f"[{wname} T={T} K{k_bits}V{v_bits} {codec}] inputs generated", flush=True)
     tc = min(T, w.calib_tokens)
     calib = K[:, :tc].reshape(B * tc, H, 128)
     ol = OracleLayer(calib if codec == "bgtq" else K[:, :1].reshape(B, H, 128), k_bits, v_bits,
@@ -80,6 +81,7 @@ def run_case(wname, T, k_bits, v_bits, codec="bgtq", pairing="half", batch=None,
             kh_all.append(kh)
             vh_all.append(vh)
         refs.append((qo, np.stack(kh_all), np.stack(vh_all)))
+    print(f"[{wname} T={T}] oracle quantized", flush=True)
     if temper:
         # choose sigma so that the logits' standard deviation is about 2 (softmax blends)
         qb = Q[0].astype(np.float64)
@@ -239,6 +241,7 @@ def test_headline_layer_full_size():
     run_case("qwen3b_128k", 131072, 3, 3, layer=5, sample_rows=rows)
 
 
+@pytest.mark.timeout(600)
 def test_longest_context_layer_full_size():
     """512K context, K2V2, one layer; decode with the automatic split-K."""
     run_case("qwen3b_512k", 524288, 2, 2, layer=0, check_codes=False)
