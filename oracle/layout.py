@@ -10,10 +10,13 @@ order (allocation.field_order), each field's code written least-significant
 bit first into a little-endian stream of 32-bit words; a row is exactly
 B_K * d / 32 words (widths sum to B_K * d bits).
 
-V tiles.  Tokens are grouped in tiles of 128 positions.  Inside a tile the
-codes are dim-major: for dim i, the 128 tokens' B_V-bit codes form one
-LSB-first stream of 4 * B_V words (token tau at bit tau * B_V).  A tile is
-d * 4 * B_V words.
+V tiles.  Tokens are grouped in tiles of 128 positions.  Inside a tile, the
+codes of one dim for 32 consecutive tokens form a segment: an LSB-first stream
+of B_V words (token 32g + e of the tile at bit e * B_V).  The 128 dims x 4
+token groups = 512 segments are stored in the order (dim // 16, g, dim % 16),
+i.e. segment index ((dim // 16) * 4 + g) * 16 + dim % 16, so that 64
+consecutive segments are the 16 dims x 4 token groups of one 16-dim slice.
+A tile is 512 * B_V words.
 """
 from __future__ import annotations
 
@@ -59,24 +62,32 @@ def unpack_k_rows(words: np.ndarray, fdims: np.ndarray, fwidths: np.ndarray, hea
     return codes
 
 
-def pack_v_tiles(codes: np.ndarray, bits: int) -> np.ndarray:
-    """codes[T, d] -> words uint32[ceil(T/128), d, 4*bits]; tokens past T are zero."""
+def _v_segments(codes: np.ndarray):
+    """codes[T, 128] -> (segments[nt * 512, 32] in storage order, nt); tokens past T are 0."""
     T, d = codes.shape
+    assert d == 128
     nt = (T + V_TILE - 1) // V_TILE
     padded = np.zeros((nt * V_TILE, d), dtype=np.uint8)
     padded[:T] = codes
-    # [tile, dim, token-in-tile]: each (tile, dim) row is one dim's 128-token stream
-    streams = padded.reshape(nt, V_TILE, d).transpose(0, 2, 1).reshape(nt * d, V_TILE)
-    w = np.zeros((nt * d, 4 * bits), dtype=np.uint32)
-    for tau in range(V_TILE):
-        _put(w, tau * bits, bits, streams[:, tau])
-    return w.reshape(nt, d, 4 * bits)
+    x = padded.reshape(nt, 4, 32, 8, 16)             # [tile, g, e, dim//16, dim%16]
+    x = x.transpose(0, 3, 1, 4, 2)                    # [tile, dim//16, g, dim%16, e]
+    return x.reshape(nt * 512, 32), nt
+
+
+def pack_v_tiles(codes: np.ndarray, bits: int) -> np.ndarray:
+    """codes[T, 128] -> words uint32[ceil(T/128), 512, bits]."""
+    seg, nt = _v_segments(codes)
+    w = np.zeros((nt * 512, bits), dtype=np.uint32)
+    for e in range(32):
+        _put(w, e * bits, bits, seg[:, e])
+    return w.reshape(nt, 512, bits)
 
 
 def unpack_v_tiles(words: np.ndarray, bits: int, T: int) -> np.ndarray:
-    nt, d, nw = words.shape
-    flat = words.reshape(nt * d, nw)
-    streams = np.zeros((nt * d, V_TILE), dtype=np.uint8)
-    for tau in range(V_TILE):
-        streams[:, tau] = _get(flat, tau * bits, bits)
-    return streams.reshape(nt, d, V_TILE).transpose(0, 2, 1).reshape(nt * V_TILE, d)[:T]
+    nt = words.shape[0]
+    flat = words.reshape(nt * 512, bits)
+    seg = np.zeros((nt * 512, 32), dtype=np.uint8)
+    for e in range(32):
+        seg[:, e] = _get(flat, e * bits, bits)
+    x = seg.reshape(nt, 8, 4, 16, 32).transpose(0, 2, 4, 1, 3)   # [tile, g, e, dim//16, dim%16]
+    return x.reshape(nt * V_TILE, 128)[:T]

@@ -131,6 +131,7 @@ __global__ __launch_bounds__(64) void greedy_plan(const double* __restrict__ scr
   P->fdim[2 * j] = P->fdim[2 * j + 1] = 0;
   P->fwidth[2 * j] = P->fwidth[2 * j + 1] = 0;
   P->foff[2 * j] = P->foff[2 * j + 1] = 0;
+  P->pdesc[j] = 0u;
   __syncthreads();
   if (b > 0) {
     P->fdim[2 * rank] = static_cast<uint8_t>(p0);
@@ -138,6 +139,7 @@ __global__ __launch_bounds__(64) void greedy_plan(const double* __restrict__ scr
     P->fwidth[2 * rank] = P->fwidth[2 * rank + 1] = static_cast<uint8_t>(b);
     P->foff[2 * rank] = static_cast<uint16_t>(off);
     P->foff[2 * rank + 1] = static_cast<uint16_t>(off + b);
+    P->pdesc[rank] = static_cast<uint32_t>(off) | (static_cast<uint32_t>(b) << 16);
   }
   P->g[p0] = P->g[p1] = g;
   P->ig[p0] = P->ig[p1] = ig;

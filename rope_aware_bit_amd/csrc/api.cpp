@@ -49,7 +49,8 @@ bool layer_ok(const kvq_cache* c, int32_t layer) {
 
 void free_device(kvq_cache* c) {
   void* ptrs[] = {c->k_codes, c->v_codes, c->k_scales, c->v_scales, c->plans,
-                  c->tables,  c->part_o,  c->part_ml,  c->energy_scratch, c->split_counters};
+                  c->tables,  c->part_o,  c->part_ml,  c->energy_scratch, c->split_counters,
+                  c->gpart_o, c->gpart_ml};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
 }
@@ -136,10 +137,10 @@ kvq_status kvq_cache_create(const kvq_config* cfg, kvq_cache** out) {
   c->v_codes_layer = B * H * cap * c->v_words * 4;  // (cap/128) tiles * 128 dims * v_words words
   c->k_scales_layer = nf ? B * cap * c->n_nf_blocks * 2 : B * H * cap * 2;
   c->v_scales_layer = c->k_scales_layer;
-  // split partials: at most 1024 splits per (sequence, head), at most 256 MiB of partials
+  // split partials: at most 256 splits per (sequence, head), at most 256 MiB of partials
   int64_t per_split = B * H * c->group * (kHeadDim + 2) * 4;
   int64_t ms = (int64_t(256) << 20) / per_split;
-  if (ms > 1024) ms = 1024;
+  if (ms > 256) ms = 256;
   if (ms < 1) ms = 1;
   c->max_splits = static_cast<int>(ms);
 
@@ -156,10 +157,14 @@ kvq_status kvq_cache_create(const kvq_config* cfg, kvq_cache** out) {
   if (st == KVQ_OK)
     st = dev_alloc(reinterpret_cast<void**>(&c->part_ml), per_split / (kHeadDim + 2) * 2 * ms, "partials");
   if (st == KVQ_OK)
-    st = dev_alloc(reinterpret_cast<void**>(&c->split_counters), sizeof(unsigned) * B * H, "counters");
+    st = dev_alloc(reinterpret_cast<void**>(&c->gpart_o), per_split / (kHeadDim + 2) * kHeadDim * 16, "partials");
+  if (st == KVQ_OK)
+    st = dev_alloc(reinterpret_cast<void**>(&c->gpart_ml), per_split / (kHeadDim + 2) * 2 * 16, "partials");
+  if (st == KVQ_OK)
+    st = dev_alloc(reinterpret_cast<void**>(&c->split_counters), sizeof(unsigned) * B * H * 17, "counters");
   if (st == KVQ_OK) {
     const hipError_t es[] = {
-        hipMemset(c->split_counters, 0, sizeof(unsigned) * B * H),
+        hipMemset(c->split_counters, 0, sizeof(unsigned) * B * H * 17),
         hipMemset(c->k_codes, 0, c->k_codes_layer * L),
         hipMemset(c->v_codes, 0, c->v_codes_layer * L),
         hipMemset(c->k_scales, 0, c->k_scales_layer * L),
@@ -266,10 +271,10 @@ kvq_status kvq_decode_attn_splits(kvq_cache* c, int32_t layer, const void* q, in
   if (dtype != KVQ_F16 && dtype != KVQ_F32) return KVQ_EINVAL;
   if (!(softmax_scale == softmax_scale)) return KVQ_EINVAL;  // NaN
   if (!c->plan_ready[layer] || c->len[layer] == 0) return KVQ_ESTATE;
-  int S = n_splits > 0 ? n_splits : kvq::auto_splits(c, c->len[layer]);
+  int S = n_splits > 0 ? n_splits : kvq::auto_splits_mfma(c, c->len[layer]);
   if (S > c->max_splits) return KVQ_EINVAL;
-  hipError_t e = kvq::launch_decode(c, layer, q, dtype, softmax_scale, out, S,
-                                    static_cast<hipStream_t>(stream));
+  hipError_t e = kvq::launch_decode_mfma(c, layer, q, dtype, softmax_scale, out, S,
+                                         static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return KVQ_OK;
 }

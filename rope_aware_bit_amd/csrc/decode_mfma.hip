@@ -1,0 +1,39 @@
+// Dispatch of the MFMA decode-attention kernels (kernel template in decode_mfma.h).
+#include "kvq_internal.h"
+
+namespace kvq {
+
+hipError_t launch_decode_mfma_g1(kvq_cache*, int, const void*, int, float, float*, int, hipStream_t);
+hipError_t launch_decode_mfma_g2(kvq_cache*, int, const void*, int, float, float*, int, hipStream_t);
+hipError_t launch_decode_mfma_g4(kvq_cache*, int, const void*, int, float, float*, int, hipStream_t);
+hipError_t launch_decode_mfma_g8(kvq_cache*, int, const void*, int, float, float*, int, hipStream_t);
+
+int auto_splits_mfma(const kvq_cache* c, int64_t len) {
+  // one 128-token tile per wave (4 waves per workgroup) when the context allows, and
+  // about two workgroups per compute unit over (splits x KV heads x sequences)
+  const int64_t n_tiles = (len + kVTile - 1) / kVTile;
+  const int64_t units = static_cast<int64_t>(c->cfg.batch) * c->cfg.n_kv_heads;
+  int64_t S = (n_tiles + 3) / 4;
+  const int64_t want = (512 + units - 1) / units;
+  if (S > want) S = want;
+  if (S > c->max_splits) S = c->max_splits;
+  if (S < 1) S = 1;
+  const int64_t tps = (n_tiles + S - 1) / S;
+  S = (n_tiles + tps - 1) / tps;
+  return static_cast<int>(S);
+}
+
+hipError_t launch_decode_mfma(kvq_cache* c, int layer, const void* q, int dtype, float scale,
+                              float* out, int n_splits, hipStream_t stream) {
+  const float kLog2e = 1.4426950408889634f;
+  const float sigma = (scale > 0.0f ? scale : 0.08838834764831845f) * kLog2e;
+  const int q_f32 = dtype == KVQ_F32;
+  switch (c->group) {
+    case 1: return launch_decode_mfma_g1(c, layer, q, q_f32, sigma, out, n_splits, stream);
+    case 2: return launch_decode_mfma_g2(c, layer, q, q_f32, sigma, out, n_splits, stream);
+    case 4: return launch_decode_mfma_g4(c, layer, q, q_f32, sigma, out, n_splits, stream);
+    default: return launch_decode_mfma_g8(c, layer, q, q_f32, sigma, out, n_splits, stream);
+  }
+}
+
+}  // namespace kvq

@@ -16,6 +16,19 @@ constexpr int kEnergyChunk = 256;    // tokens per sequential energy partial sum
 constexpr int kMaxGroup = 8;         // query heads per KV head supported
 constexpr int kNfBlock = 256;        // values per absmax block of the NF16 codec
 
+// Byte layout of the decode lookup tables that every decode workgroup copies into LDS.
+// Pair tables (widths 1..4) hold fp16x2 (CB[c0], CB[c1]) at index c0 | c1 << w; single
+// tables (widths 1..8) hold fp16 CB[c].  Each base is a multiple of its table's size, so
+// "(field << 2) | base" (pairs) and "(field << 1) | base" (singles) address an entry.
+__host__ __device__ constexpr int pair_table_base(int w) {
+  return w == 4 ? 0 : w == 3 ? 1024 : w == 2 ? 1280 : 1344;
+}
+__host__ __device__ constexpr int single_table_base(int w) {
+  return w == 8 ? 1536 : w == 7 ? 2048 : w == 6 ? 2304 : w == 5 ? 2432 : w == 4 ? 2496
+       : w == 3 ? 2528 : w == 2 ? 2544 : 2552;
+}
+constexpr int kLdsTableBytes = 2560;
+
 // Constant tables, built on the host at cache creation and copied to the device.
 struct Tables {
   uint16_t cb[kMaxBits + 1][256];    // fp16 bit patterns of CB_b[k], b = 1..8 (row 0 unused)
@@ -23,6 +36,9 @@ struct Tables {
   float delta[kMaxBits];             // greedy gain delta(b) = c(b) - c(b+1), fp32
   uint16_t nf_cb[16];                // fp16 levels of the 16-level Gaussian-quantile codebook
   float nf_bd[16];                   // 15 boundaries; [15] = +inf
+  // decode lookup tables in their LDS layout: [0] Lloyd-Max codebooks, [1] the same with
+  // the width-4 tables holding the 16-level Gaussian-quantile codebook
+  alignas(16) uint8_t lds_image[2][kLdsTableBytes];
 };
 
 // Per-(layer, KV head) plan written by the allocation kernel.
@@ -34,6 +50,7 @@ struct alignas(16) Plan {
   uint8_t fwidth[kHeadDim];          // width of field f
   uint8_t dwidth[kHeadDim];          // width of dim i
   int8_t bwidth[kBlocks];            // width of block j
+  uint32_t pdesc[kBlocks];           // stored block (pair) r in plan order: bit offset | width << 16
   int32_t n_fields;                  // stored fields (2 x blocks with width > 0)
   int32_t pad[3];
 };
@@ -63,7 +80,9 @@ struct kvq_cache {
   kvq::Tables host_tables;
   float* part_o;               // split partials [B][H][max_splits][G][128]
   float* part_ml;              // [B][H][max_splits][G][2]
-  unsigned* split_counters;    // [B][H] finished-split counters (zero between calls)
+  float* gpart_o;              // merged split groups [B][H][16][G][128]
+  float* gpart_ml;             // [B][H][16][G][2]
+  unsigned* split_counters;    // [B][H][17] finished-split / finished-group counters (zero between calls)
   int max_splits;
   double* energy_scratch;      // [H][n_chunks][64]
   int64_t energy_scratch_chunks;
@@ -79,9 +98,9 @@ hipError_t launch_alloc(kvq_cache* c, int layer, const void* keys, int dtype, in
                         const double* block_weight, hipStream_t stream);
 hipError_t launch_quantize(kvq_cache* c, int layer, const void* k, const void* v, int dtype,
                            int64_t n_new, hipStream_t stream);
-hipError_t launch_decode(kvq_cache* c, int layer, const void* q, int dtype, float scale,
-                         float* out, int n_splits, hipStream_t stream);
-int auto_splits(const kvq_cache* c, int64_t len);
+hipError_t launch_decode_mfma(kvq_cache* c, int layer, const void* q, int dtype, float scale,
+                              float* out, int n_splits, hipStream_t stream);
+int auto_splits_mfma(const kvq_cache* c, int64_t len);
 
 // Offsets of one layer's storage.
 inline uint32_t* layer_k_codes(kvq_cache* c, int layer) {

@@ -162,31 +162,34 @@ __global__ __launch_bounds__(128) void quantize_append(
   }
   __syncthreads();
 
-  // lane i assembles dim i's 128-token stream of this tile
+  // lane i assembles dim i's four 32-token segments of this tile; segment (dim, g) is stored
+  // at index ((dim / 16) * 4 + g) * 16 + dim % 16 (see the V tile layout in kvq.h)
   const int i = t;
   const int vb = NF ? 4 : v_bits;
-  const int v_words = 4 * vb;
   const int64_t lo_pos = L0 > tile * kVTile ? L0 - tile * kVTile : 0;
   const int64_t hi_pos = L0 + n_new - tile * kVTile < kVTile ? L0 + n_new - tile * kVTile : kVTile;
-  uint32_t* dst = vc + ((static_cast<int64_t>(b) * n_kv + h) * (cap / kVTile) + tile) * kVTile * v_words +
-                  static_cast<int64_t>(i) * v_words;
-  uint64_t acc = 0, msk = 0;
-  int nbits = 0, wo = 0;
-  for (int tau = 0; tau < kVTile; ++tau) {
-    const bool in = tau >= lo_pos && tau < hi_pos;
-    const uint64_t code = in ? vcode_s[i][tau] : 0;
-    const uint64_t m = in ? ((1ull << vb) - 1) : 0;
-    acc |= code << nbits;
-    msk |= m << nbits;
-    nbits += vb;
-    if (nbits >= 32) {
-      const uint32_t nw = static_cast<uint32_t>(acc), mw = static_cast<uint32_t>(msk);
-      if (mw == 0xFFFFFFFFu) dst[wo] = nw;
-      else if (mw != 0u) dst[wo] = (dst[wo] & ~mw) | (nw & mw);
-      ++wo;
-      acc >>= 32;
-      msk >>= 32;
-      nbits -= 32;
+  uint32_t* tile_dst = vc + ((static_cast<int64_t>(b) * n_kv + h) * (cap / kVTile) + tile) * kVTile * 4 * vb;
+  for (int g = 0; g < 4; ++g) {
+    uint32_t* dst = tile_dst + static_cast<int64_t>(((i / 16) * 4 + g) * 16 + i % 16) * vb;
+    uint64_t acc = 0, msk = 0;
+    int nbits = 0, wo = 0;
+    for (int e = 0; e < 32; ++e) {
+      const int tau = 32 * g + e;
+      const bool in = tau >= lo_pos && tau < hi_pos;
+      const uint64_t code = in ? vcode_s[i][tau] : 0;
+      const uint64_t m = in ? ((1ull << vb) - 1) : 0;
+      acc |= code << nbits;
+      msk |= m << nbits;
+      nbits += vb;
+      if (nbits >= 32) {
+        const uint32_t nw = static_cast<uint32_t>(acc), mw = static_cast<uint32_t>(msk);
+        if (mw == 0xFFFFFFFFu) dst[wo] = nw;
+        else if (mw != 0u) dst[wo] = (dst[wo] & ~mw) | (nw & mw);
+        ++wo;
+        acc >>= 32;
+        msk >>= 32;
+        nbits -= 32;
+      }
     }
   }
 }

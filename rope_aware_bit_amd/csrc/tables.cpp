@@ -183,6 +183,22 @@ void build_tables(Tables* t) {
   }
   for (int k = 0; k < 15; ++k) t->nf_bd[k] = static_cast<float>(0.5 * (lv[k] + lv[k + 1]));
   t->nf_bd[15] = inf;
+
+  for (int img = 0; img < 2; ++img) {
+    uint8_t* out = t->lds_image[img];
+    for (int w = 1; w <= kMaxBits; ++w) {
+      const uint16_t* cb = (img == 1 && w == 4) ? t->nf_cb : t->cb[w];
+      for (int c = 0; c < (1 << w); ++c)
+        std::memcpy(out + single_table_base(w) + 2 * c, &cb[c], 2);
+      if (w <= 4) {
+        for (int e = 0; e < (1 << (2 * w)); ++e) {
+          const uint32_t v = static_cast<uint32_t>(cb[e & ((1 << w) - 1)]) |
+                             (static_cast<uint32_t>(cb[e >> w]) << 16);
+          std::memcpy(out + pair_table_base(w) + 4 * e, &v, 4);
+        }
+      }
+    }
+  }
 }
 
 }  // namespace kvq

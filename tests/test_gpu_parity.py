@@ -92,7 +92,7 @@ def run_case(wname, T, k_bits, v_bits, codec="bgtq", pairing="half", batch=None,
     cap = info.capacity
     if check_codes:
         kw = cache.read(0, kvq.PART_K_CODES, np.uint32).reshape(B, H, cap, info.k_row_words)
-        vw = cache.read(0, kvq.PART_V_CODES, np.uint32).reshape(B, H, cap // 128, 128, info.v_dim_words)
+        vw = cache.read(0, kvq.PART_V_CODES, np.uint32).reshape(B, H, cap // 128, 512, info.v_dim_words // 4)
         kscale = cache.read(0, kvq.PART_K_SCALES, np.uint16)
         vscale = cache.read(0, kvq.PART_V_SCALES, np.uint16)
         if codec == "nf16":

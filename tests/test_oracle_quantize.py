@@ -166,13 +166,15 @@ def test_v_tile_layout():
         T = 300
         codes = rng.integers(0, 1 << bits, (T, 128)).astype(np.uint8)
         words = lay.pack_v_tiles(codes, bits)
-        assert words.shape == (3, 128, 4 * bits)
+        assert words.shape == (3, 512, bits)
         assert np.array_equal(lay.unpack_v_tiles(words, bits, T), codes)
-        # token tau of dim i in tile t sits at bit tau*bits of that dim's stream
-        t, i, tau = 1, 77, 45
-        stream = 0
-        for k, w in enumerate(words[t, i]):
-            stream |= int(w) << (32 * k)
-        assert (stream >> (tau * bits)) & ((1 << bits) - 1) == codes[t * 128 + tau, i]
+        # token 32g + e of dim d in tile t sits at bit e*bits of segment ((d//16)*4 + g)*16 + d%16
+        for (t, d, tok) in ((1, 77, 45), (0, 0, 0), (2, 127, 31), (0, 16, 100)):
+            g, e = divmod(tok, 32)
+            seg = ((d // 16) * 4 + g) * 16 + d % 16
+            stream = 0
+            for k, w in enumerate(words[t, seg]):
+                stream |= int(w) << (32 * k)
+            assert (stream >> (e * bits)) & ((1 << bits) - 1) == codes[t * 128 + tok, d]
         # padding tokens of the last tile are zero
         assert np.all(lay.unpack_v_tiles(words, bits, 384)[T:] == 0)
