@@ -39,31 +39,44 @@
 
 #include <hip/hip_fp16.h>
 
-#include <type_traits>
-#include <utility>
-
 #include "kvq_internal.h"
 
 namespace kvq {
 namespace mfma {
 
-typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kGroup = 16;        // splits merged per first-level merger
 constexpr int kMaxGroups = 16;    // so at most kGroup * kMaxGroups = 256 splits
+constexpr int kKS = 144;          // LDS row stride (words) of a staged K tile: 128 tokens + 16
+// LDS table region (bytes).  Pair tables hold fp16x2 (CB_w[c0], CB_w[c1]) at index c0 | c1 << w.
+// Widths 3 and 4 are replicated 32 times so that lane l reads copy l % 32 and random
+// lookups never collide in a bank: entry p of copy k sits at base + (p << 7) + 4 k.  Widths 5
+// and 6 are single copies (entry p at base + (p << 2)), built per workgroup when the plan
+// uses them.  The prebuilt image holds the pair tables of widths 1..4 and the single tables
+// of widths 1..8.  Every base is a multiple of its table's extent, so an entry address is
+// "(p << shift) | base".
+constexpr int kPair6Base = 0;          // 16 KB
+constexpr int kRep3Base = 16384;       // 8 KB
+constexpr int kPair5Base = 24576;      // 4 KB
+constexpr int kImageBase = 28672;      // 2.5 KB
+constexpr int kRep4Base = 32768;       // 32 KB
+constexpr int kTableRegion = 65536;
 
-// Calls f(std::integral_constant<int, I>) for I = 0 .. N-1, so that MFMA broadcast
-// selectors derived from I are compile-time constants.
-template <typename F, int... Is>
-__device__ inline void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
-  (f(std::integral_constant<int, Is>{}), ...);
-}
-template <int N, typename F>
-__device__ inline void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
+// Lookup parameters of a pair of width w: base (without the lane's copy offset) | replicated
+// << 16 | extract width << 24.  Widths 7 and 8 use two single lookups; their pair lookup is
+// kept inside the width-6 table and its result replaced.
+__device__ inline uint32_t pair_lookup_params(uint32_t w) {
+  uint32_t base, rep = 0u;
+  if (w == 4u) { base = kRep4Base; rep = 1u; }
+  else if (w == 3u) { base = kRep3Base; rep = 1u; }
+  else if (w == 5u) base = kPair5Base;
+  else if (w >= 6u) base = kPair6Base;
+  else base = kImageBase + static_cast<uint32_t>(pair_table_base(static_cast<int>(w)));
+  const uint32_t bw = w <= 6u ? 2u * w : 12u;
+  return base | (rep << 16) | (bw << 24);
 }
 
 __device__ inline float half_bits_to_float(uint16_t h) { return __half2float(__ushort_as_half(h)); }
@@ -78,29 +91,21 @@ __device__ inline uint32_t lds_u16(const char* base, uint32_t addr) {
 #define KVQ_DPP(v, ctrl) \
   __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, 0xF, 0xF, false))
 
-// Wave-wide max / sum: rotations within rows of 16 lanes, then the 4 row results
-// read out to scalars; the result is the same in every lane.
-__device__ inline float wave_max(float v) {
+// Max / sum over the 16 lanes of a row (lanes 16 r .. 16 r + 15); the result is in every
+// lane of the row.
+__device__ inline float row_max16(float v) {
   v = fmaxf(v, KVQ_DPP(v, 0x128));
   v = fmaxf(v, KVQ_DPP(v, 0x124));
   v = fmaxf(v, KVQ_DPP(v, 0x122));
   v = fmaxf(v, KVQ_DPP(v, 0x121));
-  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+  return v;
 }
-__device__ inline float wave_sum(float v) {
+__device__ inline float row_sum16(float v) {
   v += KVQ_DPP(v, 0x128);
   v += KVQ_DPP(v, 0x124);
   v += KVQ_DPP(v, 0x122);
   v += KVQ_DPP(v, 0x121);
-  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-  return (a + b) + (c + d);
+  return v;
 }
 
 // Orders a wave's LDS writes before its later LDS reads of other lanes' data (LDS
@@ -122,7 +127,7 @@ __device__ inline float ld_coh(const float* p) {
 
 // Count this workgroup in a merge counter after all of its partial stores have
 // completed; returns (in every thread) whether it was the last of `expected`.
-__device__ inline bool arrive(unsigned* counter, unsigned expected, bool* flag_s) {
+__device__ __attribute__((always_inline)) inline bool arrive(unsigned* counter, unsigned expected, bool* flag_s) {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_s_waitcnt(0);   // all outstanding memory operations of this wave
   __syncthreads();
@@ -135,50 +140,27 @@ __device__ inline bool arrive(unsigned* counter, unsigned expected, bool* flag_s
   return *flag_s;
 }
 
-// fp16 pairs (CB[c0], CB[c1]) of one K block for two tokens.  The block's 2w-bit field
-// starts at bit `off` of every row.  K rows of the 128-token tile are staged in LDS
-// word-major: kr[(d + 1) * 128 + tau] is word d of token tau's row, rows 0 and
-// k_words + 1 are zero.  The lane reads tokens `lane` and `lane + 64`.  off and w are
-// wave-uniform.
-__device__ inline void k_pair2(const uint32_t* kr, int lane, int off, int w, const char* tab,
-                               uint32_t& v0, uint32_t& v1) {
-  if (w <= 4) {
-    const int a = off + 30;  // field lands at bit 2 of the window
-    const uint32_t* p = kr + (a >> 5) * kVTile + lane;
-    const uint32_t x0 = __builtin_amdgcn_alignbit(p[kVTile], p[0], a & 31);
-    const uint32_t x1 = __builtin_amdgcn_alignbit(p[kVTile + 64], p[64], a & 31);
-    const uint32_t m = (((1u << (2 * w)) - 1u)) << 2;
-    const uint32_t pb = static_cast<uint32_t>(pair_table_base(w));
-    v0 = lds_u32(tab, (x0 & m) | pb);
-    v1 = lds_u32(tab, (x1 & m) | pb);
-  } else {
-    const int a = off + 31;  // first field at bit 1, second at bit 1 + w (2w <= 16 bits)
-    const uint32_t* p = kr + (a >> 5) * kVTile + lane;
-    const uint32_t x0 = __builtin_amdgcn_alignbit(p[kVTile], p[0], a & 31);
-    const uint32_t x1 = __builtin_amdgcn_alignbit(p[kVTile + 64], p[64], a & 31);
-    const uint32_t m = ((1u << w) - 1u) << 1;
-    const uint32_t sb = static_cast<uint32_t>(single_table_base(w));
-    v0 = lds_u16(tab, (x0 & m) | sb) | (lds_u16(tab, ((x0 >> w) & m) | sb) << 16);
-    v1 = lds_u16(tab, (x1 & m) | sb) | (lds_u16(tab, ((x1 >> w) & m) | sb) << 16);
-  }
-}
-
-// fp16 pair of V codes e, e+1 (e even) of a 32-code segment held in S[0..VB) (S[-1] and
-// S[VB] are zero words).
+// fp16 pair of V codes e, e+1 (e even) of a 32-code segment held in S[0..VB) (S[VB] is a
+// zero word).  `tab` is the table region, `lb` the lane's replica offset (lane % 32) * 4.
 template <int VB>
-__device__ inline uint32_t v_pair(const uint32_t* S, int e, const char* tab) {
+__device__ inline uint32_t v_pair(const uint32_t* S, int e, const char* tab, uint32_t lb) {
   if constexpr (VB <= 4) {
-    constexpr uint32_t mask = ((1u << (2 * VB)) - 1u) << 2;
-    const int a = e * VB + 30;
-    const uint32_t x = __builtin_amdgcn_alignbit(S[(a >> 5)], S[(a >> 5) - 1], a & 31);
-    return lds_u32(tab, (x & mask) | static_cast<uint32_t>(pair_table_base(VB)));
+    const int off = e * VB, w0 = off >> 5, sh = off & 31;
+    uint32_t code;
+    if (sh + 2 * VB <= 32) code = __builtin_amdgcn_ubfe(S[w0], sh, 2 * VB);
+    else code = __builtin_amdgcn_ubfe(__builtin_amdgcn_alignbit(S[w0 + 1], S[w0], sh), 0, 2 * VB);
+    if constexpr (VB >= 3) {
+      return lds_u32(tab, (code << 7) | lb | (VB == 4 ? kRep4Base : kRep3Base));
+    } else {
+      return lds_u32(tab + kImageBase, (code << 2) | static_cast<uint32_t>(pair_table_base(VB)));
+    }
   } else {
     constexpr uint32_t mask = ((1u << VB) - 1u) << 1;
     const int a0 = e * VB + 31, a1 = (e + 1) * VB + 31;
     const uint32_t x0 = __builtin_amdgcn_alignbit(S[(a0 >> 5)], S[(a0 >> 5) - 1], a0 & 31);
     const uint32_t x1 = __builtin_amdgcn_alignbit(S[(a1 >> 5)], S[(a1 >> 5) - 1], a1 & 31);
     constexpr uint32_t sb = static_cast<uint32_t>(single_table_base(VB));
-    return lds_u16(tab, (x0 & mask) | sb) | (lds_u16(tab, (x1 & mask) | sb) << 16);
+    return lds_u16(tab + kImageBase, (x0 & mask) | sb) | (lds_u16(tab + kImageBase, (x1 & mask) | sb) << 16);
   }
 }
 
@@ -189,7 +171,7 @@ __device__ inline uint32_t v_pair(const uint32_t* S, int e, const char* tab) {
 // `final_out`, o / l to dst_o[g*128 + i].  All loads are issued before any result is
 // needed, so the merge costs one round of memory latency.
 template <int G>
-__device__ inline void merge_level(const float* __restrict__ src_o, const float* __restrict__ src_ml,
+__device__ __attribute__((always_inline)) inline void merge_level(const float* __restrict__ src_o, const float* __restrict__ src_ml,
                                    int count, float* mw, int tid, float* __restrict__ dst_o,
                                    float* __restrict__ dst_ml, bool final_out) {
   constexpr int NOUT = G * kHeadDim;
@@ -253,44 +235,64 @@ __device__ inline void merge_level(const float* __restrict__ src_o, const float*
 }
 
 template <int G, int VB, bool NF>
-__global__ __launch_bounds__(256) void decode_mfma(
+__global__ __launch_bounds__(256, 1) void decode_mfma(
     const void* __restrict__ qv, int q_f32, float sigma, int64_t len, int n_kv, int64_t cap,
     int tiles_per_split, const Plan* __restrict__ plans, const Tables* __restrict__ tabg,
     const uint32_t* __restrict__ kc, const uint32_t* __restrict__ vc, const uint16_t* __restrict__ ks,
     const uint16_t* __restrict__ vs, int k_words, int n_nf, int n_splits, float* __restrict__ part_o,
     float* __restrict__ part_ml, float* __restrict__ gpart_o, float* __restrict__ gpart_ml,
     unsigned* __restrict__ counters, float* __restrict__ out) {
-  constexpr int HP = 2 * G;                     // query-head parts (hi, lo)
-  constexpr int HG = (HP + 3) / 4;              // 4-row groups of parts for the 4x4x4 MFMA
-  constexpr int NA = (32 * HG + 15) / 16;       // A-operand registers (16 broadcast blocks each)
-  constexpr int PCOLS = HP;                     // P columns: hi of heads 0..G-1, then lo
-  constexpr int KWV = 4 * VB;                   // words per dim per V tile
+  constexpr int PCOLS = 2 * G;                        // P columns: hi of heads 0..G-1, then lo
+  constexpr int KWV = 4 * VB;                         // words per dim per V tile
+  constexpr int QPT = (G * kHeadDim + 255) / 256;     // query values per thread at set-up
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
+  const int n = lane & 15, g = lane >> 4;             // MFMA column and row group of this lane
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int n_q = n_kv * G;
   const int64_t bh = static_cast<int64_t>(b) * n_kv + h;
 
-  __shared__ __attribute__((aligned(16))) char tab_s[kLdsTableBytes];
+  __shared__ __attribute__((aligned(16))) char tab_s[kTableRegion];
   __shared__ __attribute__((aligned(16))) _Float16 p_s[kWaves][PCOLS][kVTile];
-  __shared__ float qs_s[G][kHeadDim];
+  __shared__ __attribute__((aligned(16))) _Float16 a_s[4][16][32];
   __shared__ uint8_t fdim_s[kHeadDim];
-  __shared__ uint32_t pd_s[kBlocks];
+  __shared__ __attribute__((aligned(16))) uint32_t pd_s[kBlocks];
+  __shared__ __attribute__((aligned(16))) uint32_t px_s[kBlocks];
   __shared__ float comb_m[kWaves][G], comb_l[kWaves][G];
+  __shared__ float alpha_s[kWaves][G];
   __shared__ bool flag_s;
-  extern __shared__ __attribute__((aligned(16))) uint32_t kr_dyn[];   // [kWaves][k_words + 2][128]
-  uint32_t* kr = kr_dyn + wave * (k_words + 2) * kVTile;
+  extern __shared__ __attribute__((aligned(16))) uint32_t kr_dyn[];   // [kWaves][k_words + 1][kKS]
+  uint32_t* kr = kr_dyn + wave * (k_words + 1) * kKS;
+  float (*qs_s)[kHeadDim] = reinterpret_cast<float (*)[kHeadDim]>(kr_dyn);   // set-up only
 
   const int64_t n_tiles = (len + kVTile - 1) / kVTile;
   const int64_t t_begin = static_cast<int64_t>(s) * tiles_per_split;
   const int64_t t_end = t_begin + tiles_per_split < n_tiles ? t_begin + tiles_per_split : n_tiles;
   const Plan* P = plans + h;
 
-  // ---- per-tile loads (issued for the first tile before the setup work) ----
+  // ---- set-up loads first (small and shared by every workgroup), then the first tile's ----
+  uint4 timg = make_uint4(0u, 0u, 0u, 0u);
+  if (tid < kLdsTableBytes / 16) timg = reinterpret_cast<const uint4*>(tabg->lds_image[NF ? 1 : 0])[tid];
+  float qr[QPT], gr[QPT];
+#pragma unroll
+  for (int j = 0; j < QPT; ++j) {
+    const int k = tid + 256 * j;
+    qr[j] = gr[j] = 0.0f;
+    if (k < G * kHeadDim) {
+      const int64_t qi = (static_cast<int64_t>(b) * n_q + h * G) * kHeadDim + k;
+      qr[j] = q_f32 ? static_cast<const float*>(qv)[qi] : __half2float(static_cast<const __half*>(qv)[qi]);
+      gr[j] = P->g[k % kHeadDim];
+    }
+  }
+  const uint32_t fd_r = tid < kHeadDim ? P->fdim[tid] : 0u;
+  const uint32_t pd_r = tid < kBlocks ? P->pdesc[tid] : 0u;
+  const int n_pairs = __builtin_amdgcn_readfirstlane(P->n_fields) >> 1;
+
+  // K rows of tokens lane and lane + 64 (first 16 words), scales of tokens 16 tg + n, V segments
   uint32_t vseg[8][VB + 2];
   uint4 ka[4], kb2[4];
-  float sk0 = 0.f, sk1 = 0.f, sv0 = 0.f, sv1 = 0.f;
+  float skr[8], svr[8];
   auto load_k = [&](int64_t tile) {
     const int64_t tok0 = tile * kVTile;
     const uint4* krow0 = reinterpret_cast<const uint4*>(kc + (bh * cap + tok0 + lane) * k_words);
@@ -304,17 +306,16 @@ __global__ __launch_bounds__(256) void decode_mfma(
     }
   };
   auto load_scales = [&](int64_t tile) {
-    const int64_t t0i = tile * kVTile + lane, t1i = t0i + 64;
-    if (NF) {
-      sk0 = half_bits_to_float(ks[(static_cast<int64_t>(b) * cap + t0i) * n_nf + h / 2]);
-      sk1 = half_bits_to_float(ks[(static_cast<int64_t>(b) * cap + t1i) * n_nf + h / 2]);
-      sv0 = half_bits_to_float(vs[(static_cast<int64_t>(b) * cap + t0i) * n_nf + h / 2]);
-      sv1 = half_bits_to_float(vs[(static_cast<int64_t>(b) * cap + t1i) * n_nf + h / 2]);
-    } else {
-      sk0 = half_bits_to_float(ks[bh * cap + t0i]);
-      sk1 = half_bits_to_float(ks[bh * cap + t1i]);
-      sv0 = half_bits_to_float(vs[bh * cap + t0i]);
-      sv1 = half_bits_to_float(vs[bh * cap + t1i]);
+#pragma unroll
+    for (int tg = 0; tg < 8; ++tg) {
+      const int64_t t = tile * kVTile + 16 * tg + n;
+      if (NF) {
+        skr[tg] = half_bits_to_float(ks[(static_cast<int64_t>(b) * cap + t) * n_nf + h / 2]);
+        svr[tg] = half_bits_to_float(vs[(static_cast<int64_t>(b) * cap + t) * n_nf + h / 2]);
+      } else {
+        skr[tg] = half_bits_to_float(ks[bh * cap + t]);
+        svr[tg] = half_bits_to_float(vs[bh * cap + t]);
+      }
     }
   };
   auto load_v = [&](int64_t tile) {
@@ -333,54 +334,80 @@ __global__ __launch_bounds__(256) void decode_mfma(
     load_v(t_begin + wave);
   }
 
-  // ---- setup: decode tables, scaled query, field dims, pair descriptors into LDS ----
-  {
-    const uint4* img = reinterpret_cast<const uint4*>(tabg->lds_image[NF ? 1 : 0]);
-    if (tid < kLdsTableBytes / 16) reinterpret_cast<uint4*>(tab_s)[tid] = img[tid];
+  // ---- set-up: tables, scaled query, field dims and pair descriptors into LDS ----
+  if (tid < kLdsTableBytes / 16) reinterpret_cast<uint4*>(tab_s + kImageBase)[tid] = timg;
+#pragma unroll
+  for (int j = 0; j < QPT; ++j) {
+    const int k = tid + 256 * j;
+    if (k < G * kHeadDim) qs_s[k / kHeadDim][k % kHeadDim] = qr[j] * gr[j] * sigma;
   }
-  for (int k = tid; k < G * kHeadDim; k += blockDim.x) {
-    const int hd = k / kHeadDim, i = k % kHeadDim;
-    const int64_t qi = (static_cast<int64_t>(b) * n_q + h * G + hd) * kHeadDim + i;
-    const float qraw = q_f32 ? static_cast<const float*>(qv)[qi]
-                             : __half2float(static_cast<const __half*>(qv)[qi]);
-    qs_s[hd][i] = qraw * P->g[i] * sigma;
+  if (tid < kHeadDim) fdim_s[tid] = static_cast<uint8_t>(fd_r);
+  if (tid < kBlocks) {
+    pd_s[tid] = pd_r;
+    px_s[tid] = pair_lookup_params(pd_r >> 16);
   }
-  const int n_pairs = __builtin_amdgcn_readfirstlane(P->n_fields) >> 1;
-  if (tid < kHeadDim) fdim_s[tid] = P->fdim[tid];
-  // blocks past the stored ones get a harmless width-1 descriptor (their query part is zero)
-  if (tid < kBlocks) pd_s[tid] = tid < n_pairs ? P->pdesc[tid] : (1u << 16);
-  kr[lane] = kr[64 + lane] = 0u;
-  kr[(k_words + 1) * kVTile + lane] = kr[(k_words + 1) * kVTile + 64 + lane] = 0u;
   __syncthreads();
-
-  // ---- A operands: q' split into hi/lo fp16, laid out for A-broadcast ----
-  h4 areg[NA];
+  // query operand of the key product: a_s[c][m][k] = hi (m even) or lo (m odd) fp16 part of
+  // q'[m / 2][dim of field 32 c + k]; rows of heads >= G and fields past the stored ones are 0.
+  // Thread t fills field t % 128 for heads t / 128, t / 128 + 2, ...
   {
-    const int blk = lane >> 2, i = lane & 3;
+    const int f = tid & 127, c = f >> 5, k = f & 31;
+    const bool live = f < 2 * n_pairs;
+    const int dim = fdim_s[f];
 #pragma unroll
-    for (int a = 0; a < NA; ++a) {
-      const int mi = a * 16 + blk;
-      const int st = mi / HG, g = mi % HG;
-      const int hp = 4 * g + i;
-      const int head = hp >> 1, part = hp & 1;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int r = 2 * st + (k >> 1);
-        float qq = 0.0f;
-        if (st < 32 && head < G && r < n_pairs) qq = qs_s[head][fdim_s[2 * r + (k & 1)]];
-        const _Float16 hi = static_cast<_Float16>(qq);
-        areg[a][k] = part ? static_cast<_Float16>(qq - static_cast<float>(hi)) : hi;
-      }
+    for (int j = 0; j < 4; ++j) {
+      const int hh = 2 * j + (tid >> 7);
+      const float qq = (hh < G && live) ? qs_s[hh < G ? hh : 0][dim] : 0.0f;
+      const _Float16 hi = static_cast<_Float16>(qq);
+      a_s[c][2 * hh][k] = hi;
+      a_s[c][2 * hh + 1][k] = static_cast<_Float16>(qq - static_cast<float>(hi));
     }
   }
-
-  // ---- per-wave state ----
-  float m_run[G], l_lane[G];
+  // pair tables of widths 5 and 6 when the plan stores such blocks: entry (c1 << w) | c0 holds
+  // (CB_w[c0], CB_w[c1]); thread t fills four consecutive c0 for one c1
+  const uint64_t uses5 = __ballot((pd_s[lane] >> 16) == 5u), uses6 = __ballot((pd_s[lane] >> 16) == 6u);
+  const uint64_t uses78 = __ballot((pd_s[lane] >> 16) >= 7u);
+  if (uses6) {
+    const uint16_t* cb = reinterpret_cast<const uint16_t*>(tab_s + kImageBase + single_table_base(6));
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m_run[g] = -INFINITY;
-    l_lane[g] = 0.0f;
+    for (int j = 0; j < 4; ++j) {
+      const int e = 4 * (tid + 256 * j);   // 4096 entries
+      const uint32_t hi = static_cast<uint32_t>(cb[e >> 6]) << 16;
+      const uint2 lo = *reinterpret_cast<const uint2*>(cb + (e & 63));
+      const uint4 v = make_uint4((lo.x & 0xFFFFu) | hi, (lo.x >> 16) | hi, (lo.y & 0xFFFFu) | hi, (lo.y >> 16) | hi);
+      *reinterpret_cast<uint4*>(tab_s + kPair6Base + 4 * e) = v;
+    }
   }
+  if (uses5) {
+    const uint16_t* cb = reinterpret_cast<const uint16_t*>(tab_s + kImageBase + single_table_base(5));
+    const int e = 4 * tid;   // 1024 entries
+    const uint32_t hi = static_cast<uint32_t>(cb[e >> 5]) << 16;
+    const uint2 lo = *reinterpret_cast<const uint2*>(cb + (e & 31));
+    const uint4 v = make_uint4((lo.x & 0xFFFFu) | hi, (lo.x >> 16) | hi, (lo.y & 0xFFFFu) | hi, (lo.y >> 16) | hi);
+    *reinterpret_cast<uint4*>(tab_s + kPair5Base + 4 * e) = v;
+  }
+  // 32-fold replicas of the width-3 and width-4 pair tables: thread t writes copy t % 32 of
+  // entries t / 32, t / 32 + 8, ...
+  {
+    const int copy = tid & 31, eg = tid >> 5;
+    const char* img = tab_s + kImageBase;
+#pragma unroll 4
+    for (int e = eg; e < 256; e += 8)
+      *reinterpret_cast<uint32_t*>(tab_s + kRep4Base + (e << 7) + 4 * copy) = lds_u32(img, pair_table_base(4) + 4 * e);
+#pragma unroll
+    for (int e = eg; e < 64; e += 8)
+      *reinterpret_cast<uint32_t*>(tab_s + kRep3Base + (e << 7) + 4 * copy) = lds_u32(img, pair_table_base(3) + 4 * e);
+  }
+  const int n_chunks = (n_pairs + 15) >> 4;
+  const uint32_t lb = (lane & 31u) << 2;   // this lane's replica offset
+  __syncthreads();
+  // zero pad row after the staged K words (the area held the scaled query during set-up)
+  kr[k_words * kKS + lane] = kr[k_words * kKS + 64 + lane] = 0u;
+
+  // ---- per-wave state: lane (n, g) keeps heads 2g, 2g + 1 ----
+  const int h0 = 2 * g, h1 = 2 * g + 1;
+  const bool vh0 = h0 < G, vh1 = h1 < G;
+  float m0 = -INFINITY, m1 = -INFINITY, l0 = 0.0f, l1 = 0.0f;
   f4 oacc[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) oacc[dt] = f4{0.f, 0.f, 0.f, 0.f};
@@ -388,113 +415,175 @@ __global__ __launch_bounds__(256) void decode_mfma(
   for (int64_t tile = t_begin + wave; tile < t_end; tile += kWaves) {
     const int64_t tok0 = tile * kVTile;
     const int64_t next = tile + kWaves;
-    const bool ok0 = tok0 + lane < len, ok1 = tok0 + 64 + lane < len;
-    // positions past the sequence end get weight 0 below; their stored scales are not used
-    const float tk0 = sk0, tk1 = sk1, tv0 = ok0 ? sv0 : 0.f, tv1 = ok1 ? sv1 : 0.f;
-    // -- stage the K rows in LDS word-major, then start the next tile's K rows and scales --
+    // -- stage the K rows in LDS word-major (kr[d * kKS + tau] = word d of token tau) --
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       if (4 * k < k_words) {
-        uint32_t* dst = kr + (4 * k + 1) * kVTile + lane;
-        dst[0] = ka[k].x; dst[kVTile] = ka[k].y; dst[2 * kVTile] = ka[k].z; dst[3 * kVTile] = ka[k].w;
-        dst[64] = kb2[k].x; dst[kVTile + 64] = kb2[k].y; dst[2 * kVTile + 64] = kb2[k].z;
-        dst[3 * kVTile + 64] = kb2[k].w;
+        uint32_t* dst = kr + 4 * k * kKS + lane;
+        dst[0] = ka[k].x; dst[kKS] = ka[k].y; dst[2 * kKS] = ka[k].z; dst[3 * kKS] = ka[k].w;
+        dst[64] = kb2[k].x; dst[kKS + 64] = kb2[k].y; dst[2 * kKS + 64] = kb2[k].z; dst[3 * kKS + 64] = kb2[k].w;
       }
     }
     for (int k = 4; 4 * k < k_words; ++k) {   // rows longer than 16 words (more than 4 bits)
       const uint4* krow0 = reinterpret_cast<const uint4*>(kc + (bh * cap + tok0 + lane) * k_words);
       const uint4* krow1 = reinterpret_cast<const uint4*>(kc + (bh * cap + tok0 + 64 + lane) * k_words);
-      const uint4 a = krow0[k], c = krow1[k];
-      uint32_t* dst = kr + (4 * k + 1) * kVTile + lane;
-      dst[0] = a.x; dst[kVTile] = a.y; dst[2 * kVTile] = a.z; dst[3 * kVTile] = a.w;
-      dst[64] = c.x; dst[kVTile + 64] = c.y; dst[2 * kVTile + 64] = c.z; dst[3 * kVTile + 64] = c.w;
-    }
-    if (next < t_end) {
-      load_k(next);
-      load_scales(next);
-    }
-    // -- keys: logits of the two 64-token halves --
-    f4 acc0[HG], acc1[HG];
-#pragma unroll
-    for (int g = 0; g < HG; ++g) acc0[g] = acc1[g] = f4{0.f, 0.f, 0.f, 0.f};
-    static_for<32>([&](auto stc) {
-      constexpr int st = decltype(stc)::value;
-      // pair descriptors (bit offset | width << 16) are wave-uniform
-      const uint32_t d0 = __builtin_amdgcn_readfirstlane(pd_s[2 * st]);
-      const uint32_t d1 = __builtin_amdgcn_readfirstlane(pd_s[2 * st + 1]);
-      uint32_t b00, b10, b01, b11;
-      k_pair2(kr, lane, static_cast<int>(d0 & 0xFFFFu), static_cast<int>(d0 >> 16), tab_s, b00, b10);
-      k_pair2(kr, lane, static_cast<int>(d1 & 0xFFFFu), static_cast<int>(d1 >> 16), tab_s, b01, b11);
-      h4 bv0, bv1;
-      const uint32_t u0[2] = {b00, b01}, u1[2] = {b10, b11};
-      __builtin_memcpy(&bv0, u0, 8);
-      __builtin_memcpy(&bv1, u1, 8);
-      static_for<HG>([&](auto gc) {
-        constexpr int g = decltype(gc)::value;
-        constexpr int mi = st * HG + g;
-        acc0[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(areg[mi / 16], bv0, acc0[g], 4, mi % 16, 0);
-        acc1[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(areg[mi / 16], bv1, acc1[g], 4, mi % 16, 0);
-      });
-    });
-    float lg0[G], lg1[G];
-#pragma unroll
-    for (int hd = 0; hd < G; ++hd) {
-      const int hp = 2 * hd;
-      lg0[hd] = ok0 ? (acc0[hp / 4][hp % 4] + acc0[hp / 4][hp % 4 + 1]) * tk0 : -INFINITY;
-      lg1[hd] = ok1 ? (acc1[hp / 4][hp % 4] + acc1[hp / 4][hp % 4 + 1]) * tk1 : -INFINITY;
-    }
-    // -- online softmax over the 128-token tile --
-    bool rescale = false;
-    float al_h[G];
-#pragma unroll
-    for (int hd = 0; hd < G; ++hd) {
-      const float mt = wave_max(fmaxf(lg0[hd], lg1[hd]));
-      const float mn = fmaxf(m_run[hd], mt);
-      const float al = exp2f(m_run[hd] - mn);
-      rescale |= al != 1.0f;
-      al_h[hd] = al;
-      m_run[hd] = mn;
-      const float p0 = exp2f(lg0[hd] - mn), p1 = exp2f(lg1[hd] - mn);
-      l_lane[hd] = l_lane[hd] * al + p0 + p1;
-      const float q0 = p0 * tv0, q1 = p1 * tv1;
-      const _Float16 q0h = static_cast<_Float16>(q0), q1h = static_cast<_Float16>(q1);
-      p_s[wave][hd][lane] = q0h;
-      p_s[wave][hd][64 + lane] = q1h;
-      p_s[wave][G + hd][lane] = static_cast<_Float16>(q0 - static_cast<float>(q0h));
-      p_s[wave][G + hd][64 + lane] = static_cast<_Float16>(q1 - static_cast<float>(q1h));
+      const uint4 x0 = krow0[k], x1 = krow1[k];
+      uint32_t* dst = kr + 4 * k * kKS + lane;
+      dst[0] = x0.x; dst[kKS] = x0.y; dst[2 * kKS] = x0.z; dst[3 * kKS] = x0.w;
+      dst[64] = x1.x; dst[kKS + 64] = x1.y; dst[2 * kKS + 64] = x1.z; dst[3 * kKS + 64] = x1.w;
     }
     wave_sync();
-    if (rescale) {
-      // output column n = lane % 16 belongs to head n % G (columns >= 2G are unused)
-      const int col = lane & 15;
-      float al = 1.0f;
+    if (next < t_end) load_k(next);
+
+    // -- keys: D[part][token] = sum over fields of q'[part][field] * CB[code[token][field]],
+    //    one 16x16x32 product per (chunk of 16 pairs, group of 16 tokens) --
+    f4 dacc[8];
 #pragma unroll
-      for (int hd = 0; hd < G; ++hd)
-        if (col < PCOLS && col % G == hd) al = al_h[hd];
+    for (int tg = 0; tg < 8; ++tg) dacc[tg] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < n_chunks; ++c) {
+      {
+        const h8 aq = *reinterpret_cast<const h8*>(&a_s[c][n][8 * g]);
+        const int grp = 4 * c + g;   // this lane's pairs: 4 grp .. 4 grp + 3
+        // pairs 0, 1 come from a 32-bit window at pair 0, pairs 2, 3 from one at pair 2 (two
+        // pairs of at most 8 bits each fit); widths <= 6 use one pair lookup, 7 and 8 two
+        // single lookups
+        const uint4 dd = *reinterpret_cast<const uint4*>(&pd_s[4 * grp]);
+        const uint32_t d4[4] = {dd.x, dd.y, dd.z, dd.w};
+        const uint4 xx = *reinterpret_cast<const uint4*>(&px_s[4 * grp]);
+        const uint32_t x4[4] = {xx.x, xx.y, xx.z, xx.w};
+        uint32_t wp[4], bw[4], pb[4], ps[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          wp[p] = d4[p] >> 16;
+          bw[p] = x4[p] >> 24;
+          const uint32_t rep = (x4[p] >> 16) & 1u;
+          pb[p] = (x4[p] & 0xFFFFu) | (rep ? lb : 0u);
+          ps[p] = rep ? 7u : 2u;
+        }
+        const uint32_t offA = d4[0] & 0xFFFFu, offB = d4[2] & 0xFFFFu;
+        const uint32_t shA = offA & 31u, shB = offB & 31u;
+        const uint32_t rel1 = 2u * wp[0], rel3 = 2u * wp[2];
+        const uint32_t* kA = kr + (offA >> 5) * kKS + n;
+        const uint32_t* kB = kr + (offB >> 5) * kKS + n;
+        const bool has78 = ((uses78 >> (16 * c)) & 0xFFFFull) != 0ull;
+        // all window reads first, then extraction and lookups per token group, then the
+        // products: LDS returns in order, so each step waits only for what it uses
+        uint32_t la[8], ha[8], lb[8], hb[8], u[8][4];
+#pragma unroll
+        for (int tg = 0; tg < 8; ++tg) {
+          la[tg] = kA[16 * tg];
+          ha[tg] = kA[16 * tg + kKS];
+          lb[tg] = kB[16 * tg];
+          hb[tg] = kB[16 * tg + kKS];
+        }
+        uint32_t xa[8], xb[8];
+#pragma unroll
+        for (int tg = 0; tg < 8; ++tg) {
+          xa[tg] = __builtin_amdgcn_alignbit(ha[tg], la[tg], shA);
+          xb[tg] = __builtin_amdgcn_alignbit(hb[tg], lb[tg], shB);
+          u[tg][0] = lds_u32(tab_s, (__builtin_amdgcn_ubfe(xa[tg], 0u, bw[0]) << ps[0]) | pb[0]);
+          u[tg][1] = lds_u32(tab_s, (__builtin_amdgcn_ubfe(xa[tg], rel1, bw[1]) << ps[1]) | pb[1]);
+          u[tg][2] = lds_u32(tab_s, (__builtin_amdgcn_ubfe(xb[tg], 0u, bw[2]) << ps[2]) | pb[2]);
+          u[tg][3] = lds_u32(tab_s, (__builtin_amdgcn_ubfe(xb[tg], rel3, bw[3]) << ps[3]) | pb[3]);
+        }
+        if (has78) {
+          // blocks of 7 or 8 bits: two single lookups (lanes whose pair is narrower skip)
+          const char* tabi = tab_s + kImageBase;
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            if (wp[p] >= 7u) {
+              const uint32_t sb = static_cast<uint32_t>(kLdsTableBytes) - (4u << wp[p]);
+              const uint32_t rel = (p & 1) ? (p == 1 ? rel1 : rel3) : 0u;
+#pragma unroll
+              for (int tg = 0; tg < 8; ++tg) {
+                const uint32_t x = (p < 2) ? xa[tg] : xb[tg];
+                const uint32_t f0 = __builtin_amdgcn_ubfe(x, rel, wp[p]);
+                const uint32_t f1 = __builtin_amdgcn_ubfe(x, rel + wp[p], wp[p]);
+                u[tg][p] = lds_u16(tabi, (f0 << 1) | sb) | (lds_u16(tabi, (f1 << 1) | sb) << 16);
+              }
+            }
+          }
+        }
+#pragma unroll
+        for (int tg = 0; tg < 8; ++tg) {
+          h8 bk;
+          __builtin_memcpy(&bk, u[tg], 16);
+          dacc[tg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq, bk, dacc[tg], 0, 0, 0);
+        }
+      }
+    }
+
+    // -- online softmax: lane (n, g) holds heads 2g and 2g + 1 of tokens 16 tg + n --
+    float L0[8], L1[8];
+    float mt0 = -INFINITY, mt1 = -INFINITY;
+#pragma unroll
+    for (int tg = 0; tg < 8; ++tg) {
+      const bool ok = tok0 + 16 * tg + n < len;
+      L0[tg] = ok ? (dacc[tg][0] + dacc[tg][1]) * skr[tg] : -INFINITY;
+      L1[tg] = ok ? (dacc[tg][2] + dacc[tg][3]) * skr[tg] : -INFINITY;
+      mt0 = fmaxf(mt0, L0[tg]);
+      mt1 = fmaxf(mt1, L1[tg]);
+    }
+    mt0 = row_max16(mt0);
+    mt1 = row_max16(mt1);
+    const float mn0 = fmaxf(m0, mt0), mn1 = fmaxf(m1, mt1);
+    // hardware 2^x: arguments are <= 0 and results below the fp32 normal range only
+    // ever meet sums >= 1, so flushing them changes nothing that is kept
+    const float al0 = __builtin_amdgcn_exp2f(m0 - mn0), al1 = __builtin_amdgcn_exp2f(m1 - mn1);
+    m0 = mn0;
+    m1 = mn1;
+    l0 *= al0;
+    l1 *= al1;
+#pragma unroll
+    for (int tg = 0; tg < 8; ++tg) {
+      const bool ok = tok0 + 16 * tg + n < len;
+      const float sv = ok ? svr[tg] : 0.0f;   // stored scales past the sequence end are not used
+      const float p0 = __builtin_amdgcn_exp2f(L0[tg] - mn0), p1 = __builtin_amdgcn_exp2f(L1[tg] - mn1);
+      l0 += p0;
+      l1 += p1;
+      const float q0 = p0 * sv, q1 = p1 * sv;
+      const _Float16 q0h = static_cast<_Float16>(q0), q1h = static_cast<_Float16>(q1);
+      const int t = 16 * tg + n;
+      if (vh0) {
+        p_s[wave][h0][t] = q0h;
+        p_s[wave][G + h0][t] = static_cast<_Float16>(q0 - static_cast<float>(q0h));
+      }
+      if (vh1) {
+        p_s[wave][h1][t] = q1h;
+        p_s[wave][G + h1][t] = static_cast<_Float16>(q1 - static_cast<float>(q1h));
+      }
+    }
+    if (n == 0) {
+      if (vh0) alpha_s[wave][h0] = al0;
+      if (vh1) alpha_s[wave][h1] = al1;
+    }
+    const bool rescale = __ballot((vh0 && al0 != 1.0f) || (vh1 && al1 != 1.0f)) != 0ull;
+    if (next < t_end) load_scales(next);
+    wave_sync();
+    if (rescale) {
+      // output column n belongs to head n % G (columns >= 2G are unused)
+      const float al = n < PCOLS ? alpha_s[wave][n % G] : 1.0f;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) oacc[dt] *= al;
     }
     // -- values: O^T[dim][col] += V^T[dim][tok] P^T[tok][col] over 4 chunks of 32 tokens --
-    {
-      const int col = lane & 15, grp = lane >> 4;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        h8 bp;
-        if (col < PCOLS) {
-          bp = *reinterpret_cast<const h8*>(&p_s[wave][col][32 * grp + 8 * c]);
-        } else {
+    for (int c = 0; c < 4; ++c) {
+      h8 bp;
+      if (n < PCOLS) {
+        bp = *reinterpret_cast<const h8*>(&p_s[wave][n][32 * g + 8 * c]);
+      } else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) bp[e] = static_cast<_Float16>(0.0f);
-        }
+        for (int e = 0; e < 8; ++e) bp[e] = static_cast<_Float16>(0.0f);
+      }
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-          uint32_t pr[4];
+      for (int dt = 0; dt < 8; ++dt) {
+        uint32_t pr[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) pr[e] = v_pair<VB>(&vseg[dt][1], 8 * c + 2 * e, tab_s);
-          h8 av;
-          __builtin_memcpy(&av, pr, 16);
-          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bp, oacc[dt], 0, 0, 0);
-        }
+        for (int e = 0; e < 4; ++e) pr[e] = v_pair<VB>(&vseg[dt][1], 8 * c + 2 * e, tab_s, lb);
+        h8 av;
+        __builtin_memcpy(&av, pr, 16);
+        oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bp, oacc[dt], 0, 0, 0);
       }
     }
     wave_sync();
@@ -502,29 +591,28 @@ __global__ __launch_bounds__(256) void decode_mfma(
   }
 
   // ---- merge the 4 waves of this workgroup ----
-  float lw[G];
-#pragma unroll
-  for (int hd = 0; hd < G; ++hd) lw[hd] = wave_sum(l_lane[hd]);
-  if (lane == 0) {
-#pragma unroll
-    for (int hd = 0; hd < G; ++hd) {
-      comb_m[wave][hd] = m_run[hd];
-      comb_l[wave][hd] = lw[hd];
+  l0 = row_sum16(l0);
+  l1 = row_sum16(l1);
+  if (n == 0) {
+    if (vh0) {
+      comb_m[wave][h0] = m0;
+      comb_l[wave][h0] = l0;
+    }
+    if (vh1) {
+      comb_m[wave][h1] = m1;
+      comb_l[wave][h1] = l1;
     }
   }
-  // O^T layout: lane holds rows 4*(lane/16)+r of dim-slice dt for column lane%16;
-  // add the lo column (col + G) into the hi column (col)
+  // O^T layout: lane holds rows 4 g + r of dim slice dt for column n; add the lo column
+  // (n + G) into the hi column (n)
   float* o_s = reinterpret_cast<float*>(&p_s[0][0][0]);   // reuse: [kWaves][G][128] floats
   __syncthreads();
-  {
-    const int col = lane & 15, grp = lane >> 4;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
+  for (int dt = 0; dt < 8; ++dt) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float other = __shfl(oacc[dt][r], (lane & ~15) | ((col + G) & 15), 64);
-        if (col < G) o_s[(wave * G + col) * kHeadDim + dt * 16 + 4 * grp + r] = oacc[dt][r] + other;
-      }
+    for (int r = 0; r < 4; ++r) {
+      const float other = __shfl(oacc[dt][r], (lane & ~15) | ((n + G) & 15), 64);
+      if (n < G) o_s[(wave * G + n) * kHeadDim + dt * 16 + 4 * g + r] = oacc[dt][r] + other;
     }
   }
   __syncthreads();
@@ -587,7 +675,7 @@ hipError_t launch_gv(kvq_cache* c, int layer, const void* q, int q_f32, float si
   const int64_t n_tiles = (len + kVTile - 1) / kVTile;
   const int tps = static_cast<int>((n_tiles + S - 1) / S);
   dim3 grid(S, cfg.n_kv_heads, cfg.batch);
-  const size_t dyn = static_cast<size_t>(kWaves) * (c->k_words + 2) * kVTile * sizeof(uint32_t);
+  const size_t dyn = static_cast<size_t>(kWaves) * (c->k_words + 1) * kKS * sizeof(uint32_t);
   const Plan* plans = c->plans + static_cast<int64_t>(layer) * cfg.n_kv_heads;
   const bool nf = cfg.codec == KVQ_CODEC_NF16_B256;
   if constexpr (VB == 4) {

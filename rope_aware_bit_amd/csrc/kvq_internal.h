@@ -18,16 +18,14 @@ constexpr int kNfBlock = 256;        // values per absmax block of the NF16 code
 
 // Byte layout of the decode lookup tables that every decode workgroup copies into LDS.
 // Pair tables (widths 1..4) hold fp16x2 (CB[c0], CB[c1]) at index c0 | c1 << w; single
-// tables (widths 1..8) hold fp16 CB[c].  Each base is a multiple of its table's size, so
-// "(field << 2) | base" (pairs) and "(field << 1) | base" (singles) address an entry.
+// tables (widths 1..8) hold fp16 CB[c] at 2560 - 2^(w+2); width 0 addresses zero bytes at
+// the end.  Each base is a multiple of its table's size, so "(field << 2) | base" (pairs)
+// and "(field << 1) | base" (singles) address an entry.
 __host__ __device__ constexpr int pair_table_base(int w) {
   return w == 4 ? 0 : w == 3 ? 1024 : w == 2 ? 1280 : 1344;
 }
-__host__ __device__ constexpr int single_table_base(int w) {
-  return w == 8 ? 1536 : w == 7 ? 2048 : w == 6 ? 2304 : w == 5 ? 2432 : w == 4 ? 2496
-       : w == 3 ? 2528 : w == 2 ? 2544 : 2552;
-}
 constexpr int kLdsTableBytes = 2560;
+__host__ __device__ constexpr int single_table_base(int w) { return kLdsTableBytes - (4 << w); }
 
 // Constant tables, built on the host at cache creation and copied to the device.
 struct Tables {
