@@ -11,11 +11,16 @@ then all tokens are appended.
 A step = one kvq_decode_attn call per layer (36 launches, one query each),
 inputs resident in HBM.  `value` is the step's algorithmic bytes over its time
 (effective GB/s); tokens/s and % of the 8 TB/s peak are reported beside it.
-The roofline entry times every decode launch with HIP events on the launch
-stream.  The CPU baseline times the fp64 oracle's decode (unpack, dequantize,
-attention) of one of the 36 layers on the host and scales it to a step.
+The roofline entry divides the timed region (HIP events on the launch stream,
+which carries nothing but the decode launches) by the number of launches.  The CPU baseline times the fp64 oracle's decode (unpack, dequantize,
+attention) of layer 0, repeated for at least 10 s of host time, and scales the
+per-layer time to a step.  --traffic-probe runs one plain 256 MiB copy and one
+decode launch for the HBM byte counters (rocprofv3 --pmc FETCH_SIZE, then
+WRITE_SIZE); their per-launch figure is reported only while the decode kernel's
+sources hash to the value recorded beside it.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--traffic-probe]
 """
 from __future__ import annotations
 
@@ -30,6 +35,32 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 PLAN_BYTES_PER_HEAD = 1024   # field dims/widths/offsets and gains read by each decode launch
+CPU_SAMPLE_S = 10.0          # lower bound on the host time spent timing the oracle
+DECODE_SOURCES = ["decode_mfma.h", "decode_mfma.hip", "decode_mfma_g1.hip", "decode_mfma_g2.hip",
+                  "decode_mfma_g4.hip", "decode_mfma_g8.hip", "kvq_internal.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_mfma_qwen3b_128k_k3v3_traffic.json")
+
+
+def decode_source_hash() -> str:
+    """sha256 over the decode kernel's sources: the HBM counters are valid for this text only."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(ROOT, "rope_aware_bit_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """Per-launch HBM bytes measured by rocprofv3 counters for the current kernel text, else None."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != decode_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
 
 
 def log(*a):
@@ -53,8 +84,8 @@ def cpu_baseline(k0, v0, q0, calib, kb, vb, n_layers, bytes_per_step):
         r = ol.quantize_head(k0[:, h], v0[:, h], h)
         packed.append((r["k_words"], r["k_s16"], lay.pack_v_tiles(r["v_codes"], vb), r["v_s16"]))
     T = k0.shape[0]
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
+
+    def one_layer():
         kh, vh = [], []
         for h in range(H):
             kw, ks, vw, vs = packed[h]
@@ -62,8 +93,16 @@ def cpu_baseline(k0, v0, q0, calib, kb, vb, n_layers, bytes_per_step):
             kc = lay.unpack_k_rows(kw, dims, ws, 128)
             kh.append(at.dequant_k(kc, ks, al.dim_widths(ol.widths[h], 128), al.dim_values(ol.g[h], 128)))
             vh.append(at.dequant_v(lay.unpack_v_tiles(vw, vb, T), vs, vb))
-        out = at.decode_attention(q0.astype(np.float64), np.stack(kh), np.stack(vh))
-        dt = time.perf_counter() - t0
+        return at.decode_attention(q0.astype(np.float64), np.stack(kh), np.stack(vh))
+
+    with threadpool_limits(limits=1):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            out = one_layer()
+            reps += 1
+            if time.perf_counter() - t0 >= CPU_SAMPLE_S or reps >= n_layers:
+                break
+        dt = (time.perf_counter() - t0) / reps
     assert np.all(np.isfinite(out))
     step_s = dt * n_layers
     return {
@@ -72,8 +111,9 @@ def cpu_baseline(k0, v0, q0, calib, kb, vb, n_layers, bytes_per_step):
         "tokens_per_s": round(1.0 / step_s, 5),
         "cores": 1,
         "kind": "oracle",
-        "sample": f"1 of {n_layers} layers ({H} KV heads x {T} tokens): unpack + fp64 dequantize + "
-                  f"fp64 attention took {dt:.2f} s; scaled x{n_layers} to one step",
+        "sample": f"layer 0 of {n_layers} ({H} KV heads x {T} tokens), decoded {reps} times: unpack + "
+                  f"fp64 dequantize + fp64 attention took {dt:.2f} s per layer; scaled x{n_layers} "
+                  f"to one step",
     }
 
 
@@ -84,6 +124,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen3b_128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="run one plain copy of known size and one decode launch, then exit "
+                         "(for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the packed decode path "
@@ -110,7 +153,7 @@ def main():
     app_ms = []
     keep = None
     t_setup = time.perf_counter()
-    for layer in range(L):
+    for layer in range(1 if args.traffic_probe else L):
         k, v = gen.layer(layer)
         cache.alloc_bits(layer, k[:chunk])
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -125,9 +168,24 @@ def main():
             keep = (k.cpu().numpy(), v.cpu().numpy(), k[:chunk].cpu().numpy())
         del k, v
     qs = [gen.query(layer)[None].contiguous() for layer in range(L)]
+    if args.traffic_probe:
+        keep = None
     outs = [torch.empty(B, Hq, 128, dtype=torch.float32, device=dev) for _ in range(L)]
     torch.cuda.synchronize()
     log(f"setup {time.perf_counter() - t_setup:.1f} s")
+
+    if args.traffic_probe:
+        # a plain copy of 256 MiB (its counters give the bytes-per-count factor), then one decode
+        src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        cache.decode_attn(0, qs[0], out=outs[0])
+        torch.cuda.synchronize()
+        log(f"traffic probe: copy {src.numel() * 4} bytes read + written, one decode launch of layer 0")
+        cache.close()
+        return
 
     bytes_cache_layer = B * H * T * ((kb + vb) * 128 / 8 + 4)
     bytes_launch = bytes_cache_layer + B * Hq * 128 * 2 + B * Hq * 128 * 4 + H * PLAN_BYTES_PER_HEAD
@@ -150,17 +208,8 @@ def main():
     for o in outs:
         assert torch.isfinite(o).all()
 
-    # per-launch durations of the decode kernel (events around each launch, same stream)
-    pairs = []
-    for _ in range(args.steps):
-        for layer in range(L):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            cache.decode_attn(layer, qs[layer], out=outs[layer])
-            b.record(stream)
-            pairs.append((a, b))
-    torch.cuda.synchronize()
-    launch_us = float(np.mean([a.elapsed_time(b) for a, b in pairs])) * 1e3
+    # average decode-launch duration: the timed region holds only decode launches on this stream
+    launch_us = ms_step * 1e3 / L
 
     value = bytes_step / (ms_step * 1e-3) / 1e9
     achieved = bytes_launch / (launch_us * 1e-6) / 1e9
@@ -175,7 +224,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp32",
+        "dtype": "f16-mfma/f32",
         "data": "synthetic",
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(B / (ms_step * 1e-3), 2),
@@ -194,12 +243,12 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_split",
+            "kernel": "decode_mfma",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": recorded_traffic(),
             "launch_us": round(launch_us, 3),
             "bytes_per_launch": int(bytes_launch),
         },

@@ -91,8 +91,13 @@ typedef struct {
   int64_t len;             /* tokens appended so far */
   int32_t k_row_words;     /* 32-bit words per K row = 4*k_bits */
   int32_t v_dim_words;     /* 32-bit words per dim per 128-token V tile = 4*v_bits */
-  int64_t k_codes_bytes;   /* bytes of one layer's K rows:   [batch][n_kv][capacity][k_row_words] */
-  int64_t v_codes_bytes;   /* bytes of one layer's V tiles:  [batch][n_kv][capacity/128][128][v_dim_words] */
+  int64_t k_codes_bytes;   /* bytes of one layer's K rows: [batch][n_kv][capacity][k_row_words]; a row
+                              is the stored fields in plan order (blocks by width descending, then
+                              block index; coordinate p0 then p1), LSB first */
+  int64_t v_codes_bytes;   /* bytes of one layer's V tiles: [batch][n_kv][capacity/128][512][v_bits].
+                              A tile is 512 segments of v_bits words; segment (dim, g) holds the codes
+                              of that dim for tile tokens 32g .. 32g+31, LSB first (token 32g+e at bit
+                              e*v_bits), stored at index ((dim/16)*4 + g)*16 + dim%16 */
   int64_t k_scales_bytes;  /* fp16 K scales: BGTQ/UNIFORM [batch][n_kv][capacity];
                               NF16 [batch][capacity][n_kv*128/256] */
   int64_t v_scales_bytes;  /* fp16 V scales, same shapes as K scales */

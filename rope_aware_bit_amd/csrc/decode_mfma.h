@@ -286,8 +286,18 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(
     }
   }
   const uint32_t fd_r = tid < kHeadDim ? P->fdim[tid] : 0u;
-  const uint32_t pd_r = tid < kBlocks ? P->pdesc[tid] : 0u;
+  const uint32_t pd_r = P->pdesc[lane];   // descriptor of pair `lane` (every wave)
   const int n_pairs = __builtin_amdgcn_readfirstlane(P->n_fields) >> 1;
+  // sources of the per-workgroup pair tables (see below)
+  const uint8_t* gimg = tabg->lds_image[NF ? 1 : 0];
+  const uint32_t rep4v = reinterpret_cast<const uint32_t*>(gimg + pair_table_base(4))[tid];
+  const uint32_t rep3v = reinterpret_cast<const uint32_t*>(gimg + pair_table_base(3))[tid & 63];
+  const uint16_t* cb6 = reinterpret_cast<const uint16_t*>(gimg + single_table_base(6));
+  const uint16_t* cb5 = reinterpret_cast<const uint16_t*>(gimg + single_table_base(5));
+  const uint32_t hi6 = cb6[tid >> 2], hi5 = cb5[tid >> 3];
+  const uint4 lo6a = reinterpret_cast<const uint4*>(cb6 + ((16 * tid) & 63))[0];
+  const uint4 lo6b = reinterpret_cast<const uint4*>(cb6 + ((16 * tid) & 63))[1];
+  const uint2 lo5 = *reinterpret_cast<const uint2*>(cb5 + ((4 * tid) & 31));
 
   // K rows of tokens lane and lane + 64 (first 16 words), scales of tokens 16 tg + n, V segments
   uint32_t vseg[8][VB + 2];
@@ -346,6 +356,36 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(
     pd_s[tid] = pd_r;
     px_s[tid] = pair_lookup_params(pd_r >> 16);
   }
+  // 32-fold replicas of the width-4 and width-3 pair tables: thread t writes all copies of
+  // entry t (rotating the 16-byte pieces over the lanes spreads the banks)
+  {
+    const uint4 v4 = make_uint4(rep4v, rep4v, rep4v, rep4v), v3 = make_uint4(rep3v, rep3v, rep3v, rep3v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int jj = (j + tid) & 7;
+      *reinterpret_cast<uint4*>(tab_s + kRep4Base + (tid << 7) + 16 * jj) = v4;
+      if (tid < 64) *reinterpret_cast<uint4*>(tab_s + kRep3Base + (tid << 7) + 16 * jj) = v3;
+    }
+  }
+  // pair tables of widths 5 and 6 when the plan stores such blocks: entry (c1 << w) | c0 holds
+  // (CB_w[c0], CB_w[c1]); thread t fills 16 (w = 6) or 4 (w = 5) consecutive c0 of one c1
+  const uint64_t uses5 = __ballot((pd_r >> 16) == 5u), uses6 = __ballot((pd_r >> 16) == 6u);
+  const uint64_t uses78 = __ballot((pd_r >> 16) >= 7u);
+  if (uses6) {
+    const uint32_t hi = hi6 << 16;
+    const uint32_t lo[8] = {lo6a.x, lo6a.y, lo6a.z, lo6a.w, lo6b.x, lo6b.y, lo6b.z, lo6b.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 v = make_uint4((lo[2 * q] & 0xFFFFu) | hi, (lo[2 * q] >> 16) | hi,
+                                 (lo[2 * q + 1] & 0xFFFFu) | hi, (lo[2 * q + 1] >> 16) | hi);
+      *reinterpret_cast<uint4*>(tab_s + kPair6Base + 4 * (16 * tid + 4 * q)) = v;
+    }
+  }
+  if (uses5) {
+    const uint32_t hi = hi5 << 16;
+    const uint4 v = make_uint4((lo5.x & 0xFFFFu) | hi, (lo5.x >> 16) | hi, (lo5.y & 0xFFFFu) | hi, (lo5.y >> 16) | hi);
+    *reinterpret_cast<uint4*>(tab_s + kPair5Base + 4 * (4 * tid)) = v;
+  }
   __syncthreads();
   // query operand of the key product: a_s[c][m][k] = hi (m even) or lo (m odd) fp16 part of
   // q'[m / 2][dim of field 32 c + k]; rows of heads >= G and fields past the stored ones are 0.
@@ -362,41 +402,6 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(
       a_s[c][2 * hh][k] = hi;
       a_s[c][2 * hh + 1][k] = static_cast<_Float16>(qq - static_cast<float>(hi));
     }
-  }
-  // pair tables of widths 5 and 6 when the plan stores such blocks: entry (c1 << w) | c0 holds
-  // (CB_w[c0], CB_w[c1]); thread t fills four consecutive c0 for one c1
-  const uint64_t uses5 = __ballot((pd_s[lane] >> 16) == 5u), uses6 = __ballot((pd_s[lane] >> 16) == 6u);
-  const uint64_t uses78 = __ballot((pd_s[lane] >> 16) >= 7u);
-  if (uses6) {
-    const uint16_t* cb = reinterpret_cast<const uint16_t*>(tab_s + kImageBase + single_table_base(6));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = 4 * (tid + 256 * j);   // 4096 entries
-      const uint32_t hi = static_cast<uint32_t>(cb[e >> 6]) << 16;
-      const uint2 lo = *reinterpret_cast<const uint2*>(cb + (e & 63));
-      const uint4 v = make_uint4((lo.x & 0xFFFFu) | hi, (lo.x >> 16) | hi, (lo.y & 0xFFFFu) | hi, (lo.y >> 16) | hi);
-      *reinterpret_cast<uint4*>(tab_s + kPair6Base + 4 * e) = v;
-    }
-  }
-  if (uses5) {
-    const uint16_t* cb = reinterpret_cast<const uint16_t*>(tab_s + kImageBase + single_table_base(5));
-    const int e = 4 * tid;   // 1024 entries
-    const uint32_t hi = static_cast<uint32_t>(cb[e >> 5]) << 16;
-    const uint2 lo = *reinterpret_cast<const uint2*>(cb + (e & 31));
-    const uint4 v = make_uint4((lo.x & 0xFFFFu) | hi, (lo.x >> 16) | hi, (lo.y & 0xFFFFu) | hi, (lo.y >> 16) | hi);
-    *reinterpret_cast<uint4*>(tab_s + kPair5Base + 4 * e) = v;
-  }
-  // 32-fold replicas of the width-3 and width-4 pair tables: thread t writes copy t % 32 of
-  // entries t / 32, t / 32 + 8, ...
-  {
-    const int copy = tid & 31, eg = tid >> 5;
-    const char* img = tab_s + kImageBase;
-#pragma unroll 4
-    for (int e = eg; e < 256; e += 8)
-      *reinterpret_cast<uint32_t*>(tab_s + kRep4Base + (e << 7) + 4 * copy) = lds_u32(img, pair_table_base(4) + 4 * e);
-#pragma unroll
-    for (int e = eg; e < 64; e += 8)
-      *reinterpret_cast<uint32_t*>(tab_s + kRep3Base + (e << 7) + 4 * copy) = lds_u32(img, pair_table_base(3) + 4 * e);
   }
   const int n_chunks = (n_pairs + 15) >> 4;
   const uint32_t lb = (lane & 31u) << 2;   // this lane's replica offset
