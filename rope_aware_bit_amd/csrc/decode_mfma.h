@@ -47,7 +47,6 @@ namespace mfma {
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
 constexpr int kGroup = 16;        // splits merged per first-level merger
 constexpr int kMaxGroups = 16;    // so at most kGroup * kMaxGroups = 256 splits
 constexpr int kKS = 144;          // LDS row stride (words) of a staged K tile: 128 tokens + 16
@@ -170,16 +169,16 @@ __device__ inline uint32_t v_pair(const uint32_t* S, int e, const char* tab, uin
 // o = sum_e 2^(m_e - m*) o_e, in e order.  Writes either the merged partial or, if
 // `final_out`, o / l to dst_o[g*128 + i].  All loads are issued before any result is
 // needed, so the merge costs one round of memory latency.
-template <int G>
+template <int G, int NT>
 __device__ __attribute__((always_inline)) inline void merge_level(const float* __restrict__ src_o, const float* __restrict__ src_ml,
                                    int count, float* mw, int tid, float* __restrict__ dst_o,
                                    float* __restrict__ dst_ml, bool final_out) {
   constexpr int NOUT = G * kHeadDim;
-  constexpr int OPT = (NOUT + 255) / 256;
+  constexpr int OPT = (NOUT + NT - 1) / NT;
   float ov[OPT][kGroup];
 #pragma unroll
   for (int k = 0; k < OPT; ++k) {
-    const int idx = (tid + 256 * k) % NOUT;
+    const int idx = (tid + NT * k) % NOUT;
     const int g = idx / kHeadDim, i = idx % kHeadDim;
 #pragma unroll
     for (int e = 0; e < kGroup; ++e) {
@@ -216,7 +215,7 @@ __device__ __attribute__((always_inline)) inline void merge_level(const float* _
   __syncthreads();
 #pragma unroll
   for (int k = 0; k < OPT; ++k) {
-    const int idx = tid + 256 * k;
+    const int idx = tid + NT * k;
     if (idx >= NOUT) break;
     const int g = idx / kHeadDim, i = idx % kHeadDim;
     float o = 0.0f;
@@ -234,37 +233,90 @@ __device__ __attribute__((always_inline)) inline void merge_level(const float* _
   }
 }
 
-template <int G, int VB, bool NF>
-__global__ __launch_bounds__(256, 1) void decode_mfma(
+// One chunk of the key product for lane (n, g): the query operand, the lookup parameters of
+// the lane's four pairs (plan ranks 16 c + 4 g .. + 3) and the two 32-bit row windows (pairs
+// 0-1 and 2-3) of each of its 8 tokens 16 tg + n.
+struct KChunk {
+  h8 aq;
+  uint32_t shA, shB, rel1, rel3, baseA, baseB;
+  uint32_t wp[4], bw[4], pb[4], ps[4];
+  uint32_t la[8], ha[8], lb[8], hb[8];
+};
+
+__device__ __attribute__((always_inline)) inline KChunk k_chunk_params(
+    int c, int g, int n, const uint32_t* pd_s, const uint32_t* px_s, const _Float16 (*a_s)[16][32],
+    uint32_t lane_copy, const uint32_t* kr) {
+  KChunk k;
+  k.aq = *reinterpret_cast<const h8*>(&a_s[c][n][8 * g]);
+  const int grp = 4 * c + g;
+  const uint4 dd = *reinterpret_cast<const uint4*>(&pd_s[4 * grp]);
+  const uint4 xx = *reinterpret_cast<const uint4*>(&px_s[4 * grp]);
+  const uint32_t d4[4] = {dd.x, dd.y, dd.z, dd.w}, x4[4] = {xx.x, xx.y, xx.z, xx.w};
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    k.wp[p] = d4[p] >> 16;
+    k.bw[p] = x4[p] >> 24;
+    const uint32_t rep = (x4[p] >> 16) & 1u;
+    k.pb[p] = (x4[p] & 0xFFFFu) | (rep ? lane_copy : 0u);
+    k.ps[p] = rep ? 7u : 2u;
+  }
+  const uint32_t offA = d4[0] & 0xFFFFu, offB = d4[2] & 0xFFFFu;
+  k.shA = offA & 31u;
+  k.shB = offB & 31u;
+  k.rel1 = 2u * k.wp[0];
+  k.rel3 = 2u * k.wp[2];
+  k.baseA = (offA >> 5) * kKS + n;
+  k.baseB = (offB >> 5) * kKS + n;
+  return k;
+}
+
+__device__ __attribute__((always_inline)) inline void k_chunk_windows(KChunk& k, const uint32_t* kr) {
+#pragma unroll
+  for (int tg = 0; tg < 8; ++tg) {
+    k.la[tg] = kr[k.baseA + 16 * tg];
+    k.ha[tg] = kr[k.baseA + 16 * tg + kKS];
+    k.lb[tg] = kr[k.baseB + 16 * tg];
+    k.hb[tg] = kr[k.baseB + 16 * tg + kKS];
+  }
+}
+
+// Decode kernel.  W waves per workgroup (one or two per SIMD).  Every wave owns a region of
+// `region_words` LDS words that holds, in turn, its staged K tile, its softmax weights and its
+// share of the wave merge (and, during set-up, wave 0's region holds the scaled query).
+template <int G, int VB, bool NF, int W>
+__global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     const void* __restrict__ qv, int q_f32, float sigma, int64_t len, int n_kv, int64_t cap,
     int tiles_per_split, const Plan* __restrict__ plans, const Tables* __restrict__ tabg,
     const uint32_t* __restrict__ kc, const uint32_t* __restrict__ vc, const uint16_t* __restrict__ ks,
-    const uint16_t* __restrict__ vs, int k_words, int n_nf, int n_splits, float* __restrict__ part_o,
-    float* __restrict__ part_ml, float* __restrict__ gpart_o, float* __restrict__ gpart_ml,
-    unsigned* __restrict__ counters, float* __restrict__ out) {
+    const uint16_t* __restrict__ vs, int k_words, int n_nf, int n_splits, int region_words,
+    float* __restrict__ part_o, float* __restrict__ part_ml, float* __restrict__ gpart_o,
+    float* __restrict__ gpart_ml, unsigned* __restrict__ counters, float* __restrict__ out) {
+  constexpr int NT = 64 * W;
+  constexpr bool kPipe = W == 4;                      // one wave per SIMD: prefetch and pipeline
   constexpr int PCOLS = 2 * G;                        // P columns: hi of heads 0..G-1, then lo
   constexpr int KWV = 4 * VB;                         // words per dim per V tile
-  constexpr int QPT = (G * kHeadDim + 255) / 256;     // query values per thread at set-up
+  constexpr int QPT = (G * kHeadDim + 255) / 256;     // query values per set-up thread
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int n = lane & 15, g = lane >> 4;             // MFMA column and row group of this lane
+  const bool setup = tid < 256;                       // the first 256 threads do the set-up
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int n_q = n_kv * G;
   const int64_t bh = static_cast<int64_t>(b) * n_kv + h;
 
   __shared__ __attribute__((aligned(16))) char tab_s[kTableRegion];
-  __shared__ __attribute__((aligned(16))) _Float16 p_s[kWaves][PCOLS][kVTile];
   __shared__ __attribute__((aligned(16))) _Float16 a_s[4][16][32];
   __shared__ uint8_t fdim_s[kHeadDim];
   __shared__ __attribute__((aligned(16))) uint32_t pd_s[kBlocks];
   __shared__ __attribute__((aligned(16))) uint32_t px_s[kBlocks];
-  __shared__ float comb_m[kWaves][G], comb_l[kWaves][G];
-  __shared__ float alpha_s[kWaves][G];
+  __shared__ float comb_m[W][G], comb_l[W][G];
+  __shared__ float alpha_s[W][G];
   __shared__ bool flag_s;
-  extern __shared__ __attribute__((aligned(16))) uint32_t kr_dyn[];   // [kWaves][k_words + 1][kKS]
-  uint32_t* kr = kr_dyn + wave * (k_words + 1) * kKS;
-  float (*qs_s)[kHeadDim] = reinterpret_cast<float (*)[kHeadDim]>(kr_dyn);   // set-up only
+  extern __shared__ __attribute__((aligned(16))) uint32_t dyn_s[];   // [W][region_words]
+  uint32_t* kr = dyn_s + wave * region_words;                         // [k_words + 1][kKS]
+  _Float16* pw = reinterpret_cast<_Float16*>(kr);                     // [PCOLS][128], after keys
+  float (*qs_s)[kHeadDim] = reinterpret_cast<float (*)[kHeadDim]>(dyn_s);   // set-up only
 
   const int64_t n_tiles = (len + kVTile - 1) / kVTile;
   const int64_t t_begin = static_cast<int64_t>(s) * tiles_per_split;
@@ -272,14 +324,15 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(
   const Plan* P = plans + h;
 
   // ---- set-up loads first (small and shared by every workgroup), then the first tile's ----
+  const uint8_t* gimg = tabg->lds_image[NF ? 1 : 0];
   uint4 timg = make_uint4(0u, 0u, 0u, 0u);
-  if (tid < kLdsTableBytes / 16) timg = reinterpret_cast<const uint4*>(tabg->lds_image[NF ? 1 : 0])[tid];
+  if (tid < kLdsTableBytes / 16) timg = reinterpret_cast<const uint4*>(gimg)[tid];
   float qr[QPT], gr[QPT];
 #pragma unroll
   for (int j = 0; j < QPT; ++j) {
     const int k = tid + 256 * j;
     qr[j] = gr[j] = 0.0f;
-    if (k < G * kHeadDim) {
+    if (setup && k < G * kHeadDim) {
       const int64_t qi = (static_cast<int64_t>(b) * n_q + h * G) * kHeadDim + k;
       qr[j] = q_f32 ? static_cast<const float*>(qv)[qi] : __half2float(static_cast<const __half*>(qv)[qi]);
       gr[j] = P->g[k % kHeadDim];
@@ -288,16 +341,16 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(
   const uint32_t fd_r = tid < kHeadDim ? P->fdim[tid] : 0u;
   const uint32_t pd_r = P->pdesc[lane];   // descriptor of pair `lane` (every wave)
   const int n_pairs = __builtin_amdgcn_readfirstlane(P->n_fields) >> 1;
-  // sources of the per-workgroup pair tables (see below)
-  const uint8_t* gimg = tabg->lds_image[NF ? 1 : 0];
-  const uint32_t rep4v = reinterpret_cast<const uint32_t*>(gimg + pair_table_base(4))[tid];
-  const uint32_t rep3v = reinterpret_cast<const uint32_t*>(gimg + pair_table_base(3))[tid & 63];
+  // sources of the per-workgroup pair tables (see below); set-up threads t < 256 only
+  const int st = tid & 255;
+  const uint32_t rep4v = reinterpret_cast<const uint32_t*>(gimg + pair_table_base(4))[st];
+  const uint32_t rep3v = reinterpret_cast<const uint32_t*>(gimg + pair_table_base(3))[st & 63];
   const uint16_t* cb6 = reinterpret_cast<const uint16_t*>(gimg + single_table_base(6));
   const uint16_t* cb5 = reinterpret_cast<const uint16_t*>(gimg + single_table_base(5));
-  const uint32_t hi6 = cb6[tid >> 2], hi5 = cb5[tid >> 3];
-  const uint4 lo6a = reinterpret_cast<const uint4*>(cb6 + ((16 * tid) & 63))[0];
-  const uint4 lo6b = reinterpret_cast<const uint4*>(cb6 + ((16 * tid) & 63))[1];
-  const uint2 lo5 = *reinterpret_cast<const uint2*>(cb5 + ((4 * tid) & 31));
+  const uint32_t hi6 = cb6[st >> 2], hi5 = cb5[st >> 3];
+  const uint4 lo6a = reinterpret_cast<const uint4*>(cb6 + ((16 * st) & 63))[0];
+  const uint4 lo6b = reinterpret_cast<const uint4*>(cb6 + ((16 * st) & 63))[1];
+  const uint2 lo5 = *reinterpret_cast<const uint2*>(cb5 + ((4 * st) & 31));
 
   // K rows of tokens lane and lane + 64 (first 16 words), scales of tokens 16 tg + n, V segments
   uint32_t vseg[8][VB + 2];
@@ -341,7 +394,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(
   if (t_begin + wave < t_end) {
     load_k(t_begin + wave);
     load_scales(t_begin + wave);
-    load_v(t_begin + wave);
+    if constexpr (kPipe) load_v(t_begin + wave);
   }
 
   // ---- set-up: tables, scaled query, field dims and pair descriptors into LDS ----
@@ -349,7 +402,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(
 #pragma unroll
   for (int j = 0; j < QPT; ++j) {
     const int k = tid + 256 * j;
-    if (k < G * kHeadDim) qs_s[k / kHeadDim][k % kHeadDim] = qr[j] * gr[j] * sigma;
+    if (setup && k < G * kHeadDim) qs_s[k / kHeadDim][k % kHeadDim] = qr[j] * gr[j] * sigma;
   }
   if (tid < kHeadDim) fdim_s[tid] = static_cast<uint8_t>(fd_r);
   if (tid < kBlocks) {
@@ -358,7 +411,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(
   }
   // 32-fold replicas of the width-4 and width-3 pair tables: thread t writes all copies of
   // entry t (rotating the 16-byte pieces over the lanes spreads the banks)
-  {
+  if (setup) {
     const uint4 v4 = make_uint4(rep4v, rep4v, rep4v, rep4v), v3 = make_uint4(rep3v, rep3v, rep3v, rep3v);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -371,7 +424,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(
   // (CB_w[c0], CB_w[c1]); thread t fills 16 (w = 6) or 4 (w = 5) consecutive c0 of one c1
   const uint64_t uses5 = __ballot((pd_r >> 16) == 5u), uses6 = __ballot((pd_r >> 16) == 6u);
   const uint64_t uses78 = __ballot((pd_r >> 16) >= 7u);
-  if (uses6) {
+  if (uses6 && setup) {
     const uint32_t hi = hi6 << 16;
     const uint32_t lo[8] = {lo6a.x, lo6a.y, lo6a.z, lo6a.w, lo6b.x, lo6b.y, lo6b.z, lo6b.w};
 #pragma unroll
@@ -381,7 +434,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(
       *reinterpret_cast<uint4*>(tab_s + kPair6Base + 4 * (16 * tid + 4 * q)) = v;
     }
   }
-  if (uses5) {
+  if (uses5 && setup) {
     const uint32_t hi = hi5 << 16;
     const uint4 v = make_uint4((lo5.x & 0xFFFFu) | hi, (lo5.x >> 16) | hi, (lo5.y & 0xFFFFu) | hi, (lo5.y >> 16) | hi);
     *reinterpret_cast<uint4*>(tab_s + kPair5Base + 4 * (4 * tid)) = v;
@@ -389,8 +442,8 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(
   __syncthreads();
   // query operand of the key product: a_s[c][m][k] = hi (m even) or lo (m odd) fp16 part of
   // q'[m / 2][dim of field 32 c + k]; rows of heads >= G and fields past the stored ones are 0.
-  // Thread t fills field t % 128 for heads t / 128, t / 128 + 2, ...
-  {
+  // Thread t < 256 fills field t % 128 for heads t / 128, t / 128 + 2, ...
+  if (setup) {
     const int f = tid & 127, c = f >> 5, k = f & 31;
     const bool live = f < 2 * n_pairs;
     const int dim = fdim_s[f];
@@ -403,11 +456,8 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(
       a_s[c][2 * hh + 1][k] = static_cast<_Float16>(qq - static_cast<float>(hi));
     }
   }
-  const int n_chunks = (n_pairs + 15) >> 4;
   const uint32_t lb = (lane & 31u) << 2;   // this lane's replica offset
   __syncthreads();
-  // zero pad row after the staged K words (the area held the scaled query during set-up)
-  kr[k_words * kKS + lane] = kr[k_words * kKS + 64 + lane] = 0u;
 
   // ---- per-wave state: lane (n, g) keeps heads 2g, 2g + 1 ----
   const int h0 = 2 * g, h1 = 2 * g + 1;
@@ -417,10 +467,17 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) oacc[dt] = f4{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t tile = t_begin + wave; tile < t_end; tile += kWaves) {
+  for (int64_t tile = t_begin + wave; tile < t_end; tile += W) {
     const int64_t tok0 = tile * kVTile;
-    const int64_t next = tile + kWaves;
-    // -- stage the K rows in LDS word-major (kr[d * kKS + tau] = word d of token tau) --
+    const int64_t next = tile + W;
+    if constexpr (!kPipe) {
+      if (tile != t_begin + wave) {   // later tiles: loaded here (the other wave hides the wait)
+        load_k(tile);
+        load_scales(tile);
+      }
+    }
+    // -- stage the K rows in LDS word-major (kr[d * kKS + tau] = word d of token tau), then a
+    //    zero row after them (the area held the previous tile's softmax weights) --
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       if (4 * k < k_words) {
@@ -437,86 +494,84 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(
       dst[0] = x0.x; dst[kKS] = x0.y; dst[2 * kKS] = x0.z; dst[3 * kKS] = x0.w;
       dst[64] = x1.x; dst[kKS + 64] = x1.y; dst[2 * kKS + 64] = x1.z; dst[3 * kKS + 64] = x1.w;
     }
+    kr[k_words * kKS + lane] = kr[k_words * kKS + 64 + lane] = 0u;
     wave_sync();
-    if (next < t_end) load_k(next);
+    if constexpr (kPipe) {
+      if (next < t_end) load_k(next);
+    }
 
     // -- keys: D[part][token] = sum over fields of q'[part][field] * CB[code[token][field]],
-    //    one 16x16x32 product per (chunk of 16 pairs, group of 16 tokens) --
+    //    one 16x16x32 product per (chunk of 16 pairs, group of 16 tokens).  Chunks past the
+    //    stored pairs have zero descriptors and a zero query operand, so all four are processed
+    //    without branches. --
     f4 dacc[8];
 #pragma unroll
     for (int tg = 0; tg < 8; ++tg) dacc[tg] = f4{0.f, 0.f, 0.f, 0.f};
-    for (int c = 0; c < n_chunks; ++c) {
-      {
-        const h8 aq = *reinterpret_cast<const h8*>(&a_s[c][n][8 * g]);
-        const int grp = 4 * c + g;   // this lane's pairs: 4 grp .. 4 grp + 3
-        // pairs 0, 1 come from a 32-bit window at pair 0, pairs 2, 3 from one at pair 2 (two
-        // pairs of at most 8 bits each fit); widths <= 6 use one pair lookup, 7 and 8 two
-        // single lookups
-        const uint4 dd = *reinterpret_cast<const uint4*>(&pd_s[4 * grp]);
-        const uint32_t d4[4] = {dd.x, dd.y, dd.z, dd.w};
-        const uint4 xx = *reinterpret_cast<const uint4*>(&px_s[4 * grp]);
-        const uint32_t x4[4] = {xx.x, xx.y, xx.z, xx.w};
-        uint32_t wp[4], bw[4], pb[4], ps[4];
+    auto k_lookups = [&](const KChunk& cur, int c, uint32_t (&u)[8][4]) {
+#pragma unroll
+      for (int tg = 0; tg < 8; ++tg) {
+        const uint32_t xa = __builtin_amdgcn_alignbit(cur.ha[tg], cur.la[tg], cur.shA);
+        const uint32_t xb = __builtin_amdgcn_alignbit(cur.hb[tg], cur.lb[tg], cur.shB);
+        u[tg][0] = lds_u32(tab_s, (__builtin_amdgcn_ubfe(xa, 0u, cur.bw[0]) << cur.ps[0]) | cur.pb[0]);
+        u[tg][1] = lds_u32(tab_s, (__builtin_amdgcn_ubfe(xa, cur.rel1, cur.bw[1]) << cur.ps[1]) | cur.pb[1]);
+        u[tg][2] = lds_u32(tab_s, (__builtin_amdgcn_ubfe(xb, 0u, cur.bw[2]) << cur.ps[2]) | cur.pb[2]);
+        u[tg][3] = lds_u32(tab_s, (__builtin_amdgcn_ubfe(xb, cur.rel3, cur.bw[3]) << cur.ps[3]) | cur.pb[3]);
+      }
+      if ((uses78 >> (16 * c)) & 0xFFFFull) {
+        // blocks of 7 or 8 bits: two single lookups (lanes whose pair is narrower skip)
+        const char* tabi = tab_s + kImageBase;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          wp[p] = d4[p] >> 16;
-          bw[p] = x4[p] >> 24;
-          const uint32_t rep = (x4[p] >> 16) & 1u;
-          pb[p] = (x4[p] & 0xFFFFu) | (rep ? lb : 0u);
-          ps[p] = rep ? 7u : 2u;
-        }
-        const uint32_t offA = d4[0] & 0xFFFFu, offB = d4[2] & 0xFFFFu;
-        const uint32_t shA = offA & 31u, shB = offB & 31u;
-        const uint32_t rel1 = 2u * wp[0], rel3 = 2u * wp[2];
-        const uint32_t* kA = kr + (offA >> 5) * kKS + n;
-        const uint32_t* kB = kr + (offB >> 5) * kKS + n;
-        const bool has78 = ((uses78 >> (16 * c)) & 0xFFFFull) != 0ull;
-        // all window reads first, then extraction and lookups per token group, then the
-        // products: LDS returns in order, so each step waits only for what it uses
-        uint32_t la[8], ha[8], lb[8], hb[8], u[8][4];
+          if (cur.wp[p] >= 7u) {
+            const uint32_t sb = static_cast<uint32_t>(kLdsTableBytes) - (4u << cur.wp[p]);
+            const uint32_t rel = (p & 1) ? (p == 1 ? cur.rel1 : cur.rel3) : 0u;
 #pragma unroll
-        for (int tg = 0; tg < 8; ++tg) {
-          la[tg] = kA[16 * tg];
-          ha[tg] = kA[16 * tg + kKS];
-          lb[tg] = kB[16 * tg];
-          hb[tg] = kB[16 * tg + kKS];
-        }
-        uint32_t xa[8], xb[8];
-#pragma unroll
-        for (int tg = 0; tg < 8; ++tg) {
-          xa[tg] = __builtin_amdgcn_alignbit(ha[tg], la[tg], shA);
-          xb[tg] = __builtin_amdgcn_alignbit(hb[tg], lb[tg], shB);
-          u[tg][0] = lds_u32(tab_s, (__builtin_amdgcn_ubfe(xa[tg], 0u, bw[0]) << ps[0]) | pb[0]);
-          u[tg][1] = lds_u32(tab_s, (__builtin_amdgcn_ubfe(xa[tg], rel1, bw[1]) << ps[1]) | pb[1]);
-          u[tg][2] = lds_u32(tab_s, (__builtin_amdgcn_ubfe(xb[tg], 0u, bw[2]) << ps[2]) | pb[2]);
-          u[tg][3] = lds_u32(tab_s, (__builtin_amdgcn_ubfe(xb[tg], rel3, bw[3]) << ps[3]) | pb[3]);
-        }
-        if (has78) {
-          // blocks of 7 or 8 bits: two single lookups (lanes whose pair is narrower skip)
-          const char* tabi = tab_s + kImageBase;
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            if (wp[p] >= 7u) {
-              const uint32_t sb = static_cast<uint32_t>(kLdsTableBytes) - (4u << wp[p]);
-              const uint32_t rel = (p & 1) ? (p == 1 ? rel1 : rel3) : 0u;
-#pragma unroll
-              for (int tg = 0; tg < 8; ++tg) {
-                const uint32_t x = (p < 2) ? xa[tg] : xb[tg];
-                const uint32_t f0 = __builtin_amdgcn_ubfe(x, rel, wp[p]);
-                const uint32_t f1 = __builtin_amdgcn_ubfe(x, rel + wp[p], wp[p]);
-                u[tg][p] = lds_u16(tabi, (f0 << 1) | sb) | (lds_u16(tabi, (f1 << 1) | sb) << 16);
-              }
+            for (int tg = 0; tg < 8; ++tg) {
+              const uint32_t x = (p < 2) ? __builtin_amdgcn_alignbit(cur.ha[tg], cur.la[tg], cur.shA)
+                                         : __builtin_amdgcn_alignbit(cur.hb[tg], cur.lb[tg], cur.shB);
+              const uint32_t f0 = __builtin_amdgcn_ubfe(x, rel, cur.wp[p]);
+              const uint32_t f1 = __builtin_amdgcn_ubfe(x, rel + cur.wp[p], cur.wp[p]);
+              u[tg][p] = lds_u16(tabi, (f0 << 1) | sb) | (lds_u16(tabi, (f1 << 1) | sb) << 16);
             }
           }
         }
+      }
+    };
+    auto k_products = [&](const KChunk& cur, const uint32_t (&u)[8][4]) {
 #pragma unroll
-        for (int tg = 0; tg < 8; ++tg) {
-          h8 bk;
-          __builtin_memcpy(&bk, u[tg], 16);
-          dacc[tg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq, bk, dacc[tg], 0, 0, 0);
-        }
+      for (int tg = 0; tg < 8; ++tg) {
+        h8 bk;
+        __builtin_memcpy(&bk, u[tg], 16);
+        dacc[tg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur.aq, bk, dacc[tg], 0, 0, 0);
+      }
+    };
+    if constexpr (kPipe) {
+      // software pipeline: chunk c + 1's descriptors and row windows are read while chunk c's
+      // lookups and products run
+      KChunk cur = k_chunk_params(0, g, n, pd_s, px_s, a_s, lb, kr);
+      k_chunk_windows(cur, kr);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        KChunk nxt;
+        if (c + 1 < 4) nxt = k_chunk_params(c + 1, g, n, pd_s, px_s, a_s, lb, kr);
+        uint32_t u[8][4];
+        k_lookups(cur, c, u);
+        if (c + 1 < 4) k_chunk_windows(nxt, kr);
+        k_products(cur, u);
+        if (c + 1 < 4) cur = nxt;
+      }
+    } else {
+#pragma unroll 1
+      for (int c = 0; c < 4; ++c) {
+        KChunk cur = k_chunk_params(c, g, n, pd_s, px_s, a_s, lb, kr);
+        k_chunk_windows(cur, kr);
+        uint32_t u[8][4];
+        k_lookups(cur, c, u);
+        k_products(cur, u);
       }
     }
+    wave_sync();   // the key rows are read; the area takes the softmax weights next
+    if constexpr (!kPipe) load_v(tile);   // V segments are needed only after the softmax
 
     // -- online softmax: lane (n, g) holds heads 2g and 2g + 1 of tokens 16 tg + n --
     float L0[8], L1[8];
@@ -550,12 +605,12 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(
       const _Float16 q0h = static_cast<_Float16>(q0), q1h = static_cast<_Float16>(q1);
       const int t = 16 * tg + n;
       if (vh0) {
-        p_s[wave][h0][t] = q0h;
-        p_s[wave][G + h0][t] = static_cast<_Float16>(q0 - static_cast<float>(q0h));
+        pw[h0 * kVTile + t] = q0h;
+        pw[(G + h0) * kVTile + t] = static_cast<_Float16>(q0 - static_cast<float>(q0h));
       }
       if (vh1) {
-        p_s[wave][h1][t] = q1h;
-        p_s[wave][G + h1][t] = static_cast<_Float16>(q1 - static_cast<float>(q1h));
+        pw[h1 * kVTile + t] = q1h;
+        pw[(G + h1) * kVTile + t] = static_cast<_Float16>(q1 - static_cast<float>(q1h));
       }
     }
     if (n == 0) {
@@ -563,7 +618,9 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(
       if (vh1) alpha_s[wave][h1] = al1;
     }
     const bool rescale = __ballot((vh0 && al0 != 1.0f) || (vh1 && al1 != 1.0f)) != 0ull;
-    if (next < t_end) load_scales(next);
+    if constexpr (kPipe) {
+      if (next < t_end) load_scales(next);
+    }
     wave_sync();
     if (rescale) {
       // output column n belongs to head n % G (columns >= 2G are unused)
@@ -576,7 +633,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(
     for (int c = 0; c < 4; ++c) {
       h8 bp;
       if (n < PCOLS) {
-        bp = *reinterpret_cast<const h8*>(&p_s[wave][n][32 * g + 8 * c]);
+        bp = *reinterpret_cast<const h8*>(&pw[n * kVTile + 32 * g + 8 * c]);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) bp[e] = static_cast<_Float16>(0.0f);
@@ -592,10 +649,12 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(
       }
     }
     wave_sync();
-    if (next < t_end) load_v(next);
+    if constexpr (kPipe) {
+      if (next < t_end) load_v(next);
+    }
   }
 
-  // ---- merge the 4 waves of this workgroup ----
+  // ---- merge the W waves of this workgroup ----
   l0 = row_sum16(l0);
   l1 = row_sum16(l1);
   if (n == 0) {
@@ -609,30 +668,30 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(
     }
   }
   // O^T layout: lane holds rows 4 g + r of dim slice dt for column n; add the lo column
-  // (n + G) into the hi column (n)
-  float* o_s = reinterpret_cast<float*>(&p_s[0][0][0]);   // reuse: [kWaves][G][128] floats
+  // (n + G) into the hi column (n), into this wave's region as [G][128] floats
+  float* ow = reinterpret_cast<float*>(kr);
   __syncthreads();
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float other = __shfl(oacc[dt][r], (lane & ~15) | ((n + G) & 15), 64);
-      if (n < G) o_s[(wave * G + n) * kHeadDim + dt * 16 + 4 * g + r] = oacc[dt][r] + other;
+      if (n < G) ow[n * kHeadDim + dt * 16 + 4 * g + r] = oacc[dt][r] + other;
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < G * kHeadDim; idx += blockDim.x) {
+  for (int idx = tid; idx < G * kHeadDim; idx += NT) {
     const int hd = idx / kHeadDim, i = idx % kHeadDim;
     float ms = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) ms = fmaxf(ms, comb_m[w][hd]);
+    for (int w = 0; w < W; ++w) ms = fmaxf(ms, comb_m[w][hd]);
     float o = 0.0f, l = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < W; ++w) {
       const float mw = comb_m[w][hd];
       if (mw == -INFINITY) continue;
       const float sc = exp2f(mw - ms);
-      o += sc * o_s[(w * G + hd) * kHeadDim + i];
+      o += sc * reinterpret_cast<const float*>(dyn_s + w * region_words)[hd * kHeadDim + i];
       l += sc * comb_l[w][hd];
     }
     const int64_t p = (bh * n_splits + s) * G + hd;
@@ -648,57 +707,69 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(
   const int n_groups = (n_splits + kGroup - 1) / kGroup;
   const int gsize = n_splits - grp * kGroup < kGroup ? n_splits - grp * kGroup : kGroup;
   unsigned* cnt = counters + bh * (kMaxGroups + 1);
-  float* mw_s = reinterpret_cast<float*>(kr_dyn);   // merge scratch: 2 x [kGroup][G] + 2 x [G]
+  float* mw_s = reinterpret_cast<float*>(dyn_s);   // merge scratch: 2 x [kGroup][G] + 2 x [G]
   if (!arrive(cnt + grp, static_cast<unsigned>(gsize), &flag_s)) return;
   {
     const int64_t src = (bh * n_splits + grp * kGroup) * G;
     if (n_groups == 1) {
-      merge_level<G>(part_o + src * kHeadDim, part_ml + src * 2, gsize, mw_s, tid,
-                     out + (static_cast<int64_t>(b) * n_q + h * G) * kHeadDim, nullptr, true);
+      merge_level<G, NT>(part_o + src * kHeadDim, part_ml + src * 2, gsize, mw_s, tid,
+                         out + (static_cast<int64_t>(b) * n_q + h * G) * kHeadDim, nullptr, true);
       if (tid == 0) __hip_atomic_store(cnt + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return;
     }
     const int64_t dst = (bh * kMaxGroups + grp) * G;
-    merge_level<G>(part_o + src * kHeadDim, part_ml + src * 2, gsize, mw_s, tid,
-                   gpart_o + dst * kHeadDim, gpart_ml + dst * 2, false);
+    merge_level<G, NT>(part_o + src * kHeadDim, part_ml + src * 2, gsize, mw_s, tid,
+                       gpart_o + dst * kHeadDim, gpart_ml + dst * 2, false);
   }
   if (tid == 0) __hip_atomic_store(cnt + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (!arrive(cnt + kMaxGroups, static_cast<unsigned>(n_groups), &flag_s)) return;
   {
     const int64_t src = bh * kMaxGroups * G;
-    merge_level<G>(gpart_o + src * kHeadDim, gpart_ml + src * 2, n_groups, mw_s, tid,
-                   out + (static_cast<int64_t>(b) * n_q + h * G) * kHeadDim, nullptr, true);
+    merge_level<G, NT>(gpart_o + src * kHeadDim, gpart_ml + src * 2, n_groups, mw_s, tid,
+                       out + (static_cast<int64_t>(b) * n_q + h * G) * kHeadDim, nullptr, true);
   }
   if (tid == 0) __hip_atomic_store(cnt + kMaxGroups, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int G, int VB>
-hipError_t launch_gv(kvq_cache* c, int layer, const void* q, int q_f32, float sigma, float* out,
-                     int S, hipStream_t stream) {
+template <int G, int VB, int W>
+hipError_t launch_gvw(kvq_cache* c, int layer, const void* q, int q_f32, float sigma, float* out,
+                      int S, hipStream_t stream) {
   const kvq_config& cfg = c->cfg;
   const int64_t len = c->len[layer];
   const int64_t n_tiles = (len + kVTile - 1) / kVTile;
   const int tps = static_cast<int>((n_tiles + S - 1) / S);
   dim3 grid(S, cfg.n_kv_heads, cfg.batch);
-  const size_t dyn = static_cast<size_t>(kWaves) * (c->k_words + 1) * kKS * sizeof(uint32_t);
+  // each wave's region: its K tile + zero row, or its softmax weights / merge share
+  int region = (c->k_words + 1) * kKS;
+  if (region < G * kHeadDim) region = G * kHeadDim;
+  if (region < 2 * kGroup * G + 2 * G) region = 2 * kGroup * G + 2 * G;
+  region = (region + 3) & ~3;   // 16-byte aligned regions
+  const size_t dyn = static_cast<size_t>(W) * region * sizeof(uint32_t);
   const Plan* plans = c->plans + static_cast<int64_t>(layer) * cfg.n_kv_heads;
   const bool nf = cfg.codec == KVQ_CODEC_NF16_B256;
   if constexpr (VB == 4) {
     if (nf) {
-      hipLaunchKernelGGL((decode_mfma<G, 4, true>), grid, dim3(256), dyn, stream, q, q_f32, sigma, len,
-                         cfg.n_kv_heads, c->cap, tps, plans, c->tables, layer_k_codes(c, layer),
+      hipLaunchKernelGGL((decode_mfma<G, 4, true, W>), grid, dim3(64 * W), dyn, stream, q, q_f32, sigma,
+                         len, cfg.n_kv_heads, c->cap, tps, plans, c->tables, layer_k_codes(c, layer),
                          layer_v_codes(c, layer), layer_k_scales(c, layer), layer_v_scales(c, layer),
-                         c->k_words, c->n_nf_blocks, S, c->part_o, c->part_ml, c->gpart_o, c->gpart_ml,
-                         c->split_counters, out);
+                         c->k_words, c->n_nf_blocks, S, region, c->part_o, c->part_ml, c->gpart_o,
+                         c->gpart_ml, c->split_counters, out);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((decode_mfma<G, VB, false>), grid, dim3(256), dyn, stream, q, q_f32, sigma, len,
-                     cfg.n_kv_heads, c->cap, tps, plans, c->tables, layer_k_codes(c, layer),
+  hipLaunchKernelGGL((decode_mfma<G, VB, false, W>), grid, dim3(64 * W), dyn, stream, q, q_f32, sigma,
+                     len, cfg.n_kv_heads, c->cap, tps, plans, c->tables, layer_k_codes(c, layer),
                      layer_v_codes(c, layer), layer_k_scales(c, layer), layer_v_scales(c, layer),
-                     c->k_words, c->n_nf_blocks, S, c->part_o, c->part_ml, c->gpart_o, c->gpart_ml,
-                     c->split_counters, out);
+                     c->k_words, c->n_nf_blocks, S, region, c->part_o, c->part_ml, c->gpart_o,
+                     c->gpart_ml, c->split_counters, out);
   return hipGetLastError();
+}
+
+template <int G, int VB>
+hipError_t launch_gv(kvq_cache* c, int layer, const void* q, int q_f32, float sigma, float* out,
+                     int S, hipStream_t stream) {
+  if (decode_waves(c) == 8) return launch_gvw<G, VB, 8>(c, layer, q, q_f32, sigma, out, S, stream);
+  return launch_gvw<G, VB, 4>(c, layer, q, q_f32, sigma, out, S, stream);
 }
 
 template <int G>

@@ -9,11 +9,12 @@ hipError_t launch_decode_mfma_g4(kvq_cache*, int, const void*, int, float, float
 hipError_t launch_decode_mfma_g8(kvq_cache*, int, const void*, int, float, float*, int, hipStream_t);
 
 int auto_splits_mfma(const kvq_cache* c, int64_t len) {
-  // one workgroup (4 waves, one per SIMD) per compute unit over (splits x KV heads x
-  // sequences), and at least one 128-token tile per wave
+  // one workgroup per compute unit over (splits x KV heads x sequences), and at least one
+  // 128-token tile per wave
   const int64_t n_tiles = (len + kVTile - 1) / kVTile;
   const int64_t units = static_cast<int64_t>(c->cfg.batch) * c->cfg.n_kv_heads;
-  int64_t S = (n_tiles + 3) / 4;
+  const int W = decode_waves(c);
+  int64_t S = (n_tiles + W - 1) / W;
   const int64_t want = (256 + units - 1) / units;
   if (S > want) S = want;
   if (S > c->max_splits) S = c->max_splits;

@@ -100,6 +100,10 @@ hipError_t launch_decode_mfma(kvq_cache* c, int layer, const void* q, int dtype,
                               float* out, int n_splits, hipStream_t stream);
 int auto_splits_mfma(const kvq_cache* c, int64_t len);
 
+// Waves per decode workgroup: two per SIMD when every wave's staged K tile fits in LDS next to
+// the lookup tables (rows of at most 16 words), else one per SIMD.
+inline int decode_waves(const kvq_cache* c) { return c->k_words <= 16 ? 8 : 4; }
+
 // Offsets of one layer's storage.
 inline uint32_t* layer_k_codes(kvq_cache* c, int layer) {
   return reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(c->k_codes) + c->k_codes_layer * layer);
