@@ -45,37 +45,41 @@ namespace kvq {
 namespace mfma {
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef __attribute__((address_space(1))) void* glb_ptr;
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr int kGroup = 16;        // splits merged per first-level merger
 constexpr int kMaxGroups = 16;    // so at most kGroup * kMaxGroups = 256 splits
 constexpr int kKS = 144;          // LDS row stride (words) of a staged K tile: 128 tokens + 16
+constexpr int kPS = 136;          // LDS row stride (halves) of the softmax weights: 128 + 8
+constexpr int kOS = 10;           // LDS stride (floats) per dim of a wave's merge share: G <= 8, + 2
+constexpr int kAS = 40;           // LDS row stride (halves) of the query operand: 32 + 8
 // LDS table region (bytes).  Pair tables hold fp16x2 (CB_w[c0], CB_w[c1]) at index c0 | c1 << w.
-// Widths 3 and 4 are replicated 32 times so that lane l reads copy l % 32 and random
-// lookups never collide in a bank: entry p of copy k sits at base + (p << 7) + 4 k.  Widths 5
-// and 6 are single copies (entry p at base + (p << 2)), built per workgroup when the plan
-// uses them.  The prebuilt image holds the pair tables of widths 1..4 and the single tables
-// of widths 1..8.  Every base is a multiple of its table's extent, so an entry address is
-// "(p << shift) | base".
-constexpr int kPair6Base = 0;          // 16 KB
+// Random lookups into the larger tables would collide in LDS banks, so they are replicated:
+// the width-4 table 16 times (entry p of copy k at (p << 6) + 4 k, lane l reads copy l % 16)
+// and the width-3 table 32 times (entry p of copy k at (p << 7) + 4 k, lane l reads copy
+// l % 32).  The width-5 table is a single copy (entry p at p << 2), built per workgroup when
+// the plan uses it.  The prebuilt image holds the pair tables of widths 1..4 and the single
+// tables of widths 1..8.  Every base is a multiple of its table's extent, so an entry address
+// is "(p << shift) | copy offset | base".  Blocks of 6..8 bits use two single lookups.
+constexpr int kRep4Base = 0;           // 16 KB
 constexpr int kRep3Base = 16384;       // 8 KB
 constexpr int kPair5Base = 24576;      // 4 KB
 constexpr int kImageBase = 28672;      // 2.5 KB
-constexpr int kRep4Base = 32768;       // 32 KB
-constexpr int kTableRegion = 65536;
+constexpr int kTableRegion = kImageBase + kLdsTableBytes;
 
-// Lookup parameters of a pair of width w: base (without the lane's copy offset) | replicated
-// << 16 | extract width << 24.  Widths 7 and 8 use two single lookups; their pair lookup is
-// kept inside the width-6 table and its result replaced.
+// Lookup parameters of a pair of width w: base (without the lane's copy offset) | copy kind
+// << 16 (0 single, 1 sixteen copies, 2 thirty-two copies) | extract width << 24.  For widths of
+// 6..8 the pair lookup stays inside the width-5 table and its result is replaced.
 __device__ inline uint32_t pair_lookup_params(uint32_t w) {
-  uint32_t base, rep = 0u;
-  if (w == 4u) { base = kRep4Base; rep = 1u; }
-  else if (w == 3u) { base = kRep3Base; rep = 1u; }
-  else if (w == 5u) base = kPair5Base;
-  else if (w >= 6u) base = kPair6Base;
+  uint32_t base, kind = 0u;
+  if (w == 4u) { base = kRep4Base; kind = 1u; }
+  else if (w == 3u) { base = kRep3Base; kind = 2u; }
+  else if (w >= 5u) base = kPair5Base;
   else base = kImageBase + static_cast<uint32_t>(pair_table_base(static_cast<int>(w)));
-  const uint32_t bw = w <= 6u ? 2u * w : 12u;
-  return base | (rep << 16) | (bw << 24);
+  const uint32_t bw = w <= 5u ? 2u * w : 10u;
+  return base | (kind << 16) | (bw << 24);
 }
 
 __device__ inline float half_bits_to_float(uint16_t h) { return __half2float(__ushort_as_half(h)); }
@@ -140,7 +144,8 @@ __device__ __attribute__((always_inline)) inline bool arrive(unsigned* counter, 
 }
 
 // fp16 pair of V codes e, e+1 (e even) of a 32-code segment held in S[0..VB) (S[VB] is a
-// zero word).  `tab` is the table region, `lb` the lane's replica offset (lane % 32) * 4.
+// zero word).  `tab` is the table region, `lb` the lane's replica offset (lane % 32) * 4 (the
+// sixteen-copy table uses its low six bits).
 template <int VB>
 __device__ inline uint32_t v_pair(const uint32_t* S, int e, const char* tab, uint32_t lb) {
   if constexpr (VB <= 4) {
@@ -148,8 +153,10 @@ __device__ inline uint32_t v_pair(const uint32_t* S, int e, const char* tab, uin
     uint32_t code;
     if (sh + 2 * VB <= 32) code = __builtin_amdgcn_ubfe(S[w0], sh, 2 * VB);
     else code = __builtin_amdgcn_ubfe(__builtin_amdgcn_alignbit(S[w0 + 1], S[w0], sh), 0, 2 * VB);
-    if constexpr (VB >= 3) {
-      return lds_u32(tab, (code << 7) | lb | (VB == 4 ? kRep4Base : kRep3Base));
+    if constexpr (VB == 4) {
+      return lds_u32(tab, (code << 6) | (lb & 63u) | kRep4Base);
+    } else if constexpr (VB == 3) {
+      return lds_u32(tab, (code << 7) | lb | kRep3Base);
     } else {
       return lds_u32(tab + kImageBase, (code << 2) | static_cast<uint32_t>(pair_table_base(VB)));
     }
@@ -244,7 +251,7 @@ struct KChunk {
 };
 
 __device__ __attribute__((always_inline)) inline KChunk k_chunk_params(
-    int c, int g, int n, const uint32_t* pd_s, const uint32_t* px_s, const _Float16 (*a_s)[16][32],
+    int c, int g, int n, const uint32_t* pd_s, const uint32_t* px_s, const _Float16 (*a_s)[16][kAS],
     uint32_t lane_copy, const uint32_t* kr) {
   KChunk k;
   k.aq = *reinterpret_cast<const h8*>(&a_s[c][n][8 * g]);
@@ -256,9 +263,9 @@ __device__ __attribute__((always_inline)) inline KChunk k_chunk_params(
   for (int p = 0; p < 4; ++p) {
     k.wp[p] = d4[p] >> 16;
     k.bw[p] = x4[p] >> 24;
-    const uint32_t rep = (x4[p] >> 16) & 1u;
-    k.pb[p] = (x4[p] & 0xFFFFu) | (rep ? lane_copy : 0u);
-    k.ps[p] = rep ? 7u : 2u;
+    const uint32_t kind = (x4[p] >> 16) & 3u;
+    k.pb[p] = (x4[p] & 0xFFFFu) | (kind == 2u ? lane_copy : kind == 1u ? (lane_copy & 63u) : 0u);
+    k.ps[p] = kind == 2u ? 7u : kind == 1u ? 6u : 2u;
   }
   const uint32_t offA = d4[0] & 0xFFFFu, offB = d4[2] & 0xFFFFu;
   k.shA = offA & 31u;
@@ -289,7 +296,7 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     int tiles_per_split, const Plan* __restrict__ plans, const Tables* __restrict__ tabg,
     const uint32_t* __restrict__ kc, const uint32_t* __restrict__ vc, const uint16_t* __restrict__ ks,
     const uint16_t* __restrict__ vs, int k_words, int n_nf, int n_splits, int region_words,
-    float* __restrict__ part_o, float* __restrict__ part_ml, float* __restrict__ gpart_o,
+    int v_early, int v_off, float* __restrict__ part_o, float* __restrict__ part_ml, float* __restrict__ gpart_o,
     float* __restrict__ gpart_ml, unsigned* __restrict__ counters, float* __restrict__ out) {
   constexpr int NT = 64 * W;
   constexpr bool kPipe = W == 4;                      // one wave per SIMD: prefetch and pipeline
@@ -300,22 +307,24 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int n = lane & 15, g = lane >> 4;             // MFMA column and row group of this lane
-  const bool setup = tid < 256;                       // the first 256 threads do the set-up
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int n_q = n_kv * G;
   const int64_t bh = static_cast<int64_t>(b) * n_kv + h;
 
   __shared__ __attribute__((aligned(16))) char tab_s[kTableRegion];
-  __shared__ __attribute__((aligned(16))) _Float16 a_s[4][16][32];
+  __shared__ __attribute__((aligned(16))) _Float16 a_s[4][16][kAS];
   __shared__ uint8_t fdim_s[kHeadDim];
   __shared__ __attribute__((aligned(16))) uint32_t pd_s[kBlocks];
   __shared__ __attribute__((aligned(16))) uint32_t px_s[kBlocks];
   __shared__ float comb_m[W][G], comb_l[W][G];
   __shared__ float alpha_s[W][G];
   __shared__ bool flag_s;
+  __shared__ uint64_t wide_s;
+  __shared__ float sc_s[W][G], ms_s[G], ls_s[G];
   extern __shared__ __attribute__((aligned(16))) uint32_t dyn_s[];   // [W][region_words]
   uint32_t* kr = dyn_s + wave * region_words;                         // [k_words + 1][kKS]
-  _Float16* pw = reinterpret_cast<_Float16*>(kr);                     // [PCOLS][128], after keys
+  _Float16* pw = reinterpret_cast<_Float16*>(kr);                     // [PCOLS][kPS], after keys
+  uint32_t* vbuf = kr + v_off;                                        // [512][VB] V tile
   float (*qs_s)[kHeadDim] = reinterpret_cast<float (*)[kHeadDim]>(dyn_s);   // set-up only
 
   const int64_t n_tiles = (len + kVTile - 1) / kVTile;
@@ -323,37 +332,38 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   const int64_t t_end = t_begin + tiles_per_split < n_tiles ? t_begin + tiles_per_split : n_tiles;
   const Plan* P = plans + h;
 
-  // ---- set-up loads first (small and shared by every workgroup), then the first tile's ----
+  // ---- set-up loads first (small and shared by every workgroup), then the first tile's.
+  //      Waves 0..3 do the set-up; a wave-uniform branch lets the others skip it. ----
+  const bool setup_wave = __builtin_amdgcn_readfirstlane(wave) < 4;
   const uint8_t* gimg = tabg->lds_image[NF ? 1 : 0];
-  uint4 timg = make_uint4(0u, 0u, 0u, 0u);
-  if (tid < kLdsTableBytes / 16) timg = reinterpret_cast<const uint4*>(gimg)[tid];
-  float qr[QPT], gr[QPT];
-#pragma unroll
-  for (int j = 0; j < QPT; ++j) {
-    const int k = tid + 256 * j;
-    qr[j] = gr[j] = 0.0f;
-    if (setup && k < G * kHeadDim) {
-      const int64_t qi = (static_cast<int64_t>(b) * n_q + h * G) * kHeadDim + k;
-      qr[j] = q_f32 ? static_cast<const float*>(qv)[qi] : __half2float(static_cast<const __half*>(qv)[qi]);
-      gr[j] = P->g[k % kHeadDim];
-    }
-  }
-  const uint32_t fd_r = tid < kHeadDim ? P->fdim[tid] : 0u;
-  const uint32_t pd_r = P->pdesc[lane];   // descriptor of pair `lane` (every wave)
   const int n_pairs = __builtin_amdgcn_readfirstlane(P->n_fields) >> 1;
-  // sources of the per-workgroup pair tables (see below); set-up threads t < 256 only
-  const int st = tid & 255;
-  const uint32_t rep4v = reinterpret_cast<const uint32_t*>(gimg + pair_table_base(4))[st];
-  const uint32_t rep3v = reinterpret_cast<const uint32_t*>(gimg + pair_table_base(3))[st & 63];
-  const uint16_t* cb6 = reinterpret_cast<const uint16_t*>(gimg + single_table_base(6));
-  const uint16_t* cb5 = reinterpret_cast<const uint16_t*>(gimg + single_table_base(5));
-  const uint32_t hi6 = cb6[st >> 2], hi5 = cb5[st >> 3];
-  const uint4 lo6a = reinterpret_cast<const uint4*>(cb6 + ((16 * st) & 63))[0];
-  const uint4 lo6b = reinterpret_cast<const uint4*>(cb6 + ((16 * st) & 63))[1];
-  const uint2 lo5 = *reinterpret_cast<const uint2*>(cb5 + ((4 * st) & 31));
+  uint4 timg = make_uint4(0u, 0u, 0u, 0u);
+  float qr[QPT], gr[QPT];
+  uint32_t fd_r = 0u, pd_r = 0u, rep4v = 0u, rep3v = 0u, hi5 = 0u;
+  uint2 lo5 = make_uint2(0u, 0u);
+  if (setup_wave) {
+    if (tid < kLdsTableBytes / 16) timg = reinterpret_cast<const uint4*>(gimg)[tid];
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) {
+      const int k = tid + 256 * j;
+      qr[j] = gr[j] = 0.0f;
+      if (k < G * kHeadDim) {
+        const int64_t qi = (static_cast<int64_t>(b) * n_q + h * G) * kHeadDim + k;
+        qr[j] = q_f32 ? static_cast<const float*>(qv)[qi] : __half2float(static_cast<const __half*>(qv)[qi]);
+        gr[j] = P->g[k % kHeadDim];
+      }
+    }
+    if (tid < kHeadDim) fd_r = P->fdim[tid];
+    pd_r = P->pdesc[lane];   // descriptor of pair `lane`
+    // sources of the per-workgroup pair tables (see below)
+    rep4v = reinterpret_cast<const uint32_t*>(gimg + pair_table_base(4))[tid];
+    rep3v = reinterpret_cast<const uint32_t*>(gimg + pair_table_base(3))[tid & 63];
+    const uint16_t* cb5 = reinterpret_cast<const uint16_t*>(gimg + single_table_base(5));
+    hi5 = cb5[tid >> 3];
+    lo5 = *reinterpret_cast<const uint2*>(cb5 + ((4 * tid) & 31));
+  }
 
   // K rows of tokens lane and lane + 64 (first 16 words), scales of tokens 16 tg + n, V segments
-  uint32_t vseg[8][VB + 2];
   uint4 ka[4], kb2[4];
   float skr[8], svr[8];
   auto load_k = [&](int64_t tile) {
@@ -381,69 +391,66 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
       }
     }
   };
-  auto load_v = [&](int64_t tile) {
+  // the V tile (512 segments x VB words, contiguous in HBM) goes straight into this wave's LDS
+  // area: 2 VB copies of 64 lanes x 16 bytes, waited for with s_waitcnt vmcnt(0) before use
+  auto dma_v = [&](int64_t tile) {
     const uint32_t* vt = vc + (bh * (cap / kVTile) + tile) * (kVTile * KWV);
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-#pragma unroll
-      for (int k = 0; k < VB; ++k) vseg[dt][k + 1] = vt[(dt * 64 + lane) * VB + k];
-    }
+    for (int i = 0; i < 2 * VB; ++i)
+      __builtin_amdgcn_global_load_lds((glb_ptr)(vt + 256 * i + 4 * lane), (lds_ptr)(vbuf + 256 * i), 16, 0, 0);
   };
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt) vseg[dt][0] = vseg[dt][VB + 1] = 0u;
   if (t_begin + wave < t_end) {
     load_k(t_begin + wave);
     load_scales(t_begin + wave);
-    if constexpr (kPipe) load_v(t_begin + wave);
+    if (v_early) dma_v(t_begin + wave);
   }
 
   // ---- set-up: tables, scaled query, field dims and pair descriptors into LDS ----
-  if (tid < kLdsTableBytes / 16) reinterpret_cast<uint4*>(tab_s + kImageBase)[tid] = timg;
+  if (setup_wave) {
+    if (tid < kLdsTableBytes / 16) reinterpret_cast<uint4*>(tab_s + kImageBase)[tid] = timg;
 #pragma unroll
-  for (int j = 0; j < QPT; ++j) {
-    const int k = tid + 256 * j;
-    if (setup && k < G * kHeadDim) qs_s[k / kHeadDim][k % kHeadDim] = qr[j] * gr[j] * sigma;
-  }
-  if (tid < kHeadDim) fdim_s[tid] = static_cast<uint8_t>(fd_r);
-  if (tid < kBlocks) {
-    pd_s[tid] = pd_r;
-    px_s[tid] = pair_lookup_params(pd_r >> 16);
-  }
-  // 32-fold replicas of the width-4 and width-3 pair tables: thread t writes all copies of
-  // entry t (rotating the 16-byte pieces over the lanes spreads the banks)
-  if (setup) {
-    const uint4 v4 = make_uint4(rep4v, rep4v, rep4v, rep4v), v3 = make_uint4(rep3v, rep3v, rep3v, rep3v);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int jj = (j + tid) & 7;
-      *reinterpret_cast<uint4*>(tab_s + kRep4Base + (tid << 7) + 16 * jj) = v4;
-      if (tid < 64) *reinterpret_cast<uint4*>(tab_s + kRep3Base + (tid << 7) + 16 * jj) = v3;
+    for (int j = 0; j < QPT; ++j) {
+      const int k = tid + 256 * j;
+      if (k < G * kHeadDim) qs_s[k / kHeadDim][k % kHeadDim] = qr[j] * gr[j] * sigma;
     }
-  }
-  // pair tables of widths 5 and 6 when the plan stores such blocks: entry (c1 << w) | c0 holds
-  // (CB_w[c0], CB_w[c1]); thread t fills 16 (w = 6) or 4 (w = 5) consecutive c0 of one c1
-  const uint64_t uses5 = __ballot((pd_r >> 16) == 5u), uses6 = __ballot((pd_r >> 16) == 6u);
-  const uint64_t uses78 = __ballot((pd_r >> 16) >= 7u);
-  if (uses6 && setup) {
-    const uint32_t hi = hi6 << 16;
-    const uint32_t lo[8] = {lo6a.x, lo6a.y, lo6a.z, lo6a.w, lo6b.x, lo6b.y, lo6b.z, lo6b.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint4 v = make_uint4((lo[2 * q] & 0xFFFFu) | hi, (lo[2 * q] >> 16) | hi,
-                                 (lo[2 * q + 1] & 0xFFFFu) | hi, (lo[2 * q + 1] >> 16) | hi);
-      *reinterpret_cast<uint4*>(tab_s + kPair6Base + 4 * (16 * tid + 4 * q)) = v;
+    if (tid < kHeadDim) fdim_s[tid] = static_cast<uint8_t>(fd_r);
+    if (tid < kBlocks) {
+      pd_s[tid] = pd_r;
+      px_s[tid] = pair_lookup_params(pd_r >> 16);
     }
-  }
-  if (uses5 && setup) {
-    const uint32_t hi = hi5 << 16;
-    const uint4 v = make_uint4((lo5.x & 0xFFFFu) | hi, (lo5.x >> 16) | hi, (lo5.y & 0xFFFFu) | hi, (lo5.y >> 16) | hi);
-    *reinterpret_cast<uint4*>(tab_s + kPair5Base + 4 * (4 * tid)) = v;
+    // replicas of the width-4 (16 copies) and width-3 (32 copies) pair tables: thread t writes
+    // all copies of entry t (rotating the 16-byte pieces over the lanes spreads the banks)
+    {
+      const uint4 v4 = make_uint4(rep4v, rep4v, rep4v, rep4v), v3 = make_uint4(rep3v, rep3v, rep3v, rep3v);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int jj = (j + tid) & 3;
+        *reinterpret_cast<uint4*>(tab_s + kRep4Base + (tid << 6) + 16 * jj) = v4;
+      }
+      if (tid < 64) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int jj = (j + tid) & 7;
+          *reinterpret_cast<uint4*>(tab_s + kRep3Base + (tid << 7) + 16 * jj) = v3;
+        }
+      }
+    }
+    // pair table of width 5 when the plan stores such blocks: entry (c1 << 5) | c0 holds
+    // (CB_5[c0], CB_5[c1]); thread t fills 4 consecutive c0 of one c1
+    const uint64_t uses5 = __ballot((pd_r >> 16) == 5u);
+    const uint64_t wide = __ballot((pd_r >> 16) >= 6u);
+    if (tid == 0) wide_s = wide;
+    if (uses5) {
+      const uint32_t hi = hi5 << 16;
+      const uint4 v = make_uint4((lo5.x & 0xFFFFu) | hi, (lo5.x >> 16) | hi, (lo5.y & 0xFFFFu) | hi, (lo5.y >> 16) | hi);
+      *reinterpret_cast<uint4*>(tab_s + kPair5Base + 4 * (4 * tid)) = v;
+    }
   }
   __syncthreads();
   // query operand of the key product: a_s[c][m][k] = hi (m even) or lo (m odd) fp16 part of
   // q'[m / 2][dim of field 32 c + k]; rows of heads >= G and fields past the stored ones are 0.
   // Thread t < 256 fills field t % 128 for heads t / 128, t / 128 + 2, ...
-  if (setup) {
+  if (setup_wave) {
     const int f = tid & 127, c = f >> 5, k = f & 31;
     const bool live = f < 2 * n_pairs;
     const int dim = fdim_s[f];
@@ -458,6 +465,7 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   }
   const uint32_t lb = (lane & 31u) << 2;   // this lane's replica offset
   __syncthreads();
+  const uint64_t uses_wide = wide_s;       // pairs (plan ranks) with blocks of 6..8 bits
 
   // ---- per-wave state: lane (n, g) keeps heads 2g, 2g + 1 ----
   const int h0 = 2 * g, h1 = 2 * g + 1;
@@ -474,6 +482,7 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
       if (tile != t_begin + wave) {   // later tiles: loaded here (the other wave hides the wait)
         load_k(tile);
         load_scales(tile);
+        if (v_early) dma_v(tile);
       }
     }
     // -- stage the K rows in LDS word-major (kr[d * kKS + tau] = word d of token tau), then a
@@ -517,12 +526,12 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
         u[tg][2] = lds_u32(tab_s, (__builtin_amdgcn_ubfe(xb, 0u, cur.bw[2]) << cur.ps[2]) | cur.pb[2]);
         u[tg][3] = lds_u32(tab_s, (__builtin_amdgcn_ubfe(xb, cur.rel3, cur.bw[3]) << cur.ps[3]) | cur.pb[3]);
       }
-      if ((uses78 >> (16 * c)) & 0xFFFFull) {
-        // blocks of 7 or 8 bits: two single lookups (lanes whose pair is narrower skip)
+      if ((uses_wide >> (16 * c)) & 0xFFFFull) {
+        // blocks of 6..8 bits: two single lookups (lanes whose pair is narrower skip)
         const char* tabi = tab_s + kImageBase;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          if (cur.wp[p] >= 7u) {
+          if (cur.wp[p] >= 6u) {
             const uint32_t sb = static_cast<uint32_t>(kLdsTableBytes) - (4u << cur.wp[p]);
             const uint32_t rel = (p & 1) ? (p == 1 ? cur.rel1 : cur.rel3) : 0u;
 #pragma unroll
@@ -570,8 +579,8 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
         k_products(cur, u);
       }
     }
-    wave_sync();   // the key rows are read; the area takes the softmax weights next
-    if constexpr (!kPipe) load_v(tile);   // V segments are needed only after the softmax
+    wave_sync();   // the key rows are read; the area takes the softmax weights (and V) next
+    if (!v_early) dma_v(tile);
 
     // -- online softmax: lane (n, g) holds heads 2g and 2g + 1 of tokens 16 tg + n --
     float L0[8], L1[8];
@@ -605,12 +614,12 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
       const _Float16 q0h = static_cast<_Float16>(q0), q1h = static_cast<_Float16>(q1);
       const int t = 16 * tg + n;
       if (vh0) {
-        pw[h0 * kVTile + t] = q0h;
-        pw[(G + h0) * kVTile + t] = static_cast<_Float16>(q0 - static_cast<float>(q0h));
+        pw[h0 * kPS + t] = q0h;
+        pw[(G + h0) * kPS + t] = static_cast<_Float16>(q0 - static_cast<float>(q0h));
       }
       if (vh1) {
-        pw[h1 * kVTile + t] = q1h;
-        pw[(G + h1) * kVTile + t] = static_cast<_Float16>(q1 - static_cast<float>(q1h));
+        pw[h1 * kPS + t] = q1h;
+        pw[(G + h1) * kPS + t] = static_cast<_Float16>(q1 - static_cast<float>(q1h));
       }
     }
     if (n == 0) {
@@ -629,11 +638,20 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
       for (int dt = 0; dt < 8; ++dt) oacc[dt] *= al;
     }
     // -- values: O^T[dim][col] += V^T[dim][tok] P^T[tok][col] over 4 chunks of 32 tokens --
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the V tile copy has landed
+    wave_sync();
+    uint32_t vseg[8][VB + 2];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      vseg[dt][0] = vseg[dt][VB + 1] = 0u;
+#pragma unroll
+      for (int k = 0; k < VB; ++k) vseg[dt][k + 1] = vbuf[(dt * 64 + lane) * VB + k];
+    }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       h8 bp;
       if (n < PCOLS) {
-        bp = *reinterpret_cast<const h8*>(&pw[n * kVTile + 32 * g + 8 * c]);
+        bp = *reinterpret_cast<const h8*>(&pw[n * kPS + 32 * g + 8 * c]);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) bp[e] = static_cast<_Float16>(0.0f);
@@ -650,7 +668,7 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     }
     wave_sync();
     if constexpr (kPipe) {
-      if (next < t_end) load_v(next);
+      if (v_early && next < t_end) dma_v(next);
     }
   }
 
@@ -668,7 +686,8 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     }
   }
   // O^T layout: lane holds rows 4 g + r of dim slice dt for column n; add the lo column
-  // (n + G) into the hi column (n), into this wave's region as [G][128] floats
+  // (n + G) into the hi column (n), into this wave's region as [128][kOS] floats (the padded
+  // stride keeps the 32 writing lanes on distinct banks)
   float* ow = reinterpret_cast<float*>(kr);
   __syncthreads();
 #pragma unroll
@@ -676,29 +695,38 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float other = __shfl(oacc[dt][r], (lane & ~15) | ((n + G) & 15), 64);
-      if (n < G) ow[n * kHeadDim + dt * 16 + 4 * g + r] = oacc[dt][r] + other;
+      if (n < G) ow[(dt * 16 + 4 * g + r) * kOS + n] = oacc[dt][r] + other;
     }
+  }
+  __syncthreads();
+  // scale of each wave's share per head: 2^(m_w - max_w m_w), 0 for waves without tokens
+  if (tid < G) {
+    float ms = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < W; ++w) ms = fmaxf(ms, comb_m[w][tid]);
+    float l = 0.0f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      const float mw = comb_m[w][tid];
+      const float sc = mw == -INFINITY ? 0.0f : exp2f(mw - ms);
+      sc_s[w][tid] = sc;
+      l += sc * comb_l[w][tid];
+    }
+    ms_s[tid] = ms;
+    ls_s[tid] = l;
   }
   __syncthreads();
   for (int idx = tid; idx < G * kHeadDim; idx += NT) {
     const int hd = idx / kHeadDim, i = idx % kHeadDim;
-    float ms = -INFINITY;
+    float o = 0.0f;
 #pragma unroll
-    for (int w = 0; w < W; ++w) ms = fmaxf(ms, comb_m[w][hd]);
-    float o = 0.0f, l = 0.0f;
-#pragma unroll
-    for (int w = 0; w < W; ++w) {
-      const float mw = comb_m[w][hd];
-      if (mw == -INFINITY) continue;
-      const float sc = exp2f(mw - ms);
-      o += sc * reinterpret_cast<const float*>(dyn_s + w * region_words)[hd * kHeadDim + i];
-      l += sc * comb_l[w][hd];
-    }
+    for (int w = 0; w < W; ++w)
+      o += sc_s[w][hd] * reinterpret_cast<const float*>(dyn_s + w * region_words)[i * kOS + hd];
     const int64_t p = (bh * n_splits + s) * G + hd;
     st_coh(part_o + p * kHeadDim + i, o);
     if (i == 0) {
-      st_coh(part_ml + p * 2 + 0, ms);
-      st_coh(part_ml + p * 2 + 1, l);
+      st_coh(part_ml + p * 2 + 0, ms_s[hd]);
+      st_coh(part_ml + p * 2 + 1, ls_s[hd]);
     }
   }
 
@@ -733,18 +761,13 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
 
 template <int G, int VB, int W>
 hipError_t launch_gvw(kvq_cache* c, int layer, const void* q, int q_f32, float sigma, float* out,
-                      int S, hipStream_t stream) {
+                      int S, const DecodeShape& sh, hipStream_t stream) {
   const kvq_config& cfg = c->cfg;
   const int64_t len = c->len[layer];
   const int64_t n_tiles = (len + kVTile - 1) / kVTile;
   const int tps = static_cast<int>((n_tiles + S - 1) / S);
   dim3 grid(S, cfg.n_kv_heads, cfg.batch);
-  // each wave's region: its K tile + zero row, or its softmax weights / merge share
-  int region = (c->k_words + 1) * kKS;
-  if (region < G * kHeadDim) region = G * kHeadDim;
-  if (region < 2 * kGroup * G + 2 * G) region = 2 * kGroup * G + 2 * G;
-  region = (region + 3) & ~3;   // 16-byte aligned regions
-  const size_t dyn = static_cast<size_t>(W) * region * sizeof(uint32_t);
+  const size_t dyn = static_cast<size_t>(W) * sh.region_words * sizeof(uint32_t);
   const Plan* plans = c->plans + static_cast<int64_t>(layer) * cfg.n_kv_heads;
   const bool nf = cfg.codec == KVQ_CODEC_NF16_B256;
   if constexpr (VB == 4) {
@@ -752,24 +775,25 @@ hipError_t launch_gvw(kvq_cache* c, int layer, const void* q, int q_f32, float s
       hipLaunchKernelGGL((decode_mfma<G, 4, true, W>), grid, dim3(64 * W), dyn, stream, q, q_f32, sigma,
                          len, cfg.n_kv_heads, c->cap, tps, plans, c->tables, layer_k_codes(c, layer),
                          layer_v_codes(c, layer), layer_k_scales(c, layer), layer_v_scales(c, layer),
-                         c->k_words, c->n_nf_blocks, S, region, c->part_o, c->part_ml, c->gpart_o,
-                         c->gpart_ml, c->split_counters, out);
+                         c->k_words, c->n_nf_blocks, S, sh.region_words, sh.v_early, sh.v_off, c->part_o,
+                         c->part_ml, c->gpart_o, c->gpart_ml, c->split_counters, out);
       return hipGetLastError();
     }
   }
   hipLaunchKernelGGL((decode_mfma<G, VB, false, W>), grid, dim3(64 * W), dyn, stream, q, q_f32, sigma,
                      len, cfg.n_kv_heads, c->cap, tps, plans, c->tables, layer_k_codes(c, layer),
                      layer_v_codes(c, layer), layer_k_scales(c, layer), layer_v_scales(c, layer),
-                     c->k_words, c->n_nf_blocks, S, region, c->part_o, c->part_ml, c->gpart_o,
-                     c->gpart_ml, c->split_counters, out);
+                     c->k_words, c->n_nf_blocks, S, sh.region_words, sh.v_early, sh.v_off, c->part_o,
+                     c->part_ml, c->gpart_o, c->gpart_ml, c->split_counters, out);
   return hipGetLastError();
 }
 
 template <int G, int VB>
 hipError_t launch_gv(kvq_cache* c, int layer, const void* q, int q_f32, float sigma, float* out,
                      int S, hipStream_t stream) {
-  if (decode_waves(c) == 8) return launch_gvw<G, VB, 8>(c, layer, q, q_f32, sigma, out, S, stream);
-  return launch_gvw<G, VB, 4>(c, layer, q, q_f32, sigma, out, S, stream);
+  const DecodeShape sh = decode_shape(c);
+  if (sh.waves == 8) return launch_gvw<G, VB, 8>(c, layer, q, q_f32, sigma, out, S, sh, stream);
+  return launch_gvw<G, VB, 4>(c, layer, q, q_f32, sigma, out, S, sh, stream);
 }
 
 template <int G>

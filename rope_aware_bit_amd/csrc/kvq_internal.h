@@ -100,9 +100,33 @@ hipError_t launch_decode_mfma(kvq_cache* c, int layer, const void* q, int dtype,
                               float* out, int n_splits, hipStream_t stream);
 int auto_splits_mfma(const kvq_cache* c, int64_t len);
 
-// Waves per decode workgroup: two per SIMD when every wave's staged K tile fits in LDS next to
-// the lookup tables (rows of at most 16 words), else one per SIMD.
-inline int decode_waves(const kvq_cache* c) { return c->k_words <= 16 ? 8 : 4; }
+// Launch shape of the decode kernel for a cache: waves per workgroup (8 = two per SIMD, or 4),
+// whether each wave's V tile has its own LDS area (copied at tile start) or reuses the K area
+// after the key product, the LDS words of each wave's region and the V area's offset in it.
+struct DecodeShape {
+  int waves, v_early, region_words, v_off;
+};
+inline DecodeShape decode_shape(const kvq_cache* c) {
+  constexpr int kKS = 144, kPS = 136, kOS = 10, kLds = 163840;
+  constexpr int kStaticBase = 28672 + 2560 + 4 * 16 * 40 * 2 + 128 + 2 * 64 * 4 + 64;
+  const int G = c->group;
+  const int vb = c->cfg.codec == KVQ_CODEC_NF16_B256 ? 4 : c->cfg.v_bits;
+  int kpart = (c->k_words + 1) * kKS;
+  if (kpart < G * kPS) kpart = G * kPS;
+  if (kpart < 128 * kOS) kpart = 128 * kOS;
+  if (kpart < G * 128) kpart = G * 128;
+  kpart = (kpart + 3) & ~3;
+  const int vwords = 512 * vb;
+  const int early = kpart + vwords;
+  int late = ((G * kPS + 3) & ~3) + vwords;
+  if (late < kpart) late = kpart;
+  for (int w : {8, 4}) {
+    const int stat = kStaticBase + 16 * w * G + 64 * G;
+    if (stat + 4 * w * early <= kLds) return {w, 1, early, kpart};
+  }
+  return {4, 0, late, (G * kPS + 3) & ~3};
+}
+inline int decode_waves(const kvq_cache* c) { return decode_shape(c).waves; }
 
 // Offsets of one layer's storage.
 inline uint32_t* layer_k_codes(kvq_cache* c, int layer) {
