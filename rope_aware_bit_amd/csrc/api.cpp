@@ -49,8 +49,7 @@ bool layer_ok(const kvq_cache* c, int32_t layer) {
 
 void free_device(kvq_cache* c) {
   void* ptrs[] = {c->k_codes, c->v_codes, c->k_scales, c->v_scales, c->plans,
-                  c->tables,  c->part_o,  c->part_ml,  c->energy_scratch, c->split_counters,
-                  c->gpart_o, c->gpart_ml};
+                  c->tables,  c->part_o,  c->part_ml,  c->energy_scratch, c->split_counters};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
 }
@@ -145,6 +144,7 @@ kvq_status kvq_cache_create(const kvq_config* cfg, kvq_cache** out) {
   c->max_splits = static_cast<int>(ms);
 
   hipError_t e = hipGetDevice(&c->device);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&c->n_cu, hipDeviceAttributeMultiprocessorCount, c->device);
   kvq_status st = e == hipSuccess ? KVQ_OK : hip_fail(e, "hipGetDevice");
   if (st == KVQ_OK) st = dev_alloc(reinterpret_cast<void**>(&c->k_codes), c->k_codes_layer * L, "K codes");
   if (st == KVQ_OK) st = dev_alloc(reinterpret_cast<void**>(&c->v_codes), c->v_codes_layer * L, "V codes");
@@ -157,14 +157,10 @@ kvq_status kvq_cache_create(const kvq_config* cfg, kvq_cache** out) {
   if (st == KVQ_OK)
     st = dev_alloc(reinterpret_cast<void**>(&c->part_ml), per_split / (kHeadDim + 2) * 2 * ms, "partials");
   if (st == KVQ_OK)
-    st = dev_alloc(reinterpret_cast<void**>(&c->gpart_o), per_split / (kHeadDim + 2) * kHeadDim * 16, "partials");
-  if (st == KVQ_OK)
-    st = dev_alloc(reinterpret_cast<void**>(&c->gpart_ml), per_split / (kHeadDim + 2) * 2 * 16, "partials");
-  if (st == KVQ_OK)
-    st = dev_alloc(reinterpret_cast<void**>(&c->split_counters), sizeof(unsigned) * B * H * 17, "counters");
+    st = dev_alloc(reinterpret_cast<void**>(&c->split_counters), sizeof(unsigned) * B * H, "counters");
   if (st == KVQ_OK) {
     const hipError_t es[] = {
-        hipMemset(c->split_counters, 0, sizeof(unsigned) * B * H * 17),
+        hipMemset(c->split_counters, 0, sizeof(unsigned) * B * H),
         hipMemset(c->k_codes, 0, c->k_codes_layer * L),
         hipMemset(c->v_codes, 0, c->v_codes_layer * L),
         hipMemset(c->k_scales, 0, c->k_scales_layer * L),

@@ -49,8 +49,8 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 typedef __attribute__((address_space(1))) void* glb_ptr;
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-constexpr int kGroup = 16;        // splits merged per first-level merger
-constexpr int kMaxGroups = 16;    // so at most kGroup * kMaxGroups = 256 splits
+constexpr int kMaxMergers = 64;   // workgroups that merge the splits of one (sequence, KV head)
+constexpr int kMaxPolls = 1 << 22;  // bound on a merger's wait for the other splits
 constexpr int kKS = 144;          // LDS row stride (words) of a staged K tile: 128 tokens + 16
 constexpr int kPS = 136;          // LDS row stride (halves) of the softmax weights: 128 + 8
 constexpr int kOS = 10;           // LDS stride (floats) per dim of a wave's merge share: G <= 8, + 2
@@ -69,17 +69,43 @@ constexpr int kPair5Base = 24576;      // 4 KB
 constexpr int kImageBase = 28672;      // 2.5 KB
 constexpr int kTableRegion = kImageBase + kLdsTableBytes;
 
-// Lookup parameters of a pair of width w: base (without the lane's copy offset) | copy kind
-// << 16 (0 single, 1 sixteen copies, 2 thirty-two copies) | extract width << 24.  For widths of
-// 6..8 the pair lookup stays inside the width-5 table and its result is replaced.
-__device__ inline uint32_t pair_lookup_params(uint32_t w) {
-  uint32_t base, kind = 0u;
-  if (w == 4u) { base = kRep4Base; kind = 1u; }
-  else if (w == 3u) { base = kRep3Base; kind = 2u; }
-  else if (w >= 5u) base = kPair5Base;
-  else base = kImageBase + static_cast<uint32_t>(pair_table_base(static_cast<int>(w)));
-  const uint32_t bw = w <= 5u ? 2u * w : 10u;
-  return base | (kind << 16) | (bw << 24);
+// Key-product parameters of one (chunk c, lane group g): the four pairs of plan ranks
+// 16 c + 4 g + p, p = 0..3, held in LDS as 24 words
+//   [0..3]  table base of pair p (with the part of the lane's replica offset fixed by g)
+//   [4..7]  mask applied to 4 n (the rest of the replica offset; 0 for single tables)
+//   [8..11] extract width (2 w; 10 for w >= 5, whose lookups are replaced)
+//   [12..15] left shift of the extracted code (2 single table, 6 sixteen copies, 32: 7)
+//   [16..19] bit shift of window A (pairs 0, 1) and B (pairs 2, 3); bit offset of pairs 1, 3
+//   [20..21] byte offset of the first word of windows A and B in a staged K tile
+constexpr int kParamWords = 24;
+__device__ inline void write_pair_params(uint32_t* kp, int r, uint32_t desc) {
+  const int c = r >> 4, g = (r >> 2) & 3, p = r & 3;
+  const uint32_t w = desc >> 16, off = desc & 0xFFFFu;
+  uint32_t base, mask = 0u, shift = 2u;
+  if (w == 4u) {
+    base = kRep4Base;
+    mask = 0x3Cu;
+    shift = 6u;
+  } else if (w == 3u) {
+    base = kRep3Base | (64u * (g & 1));   // lane & 31 = n + 16 (g & 1)
+    mask = 0x3Cu;
+    shift = 7u;
+  } else if (w >= 5u) {
+    base = kPair5Base;
+  } else {
+    base = kImageBase + static_cast<uint32_t>(pair_table_base(static_cast<int>(w)));
+  }
+  uint32_t* blk = kp + (4 * c + g) * kParamWords;
+  blk[p] = base;
+  blk[4 + p] = mask;
+  blk[8 + p] = w <= 5u ? 2u * w : 10u;
+  blk[12 + p] = shift;
+  if ((p & 1) == 0) {
+    const int k = p >> 1;   // window A or B
+    blk[16 + k] = off & 31u;
+    blk[18 + k] = 2u * w;
+    blk[20 + k] = (off >> 5) * kKS * 4u;
+  }
 }
 
 __device__ inline float half_bits_to_float(uint16_t h) { return __half2float(__ushort_as_half(h)); }
@@ -111,6 +137,24 @@ __device__ inline float row_sum16(float v) {
   return v;
 }
 
+// Max / sum over the 64 lanes of a wave (rows through DPP, then the four row results).
+__device__ inline float wave_max(float v) {
+  v = row_max16(v);
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+__device__ inline float wave_sum(float v) {
+  v = row_sum16(v);
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (a + b) + (c + d);
+}
+
 // Orders a wave's LDS writes before its later LDS reads of other lanes' data (LDS
 // instructions of one wave execute in issue order; this keeps the compiler from moving
 // them across).
@@ -126,21 +170,6 @@ __device__ inline void st_coh(float* p, float v) {
 }
 __device__ inline float ld_coh(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Count this workgroup in a merge counter after all of its partial stores have
-// completed; returns (in every thread) whether it was the last of `expected`.
-__device__ __attribute__((always_inline)) inline bool arrive(unsigned* counter, unsigned expected, bool* flag_s) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_s_waitcnt(0);   // all outstanding memory operations of this wave
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *flag_s = prev == expected - 1u;
-  }
-  __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  return *flag_s;
 }
 
 // fp16 pair of V codes e, e+1 (e even) of a 32-code segment held in S[0..VB) (S[VB] is a
@@ -170,121 +199,136 @@ __device__ inline uint32_t v_pair(const uint32_t* S, int e, const char* tab, uin
   }
 }
 
-// Merge `count` (1..kGroup) consecutive split partials of one (sequence, KV head):
-// partial e holds, per head g, (m, l) at ml[(e*G + g)*2 + {0,1}] and the unnormalised
-// output at o[(e*G + g)*128 + i].  m* = max_e m_e, l = sum_e 2^(m_e - m*) l_e and
-// o = sum_e 2^(m_e - m*) o_e, in e order.  Writes either the merged partial or, if
-// `final_out`, o / l to dst_o[g*128 + i].  All loads are issued before any result is
-// needed, so the merge costs one round of memory latency.
+// Merge of the S split partials of one (sequence, KV head), restricted to outputs
+// [first, first + count) of the G x 128 (head-major) outputs; count is a power of two.
+// Partial e holds, per head hd, (m, l) at ml[(e G + hd) 2 + {0, 1}] and the unnormalised
+// output at o[(e G + hd) 128 + i].  With m* = max_e m_e and w_e = 2^(m_e - m*) (0 for a
+// partial without tokens), out = sum_e w_e o_e / sum_e w_e l_e.  Every thread issues its
+// first kPre output loads at once while wave hh loads the (m, l) of head hd0 + hh into
+// registers, so the common case costs one round of memory latency.  `smem` holds
+// nh S + NT + nh floats (nh = heads covered); S <= 256.
 template <int G, int NT>
-__device__ __attribute__((always_inline)) inline void merge_level(const float* __restrict__ src_o, const float* __restrict__ src_ml,
-                                   int count, float* mw, int tid, float* __restrict__ dst_o,
-                                   float* __restrict__ dst_ml, bool final_out) {
-  constexpr int NOUT = G * kHeadDim;
-  constexpr int OPT = (NOUT + NT - 1) / NT;
-  float ov[OPT][kGroup];
+__device__ __attribute__((always_inline)) inline void merge_slice(
+    const float* __restrict__ src_o, const float* __restrict__ src_ml, int S, int first, int count,
+    float* smem, int tid, float* __restrict__ dst) {
+  constexpr int kPre = 16;
+  const int hd0 = first / kHeadDim;
+  const int nh = count > kHeadDim ? count / kHeadDim : 1;
+  const int P = count < NT ? count : NT;          // outputs per pass
+  const int R = NT / P;                           // threads per output
+  const int j = tid % P, e0 = tid / P;
+  float* wv = smem;                               // [nh][S] weights
+  float* red = wv + nh * S;                       // [NT] per-thread partial outputs
+  float* Ls = red + NT;                           // [nh] merged sums
+  float ov[kPre];
 #pragma unroll
-  for (int k = 0; k < OPT; ++k) {
-    const int idx = (tid + NT * k) % NOUT;
-    const int g = idx / kHeadDim, i = idx % kHeadDim;
+  for (int k = 0; k < kPre; ++k) {
+    const int e = e0 + R * k;
+    ov[k] = e < S ? ld_coh(src_o + static_cast<int64_t>(e) * G * kHeadDim + first + j) : 0.0f;
+  }
+  const int wave = tid >> 6, lane = tid & 63;
+  for (int hh = wave; hh < nh; hh += NT / 64) {
+    const float* ml = src_ml + (hd0 + hh) * 2;
+    float mr[4], lr[4];
 #pragma unroll
-    for (int e = 0; e < kGroup; ++e) {
-      const int ee = e < count ? e : count - 1;   // loads stay in range; weight 0 below
-      ov[k][e] = ld_coh(src_o + (ee * G + g) * kHeadDim + i);
+    for (int k = 0; k < 4; ++k) {
+      const int e = lane + 64 * k;
+      mr[k] = e < S ? ld_coh(ml + e * G * 2) : -INFINITY;
+      lr[k] = e < S ? ld_coh(ml + e * G * 2 + 1) : 0.0f;
     }
-  }
-  float* wv = mw;                       // [kGroup][G] maxima, then weights
-  float* lv = mw + kGroup * G;          // [kGroup][G] sums
-  float* ms = lv + kGroup * G;          // [G] merged max
-  float* ls = ms + G;                   // [G] merged sum
-  if (tid < kGroup * G) {
-    const int e = tid / G, g = tid % G;
-    const int ee = e < count ? e : count - 1;
-    const float m = ld_coh(src_ml + (ee * G + g) * 2);
-    const float l = ld_coh(src_ml + (ee * G + g) * 2 + 1);
-    wv[tid] = e < count ? m : -INFINITY;
-    lv[tid] = l;
-  }
-  __syncthreads();
-  if (tid < G) {
-    float m = -INFINITY;
-    for (int e = 0; e < kGroup; ++e) m = fmaxf(m, wv[e * G + tid]);
+    const float m = wave_max(fmaxf(fmaxf(mr[0], mr[1]), fmaxf(mr[2], mr[3])));
     float l = 0.0f;
-    for (int e = 0; e < kGroup; ++e) {
-      const float me = wv[e * G + tid];
-      const float w = me == -INFINITY ? 0.0f : exp2f(me - m);
-      l += w * lv[e * G + tid];
-      wv[e * G + tid] = w;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = lane + 64 * k;
+      const float w = mr[k] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mr[k] - m);
+      if (e < S) wv[hh * S + e] = w;
+      l += w * lr[k];
     }
-    ms[tid] = m;
-    ls[tid] = l;
+    l = wave_sum(l);
+    if (lane == 0) Ls[hh] = l;
   }
   __syncthreads();
+  for (int pass = 0; pass * P < count; ++pass) {
+    const int oi = first + pass * P + j;            // output index (head-major)
+    const int hh = oi / kHeadDim - hd0;
+    float acc = 0.0f;
+    int e = e0;
+    if (pass == 0) {
 #pragma unroll
-  for (int k = 0; k < OPT; ++k) {
-    const int idx = tid + NT * k;
-    if (idx >= NOUT) break;
-    const int g = idx / kHeadDim, i = idx % kHeadDim;
-    float o = 0.0f;
-#pragma unroll
-    for (int e = 0; e < kGroup; ++e) o += wv[e * G + g] * ov[k][e];
-    if (final_out) {
-      dst_o[g * kHeadDim + i] = o / ls[g];
-    } else {
-      st_coh(dst_o + g * kHeadDim + i, o);
-      if (i == 0) {
-        st_coh(dst_ml + g * 2 + 0, ms[g]);
-        st_coh(dst_ml + g * 2 + 1, ls[g]);
-      }
+      for (int k = 0; k < kPre; ++k, e += R)
+        if (e < S) acc += wv[hh * S + e] * ov[k];
     }
+    for (; e < S; e += R) acc += wv[hh * S + e] * ld_coh(src_o + static_cast<int64_t>(e) * G * kHeadDim + oi);
+    red[tid] = acc;
+    __syncthreads();
+    if (tid < P) {
+      float o = 0.0f;
+      int r = 0;
+      for (; r + 8 <= R; r += 8) {
+        float t[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) t[k] = red[tid + P * (r + k)];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o += t[k];
+      }
+      for (; r < R; ++r) o += red[tid + P * r];
+      dst[oi] = o / Ls[hh];
+    }
+    __syncthreads();
   }
 }
 
-// One chunk of the key product for lane (n, g): the query operand, the lookup parameters of
-// the lane's four pairs (plan ranks 16 c + 4 g .. + 3) and the two 32-bit row windows (pairs
-// 0-1 and 2-3) of each of its 8 tokens 16 tg + n.
-struct KChunk {
+// Key product of lane (n, g) in chunk c: the query operand, the lookup parameters of the
+// lane's four pairs (plan ranks 16 c + 4 g .. + 3); and, per half of the tile, the two 32-bit
+// row windows (pairs 0-1 and 2-3) of its four tokens 16 tg + n, tg = 4 half .. 4 half + 3.
+struct KPar {
   h8 aq;
   uint32_t shA, shB, rel1, rel3, baseA, baseB;
-  uint32_t wp[4], bw[4], pb[4], ps[4];
-  uint32_t la[8], ha[8], lb[8], hb[8];
+  uint32_t bw[4], pb[4], ps[4];
+};
+struct KWin {
+  uint32_t la[4], ha[4], lb[4], hb[4];
 };
 
-__device__ __attribute__((always_inline)) inline KChunk k_chunk_params(
-    int c, int g, int n, const uint32_t* pd_s, const uint32_t* px_s, const _Float16 (*a_s)[16][kAS],
-    uint32_t lane_copy, const uint32_t* kr) {
-  KChunk k;
+__device__ __attribute__((always_inline)) inline KPar k_params(int c, int g, int n, const uint32_t* kp_s,
+                                                              const _Float16 (*a_s)[16][kAS]) {
+  KPar k;
   k.aq = *reinterpret_cast<const h8*>(&a_s[c][n][8 * g]);
-  const int grp = 4 * c + g;
-  const uint4 dd = *reinterpret_cast<const uint4*>(&pd_s[4 * grp]);
-  const uint4 xx = *reinterpret_cast<const uint4*>(&px_s[4 * grp]);
-  const uint32_t d4[4] = {dd.x, dd.y, dd.z, dd.w}, x4[4] = {xx.x, xx.y, xx.z, xx.w};
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    k.wp[p] = d4[p] >> 16;
-    k.bw[p] = x4[p] >> 24;
-    const uint32_t kind = (x4[p] >> 16) & 3u;
-    k.pb[p] = (x4[p] & 0xFFFFu) | (kind == 2u ? lane_copy : kind == 1u ? (lane_copy & 63u) : 0u);
-    k.ps[p] = kind == 2u ? 7u : kind == 1u ? 6u : 2u;
-  }
-  const uint32_t offA = d4[0] & 0xFFFFu, offB = d4[2] & 0xFFFFu;
-  k.shA = offA & 31u;
-  k.shB = offB & 31u;
-  k.rel1 = 2u * k.wp[0];
-  k.rel3 = 2u * k.wp[2];
-  k.baseA = (offA >> 5) * kKS + n;
-  k.baseB = (offB >> 5) * kKS + n;
+  const uint32_t* blk = kp_s + (4 * c + g) * kParamWords;
+  const uint4 b4 = *reinterpret_cast<const uint4*>(blk);
+  const uint4 m4 = *reinterpret_cast<const uint4*>(blk + 4);
+  const uint4 w4 = *reinterpret_cast<const uint4*>(blk + 8);
+  const uint4 s4 = *reinterpret_cast<const uint4*>(blk + 12);
+  const uint4 x4 = *reinterpret_cast<const uint4*>(blk + 16);
+  const uint2 y2 = *reinterpret_cast<const uint2*>(blk + 20);
+  const uint32_t n4 = 4u * static_cast<uint32_t>(n);
+  k.pb[0] = (n4 & m4.x) | b4.x;
+  k.pb[1] = (n4 & m4.y) | b4.y;
+  k.pb[2] = (n4 & m4.z) | b4.z;
+  k.pb[3] = (n4 & m4.w) | b4.w;
+  k.bw[0] = w4.x; k.bw[1] = w4.y; k.bw[2] = w4.z; k.bw[3] = w4.w;
+  k.ps[0] = s4.x; k.ps[1] = s4.y; k.ps[2] = s4.z; k.ps[3] = s4.w;
+  k.shA = x4.x;
+  k.shB = x4.y;
+  k.rel1 = x4.z;
+  k.rel3 = x4.w;
+  k.baseA = y2.x + n4;
+  k.baseB = y2.y + n4;
   return k;
 }
 
-__device__ __attribute__((always_inline)) inline void k_chunk_windows(KChunk& k, const uint32_t* kr) {
+__device__ __attribute__((always_inline)) inline KWin k_windows(const KPar& k, const uint32_t* kr, int half) {
+  const char* kb = reinterpret_cast<const char*>(kr) + 256 * half;   // 64 tokens x 4 bytes
+  KWin w;
 #pragma unroll
-  for (int tg = 0; tg < 8; ++tg) {
-    k.la[tg] = kr[k.baseA + 16 * tg];
-    k.ha[tg] = kr[k.baseA + 16 * tg + kKS];
-    k.lb[tg] = kr[k.baseB + 16 * tg];
-    k.hb[tg] = kr[k.baseB + 16 * tg + kKS];
+  for (int t = 0; t < 4; ++t) {
+    w.la[t] = lds_u32(kb, k.baseA + 64 * t);
+    w.ha[t] = lds_u32(kb, k.baseA + 64 * t + 4 * kKS);
+    w.lb[t] = lds_u32(kb, k.baseB + 64 * t);
+    w.hb[t] = lds_u32(kb, k.baseB + 64 * t + 4 * kKS);
   }
+  return w;
 }
 
 // Decode kernel.  W waves per workgroup (one or two per SIMD).  Every wave owns a region of
@@ -295,9 +339,9 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     const void* __restrict__ qv, int q_f32, float sigma, int64_t len, int n_kv, int64_t cap,
     int tiles_per_split, const Plan* __restrict__ plans, const Tables* __restrict__ tabg,
     const uint32_t* __restrict__ kc, const uint32_t* __restrict__ vc, const uint16_t* __restrict__ ks,
-    const uint16_t* __restrict__ vs, int k_words, int n_nf, int n_splits, int region_words,
-    int v_early, int v_off, float* __restrict__ part_o, float* __restrict__ part_ml, float* __restrict__ gpart_o,
-    float* __restrict__ gpart_ml, unsigned* __restrict__ counters, float* __restrict__ out) {
+    const uint16_t* __restrict__ vs, int k_words, int n_nf, int n_splits, int n_mergers, int region_words,
+    int v_early, int v_off, float* __restrict__ part_o, float* __restrict__ part_ml,
+    unsigned* __restrict__ counters, float* __restrict__ out) {
   constexpr int NT = 64 * W;
   constexpr bool kPipe = W == 4;                      // one wave per SIMD: prefetch and pipeline
   constexpr int PCOLS = 2 * G;                        // P columns: hi of heads 0..G-1, then lo
@@ -315,12 +359,12 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   __shared__ __attribute__((aligned(16))) _Float16 a_s[4][16][kAS];
   __shared__ uint8_t fdim_s[kHeadDim];
   __shared__ __attribute__((aligned(16))) uint32_t pd_s[kBlocks];
-  __shared__ __attribute__((aligned(16))) uint32_t px_s[kBlocks];
-  __shared__ float comb_m[W][G], comb_l[W][G];
+  __shared__ __attribute__((aligned(16))) uint32_t kp_s[16 * kParamWords];
+  __shared__ __attribute__((aligned(16))) float comb_m[G][W];
+  __shared__ __attribute__((aligned(16))) float comb_l[G][W];
   __shared__ float alpha_s[W][G];
-  __shared__ bool flag_s;
+  __shared__ unsigned arrive_s;
   __shared__ uint64_t wide_s;
-  __shared__ float sc_s[W][G], ms_s[G], ls_s[G];
   extern __shared__ __attribute__((aligned(16))) uint32_t dyn_s[];   // [W][region_words]
   uint32_t* kr = dyn_s + wave * region_words;                         // [k_words + 1][kKS]
   _Float16* pw = reinterpret_cast<_Float16*>(kr);                     // [PCOLS][kPS], after keys
@@ -365,7 +409,6 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
 
   // K rows of tokens lane and lane + 64 (first 16 words), scales of tokens 16 tg + n, V segments
   uint4 ka[4], kb2[4];
-  float skr[8], svr[8];
   auto load_k = [&](int64_t tile) {
     const int64_t tok0 = tile * kVTile;
     const uint4* krow0 = reinterpret_cast<const uint4*>(kc + (bh * cap + tok0 + lane) * k_words);
@@ -378,18 +421,29 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
       }
     }
   };
+  uint32_t skp[4], svp[4];   // fp16 scales of tokens 16 tg + n, two per register (tg even: low half)
   auto load_scales = [&](int64_t tile) {
 #pragma unroll
-    for (int tg = 0; tg < 8; ++tg) {
-      const int64_t t = tile * kVTile + 16 * tg + n;
+    for (int j = 0; j < 4; ++j) {
+      const int64_t t0 = tile * kVTile + 32 * j + n, t1 = t0 + 16;
+      uint32_t k0, k1, v0, v1;
       if (NF) {
-        skr[tg] = half_bits_to_float(ks[(static_cast<int64_t>(b) * cap + t) * n_nf + h / 2]);
-        svr[tg] = half_bits_to_float(vs[(static_cast<int64_t>(b) * cap + t) * n_nf + h / 2]);
+        k0 = ks[(static_cast<int64_t>(b) * cap + t0) * n_nf + h / 2];
+        k1 = ks[(static_cast<int64_t>(b) * cap + t1) * n_nf + h / 2];
+        v0 = vs[(static_cast<int64_t>(b) * cap + t0) * n_nf + h / 2];
+        v1 = vs[(static_cast<int64_t>(b) * cap + t1) * n_nf + h / 2];
       } else {
-        skr[tg] = half_bits_to_float(ks[bh * cap + t]);
-        svr[tg] = half_bits_to_float(vs[bh * cap + t]);
+        k0 = ks[bh * cap + t0];
+        k1 = ks[bh * cap + t1];
+        v0 = vs[bh * cap + t0];
+        v1 = vs[bh * cap + t1];
       }
+      skp[j] = k0 | (k1 << 16);
+      svp[j] = v0 | (v1 << 16);
     }
+  };
+  auto scale_of = [](const uint32_t (&pk)[4], int tg) {
+    return half_bits_to_float(static_cast<uint16_t>(pk[tg >> 1] >> (16 * (tg & 1))));
   };
   // the V tile (512 segments x VB words, contiguous in HBM) goes straight into this wave's LDS
   // area: 2 VB copies of 64 lanes x 16 bytes, waited for with s_waitcnt vmcnt(0) before use
@@ -416,7 +470,7 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     if (tid < kHeadDim) fdim_s[tid] = static_cast<uint8_t>(fd_r);
     if (tid < kBlocks) {
       pd_s[tid] = pd_r;
-      px_s[tid] = pair_lookup_params(pd_r >> 16);
+      write_pair_params(kp_s, tid, pd_r);
     }
     // replicas of the width-4 (16 copies) and width-3 (32 copies) pair tables: thread t writes
     // all copies of entry t (rotating the 16-byte pieces over the lanes spreads the banks)
@@ -516,67 +570,65 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     f4 dacc[8];
 #pragma unroll
     for (int tg = 0; tg < 8; ++tg) dacc[tg] = f4{0.f, 0.f, 0.f, 0.f};
-    auto k_lookups = [&](const KChunk& cur, int c, uint32_t (&u)[8][4]) {
+    auto k_lookups = [&](const KPar& P, const KWin& Wn, int c, uint32_t (&u)[4][4]) {
 #pragma unroll
-      for (int tg = 0; tg < 8; ++tg) {
-        const uint32_t xa = __builtin_amdgcn_alignbit(cur.ha[tg], cur.la[tg], cur.shA);
-        const uint32_t xb = __builtin_amdgcn_alignbit(cur.hb[tg], cur.lb[tg], cur.shB);
-        u[tg][0] = lds_u32(tab_s, (__builtin_amdgcn_ubfe(xa, 0u, cur.bw[0]) << cur.ps[0]) | cur.pb[0]);
-        u[tg][1] = lds_u32(tab_s, (__builtin_amdgcn_ubfe(xa, cur.rel1, cur.bw[1]) << cur.ps[1]) | cur.pb[1]);
-        u[tg][2] = lds_u32(tab_s, (__builtin_amdgcn_ubfe(xb, 0u, cur.bw[2]) << cur.ps[2]) | cur.pb[2]);
-        u[tg][3] = lds_u32(tab_s, (__builtin_amdgcn_ubfe(xb, cur.rel3, cur.bw[3]) << cur.ps[3]) | cur.pb[3]);
+      for (int t = 0; t < 4; ++t) {
+        const uint32_t xa = __builtin_amdgcn_alignbit(Wn.ha[t], Wn.la[t], P.shA);
+        const uint32_t xb = __builtin_amdgcn_alignbit(Wn.hb[t], Wn.lb[t], P.shB);
+        u[t][0] = lds_u32(tab_s, (__builtin_amdgcn_ubfe(xa, 0u, P.bw[0]) << P.ps[0]) | P.pb[0]);
+        u[t][1] = lds_u32(tab_s, (__builtin_amdgcn_ubfe(xa, P.rel1, P.bw[1]) << P.ps[1]) | P.pb[1]);
+        u[t][2] = lds_u32(tab_s, (__builtin_amdgcn_ubfe(xb, 0u, P.bw[2]) << P.ps[2]) | P.pb[2]);
+        u[t][3] = lds_u32(tab_s, (__builtin_amdgcn_ubfe(xb, P.rel3, P.bw[3]) << P.ps[3]) | P.pb[3]);
       }
       if ((uses_wide >> (16 * c)) & 0xFFFFull) {
         // blocks of 6..8 bits: two single lookups (lanes whose pair is narrower skip)
         const char* tabi = tab_s + kImageBase;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          if (cur.wp[p] >= 6u) {
-            const uint32_t sb = static_cast<uint32_t>(kLdsTableBytes) - (4u << cur.wp[p]);
-            const uint32_t rel = (p & 1) ? (p == 1 ? cur.rel1 : cur.rel3) : 0u;
+          const uint32_t wp = pd_s[16 * c + 4 * g + p] >> 16;
+          if (wp >= 6u) {
+            const uint32_t sb = static_cast<uint32_t>(kLdsTableBytes) - (4u << wp);
+            const uint32_t rel = (p & 1) ? (p == 1 ? P.rel1 : P.rel3) : 0u;
 #pragma unroll
-            for (int tg = 0; tg < 8; ++tg) {
-              const uint32_t x = (p < 2) ? __builtin_amdgcn_alignbit(cur.ha[tg], cur.la[tg], cur.shA)
-                                         : __builtin_amdgcn_alignbit(cur.hb[tg], cur.lb[tg], cur.shB);
-              const uint32_t f0 = __builtin_amdgcn_ubfe(x, rel, cur.wp[p]);
-              const uint32_t f1 = __builtin_amdgcn_ubfe(x, rel + cur.wp[p], cur.wp[p]);
-              u[tg][p] = lds_u16(tabi, (f0 << 1) | sb) | (lds_u16(tabi, (f1 << 1) | sb) << 16);
+            for (int t = 0; t < 4; ++t) {
+              const uint32_t x = (p < 2) ? __builtin_amdgcn_alignbit(Wn.ha[t], Wn.la[t], P.shA)
+                                         : __builtin_amdgcn_alignbit(Wn.hb[t], Wn.lb[t], P.shB);
+              const uint32_t f0 = __builtin_amdgcn_ubfe(x, rel, wp);
+              const uint32_t f1 = __builtin_amdgcn_ubfe(x, rel + wp, wp);
+              u[t][p] = lds_u16(tabi, (f0 << 1) | sb) | (lds_u16(tabi, (f1 << 1) | sb) << 16);
             }
           }
         }
       }
     };
-    auto k_products = [&](const KChunk& cur, const uint32_t (&u)[8][4]) {
+    auto k_products = [&](const KPar& P, const uint32_t (&u)[4][4], int half) {
 #pragma unroll
-      for (int tg = 0; tg < 8; ++tg) {
+      for (int t = 0; t < 4; ++t) {
         h8 bk;
-        __builtin_memcpy(&bk, u[tg], 16);
-        dacc[tg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur.aq, bk, dacc[tg], 0, 0, 0);
+        __builtin_memcpy(&bk, u[t], 16);
+        dacc[4 * half + t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(P.aq, bk, dacc[4 * half + t], 0, 0, 0);
       }
     };
-    if constexpr (kPipe) {
-      // software pipeline: chunk c + 1's descriptors and row windows are read while chunk c's
-      // lookups and products run
-      KChunk cur = k_chunk_params(0, g, n, pd_s, px_s, a_s, lb, kr);
-      k_chunk_windows(cur, kr);
+    // software pipeline over the 8 (chunk, half) steps: the next step's row windows are read
+    // before this step's lookups, and chunk c + 1's parameters during chunk c's first half
+    {
+      KPar P[4];
+      P[0] = k_params(0, g, n, kp_s, a_s);
+      KWin Wc = k_windows(P[0], kr, 0);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        KChunk nxt;
-        if (c + 1 < 4) nxt = k_chunk_params(c + 1, g, n, pd_s, px_s, a_s, lb, kr);
-        uint32_t u[8][4];
-        k_lookups(cur, c, u);
-        if (c + 1 < 4) k_chunk_windows(nxt, kr);
-        k_products(cur, u);
-        if (c + 1 < 4) cur = nxt;
-      }
-    } else {
-#pragma unroll 1
-      for (int c = 0; c < 4; ++c) {
-        KChunk cur = k_chunk_params(c, g, n, pd_s, px_s, a_s, lb, kr);
-        k_chunk_windows(cur, kr);
-        uint32_t u[8][4];
-        k_lookups(cur, c, u);
-        k_products(cur, u);
+      for (int hc = 0; hc < 8; ++hc) {
+        const int c = hc >> 1, half = hc & 1;
+        KWin Wn;
+        if (half == 0) {
+          Wn = k_windows(P[c], kr, 1);
+          if (c + 1 < 4) P[c + 1] = k_params(c + 1, g, n, kp_s, a_s);
+        } else if (c + 1 < 4) {
+          Wn = k_windows(P[c + 1], kr, 0);
+        }
+        uint32_t u[4][4];
+        k_lookups(P[c], Wc, c, u);
+        k_products(P[c], u, half);
+        if (hc + 1 < 8) Wc = Wn;
       }
     }
     wave_sync();   // the key rows are read; the area takes the softmax weights (and V) next
@@ -585,11 +637,13 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     // -- online softmax: lane (n, g) holds heads 2g and 2g + 1 of tokens 16 tg + n --
     float L0[8], L1[8];
     float mt0 = -INFINITY, mt1 = -INFINITY;
+    const int rem = len - tok0 < kVTile ? static_cast<int>(len - tok0) : kVTile;   // valid tokens
 #pragma unroll
     for (int tg = 0; tg < 8; ++tg) {
-      const bool ok = tok0 + 16 * tg + n < len;
-      L0[tg] = ok ? (dacc[tg][0] + dacc[tg][1]) * skr[tg] : -INFINITY;
-      L1[tg] = ok ? (dacc[tg][2] + dacc[tg][3]) * skr[tg] : -INFINITY;
+      const float bias = 16 * tg + n < rem ? 0.0f : -INFINITY;
+      const float sk = scale_of(skp, tg);
+      L0[tg] = fmaf(dacc[tg][0] + dacc[tg][1], sk, bias);
+      L1[tg] = fmaf(dacc[tg][2] + dacc[tg][3], sk, bias);
       mt0 = fmaxf(mt0, L0[tg]);
       mt1 = fmaxf(mt1, L1[tg]);
     }
@@ -605,8 +659,8 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     l1 *= al1;
 #pragma unroll
     for (int tg = 0; tg < 8; ++tg) {
-      const bool ok = tok0 + 16 * tg + n < len;
-      const float sv = ok ? svr[tg] : 0.0f;   // stored scales past the sequence end are not used
+      // tokens past the sequence end have p = 0; their stored scales are finite (zero-filled)
+      const float sv = scale_of(svp, tg);
       const float p0 = __builtin_amdgcn_exp2f(L0[tg] - mn0), p1 = __builtin_amdgcn_exp2f(L1[tg] - mn1);
       l0 += p0;
       l1 += p1;
@@ -672,91 +726,103 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     }
   }
 
-  // ---- merge the W waves of this workgroup ----
+  // ---- merge the W waves of this workgroup: each wave adds its lo columns (n + G) into its
+  //      hi columns (n) and writes them, with its (m, l), to LDS; after one barrier every
+  //      thread combines the waves for its outputs ----
   l0 = row_sum16(l0);
   l1 = row_sum16(l1);
+  float* ow = reinterpret_cast<float*>(kr);   // [128][kOS]: dim-major, padded (distinct banks)
   if (n == 0) {
     if (vh0) {
-      comb_m[wave][h0] = m0;
-      comb_l[wave][h0] = l0;
+      comb_m[h0][wave] = m0;
+      comb_l[h0][wave] = l0;
     }
     if (vh1) {
-      comb_m[wave][h1] = m1;
-      comb_l[wave][h1] = l1;
+      comb_m[h1][wave] = m1;
+      comb_l[h1][wave] = l1;
     }
   }
-  // O^T layout: lane holds rows 4 g + r of dim slice dt for column n; add the lo column
-  // (n + G) into the hi column (n), into this wave's region as [128][kOS] floats (the padded
-  // stride keeps the 32 writing lanes on distinct banks)
-  float* ow = reinterpret_cast<float*>(kr);
-  __syncthreads();
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float other = __shfl(oacc[dt][r], (lane & ~15) | ((n + G) & 15), 64);
+      // lane n reads lane (n + G) mod 16 of its row
+      const float other = KVQ_DPP(oacc[dt][r], 0x120 + (16 - G) % 16);
       if (n < G) ow[(dt * 16 + 4 * g + r) * kOS + n] = oacc[dt][r] + other;
     }
   }
   __syncthreads();
-  // scale of each wave's share per head: 2^(m_w - max_w m_w), 0 for waves without tokens
-  if (tid < G) {
-    float ms = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < W; ++w) ms = fmaxf(ms, comb_m[w][tid]);
-    float l = 0.0f;
-#pragma unroll
-    for (int w = 0; w < W; ++w) {
-      const float mw = comb_m[w][tid];
-      const float sc = mw == -INFINITY ? 0.0f : exp2f(mw - ms);
-      sc_s[w][tid] = sc;
-      l += sc * comb_l[w][tid];
-    }
-    ms_s[tid] = ms;
-    ls_s[tid] = l;
-  }
-  __syncthreads();
+  const int64_t out_base = (static_cast<int64_t>(b) * n_q + h * G) * kHeadDim;
   for (int idx = tid; idx < G * kHeadDim; idx += NT) {
     const int hd = idx / kHeadDim, i = idx % kHeadDim;
-    float o = 0.0f;
+    float mw[W], lw[W], ov[W];
 #pragma unroll
-    for (int w = 0; w < W; ++w)
-      o += sc_s[w][hd] * reinterpret_cast<const float*>(dyn_s + w * region_words)[i * kOS + hd];
-    const int64_t p = (bh * n_splits + s) * G + hd;
-    st_coh(part_o + p * kHeadDim + i, o);
-    if (i == 0) {
-      st_coh(part_ml + p * 2 + 0, ms_s[hd]);
-      st_coh(part_ml + p * 2 + 1, ls_s[hd]);
+    for (int w = 0; w < W; w += 4) {
+      const float4 m4 = *reinterpret_cast<const float4*>(&comb_m[hd][w]);
+      const float4 l4 = *reinterpret_cast<const float4*>(&comb_l[hd][w]);
+      mw[w] = m4.x; mw[w + 1] = m4.y; mw[w + 2] = m4.z; mw[w + 3] = m4.w;
+      lw[w] = l4.x; lw[w + 1] = l4.y; lw[w + 2] = l4.z; lw[w + 3] = l4.w;
+    }
+#pragma unroll
+    for (int w = 0; w < W; ++w) ov[w] = reinterpret_cast<const float*>(dyn_s + w * region_words)[i * kOS + hd];
+    float ms = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < W; ++w) ms = fmaxf(ms, mw[w]);
+    float o = 0.0f, l = 0.0f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      // 0 for waves without tokens; hardware 2^x (weights far below 1 only meet sums >= 1)
+      const float sc = mw[w] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw[w] - ms);
+      o += sc * ov[w];
+      l += sc * lw[w];
+    }
+    if (n_splits == 1) {
+      out[out_base + idx] = o / l;
+    } else {
+      const int64_t p = (bh * n_splits + s) * G + hd;
+      st_coh(part_o + p * kHeadDim + i, o);
+      if (i == 0) {
+        st_coh(part_ml + p * 2 + 0, ms);
+        st_coh(part_ml + p * 2 + 1, l);
+      }
     }
   }
+  if (n_splits == 1) return;
 
-  // ---- split merge, two levels ----
-  const int grp = s / kGroup;
-  const int n_groups = (n_splits + kGroup - 1) / kGroup;
-  const int gsize = n_splits - grp * kGroup < kGroup ? n_splits - grp * kGroup : kGroup;
-  unsigned* cnt = counters + bh * (kMaxGroups + 1);
-  float* mw_s = reinterpret_cast<float*>(dyn_s);   // merge scratch: 2 x [kGroup][G] + 2 x [G]
-  if (!arrive(cnt + grp, static_cast<unsigned>(gsize), &flag_s)) return;
-  {
-    const int64_t src = (bh * n_splits + grp * kGroup) * G;
-    if (n_groups == 1) {
-      merge_level<G, NT>(part_o + src * kHeadDim, part_ml + src * 2, gsize, mw_s, tid,
-                         out + (static_cast<int64_t>(b) * n_q + h * G) * kHeadDim, nullptr, true);
-      if (tid == 0) __hip_atomic_store(cnt + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return;
+  // ---- split merge: the last n_mergers workgroups of this (sequence, KV head) to finish
+  //      each merge one slice of the outputs; all but the very last wait (bounded) until the
+  //      counter has wrapped to 0, i.e. every split has stored its partial ----
+  unsigned* cnt = counters + bh;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);   // this wave's partial stores have completed
+  __syncthreads();
+  if (tid == 0) {
+    // wraps to 0 on the last of the n_splits arrivals
+    arrive_s = __builtin_amdgcn_atomic_inc32(cnt, static_cast<unsigned>(n_splits - 1), __ATOMIC_RELAXED, "agent");
+    if (arrive_s + 1u < static_cast<unsigned>(n_splits) &&
+        arrive_s + static_cast<unsigned>(n_mergers) >= static_cast<unsigned>(n_splits)) {
+      for (int polls = 0; polls < kMaxPolls; ++polls) {
+        if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
     }
-    const int64_t dst = (bh * kMaxGroups + grp) * G;
-    merge_level<G, NT>(part_o + src * kHeadDim, part_ml + src * 2, gsize, mw_s, tid,
-                       gpart_o + dst * kHeadDim, gpart_ml + dst * 2, false);
   }
-  if (tid == 0) __hip_atomic_store(cnt + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (!arrive(cnt + kMaxGroups, static_cast<unsigned>(n_groups), &flag_s)) return;
-  {
-    const int64_t src = bh * kMaxGroups * G;
-    merge_level<G, NT>(gpart_o + src * kHeadDim, gpart_ml + src * 2, n_groups, mw_s, tid,
-                       out + (static_cast<int64_t>(b) * n_q + h * G) * kHeadDim, nullptr, true);
-  }
-  if (tid == 0) __hip_atomic_store(cnt + kMaxGroups, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  const int rank = static_cast<int>(arrive_s) - (n_splits - n_mergers);
+  if (rank < 0) return;
+  const int count = G * kHeadDim / n_mergers;
+  merge_slice<G, NT>(part_o + bh * n_splits * G * kHeadDim, part_ml + bh * n_splits * G * 2, n_splits,
+                     rank * count, count, reinterpret_cast<float*>(dyn_s), tid, out + out_base);
+}
+
+// Workgroups that merge the splits of one (sequence, KV head): a power of two, at most 64 and
+// at most S, small enough that the waiting mergers of all units occupy fewer than all compute
+// units (units x (K - 1) < CUs), so the splits they wait for can always be scheduled.
+inline int split_mergers(int S, int64_t units, int n_cu) {
+  int k = kMaxMergers;
+  while (k > 1 && (k > S || units * (k - 1) >= n_cu)) k >>= 1;
+  return k;
 }
 
 template <int G, int VB, int W>
@@ -770,21 +836,22 @@ hipError_t launch_gvw(kvq_cache* c, int layer, const void* q, int q_f32, float s
   const size_t dyn = static_cast<size_t>(W) * sh.region_words * sizeof(uint32_t);
   const Plan* plans = c->plans + static_cast<int64_t>(layer) * cfg.n_kv_heads;
   const bool nf = cfg.codec == KVQ_CODEC_NF16_B256;
+  const int mergers = split_mergers(S, static_cast<int64_t>(cfg.batch) * cfg.n_kv_heads, c->n_cu);
   if constexpr (VB == 4) {
     if (nf) {
       hipLaunchKernelGGL((decode_mfma<G, 4, true, W>), grid, dim3(64 * W), dyn, stream, q, q_f32, sigma,
                          len, cfg.n_kv_heads, c->cap, tps, plans, c->tables, layer_k_codes(c, layer),
                          layer_v_codes(c, layer), layer_k_scales(c, layer), layer_v_scales(c, layer),
-                         c->k_words, c->n_nf_blocks, S, sh.region_words, sh.v_early, sh.v_off, c->part_o,
-                         c->part_ml, c->gpart_o, c->gpart_ml, c->split_counters, out);
+                         c->k_words, c->n_nf_blocks, S, mergers, sh.region_words, sh.v_early, sh.v_off,
+                         c->part_o, c->part_ml, c->split_counters, out);
       return hipGetLastError();
     }
   }
   hipLaunchKernelGGL((decode_mfma<G, VB, false, W>), grid, dim3(64 * W), dyn, stream, q, q_f32, sigma,
                      len, cfg.n_kv_heads, c->cap, tps, plans, c->tables, layer_k_codes(c, layer),
                      layer_v_codes(c, layer), layer_k_scales(c, layer), layer_v_scales(c, layer),
-                     c->k_words, c->n_nf_blocks, S, sh.region_words, sh.v_early, sh.v_off, c->part_o,
-                     c->part_ml, c->gpart_o, c->gpart_ml, c->split_counters, out);
+                     c->k_words, c->n_nf_blocks, S, mergers, sh.region_words, sh.v_early, sh.v_off,
+                     c->part_o, c->part_ml, c->split_counters, out);
   return hipGetLastError();
 }
 

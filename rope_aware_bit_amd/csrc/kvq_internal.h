@@ -61,6 +61,7 @@ void build_tables(Tables* t);
 struct kvq_cache {
   kvq_config cfg;
   int device;
+  int n_cu;                    // compute units of the device
   int64_t cap;                 // token capacity per sequence, multiple of kVTile
   int group;                   // n_q / n_kv
   int k_words;                 // 32-bit words per K row
@@ -78,9 +79,7 @@ struct kvq_cache {
   kvq::Tables host_tables;
   float* part_o;               // split partials [B][H][max_splits][G][128]
   float* part_ml;              // [B][H][max_splits][G][2]
-  float* gpart_o;              // merged split groups [B][H][16][G][128]
-  float* gpart_ml;             // [B][H][16][G][2]
-  unsigned* split_counters;    // [B][H][17] finished-split / finished-group counters (zero between calls)
+  unsigned* split_counters;    // [B][H] finished-split counters (zero between calls)
   int max_splits;
   double* energy_scratch;      // [H][n_chunks][64]
   int64_t energy_scratch_chunks;
@@ -108,7 +107,7 @@ struct DecodeShape {
 };
 inline DecodeShape decode_shape(const kvq_cache* c) {
   constexpr int kKS = 144, kPS = 136, kOS = 10, kLds = 163840;
-  constexpr int kStaticBase = 28672 + 2560 + 4 * 16 * 40 * 2 + 128 + 2 * 64 * 4 + 64;
+  constexpr int kStaticBase = 28672 + 2560 + 4 * 16 * 40 * 2 + 128 + 64 * 4 + 16 * 24 * 4 + 64;
   const int G = c->group;
   const int vb = c->cfg.codec == KVQ_CODEC_NF16_B256 ? 4 : c->cfg.v_bits;
   int kpart = (c->k_words + 1) * kKS;
