@@ -156,12 +156,15 @@ kvq_status kvq_quantize_append(kvq_cache* cache, int32_t layer, const void* k, c
 /* Grouped-query decode attention of one query per sequence against the packed
    cache of one layer: logits sigma * <q_h, x_hat^K> over every appended token,
    softmax, weighted sum of x_hat^V; KV head of query head h is h / group.
-   q:     [batch][n_q_heads][128] (dtype).
+   q:     [batch][n_q_heads][128] (dtype), 4-byte aligned.
    softmax_scale: sigma; <= 0 selects 1/sqrt(128).
-   out:   [batch][n_q_heads][128] fp32 device buffer.
+   out:   [batch][n_q_heads][128] fp32 device buffer, 16-byte aligned.
    The context is split into chunks processed in parallel, each producing a
-   partial (max, sum, weighted sum) that a second pass combines in fixed order.
-   Errors: KVQ_EINVAL, KVQ_ESTATE (layer empty or without plan). */
+   partial (max, sum, weighted sum); the last chunks of each (sequence, KV head)
+   to finish combine them in fixed order.  Decode calls on one cache must not
+   overlap in time (they share the partial buffers).
+   Errors: KVQ_EINVAL (also a misaligned q or out), KVQ_ESTATE (layer empty or
+   without plan). */
 kvq_status kvq_decode_attn(kvq_cache* cache, int32_t layer, const void* q, int32_t dtype,
                            float softmax_scale, float* out, kvq_stream stream);
 

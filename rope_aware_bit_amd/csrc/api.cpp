@@ -49,7 +49,7 @@ bool layer_ok(const kvq_cache* c, int32_t layer) {
 
 void free_device(kvq_cache* c) {
   void* ptrs[] = {c->k_codes, c->v_codes, c->k_scales, c->v_scales, c->plans,
-                  c->tables,  c->part_o,  c->part_ml,  c->energy_scratch, c->split_counters};
+                  c->tables,  c->part_o,  c->part_l,  c->part_mt, c->energy_scratch, c->split_epochs};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
 }
@@ -155,12 +155,15 @@ kvq_status kvq_cache_create(const kvq_config* cfg, kvq_cache** out) {
   if (st == KVQ_OK)
     st = dev_alloc(reinterpret_cast<void**>(&c->part_o), per_split / (kHeadDim + 2) * kHeadDim * ms, "partials");
   if (st == KVQ_OK)
-    st = dev_alloc(reinterpret_cast<void**>(&c->part_ml), per_split / (kHeadDim + 2) * 2 * ms, "partials");
+    st = dev_alloc(reinterpret_cast<void**>(&c->part_l), per_split / (kHeadDim + 2) * ms, "partials");
   if (st == KVQ_OK)
-    st = dev_alloc(reinterpret_cast<void**>(&c->split_counters), sizeof(unsigned) * B * H, "counters");
+    st = dev_alloc(reinterpret_cast<void**>(&c->part_mt), per_split / (kHeadDim + 2) * 2 * ms, "partials");
+  if (st == KVQ_OK)
+    st = dev_alloc(reinterpret_cast<void**>(&c->split_epochs), sizeof(unsigned) * B * H, "split tags");
   if (st == KVQ_OK) {
     const hipError_t es[] = {
-        hipMemset(c->split_counters, 0, sizeof(unsigned) * B * H),
+        hipMemset(c->split_epochs, 0, sizeof(unsigned) * B * H),
+        hipMemset(c->part_mt, 0, per_split / (kHeadDim + 2) * 2 * ms),
         hipMemset(c->k_codes, 0, c->k_codes_layer * L),
         hipMemset(c->v_codes, 0, c->v_codes_layer * L),
         hipMemset(c->k_scales, 0, c->k_scales_layer * L),
@@ -265,10 +268,19 @@ kvq_status kvq_decode_attn_splits(kvq_cache* c, int32_t layer, const void* q, in
                                   kvq_stream stream) {
   if (!layer_ok(c, layer) || !q || !out) return KVQ_EINVAL;
   if (dtype != KVQ_F16 && dtype != KVQ_F32) return KVQ_EINVAL;
+  if (reinterpret_cast<uintptr_t>(q) % 4 || reinterpret_cast<uintptr_t>(out) % 16) {
+    g_last_error = "decode: q must be 4-byte and out 16-byte aligned";
+    return KVQ_EINVAL;
+  }
   if (!(softmax_scale == softmax_scale)) return KVQ_EINVAL;  // NaN
   if (!c->plan_ready[layer] || c->len[layer] == 0) return KVQ_ESTATE;
   int S = n_splits > 0 ? n_splits : kvq::auto_splits_mfma(c, c->len[layer]);
   if (S > c->max_splits) return KVQ_EINVAL;
+  const int64_t units = static_cast<int64_t>(c->cfg.batch) * c->cfg.n_kv_heads;
+  if (S > 1 && kvq::decode_split_mergers(S, units, c->n_cu) == 0) {
+    g_last_error = "decode: more split units than compute units can merge; use one split";
+    return KVQ_EINVAL;
+  }
   hipError_t e = kvq::launch_decode_mfma(c, layer, q, dtype, softmax_scale, out, S,
                                          static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decode launch");

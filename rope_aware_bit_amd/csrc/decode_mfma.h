@@ -49,7 +49,6 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 typedef __attribute__((address_space(1))) void* glb_ptr;
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-constexpr int kMaxMergers = 64;   // workgroups that merge the splits of one (sequence, KV head)
 constexpr int kMaxPolls = 1 << 22;  // bound on a merger's wait for the other splits
 constexpr int kKS = 144;          // LDS row stride (words) of a staged K tile: 128 tokens + 16
 constexpr int kPS = 136;          // LDS row stride (halves) of the softmax weights: 128 + 8
@@ -171,6 +170,14 @@ __device__ inline void st_coh(float* p, float v) {
 __device__ inline float ld_coh(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Four consecutive floats (8-byte aligned) read at device scope, two per 64-bit load.
+__device__ inline float4 ld_coh4(const float* p) {
+  const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
+  const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float4(__uint_as_float(static_cast<uint32_t>(a)), __uint_as_float(static_cast<uint32_t>(a >> 32)),
+                     __uint_as_float(static_cast<uint32_t>(b)), __uint_as_float(static_cast<uint32_t>(b >> 32)));
+}
 
 // fp16 pair of V codes e, e+1 (e even) of a 32-code segment held in S[0..VB) (S[VB] is a
 // zero word).  `tab` is the table region, `lb` the lane's replica offset (lane % 32) * 4 (the
@@ -201,79 +208,105 @@ __device__ inline uint32_t v_pair(const uint32_t* S, int e, const char* tab, uin
 
 // Merge of the S split partials of one (sequence, KV head), restricted to outputs
 // [first, first + count) of the G x 128 (head-major) outputs; count is a power of two.
-// Partial e holds, per head hd, (m, l) at ml[(e G + hd) 2 + {0, 1}] and the unnormalised
-// output at o[(e G + hd) 128 + i].  With m* = max_e m_e and w_e = 2^(m_e - m*) (0 for a
-// partial without tokens), out = sum_e w_e o_e / sum_e w_e l_e.  Every thread issues its
-// first kPre output loads at once while wave hh loads the (m, l) of head hd0 + hh into
-// registers, so the common case costs one round of memory latency.  `smem` holds
-// nh S + NT + nh floats (nh = heads covered); S <= 256.
+// Split e publishes, per head hd, its unnormalised output at o[(e G + hd) 128 + i] and its
+// sum at l[e G + hd], and only once those stores have completed, its maximum together with
+// the tag `want` as one 64-bit word at mt[e G + hd].  Wave hh polls the words of head
+// hd0 + hh until every split carries the tag (bounded), which also hands it the maxima; with
+// m* = max_e m_e and w_e = 2^(m_e - m*), out = sum_e w_e o_e / sum_e w_e l_e.  `bump`, if
+// not null, receives `want` once every split is seen (the next call's tag base).  `smem`
+// holds nh S + 4 NT + nh floats (+3 alignment; nh = heads covered); S <= 256.
 template <int G, int NT>
 __device__ __attribute__((always_inline)) inline void merge_slice(
-    const float* __restrict__ src_o, const float* __restrict__ src_ml, int S, int first, int count,
-    float* smem, int tid, float* __restrict__ dst) {
-  constexpr int kPre = 16;
+    const float* __restrict__ src_o, const float* __restrict__ src_l, const uint64_t* __restrict__ src_mt,
+    unsigned want, unsigned* bump, int S, int first, int count, float* smem, int tid,
+    float* __restrict__ dst) {
+  constexpr int kPre = 8;
   const int hd0 = first / kHeadDim;
   const int nh = count > kHeadDim ? count / kHeadDim : 1;
-  const int P = count < NT ? count : NT;          // outputs per pass
-  const int R = NT / P;                           // threads per output
-  const int j = tid % P, e0 = tid / P;
   float* wv = smem;                               // [nh][S] weights
-  float* red = wv + nh * S;                       // [NT] per-thread partial outputs
-  float* Ls = red + NT;                           // [nh] merged sums
-  float ov[kPre];
-#pragma unroll
-  for (int k = 0; k < kPre; ++k) {
-    const int e = e0 + R * k;
-    ov[k] = e < S ? ld_coh(src_o + static_cast<int64_t>(e) * G * kHeadDim + first + j) : 0.0f;
-  }
   const int wave = tid >> 6, lane = tid & 63;
   for (int hh = wave; hh < nh; hh += NT / 64) {
-    const float* ml = src_ml + (hd0 + hh) * 2;
-    float mr[4], lr[4];
+    const uint64_t* mt = src_mt + hd0 + hh;
+    float mr[4];
+    bool ok[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const int e = lane + 64 * k;
-      mr[k] = e < S ? ld_coh(ml + e * G * 2) : -INFINITY;
-      lr[k] = e < S ? ld_coh(ml + e * G * 2 + 1) : 0.0f;
+      ok[k] = lane + 64 * k >= S;
+      mr[k] = -INFINITY;
     }
+    for (int polls = 0; polls < kMaxPolls; ++polls) {
+      bool mine = true;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (!ok[k]) {
+          const uint64_t v = __hip_atomic_load(mt + (lane + 64 * k) * G, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (static_cast<unsigned>(v >> 32) == want) {
+            ok[k] = true;
+            mr[k] = __uint_as_float(static_cast<unsigned>(v));
+          } else {
+            mine = false;
+          }
+        }
+      }
+      if (__ballot(!mine) == 0ull) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (hh == 0 && lane == 0 && bump) __hip_atomic_store(bump, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const float m = wave_max(fmaxf(fmaxf(mr[0], mr[1]), fmaxf(mr[2], mr[3])));
-    float l = 0.0f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int e = lane + 64 * k;
-      const float w = mr[k] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mr[k] - m);
-      if (e < S) wv[hh * S + e] = w;
-      l += w * lr[k];
+      if (e < S) wv[hh * S + e] = mr[k] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mr[k] - m);
     }
-    l = wave_sum(l);
-    if (lane == 0) Ls[hh] = l;
   }
   __syncthreads();
-  for (int pass = 0; pass * P < count; ++pass) {
-    const int oi = first + pass * P + j;            // output index (head-major)
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  // outputs in groups of four (one 16-byte load per split and group)
+  const int P4 = count / 4 < NT ? count / 4 : NT;   // groups per pass
+  const int R = NT / P4;                              // threads per group
+  const int j4 = tid % P4, e0 = tid / P4;
+  float4* red = reinterpret_cast<float4*>(smem + ((nh * S + 3) & ~3));   // [NT]
+  float* Ls = reinterpret_cast<float*>(red + NT);                        // [nh] merged sums
+  for (int pass = 0; pass * 4 * P4 < count; ++pass) {
+    const int oi = first + 4 * (pass * P4 + j4);    // first output of the group (head-major)
     const int hh = oi / kHeadDim - hd0;
-    float acc = 0.0f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    auto add = [&](float w, float4 o) {
+      acc.x += w * o.x; acc.y += w * o.y; acc.z += w * o.z; acc.w += w * o.w;
+    };
     int e = e0;
     if (pass == 0) {
+      float4 ov[kPre];
+#pragma unroll
+      for (int k = 0; k < kPre; ++k) {
+        const int ek = e0 + R * k;
+        ov[k] = ek < S ? ld_coh4(src_o + static_cast<int64_t>(ek) * G * kHeadDim + oi) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      if (wave < nh) {   // merged sum of head hd0 + wave
+        float l = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int ek = lane + 64 * k;
+          if (ek < S) l += wv[wave * S + ek] * ld_coh(src_l + ek * G + hd0 + wave);
+        }
+        l = wave_sum(l);
+        if (lane == 0) Ls[wave] = l;
+      }
 #pragma unroll
       for (int k = 0; k < kPre; ++k, e += R)
-        if (e < S) acc += wv[hh * S + e] * ov[k];
+        if (e < S) add(wv[hh * S + e], ov[k]);
     }
-    for (; e < S; e += R) acc += wv[hh * S + e] * ld_coh(src_o + static_cast<int64_t>(e) * G * kHeadDim + oi);
+    for (; e < S; e += R) add(wv[hh * S + e], ld_coh4(src_o + static_cast<int64_t>(e) * G * kHeadDim + oi));
     red[tid] = acc;
     __syncthreads();
-    if (tid < P) {
-      float o = 0.0f;
-      int r = 0;
-      for (; r + 8 <= R; r += 8) {
-        float t[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) t[k] = red[tid + P * (r + k)];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) o += t[k];
+    if (tid < P4) {
+      float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int r = 0; r < R; ++r) {
+        const float4 t = red[tid + P4 * r];
+        o.x += t.x; o.y += t.y; o.z += t.z; o.w += t.w;
       }
-      for (; r < R; ++r) o += red[tid + P * r];
-      dst[oi] = o / Ls[hh];
+      const float inv = 1.0f / Ls[hh];
+      *reinterpret_cast<float4*>(dst + oi) = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
     }
     __syncthreads();
   }
@@ -340,8 +373,8 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     int tiles_per_split, const Plan* __restrict__ plans, const Tables* __restrict__ tabg,
     const uint32_t* __restrict__ kc, const uint32_t* __restrict__ vc, const uint16_t* __restrict__ ks,
     const uint16_t* __restrict__ vs, int k_words, int n_nf, int n_splits, int n_mergers, int region_words,
-    int v_early, int v_off, float* __restrict__ part_o, float* __restrict__ part_ml,
-    unsigned* __restrict__ counters, float* __restrict__ out) {
+    int v_early, int v_off, float* __restrict__ part_o, float* __restrict__ part_l,
+    uint64_t* __restrict__ part_mt, unsigned* __restrict__ epochs, float* __restrict__ out) {
   constexpr int NT = 64 * W;
   constexpr bool kPipe = W == 4;                      // one wave per SIMD: prefetch and pipeline
   constexpr int PCOLS = 2 * G;                        // P columns: hi of heads 0..G-1, then lo
@@ -363,7 +396,7 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   __shared__ __attribute__((aligned(16))) float comb_m[G][W];
   __shared__ __attribute__((aligned(16))) float comb_l[G][W];
   __shared__ float alpha_s[W][G];
-  __shared__ unsigned arrive_s;
+  __shared__ float ms_s[G];
   __shared__ uint64_t wide_s;
   extern __shared__ __attribute__((aligned(16))) uint32_t dyn_s[];   // [W][region_words]
   uint32_t* kr = dyn_s + wave * region_words;                         // [k_words + 1][kKS]
@@ -377,35 +410,33 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   const Plan* P = plans + h;
 
   // ---- set-up loads first (small and shared by every workgroup), then the first tile's.
-  //      Waves 0..3 do the set-up; a wave-uniform branch lets the others skip it. ----
+  //      Every load is unconditional (clamped indices; waves 4..7 repeat those of waves 0..3
+  //      and discard them) and nothing loaded is used before all are issued, so they share
+  //      one round of memory latency. ----
   const bool setup_wave = __builtin_amdgcn_readfirstlane(wave) < 4;
+  const int st = tid & 255;   // set-up thread
   const uint8_t* gimg = tabg->lds_image[NF ? 1 : 0];
-  const int n_pairs = __builtin_amdgcn_readfirstlane(P->n_fields) >> 1;
-  uint4 timg = make_uint4(0u, 0u, 0u, 0u);
-  float qr[QPT], gr[QPT];
-  uint32_t fd_r = 0u, pd_r = 0u, rep4v = 0u, rep3v = 0u, hi5 = 0u;
-  uint2 lo5 = make_uint2(0u, 0u);
-  if (setup_wave) {
-    if (tid < kLdsTableBytes / 16) timg = reinterpret_cast<const uint4*>(gimg)[tid];
+  const uint4 timg = reinterpret_cast<const uint4*>(gimg)[st < kLdsTableBytes / 16 ? st : kLdsTableBytes / 16 - 1];
+  uint32_t qraw[QPT];
+  float gr[QPT];
 #pragma unroll
-    for (int j = 0; j < QPT; ++j) {
-      const int k = tid + 256 * j;
-      qr[j] = gr[j] = 0.0f;
-      if (k < G * kHeadDim) {
-        const int64_t qi = (static_cast<int64_t>(b) * n_q + h * G) * kHeadDim + k;
-        qr[j] = q_f32 ? static_cast<const float*>(qv)[qi] : __half2float(static_cast<const __half*>(qv)[qi]);
-        gr[j] = P->g[k % kHeadDim];
-      }
-    }
-    if (tid < kHeadDim) fd_r = P->fdim[tid];
-    pd_r = P->pdesc[lane];   // descriptor of pair `lane`
-    // sources of the per-workgroup pair tables (see below)
-    rep4v = reinterpret_cast<const uint32_t*>(gimg + pair_table_base(4))[tid];
-    rep3v = reinterpret_cast<const uint32_t*>(gimg + pair_table_base(3))[tid & 63];
-    const uint16_t* cb5 = reinterpret_cast<const uint16_t*>(gimg + single_table_base(5));
-    hi5 = cb5[tid >> 3];
-    lo5 = *reinterpret_cast<const uint2*>(cb5 + ((4 * tid) & 31));
+  for (int j = 0; j < QPT; ++j) {
+    const int k = st + 256 * j < G * kHeadDim ? st + 256 * j : G * kHeadDim - 1;
+    const int64_t qi = (static_cast<int64_t>(b) * n_q + h * G) * kHeadDim + k;
+    // fp32: the element; fp16: the aligned 32-bit word holding it (q is 4-byte aligned)
+    const int64_t byte = q_f32 ? 4 * qi : (2 * qi) & ~static_cast<int64_t>(3);
+    qraw[j] = *reinterpret_cast<const uint32_t*>(static_cast<const char*>(qv) + byte);
+    gr[j] = P->g[k % kHeadDim];
   }
+  const uint32_t fd_r = P->fdim[st & (kHeadDim - 1)];
+  const uint32_t pd_r = P->pdesc[lane];   // descriptor of pair `lane`
+  const int nf_r = P->n_fields;
+  // sources of the per-workgroup pair tables (see below)
+  const uint32_t rep4v = reinterpret_cast<const uint32_t*>(gimg + pair_table_base(4))[st];
+  const uint32_t rep3v = reinterpret_cast<const uint32_t*>(gimg + pair_table_base(3))[st & 63];
+  const uint16_t* cb5 = reinterpret_cast<const uint16_t*>(gimg + single_table_base(5));
+  const uint32_t hi5 = cb5[st >> 3];
+  const uint2 lo5 = *reinterpret_cast<const uint2*>(cb5 + ((4 * st) & 31));
 
   // K rows of tokens lane and lane + 64 (first 16 words), scales of tokens 16 tg + n, V segments
   uint4 ka[4], kb2[4];
@@ -413,33 +444,35 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     const int64_t tok0 = tile * kVTile;
     const uint4* krow0 = reinterpret_cast<const uint4*>(kc + (bh * cap + tok0 + lane) * k_words);
     const uint4* krow1 = reinterpret_cast<const uint4*>(kc + (bh * cap + tok0 + 64 + lane) * k_words);
+    const int last = (k_words >> 2) - 1;   // rows are whole 16-byte units; shorter rows repeat
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      if (4 * k < k_words) {
-        ka[k] = krow0[k];
-        kb2[k] = krow1[k];
+      ka[k] = krow0[k < last ? k : last];
+      kb2[k] = krow1[k < last ? k : last];
+    }
+  };
+  uint32_t skr[8], svr[8];   // fp16 bits of the scales of tokens 16 tg + n
+  auto load_scales = [&](int64_t tile) {
+#pragma unroll
+    for (int tg = 0; tg < 8; ++tg) {
+      const int64_t t = tile * kVTile + 16 * tg + n;
+      if (NF) {
+        skr[tg] = ks[(static_cast<int64_t>(b) * cap + t) * n_nf + h / 2];
+        svr[tg] = vs[(static_cast<int64_t>(b) * cap + t) * n_nf + h / 2];
+      } else {
+        skr[tg] = ks[bh * cap + t];
+        svr[tg] = vs[bh * cap + t];
       }
     }
   };
-  uint32_t skp[4], svp[4];   // fp16 scales of tokens 16 tg + n, two per register (tg even: low half)
-  auto load_scales = [&](int64_t tile) {
+  // after the K staging (which waits for the tile's K rows and scales), the scales are packed
+  // two per register for the rest of the tile
+  uint32_t skp[4], svp[4];
+  auto pack_scales = [&]() {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int64_t t0 = tile * kVTile + 32 * j + n, t1 = t0 + 16;
-      uint32_t k0, k1, v0, v1;
-      if (NF) {
-        k0 = ks[(static_cast<int64_t>(b) * cap + t0) * n_nf + h / 2];
-        k1 = ks[(static_cast<int64_t>(b) * cap + t1) * n_nf + h / 2];
-        v0 = vs[(static_cast<int64_t>(b) * cap + t0) * n_nf + h / 2];
-        v1 = vs[(static_cast<int64_t>(b) * cap + t1) * n_nf + h / 2];
-      } else {
-        k0 = ks[bh * cap + t0];
-        k1 = ks[bh * cap + t1];
-        v0 = vs[bh * cap + t0];
-        v1 = vs[bh * cap + t1];
-      }
-      skp[j] = k0 | (k1 << 16);
-      svp[j] = v0 | (v1 << 16);
+      skp[j] = (skr[2 * j] & 0xFFFFu) | (skr[2 * j + 1] << 16);
+      svp[j] = (svr[2 * j] & 0xFFFFu) | (svr[2 * j + 1] << 16);
     }
   };
   auto scale_of = [](const uint32_t (&pk)[4], int tg) {
@@ -465,7 +498,9 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
 #pragma unroll
     for (int j = 0; j < QPT; ++j) {
       const int k = tid + 256 * j;
-      if (k < G * kHeadDim) qs_s[k / kHeadDim][k % kHeadDim] = qr[j] * gr[j] * sigma;
+      const float qf = q_f32 ? __uint_as_float(qraw[j])
+                             : half_bits_to_float(static_cast<uint16_t>(qraw[j] >> (16 * (k & 1))));
+      if (k < G * kHeadDim) qs_s[k / kHeadDim][k % kHeadDim] = qf * gr[j] * sigma;
     }
     if (tid < kHeadDim) fdim_s[tid] = static_cast<uint8_t>(fd_r);
     if (tid < kBlocks) {
@@ -506,7 +541,7 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   // Thread t < 256 fills field t % 128 for heads t / 128, t / 128 + 2, ...
   if (setup_wave) {
     const int f = tid & 127, c = f >> 5, k = f & 31;
-    const bool live = f < 2 * n_pairs;
+    const bool live = f < (__builtin_amdgcn_readfirstlane(nf_r) & ~1);
     const int dim = fdim_s[f];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -558,6 +593,7 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
       dst[64] = x1.x; dst[kKS + 64] = x1.y; dst[2 * kKS + 64] = x1.z; dst[3 * kKS + 64] = x1.w;
     }
     kr[k_words * kKS + lane] = kr[k_words * kKS + 64 + lane] = 0u;
+    pack_scales();
     wave_sync();
     if constexpr (kPipe) {
       if (next < t_end) load_k(next);
@@ -609,27 +645,18 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
         dacc[4 * half + t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(P.aq, bk, dacc[4 * half + t], 0, 0, 0);
       }
     };
-    // software pipeline over the 8 (chunk, half) steps: the next step's row windows are read
-    // before this step's lookups, and chunk c + 1's parameters during chunk c's first half
-    {
-      KPar P[4];
-      P[0] = k_params(0, g, n, kp_s, a_s);
-      KWin Wc = k_windows(P[0], kr, 0);
-#pragma unroll
-      for (int hc = 0; hc < 8; ++hc) {
-        const int c = hc >> 1, half = hc & 1;
-        KWin Wn;
-        if (half == 0) {
-          Wn = k_windows(P[c], kr, 1);
-          if (c + 1 < 4) P[c + 1] = k_params(c + 1, g, n, kp_s, a_s);
-        } else if (c + 1 < 4) {
-          Wn = k_windows(P[c + 1], kr, 0);
-        }
-        uint32_t u[4][4];
-        k_lookups(P[c], Wc, c, u);
-        k_products(P[c], u, half);
-        if (hc + 1 < 8) Wc = Wn;
-      }
+    // per chunk: parameters, then the first half's row windows; the second half's windows are
+    // read before the first half's lookups
+#pragma unroll 1
+    for (int c = 0; c < 4; ++c) {
+      const KPar P = k_params(c, g, n, kp_s, a_s);
+      const KWin W0 = k_windows(P, kr, 0);
+      const KWin W1 = k_windows(P, kr, 1);
+      uint32_t u[4][4];
+      k_lookups(P, W0, c, u);
+      k_products(P, u, 0);
+      k_lookups(P, W1, c, u);
+      k_products(P, u, 1);
     }
     wave_sync();   // the key rows are read; the area takes the softmax weights (and V) next
     if (!v_early) dma_v(tile);
@@ -726,6 +753,9 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     }
   }
 
+  // tag base of this call's split partials (read before this workgroup publishes anything)
+  const unsigned epoch = __hip_atomic_load(epochs + bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
   // ---- merge the W waves of this workgroup: each wave adds its lo columns (n + G) into its
   //      hi columns (n) and writes them, with its (m, l), to LDS; after one barrier every
   //      thread combines the waves for its outputs ----
@@ -782,47 +812,30 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
       const int64_t p = (bh * n_splits + s) * G + hd;
       st_coh(part_o + p * kHeadDim + i, o);
       if (i == 0) {
-        st_coh(part_ml + p * 2 + 0, ms);
-        st_coh(part_ml + p * 2 + 1, l);
+        st_coh(part_l + p, l);
+        ms_s[hd] = ms;
       }
     }
   }
   if (n_splits == 1) return;
 
-  // ---- split merge: the last n_mergers workgroups of this (sequence, KV head) to finish
-  //      each merge one slice of the outputs; all but the very last wait (bounded) until the
-  //      counter has wrapped to 0, i.e. every split has stored its partial ----
-  unsigned* cnt = counters + bh;
+  // ---- split merge.  Each split publishes its maxima with this call's tag once its output
+  //      and sum stores have completed; the last n_mergers splits of this (sequence, KV head)
+  //      each merge one slice of the outputs, waiting (bounded) for every split's tag ----
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_s_waitcnt(0);   // this wave's partial stores have completed
   __syncthreads();
-  if (tid == 0) {
-    // wraps to 0 on the last of the n_splits arrivals
-    arrive_s = __builtin_amdgcn_atomic_inc32(cnt, static_cast<unsigned>(n_splits - 1), __ATOMIC_RELAXED, "agent");
-    if (arrive_s + 1u < static_cast<unsigned>(n_splits) &&
-        arrive_s + static_cast<unsigned>(n_mergers) >= static_cast<unsigned>(n_splits)) {
-      for (int polls = 0; polls < kMaxPolls; ++polls) {
-        if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) break;
-        __builtin_amdgcn_s_sleep(1);
-      }
-    }
+  const unsigned tag = epoch + 1u;
+  if (tid < G) {
+    const uint64_t v = (static_cast<uint64_t>(tag) << 32) | __float_as_uint(ms_s[tid]);
+    __hip_atomic_store(part_mt + (bh * n_splits + s) * G + tid, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  const int rank = static_cast<int>(arrive_s) - (n_splits - n_mergers);
+  const int rank = s - (n_splits - n_mergers);
   if (rank < 0) return;
   const int count = G * kHeadDim / n_mergers;
-  merge_slice<G, NT>(part_o + bh * n_splits * G * kHeadDim, part_ml + bh * n_splits * G * 2, n_splits,
+  merge_slice<G, NT>(part_o + bh * n_splits * G * kHeadDim, part_l + bh * n_splits * G,
+                     part_mt + bh * n_splits * G, tag, rank == 0 ? epochs + bh : nullptr, n_splits,
                      rank * count, count, reinterpret_cast<float*>(dyn_s), tid, out + out_base);
-}
-
-// Workgroups that merge the splits of one (sequence, KV head): a power of two, at most 64 and
-// at most S, small enough that the waiting mergers of all units occupy fewer than all compute
-// units (units x (K - 1) < CUs), so the splits they wait for can always be scheduled.
-inline int split_mergers(int S, int64_t units, int n_cu) {
-  int k = kMaxMergers;
-  while (k > 1 && (k > S || units * (k - 1) >= n_cu)) k >>= 1;
-  return k;
 }
 
 template <int G, int VB, int W>
@@ -836,14 +849,14 @@ hipError_t launch_gvw(kvq_cache* c, int layer, const void* q, int q_f32, float s
   const size_t dyn = static_cast<size_t>(W) * sh.region_words * sizeof(uint32_t);
   const Plan* plans = c->plans + static_cast<int64_t>(layer) * cfg.n_kv_heads;
   const bool nf = cfg.codec == KVQ_CODEC_NF16_B256;
-  const int mergers = split_mergers(S, static_cast<int64_t>(cfg.batch) * cfg.n_kv_heads, c->n_cu);
+  const int mergers = decode_split_mergers(S, static_cast<int64_t>(cfg.batch) * cfg.n_kv_heads, c->n_cu);
   if constexpr (VB == 4) {
     if (nf) {
       hipLaunchKernelGGL((decode_mfma<G, 4, true, W>), grid, dim3(64 * W), dyn, stream, q, q_f32, sigma,
                          len, cfg.n_kv_heads, c->cap, tps, plans, c->tables, layer_k_codes(c, layer),
                          layer_v_codes(c, layer), layer_k_scales(c, layer), layer_v_scales(c, layer),
                          c->k_words, c->n_nf_blocks, S, mergers, sh.region_words, sh.v_early, sh.v_off,
-                         c->part_o, c->part_ml, c->split_counters, out);
+                         c->part_o, c->part_l, c->part_mt, c->split_epochs, out);
       return hipGetLastError();
     }
   }
@@ -851,7 +864,7 @@ hipError_t launch_gvw(kvq_cache* c, int layer, const void* q, int q_f32, float s
                      len, cfg.n_kv_heads, c->cap, tps, plans, c->tables, layer_k_codes(c, layer),
                      layer_v_codes(c, layer), layer_k_scales(c, layer), layer_v_scales(c, layer),
                      c->k_words, c->n_nf_blocks, S, mergers, sh.region_words, sh.v_early, sh.v_off,
-                     c->part_o, c->part_ml, c->split_counters, out);
+                     c->part_o, c->part_l, c->part_mt, c->split_epochs, out);
   return hipGetLastError();
 }
 

@@ -78,8 +78,9 @@ struct kvq_cache {
   kvq::Tables* tables;         // device copy
   kvq::Tables host_tables;
   float* part_o;               // split partials [B][H][max_splits][G][128]
-  float* part_ml;              // [B][H][max_splits][G][2]
-  unsigned* split_counters;    // [B][H] finished-split counters (zero between calls)
+  float* part_l;               // split softmax sums [B][H][max_splits][G]
+  uint64_t* part_mt;           // split maxima | publication tag << 32 [B][H][max_splits][G]
+  unsigned* split_epochs;      // [B][H] tag base of the next call's split partials
   int max_splits;
   double* energy_scratch;      // [H][n_chunks][64]
   int64_t energy_scratch_chunks;
@@ -126,6 +127,16 @@ inline DecodeShape decode_shape(const kvq_cache* c) {
   return {4, 0, late, (G * kPS + 3) & ~3};
 }
 inline int decode_waves(const kvq_cache* c) { return decode_shape(c).waves; }
+
+// Workgroups that merge the S splits of one (sequence, KV head) in the decode kernel: a power
+// of two, at most 16 and at most S, small enough that the waiting mergers of all units occupy
+// fewer than all compute units (units x K < CUs), so the splits they wait for can always be
+// scheduled.  0: no such count (the call is rejected).
+inline int decode_split_mergers(int S, int64_t units, int n_cu) {
+  int k = 16;
+  while (k > 1 && (k > S || units * k >= n_cu)) k >>= 1;
+  return units * k < n_cu ? k : 0;
+}
 
 // Offsets of one layer's storage.
 inline uint32_t* layer_k_codes(kvq_cache* c, int layer) {
