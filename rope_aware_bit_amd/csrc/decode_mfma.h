@@ -56,24 +56,27 @@ constexpr int kOS = 10;           // LDS stride (floats) per dim of a wave's mer
 constexpr int kAS = 40;           // LDS row stride (halves) of the query operand: 32 + 8
 // LDS table region (bytes).  Pair tables hold fp16x2 (CB_w[c0], CB_w[c1]) at index c0 | c1 << w.
 // Random lookups into the larger tables would collide in LDS banks, so they are replicated:
-// the width-4 table 16 times (entry p of copy k at (p << 6) + 4 k, lane l reads copy l % 16)
-// and the width-3 table 32 times (entry p of copy k at (p << 7) + 4 k, lane l reads copy
-// l % 32).  The width-5 table is a single copy (entry p at p << 2), built per workgroup when
-// the plan uses it.  The prebuilt image holds the pair tables of widths 1..4 and the single
-// tables of widths 1..8.  Every base is a multiple of its table's extent, so an entry address
-// is "(p << shift) | copy offset | base".  Blocks of 6..8 bits use two single lookups.
+// the width-4 pair table 16 times (entry p of copy k at (p << 6) + 4 k, lane l reads copy
+// l % 16) and the width-3 pair table 32 times (entry p of copy k at (p << 7) + 4 k, lane l
+// reads copy l % 32).  Widths 5 and 6 use single tables (one fp16 in the low half of a 32-bit
+// slot) replicated 32 times the same way, built per workgroup when the plan uses them; a pair
+// costs two lookups.  The prebuilt image holds the pair tables of widths 1..4 and the single
+// tables of widths 1..8 (widths 7 and 8 use two single lookups there).  Every base is a
+// multiple of its table's extent, so an entry address is "(p << shift) | copy offset | base".
 constexpr int kRep4Base = 0;           // 16 KB
 constexpr int kRep3Base = 16384;       // 8 KB
-constexpr int kPair5Base = 24576;      // 4 KB
-constexpr int kImageBase = 28672;      // 2.5 KB
+constexpr int kSing6Base = 24576;      // 8 KB
+constexpr int kSing5Base = 32768;      // 4 KB
+constexpr int kImageBase = 36864;      // 2.5 KB
 constexpr int kTableRegion = kImageBase + kLdsTableBytes;
 
 // Key-product parameters of one (chunk c, lane group g): the four pairs of plan ranks
 // 16 c + 4 g + p, p = 0..3, held in LDS as 24 words
 //   [0..3]  table base of pair p (with the part of the lane's replica offset fixed by g)
 //   [4..7]  mask applied to 4 n (the rest of the replica offset; 0 for single tables)
-//   [8..11] extract width (2 w; 10 for w >= 5, whose lookups are replaced)
-//   [12..15] left shift of the extracted code (2 single table, 6 sixteen copies, 32: 7)
+//   [8..11] extract width (2 w for pair tables; w for widths 5, 6, whose first field is
+//           looked up here; 0 for widths 7, 8, whose lookups are replaced)
+//   [12..15] left shift of the extracted code (2 single copy, 6 sixteen copies, 32: 7)
 //   [16..19] bit shift of window A (pairs 0, 1) and B (pairs 2, 3); bit offset of pairs 1, 3
 //   [20..21] byte offset of the first word of windows A and B in a staged K tile
 constexpr int kParamWords = 24;
@@ -89,15 +92,19 @@ __device__ inline void write_pair_params(uint32_t* kp, int r, uint32_t desc) {
     base = kRep3Base | (64u * (g & 1));   // lane & 31 = n + 16 (g & 1)
     mask = 0x3Cu;
     shift = 7u;
-  } else if (w >= 5u) {
-    base = kPair5Base;
+  } else if (w == 5u || w == 6u) {
+    base = (w == 5u ? kSing5Base : kSing6Base) | (64u * (g & 1));
+    mask = 0x3Cu;
+    shift = 7u;
+  } else if (w >= 7u) {
+    base = kImageBase;   // placeholder read, replaced
   } else {
     base = kImageBase + static_cast<uint32_t>(pair_table_base(static_cast<int>(w)));
   }
   uint32_t* blk = kp + (4 * c + g) * kParamWords;
   blk[p] = base;
   blk[4 + p] = mask;
-  blk[8 + p] = w <= 5u ? 2u * w : 10u;
+  blk[8 + p] = w <= 4u ? 2u * w : w <= 6u ? w : 0u;
   blk[12 + p] = shift;
   if ((p & 1) == 0) {
     const int k = p >> 1;   // window A or B
@@ -136,6 +143,22 @@ __device__ inline float row_sum16(float v) {
   return v;
 }
 
+// Global-to-LDS copy of 16 bytes per lane to the LDS bytes lds + 16 lane .. + 15 (lds is
+// wave-uniform).  Issued from assembly, so the compiler neither counts it nor waits for it
+// before other LDS accesses (it cannot prove them disjoint); the wave that reads the copy waits
+// for it with s_waitcnt vmcnt(0).  Only safe where the compiler has no loads of its own in
+// flight whose completion it would then count wrongly, and M0 is declared written.
+__device__ inline void dma16(const void* g, const void* lds) {
+  typedef __attribute__((address_space(3))) char lds_char;
+  const uint32_t base =
+      __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<size_t>((lds_char*)lds)));
+  uint32_t m0;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               : "={m0}"(m0)
+               : "v"(g), "s"(base)
+               : "memory");
+}
+
 // Max / sum over the 64 lanes of a wave (rows through DPP, then the four row results).
 __device__ inline float wave_max(float v) {
   v = row_max16(v);
@@ -154,13 +177,25 @@ __device__ inline float wave_sum(float v) {
   return (a + b) + (c + d);
 }
 
-// Orders a wave's LDS writes before its later LDS reads of other lanes' data (LDS
-// instructions of one wave execute in issue order; this keeps the compiler from moving
-// them across).
+// Orders a wave's LDS writes before its later LDS reads of other lanes' data: LDS
+// instructions of one wave execute in issue order, so only the compiler must be kept from
+// moving memory accesses across.  (A memory-model fence would also wait for the wave's
+// global-to-LDS copies in flight.)
 __device__ inline void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  asm volatile("" ::: "memory");
   __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier for LDS data: this wave's LDS accesses complete (lgkmcnt(0)), then all
+// waves meet.  LDS has no caches, so the data written before is visible after.  Unlike
+// __syncthreads it does not wait for global loads or global-to-LDS copies in flight; LDS
+// written by such copies must be waited for (vmcnt) by the wave that reads it.
+__device__ inline void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // Device-coherent (agent-scope) stores / loads of split partials.
@@ -401,7 +436,15 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   extern __shared__ __attribute__((aligned(16))) uint32_t dyn_s[];   // [W][region_words]
   uint32_t* kr = dyn_s + wave * region_words;                         // [k_words + 1][kKS]
   _Float16* pw = reinterpret_cast<_Float16*>(kr);                     // [PCOLS][kPS], after keys
-  uint32_t* vbuf = kr + v_off;                                        // [512][VB] V tile
+  // [512][VB] V tile, written by global-to-LDS loads.  With 8 waves it is an LDS object of its
+  // own, so the compiler need not wait for those loads before reading the K tile.
+  uint32_t* vbuf;
+  if constexpr (W == 8) {
+    __shared__ __attribute__((aligned(16))) uint32_t vbuf_s[W][kVTile * 4 * VB];
+    vbuf = vbuf_s[wave];
+  } else {
+    vbuf = kr + v_off;
+  }
   float (*qs_s)[kHeadDim] = reinterpret_cast<float (*)[kHeadDim]>(dyn_s);   // set-up only
 
   const int64_t n_tiles = (len + kVTile - 1) / kVTile;
@@ -434,9 +477,8 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   // sources of the per-workgroup pair tables (see below)
   const uint32_t rep4v = reinterpret_cast<const uint32_t*>(gimg + pair_table_base(4))[st];
   const uint32_t rep3v = reinterpret_cast<const uint32_t*>(gimg + pair_table_base(3))[st & 63];
-  const uint16_t* cb5 = reinterpret_cast<const uint16_t*>(gimg + single_table_base(5));
-  const uint32_t hi5 = cb5[st >> 3];
-  const uint2 lo5 = *reinterpret_cast<const uint2*>(cb5 + ((4 * st) & 31));
+  // rows 0..31: CB_5[st]; rows 32..95: CB_6[st - 32] (higher threads read a valid entry, unused)
+  const uint32_t cb56 = reinterpret_cast<const uint16_t*>(gimg + single_table_base(st < 32 ? 5 : 6))[st < 32 ? st : (st - 32) & 63];
 
   // K rows of tokens lane and lane + 64 (first 16 words), scales of tokens 16 tg + n, V segments
   uint4 ka[4], kb2[4];
@@ -482,15 +524,23 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   // area: 2 VB copies of 64 lanes x 16 bytes, waited for with s_waitcnt vmcnt(0) before use
   auto dma_v = [&](int64_t tile) {
     const uint32_t* vt = vc + (bh * (cap / kVTile) + tile) * (kVTile * KWV);
+    // 8 waves: every load of this wave has been consumed by now; saying so keeps the compiler
+    // from waiting later (for loads it would believe in flight, and so for the copy)
+    if constexpr (W == 8) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 #pragma unroll
-    for (int i = 0; i < 2 * VB; ++i)
-      __builtin_amdgcn_global_load_lds((glb_ptr)(vt + 256 * i + 4 * lane), (lds_ptr)(vbuf + 256 * i), 16, 0, 0);
+    for (int i = 0; i < 2 * VB; ++i) {
+      if constexpr (W == 8)
+        dma16(vt + 256 * i + 4 * lane, vbuf + 256 * i);
+      else
+        __builtin_amdgcn_global_load_lds((glb_ptr)(vt + 256 * i + 4 * lane), (lds_ptr)(vbuf + 256 * i), 16, 0, 0);
+    }
   };
-  if (t_begin + wave < t_end) {
-    load_k(t_begin + wave);
-    load_scales(t_begin + wave);
-    if (v_early) dma_v(t_begin + wave);
-  }
+  // the first tile's K rows and scales are loaded unconditionally (a wave without a tile of
+  // its own reads the split's last tile and discards it); its V tile is copied once the
+  // set-up data has been used, so waiting for the set-up loads never waits for it
+  const int64_t t0 = t_begin + wave < t_end ? t_begin + wave : t_end - 1;
+  load_k(t0);
+  load_scales(t0);
 
   // ---- set-up: tables, scaled query, field dims and pair descriptors into LDS ----
   if (setup_wave) {
@@ -524,18 +574,21 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
         }
       }
     }
-    // pair table of width 5 when the plan stores such blocks: entry (c1 << 5) | c0 holds
-    // (CB_5[c0], CB_5[c1]); thread t fills 4 consecutive c0 of one c1
-    const uint64_t uses5 = __ballot((pd_r >> 16) == 5u);
-    const uint64_t wide = __ballot((pd_r >> 16) >= 6u);
+    // single tables of widths 5 and 6 when the plan stores such blocks: thread t < 96 writes
+    // the 32 copies of one entry
+    const uint32_t pw = pd_r >> 16;
+    const uint64_t uses56 = __ballot(pw == 5u || pw == 6u);
+    const uint64_t wide = __ballot(pw >= 5u);
     if (tid == 0) wide_s = wide;
-    if (uses5) {
-      const uint32_t hi = hi5 << 16;
-      const uint4 v = make_uint4((lo5.x & 0xFFFFu) | hi, (lo5.x >> 16) | hi, (lo5.y & 0xFFFFu) | hi, (lo5.y >> 16) | hi);
-      *reinterpret_cast<uint4*>(tab_s + kPair5Base + 4 * (4 * tid)) = v;
+    if (uses56 && tid < 96) {
+      const uint4 v = make_uint4(cb56, cb56, cb56, cb56);
+      char* row = tab_s + (tid < 32 ? kSing5Base + (tid << 7) : kSing6Base + ((tid - 32) << 7));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) *reinterpret_cast<uint4*>(row + 16 * ((j + tid) & 7)) = v;
     }
   }
-  __syncthreads();
+  lds_barrier();
+  if (W == 4 && v_early) dma_v(t0);   // (8 waves: copied after the tile's K rows are staged)
   // query operand of the key product: a_s[c][m][k] = hi (m even) or lo (m odd) fp16 part of
   // q'[m / 2][dim of field 32 c + k]; rows of heads >= G and fields past the stored ones are 0.
   // Thread t < 256 fills field t % 128 for heads t / 128, t / 128 + 2, ...
@@ -553,8 +606,8 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     }
   }
   const uint32_t lb = (lane & 31u) << 2;   // this lane's replica offset
-  __syncthreads();
-  const uint64_t uses_wide = wide_s;       // pairs (plan ranks) with blocks of 6..8 bits
+  lds_barrier();
+  const uint64_t uses_wide = wide_s;       // pairs (plan ranks) with blocks of 5..8 bits
 
   // ---- per-wave state: lane (n, g) keeps heads 2g, 2g + 1 ----
   const int h0 = 2 * g, h1 = 2 * g + 1;
@@ -564,14 +617,15 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) oacc[dt] = f4{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t tile = t_begin + wave; tile < t_end; tile += W) {
+  // one 128-token tile of this wave; the first is peeled out of the loop, so that the compiler
+  // counts its loads in flight exactly (no merge at a loop header)
+  auto tile_body = [&](int64_t tile, bool first) __attribute__((always_inline)) {
     const int64_t tok0 = tile * kVTile;
     const int64_t next = tile + W;
     if constexpr (!kPipe) {
-      if (tile != t_begin + wave) {   // later tiles: loaded here (the other wave hides the wait)
+      if (!first) {   // later tiles: loaded here (the other wave hides the wait)
         load_k(tile);
         load_scales(tile);
-        if (v_early) dma_v(tile);
       }
     }
     // -- stage the K rows in LDS word-major (kr[d * kKS + tau] = word d of token tau), then a
@@ -584,7 +638,9 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
         dst[64] = kb2[k].x; dst[kKS + 64] = kb2[k].y; dst[2 * kKS + 64] = kb2[k].z; dst[3 * kKS + 64] = kb2[k].w;
       }
     }
-    for (int k = 4; 4 * k < k_words; ++k) {   // rows longer than 16 words (more than 4 bits)
+#pragma unroll
+    for (int k = 4; k < 8; ++k) {   // rows longer than 16 words (more than 4 bits)
+      if (4 * k >= k_words) break;
       const uint4* krow0 = reinterpret_cast<const uint4*>(kc + (bh * cap + tok0 + lane) * k_words);
       const uint4* krow1 = reinterpret_cast<const uint4*>(kc + (bh * cap + tok0 + 64 + lane) * k_words);
       const uint4 x0 = krow0[k], x1 = krow1[k];
@@ -595,6 +651,9 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     kr[k_words * kKS + lane] = kr[k_words * kKS + 64 + lane] = 0u;
     pack_scales();
     wave_sync();
+    // 8 waves: the V tile is copied now, when no other load of this wave is in flight, and
+    // arrives during the key product
+    if constexpr (W == 8) dma_v(tile);
     if constexpr (kPipe) {
       if (next < t_end) load_k(next);
     }
@@ -617,14 +676,23 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
         u[t][3] = lds_u32(tab_s, (__builtin_amdgcn_ubfe(xb, P.rel3, P.bw[3]) << P.ps[3]) | P.pb[3]);
       }
       if ((uses_wide >> (16 * c)) & 0xFFFFull) {
-        // blocks of 6..8 bits: two single lookups (lanes whose pair is narrower skip)
+        // blocks of 5..8 bits (lanes whose pair is narrower skip): widths 5, 6 add the second
+        // field from the replicated single table; widths 7, 8 take two single lookups
         const char* tabi = tab_s + kImageBase;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           const uint32_t wp = pd_s[16 * c + 4 * g + p] >> 16;
-          if (wp >= 6u) {
+          const uint32_t rel = (p & 1) ? (p == 1 ? P.rel1 : P.rel3) : 0u;
+          if (wp == 5u || wp == 6u) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const uint32_t x = (p < 2) ? __builtin_amdgcn_alignbit(Wn.ha[t], Wn.la[t], P.shA)
+                                         : __builtin_amdgcn_alignbit(Wn.hb[t], Wn.lb[t], P.shB);
+              const uint32_t f1 = __builtin_amdgcn_ubfe(x, rel + wp, wp);
+              u[t][p] |= lds_u32(tab_s, (f1 << 7) | P.pb[p]) << 16;
+            }
+          } else if (wp >= 7u) {
             const uint32_t sb = static_cast<uint32_t>(kLdsTableBytes) - (4u << wp);
-            const uint32_t rel = (p & 1) ? (p == 1 ? P.rel1 : P.rel3) : 0u;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
               const uint32_t x = (p < 2) ? __builtin_amdgcn_alignbit(Wn.ha[t], Wn.la[t], P.shA)
@@ -659,7 +727,7 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
       k_products(P, u, 1);
     }
     wave_sync();   // the key rows are read; the area takes the softmax weights (and V) next
-    if (!v_early) dma_v(tile);
+    if (W == 4 && !v_early) dma_v(tile);
 
     // -- online softmax: lane (n, g) holds heads 2g and 2g + 1 of tokens 16 tg + n --
     float L0[8], L1[8];
@@ -751,6 +819,10 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     if constexpr (kPipe) {
       if (v_early && next < t_end) dma_v(next);
     }
+  };
+  if (t_begin + wave < t_end) {
+    tile_body(t_begin + wave, true);
+    for (int64_t tile = t_begin + wave + W; tile < t_end; tile += W) tile_body(tile, false);
   }
 
   // tag base of this call's split partials (read before this workgroup publishes anything)
@@ -781,7 +853,7 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
       if (n < G) ow[(dt * 16 + 4 * g + r) * kOS + n] = oacc[dt][r] + other;
     }
   }
-  __syncthreads();
+  lds_barrier();
   const int64_t out_base = (static_cast<int64_t>(b) * n_q + h * G) * kHeadDim;
   for (int idx = tid; idx < G * kHeadDim; idx += NT) {
     const int hd = idx / kHeadDim, i = idx % kHeadDim;
@@ -872,7 +944,10 @@ template <int G, int VB>
 hipError_t launch_gv(kvq_cache* c, int layer, const void* q, int q_f32, float sigma, float* out,
                      int S, hipStream_t stream) {
   const DecodeShape sh = decode_shape(c);
-  if (sh.waves == 8) return launch_gvw<G, VB, 8>(c, layer, q, q_f32, sigma, out, S, sh, stream);
+  if constexpr (VB <= 4) {   // wider V tiles never leave room for 8 waves
+    if (sh.waves == 8) return launch_gvw<G, VB, 8>(c, layer, q, q_f32, sigma, out, S, sh, stream);
+  }
+  if (sh.waves != 4) return hipErrorInvalidConfiguration;
   return launch_gvw<G, VB, 4>(c, layer, q, q_f32, sigma, out, S, sh, stream);
 }
 

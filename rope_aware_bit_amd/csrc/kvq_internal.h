@@ -101,14 +101,15 @@ hipError_t launch_decode_mfma(kvq_cache* c, int layer, const void* q, int dtype,
 int auto_splits_mfma(const kvq_cache* c, int64_t len);
 
 // Launch shape of the decode kernel for a cache: waves per workgroup (8 = two per SIMD, or 4),
-// whether each wave's V tile has its own LDS area (copied at tile start) or reuses the K area
-// after the key product, the LDS words of each wave's region and the V area's offset in it.
+// whether each wave's V tile has an LDS area of its own (copied at tile start; a static array
+// with 8 waves) or reuses the K area after the key product, the dynamic LDS words of each
+// wave's region and the V area's offset in it (4 waves).
 struct DecodeShape {
   int waves, v_early, region_words, v_off;
 };
 inline DecodeShape decode_shape(const kvq_cache* c) {
   constexpr int kKS = 144, kPS = 136, kOS = 10, kLds = 163840;
-  constexpr int kStaticBase = 28672 + 2560 + 4 * 16 * 40 * 2 + 128 + 64 * 4 + 16 * 24 * 4 + 64;
+  constexpr int kStaticBase = 36864 + 2560 + 4 * 16 * 40 * 2 + 128 + 64 * 4 + 16 * 24 * 4 + 64;
   const int G = c->group;
   const int vb = c->cfg.codec == KVQ_CODEC_NF16_B256 ? 4 : c->cfg.v_bits;
   int kpart = (c->k_words + 1) * kKS;
@@ -117,13 +118,14 @@ inline DecodeShape decode_shape(const kvq_cache* c) {
   if (kpart < G * 128) kpart = G * 128;
   kpart = (kpart + 3) & ~3;
   const int vwords = 512 * vb;
-  const int early = kpart + vwords;
+  {
+    const int stat = kStaticBase + 16 * 8 * G + 64 * G + 4 * 8 * vwords;
+    if (stat + 4 * 8 * kpart <= kLds) return {8, 1, kpart, 0};
+  }
+  const int stat = kStaticBase + 16 * 4 * G + 64 * G;
+  if (stat + 4 * 4 * (kpart + vwords) <= kLds) return {4, 1, kpart + vwords, kpart};
   int late = ((G * kPS + 3) & ~3) + vwords;
   if (late < kpart) late = kpart;
-  for (int w : {8, 4}) {
-    const int stat = kStaticBase + 16 * w * G + 64 * G;
-    if (stat + 4 * w * early <= kLds) return {w, 1, early, kpart};
-  }
   return {4, 0, late, (G * kPS + 3) & ~3};
 }
 inline int decode_waves(const kvq_cache* c) { return decode_shape(c).waves; }
