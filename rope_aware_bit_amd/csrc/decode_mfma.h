@@ -70,8 +70,15 @@ constexpr int kSing5Base = 32768;      // 4 KB
 constexpr int kImageBase = 36864;      // 2.5 KB
 constexpr int kTableRegion = kImageBase + kLdsTableBytes;
 
-// Key-product parameters of one (chunk c, lane group g): the four pairs of plan ranks
-// 16 c + 4 g + p, p = 0..3, held in LDS as 24 words
+// Pairs of plan ranks go to the product slots in pairs of pairs: in chunk c, lane group g
+// handles ranks 16 c + 2 g, + 1 (positions 0, 1: one row window) and 16 c + 8 + 2 g, + 1
+// (positions 2, 3: the other window).  The widest pairs (lowest ranks) thus share positions
+// 0 and 1 across the lane groups.  Field f of the plan sits in chunk f / 32 at slot
+// k = 8 g + 2 p + (f % 2) of the 32-field product.
+__host__ __device__ constexpr int slot_field(int c, int k) {
+  return 32 * c + 4 * (k >> 3) + 2 * ((k >> 1) & 1) + 16 * ((k >> 2) & 1) + (k & 1);
+}
+// Key-product parameters of one (chunk c, lane group g): its four pairs, held in LDS as 24 words
 //   [0..3]  table base of pair p (with the part of the lane's replica offset fixed by g)
 //   [4..7]  mask applied to 4 n (the rest of the replica offset; 0 for single tables)
 //   [8..11] extract width (2 w for pair tables; w for widths 5, 6, whose first field is
@@ -79,9 +86,10 @@ constexpr int kTableRegion = kImageBase + kLdsTableBytes;
 //   [12..15] left shift of the extracted code (2 single copy, 6 sixteen copies, 32: 7)
 //   [16..19] bit shift of window A (pairs 0, 1) and B (pairs 2, 3); bit offset of pairs 1, 3
 //   [20..21] byte offset of the first word of windows A and B in a staged K tile
+//   [22]    block width of pair p in byte p
 constexpr int kParamWords = 24;
 __device__ inline void write_pair_params(uint32_t* kp, int r, uint32_t desc) {
-  const int c = r >> 4, g = (r >> 2) & 3, p = r & 3;
+  const int c = r >> 4, g = (r & 7) >> 1, p = (r & 1) | (((r >> 3) & 1) << 1);
   const uint32_t w = desc >> 16, off = desc & 0xFFFFu;
   uint32_t base, mask = 0u, shift = 2u;
   if (w == 4u) {
@@ -106,6 +114,7 @@ __device__ inline void write_pair_params(uint32_t* kp, int r, uint32_t desc) {
   blk[4 + p] = mask;
   blk[8 + p] = w <= 4u ? 2u * w : w <= 6u ? w : 0u;
   blk[12 + p] = shift;
+  reinterpret_cast<uint8_t*>(blk + 22)[p] = static_cast<uint8_t>(w);
   if ((p & 1) == 0) {
     const int k = p >> 1;   // window A or B
     blk[16 + k] = off & 31u;
@@ -348,11 +357,11 @@ __device__ __attribute__((always_inline)) inline void merge_slice(
 }
 
 // Key product of lane (n, g) in chunk c: the query operand, the lookup parameters of the
-// lane's four pairs (plan ranks 16 c + 4 g .. + 3); and, per half of the tile, the two 32-bit
+// lane's four pairs (positions 0..3, see slot_field); and, per half of the tile, the two 32-bit
 // row windows (pairs 0-1 and 2-3) of its four tokens 16 tg + n, tg = 4 half .. 4 half + 3.
 struct KPar {
   h8 aq;
-  uint32_t shA, shB, rel1, rel3, baseA, baseB;
+  uint32_t shA, shB, rel1, rel3, baseA, baseB, wid;
   uint32_t bw[4], pb[4], ps[4];
 };
 struct KWin {
@@ -369,7 +378,7 @@ __device__ __attribute__((always_inline)) inline KPar k_params(int c, int g, int
   const uint4 w4 = *reinterpret_cast<const uint4*>(blk + 8);
   const uint4 s4 = *reinterpret_cast<const uint4*>(blk + 12);
   const uint4 x4 = *reinterpret_cast<const uint4*>(blk + 16);
-  const uint2 y2 = *reinterpret_cast<const uint2*>(blk + 20);
+  const uint4 y4 = *reinterpret_cast<const uint4*>(blk + 20);
   const uint32_t n4 = 4u * static_cast<uint32_t>(n);
   k.pb[0] = (n4 & m4.x) | b4.x;
   k.pb[1] = (n4 & m4.y) | b4.y;
@@ -381,8 +390,9 @@ __device__ __attribute__((always_inline)) inline KPar k_params(int c, int g, int
   k.shB = x4.y;
   k.rel1 = x4.z;
   k.rel3 = x4.w;
-  k.baseA = y2.x + n4;
-  k.baseB = y2.y + n4;
+  k.baseA = y4.x + n4;
+  k.baseB = y4.y + n4;
+  k.wid = y4.z;
   return k;
 }
 
@@ -432,7 +442,7 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   __shared__ __attribute__((aligned(16))) float comb_l[G][W];
   __shared__ float alpha_s[W][G];
   __shared__ float ms_s[G];
-  __shared__ uint64_t wide_s;
+  __shared__ uint64_t wide_s, w56_s, w78_s;
   extern __shared__ __attribute__((aligned(16))) uint32_t dyn_s[];   // [W][region_words]
   uint32_t* kr = dyn_s + wave * region_words;                         // [k_words + 1][kKS]
   _Float16* pw = reinterpret_cast<_Float16*>(kr);                     // [PCOLS][kPS], after keys
@@ -577,10 +587,15 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     // single tables of widths 5 and 6 when the plan stores such blocks: thread t < 96 writes
     // the 32 copies of one entry
     const uint32_t pw = pd_r >> 16;
-    const uint64_t uses56 = __ballot(pw == 5u || pw == 6u);
     const uint64_t wide = __ballot(pw >= 5u);
-    if (tid == 0) wide_s = wide;
-    if (uses56 && tid < 96) {
+    const uint64_t w56 = __ballot(pw == 5u || pw == 6u);
+    const uint64_t w78 = __ballot(pw >= 7u);
+    if (tid == 0) {
+      wide_s = wide;
+      w56_s = w56;
+      w78_s = w78;
+    }
+    if (w56 && tid < 96) {
       const uint4 v = make_uint4(cb56, cb56, cb56, cb56);
       char* row = tab_s + (tid < 32 ? kSing5Base + (tid << 7) : kSing6Base + ((tid - 32) << 7));
 #pragma unroll
@@ -593,7 +608,7 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   // q'[m / 2][dim of field 32 c + k]; rows of heads >= G and fields past the stored ones are 0.
   // Thread t < 256 fills field t % 128 for heads t / 128, t / 128 + 2, ...
   if (setup_wave) {
-    const int f = tid & 127, c = f >> 5, k = f & 31;
+    const int c = (tid >> 5) & 3, k = tid & 31, f = slot_field(c, k);
     const bool live = f < (__builtin_amdgcn_readfirstlane(nf_r) & ~1);
     const int dim = fdim_s[f];
 #pragma unroll
@@ -608,6 +623,8 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   const uint32_t lb = (lane & 31u) << 2;   // this lane's replica offset
   lds_barrier();
   const uint64_t uses_wide = wide_s;       // pairs (plan ranks) with blocks of 5..8 bits
+  const uint64_t uses_w56 = w56_s;         // pairs with blocks of 5 or 6 bits
+  const uint64_t uses_w78 = w78_s;         // pairs with blocks of 7 or 8 bits
 
   // ---- per-wave state: lane (n, g) keeps heads 2g, 2g + 1 ----
   const int h0 = 2 * g, h1 = 2 * g + 1;
@@ -666,40 +683,65 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
 #pragma unroll
     for (int tg = 0; tg < 8; ++tg) dacc[tg] = f4{0.f, 0.f, 0.f, 0.f};
     auto k_lookups = [&](const KPar& P, const KWin& Wn, int c, uint32_t (&u)[4][4]) {
+      uint32_t xa[4], xb[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const uint32_t xa = __builtin_amdgcn_alignbit(Wn.ha[t], Wn.la[t], P.shA);
-        const uint32_t xb = __builtin_amdgcn_alignbit(Wn.hb[t], Wn.lb[t], P.shB);
-        u[t][0] = lds_u32(tab_s, (__builtin_amdgcn_ubfe(xa, 0u, P.bw[0]) << P.ps[0]) | P.pb[0]);
-        u[t][1] = lds_u32(tab_s, (__builtin_amdgcn_ubfe(xa, P.rel1, P.bw[1]) << P.ps[1]) | P.pb[1]);
-        u[t][2] = lds_u32(tab_s, (__builtin_amdgcn_ubfe(xb, 0u, P.bw[2]) << P.ps[2]) | P.pb[2]);
-        u[t][3] = lds_u32(tab_s, (__builtin_amdgcn_ubfe(xb, P.rel3, P.bw[3]) << P.ps[3]) | P.pb[3]);
+        xa[t] = __builtin_amdgcn_alignbit(Wn.ha[t], Wn.la[t], P.shA);
+        xb[t] = __builtin_amdgcn_alignbit(Wn.hb[t], Wn.lb[t], P.shB);
+        u[t][0] = lds_u32(tab_s, (__builtin_amdgcn_ubfe(xa[t], 0u, P.bw[0]) << P.ps[0]) | P.pb[0]);
+        u[t][1] = lds_u32(tab_s, (__builtin_amdgcn_ubfe(xa[t], P.rel1, P.bw[1]) << P.ps[1]) | P.pb[1]);
+        u[t][2] = lds_u32(tab_s, (__builtin_amdgcn_ubfe(xb[t], 0u, P.bw[2]) << P.ps[2]) | P.pb[2]);
+        u[t][3] = lds_u32(tab_s, (__builtin_amdgcn_ubfe(xb[t], P.rel3, P.bw[3]) << P.ps[3]) | P.pb[3]);
       }
       if ((uses_wide >> (16 * c)) & 0xFFFFull) {
-        // blocks of 5..8 bits (lanes whose pair is narrower skip): widths 5, 6 add the second
-        // field from the replicated single table; widths 7, 8 take two single lookups
-        const char* tabi = tab_s + kImageBase;
+        // blocks of 5..8 bits, without branches per pair (lanes whose pair is narrower read a
+        // placeholder and keep their value): widths 5, 6 add the second field from their
+        // replicated single table; widths 7, 8 take both fields from the image's single tables
+        // widths 7, 8 have the lowest ranks, so in practice only positions 0, 1 hold them (the
+        // ranks of positions 2, 3 are bits 8..15 of the chunk's mask)
+        const uint32_t m78 = static_cast<uint32_t>(uses_w78 >> (16 * c));
+        uint32_t v[4][4];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          const uint32_t wp = pd_s[16 * c + 4 * g + p] >> 16;
+          const uint32_t w = (P.wid >> (8 * p)) & 0xFFu;
           const uint32_t rel = (p & 1) ? (p == 1 ? P.rel1 : P.rel3) : 0u;
-          if (wp == 5u || wp == 6u) {
+          const bool is56 = w - 5u <= 1u;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              const uint32_t x = (p < 2) ? __builtin_amdgcn_alignbit(Wn.ha[t], Wn.la[t], P.shA)
-                                         : __builtin_amdgcn_alignbit(Wn.hb[t], Wn.lb[t], P.shB);
-              const uint32_t f1 = __builtin_amdgcn_ubfe(x, rel + wp, wp);
-              u[t][p] |= lds_u32(tab_s, (f1 << 7) | P.pb[p]) << 16;
-            }
-          } else if (wp >= 7u) {
-            const uint32_t sb = static_cast<uint32_t>(kLdsTableBytes) - (4u << wp);
+          for (int t = 0; t < 4; ++t) {
+            const uint32_t f1 = __builtin_amdgcn_ubfe(p < 2 ? xa[t] : xb[t], rel + w, w);
+            v[t][p] = lds_u32(tab_s, is56 ? (f1 << 7) | P.pb[p] : static_cast<uint32_t>(kImageBase));
+          }
+        }
+        auto singles78 = [&](int p, uint32_t (&lo)[4], uint32_t (&hi)[4]) {
+          const uint32_t w = (P.wid >> (8 * p)) & 0xFFu;
+          const uint32_t rel = (p & 1) ? (p == 1 ? P.rel1 : P.rel3) : 0u;
+          const bool is78 = w >= 7u;
+          const uint32_t sb = kImageBase + static_cast<uint32_t>(kLdsTableBytes) - (4u << (is78 ? w : 7u));
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              const uint32_t x = (p < 2) ? __builtin_amdgcn_alignbit(Wn.ha[t], Wn.la[t], P.shA)
-                                         : __builtin_amdgcn_alignbit(Wn.hb[t], Wn.lb[t], P.shB);
-              const uint32_t f0 = __builtin_amdgcn_ubfe(x, rel, wp);
-              const uint32_t f1 = __builtin_amdgcn_ubfe(x, rel + wp, wp);
-              u[t][p] = lds_u16(tabi, (f0 << 1) | sb) | (lds_u16(tabi, (f1 << 1) | sb) << 16);
+          for (int t = 0; t < 4; ++t) {
+            const uint32_t x = p < 2 ? xa[t] : xb[t];
+            const uint32_t f0 = __builtin_amdgcn_ubfe(x, rel, w), f1 = __builtin_amdgcn_ubfe(x, rel + w, w);
+            lo[t] = lds_u16(tab_s, is78 ? (f0 << 1) + sb : static_cast<uint32_t>(kImageBase));
+            hi[t] = lds_u16(tab_s, is78 ? (f1 << 1) + sb : static_cast<uint32_t>(kImageBase));
+          }
+        };
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t w = (P.wid >> (8 * p)) & 0xFFu;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) u[t][p] = w - 5u <= 1u ? u[t][p] | (v[t][p] << 16) : u[t][p];
+        }
+#pragma unroll
+        for (int pp = 0; pp < 4; pp += 2) {
+          if (m78 & (pp == 0 ? 0xFFu : 0xFF00u)) {
+            uint32_t lo[2][4], hi[2][4];
+            singles78(pp, lo[0], hi[0]);
+            singles78(pp + 1, lo[1], hi[1]);
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              const uint32_t w = (P.wid >> (8 * (pp + q))) & 0xFFu;
+#pragma unroll
+              for (int t = 0; t < 4; ++t) u[t][pp + q] = w >= 7u ? lo[q][t] | (hi[q][t] << 16) : u[t][pp + q];
             }
           }
         }
