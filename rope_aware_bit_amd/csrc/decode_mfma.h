@@ -7,34 +7,29 @@
 // The 256-value absmax codec (NQKV review, "What carries the argument") uses one
 // scale per 256 values (two KV heads share it) and its 16-level table.
 //
-// Work decomposition.  One workgroup of 4 waves per (context split, KV head,
-// sequence); each wave walks 128-token tiles of the split on its own, keeping
-// its own running max / sum / output, and the waves are merged through LDS at
-// the end.  Splits are merged in two levels inside the same kernel: the last
-// workgroup of each group of 16 consecutive splits merges the group, and the
-// last group merger merges the groups, always in split order.
+// Work decomposition.  One workgroup of W waves (8: two per SIMD, or 4) per (context split,
+// KV head, sequence); each wave walks 128-token tiles of the split on its own, keeping its own
+// running max / sum / output, and the waves are merged through LDS at the end.  The last
+// splits of each (sequence, KV head) to finish merge the splits, each one slice of the
+// outputs, always in split order.
 //
-// Keys (lane = token).  The K rows of a tile are staged in LDS word-major.  Every
-// stored RoPE block contributes a pair of fields (p0, p1) of the same width w;
-// the pair's 2w bits are cut out of the row with one funnel shift at a
-// wave-uniform offset and looked up in an LDS table of fp16 pairs (w <= 4; two
-// single lookups for w >= 5), giving two fp16 codebook values.  Two pairs form
-// the 4-element B operand of a 4x4x4 (16-block) f16 MFMA whose A operand, the
-// query pre-multiplied by gains and sigma' and split into fp16 hi + lo parts,
-// is broadcast from one of 16 lane blocks (A-broadcast), so 64 tokens x 4
-// query-head parts are produced per instruction with no data exchange.
+// Keys (lane = token).  The K rows of a tile are staged in LDS word-major.  Every stored RoPE
+// block contributes a pair of fields of the same width w; a lane cuts two pairs out of a 32-bit
+// row window with one funnel shift and looks each up in an LDS table of fp16 pairs (w <= 4;
+// two single lookups for w >= 5).  Four pairs of a token form 8 fp16 values of the B operand
+// of a 16x16x32 f16 MFMA whose A operand is the query, pre-multiplied by gains and sigma' and
+// split into fp16 hi + lo parts (16 rows = 8 heads x 2 parts).
 //
-// Values (lane = dim, 8 tokens).  V tiles are stored in the order of the 16x16x32
-// f16 MFMA A operand: each lane loads B_V contiguous words per 16-dim slice and
-// cuts 8 codes of one dim at compile-time offsets (pairs through the same LDS
-// tables).  The B operand is the softmax weight p * s^V split into fp16 hi + lo,
-// written by the key lanes to LDS and read back 8 tokens at a time.
+// Values (lane = dim, 8 tokens).  V tiles are stored in the order of the 16x16x32 f16 MFMA A
+// operand and copied into LDS by global-to-LDS loads: each lane reads B_V words per 16-dim
+// slice and cuts 8 codes of one dim at compile-time offsets (pairs through the same tables).
+// The B operand is the softmax weight p * s^V split into fp16 hi + lo, written by the key
+// lanes to LDS and read back 8 tokens at a time.
 //
-// Cross-workgroup merging.  Split partials are written and read with agent-scope
-// (device-coherent) atomic stores and loads.  A workgroup waits for its stores to
-// complete (s_waitcnt) before it increments the merge counter, and the merger
-// reads the partials only after it has seen the counter reach the group size,
-// so no cache-wide write-back or invalidation is needed.
+// Cross-workgroup merging.  Split partials are written with agent-scope (device-coherent)
+// stores.  Once they have completed (s_waitcnt), the split stores its maxima together with a
+// per-call tag as 64-bit words; the merging workgroups poll those words, so no counter and no
+// cache-wide write-back or invalidation is needed.
 #pragma once
 
 #include <hip/hip_fp16.h>
