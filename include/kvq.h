@@ -122,7 +122,8 @@ void kvq_cache_destroy(kvq_cache* cache);
    page, abstract: each RoPE block gets an energy score computed from keys
    alone, then integer widths are handed out one step at a time to the block
    whose marginal gain is largest).
-   keys:   [n_tok][n_kv_heads][128] post-RoPE calibration keys (dtype), n_tok >= 1.
+   keys:   [n_tok][n_kv_heads][128] post-RoPE calibration keys (dtype), n_tok >= 1,
+           16-byte aligned.
            May be NULL for the UNIFORM and NF16 codecs, whose plans are fixed.
    block_weight: NULL, or a device fp64 array [n_kv_heads][64] of per-block
            weights multiplying the energy score before the greedy.
@@ -144,7 +145,8 @@ kvq_status kvq_get_plan(const kvq_cache* cache, int32_t layer, int8_t* bits, flo
 
 /* Quantize and append n_new tokens to every sequence of one layer
    (per-token scale, codebook lookup and bit-packing; append-only).
-   k, v:  [batch][n_new][n_kv_heads][128] post-RoPE keys and values (dtype).
+   k, v:  [batch][n_new][n_kv_heads][128] post-RoPE keys and values (dtype),
+          16-byte aligned.
    n_new = 0 is a no-op.  Row quantizer, in IEEE fp32/fp64 with no fused ops:
    y = x * ig_j; s = fp16(fp32(sqrt(sum y^2 / 128))); u = y * fp32(1/s);
    code = number of codebook boundaries below u.  NF16: s = fp16(absmax) per

@@ -4,14 +4,22 @@
 // frequency block of each (layer, KV head) gets an energy score computed from
 // keys alone; integer widths are then raised greedily by marginal gain.
 //
-// Kernel 1 (energy_chunks): one 64-lane wave per (256-token chunk, KV head);
-// lane j sums the block's squared norm over the chunk in token order (fp64;
-// each term x0*x0 + x1*x1 with exact squares and one rounding).
-// Kernel 2 (greedy_plan): one wave per KV head; lane j adds the chunk partials
-// in chunk order, divides by 2T, then runs the (k_bits - b_min) * 64 greedy
-// steps with a wave-wide argmax (ties to the lowest lane = smallest block),
-// derives gains sqrt(m_j / mean m) and writes the plan (field order: blocks by
-// width descending then index, coordinate p0 then p1).
+// Kernel 1 (energy_chunks): one workgroup per (256-token chunk, KV head).  The
+// chunk's keys of that head are first copied into LDS with coalesced loads (one
+// round of memory latency); lane j then sums block j's squared norm over the
+// chunk in token order (fp64; each term x0*x0 + x1*x1 with exact squares and one
+// rounding).
+// Kernel 2 (greedy_plan): one workgroup per KV head.  Lane j adds the chunk
+// partials in chunk order and divides by 2T.  The greedy raises, (k_bits - b_min)
+// * 64 times, the block with the largest s_j * delta(b_j) (ties to the smallest
+// block).  delta is strictly decreasing, so block j's candidate gains
+// s_j * delta(b), b = b_min .. b_max - 1, decrease in b and the greedy takes the
+// candidates of all blocks in the order (gain descending, block ascending, b
+// ascending): the width of block j is b_min plus the number of its candidates
+// among the first N of that order.  A bitonic sort of the 512 candidates in LDS
+// gives that order, hence the same widths as the sequential steps.
+// Gains sqrt(m_j / mean m) and the plan (field order: blocks by width
+// descending then index, coordinate p0 then p1) follow.
 #include <hip/hip_fp16.h>
 
 #include <cmath>
@@ -28,71 +36,114 @@ __device__ inline float load_f<__half>(const __half* p) { return __half2float(*p
 template <>
 __device__ inline float load_f<float>(const float* p) { return *p; }
 
+constexpr int kEnergyTok = 128;   // tokens staged in LDS at a time (a chunk is 1 or 2 stages)
+
 template <typename T>
-__global__ __launch_bounds__(64) void energy_chunks(const T* __restrict__ keys, int64_t n_tok,
-                                                    int n_kv, int pairing, double* __restrict__ scratch,
-                                                    int64_t n_chunks) {
-  const int j = threadIdx.x;
+__global__ __launch_bounds__(256) void energy_chunks(const T* __restrict__ keys, int64_t n_tok,
+                                                     int n_kv, int pairing, double* __restrict__ scratch,
+                                                     int64_t n_chunks) {
+  const int tid = threadIdx.x, j = tid;
   const int h = blockIdx.y;
   const int64_t c = blockIdx.x;
   const int p0 = pairing == KVQ_ROPE_HALF ? j : 2 * j;
   const int p1 = pairing == KVQ_ROPE_HALF ? j + kBlocks : 2 * j + 1;
-  const int64_t t0 = c * kEnergyChunk;
-  const int64_t t1 = t0 + kEnergyChunk < n_tok ? t0 + kEnergyChunk : n_tok;
+  __shared__ T x_s[kEnergyTok][kHeadDim + 16 / sizeof(T)];   // padded rows
+  constexpr int kVec = 16 / sizeof(T);                       // elements per 16-byte load
   double acc = 0.0;
-  for (int64_t t = t0; t < t1; ++t) {
-    const T* row = keys + (t * n_kv + h) * kHeadDim;
-    const double x0 = static_cast<double>(load_f(row + p0));
-    const double x1 = static_cast<double>(load_f(row + p1));
-    acc = __dadd_rn(acc, __dadd_rn(__dmul_rn(x0, x0), __dmul_rn(x1, x1)));
+  for (int64_t s0 = c * kEnergyChunk; s0 < (c + 1) * kEnergyChunk && s0 < n_tok; s0 += kEnergyTok) {
+    const int64_t ns = n_tok - s0 < kEnergyTok ? n_tok - s0 : kEnergyTok;
+    // stage: thread t copies 16-byte pieces t, t + 256, ... of the stage's rows
+    for (int k = tid; k < kEnergyTok * kHeadDim / kVec; k += 256) {
+      const int r = k / (kHeadDim / kVec), q = k % (kHeadDim / kVec);
+      if (r < ns) {
+        const uint4 v = *reinterpret_cast<const uint4*>(keys + ((s0 + r) * n_kv + h) * kHeadDim + q * kVec);
+        *reinterpret_cast<uint4*>(&x_s[r][q * kVec]) = v;
+      }
+    }
+    __syncthreads();
+    if (j < kBlocks) {
+      for (int r = 0; r < ns; ++r) {
+        const double x0 = static_cast<double>(load_f(&x_s[r][p0]));
+        const double x1 = static_cast<double>(load_f(&x_s[r][p1]));
+        acc = __dadd_rn(acc, __dadd_rn(__dmul_rn(x0, x0), __dmul_rn(x1, x1)));
+      }
+    }
+    __syncthreads();
   }
-  scratch[(static_cast<int64_t>(h) * n_chunks + c) * kBlocks + j] = acc;
+  if (j < kBlocks) scratch[(static_cast<int64_t>(h) * n_chunks + c) * kBlocks + j] = acc;
 }
 
-__global__ __launch_bounds__(64) void greedy_plan(const double* __restrict__ scratch, int64_t n_chunks,
-                                                  int64_t n_tok, const double* __restrict__ weight,
-                                                  int k_bits, int b_min, int b_max, int codec,
-                                                  int pairing, const Tables* __restrict__ tab,
-                                                  Plan* __restrict__ plans) {
-  const int j = threadIdx.x;
+__global__ __launch_bounds__(512) void greedy_plan(const double* __restrict__ scratch, int64_t n_chunks,
+                                                   int64_t n_tok, const double* __restrict__ weight,
+                                                   int k_bits, int b_min, int b_max, int codec,
+                                                   int pairing, const Tables* __restrict__ tab,
+                                                   Plan* __restrict__ plans) {
+  const int tid = threadIdx.x;
   const int h = blockIdx.x;
   __shared__ double m_s[kBlocks];
   __shared__ int w_s[kBlocks];
+  __shared__ double cand_s[kBlocks * kMaxBits];   // candidate gains, then sorted
+  __shared__ int cid_s[kBlocks * kMaxBits];       // candidate j * 8 + b, sorted alongside
+  __shared__ int cnt_s[kBlocks];
   __shared__ double mbar_s;
   __shared__ int nf_s;
 
   const bool bgtq = codec == KVQ_CODEC_BGTQ;
-  double m = 0.0;
-  if (bgtq) {
-    double S = 0.0;
-    for (int64_t c = 0; c < n_chunks; ++c)
-      S = __dadd_rn(S, scratch[(static_cast<int64_t>(h) * n_chunks + c) * kBlocks + j]);
-    m = __ddiv_rn(S, 2.0 * static_cast<double>(n_tok));
-  }
-  // equal scores make the greedy hand out a uniform width (UNIFORM and NF16 plans)
-  const double s = bgtq ? (weight ? __dmul_rn(m, weight[h * kBlocks + j]) : m) : 1.0;
-
-  int b = b_min;
-  const int steps = (k_bits - b_min) * kBlocks;
-  for (int it = 0; it < steps; ++it) {
-    double bv = b < b_max ? __dmul_rn(s, static_cast<double>(tab->delta[b])) : -INFINITY;
-    int bi = j;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const double ov = __shfl_xor(bv, off, 64);
-      const int oi = __shfl_xor(bi, off, 64);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
+  if (tid < kBlocks) {
+    const int j = tid;
+    double m = 0.0;
+    if (bgtq) {
+      double S = 0.0;
+      for (int64_t c = 0; c < n_chunks; ++c)
+        S = __dadd_rn(S, scratch[(static_cast<int64_t>(h) * n_chunks + c) * kBlocks + j]);
+      m = __ddiv_rn(S, 2.0 * static_cast<double>(n_tok));
     }
-    if (bi == j) ++b;
+    m_s[j] = m;
+    cnt_s[j] = 0;
   }
-
-  m_s[j] = m;
-  w_s[j] = b;
   __syncthreads();
-  if (j == 0) {
+  // candidate (j, b) for b in [b_min, b_max): gain s_j * delta(b); others are absent (-inf,
+  // sorted last)
+  {
+    const int j = tid >> 3, b = tid & 7;
+    const double m = m_s[j];
+    // equal scores make the greedy hand out a uniform width (UNIFORM and NF16 plans)
+    const double sj = bgtq ? (weight ? __dmul_rn(m, weight[h * kBlocks + j]) : m) : 1.0;
+    cand_s[tid] = (b >= b_min && b < b_max) ? __dmul_rn(sj, static_cast<double>(tab->delta[b])) : -INFINITY;
+    cid_s[tid] = tid;
+  }
+  __syncthreads();
+  // bitonic sort of the 512 candidates into the greedy's order: gain descending, then
+  // (block, step) ascending; "a before b" is a total order, so the sort is unique
+  for (int k = 2; k <= kBlocks * kMaxBits; k <<= 1) {
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      const int i = tid, pr = i ^ jj;
+      if (pr > i) {
+        const double va = cand_s[i], vb = cand_s[pr];
+        const int ia = cid_s[i], ib = cid_s[pr];
+        const bool a_first = va > vb || (va == vb && ia < ib);
+        const bool up = (i & k) == 0;   // this half of the bitonic block in "before" order
+        if (a_first != up) {
+          cand_s[i] = vb;
+          cand_s[pr] = va;
+          cid_s[i] = ib;
+          cid_s[pr] = ia;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // the greedy's (k_bits - b_min) * 64 steps take the first candidates of that order
+  if (tid < (k_bits - b_min) * kBlocks) atomicAdd(&cnt_s[cid_s[tid] >> 3], 1);
+  __syncthreads();
+  // threads 0..63 finish block j = tid; all threads keep meeting at the barriers
+  const bool act = tid < kBlocks;
+  const int j = act ? tid : 0;
+  const double m = m_s[j];
+  const int b = b_min + cnt_s[j];
+  if (act) w_s[j] = b;
+  __syncthreads();
+  if (tid == 0) {
     double t = 0.0;
     int nf = 0;
     for (int k = 0; k < kBlocks; ++k) {
@@ -128,11 +179,14 @@ __global__ __launch_bounds__(64) void greedy_plan(const double* __restrict__ scr
   const int p1 = pairing == KVQ_ROPE_HALF ? j + kBlocks : 2 * j + 1;
   Plan* P = plans + h;
   // fields past n_fields are zero: every lane first clears two slots, then writes its own
-  P->fdim[2 * j] = P->fdim[2 * j + 1] = 0;
-  P->fwidth[2 * j] = P->fwidth[2 * j + 1] = 0;
-  P->foff[2 * j] = P->foff[2 * j + 1] = 0;
-  P->pdesc[j] = 0u;
+  if (act) {
+    P->fdim[2 * j] = P->fdim[2 * j + 1] = 0;
+    P->fwidth[2 * j] = P->fwidth[2 * j + 1] = 0;
+    P->foff[2 * j] = P->foff[2 * j + 1] = 0;
+    P->pdesc[j] = 0u;
+  }
   __syncthreads();
+  if (!act) return;
   if (b > 0) {
     P->fdim[2 * rank] = static_cast<uint8_t>(p0);
     P->fdim[2 * rank + 1] = static_cast<uint8_t>(p1);
@@ -162,11 +216,11 @@ hipError_t launch_alloc(kvq_cache* c, int layer, const void* keys, int dtype, in
   if (bgtq) {
     dim3 grid(static_cast<unsigned>(n_chunks), static_cast<unsigned>(H));
     if (dtype == KVQ_F16)
-      hipLaunchKernelGGL(energy_chunks<__half>, grid, dim3(64), 0, stream,
+      hipLaunchKernelGGL(energy_chunks<__half>, grid, dim3(256), 0, stream,
                          static_cast<const __half*>(keys), n_tok, H, cfg.pairing, c->energy_scratch,
                          n_chunks);
     else
-      hipLaunchKernelGGL(energy_chunks<float>, grid, dim3(64), 0, stream,
+      hipLaunchKernelGGL(energy_chunks<float>, grid, dim3(256), 0, stream,
                          static_cast<const float*>(keys), n_tok, H, cfg.pairing, c->energy_scratch,
                          n_chunks);
     hipError_t e = hipGetLastError();
@@ -175,7 +229,7 @@ hipError_t launch_alloc(kvq_cache* c, int layer, const void* keys, int dtype, in
   const int k_bits = cfg.codec == KVQ_CODEC_NF16_B256 ? 4 : cfg.k_bits;
   const int b_min = bgtq ? cfg.b_min : 0;
   const int b_max = bgtq ? cfg.b_max : kMaxBits;
-  hipLaunchKernelGGL(greedy_plan, dim3(H), dim3(64), 0, stream, c->energy_scratch, n_chunks, n_tok,
+  hipLaunchKernelGGL(greedy_plan, dim3(H), dim3(kBlocks * kMaxBits), 0, stream, c->energy_scratch, n_chunks, n_tok,
                      block_weight, k_bits, b_min, b_max, cfg.codec, cfg.pairing, c->tables,
                      c->plans + static_cast<int64_t>(layer) * H);
   return hipGetLastError();

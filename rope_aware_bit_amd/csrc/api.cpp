@@ -200,6 +200,10 @@ kvq_status kvq_alloc_bits(kvq_cache* c, int32_t layer, const void* keys, int32_t
   if (dtype != KVQ_F16 && dtype != KVQ_F32) return KVQ_EINVAL;
   const bool bgtq = c->cfg.codec == KVQ_CODEC_BGTQ;
   if (bgtq && (!keys || n_tok < 1)) return KVQ_EINVAL;
+  if (bgtq && reinterpret_cast<uintptr_t>(keys) % 16) {
+    g_last_error = "alloc_bits: keys must be 16-byte aligned";
+    return KVQ_EINVAL;
+  }
   if (bgtq && n_tok > (int64_t(1) << 31)) return KVQ_EINVAL;
   if (c->len[layer] > 0) return KVQ_ESTATE;
   if (bgtq) {
@@ -255,6 +259,10 @@ kvq_status kvq_quantize_append(kvq_cache* c, int32_t layer, const void* k, const
   if (n_new < 0) return KVQ_EINVAL;
   if (n_new == 0) return KVQ_OK;
   if (!k || !v) return KVQ_EINVAL;
+  if (reinterpret_cast<uintptr_t>(k) % 16 || reinterpret_cast<uintptr_t>(v) % 16) {
+    g_last_error = "quantize_append: k and v must be 16-byte aligned";
+    return KVQ_EINVAL;
+  }
   if (!c->plan_ready[layer]) return KVQ_ESTATE;
   if (c->len[layer] + n_new > c->cfg.max_tokens) return KVQ_ECAPACITY;
   hipError_t e = kvq::launch_quantize(c, layer, k, v, dtype, n_new, static_cast<hipStream_t>(stream));

@@ -12,12 +12,17 @@
 // [n_kv * 128] vector is divided by its absolute maximum and mapped to the
 // 16-level Gaussian-quantile codebook.
 //
-// One workgroup of 128 lanes handles one 128-position V tile of one (sequence,
-// KV head); lane t owns token position tile*128 + t.  K rows are written row by
-// row (fields in plan order, LSB first).  V codes go through LDS so that lane i
-// can assemble dim i's 128-token stream; positions outside the appended range
-// keep the bits already stored (read-modify-write of partial words; a tile is
-// owned by exactly one workgroup of the launch).
+// One workgroup of 256 threads handles 8 consecutive positions of one (sequence, KV head):
+//   1. the group's K and V rows (for the 256-value codec both heads of the block) are copied
+//      into LDS with coalesced 16-byte loads;
+//   2. one lane per token computes the token's scales in the order above;
+//   3. every thread quantizes four K (token, field) and four V (token, dim) elements with
+//      branchless binary searches over the width's boundaries, all eight in lock step, and ORs
+//      each code into the LDS image of its K row word and V segment word;
+//   4. the group's K rows are stored as one contiguous run, and its V segment words are
+//      OR-ed into HBM with atomics: a 32-position V segment is shared by four workgroups,
+//      and positions at or past the sequence length are still zero (the cache is zero-filled
+//      at creation and only appended to), so the ORs compose.
 #include <hip/hip_fp16.h>
 
 #include "kvq_internal.h"
@@ -25,171 +30,188 @@
 namespace kvq {
 namespace {
 
-template <typename T>
-__device__ inline float load_f(const T* p);
-template <>
-__device__ inline float load_f<__half>(const __half* p) { return __half2float(*p); }
-template <>
-__device__ inline float load_f<float>(const float* p) { return *p; }
+constexpr int kGroupTok = 8;    // positions per workgroup
+constexpr int kThreads = 256;
 
-// number of entries of bd[0..n) strictly below u (bd ascending)
-__device__ inline int count_below(const float* bd, int n, float u) {
-  int lo = 0, hi = n;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (bd[mid] < u) lo = mid + 1; else hi = mid;
-  }
-  return lo;
-}
+template <typename T>
+__device__ inline float to_f(T v);
+template <>
+__device__ inline float to_f<__half>(__half v) { return __half2float(v); }
+template <>
+__device__ inline float to_f<float>(float v) { return v; }
 
 __device__ inline float inv_scale(__half s16) {
   const float s = __half2float(s16);
   return s == 0.0f ? 0.0f : __fdiv_rn(1.0f, s);
 }
 
-// RMS scale of a row after multiplying by the per-dim inverse gains
-template <typename T>
-__device__ inline __half row_rms(const T* x, const float* ig) {
-  double ss = 0.0;
-  for (int i = 0; i < kHeadDim; ++i) {
-    const double y = static_cast<double>(__fmul_rn(load_f(x + i), ig[i]));
-    ss = __dadd_rn(ss, __dmul_rn(y, y));
-  }
-  const float s32 = static_cast<float>(__dsqrt_rn(ss / static_cast<double>(kHeadDim)));
-  return __float2half_rn(s32);
-}
-
-// absolute maximum of 256 consecutive values
-template <typename T>
-__device__ inline __half block_absmax(const T* x) {
-  float a = 0.0f;
-  for (int i = 0; i < kNfBlock; ++i) a = fmaxf(a, fabsf(load_f(x + i)));
-  return __float2half_rn(a);
-}
-
 template <typename T, bool NF>
-__global__ __launch_bounds__(128) void quantize_append(
+__global__ __launch_bounds__(kThreads) void quantize_append(
     const T* __restrict__ kin, const T* __restrict__ vin, int64_t n_new, int64_t L0, int n_kv,
     int64_t cap, const Plan* __restrict__ plans, const Tables* __restrict__ tab,
     uint32_t* __restrict__ kc, uint32_t* __restrict__ vc, uint16_t* __restrict__ ks,
     uint16_t* __restrict__ vs, int k_words, int v_bits, int n_nf) {
-  const int t = threadIdx.x;
+  constexpr int kVec = 16 / sizeof(T);            // elements per 16-byte load
+  constexpr int kRowW = kHeadDim * static_cast<int>(sizeof(T)) / 4 + 1;   // odd: no bank conflicts
+  constexpr int kHeads = NF ? 2 : 1;              // heads staged per tensor
+  constexpr int kEl = kHeadDim * kGroupTok / kThreads;   // K (and V) elements per thread
+  const int tid = threadIdx.x;
   const int h = blockIdx.y;
   const int b = blockIdx.z;
-  const int64_t tile = L0 / kVTile + blockIdx.x;
-  const int64_t pos = tile * kVTile + t;
-  const bool live = pos >= L0 && pos < L0 + n_new;
+  const int64_t g0 = (L0 / kGroupTok + blockIdx.x) * kGroupTok;   // first position of the group
+  // appended positions of the group: [lo, hi) relative to g0
+  const int lo = static_cast<int>(L0 > g0 ? L0 - g0 : 0);
+  const int hi = static_cast<int>(L0 + n_new - g0 < kGroupTok ? L0 + n_new - g0 : kGroupTok);
+  const int vb = NF ? 4 : v_bits;
+  const int eb = static_cast<int>(g0 % 32);       // first position inside its V segment
+  const int vw0 = eb * vb / 32;                   // first segment word the group touches
+  const int nvw = ((eb + kGroupTok) * vb + 31) / 32 - vw0;   // segment words it touches (<= 3)
 
-  __shared__ float bd_s[kMaxBits + 1][256];
+  __shared__ uint32_t x_s[2][kHeads][kGroupTok][kRowW];   // [K, V][head][token] rows of T
+  auto xval = [&](int tsr, int hh, int r, int i) {
+    return to_f(reinterpret_cast<const T*>(&x_s[tsr][hh][r][0])[i]);
+  };
+  __shared__ float bd_s[(kMaxBits + 1) * 256];
   __shared__ float ig_s[kHeadDim];
-  __shared__ uint8_t fdim_s[kHeadDim];
-  __shared__ uint8_t fw_s[kHeadDim];
-  __shared__ uint8_t vcode_s[kHeadDim][kVTile + 4];
+  __shared__ uint8_t fdim_s[kHeadDim], fw_s[kHeadDim];
+  __shared__ uint16_t foff_s[kHeadDim];
+  __shared__ __attribute__((aligned(16))) uint32_t krow_s[kGroupTok * 4 * kMaxBits];
+  __shared__ uint32_t vw_s[kHeadDim][4];           // the group's V segment words, per dim
+  __shared__ float isk_s[kGroupTok], isv_s[kGroupTok];
   __shared__ int nf_s;
 
-  const Plan* P = plans + h;
-  for (int k = t; k < (kMaxBits + 1) * 256; k += blockDim.x) {
-    const int bb = k >> 8, e = k & 255;
-    bd_s[bb][e] = NF ? (bb == 4 && e < 16 ? tab->nf_bd[e] : INFINITY) : tab->bd[bb][e];
+  // ---- 1. stage rows, tables and plan; clear the word images ----
+  const int h0 = NF ? (h & ~1) : h;   // first head of the staged block
+  for (int k = tid; k < 2 * kHeads * kGroupTok * (kHeadDim / kVec); k += kThreads) {
+    const int q = k % (kHeadDim / kVec);
+    const int r = (k / (kHeadDim / kVec)) % kGroupTok;
+    const int hh = (k / (kHeadDim / kVec * kGroupTok)) % kHeads;
+    const int tsr = k / (kHeadDim / kVec * kGroupTok * kHeads);   // 0: K, 1: V
+    if (r >= lo && r < hi) {
+      const int64_t src = ((static_cast<int64_t>(b) * n_new + (g0 + r - L0)) * n_kv + h0 + hh) * kHeadDim + q * kVec;
+      const T* in = tsr ? vin : kin;
+      const uint4 v4 = *reinterpret_cast<const uint4*>(in + src);
+      uint32_t* d = &x_s[tsr][hh][r][q * 4];
+      d[0] = v4.x;
+      d[1] = v4.y;
+      d[2] = v4.z;
+      d[3] = v4.w;
+    }
   }
-  ig_s[t] = P->ig[t];
-  fdim_s[t] = P->fdim[t];
-  fw_s[t] = P->fwidth[t];
-  if (t == 0) nf_s = P->n_fields;
+  const Plan* P = plans + h;
+  for (int k = tid; k < (kMaxBits + 1) * 256; k += kThreads) {
+    const int bb = k >> 8, e = k & 255;
+    bd_s[k] = NF ? (bb == 4 && e < 16 ? tab->nf_bd[e] : INFINITY) : tab->bd[bb][e];
+  }
+  if (tid < kHeadDim) {
+    ig_s[tid] = P->ig[tid];
+    fdim_s[tid] = P->fdim[tid];
+    fw_s[tid] = P->fwidth[tid];
+    foff_s[tid] = P->foff[tid];
+    vw_s[tid][0] = vw_s[tid][1] = vw_s[tid][2] = vw_s[tid][3] = 0u;
+  }
+  for (int k = tid; k < kGroupTok * k_words; k += kThreads) krow_s[k] = 0u;
+  if (tid == 0) nf_s = P->n_fields;
   __syncthreads();
 
-  if (live) {
-    const int64_t src_row = (static_cast<int64_t>(b) * n_new + (pos - L0)) * n_kv + h;
-    // ---- K ----
-    const T* x = kin + src_row * kHeadDim;
-    __half s16;
+  // ---- 2. scales: lanes 0..7 K, 8..15 V (one token each, in the quantizer's order) ----
+  const int hsel = h - h0;   // this head's staged rows
+  if (tid < 2 * kGroupTok) {
+    const int tsr = tid / kGroupTok, r = tid % kGroupTok;
+    __half s16 = __float2half_rn(0.0f);
     if (NF) {
-      const T* blk = kin + ((static_cast<int64_t>(b) * n_new + (pos - L0)) * n_kv) * kHeadDim +
-                     static_cast<int64_t>(h / 2) * kNfBlock;
-      s16 = block_absmax(blk);
-    } else {
-      s16 = row_rms(x, ig_s);
-    }
-    const float is = inv_scale(s16);
-    uint32_t* row = kc + ((static_cast<int64_t>(b) * n_kv + h) * cap + pos) * k_words;
-    uint64_t acc = 0;
-    int nbits = 0, wo = 0;
-    for (int f = 0; f < nf_s; ++f) {
-      const int i = fdim_s[f], w = fw_s[f];
-      const float y = NF ? load_f(x + i) : __fmul_rn(load_f(x + i), ig_s[i]);
-      const float u = __fmul_rn(y, is);
-      const uint32_t code = static_cast<uint32_t>(count_below(bd_s[w], (1 << w) - 1, u));
-      acc |= static_cast<uint64_t>(code) << nbits;
-      nbits += w;
-      if (nbits >= 32) {
-        row[wo++] = static_cast<uint32_t>(acc);
-        acc >>= 32;
-        nbits -= 32;
-      }
-    }
-    const uint16_t sbits = __half_as_ushort(s16);
-    if (NF) {
-      if ((h & 1) == 0) ks[(static_cast<int64_t>(b) * cap + pos) * n_nf + h / 2] = sbits;
-    } else {
-      ks[(static_cast<int64_t>(b) * n_kv + h) * cap + pos] = sbits;
-    }
-    // ---- V ----
-    const T* xv = vin + src_row * kHeadDim;
-    __half sv;
-    if (NF) {
-      const T* blk = vin + ((static_cast<int64_t>(b) * n_new + (pos - L0)) * n_kv) * kHeadDim +
-                     static_cast<int64_t>(h / 2) * kNfBlock;
-      sv = block_absmax(blk);
+      float a = 0.0f;
+      for (int hh = 0; hh < kHeads; ++hh)
+        for (int i = 0; i < kHeadDim; ++i) a = fmaxf(a, fabsf(xval(tsr, hh, r, i)));
+      s16 = __float2half_rn(a);
     } else {
       double ss = 0.0;
       for (int i = 0; i < kHeadDim; ++i) {
-        const double y = static_cast<double>(load_f(xv + i));
+        const float x = xval(tsr, hsel, r, i);
+        const double y = static_cast<double>(tsr == 0 ? __fmul_rn(x, ig_s[i]) : x);
         ss = __dadd_rn(ss, __dmul_rn(y, y));
       }
-      sv = __float2half_rn(static_cast<float>(__dsqrt_rn(ss / static_cast<double>(kHeadDim))));
+      s16 = __float2half_rn(static_cast<float>(__dsqrt_rn(ss / static_cast<double>(kHeadDim))));
     }
-    const float isv = inv_scale(sv);
-    const int vb = NF ? 4 : v_bits;
-    for (int i = 0; i < kHeadDim; ++i)
-      vcode_s[i][t] = static_cast<uint8_t>(
-          count_below(bd_s[vb], (1 << vb) - 1, __fmul_rn(load_f(xv + i), isv)));
-    const uint16_t vbits16 = __half_as_ushort(sv);
-    if (NF) {
-      if ((h & 1) == 0) vs[(static_cast<int64_t>(b) * cap + pos) * n_nf + h / 2] = vbits16;
-    } else {
-      vs[(static_cast<int64_t>(b) * n_kv + h) * cap + pos] = vbits16;
+    (tsr == 0 ? isk_s : isv_s)[r] = inv_scale(s16);
+    if (r >= lo && r < hi) {
+      const int64_t pos = g0 + r;
+      const uint16_t bits = __half_as_ushort(s16);
+      uint16_t* sc = tsr == 0 ? ks : vs;
+      if (NF) {
+        if ((h & 1) == 0) sc[(static_cast<int64_t>(b) * cap + pos) * n_nf + h / 2] = bits;
+      } else {
+        sc[(static_cast<int64_t>(b) * n_kv + h) * cap + pos] = bits;
+      }
     }
   }
   __syncthreads();
 
-  // lane i assembles dim i's four 32-token segments of this tile; segment (dim, g) is stored
-  // at index ((dim / 16) * 4 + g) * 16 + dim % 16 (see the V tile layout in kvq.h)
-  const int i = t;
-  const int vb = NF ? 4 : v_bits;
-  const int64_t lo_pos = L0 > tile * kVTile ? L0 - tile * kVTile : 0;
-  const int64_t hi_pos = L0 + n_new - tile * kVTile < kVTile ? L0 + n_new - tile * kVTile : kVTile;
-  uint32_t* tile_dst = vc + ((static_cast<int64_t>(b) * n_kv + h) * (cap / kVTile) + tile) * kVTile * 4 * vb;
-  for (int g = 0; g < 4; ++g) {
-    uint32_t* dst = tile_dst + static_cast<int64_t>(((i / 16) * 4 + g) * 16 + i % 16) * vb;
-    uint64_t acc = 0, msk = 0;
-    int nbits = 0, wo = 0;
-    for (int e = 0; e < 32; ++e) {
-      const int tau = 32 * g + e;
-      const bool in = tau >= lo_pos && tau < hi_pos;
-      const uint64_t code = in ? vcode_s[i][tau] : 0;
-      const uint64_t m = in ? ((1ull << vb) - 1) : 0;
-      acc |= code << nbits;
-      msk |= m << nbits;
-      nbits += vb;
-      if (nbits >= 32) {
-        const uint32_t nw = static_cast<uint32_t>(acc), mw = static_cast<uint32_t>(msk);
-        if (mw == 0xFFFFFFFFu) dst[wo] = nw;
-        else if (mw != 0u) dst[wo] = (dst[wo] & ~mw) | (nw & mw);
-        ++wo;
-        acc >>= 32;
-        msk >>= 32;
-        nbits -= 32;
-      }
+  // ---- 3. codes: element e = tid + 256 m is K (field e / 8, token e % 8) and V (dim e / 8,
+  //      token e % 8); the eight searches of a thread advance in lock step ----
+  const int nfld = nf_s;
+  uint32_t pos[2 * kEl], tb[2 * kEl];
+  int wd[2 * kEl];
+  float u[2 * kEl];
+#pragma unroll
+  for (int m = 0; m < kEl; ++m) {
+    const int e = tid + kThreads * m, f = e / kGroupTok, r = e % kGroupTok;
+    const bool live = r >= lo && r < hi;
+    const bool kl = live && f < nfld;
+    const int i = kl ? fdim_s[f] : 0;
+    const int w = kl ? fw_s[f] : 0;
+    const float x = xval(0, hsel, r, i);
+    const float y = NF ? x : __fmul_rn(x, ig_s[i]);
+    u[m] = __fmul_rn(y, isk_s[r]);
+    wd[m] = w;
+    tb[m] = static_cast<uint32_t>(w) * 256u;
+    pos[m] = 0u;
+    u[kEl + m] = __fmul_rn(xval(1, hsel, r, f), isv_s[r]);   // V: dim f
+    wd[kEl + m] = live ? vb : 0;
+    tb[kEl + m] = static_cast<uint32_t>(vb) * 256u;
+    pos[kEl + m] = 0u;
+  }
+  const int steps = nfld > 0 && fw_s[0] > vb ? fw_s[0] : vb;   // plan order: widest field first
+  for (int st = 0; st < steps; ++st) {
+#pragma unroll
+    for (int m = 0; m < 2 * kEl; ++m) {
+      const int sh = wd[m] - 1 - st;
+      const uint32_t step = sh >= 0 ? 1u << sh : 0u;
+      const float bdv = bd_s[tb[m] + pos[m] + (step ? step : 1u) - 1u];
+      pos[m] += (step != 0u && bdv < u[m]) ? step : 0u;
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < kEl; ++m) {
+    const int e = tid + kThreads * m, f = e / kGroupTok, r = e % kGroupTok;
+    if (wd[m] > 0) {   // K code into its row word(s)
+      const int off = foff_s[f], w = wd[m];
+      const int word = off >> 5, sh = off & 31;
+      atomicOr(&krow_s[r * k_words + word], pos[m] << sh);
+      if (sh + w > 32) atomicOr(&krow_s[r * k_words + word + 1], pos[m] >> (32 - sh));
+    }
+    if (wd[kEl + m] > 0) {   // V code into its segment word(s)
+      const int bit = (eb + r) * vb - 32 * vw0, word = bit >> 5, sh = bit & 31;
+      const uint32_t code = pos[kEl + m];
+      atomicOr(&vw_s[f][word], code << sh);
+      if (sh + vb > 32) atomicOr(&vw_s[f][word + 1], code >> (32 - sh));
+    }
+  }
+  __syncthreads();
+
+  // ---- 4. stores ----
+  {
+    uint32_t* dst = kc + ((static_cast<int64_t>(b) * n_kv + h) * cap + g0) * k_words;
+    for (int k = tid + lo * k_words; k < hi * k_words; k += kThreads) dst[k] = krow_s[k];
+  }
+  {
+    const int64_t tile = g0 / kVTile;
+    const int gq = static_cast<int>((g0 % kVTile) / 32);   // segment group in the tile
+    uint32_t* tile_dst = vc + ((static_cast<int64_t>(b) * n_kv + h) * (cap / kVTile) + tile) * kVTile * 4 * vb;
+    for (int k = tid; k < kHeadDim * nvw; k += kThreads) {
+      const int i = k / nvw, w = k % nvw;
+      const uint32_t bits = vw_s[i][w];
+      if (bits) atomicOr(tile_dst + static_cast<int64_t>(((i / 16) * 4 + gq) * 16 + i % 16) * vb + vw0 + w, bits);
     }
   }
 }
@@ -200,13 +222,13 @@ hipError_t launch_quantize(kvq_cache* c, int layer, const void* k, const void* v
                            int64_t n_new, hipStream_t stream) {
   const kvq_config& cfg = c->cfg;
   const int64_t L0 = c->len[layer];
-  const int64_t first = L0 / kVTile, last = (L0 + n_new - 1) / kVTile;
+  const int64_t first = L0 / kGroupTok, last = (L0 + n_new - 1) / kGroupTok;
   dim3 grid(static_cast<unsigned>(last - first + 1), static_cast<unsigned>(cfg.n_kv_heads),
             static_cast<unsigned>(cfg.batch));
   const bool nf = cfg.codec == KVQ_CODEC_NF16_B256;
   const Plan* plans = c->plans + static_cast<int64_t>(layer) * cfg.n_kv_heads;
 #define KVQ_LAUNCH_Q(T, NF)                                                                      \
-  hipLaunchKernelGGL((quantize_append<T, NF>), grid, dim3(128), 0, stream,                      \
+  hipLaunchKernelGGL((quantize_append<T, NF>), grid, dim3(kThreads), 0, stream,                 \
                      static_cast<const T*>(k), static_cast<const T*>(v), n_new, L0,              \
                      cfg.n_kv_heads, c->cap, plans, c->tables, layer_k_codes(c, layer),          \
                      layer_v_codes(c, layer), layer_k_scales(c, layer), layer_v_scales(c, layer), \
