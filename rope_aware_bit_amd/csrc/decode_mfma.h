@@ -53,17 +53,21 @@ constexpr int kAS = 40;           // LDS row stride (halves) of the query operan
 // Random lookups into the larger tables would collide in LDS banks, so they are replicated:
 // the width-4 pair table 16 times (entry p of copy k at (p << 6) + 4 k, lane l reads copy
 // l % 16) and the width-3 pair table 32 times (entry p of copy k at (p << 7) + 4 k, lane l
-// reads copy l % 32).  Widths 5 and 6 use single tables (one fp16 in the low half of a 32-bit
-// slot) replicated 32 times the same way, built per workgroup when the plan uses them; a pair
-// costs two lookups.  The prebuilt image holds the pair tables of widths 1..4 and the single
-// tables of widths 1..8 (widths 7 and 8 use two single lookups there).  Every base is a
-// multiple of its table's extent, so an entry address is "(p << shift) | copy offset | base".
+// reads copy l % 32).  Widths 5..8 use single tables (one fp16 in the low half of a 32-bit
+// slot, the high half zero), built per workgroup when the plan uses them: widths 5 and 6
+// replicated 32 times the same way, widths 7 and 8 once (few blocks are that wide); a pair
+// costs two lookups in the same table.  The prebuilt image holds the pair tables of widths 1..4
+// and the fp16 single tables of widths 1..8.  Every base is a multiple of its table's extent,
+// so an entry address is "(p << shift) | copy offset | base".
 constexpr int kRep4Base = 0;           // 16 KB
 constexpr int kRep3Base = 16384;       // 8 KB
 constexpr int kSing6Base = 24576;      // 8 KB
 constexpr int kSing5Base = 32768;      // 4 KB
 constexpr int kImageBase = 36864;      // 2.5 KB
-constexpr int kTableRegion = kImageBase + kLdsTableBytes;
+constexpr int kSing7Base = 39424;      // 512 B
+constexpr int kSing8Base = 39936;      // 1 KB
+constexpr int kTableRegion = 40960;
+static_assert(kImageBase + kLdsTableBytes <= kSing7Base, "table region overlap");
 
 // Pairs of plan ranks go to the product slots in pairs of pairs: in chunk c, lane group g
 // handles ranks 16 c + 2 g, + 1 (positions 0, 1: one row window) and 16 c + 8 + 2 g, + 1
@@ -76,8 +80,8 @@ __host__ __device__ constexpr int slot_field(int c, int k) {
 // Key-product parameters of one (chunk c, lane group g): its four pairs, held in LDS as 24 words
 //   [0..3]  table base of pair p (with the part of the lane's replica offset fixed by g)
 //   [4..7]  mask applied to 4 n (the rest of the replica offset; 0 for single tables)
-//   [8..11] extract width (2 w for pair tables; w for widths 5, 6, whose first field is
-//           looked up here; 0 for widths 7, 8, whose lookups are replaced)
+//   [8..11] extract width (2 w for pair tables; w for widths 5..8, whose first field is
+//           looked up here)
 //   [12..15] left shift of the extracted code (2 single copy, 6 sixteen copies, 32: 7)
 //   [16..19] bit shift of window A (pairs 0, 1) and B (pairs 2, 3); bit offset of pairs 1, 3
 //   [20..21] byte offset of the first word of windows A and B in a staged K tile
@@ -100,14 +104,14 @@ __device__ inline void write_pair_params(uint32_t* kp, int r, uint32_t desc) {
     mask = 0x3Cu;
     shift = 7u;
   } else if (w >= 7u) {
-    base = kImageBase;   // placeholder read, replaced
+    base = w == 7u ? kSing7Base : kSing8Base;
   } else {
     base = kImageBase + static_cast<uint32_t>(pair_table_base(static_cast<int>(w)));
   }
   uint32_t* blk = kp + (4 * c + g) * kParamWords;
   blk[p] = base;
   blk[4 + p] = mask;
-  blk[8 + p] = w <= 4u ? 2u * w : w <= 6u ? w : 0u;
+  blk[8 + p] = w <= 4u ? 2u * w : w;
   blk[12 + p] = shift;
   reinterpret_cast<uint8_t*>(blk + 22)[p] = static_cast<uint8_t>(w);
   if ((p & 1) == 0) {
@@ -437,7 +441,7 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   __shared__ __attribute__((aligned(16))) float comb_l[G][W];
   __shared__ float alpha_s[W][G];
   __shared__ float ms_s[G];
-  __shared__ uint64_t wide_s, w56_s, w78_s;
+  __shared__ uint64_t wide_s;
   extern __shared__ __attribute__((aligned(16))) uint32_t dyn_s[];   // [W][region_words]
   uint32_t* kr = dyn_s + wave * region_words;                         // [k_words + 1][kKS]
   _Float16* pw = reinterpret_cast<_Float16*>(kr);                     // [PCOLS][kPS], after keys
@@ -484,6 +488,9 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   const uint32_t rep3v = reinterpret_cast<const uint32_t*>(gimg + pair_table_base(3))[st & 63];
   // rows 0..31: CB_5[st]; rows 32..95: CB_6[st - 32] (higher threads read a valid entry, unused)
   const uint32_t cb56 = reinterpret_cast<const uint16_t*>(gimg + single_table_base(st < 32 ? 5 : 6))[st < 32 ? st : (st - 32) & 63];
+  // CB_8[st] and CB_7[st % 128]
+  const uint32_t cb8 = reinterpret_cast<const uint16_t*>(gimg + single_table_base(8))[st];
+  const uint32_t cb7 = reinterpret_cast<const uint16_t*>(gimg + single_table_base(7))[st & 127];
 
   // K rows of tokens lane and lane + 64 (first 16 words), scales of tokens 16 tg + n, V segments
   uint4 ka[4], kb2[4];
@@ -579,22 +586,23 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
         }
       }
     }
-    // single tables of widths 5 and 6 when the plan stores such blocks: thread t < 96 writes
-    // the 32 copies of one entry
+    // single tables of widths 5..8 when the plan stores such blocks: for widths 5 and 6,
+    // thread t < 96 writes the 32 copies of one entry; for widths 7 and 8, thread t writes
+    // CB_8[t] and (t < 128) CB_7[t]
     const uint32_t pw = pd_r >> 16;
     const uint64_t wide = __ballot(pw >= 5u);
     const uint64_t w56 = __ballot(pw == 5u || pw == 6u);
     const uint64_t w78 = __ballot(pw >= 7u);
-    if (tid == 0) {
-      wide_s = wide;
-      w56_s = w56;
-      w78_s = w78;
-    }
+    if (tid == 0) wide_s = wide;
     if (w56 && tid < 96) {
       const uint4 v = make_uint4(cb56, cb56, cb56, cb56);
       char* row = tab_s + (tid < 32 ? kSing5Base + (tid << 7) : kSing6Base + ((tid - 32) << 7));
 #pragma unroll
       for (int j = 0; j < 8; ++j) *reinterpret_cast<uint4*>(row + 16 * ((j + tid) & 7)) = v;
+    }
+    if (w78) {
+      *reinterpret_cast<uint32_t*>(tab_s + kSing8Base + 4 * tid) = cb8;
+      if (tid < 128) *reinterpret_cast<uint32_t*>(tab_s + kSing7Base + 4 * tid) = cb7;
     }
   }
   lds_barrier();
@@ -618,8 +626,6 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   const uint32_t lb = (lane & 31u) << 2;   // this lane's replica offset
   lds_barrier();
   const uint64_t uses_wide = wide_s;       // pairs (plan ranks) with blocks of 5..8 bits
-  const uint64_t uses_w56 = w56_s;         // pairs with blocks of 5 or 6 bits
-  const uint64_t uses_w78 = w78_s;         // pairs with blocks of 7 or 8 bits
 
   // ---- per-wave state: lane (n, g) keeps heads 2g, 2g + 1 ----
   const int h0 = 2 * g, h1 = 2 * g + 1;
@@ -689,56 +695,22 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
         u[t][3] = lds_u32(tab_s, (__builtin_amdgcn_ubfe(xb[t], P.rel3, P.bw[3]) << P.ps[3]) | P.pb[3]);
       }
       if ((uses_wide >> (16 * c)) & 0xFFFFull) {
-        // blocks of 5..8 bits, without branches per pair (lanes whose pair is narrower read a
-        // placeholder and keep their value): widths 5, 6 add the second field from their
-        // replicated single table; widths 7, 8 take both fields from the image's single tables
-        // widths 7, 8 have the lowest ranks, so in practice only positions 0, 1 hold them (the
-        // ranks of positions 2, 3 are bits 8..15 of the chunk's mask)
-        const uint32_t m78 = static_cast<uint32_t>(uses_w78 >> (16 * c));
-        uint32_t v[4][4];
+        // blocks of 5..8 bits, without branches per pair: the first field was looked up above;
+        // the second comes from the same single table (same shift and base) into the high
+        // half.  Lanes whose pair is narrower read a placeholder and keep their value.
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           const uint32_t w = (P.wid >> (8 * p)) & 0xFFu;
           const uint32_t rel = (p & 1) ? (p == 1 ? P.rel1 : P.rel3) : 0u;
-          const bool is56 = w - 5u <= 1u;
+          const bool wide = w >= 5u;
+          uint32_t v[4];
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             const uint32_t f1 = __builtin_amdgcn_ubfe(p < 2 ? xa[t] : xb[t], rel + w, w);
-            v[t][p] = lds_u32(tab_s, is56 ? (f1 << 7) | P.pb[p] : static_cast<uint32_t>(kImageBase));
+            v[t] = lds_u32(tab_s, wide ? (f1 << P.ps[p]) | P.pb[p] : static_cast<uint32_t>(kImageBase));
           }
-        }
-        auto singles78 = [&](int p, uint32_t (&lo)[4], uint32_t (&hi)[4]) {
-          const uint32_t w = (P.wid >> (8 * p)) & 0xFFu;
-          const uint32_t rel = (p & 1) ? (p == 1 ? P.rel1 : P.rel3) : 0u;
-          const bool is78 = w >= 7u;
-          const uint32_t sb = kImageBase + static_cast<uint32_t>(kLdsTableBytes) - (4u << (is78 ? w : 7u));
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const uint32_t x = p < 2 ? xa[t] : xb[t];
-            const uint32_t f0 = __builtin_amdgcn_ubfe(x, rel, w), f1 = __builtin_amdgcn_ubfe(x, rel + w, w);
-            lo[t] = lds_u16(tab_s, is78 ? (f0 << 1) + sb : static_cast<uint32_t>(kImageBase));
-            hi[t] = lds_u16(tab_s, is78 ? (f1 << 1) + sb : static_cast<uint32_t>(kImageBase));
-          }
-        };
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const uint32_t w = (P.wid >> (8 * p)) & 0xFFu;
-#pragma unroll
-          for (int t = 0; t < 4; ++t) u[t][p] = w - 5u <= 1u ? u[t][p] | (v[t][p] << 16) : u[t][p];
-        }
-#pragma unroll
-        for (int pp = 0; pp < 4; pp += 2) {
-          if (m78 & (pp == 0 ? 0xFFu : 0xFF00u)) {
-            uint32_t lo[2][4], hi[2][4];
-            singles78(pp, lo[0], hi[0]);
-            singles78(pp + 1, lo[1], hi[1]);
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-              const uint32_t w = (P.wid >> (8 * (pp + q))) & 0xFFu;
-#pragma unroll
-              for (int t = 0; t < 4; ++t) u[t][pp + q] = w >= 7u ? lo[q][t] | (hi[q][t] << 16) : u[t][pp + q];
-            }
-          }
+          for (int t = 0; t < 4; ++t) u[t][p] = wide ? u[t][p] | (v[t] << 16) : u[t][p];
         }
       }
     };

@@ -109,7 +109,7 @@ struct DecodeShape {
 };
 inline DecodeShape decode_shape(const kvq_cache* c) {
   constexpr int kKS = 144, kPS = 136, kOS = 10, kLds = 163840;
-  constexpr int kStaticBase = 36864 + 2560 + 4 * 16 * 40 * 2 + 128 + 64 * 4 + 16 * 24 * 4 + 64;
+  constexpr int kStaticBase = 40960 + 4 * 16 * 40 * 2 + 128 + 64 * 4 + 16 * 24 * 4 + 64;
   const int G = c->group;
   const int vb = c->cfg.codec == KVQ_CODEC_NF16_B256 ? 4 : c->cfg.v_bits;
   int kpart = (c->k_words + 1) * kKS;
