@@ -45,6 +45,8 @@ typedef __attribute__((address_space(1))) void* glb_ptr;
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxPolls = 1 << 22;  // bound on a merger's wait for the other splits
+constexpr int kCohAux = 16;         // buffer-load cache policy sc1: coherent at device scope
+constexpr int kRawBuffer = 0x00020000;   // buffer descriptor word 3: raw 32-bit data
 constexpr int kKS = 144;          // LDS row stride (words) of a staged K tile: 128 tokens + 16
 constexpr int kPS = 136;          // LDS row stride (halves) of the softmax weights: 128 + 8
 constexpr int kOS = 10;           // LDS stride (floats) per dim of a wave's merge share: G <= 8, + 2
@@ -213,13 +215,12 @@ __device__ inline void st_coh(float* p, float v) {
 __device__ inline float ld_coh(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// Four consecutive floats (8-byte aligned) read at device scope, two per 64-bit load.
-__device__ inline float4 ld_coh4(const float* p) {
-  const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
-  const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return make_float4(__uint_as_float(static_cast<uint32_t>(a)), __uint_as_float(static_cast<uint32_t>(a >> 32)),
-                     __uint_as_float(static_cast<uint32_t>(b)), __uint_as_float(static_cast<uint32_t>(b >> 32)));
+// Four consecutive floats (16-byte aligned) at byte offset `off` of the buffer `r`, read at
+// device scope (sc1) with one 16-byte buffer load.
+__device__ inline float4 ld_coh4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef unsigned u4 __attribute__((ext_vector_type(4)));
+  const u4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCohAux);
+  return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
 }
 
 // fp16 pair of V codes e, e+1 (e even) of a 32-code segment held in S[0..VB) (S[VB] is a
@@ -305,6 +306,8 @@ __device__ __attribute__((always_inline)) inline void merge_slice(
   __syncthreads();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   // outputs in groups of four (one 16-byte load per split and group)
+  const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(src_o), 0, S * G * kHeadDim * 4, kRawBuffer);
   const int P4 = count / 4 < NT ? count / 4 : NT;   // groups per pass
   const int R = NT / P4;                              // threads per group
   const int j4 = tid % P4, e0 = tid / P4;
@@ -323,7 +326,7 @@ __device__ __attribute__((always_inline)) inline void merge_slice(
 #pragma unroll
       for (int k = 0; k < kPre; ++k) {
         const int ek = e0 + R * k;
-        ov[k] = ek < S ? ld_coh4(src_o + static_cast<int64_t>(ek) * G * kHeadDim + oi) : make_float4(0.f, 0.f, 0.f, 0.f);
+        ov[k] = ek < S ? ld_coh4(ro, 4u * static_cast<uint32_t>(ek * G * kHeadDim + oi)) : make_float4(0.f, 0.f, 0.f, 0.f);
       }
       if (wave < nh) {   // merged sum of head hd0 + wave
         float l = 0.0f;
@@ -339,7 +342,7 @@ __device__ __attribute__((always_inline)) inline void merge_slice(
       for (int k = 0; k < kPre; ++k, e += R)
         if (e < S) add(wv[hh * S + e], ov[k]);
     }
-    for (; e < S; e += R) add(wv[hh * S + e], ld_coh4(src_o + static_cast<int64_t>(e) * G * kHeadDim + oi));
+    for (; e < S; e += R) add(wv[hh * S + e], ld_coh4(ro, 4u * static_cast<uint32_t>(e * G * kHeadDim + oi)));
     red[tid] = acc;
     __syncthreads();
     if (tid < P4) {
