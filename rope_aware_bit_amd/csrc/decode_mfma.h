@@ -216,7 +216,8 @@ __device__ inline float ld_coh(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // Four consecutive floats (16-byte aligned) at byte offset `off` of the buffer `r`, read at
-// device scope (sc1) with one 16-byte buffer load.
+// device scope (sc1) with one 16-byte buffer load (buffer stores with the same policy write
+// them coherently).
 __device__ inline float4 ld_coh4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   typedef unsigned u4 __attribute__((ext_vector_type(4)));
   const u4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCohAux);
@@ -867,9 +868,13 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   }
   lds_barrier();
   const int64_t out_base = (static_cast<int64_t>(b) * n_q + h * G) * kHeadDim;
-  for (int idx = tid; idx < G * kHeadDim; idx += NT) {
-    const int hd = idx / kHeadDim, i = idx % kHeadDim;
-    float mw[W], lw[W], ov[W];
+  // thread q combines outputs 4 i .. 4 i + 3 of head hd = q % G (i = q / G: the lanes of a
+  // wave read distinct LDS banks) and stores them as one 16-byte word
+  const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+      part_o + (bh * n_splits + s) * G * kHeadDim, 0, G * kHeadDim * 4, kRawBuffer);
+  for (int q = tid; q < G * kHeadDim / 4; q += NT) {
+    const int hd = q % G, i0 = 4 * (q / G);
+    float mw[W], lw[W], sc[W];
 #pragma unroll
     for (int w = 0; w < W; w += 4) {
       const float4 m4 = *reinterpret_cast<const float4*>(&comb_m[hd][w]);
@@ -877,26 +882,29 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
       mw[w] = m4.x; mw[w + 1] = m4.y; mw[w + 2] = m4.z; mw[w + 3] = m4.w;
       lw[w] = l4.x; lw[w + 1] = l4.y; lw[w + 2] = l4.z; lw[w + 3] = l4.w;
     }
-#pragma unroll
-    for (int w = 0; w < W; ++w) ov[w] = reinterpret_cast<const float*>(dyn_s + w * region_words)[i * kOS + hd];
     float ms = -INFINITY;
 #pragma unroll
     for (int w = 0; w < W; ++w) ms = fmaxf(ms, mw[w]);
-    float o = 0.0f, l = 0.0f;
+    float o[4] = {0.0f, 0.0f, 0.0f, 0.0f}, l = 0.0f;
 #pragma unroll
     for (int w = 0; w < W; ++w) {
       // 0 for waves without tokens; hardware 2^x (weights far below 1 only meet sums >= 1)
-      const float sc = mw[w] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw[w] - ms);
-      o += sc * ov[w];
-      l += sc * lw[w];
+      sc[w] = mw[w] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw[w] - ms);
+      l += sc[w] * lw[w];
+      const float* ow_w = reinterpret_cast<const float*>(dyn_s + w * region_words);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] += sc[w] * ow_w[(i0 + j) * kOS + hd];
     }
     if (n_splits == 1) {
-      out[out_base + idx] = o / l;
+      const float inv = 1.0f / l;
+      *reinterpret_cast<float4*>(out + out_base + hd * kHeadDim + i0) =
+          make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
     } else {
-      const int64_t p = (bh * n_splits + s) * G + hd;
-      st_coh(part_o + p * kHeadDim + i, o);
-      if (i == 0) {
-        st_coh(part_l + p, l);
+      typedef float fv4 __attribute__((ext_vector_type(4)));
+      __builtin_amdgcn_raw_buffer_store_b128(fv4{o[0], o[1], o[2], o[3]}, rp,
+                                             4u * static_cast<uint32_t>(hd * kHeadDim + i0), 0, kCohAux);
+      if (i0 == 0) {
+        st_coh(part_l + (bh * n_splits + s) * G + hd, l);
         ms_s[hd] = ms;
       }
     }
