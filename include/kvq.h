@@ -177,6 +177,28 @@ kvq_status kvq_decode_attn_splits(kvq_cache* cache, int32_t layer, const void* q
                                   float softmax_scale, float* out, int32_t n_splits,
                                   kvq_stream stream);
 
+/* Key-cache fidelity diagnostics of `layer`: how well the stored keys preserve the
+   attention logits, after "RoPE-Aware Bit Allocation for KV-Cache Quantization",
+   abstract (per-layer query-key logit mean absolute error, keys only) and
+   "KV Cache Quantization on WikiText-2 prompt 2048-token (train)", evaluation
+   results (softmax KL divergence).  For sequence b and query head h (KV head
+   h / G), over the len(layer) cached positions t, in fp64:
+     a_t  = sigma * <q_h, k_t>     (k: the keys as given),
+     a^_t = sigma * <q_h, k^_t>    (k^: the stored keys, dequantized as decode
+                                    reads them),
+     mae[b][h] = mean_t |a_t - a^_t|,  kl[b][h] = KL(softmax(a) || softmax(a^)),
+   with sigma = softmax_scale, or 1/sqrt(head_dim) when softmax_scale <= 0.
+   q:    [batch][n_q_heads][head_dim] of `dtype`, device;
+   keys: [batch][len(layer)][n_kv_heads][head_dim] of `dtype`, device, 16-byte
+         aligned: the keys appended to this layer, in order (post-RoPE);
+   mae, kl: [batch][n_q_heads] fp64, device, caller-owned.
+   Uses a statistics buffer of the cache: calls on one cache must not overlap in
+   time.  Errors: KVQ_EINVAL (null or misaligned pointer, bad dtype or scale),
+   KVQ_ESTATE (layer empty or without plan). */
+kvq_status kvq_key_fidelity(kvq_cache* cache, int32_t layer, const void* q, const void* keys,
+                            int32_t dtype, float softmax_scale, double* mae, double* kl,
+                            kvq_stream stream);
+
 /* Tokens appended so far to `layer` (host bookkeeping; does not synchronize). */
 kvq_status kvq_seq_len(const kvq_cache* cache, int32_t layer, int64_t* len);
 

@@ -49,7 +49,8 @@ bool layer_ok(const kvq_cache* c, int32_t layer) {
 
 void free_device(kvq_cache* c) {
   void* ptrs[] = {c->k_codes, c->v_codes, c->k_scales, c->v_scales, c->plans,
-                  c->tables,  c->part_o,  c->part_l,  c->part_mt, c->energy_scratch, c->split_epochs};
+                  c->tables,  c->part_o,  c->part_l,  c->part_mt, c->energy_scratch, c->split_epochs,
+                  c->fid_part};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
 }
@@ -160,6 +161,12 @@ kvq_status kvq_cache_create(const kvq_config* cfg, kvq_cache** out) {
     st = dev_alloc(reinterpret_cast<void**>(&c->part_mt), per_split / (kHeadDim + 2) * 2 * ms, "partials");
   if (st == KVQ_OK)
     st = dev_alloc(reinterpret_cast<void**>(&c->split_epochs), sizeof(unsigned) * B * H, "split tags");
+  // fidelity diagnostics: about four workgroups per compute unit over the (sequence, KV head)
+  // units, six fp64 statistics per query head and split
+  c->fid_max_splits = static_cast<int>((4LL * c->n_cu + B * H - 1) / (B * H));
+  if (st == KVQ_OK)
+    st = dev_alloc(reinterpret_cast<void**>(&c->fid_part),
+                   sizeof(double) * 6 * B * H * c->group * c->fid_max_splits, "fidelity statistics");
   if (st == KVQ_OK) {
     const hipError_t es[] = {
         hipMemset(c->split_epochs, 0, sizeof(unsigned) * B * H),
@@ -298,6 +305,25 @@ kvq_status kvq_decode_attn_splits(kvq_cache* c, int32_t layer, const void* q, in
 kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, const void* q, int32_t dtype,
                            float softmax_scale, float* out, kvq_stream stream) {
   return kvq_decode_attn_splits(c, layer, q, dtype, softmax_scale, out, 0, stream);
+}
+
+kvq_status kvq_key_fidelity(kvq_cache* c, int32_t layer, const void* q, const void* keys,
+                            int32_t dtype, float softmax_scale, double* mae, double* kl,
+                            kvq_stream stream) {
+  if (!layer_ok(c, layer) || !q || !keys || !mae || !kl) return KVQ_EINVAL;
+  if (dtype != KVQ_F16 && dtype != KVQ_F32) return KVQ_EINVAL;
+  const size_t el = dtype == KVQ_F16 ? 2 : 4;
+  if (reinterpret_cast<uintptr_t>(q) % el || reinterpret_cast<uintptr_t>(keys) % 16 ||
+      reinterpret_cast<uintptr_t>(mae) % 8 || reinterpret_cast<uintptr_t>(kl) % 8) {
+    g_last_error = "fidelity: keys must be 16-byte, mae and kl 8-byte aligned";
+    return KVQ_EINVAL;
+  }
+  if (!(softmax_scale == softmax_scale)) return KVQ_EINVAL;  // NaN
+  if (!c->plan_ready[layer] || c->len[layer] == 0) return KVQ_ESTATE;
+  hipError_t e = kvq::launch_fidelity(c, layer, q, keys, dtype, softmax_scale, mae, kl,
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "fidelity launch");
+  return KVQ_OK;
 }
 
 kvq_status kvq_seq_len(const kvq_cache* c, int32_t layer, int64_t* len) {

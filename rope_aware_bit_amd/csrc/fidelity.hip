@@ -1,0 +1,282 @@
+// Key-cache fidelity diagnostics on gfx950: attention-logit MAE and softmax KL of the stored
+// keys against the keys as given.
+//
+// RoPE-Aware Bit Allocation for KV-Cache Quantization, abstract: the allocation is judged by
+// how well the stored keys preserve the query-key logits (per-layer mean absolute error,
+// keys only); KV Cache Quantization on WikiText-2 prompt 2048-token (train), evaluation
+// results: the softmax KL divergence of the attention distributions.  For query head h of
+// sequence b, over the cached positions t:
+//   a_t = sigma <q_h, k_t>,   a^_t = sigma <q_h, k^_t>,  k^ = the cache's keys dequantized
+//   (s_t g_i CB_{b_i}[code], or s_t NF[code] for the 256-value codec), all in fp64;
+//   mae = mean_t |a_t - a^_t|,  kl = KL(softmax(a) || softmax(a^)).
+//
+// Kernel 1 (fidelity_partials): one 256-lane workgroup per (split, KV head, sequence).  It
+// stages 64 positions at a time (the given keys with 16-byte loads, the packed rows, the
+// scales); lane (t, part) computes both logits of position t for query heads part and
+// part + 4 of the group, in fp64, and keeps running statistics per head: sum |a - a^|, and
+// for each distribution a running maximum M, the sum Z = sum e^(x - M) and (for a)
+// W = sum e^(a - M_a) (a - a^).  A wave then merges its 64 positions and stores the split's
+// six numbers per head.
+// Kernel 2 (fidelity_merge): one wave per (sequence, query head) merges the splits and
+// writes mae = sum |a - a^| / T and kl = W / Z_a - M_a - ln Z_a + M_b + ln Z_b.
+#include <hip/hip_fp16.h>
+
+#include <cmath>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kFidTok = 64;       // positions staged per round
+constexpr int kFidStats = 6;      // sum|d|, M_a, Z_a, W_a, M_b, Z_b
+
+template <typename T>
+__device__ inline double to_d(T v);
+template <>
+__device__ inline double to_d<__half>(__half v) { return static_cast<double>(__half2float(v)); }
+template <>
+__device__ inline double to_d<float>(float v) { return static_cast<double>(v); }
+
+struct Stats {
+  double abs_sum, ma, za, wa, mb, zb;
+};
+
+__device__ inline void stats_init(Stats& s) {
+  s.abs_sum = 0.0;
+  s.ma = s.mb = -INFINITY;
+  s.za = s.wa = s.zb = 0.0;
+}
+
+// adds one position with logits a (reference) and b (stored keys)
+__device__ inline void stats_add(Stats& s, double a, double b) {
+  s.abs_sum += fabs(a - b);
+  if (a > s.ma) {
+    const double r = exp(s.ma - a);   // 0 for the first position
+    s.za = s.za * r + 1.0;
+    s.wa = s.wa * r + (a - b);
+    s.ma = a;
+  } else {
+    const double e = exp(a - s.ma);
+    s.za += e;
+    s.wa += e * (a - b);
+  }
+  if (b > s.mb) {
+    s.zb = s.zb * exp(s.mb - b) + 1.0;
+    s.mb = b;
+  } else {
+    s.zb += exp(b - s.mb);
+  }
+}
+
+// merges o into s (either may be empty: M = -inf, Z = 0)
+__device__ inline void stats_merge(Stats& s, const Stats& o) {
+  s.abs_sum += o.abs_sum;
+  if (o.za > 0.0) {
+    if (s.za == 0.0) {
+      s.ma = o.ma;
+      s.za = o.za;
+      s.wa = o.wa;
+    } else {
+      const double m = fmax(s.ma, o.ma);
+      const double r1 = exp(s.ma - m), r2 = exp(o.ma - m);
+      s.za = s.za * r1 + o.za * r2;
+      s.wa = s.wa * r1 + o.wa * r2;
+      s.ma = m;
+    }
+  }
+  if (o.zb > 0.0) {
+    if (s.zb == 0.0) {
+      s.mb = o.mb;
+      s.zb = o.zb;
+    } else {
+      const double m = fmax(s.mb, o.mb);
+      s.zb = s.zb * exp(s.mb - m) + o.zb * exp(o.mb - m);
+      s.mb = m;
+    }
+  }
+}
+
+__device__ inline Stats stats_shfl_xor(const Stats& s, int mask) {
+  Stats o;
+  o.abs_sum = __shfl_xor(s.abs_sum, mask);
+  o.ma = __shfl_xor(s.ma, mask);
+  o.za = __shfl_xor(s.za, mask);
+  o.wa = __shfl_xor(s.wa, mask);
+  o.mb = __shfl_xor(s.mb, mask);
+  o.zb = __shfl_xor(s.zb, mask);
+  return o;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void fidelity_partials(
+    const T* __restrict__ q, const T* __restrict__ keys, int64_t len, int n_kv, int G, int64_t cap,
+    double sigma, int64_t tok_per_split, const Plan* __restrict__ plans, const Tables* __restrict__ tab,
+    const uint32_t* __restrict__ kc, const uint16_t* __restrict__ ks, int k_words, int n_nf, int nf,
+    double* __restrict__ part, int S) {
+  constexpr int kVec = 16 / sizeof(T);
+  constexpr int kRow = kHeadDim + kVec;            // padded key row (elements)
+  const int tid = threadIdx.x;
+  const int t = tid & 63, quarter = tid >> 6;
+  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int64_t bh = static_cast<int64_t>(b) * n_kv + h;
+  const int64_t t_begin = s * tok_per_split;
+  const int64_t t_end = t_begin + tok_per_split < len ? t_begin + tok_per_split : len;
+
+  __shared__ double q_s[kMaxGroup][kHeadDim];
+  __shared__ double g_s[kHeadDim];
+  __shared__ uint16_t cb_s[kMaxBits + 1][256];
+  __shared__ uint8_t fdim_s[kHeadDim], fw_s[kHeadDim];
+  __shared__ uint16_t foff_s[kHeadDim];
+  __shared__ __attribute__((aligned(16))) T x_s[kFidTok][kRow];
+  __shared__ uint32_t kr_s[kFidTok][4 * kMaxBits + 1];
+  __shared__ double sc_s[kFidTok];
+  __shared__ int nf_s;
+
+  const Plan* P = plans + h;
+  for (int k = tid; k < G * kHeadDim; k += 256)
+    q_s[k / kHeadDim][k % kHeadDim] = to_d(q[(static_cast<int64_t>(b) * n_kv * G + h * G) * kHeadDim + k]);
+  for (int k = tid; k < (kMaxBits + 1) * 256; k += 256) {
+    const int w = k >> 8, c = k & 255;
+    cb_s[w][c] = nf ? (w == 4 && c < 16 ? tab->nf_cb[c] : 0) : (w >= 1 ? tab->cb[w][c] : 0);
+  }
+  if (tid < kHeadDim) {
+    g_s[tid] = nf ? 1.0 : static_cast<double>(P->g[tid]);
+    fdim_s[tid] = P->fdim[tid];
+    fw_s[tid] = P->fwidth[tid];
+    foff_s[tid] = P->foff[tid];
+  }
+  if (tid == 0) nf_s = P->n_fields;
+  __syncthreads();
+  const int n_fields = nf_s;
+
+  Stats st[2];
+  stats_init(st[0]);
+  stats_init(st[1]);
+  for (int64_t r0 = t_begin; r0 < t_end; r0 += kFidTok) {
+    const int nr = t_end - r0 < kFidTok ? static_cast<int>(t_end - r0) : kFidTok;
+    // stage the given keys (16-byte pieces), the packed rows and the scales
+    for (int k = tid; k < nr * (kHeadDim / kVec); k += 256) {
+      const int r = k / (kHeadDim / kVec), c = k % (kHeadDim / kVec);
+      const int64_t src = ((static_cast<int64_t>(b) * len + r0 + r) * n_kv + h) * kHeadDim + c * kVec;
+      *reinterpret_cast<uint4*>(&x_s[r][c * kVec]) = *reinterpret_cast<const uint4*>(keys + src);
+    }
+    for (int k = tid; k < nr * k_words; k += 256) {
+      const int r = k / k_words, c = k % k_words;
+      kr_s[r][c] = kc[(bh * cap + r0 + r) * k_words + c];
+    }
+    if (tid < nr) {
+      const uint16_t sb = nf ? ks[(static_cast<int64_t>(b) * cap + r0 + tid) * n_nf + h / 2] : ks[bh * cap + r0 + tid];
+      sc_s[tid] = static_cast<double>(__half2float(__ushort_as_half(sb)));
+    }
+    if (tid < kFidTok) kr_s[tid][k_words] = 0u;   // zero word after the row (fields read two words)
+    __syncthreads();
+    if (t < nr) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int hl = quarter + 4 * j;
+        if (hl >= G) continue;
+        double a = 0.0, ah = 0.0;
+        // the row in 16-byte pieces: with the padded stride, 8 consecutive lanes read 8
+        // distinct groups of banks
+        for (int c = 0; c < kHeadDim / kVec; ++c) {
+          const uint4 raw = *reinterpret_cast<const uint4*>(&x_s[t][c * kVec]);
+          T xv[kVec];
+          __builtin_memcpy(xv, &raw, 16);
+#pragma unroll
+          for (int e = 0; e < kVec; ++e) a += to_d(xv[e]) * q_s[hl][c * kVec + e];
+        }
+        const double s16 = sc_s[t];
+        for (int f = 0; f < n_fields; ++f) {
+          const int off = foff_s[f], w = fw_s[f], dim = fdim_s[f];
+          const uint64_t two = static_cast<uint64_t>(kr_s[t][off >> 5]) |
+                               (static_cast<uint64_t>(kr_s[t][(off >> 5) + 1]) << 32);
+          const uint32_t code = static_cast<uint32_t>(two >> (off & 31)) & ((1u << w) - 1u);
+          const double c = static_cast<double>(__half2float(__ushort_as_half(cb_s[w][code])));
+          const double kh = (s16 * g_s[dim]) * c;
+          ah += kh * q_s[hl][dim];
+        }
+        stats_add(st[j], sigma * a, sigma * ah);
+      }
+    }
+    __syncthreads();
+  }
+  // merge the 64 positions of the wave, then lane 0 stores the split's statistics per head
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    for (int m = 32; m >= 1; m >>= 1) {
+      const Stats o = stats_shfl_xor(st[j], m);
+      stats_merge(st[j], o);
+    }
+    const int hl = quarter + 4 * j;
+    if (t == 0 && hl < G) {
+      double* p = part + ((bh * G + hl) * S + s) * kFidStats;
+      p[0] = st[j].abs_sum;
+      p[1] = st[j].ma;
+      p[2] = st[j].za;
+      p[3] = st[j].wa;
+      p[4] = st[j].mb;
+      p[5] = st[j].zb;
+    }
+  }
+}
+
+__global__ __launch_bounds__(64) void fidelity_merge(const double* __restrict__ part, int S, int64_t len,
+                                                     double* __restrict__ mae, double* __restrict__ kl) {
+  const int lane = threadIdx.x;
+  const int64_t hq = blockIdx.x;   // sequence * n_q + query head
+  Stats st;
+  stats_init(st);
+  for (int s = lane; s < S; s += 64) {
+    const double* p = part + (hq * S + s) * kFidStats;
+    Stats o{p[0], p[1], p[2], p[3], p[4], p[5]};
+    stats_merge(st, o);
+  }
+  for (int m = 32; m >= 1; m >>= 1) {
+    const Stats o = stats_shfl_xor(st, m);
+    stats_merge(st, o);
+  }
+  if (lane == 0) {
+    mae[hq] = st.abs_sum / static_cast<double>(len);
+    kl[hq] = st.wa / st.za - st.ma - log(st.za) + st.mb + log(st.zb);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fidelity(kvq_cache* c, int layer, const void* q, const void* keys, int dtype,
+                           float scale, double* mae, double* kl, hipStream_t stream) {
+  const kvq_config& cfg = c->cfg;
+  const int64_t len = c->len[layer];
+  const int H = cfg.n_kv_heads, B = cfg.batch, G = c->group;
+  const int64_t units = static_cast<int64_t>(B) * H;
+  // about four workgroups per compute unit, at least 256 positions each
+  int64_t S = (4LL * c->n_cu + units - 1) / units;
+  const int64_t by_len = (len + 255) / 256;
+  if (S > by_len) S = by_len;
+  if (S > c->fid_max_splits) S = c->fid_max_splits;
+  if (S < 1) S = 1;
+  const int64_t per = ((len + S - 1) / S + kFidTok - 1) / kFidTok * kFidTok;
+  S = (len + per - 1) / per;
+  const double sigma = scale > 0.0f ? static_cast<double>(scale) : 1.0 / std::sqrt(static_cast<double>(kHeadDim));
+  const bool nf = cfg.codec == KVQ_CODEC_NF16_B256;
+  const Plan* plans = c->plans + static_cast<int64_t>(layer) * H;
+  dim3 grid(static_cast<unsigned>(S), static_cast<unsigned>(H), static_cast<unsigned>(B));
+  if (dtype == KVQ_F16)
+    hipLaunchKernelGGL(fidelity_partials<__half>, grid, dim3(256), 0, stream, static_cast<const __half*>(q),
+                       static_cast<const __half*>(keys), len, H, G, c->cap, sigma, per, plans, c->tables,
+                       layer_k_codes(c, layer), layer_k_scales(c, layer), c->k_words, c->n_nf_blocks,
+                       nf ? 1 : 0, c->fid_part, static_cast<int>(S));
+  else
+    hipLaunchKernelGGL(fidelity_partials<float>, grid, dim3(256), 0, stream, static_cast<const float*>(q),
+                       static_cast<const float*>(keys), len, H, G, c->cap, sigma, per, plans, c->tables,
+                       layer_k_codes(c, layer), layer_k_scales(c, layer), c->k_words, c->n_nf_blocks,
+                       nf ? 1 : 0, c->fid_part, static_cast<int>(S));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fidelity_merge, dim3(static_cast<unsigned>(units * G)), dim3(64), 0, stream, c->fid_part,
+                     static_cast<int>(S), len, mae, kl);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -83,6 +83,8 @@ struct kvq_cache {
   unsigned* split_epochs;      // [B][H] tag base of the next call's split partials
   int max_splits;
   double* energy_scratch;      // [H][n_chunks][64]
+  double* fid_part;            // fidelity split statistics [B][n_q][fid_max_splits][6]
+  int fid_max_splits;
   int64_t energy_scratch_chunks;
   // byte sizes per layer
   int64_t k_codes_layer, v_codes_layer, k_scales_layer, v_scales_layer;
@@ -98,6 +100,8 @@ hipError_t launch_quantize(kvq_cache* c, int layer, const void* k, const void* v
                            int64_t n_new, hipStream_t stream);
 hipError_t launch_decode_mfma(kvq_cache* c, int layer, const void* q, int dtype, float scale,
                               float* out, int n_splits, hipStream_t stream);
+hipError_t launch_fidelity(kvq_cache* c, int layer, const void* q, const void* keys, int dtype,
+                           float scale, double* mae, double* kl, hipStream_t stream);
 int auto_splits_mfma(const kvq_cache* c, int64_t len);
 
 // Launch shape of the decode kernel for a cache: waves per workgroup (8 = two per SIMD, or 4),

@@ -24,7 +24,7 @@ PART_K_CODES, PART_V_CODES, PART_K_SCALES, PART_V_SCALES = range(4)
 
 EXPORTED = (
     "kvq_cache_create", "kvq_cache_destroy", "kvq_alloc_bits", "kvq_get_plan",
-    "kvq_quantize_append", "kvq_decode_attn", "kvq_decode_attn_splits", "kvq_seq_len",
+    "kvq_quantize_append", "kvq_decode_attn", "kvq_decode_attn_splits", "kvq_key_fidelity", "kvq_seq_len",
     "kvq_layer_info_get", "kvq_read_cache", "kvq_codebook", "kvq_delta",
     "kvq_nf16_codebook", "kvq_status_str", "kvq_last_error",
 )
@@ -67,6 +67,7 @@ def _load() -> ctypes.CDLL:
         "kvq_quantize_append": (I32, [P, I32, P, P, I32, I64, P]),
         "kvq_decode_attn": (I32, [P, I32, P, I32, F32, P, P]),
         "kvq_decode_attn_splits": (I32, [P, I32, P, I32, F32, P, I32, P]),
+        "kvq_key_fidelity": (I32, [P, I32, P, P, I32, F32, P, P, P]),
         "kvq_seq_len": (I32, [P, I32, ctypes.POINTER(I64)]),
         "kvq_layer_info_get": (I32, [P, I32, ctypes.POINTER(kvq_layer_info)]),
         "kvq_read_cache": (I32, [P, I32, I32, I64, I64, P]),
@@ -233,6 +234,25 @@ class Cache:
         _check(lib.kvq_decode_attn_splits(self._h, layer, _ptr(q), _dtype_code(q), float(scale),
                                           _ptr(out), int(n_splits), _stream(stream)), "kvq_decode_attn")
         return out
+
+    def key_fidelity(self, layer: int, q, keys, scale: float = 0.0, stream=None):
+        """(mae, kl) fp64 [batch, n_q_heads] of the stored keys of `layer` against `keys`
+        [batch, len, n_kv_heads, head_dim] (the keys appended to it), for queries q."""
+        import torch
+        B, Hq, d = self.cfg.batch, self.cfg.n_q_heads, self.cfg.head_dim
+        if q.dim() != 3 or tuple(q.shape) != (B, Hq, d):
+            raise ValueError(f"q must be [batch, n_q_heads, head_dim], got {tuple(q.shape)}")
+        if keys.dim() != 4 or keys.shape[0] != B or keys.shape[2] != self.cfg.n_kv_heads or keys.shape[3] != d:
+            raise ValueError(f"keys must be [batch, len, n_kv_heads, head_dim], got {tuple(keys.shape)}")
+        if keys.shape[1] != self.seq_len(layer):
+            raise ValueError("keys must hold exactly the positions appended to the layer")
+        if keys.dtype != q.dtype:
+            raise ValueError("q and keys must have the same dtype")
+        mae = torch.empty((B, Hq), dtype=torch.float64, device=q.device)
+        kl = torch.empty((B, Hq), dtype=torch.float64, device=q.device)
+        _check(lib.kvq_key_fidelity(self._h, layer, _ptr(q), _ptr(keys), _dtype_code(q), float(scale),
+                                    _ptr(mae), _ptr(kl), _stream(stream)), "kvq_key_fidelity")
+        return mae, kl
 
     def seq_len(self, layer: int) -> int:
         n = ctypes.c_int64()

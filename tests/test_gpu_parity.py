@@ -2,12 +2,15 @@
 
 Plans, codes, packed words and scales must be bit-exact; decode attention
 must match the oracle's fp64 attention over its own dequantized cache within
-max-abs 2e-3 and relative L2 1e-3.
+max-abs 2e-3 and relative L2 1e-3.  The key-fidelity diagnostics (fp64 on both
+sides, the same exact products, sums in another order) must match the oracle's
+within 1e-9 relative + 1e-12 absolute.
 """
 import numpy as np
 import pytest
 
 from oracle import attention as at
+from oracle import fidelity as fd
 from oracle import layout as lay
 from synth import WORKLOADS, gen_layer, gen_query
 from tests.parity import CODEC, PAIRING, OracleLayer, assert_attention_close, errors
@@ -28,7 +31,7 @@ def _kvq():
 
 def run_case(wname, T, k_bits, v_bits, codec="bgtq", pairing="half", batch=None, layer=0,
              chunks=None, n_splits=0, noise="gauss", temper=False, check_codes=True, sample_rows=None,
-             b_min=0, b_max=8):
+             b_min=0, b_max=8, fidelity=True):
     """Quantize T tokens of one layer on the GPU and in the oracle; compare everything."""
     torch = _torch()
     kvq = _kvq()
@@ -123,8 +126,25 @@ def run_case(wname, T, k_bits, v_bits, codec="bgtq", pairing="half", batch=None,
     ref = np.stack([at.decode_attention(Q[b].astype(np.float64), refs[b][1], refs[b][2],
                                         sigma if sigma > 0 else None) for b in range(B)])
     res = assert_attention_close(got, ref, f"{wname} T={T} K{k_bits}V{v_bits} {codec}")
+    if fidelity:
+        mae, kl = cache.key_fidelity(0, Qt, Kt, scale=sigma)
+        mae, kl = mae.cpu().numpy(), kl.cpu().numpy()
+        for b in range(B):
+            # the ABI takes the scale as fp32
+            rm, rk = fd.logit_fidelity(Q[b], np.transpose(K[b], (1, 0, 2)), refs[b][1],
+                                       float(np.float32(sigma)) if sigma > 0 else None)
+            assert_fidelity_close(mae[b], rm, f"{wname} T={T} mae b={b}")
+            assert_fidelity_close(kl[b], rk, f"{wname} T={T} kl b={b}")
     cache.close()
     return res
+
+
+FID_REL, FID_ABS = 1e-9, 1e-12
+
+
+def assert_fidelity_close(gpu, ref, what):
+    err = np.abs(np.asarray(gpu) - ref)
+    assert np.all(err <= FID_REL * np.abs(ref) + FID_ABS), f"{what}: max err {err.max():.3e} ref {ref}"
 
 
 def test_tiny_end_to_end():
@@ -214,6 +234,9 @@ def test_error_states():
     with pytest.raises(kvq.KvqError) as e:
         cache.decode_attn(0, q)                               # empty layer
     assert e.value.status == kvq.KVQ_ESTATE
+    st = torch.zeros(2, dtype=torch.float64, device=dev)
+    assert kvq.lib.kvq_key_fidelity(cache.handle, 0, q.data_ptr(), x.data_ptr(), kvq.KVQ_F16, 0.0,
+                                    st.data_ptr(), st.data_ptr(), None) == kvq.KVQ_ESTATE   # empty layer
     cache.quantize_append(0, x[:, :0].contiguous(), x[:, :0].contiguous())   # n_new = 0 is a no-op
     assert cache.seq_len(0) == 0
     cache.quantize_append(0, x, x)
@@ -230,6 +253,11 @@ def test_error_states():
     assert e.value.status == kvq.KVQ_EINVAL
     out = cache.decode_attn(0, q)
     assert torch.isfinite(out).all()
+    raw = torch.zeros(1 * 10 * 2 * 128 + 1, dtype=torch.float16, device=dev)
+    assert kvq.lib.kvq_key_fidelity(cache.handle, 0, q.data_ptr(), raw.data_ptr() + 2, kvq.KVQ_F16, 0.0,
+                                    out.data_ptr(), out.data_ptr(), None) == kvq.KVQ_EINVAL   # misaligned keys
+    mae, kl = cache.key_fidelity(0, q, x)
+    assert torch.isfinite(mae).all() and torch.isfinite(kl).all()
     cache.close()
 
 
