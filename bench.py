@@ -166,10 +166,11 @@ def main():
         app_ms.append(e0.elapsed_time(e1))
         if layer == 0:
             keep = (k.cpu().numpy(), v.cpu().numpy(), k[:chunk].cpu().numpy())
+            keys0 = k[None].contiguous()        # layer 0's keys as given, for the fidelity diagnostics
         del k, v
     qs = [gen.query(layer)[None].contiguous() for layer in range(L)]
     if args.traffic_probe:
-        keep = None
+        keep = keys0 = None
     outs = [torch.empty(B, Hq, 128, dtype=torch.float32, device=dev) for _ in range(L)]
     torch.cuda.synchronize()
     log(f"setup {time.perf_counter() - t_setup:.1f} s")
@@ -208,6 +209,21 @@ def main():
     for o in outs:
         assert torch.isfinite(o).all()
 
+    # key-fidelity diagnostics of layer 0 (logit MAE and softmax KL against the given keys)
+    fid_reps = 5
+    cache.key_fidelity(0, qs[0], keys0)
+    torch.cuda.synchronize()
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    f0.record(stream)
+    for _ in range(fid_reps):
+        mae, kl = cache.key_fidelity(0, qs[0], keys0)
+    f1.record(stream)
+    torch.cuda.synchronize()
+    fid_us = f0.elapsed_time(f1) * 1e3 / fid_reps
+    fid_bytes = B * T * H * (128 * 2 + kb * 16 + 2) + B * Hq * 128 * 2
+    fid_flops = 2 * 2 * 128 * B * T * Hq          # two fp64 dot products per (position, query head)
+    del keys0
+
     # average decode-launch duration: the timed region holds only decode launches on this stream
     launch_us = ms_step * 1e3 / L
 
@@ -240,6 +256,14 @@ def main():
             "us_per_layer": round(float(np.mean(app_ms)) * 1e3, 2),
             "GB/s": round((B * H * chunk * (2 * 128 * 2 + (kb + vb) * 16 + 4)) /
                           (float(np.mean(app_ms)) * 1e-3) / 1e9, 2),
+        },
+        "fidelity": {
+            "layer": 0,
+            "us_per_layer": round(fid_us, 2),
+            "GB/s": round(fid_bytes / (fid_us * 1e-6) / 1e9, 2),
+            "fp64_TFLOP/s": round(fid_flops / (fid_us * 1e-6) / 1e12, 2),
+            "logit_mae_mean": round(float(mae.mean()), 6),
+            "softmax_kl_mean": float(f"{float(kl.mean()):.6g}"),
         },
         "roofline": {
             "bound": "hbm",

@@ -12,11 +12,12 @@
 //
 // Kernel 1 (fidelity_partials): one 256-lane workgroup per (split, KV head, sequence).  It
 // stages 64 positions at a time (the given keys with 16-byte loads, the packed rows, the
-// scales); lane (t, part) computes both logits of position t for query heads part and
-// part + 4 of the group, in fp64, and keeps running statistics per head: sum |a - a^|, and
-// for each distribution a running maximum M, the sum Z = sum e^(x - M) and (for a)
-// W = sum e^(a - M_a) (a - a^).  A wave then merges its 64 positions and stores the split's
-// six numbers per head.
+// scales).  Four lanes share a position: each takes a quarter of the dims (given row) and of
+// the fields (stored row) for all G heads, in fp64, and the quarters are summed across the
+// four lanes.  Lane quarter q then keeps running statistics of heads q and q + 4: sum
+// |a - a^|, and for each distribution a running maximum M, the sum Z = sum e^(x - M) and
+// (for a) W = sum e^(a - M_a) (a - a^).  The lanes' statistics are merged within each wave,
+// then across the four waves, and the split's six numbers per head are stored.
 // Kernel 2 (fidelity_merge): one wave per (sequence, query head) merges the splits and
 // writes mae = sum |a - a^| / T and kl = W / Z_a - M_a - ln Z_a + M_b + ln Z_b.
 #include <hip/hip_fp16.h>
@@ -108,16 +109,16 @@ __device__ inline Stats stats_shfl_xor(const Stats& s, int mask) {
   return o;
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void fidelity_partials(
-    const T* __restrict__ q, const T* __restrict__ keys, int64_t len, int n_kv, int G, int64_t cap,
+template <typename T, int G>
+__global__ __launch_bounds__(256, 2) void fidelity_partials(
+    const T* __restrict__ q, const T* __restrict__ keys, int64_t len, int n_kv, int64_t cap,
     double sigma, int64_t tok_per_split, const Plan* __restrict__ plans, const Tables* __restrict__ tab,
     const uint32_t* __restrict__ kc, const uint16_t* __restrict__ ks, int k_words, int n_nf, int nf,
     double* __restrict__ part, int S) {
   constexpr int kVec = 16 / sizeof(T);
   constexpr int kRow = kHeadDim + kVec;            // padded key row (elements)
   const int tid = threadIdx.x;
-  const int t = tid & 63, quarter = tid >> 6;
+  const int t = tid >> 2, quarter = tid & 3;   // position of the round, quarter of the row
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int64_t bh = static_cast<int64_t>(b) * n_kv + h;
   const int64_t t_begin = s * tok_per_split;
@@ -172,52 +173,99 @@ __global__ __launch_bounds__(256) void fidelity_partials(
     if (tid < kFidTok) kr_s[tid][k_words] = 0u;   // zero word after the row (fields read two words)
     __syncthreads();
     if (t < nr) {
+      // lane (t, quarter): dims 32 quarter .. + 31 of the given row and fields 32 quarter ..
+      // + 31 of the stored row, for all G heads; the four quarters are then summed
+      double a[G], ah[G];
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) a[hh] = ah[hh] = 0.0;
+      constexpr int kPer = 32 / kVec;   // 16-byte pieces per quarter row
+#pragma unroll 1
+      for (int cc = 0; cc < kPer; ++cc) {
+        const int c = quarter * kPer + (cc + quarter) % kPer;   // rotated: fewer bank conflicts
+        const uint4 raw = *reinterpret_cast<const uint4*>(&x_s[t][c * kVec]);
+        T xv[kVec];
+        __builtin_memcpy(xv, &raw, 16);
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) {
+          const double x = to_d(xv[e]);
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh) a[hh] += x * q_s[hh][c * kVec + e];
+        }
+      }
+      const double s16 = sc_s[t];
+      const int f_end = n_fields < 32 * quarter + 32 ? n_fields : 32 * quarter + 32;
+#pragma unroll 2
+      for (int f = 32 * quarter; f < f_end; ++f) {
+        const int off = foff_s[f], w = fw_s[f], dim = fdim_s[f];
+        const uint64_t two = static_cast<uint64_t>(kr_s[t][off >> 5]) |
+                             (static_cast<uint64_t>(kr_s[t][(off >> 5) + 1]) << 32);
+        const uint32_t code = static_cast<uint32_t>(two >> (off & 31)) & ((1u << w) - 1u);
+        const double c = static_cast<double>(__half2float(__ushort_as_half(cb_s[w][code])));
+        const double kh = (s16 * g_s[dim]) * c;
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) ah[hh] += kh * q_s[hh][dim];
+      }
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        a[hh] += __shfl_xor(a[hh], 1);
+        a[hh] += __shfl_xor(a[hh], 2);
+        ah[hh] += __shfl_xor(ah[hh], 1);
+        ah[hh] += __shfl_xor(ah[hh], 2);
+      }
+      // lane (t, quarter) keeps the statistics of heads quarter and quarter + 4
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int hl = quarter + 4 * j;
         if (hl >= G) continue;
-        double a = 0.0, ah = 0.0;
-        // the row in 16-byte pieces: with the padded stride, 8 consecutive lanes read 8
-        // distinct groups of banks
-        for (int c = 0; c < kHeadDim / kVec; ++c) {
-          const uint4 raw = *reinterpret_cast<const uint4*>(&x_s[t][c * kVec]);
-          T xv[kVec];
-          __builtin_memcpy(xv, &raw, 16);
+        double av = a[0], bv = ah[0];
 #pragma unroll
-          for (int e = 0; e < kVec; ++e) a += to_d(xv[e]) * q_s[hl][c * kVec + e];
+        for (int hh = 1; hh < G; ++hh) {
+          if (hh == hl) {
+            av = a[hh];
+            bv = ah[hh];
+          }
         }
-        const double s16 = sc_s[t];
-        for (int f = 0; f < n_fields; ++f) {
-          const int off = foff_s[f], w = fw_s[f], dim = fdim_s[f];
-          const uint64_t two = static_cast<uint64_t>(kr_s[t][off >> 5]) |
-                               (static_cast<uint64_t>(kr_s[t][(off >> 5) + 1]) << 32);
-          const uint32_t code = static_cast<uint32_t>(two >> (off & 31)) & ((1u << w) - 1u);
-          const double c = static_cast<double>(__half2float(__ushort_as_half(cb_s[w][code])));
-          const double kh = (s16 * g_s[dim]) * c;
-          ah += kh * q_s[hl][dim];
-        }
-        stats_add(st[j], sigma * a, sigma * ah);
+        stats_add(st[j], sigma * av, sigma * bv);
       }
     }
     __syncthreads();
   }
-  // merge the 64 positions of the wave, then lane 0 stores the split's statistics per head
+  // merge the wave's positions (lanes of one quarter), then the four waves through LDS
+  __shared__ double wst_s[4][kMaxGroup][kFidStats];
+  const int wave = tid >> 6;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    for (int m = 32; m >= 1; m >>= 1) {
+    for (int m = 4; m <= 32; m <<= 1) {
       const Stats o = stats_shfl_xor(st[j], m);
       stats_merge(st[j], o);
     }
     const int hl = quarter + 4 * j;
-    if (t == 0 && hl < G) {
-      double* p = part + ((bh * G + hl) * S + s) * kFidStats;
-      p[0] = st[j].abs_sum;
-      p[1] = st[j].ma;
-      p[2] = st[j].za;
-      p[3] = st[j].wa;
-      p[4] = st[j].mb;
-      p[5] = st[j].zb;
+    if ((tid & 63) < 4 && hl < G) {
+      double* d = wst_s[wave][hl];
+      d[0] = st[j].abs_sum;
+      d[1] = st[j].ma;
+      d[2] = st[j].za;
+      d[3] = st[j].wa;
+      d[4] = st[j].mb;
+      d[5] = st[j].zb;
     }
+  }
+  __syncthreads();
+  if (tid < G) {
+    Stats acc;
+    stats_init(acc);
+    for (int w = 0; w < 4; ++w) {
+      const double* d = wst_s[w][tid];
+      const Stats o{d[0], d[1], d[2], d[3], d[4], d[5]};
+      stats_merge(acc, o);
+    }
+    double* p = part + ((bh * G + tid) * S + s) * kFidStats;
+    p[0] = acc.abs_sum;
+    p[1] = acc.ma;
+    p[2] = acc.za;
+    p[3] = acc.wa;
+    p[4] = acc.mb;
+    p[5] = acc.zb;
   }
 }
 
@@ -262,16 +310,25 @@ hipError_t launch_fidelity(kvq_cache* c, int layer, const void* q, const void* k
   const bool nf = cfg.codec == KVQ_CODEC_NF16_B256;
   const Plan* plans = c->plans + static_cast<int64_t>(layer) * H;
   dim3 grid(static_cast<unsigned>(S), static_cast<unsigned>(H), static_cast<unsigned>(B));
-  if (dtype == KVQ_F16)
-    hipLaunchKernelGGL(fidelity_partials<__half>, grid, dim3(256), 0, stream, static_cast<const __half*>(q),
-                       static_cast<const __half*>(keys), len, H, G, c->cap, sigma, per, plans, c->tables,
-                       layer_k_codes(c, layer), layer_k_scales(c, layer), c->k_words, c->n_nf_blocks,
-                       nf ? 1 : 0, c->fid_part, static_cast<int>(S));
-  else
-    hipLaunchKernelGGL(fidelity_partials<float>, grid, dim3(256), 0, stream, static_cast<const float*>(q),
-                       static_cast<const float*>(keys), len, H, G, c->cap, sigma, per, plans, c->tables,
-                       layer_k_codes(c, layer), layer_k_scales(c, layer), c->k_words, c->n_nf_blocks,
-                       nf ? 1 : 0, c->fid_part, static_cast<int>(S));
+#define KVQ_FID(T, GG)                                                                              \
+  hipLaunchKernelGGL((fidelity_partials<T, GG>), grid, dim3(256), 0, stream, static_cast<const T*>(q), \
+                     static_cast<const T*>(keys), len, H, c->cap, sigma, per, plans, c->tables,       \
+                     layer_k_codes(c, layer), layer_k_scales(c, layer), c->k_words, c->n_nf_blocks,   \
+                     nf ? 1 : 0, c->fid_part, static_cast<int>(S))
+#define KVQ_FID_G(T)                  \
+  switch (G) {                        \
+    case 1: KVQ_FID(T, 1); break;     \
+    case 2: KVQ_FID(T, 2); break;     \
+    case 4: KVQ_FID(T, 4); break;     \
+    default: KVQ_FID(T, 8); break;    \
+  }
+  if (dtype == KVQ_F16) {
+    KVQ_FID_G(__half)
+  } else {
+    KVQ_FID_G(float)
+  }
+#undef KVQ_FID_G
+#undef KVQ_FID
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(fidelity_merge, dim3(static_cast<unsigned>(units * G)), dim3(64), 0, stream, c->fid_part,
