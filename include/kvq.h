@@ -83,6 +83,11 @@ typedef struct {
   int32_t codec;       /* kvq_codec; NF16_B256 needs k_bits = v_bits = 4 and
                           n_kv_heads*128 divisible by 256 */
   int32_t pairing;     /* kvq_pairing */
+  int32_t recent_window; /* R in [0, 4096]: the most recent min(len, R) tokens of each
+                            sequence and layer are kept in fp16 (K and V) instead of the
+                            packed cache; 0 = none.  The paper's own results use none (RoPE-
+                            aware bit allocation page, abstract: "without an fp16 recent-key
+                            buffer"); the leaderboard's "Buffer Setting" is this option. */
 } kvq_config;
 
 /* Layout facts of one layer's packed storage, for parity dumps (see kvq_read_cache). */
@@ -102,13 +107,20 @@ typedef struct {
                               NF16 [batch][capacity][n_kv*128/256] */
   int64_t v_scales_bytes;  /* fp16 V scales, same shapes as K scales */
   int32_t plan_ready;      /* 1 once kvq_alloc_bits has run for this layer */
+  int32_t recent_window;   /* R of the config */
+  int64_t packed_len;      /* positions held by the packed storage: max(0, len - R); positions
+                              packed_len .. len-1 are in the recent window */
+  int64_t recent_bytes;    /* bytes of one layer's recent-window K (or V) ring:
+                              [batch][R][n_kv][128] fp16, position p in slot p mod R */
 } kvq_layer_info;
 
 typedef enum {
   KVQ_PART_K_CODES = 0,
   KVQ_PART_V_CODES = 1,
   KVQ_PART_K_SCALES = 2,
-  KVQ_PART_V_SCALES = 3
+  KVQ_PART_V_SCALES = 3,
+  KVQ_PART_K_RECENT = 4,   /* recent-window rings (see kvq_layer_info) */
+  KVQ_PART_V_RECENT = 5
 } kvq_part;
 
 /* Create a cache for cfg and allocate its full capacity on the current device.
@@ -151,6 +163,10 @@ kvq_status kvq_get_plan(const kvq_cache* cache, int32_t layer, int8_t* bits, flo
    y = x * ig_j; s = fp16(fp32(sqrt(sum y^2 / 128))); u = y * fp32(1/s);
    code = number of codebook boundaries below u.  NF16: s = fp16(absmax) per
    256 values, u = x * fp32(1/s).
+   With a recent window R > 0, positions stay in fp16 (rounded once if given in
+   fp32) while they are among the last R of the sequence; a position is
+   quantized, from its fp16 copy, when it leaves the window, so the packed
+   storage always covers positions 0 .. len-R-1.
    Errors: KVQ_EINVAL, KVQ_ESTATE (no plan for the layer), KVQ_ECAPACITY. */
 kvq_status kvq_quantize_append(kvq_cache* cache, int32_t layer, const void* k, const void* v,
                                int32_t dtype, int64_t n_new, kvq_stream stream);
@@ -161,6 +177,8 @@ kvq_status kvq_quantize_append(kvq_cache* cache, int32_t layer, const void* k, c
    q:     [batch][n_q_heads][128] (dtype), 4-byte aligned.
    softmax_scale: sigma; <= 0 selects 1/sqrt(128).
    out:   [batch][n_q_heads][128] fp32 device buffer, 16-byte aligned.
+   With a recent window, the last min(len, R) tokens are read in fp16 from the
+   window (x_hat = the fp16 values) and the others from the packed storage.
    The context is split into chunks processed in parallel, each producing a
    partial (max, sum, weighted sum); the last chunks of each (sequence, KV head)
    to finish combine them in fixed order.  Decode calls on one cache must not
@@ -185,7 +203,7 @@ kvq_status kvq_decode_attn_splits(kvq_cache* cache, int32_t layer, const void* q
    h / G), over the len(layer) cached positions t, in fp64:
      a_t  = sigma * <q_h, k_t>     (k: the keys as given),
      a^_t = sigma * <q_h, k^_t>    (k^: the stored keys, dequantized as decode
-                                    reads them),
+                                    reads them; fp16 copies inside a recent window),
      mae[b][h] = mean_t |a_t - a^_t|,  kl[b][h] = KL(softmax(a) || softmax(a^)),
    with sigma = softmax_scale, or 1/sqrt(head_dim) when softmax_scale <= 0.
    q:    [batch][n_q_heads][head_dim] of `dtype`, device;

@@ -32,6 +32,7 @@ bool config_valid(const kvq_config* c) {
   const int G = c->n_q_heads / c->n_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return false;
   if (c->codec < KVQ_CODEC_BGTQ || c->codec > KVQ_CODEC_NF16_B256) return false;
+  if (c->recent_window < 0 || c->recent_window > kvq::kMaxRecent) return false;
   if (c->pairing != KVQ_ROPE_HALF && c->pairing != KVQ_ROPE_INTERLEAVED) return false;
   if (c->v_bits < 1 || c->v_bits > kMaxBits) return false;
   if (c->b_min < 0 || c->b_max > kMaxBits || c->b_min > c->b_max) return false;
@@ -50,7 +51,7 @@ bool layer_ok(const kvq_cache* c, int32_t layer) {
 void free_device(kvq_cache* c) {
   void* ptrs[] = {c->k_codes, c->v_codes, c->k_scales, c->v_scales, c->plans,
                   c->tables,  c->part_o,  c->part_l,  c->part_mt, c->energy_scratch, c->split_epochs,
-                  c->fid_part};
+                  c->fid_part, c->k_recent, c->v_recent};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
 }
@@ -137,6 +138,7 @@ kvq_status kvq_cache_create(const kvq_config* cfg, kvq_cache** out) {
   c->v_codes_layer = B * H * cap * c->v_words * 4;  // (cap/128) tiles * 128 dims * v_words words
   c->k_scales_layer = nf ? B * cap * c->n_nf_blocks * 2 : B * H * cap * 2;
   c->v_scales_layer = c->k_scales_layer;
+  c->recent_layer = B * cfg->recent_window * H * kHeadDim * 2;
   // split partials: at most 256 splits per (sequence, head), at most 256 MiB of partials
   int64_t per_split = B * H * c->group * (kHeadDim + 2) * 4;
   int64_t ms = (int64_t(256) << 20) / per_split;
@@ -151,6 +153,10 @@ kvq_status kvq_cache_create(const kvq_config* cfg, kvq_cache** out) {
   if (st == KVQ_OK) st = dev_alloc(reinterpret_cast<void**>(&c->v_codes), c->v_codes_layer * L, "V codes");
   if (st == KVQ_OK) st = dev_alloc(reinterpret_cast<void**>(&c->k_scales), c->k_scales_layer * L, "K scales");
   if (st == KVQ_OK) st = dev_alloc(reinterpret_cast<void**>(&c->v_scales), c->v_scales_layer * L, "V scales");
+  if (st == KVQ_OK && c->recent_layer > 0) {
+    st = dev_alloc(reinterpret_cast<void**>(&c->k_recent), c->recent_layer * L, "recent K");
+    if (st == KVQ_OK) st = dev_alloc(reinterpret_cast<void**>(&c->v_recent), c->recent_layer * L, "recent V");
+  }
   if (st == KVQ_OK) st = dev_alloc(reinterpret_cast<void**>(&c->plans), sizeof(kvq::Plan) * L * H, "plans");
   if (st == KVQ_OK) st = dev_alloc(reinterpret_cast<void**>(&c->tables), sizeof(kvq::Tables), "tables");
   if (st == KVQ_OK)
@@ -175,6 +181,8 @@ kvq_status kvq_cache_create(const kvq_config* cfg, kvq_cache** out) {
         hipMemset(c->v_codes, 0, c->v_codes_layer * L),
         hipMemset(c->k_scales, 0, c->k_scales_layer * L),
         hipMemset(c->v_scales, 0, c->v_scales_layer * L),
+        c->k_recent ? hipMemset(c->k_recent, 0, c->recent_layer * L) : hipSuccess,
+        c->v_recent ? hipMemset(c->v_recent, 0, c->recent_layer * L) : hipSuccess,
         hipMemset(c->plans, 0, sizeof(kvq::Plan) * L * H),
         hipMemcpy(c->tables, &c->host_tables, sizeof(kvq::Tables), hipMemcpyHostToDevice),
         hipDeviceSynchronize()};
@@ -272,7 +280,30 @@ kvq_status kvq_quantize_append(kvq_cache* c, int32_t layer, const void* k, const
   }
   if (!c->plan_ready[layer]) return KVQ_ESTATE;
   if (c->len[layer] + n_new > c->cfg.max_tokens) return KVQ_ECAPACITY;
-  hipError_t e = kvq::launch_quantize(c, layer, k, v, dtype, n_new, static_cast<hipStream_t>(stream));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t len = c->len[layer], R = c->cfg.recent_window;
+  hipError_t e = hipSuccess;
+  if (R == 0) {
+    e = kvq::launch_quantize(c, layer, k, v, dtype, n_new, n_new, len, s);
+  } else {
+    // positions [p_old, p_new) leave the window for the packed storage: first those already
+    // buffered (from their fp16 copies, slot p mod R, in at most two contiguous runs), then
+    // new ones that arrive already outside the window; the remaining new positions are
+    // copied into the ring (after the evictions: they reuse the evicted slots)
+    const int64_t p_old = len > R ? len - R : 0, p_new = len + n_new > R ? len + n_new - R : 0;
+    const int64_t e_end = p_new < len ? p_new : len;
+    for (int64_t p = p_old; p < e_end && e == hipSuccess;) {
+      const int64_t slot = p % R, run = e_end - p < R - slot ? e_end - p : R - slot;
+      const int64_t off = slot * c->cfg.n_kv_heads * kHeadDim;
+      e = kvq::launch_quantize(c, layer, kvq::layer_k_recent(c, layer) + off, kvq::layer_v_recent(c, layer) + off,
+                               KVQ_F16, run, R, p, s);
+      p += run;
+    }
+    if (e == hipSuccess && p_new > len) e = kvq::launch_quantize(c, layer, k, v, dtype, p_new - len, n_new, len, s);
+    const int64_t w0 = p_new > len ? p_new : len;
+    if (e == hipSuccess && w0 < len + n_new)
+      e = kvq::launch_recent_write(c, layer, k, v, dtype, n_new, w0 - len, w0, len + n_new - w0, s);
+  }
   if (e != hipSuccess) return hip_fail(e, "quantize launch");
   c->len[layer] += n_new;
   return KVQ_OK;
@@ -289,10 +320,13 @@ kvq_status kvq_decode_attn_splits(kvq_cache* c, int32_t layer, const void* q, in
   }
   if (!(softmax_scale == softmax_scale)) return KVQ_EINVAL;  // NaN
   if (!c->plan_ready[layer] || c->len[layer] == 0) return KVQ_ESTATE;
-  int S = n_splits > 0 ? n_splits : kvq::auto_splits_mfma(c, c->len[layer]);
-  if (S > c->max_splits) return KVQ_EINVAL;
+  // S splits of the packed positions, plus one workgroup for the recent window if any
+  const int64_t plen = kvq::packed_len(c, layer);
+  int S = plen == 0 ? 0 : n_splits > 0 ? n_splits : kvq::auto_splits_mfma(c, plen);
+  const int S_all = S + (c->len[layer] > plen ? 1 : 0);
+  if (S_all > c->max_splits) return KVQ_EINVAL;
   const int64_t units = static_cast<int64_t>(c->cfg.batch) * c->cfg.n_kv_heads;
-  if (S > 1 && kvq::decode_split_mergers(S, units, c->n_cu) == 0) {
+  if (S_all > 1 && kvq::decode_split_mergers(S_all, units, c->n_cu) == 0) {
     g_last_error = "decode: more split units than compute units can merge; use one split";
     return KVQ_EINVAL;
   }
@@ -343,6 +377,9 @@ kvq_status kvq_layer_info_get(const kvq_cache* c, int32_t layer, kvq_layer_info*
   info->k_scales_bytes = c->k_scales_layer;
   info->v_scales_bytes = c->v_scales_layer;
   info->plan_ready = c->plan_ready[layer];
+  info->recent_window = c->cfg.recent_window;
+  info->packed_len = kvq::packed_len(c, layer);
+  info->recent_bytes = c->recent_layer;
   return KVQ_OK;
 }
 
@@ -357,6 +394,8 @@ kvq_status kvq_read_cache(const kvq_cache* c, int32_t layer, int32_t part, int64
     case KVQ_PART_V_CODES: base = reinterpret_cast<const char*>(kvq::layer_v_codes(m, layer)); size = c->v_codes_layer; break;
     case KVQ_PART_K_SCALES: base = reinterpret_cast<const char*>(kvq::layer_k_scales(m, layer)); size = c->k_scales_layer; break;
     case KVQ_PART_V_SCALES: base = reinterpret_cast<const char*>(kvq::layer_v_scales(m, layer)); size = c->v_scales_layer; break;
+    case KVQ_PART_K_RECENT: base = reinterpret_cast<const char*>(kvq::layer_k_recent(m, layer)); size = c->recent_layer; break;
+    case KVQ_PART_V_RECENT: base = reinterpret_cast<const char*>(kvq::layer_v_recent(m, layer)); size = c->recent_layer; break;
     default: return KVQ_EINVAL;
   }
   if (offset + nbytes > size) return KVQ_EINVAL;

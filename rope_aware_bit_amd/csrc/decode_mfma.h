@@ -417,7 +417,8 @@ __device__ __attribute__((always_inline)) inline KWin k_windows(const KPar& k, c
 // share of the wave merge (and, during set-up, wave 0's region holds the scaled query).
 template <int G, int VB, bool NF, int W>
 __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
-    const void* __restrict__ qv, int q_f32, float sigma, int64_t len, int n_kv, int64_t cap,
+    const void* __restrict__ qv, int q_f32, float sigma, int64_t len, int n_packed_splits,
+    const __half* __restrict__ rk, const __half* __restrict__ rv, int R, int64_t n_recent, int n_kv, int64_t cap,
     int tiles_per_split, const Plan* __restrict__ plans, const Tables* __restrict__ tabg,
     const uint32_t* __restrict__ kc, const uint32_t* __restrict__ vc, const uint16_t* __restrict__ ks,
     const uint16_t* __restrict__ vs, int k_words, int n_nf, int n_splits, int n_mergers, int region_words,
@@ -460,9 +461,12 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   }
   float (*qs_s)[kHeadDim] = reinterpret_cast<float (*)[kHeadDim]>(dyn_s);   // set-up only
 
+  // `len` packed positions in 128-token tiles; workgroup n_packed_splits (if any) reads the
+  // n_recent positions len .. len + n_recent - 1 of the recent window instead
+  const bool recent_wg = s == n_packed_splits;
   const int64_t n_tiles = (len + kVTile - 1) / kVTile;
-  const int64_t t_begin = static_cast<int64_t>(s) * tiles_per_split;
-  const int64_t t_end = t_begin + tiles_per_split < n_tiles ? t_begin + tiles_per_split : n_tiles;
+  const int64_t t_begin = recent_wg ? n_tiles : static_cast<int64_t>(s) * tiles_per_split;
+  const int64_t t_end = recent_wg ? n_tiles : (t_begin + tiles_per_split < n_tiles ? t_begin + tiles_per_split : n_tiles);
   const Plan* P = plans + h;
 
   // ---- set-up loads first (small and shared by every workgroup), then the first tile's.
@@ -554,7 +558,7 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   // the first tile's K rows and scales are loaded unconditionally (a wave without a tile of
   // its own reads the split's last tile and discards it); its V tile is copied once the
   // set-up data has been used, so waiting for the set-up loads never waits for it
-  const int64_t t0 = t_begin + wave < t_end ? t_begin + wave : t_end - 1;
+  const int64_t t0 = t_begin + wave < t_end ? t_begin + wave : (t_end > 0 ? t_end - 1 : 0);
   load_k(t0);
   load_scales(t0);
 
@@ -745,7 +749,7 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     // -- online softmax: lane (n, g) holds heads 2g and 2g + 1 of tokens 16 tg + n --
     float L0[8], L1[8];
     float mt0 = -INFINITY, mt1 = -INFINITY;
-    const int rem = len - tok0 < kVTile ? static_cast<int>(len - tok0) : kVTile;   // valid tokens
+    const int rem = len - tok0 < kVTile ? static_cast<int>(len - tok0) : kVTile;   // valid packed tokens
 #pragma unroll
     for (int tg = 0; tg < 8; ++tg) {
       const float bias = 16 * tg + n < rem ? 0.0f : -INFINITY;
@@ -836,6 +840,104 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   if (t_begin + wave < t_end) {
     tile_body(t_begin + wave, true);
     for (int64_t tile = t_begin + wave + W; tile < t_end; tile += W) tile_body(tile, false);
+  }
+  if (recent_wg) {
+    // ---- recent window (fp16 K and V, no scales): wave w takes 64-position chunks w, w + W,
+    //      ...  Lane t computes the G logits of position t of the chunk from this wave's copy
+    //      of q * sigma' in LDS; the online softmax runs per head on wave reductions; lane
+    //      (n, g) with n < G then accumulates head n's outputs at the dims the value product
+    //      would hold (16 dt + 4 g + r), so the wave merge below is shared.  The lo columns
+    //      stay zero. ----
+    float* qn = reinterpret_cast<float*>(kr);       // [G][128]
+    float* pwf = qn + G * kHeadDim;                 // [G][64]
+    for (int k = lane; k < G * kHeadDim; k += 64) {
+      const int64_t qi = (static_cast<int64_t>(b) * n_q + h * G) * kHeadDim + k;
+      const float qf = q_f32 ? reinterpret_cast<const float*>(qv)[qi]
+                             : __half2float(reinterpret_cast<const __half*>(qv)[qi]);
+      qn[k] = qf * sigma;
+    }
+    wave_sync();
+    float mr[G], lr[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      mr[hh] = -INFINITY;
+      lr[hh] = 0.0f;
+    }
+    const int64_t n_chunks = (n_recent + 63) / 64;
+    for (int64_t ci = wave; ci < n_chunks; ci += W) {
+      const int64_t c0 = len + ci * 64;                       // first position of the chunk
+      const int nvalid = n_recent - ci * 64 < 64 ? static_cast<int>(n_recent - ci * 64) : 64;
+      const bool valid = lane < nvalid;
+      const int64_t slot = (c0 + (valid ? lane : 0)) % R;
+      const __half* krow = rk + ((static_cast<int64_t>(b) * R + slot) * n_kv + h) * kHeadDim;
+      float lg[G];
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) lg[hh] = 0.0f;
+#pragma unroll 2
+      for (int c8 = 0; c8 < kHeadDim / 8; ++c8) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(krow + 8 * c8);
+        __half xh[8];
+        __builtin_memcpy(xh, &raw, 16);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = __half2float(xh[e]);
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh) lg[hh] = fmaf(x, qn[hh * kHeadDim + 8 * c8 + e], lg[hh]);
+        }
+      }
+      float al[G];
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        const float x = valid ? lg[hh] : -INFINITY;
+        const float mn = fmaxf(mr[hh], wave_max(x));
+        al[hh] = __builtin_amdgcn_exp2f(mr[hh] - mn);   // 0 on the first chunk
+        const float pp = valid ? __builtin_amdgcn_exp2f(x - mn) : 0.0f;
+        lr[hh] = lr[hh] * al[hh] + wave_sum(pp);
+        mr[hh] = mn;
+        pwf[hh * 64 + lane] = pp;
+      }
+      wave_sync();
+      if (n < G) {
+        float a_n = al[0];
+#pragma unroll
+        for (int hh = 1; hh < G; ++hh) a_n = n == hh ? al[hh] : a_n;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) oacc[dt] *= a_n;
+        for (int t = 0; t < nvalid; ++t) {
+          const float pt = pwf[n * 64 + t];
+          const __half* vrow = rv + ((static_cast<int64_t>(b) * R + (c0 + t) % R) * n_kv + h) * kHeadDim + 4 * g;
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) {
+            const uint2 raw = *reinterpret_cast<const uint2*>(vrow + 16 * dt);
+            __half vh[4];
+            __builtin_memcpy(vh, &raw, 8);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) oacc[dt][r] = fmaf(pt, __half2float(vh[r]), oacc[dt][r]);
+          }
+        }
+      }
+      wave_sync();
+    }
+    // row g's lanes carry heads 2g, 2g + 1: the maxima in every lane, the sums in lane n = 0
+    // (summed over the row below)
+    float m_a = mr[0], m_b = -INFINITY, l_a = lr[0], l_b = 0.0f;
+    if constexpr (G > 1) {
+      m_b = mr[1];
+      l_b = lr[1];
+#pragma unroll
+      for (int hh = 2; hh < G; hh += 2) {
+        if (2 * g == hh) {
+          m_a = mr[hh];
+          m_b = mr[hh + 1];
+          l_a = lr[hh];
+          l_b = lr[hh + 1];
+        }
+      }
+    }
+    m0 = m_a;
+    m1 = m_b;
+    l0 = n == 0 ? l_a : 0.0f;
+    l1 = n == 0 ? l_b : 0.0f;
   }
 
   // tag base of this call's split partials (read before this workgroup publishes anything)
@@ -934,28 +1036,34 @@ template <int G, int VB, int W>
 hipError_t launch_gvw(kvq_cache* c, int layer, const void* q, int q_f32, float sigma, float* out,
                       int S, const DecodeShape& sh, hipStream_t stream) {
   const kvq_config& cfg = c->cfg;
-  const int64_t len = c->len[layer];
-  const int64_t n_tiles = (len + kVTile - 1) / kVTile;
-  const int tps = static_cast<int>((n_tiles + S - 1) / S);
-  dim3 grid(S, cfg.n_kv_heads, cfg.batch);
+  // S packed splits over the packed positions, plus one workgroup for the recent window
+  const int64_t plen = packed_len(c, layer);
+  const int64_t n_recent = c->len[layer] - plen;
+  const int64_t n_tiles = (plen + kVTile - 1) / kVTile;
+  const int tps = S > 0 ? static_cast<int>((n_tiles + S - 1) / S) : 0;
+  const int S_all = S + (n_recent > 0 ? 1 : 0);
+  const __half* rk = n_recent > 0 ? layer_k_recent(c, layer) : nullptr;
+  const __half* rv = n_recent > 0 ? layer_v_recent(c, layer) : nullptr;
+  const int R = cfg.recent_window;
+  dim3 grid(S_all, cfg.n_kv_heads, cfg.batch);
   const size_t dyn = static_cast<size_t>(W) * sh.region_words * sizeof(uint32_t);
   const Plan* plans = c->plans + static_cast<int64_t>(layer) * cfg.n_kv_heads;
   const bool nf = cfg.codec == KVQ_CODEC_NF16_B256;
-  const int mergers = decode_split_mergers(S, static_cast<int64_t>(cfg.batch) * cfg.n_kv_heads, c->n_cu);
+  const int mergers = decode_split_mergers(S_all, static_cast<int64_t>(cfg.batch) * cfg.n_kv_heads, c->n_cu);
   if constexpr (VB == 4) {
     if (nf) {
       hipLaunchKernelGGL((decode_mfma<G, 4, true, W>), grid, dim3(64 * W), dyn, stream, q, q_f32, sigma,
-                         len, cfg.n_kv_heads, c->cap, tps, plans, c->tables, layer_k_codes(c, layer),
+                         plen, S, rk, rv, R, n_recent, cfg.n_kv_heads, c->cap, tps, plans, c->tables, layer_k_codes(c, layer),
                          layer_v_codes(c, layer), layer_k_scales(c, layer), layer_v_scales(c, layer),
-                         c->k_words, c->n_nf_blocks, S, mergers, sh.region_words, sh.v_early, sh.v_off,
+                         c->k_words, c->n_nf_blocks, S_all, mergers, sh.region_words, sh.v_early, sh.v_off,
                          c->part_o, c->part_l, c->part_mt, c->split_epochs, out);
       return hipGetLastError();
     }
   }
   hipLaunchKernelGGL((decode_mfma<G, VB, false, W>), grid, dim3(64 * W), dyn, stream, q, q_f32, sigma,
-                     len, cfg.n_kv_heads, c->cap, tps, plans, c->tables, layer_k_codes(c, layer),
+                     plen, S, rk, rv, R, n_recent, cfg.n_kv_heads, c->cap, tps, plans, c->tables, layer_k_codes(c, layer),
                      layer_v_codes(c, layer), layer_k_scales(c, layer), layer_v_scales(c, layer),
-                     c->k_words, c->n_nf_blocks, S, mergers, sh.region_words, sh.v_early, sh.v_off,
+                     c->k_words, c->n_nf_blocks, S_all, mergers, sh.region_words, sh.v_early, sh.v_off,
                      c->part_o, c->part_l, c->part_mt, c->split_epochs, out);
   return hipGetLastError();
 }

@@ -10,7 +10,8 @@ hipError_t launch_decode_mfma_g8(kvq_cache*, int, const void*, int, float, float
 
 int auto_splits_mfma(const kvq_cache* c, int64_t len) {
   // one workgroup per compute unit over (splits x KV heads x sequences), and at least one
-  // 128-token tile per wave
+  // 128-token tile per wave; `len` packed positions (none: no packed split)
+  if (len <= 0) return 0;
   const int64_t n_tiles = (len + kVTile - 1) / kVTile;
   const int64_t units = static_cast<int64_t>(c->cfg.batch) * c->cfg.n_kv_heads;
   const int W = decode_waves(c);

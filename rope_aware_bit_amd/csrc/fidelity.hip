@@ -7,7 +7,8 @@
 // results: the softmax KL divergence of the attention distributions.  For query head h of
 // sequence b, over the cached positions t:
 //   a_t = sigma <q_h, k_t>,   a^_t = sigma <q_h, k^_t>,  k^ = the cache's keys dequantized
-//   (s_t g_i CB_{b_i}[code], or s_t NF[code] for the 256-value codec), all in fp64;
+//   (s_t g_i CB_{b_i}[code], or s_t NF[code] for the 256-value codec; the fp16 copies for
+//   positions in the recent window), all in fp64;
 //   mae = mean_t |a_t - a^_t|,  kl = KL(softmax(a) || softmax(a^)).
 //
 // Kernel 1 (fidelity_partials): one 256-lane workgroup per (split, KV head, sequence).  It
@@ -114,7 +115,7 @@ __global__ __launch_bounds__(256, 2) void fidelity_partials(
     const T* __restrict__ q, const T* __restrict__ keys, int64_t len, int n_kv, int64_t cap,
     double sigma, int64_t tok_per_split, const Plan* __restrict__ plans, const Tables* __restrict__ tab,
     const uint32_t* __restrict__ kc, const uint16_t* __restrict__ ks, int k_words, int n_nf, int nf,
-    double* __restrict__ part, int S) {
+    int64_t plen, const __half* __restrict__ rk, int R, double* __restrict__ part, int S) {
   constexpr int kVec = 16 / sizeof(T);
   constexpr int kRow = kHeadDim + kVec;            // padded key row (elements)
   const int tid = threadIdx.x;
@@ -131,6 +132,7 @@ __global__ __launch_bounds__(256, 2) void fidelity_partials(
   __shared__ uint16_t foff_s[kHeadDim];
   __shared__ __attribute__((aligned(16))) T x_s[kFidTok][kRow];
   __shared__ uint32_t kr_s[kFidTok][4 * kMaxBits + 1];
+  __shared__ __attribute__((aligned(16))) __half xr_s[kFidTok][kHeadDim + 8];   // recent-window rows
   __shared__ double sc_s[kFidTok];
   __shared__ int nf_s;
 
@@ -162,11 +164,20 @@ __global__ __launch_bounds__(256, 2) void fidelity_partials(
       const int64_t src = ((static_cast<int64_t>(b) * len + r0 + r) * n_kv + h) * kHeadDim + c * kVec;
       *reinterpret_cast<uint4*>(&x_s[r][c * kVec]) = *reinterpret_cast<const uint4*>(keys + src);
     }
+    // stored rows: packed below plen, fp16 ring copies (slot p mod R) from plen on
     for (int k = tid; k < nr * k_words; k += 256) {
       const int r = k / k_words, c = k % k_words;
-      kr_s[r][c] = kc[(bh * cap + r0 + r) * k_words + c];
+      if (r0 + r < plen) kr_s[r][c] = kc[(bh * cap + r0 + r) * k_words + c];
     }
-    if (tid < nr) {
+    for (int k = tid; k < nr * (kHeadDim / 8); k += 256) {
+      const int r = k / (kHeadDim / 8), c = k % (kHeadDim / 8);
+      if (r0 + r >= plen) {
+        const int64_t slot = (r0 + r) % R;
+        *reinterpret_cast<uint4*>(&xr_s[r][8 * c]) =
+            *reinterpret_cast<const uint4*>(rk + ((static_cast<int64_t>(b) * R + slot) * n_kv + h) * kHeadDim + 8 * c);
+      }
+    }
+    if (tid < nr && r0 + tid < plen) {
       const uint16_t sb = nf ? ks[(static_cast<int64_t>(b) * cap + r0 + tid) * n_nf + h / 2] : ks[bh * cap + r0 + tid];
       sc_s[tid] = static_cast<double>(__half2float(__ushort_as_half(sb)));
     }
@@ -192,8 +203,23 @@ __global__ __launch_bounds__(256, 2) void fidelity_partials(
           for (int hh = 0; hh < G; ++hh) a[hh] += x * q_s[hh][c * kVec + e];
         }
       }
+      if (r0 + t >= plen) {
+        // recent window: the stored key is the fp16 copy (dims of this quarter)
+#pragma unroll 1
+        for (int c = 4 * quarter; c < 4 * quarter + 4; ++c) {
+          const uint4 raw = *reinterpret_cast<const uint4*>(&xr_s[t][8 * c]);
+          __half xv[8];
+          __builtin_memcpy(xv, &raw, 16);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const double x = static_cast<double>(__half2float(xv[e]));
+#pragma unroll
+            for (int hh = 0; hh < G; ++hh) ah[hh] += x * q_s[hh][8 * c + e];
+          }
+        }
+      }
       const double s16 = sc_s[t];
-      const int f_end = n_fields < 32 * quarter + 32 ? n_fields : 32 * quarter + 32;
+      const int f_end = r0 + t >= plen ? 0 : n_fields < 32 * quarter + 32 ? n_fields : 32 * quarter + 32;
 #pragma unroll 2
       for (int f = 32 * quarter; f < f_end; ++f) {
         const int off = foff_s[f], w = fw_s[f], dim = fdim_s[f];
@@ -295,7 +321,7 @@ __global__ __launch_bounds__(64) void fidelity_merge(const double* __restrict__ 
 hipError_t launch_fidelity(kvq_cache* c, int layer, const void* q, const void* keys, int dtype,
                            float scale, double* mae, double* kl, hipStream_t stream) {
   const kvq_config& cfg = c->cfg;
-  const int64_t len = c->len[layer];
+  const int64_t len = c->len[layer], plen = packed_len(c, layer);
   const int H = cfg.n_kv_heads, B = cfg.batch, G = c->group;
   const int64_t units = static_cast<int64_t>(B) * H;
   // about four workgroups per compute unit, at least 256 positions each
@@ -314,7 +340,8 @@ hipError_t launch_fidelity(kvq_cache* c, int layer, const void* q, const void* k
   hipLaunchKernelGGL((fidelity_partials<T, GG>), grid, dim3(256), 0, stream, static_cast<const T*>(q), \
                      static_cast<const T*>(keys), len, H, c->cap, sigma, per, plans, c->tables,       \
                      layer_k_codes(c, layer), layer_k_scales(c, layer), c->k_words, c->n_nf_blocks,   \
-                     nf ? 1 : 0, c->fid_part, static_cast<int>(S))
+                     nf ? 1 : 0, plen, plen < len ? layer_k_recent(c, layer) : nullptr,       \
+                     c->cfg.recent_window > 0 ? c->cfg.recent_window : 1, c->fid_part, static_cast<int>(S))
 #define KVQ_FID_G(T)                  \
   switch (G) {                        \
     case 1: KVQ_FID(T, 1); break;     \

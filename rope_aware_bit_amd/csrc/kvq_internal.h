@@ -1,6 +1,7 @@
 // Internal definitions shared by the libkvq host code and its gfx950 kernels.
 #pragma once
 
+#include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -15,6 +16,7 @@ constexpr int kVTile = 128;          // tokens per dim-major V tile
 constexpr int kEnergyChunk = 256;    // tokens per sequential energy partial sum
 constexpr int kMaxGroup = 8;         // query heads per KV head supported
 constexpr int kNfBlock = 256;        // values per absmax block of the NF16 codec
+constexpr int kMaxRecent = 4096;     // largest recent window (tokens)
 
 // Byte layout of the decode lookup tables that every decode workgroup copies into LDS.
 // Pair tables (widths 1..4) hold fp16x2 (CB[c0], CB[c1]) at index c0 | c1 << w; single
@@ -74,6 +76,8 @@ struct kvq_cache {
   uint32_t* v_codes;           // [L][B][H][cap/128][128][v_words]
   uint16_t* k_scales;          // BGTQ/UNI [L][B][H][cap]; NF16 [L][B][cap][nnf]
   uint16_t* v_scales;
+  __half* k_recent;            // recent-window rings [L][B][R][H][128] fp16 (R > 0)
+  __half* v_recent;
   kvq::Plan* plans;            // [L][H]
   kvq::Tables* tables;         // device copy
   kvq::Tables host_tables;
@@ -87,7 +91,7 @@ struct kvq_cache {
   int fid_max_splits;
   int64_t energy_scratch_chunks;
   // byte sizes per layer
-  int64_t k_codes_layer, v_codes_layer, k_scales_layer, v_scales_layer;
+  int64_t k_codes_layer, v_codes_layer, k_scales_layer, v_scales_layer, recent_layer;
 };
 
 namespace kvq {
@@ -96,8 +100,13 @@ namespace kvq {
 // return the launch status; arguments are validated by the caller.
 hipError_t launch_alloc(kvq_cache* c, int layer, const void* keys, int dtype, int64_t n_tok,
                         const double* block_weight, hipStream_t stream);
+// Quantizes positions L0 .. L0 + n_new - 1 of every sequence from rows 0 .. n_new - 1 of
+// [batch][in_stride][n_kv][128] K and V inputs into the packed storage.
 hipError_t launch_quantize(kvq_cache* c, int layer, const void* k, const void* v, int dtype,
-                           int64_t n_new, hipStream_t stream);
+                           int64_t n_new, int64_t in_stride, int64_t L0, hipStream_t stream);
+hipError_t launch_recent_write(kvq_cache* c, int layer, const void* k, const void* v, int dtype,
+                               int64_t in_stride, int64_t row0, int64_t pos0, int64_t count,
+                               hipStream_t stream);
 hipError_t launch_decode_mfma(kvq_cache* c, int layer, const void* q, int dtype, float scale,
                               float* out, int n_splits, hipStream_t stream);
 hipError_t launch_fidelity(kvq_cache* c, int layer, const void* q, const void* keys, int dtype,
@@ -120,6 +129,7 @@ inline DecodeShape decode_shape(const kvq_cache* c) {
   if (kpart < G * kPS) kpart = G * kPS;
   if (kpart < 128 * kOS) kpart = 128 * kOS;
   if (kpart < G * 128) kpart = G * 128;
+  if (kpart < G * 192) kpart = G * 192;   // recent window: q * sigma' and one chunk's weights
   kpart = (kpart + 3) & ~3;
   const int vwords = 512 * vb;
   {
@@ -153,6 +163,17 @@ inline uint32_t* layer_v_codes(kvq_cache* c, int layer) {
 }
 inline uint16_t* layer_k_scales(kvq_cache* c, int layer) {
   return reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(c->k_scales) + c->k_scales_layer * layer);
+}
+inline __half* layer_k_recent(kvq_cache* c, int layer) {
+  return reinterpret_cast<__half*>(reinterpret_cast<char*>(c->k_recent) + c->recent_layer * layer);
+}
+inline __half* layer_v_recent(kvq_cache* c, int layer) {
+  return reinterpret_cast<__half*>(reinterpret_cast<char*>(c->v_recent) + c->recent_layer * layer);
+}
+// Positions of `layer` held by the packed storage (the rest are in the recent window).
+inline int64_t packed_len(const kvq_cache* c, int layer) {
+  const int64_t len = c->len[layer], R = c->cfg.recent_window;
+  return len > R ? len - R : 0;
 }
 inline uint16_t* layer_v_scales(kvq_cache* c, int layer) {
   return reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(c->v_scales) + c->v_scales_layer * layer);

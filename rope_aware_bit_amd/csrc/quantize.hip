@@ -47,7 +47,7 @@ __device__ inline float inv_scale(__half s16) {
 
 template <typename T, bool NF>
 __global__ __launch_bounds__(kThreads) void quantize_append(
-    const T* __restrict__ kin, const T* __restrict__ vin, int64_t n_new, int64_t L0, int n_kv,
+    const T* __restrict__ kin, const T* __restrict__ vin, int64_t n_new, int64_t in_stride, int64_t L0, int n_kv,
     int64_t cap, const Plan* __restrict__ plans, const Tables* __restrict__ tab,
     uint32_t* __restrict__ kc, uint32_t* __restrict__ vc, uint16_t* __restrict__ ks,
     uint16_t* __restrict__ vs, int k_words, int v_bits, int n_nf) {
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kThreads) void quantize_append(
     const int hh = (k / (kHeadDim / kVec * kGroupTok)) % kHeads;
     const int tsr = k / (kHeadDim / kVec * kGroupTok * kHeads);   // 0: K, 1: V
     if (r >= lo && r < hi) {
-      const int64_t src = ((static_cast<int64_t>(b) * n_new + (g0 + r - L0)) * n_kv + h0 + hh) * kHeadDim + q * kVec;
+      const int64_t src = ((static_cast<int64_t>(b) * in_stride + (g0 + r - L0)) * n_kv + h0 + hh) * kHeadDim + q * kVec;
       const T* in = tsr ? vin : kin;
       const uint4 v4 = *reinterpret_cast<const uint4*>(in + src);
       uint32_t* d = &x_s[tsr][hh][r][q * 4];
@@ -219,9 +219,8 @@ __global__ __launch_bounds__(kThreads) void quantize_append(
 }  // namespace
 
 hipError_t launch_quantize(kvq_cache* c, int layer, const void* k, const void* v, int dtype,
-                           int64_t n_new, hipStream_t stream) {
+                           int64_t n_new, int64_t in_stride, int64_t L0, hipStream_t stream) {
   const kvq_config& cfg = c->cfg;
-  const int64_t L0 = c->len[layer];
   const int64_t first = L0 / kGroupTok, last = (L0 + n_new - 1) / kGroupTok;
   dim3 grid(static_cast<unsigned>(last - first + 1), static_cast<unsigned>(cfg.n_kv_heads),
             static_cast<unsigned>(cfg.batch));
@@ -229,7 +228,7 @@ hipError_t launch_quantize(kvq_cache* c, int layer, const void* k, const void* v
   const Plan* plans = c->plans + static_cast<int64_t>(layer) * cfg.n_kv_heads;
 #define KVQ_LAUNCH_Q(T, NF)                                                                      \
   hipLaunchKernelGGL((quantize_append<T, NF>), grid, dim3(kThreads), 0, stream,                 \
-                     static_cast<const T*>(k), static_cast<const T*>(v), n_new, L0,              \
+                     static_cast<const T*>(k), static_cast<const T*>(v), n_new, in_stride, L0,   \
                      cfg.n_kv_heads, c->cap, plans, c->tables, layer_k_codes(c, layer),          \
                      layer_v_codes(c, layer), layer_k_scales(c, layer), layer_v_scales(c, layer), \
                      c->k_words, cfg.v_bits, c->n_nf_blocks)
@@ -239,6 +238,45 @@ hipError_t launch_quantize(kvq_cache* c, int layer, const void* k, const void* v
     if (nf) KVQ_LAUNCH_Q(float, true); else KVQ_LAUNCH_Q(float, false);
   }
 #undef KVQ_LAUNCH_Q
+  return hipGetLastError();
+}
+
+namespace {
+
+// Copies `count` new positions (input rows row0 .. row0 + count - 1 of a [batch][in_stride]
+// [n_kv][128] tensor, positions pos0 ..) into a recent-window ring [batch][R][n_kv][128] fp16
+// at slot position mod R, rounding fp32 inputs to fp16 (nearest even).  One workgroup per
+// (position, sequence); thread i copies element i of every head.
+template <typename T>
+__global__ __launch_bounds__(256) void recent_write(const T* __restrict__ kin, const T* __restrict__ vin,
+                                                   int64_t in_stride, int64_t row0, int64_t pos0, int n_kv,
+                                                   int R, __half* __restrict__ kr, __half* __restrict__ vr) {
+  const int64_t i = blockIdx.x;
+  const int b = blockIdx.y;
+  const int64_t slot = (pos0 + i) % R;
+  const int64_t src = (static_cast<int64_t>(b) * in_stride + row0 + i) * n_kv * kHeadDim;
+  const int64_t dst = (static_cast<int64_t>(b) * R + slot) * n_kv * kHeadDim;
+  for (int e = threadIdx.x; e < n_kv * kHeadDim; e += 256) {
+    kr[dst + e] = __float2half_rn(static_cast<float>(kin[src + e]));
+    vr[dst + e] = __float2half_rn(static_cast<float>(vin[src + e]));
+  }
+}
+
+}  // namespace
+
+hipError_t launch_recent_write(kvq_cache* c, int layer, const void* k, const void* v, int dtype,
+                               int64_t in_stride, int64_t row0, int64_t pos0, int64_t count,
+                               hipStream_t stream) {
+  const kvq_config& cfg = c->cfg;
+  dim3 grid(static_cast<unsigned>(count), static_cast<unsigned>(cfg.batch));
+  if (dtype == KVQ_F16)
+    hipLaunchKernelGGL(recent_write<__half>, grid, dim3(256), 0, stream, static_cast<const __half*>(k),
+                       static_cast<const __half*>(v), in_stride, row0, pos0, cfg.n_kv_heads,
+                       cfg.recent_window, layer_k_recent(c, layer), layer_v_recent(c, layer));
+  else
+    hipLaunchKernelGGL(recent_write<float>, grid, dim3(256), 0, stream, static_cast<const float*>(k),
+                       static_cast<const float*>(v), in_stride, row0, pos0, cfg.n_kv_heads,
+                       cfg.recent_window, layer_k_recent(c, layer), layer_v_recent(c, layer));
   return hipGetLastError();
 }
 

@@ -20,7 +20,7 @@ KVQ_OK, KVQ_EINVAL, KVQ_ENOMEM, KVQ_ECAPACITY, KVQ_ESTATE, KVQ_EHIP = range(6)
 KVQ_F16, KVQ_F32 = 0, 1
 CODEC_BGTQ, CODEC_UNIFORM, CODEC_NF16_B256 = 0, 1, 2
 ROPE_HALF, ROPE_INTERLEAVED = 0, 1
-PART_K_CODES, PART_V_CODES, PART_K_SCALES, PART_V_SCALES = range(4)
+PART_K_CODES, PART_V_CODES, PART_K_SCALES, PART_V_SCALES, PART_K_RECENT, PART_V_RECENT = range(6)
 
 EXPORTED = (
     "kvq_cache_create", "kvq_cache_destroy", "kvq_alloc_bits", "kvq_get_plan",
@@ -42,6 +42,7 @@ class kvq_config(ctypes.Structure):
         ("head_dim", ctypes.c_int32), ("batch", ctypes.c_int32), ("max_tokens", ctypes.c_int64),
         ("k_bits", ctypes.c_int32), ("v_bits", ctypes.c_int32), ("b_min", ctypes.c_int32),
         ("b_max", ctypes.c_int32), ("codec", ctypes.c_int32), ("pairing", ctypes.c_int32),
+        ("recent_window", ctypes.c_int32),
     ]
 
 
@@ -51,6 +52,7 @@ class kvq_layer_info(ctypes.Structure):
         ("v_dim_words", ctypes.c_int32), ("k_codes_bytes", ctypes.c_int64),
         ("v_codes_bytes", ctypes.c_int64), ("k_scales_bytes", ctypes.c_int64),
         ("v_scales_bytes", ctypes.c_int64), ("plan_ready", ctypes.c_int32),
+        ("recent_window", ctypes.c_int32), ("packed_len", ctypes.c_int64), ("recent_bytes", ctypes.c_int64),
     ]
 
 
@@ -159,11 +161,12 @@ class Config:
     b_max: int = 8
     codec: int = CODEC_BGTQ
     pairing: int = ROPE_HALF
+    recent_window: int = 0
 
     def to_c(self) -> kvq_config:
         return kvq_config(self.n_layers, self.n_kv_heads, self.n_q_heads, self.head_dim, self.batch,
                           self.max_tokens, self.k_bits, self.v_bits, self.b_min, self.b_max,
-                          self.codec, self.pairing)
+                          self.codec, self.pairing, self.recent_window)
 
 
 def create_status(cfg: Config) -> int:
@@ -267,7 +270,8 @@ class Cache:
     def read(self, layer: int, part: int, dtype, offset: int = 0, nbytes: Optional[int] = None) -> np.ndarray:
         info = self.layer_info(layer)
         size = {PART_K_CODES: info.k_codes_bytes, PART_V_CODES: info.v_codes_bytes,
-                PART_K_SCALES: info.k_scales_bytes, PART_V_SCALES: info.v_scales_bytes}[part]
+                PART_K_SCALES: info.k_scales_bytes, PART_V_SCALES: info.v_scales_bytes,
+                PART_K_RECENT: info.recent_bytes, PART_V_RECENT: info.recent_bytes}[part]
         n = size - offset if nbytes is None else nbytes
         buf = np.empty(n, dtype=np.uint8)
         _check(lib.kvq_read_cache(self._h, layer, part, offset, n, buf.ctypes.data), "kvq_read_cache")

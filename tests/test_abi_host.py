@@ -67,6 +67,8 @@ BAD = [
     dict(pairing=2),
     dict(codec=2, k_bits=3),            # NF16 needs K4V4
     dict(codec=2, n_kv_heads=1, n_q_heads=1),  # NF16 needs n_kv*128 % 256 == 0
+    dict(recent_window=-1),
+    dict(recent_window=4097),
 ]
 
 

@@ -12,6 +12,7 @@ import pytest
 from oracle import attention as at
 from oracle import fidelity as fd
 from oracle import layout as lay
+from oracle import window as wn
 from synth import WORKLOADS, gen_layer, gen_query
 from tests.parity import CODEC, PAIRING, OracleLayer, assert_attention_close, errors
 
@@ -31,8 +32,12 @@ def _kvq():
 
 def run_case(wname, T, k_bits, v_bits, codec="bgtq", pairing="half", batch=None, layer=0,
              chunks=None, n_splits=0, noise="gauss", temper=False, check_codes=True, sample_rows=None,
-             b_min=0, b_max=8, fidelity=True):
-    """Quantize T tokens of one layer on the GPU and in the oracle; compare everything."""
+             b_min=0, b_max=8, fidelity=True, recent=0):
+    """Quantize T tokens of one layer on the GPU and in the oracle; compare everything.
+
+    recent > 0: the last `recent` positions stay in the fp16 window.  A position that was inside
+    the window at the end of its append went through fp16 (fp32 inputs are rounded), and the
+    packed storage holds positions 0 .. T - recent - 1."""
     torch = _torch()
     kvq = _kvq()
     w = WORKLOADS[wname]
@@ -55,7 +60,7 @@ def run_case(wname, T, k_bits, v_bits, codec="bgtq", pairing="half", batch=None,
 
     cfg = kvq.Config(n_layers=1, n_kv_heads=H, n_q_heads=Hq, batch=B, max_tokens=T, k_bits=k_bits,
                      v_bits=v_bits, b_min=b_min, b_max=b_max, codec=CODEC[codec],
-                     pairing=PAIRING[pairing])
+                     pairing=PAIRING[pairing], recent_window=recent)
     cache = kvq.Cache(cfg)
     dev = torch.device("cuda:0")
     cache.alloc_bits(0, torch.from_numpy(np.ascontiguousarray(calib)).to(dev) if codec == "bgtq" else None)
@@ -65,6 +70,10 @@ def run_case(wname, T, k_bits, v_bits, codec="bgtq", pairing="half", batch=None,
 
     bounds = [0, T] if chunks is None else [0, *np.cumsum(chunks).tolist()]
     assert bounds[-1] == T
+    P = wn.packed_len(T, recent)                          # packed positions
+    # the rows each position is stored from (fp16 copies where it went through the window)
+    Ke = np.stack([wn.stored_rows(K[b], bounds, recent) for b in range(B)])
+    Ve = np.stack([wn.stored_rows(V[b], bounds, recent) for b in range(B)])
     Kt = torch.from_numpy(K).to(dev)
     Vt = torch.from_numpy(V).to(dev)
     for a, z in zip(bounds[:-1], bounds[1:]):
@@ -76,13 +85,18 @@ def run_case(wname, T, k_bits, v_bits, codec="bgtq", pairing="half", batch=None,
     for b in range(B):
         kh_all, vh_all, qo = [], [], []
         for h in range(H):
-            r = ol.quantize_head(K[b, :, h], V[b, :, h], h,
-                                 K[b].reshape(T, H * 128) if codec == "nf16" else None,
-                                 V[b].reshape(T, H * 128) if codec == "nf16" else None)
+            kh = np.zeros((0, 128))
+            vh = np.zeros((0, 128))
+            r = None
+            if P > 0:
+                r = ol.quantize_head(Ke[b, :P, h], Ve[b, :P, h], h,
+                                     Ke[b, :P].reshape(P, H * 128) if codec == "nf16" else None,
+                                     Ve[b, :P].reshape(P, H * 128) if codec == "nf16" else None)
+                kh, vh = ol.dequant(r, h)
             qo.append(r)
-            kh, vh = ol.dequant(r, h)
-            kh_all.append(kh)
-            vh_all.append(vh)
+            # the recent window holds the fp16 values themselves
+            kh_all.append(np.concatenate([kh, Ke[b, P:, h].astype(np.float64)]))
+            vh_all.append(np.concatenate([vh, Ve[b, P:, h].astype(np.float64)]))
         refs.append((qo, np.stack(kh_all), np.stack(vh_all)))
     print(f"[{wname} T={T}] oracle quantized", flush=True)
     if temper:
@@ -104,20 +118,29 @@ def run_case(wname, T, k_bits, v_bits, codec="bgtq", pairing="half", batch=None,
         else:
             kscale = kscale.reshape(B, H, cap)
             vscale = vscale.reshape(B, H, cap)
-        nt = (T + 127) // 128
+        nt = (P + 127) // 128
         vb = 4 if codec == "nf16" else v_bits
+        assert info.packed_len == P
         for b in range(B):
             for h in range(H):
                 r = refs[b][0][h]
+                if P == 0:
+                    break
                 rows = slice(None) if sample_rows is None else sample_rows
-                assert np.array_equal(kw[b, h, :T][rows], r["k_words"][rows]), f"K words differ b={b} h={h}"
+                assert np.array_equal(kw[b, h, :P][rows], r["k_words"][rows]), f"K words differ b={b} h={h}"
                 assert np.array_equal(vw[b, h, :nt], lay.pack_v_tiles(r["v_codes"], vb)), f"V tiles differ b={b} h={h}"
                 if codec == "nf16":
-                    assert np.array_equal(kscale[b, :T], r["k_scale_blocks"].view(np.uint16))
-                    assert np.array_equal(vscale[b, :T], r["v_scale_blocks"].view(np.uint16))
+                    assert np.array_equal(kscale[b, :P], r["k_scale_blocks"].view(np.uint16))
+                    assert np.array_equal(vscale[b, :P], r["v_scale_blocks"].view(np.uint16))
                 else:
-                    assert np.array_equal(kscale[b, h, :T], r["k_s16"].view(np.uint16)), f"K scales b={b} h={h}"
-                    assert np.array_equal(vscale[b, h, :T], r["v_s16"].view(np.uint16)), f"V scales b={b} h={h}"
+                    assert np.array_equal(kscale[b, h, :P], r["k_s16"].view(np.uint16)), f"K scales b={b} h={h}"
+                    assert np.array_equal(vscale[b, h, :P], r["v_s16"].view(np.uint16)), f"V scales b={b} h={h}"
+        if recent > 0:
+            kr = cache.read(0, kvq.PART_K_RECENT, np.float16).reshape(B, recent, H, 128)
+            vr = cache.read(0, kvq.PART_V_RECENT, np.float16).reshape(B, recent, H, 128)
+            pos = np.arange(P, T)
+            assert np.array_equal(kr[:, pos % recent].view(np.uint16), Ke[:, P:].astype(np.float16).view(np.uint16))
+            assert np.array_equal(vr[:, pos % recent].view(np.uint16), Ve[:, P:].astype(np.float16).view(np.uint16))
 
     Qt = torch.from_numpy(Q).to(dev)
     out = cache.decode_attn(0, Qt, scale=sigma, n_splits=n_splits)
@@ -190,6 +213,33 @@ def test_nf16_codec_gauss_and_t5():
 
 def test_bgtq_batched_t5():
     run_case("llama8b_b64", 2048, 4, 4, batch=4, noise="t5", temper=True)
+
+
+def test_recent_window_ragged_appends():
+    """fp16 recent window of 256 positions: evictions from the ring (with wrap), positions
+    that arrive already outside the window, fp32 inputs rounded to fp16 in the window."""
+    run_case("tiny", 1000, 3, 3, chunks=[100, 200, 37, 1, 662], recent=256)
+
+
+def test_recent_window_holds_everything():
+    run_case("tiny", 300, 4, 4, chunks=[299, 1], recent=512)
+
+
+@pytest.mark.parametrize("n_splits", [0, 5])
+def test_recent_window_qwen_k3v2(n_splits):
+    """Qwen2.5-3B-shaped layer (8 query heads per KV head), asymmetric K3V2, 1024-position
+    window, prefill then decode-sized appends."""
+    run_case("qwen3b_128k", 20000, 3, 2, chunks=[2048, 17000, 951, 1], recent=1024, temper=True,
+             n_splits=n_splits)
+
+
+def test_recent_window_nf16():
+    run_case("llama8b_32k", 3000, 4, 4, codec="nf16", chunks=[1000, 1999, 1], recent=128)
+
+
+def test_asymmetric_k3v2_qwen_shape():
+    """The paper's K3V2 setting (abstract), no recent window, on the Qwen2.5-3B shape."""
+    run_case("qwen3b_128k", 20000, 3, 2, temper=True)
 
 
 def test_b_min_b_max_limits():
