@@ -209,6 +209,33 @@ def main():
     for o in outs:
         assert torch.isfinite(o).all()
 
+    # variants on layer 0's data (one layer each): the asymmetric K3V2 budget, and an fp16 recent
+    # window of 1024 positions; decode launches timed like the step
+    variants = {}
+    k0d = keys0[0]
+    v0d = torch.from_numpy(keep[1]).to(dev) if keep is not None else None
+    if v0d is not None:
+        for label, vk, vv, R in (("K3V2", 3, 2, 0), ("K3V3_recent1024", 3, 3, 1024)):
+            vc = kvq.Cache(kvq.Config(1, H, Hq, B, T, vk, vv, recent_window=R))
+            vc.alloc_bits(0, k0d[:chunk])
+            vc.quantize_append(0, k0d[None], v0d[None])
+            vo = torch.empty(B, Hq, 128, dtype=torch.float32, device=dev)
+            for _ in range(5):
+                vc.decode_attn(0, qs[0], out=vo)
+            torch.cuda.synchronize()
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            for _ in range(50):
+                vc.decode_attn(0, qs[0], out=vo)
+            a1.record(stream)
+            torch.cuda.synchronize()
+            us = a0.elapsed_time(a1) * 1e3 / 50
+            vbytes = B * H * ((T - R) * ((vk + vv) * 128 / 8 + 4) + R * 512) + B * Hq * 128 * 6 + H * PLAN_BYTES_PER_HEAD
+            variants[label] = {"k_bits": vk, "v_bits": vv, "recent_window": R, "us_per_launch": round(us, 2),
+                               "GB/s": round(vbytes / (us * 1e-6) / 1e9, 2)}
+            vc.close()
+        del v0d
+
     # key-fidelity diagnostics of layer 0 (logit MAE and softmax KL against the given keys)
     fid_reps = 5
     cache.key_fidelity(0, qs[0], keys0)
@@ -257,6 +284,7 @@ def main():
             "GB/s": round((B * H * chunk * (2 * 128 * 2 + (kb + vb) * 16 + 4)) /
                           (float(np.mean(app_ms)) * 1e-3) / 1e9, 2),
         },
+        "variants": variants,
         "fidelity": {
             "layer": 0,
             "us_per_layer": round(fid_us, 2),

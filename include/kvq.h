@@ -83,7 +83,7 @@ typedef struct {
   int32_t codec;       /* kvq_codec; NF16_B256 needs k_bits = v_bits = 4 and
                           n_kv_heads*128 divisible by 256 */
   int32_t pairing;     /* kvq_pairing */
-  int32_t recent_window; /* R in [0, 4096]: the most recent min(len, R) tokens of each
+  int32_t recent_window; /* R in [0, 4096], a multiple of 128: the most recent min(len, R) tokens of each
                             sequence and layer are kept in fp16 (K and V) instead of the
                             packed cache; 0 = none.  The paper's own results use none (RoPE-
                             aware bit allocation page, abstract: "without an fp16 recent-key
@@ -110,8 +110,9 @@ typedef struct {
   int32_t recent_window;   /* R of the config */
   int64_t packed_len;      /* positions held by the packed storage: max(0, len - R); positions
                               packed_len .. len-1 are in the recent window */
-  int64_t recent_bytes;    /* bytes of one layer's recent-window K (or V) ring:
-                              [batch][R][n_kv][128] fp16, position p in slot p mod R */
+  int64_t recent_bytes;    /* bytes of one layer's recent-window K (or V) ring, fp16, position p in
+                              slot p mod R: K [batch][R][n_kv][128]; V in dim-major 128-slot tiles
+                              [batch][n_kv][R/128][128 dims][128 slots] */
 } kvq_layer_info;
 
 typedef enum {

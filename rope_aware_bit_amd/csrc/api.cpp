@@ -32,7 +32,7 @@ bool config_valid(const kvq_config* c) {
   const int G = c->n_q_heads / c->n_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return false;
   if (c->codec < KVQ_CODEC_BGTQ || c->codec > KVQ_CODEC_NF16_B256) return false;
-  if (c->recent_window < 0 || c->recent_window > kvq::kMaxRecent) return false;
+  if (c->recent_window < 0 || c->recent_window > kvq::kMaxRecent || c->recent_window % 128) return false;
   if (c->pairing != KVQ_ROPE_HALF && c->pairing != KVQ_ROPE_INTERLEAVED) return false;
   if (c->v_bits < 1 || c->v_bits > kMaxBits) return false;
   if (c->b_min < 0 || c->b_max > kMaxBits || c->b_min > c->b_max) return false;
@@ -284,22 +284,18 @@ kvq_status kvq_quantize_append(kvq_cache* c, int32_t layer, const void* k, const
   const int64_t len = c->len[layer], R = c->cfg.recent_window;
   hipError_t e = hipSuccess;
   if (R == 0) {
-    e = kvq::launch_quantize(c, layer, k, v, dtype, n_new, n_new, len, s);
+    e = kvq::launch_quantize(c, layer, k, v, dtype, n_new, n_new, 0, len, s);
   } else {
     // positions [p_old, p_new) leave the window for the packed storage: first those already
-    // buffered (from their fp16 copies, slot p mod R, in at most two contiguous runs), then
-    // new ones that arrive already outside the window; the remaining new positions are
-    // copied into the ring (after the evictions: they reuse the evicted slots)
+    // buffered (from their fp16 copies in the rings), then new ones that arrive already
+    // outside the window; the remaining new positions are copied into the rings (after the
+    // evictions: they reuse the evicted slots)
     const int64_t p_old = len > R ? len - R : 0, p_new = len + n_new > R ? len + n_new - R : 0;
     const int64_t e_end = p_new < len ? p_new : len;
-    for (int64_t p = p_old; p < e_end && e == hipSuccess;) {
-      const int64_t slot = p % R, run = e_end - p < R - slot ? e_end - p : R - slot;
-      const int64_t off = slot * c->cfg.n_kv_heads * kHeadDim;
-      e = kvq::launch_quantize(c, layer, kvq::layer_k_recent(c, layer) + off, kvq::layer_v_recent(c, layer) + off,
-                               KVQ_F16, run, R, p, s);
-      p += run;
-    }
-    if (e == hipSuccess && p_new > len) e = kvq::launch_quantize(c, layer, k, v, dtype, p_new - len, n_new, len, s);
+    if (e_end > p_old)
+      e = kvq::launch_quantize(c, layer, kvq::layer_k_recent(c, layer), kvq::layer_v_recent(c, layer), KVQ_F16,
+                               e_end - p_old, 0, static_cast<int>(R), p_old, s);
+    if (e == hipSuccess && p_new > len) e = kvq::launch_quantize(c, layer, k, v, dtype, p_new - len, n_new, 0, len, s);
     const int64_t w0 = p_new > len ? p_new : len;
     if (e == hipSuccess && w0 < len + n_new)
       e = kvq::launch_recent_write(c, layer, k, v, dtype, n_new, w0 - len, w0, len + n_new - w0, s);
@@ -322,8 +318,10 @@ kvq_status kvq_decode_attn_splits(kvq_cache* c, int32_t layer, const void* q, in
   if (!c->plan_ready[layer] || c->len[layer] == 0) return KVQ_ESTATE;
   // S splits of the packed positions, plus one workgroup for the recent window if any
   const int64_t plen = kvq::packed_len(c, layer);
-  int S = plen == 0 ? 0 : n_splits > 0 ? n_splits : kvq::auto_splits_mfma(c, plen);
-  const int S_all = S + (c->len[layer] > plen ? 1 : 0);
+  const int64_t nb = c->len[layer] - plen;
+  const int n_rwg = static_cast<int>((nb + 127) / 128);   // recent-window workgroups (one ring tile each)
+  const int S = plen == 0 ? 0 : n_splits > 0 ? n_splits : kvq::auto_splits_mfma(c, plen, n_rwg);
+  const int S_all = S + n_rwg;
   if (S_all > c->max_splits) return KVQ_EINVAL;
   const int64_t units = static_cast<int64_t>(c->cfg.batch) * c->cfg.n_kv_heads;
   if (S_all > 1 && kvq::decode_split_mergers(S_all, units, c->n_cu) == 0) {

@@ -461,9 +461,9 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   }
   float (*qs_s)[kHeadDim] = reinterpret_cast<float (*)[kHeadDim]>(dyn_s);   // set-up only
 
-  // `len` packed positions in 128-token tiles; workgroup n_packed_splits (if any) reads the
-  // n_recent positions len .. len + n_recent - 1 of the recent window instead
-  const bool recent_wg = s == n_packed_splits;
+  // `len` packed positions in 128-token tiles; workgroups from n_packed_splits on read the
+  // n_recent positions of the recent window instead (one 128-slot ring tile per wave)
+  const bool recent_wg = s >= n_packed_splits;
   const int64_t n_tiles = (len + kVTile - 1) / kVTile;
   const int64_t t_begin = recent_wg ? n_tiles : static_cast<int64_t>(s) * tiles_per_split;
   const int64_t t_end = recent_wg ? n_tiles : (t_begin + tiles_per_split < n_tiles ? t_begin + tiles_per_split : n_tiles);
@@ -570,7 +570,8 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
       const int k = tid + 256 * j;
       const float qf = q_f32 ? __uint_as_float(qraw[j])
                              : half_bits_to_float(static_cast<uint16_t>(qraw[j] >> (16 * (k & 1))));
-      if (k < G * kHeadDim) qs_s[k / kHeadDim][k % kHeadDim] = qf * gr[j] * sigma;
+      // the recent window holds the keys as given: no gains there
+      if (k < G * kHeadDim) qs_s[k / kHeadDim][k % kHeadDim] = qf * (recent_wg ? 1.0f : gr[j]) * sigma;
     }
     if (tid < kHeadDim) fdim_s[tid] = static_cast<uint8_t>(fd_r);
     if (tid < kBlocks) {
@@ -619,9 +620,10 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   // q'[m / 2][dim of field 32 c + k]; rows of heads >= G and fields past the stored ones are 0.
   // Thread t < 256 fills field t % 128 for heads t / 128, t / 128 + 2, ...
   if (setup_wave) {
+    // (recent window: natural dim order, every dim stored)
     const int c = (tid >> 5) & 3, k = tid & 31, f = slot_field(c, k);
-    const bool live = f < (__builtin_amdgcn_readfirstlane(nf_r) & ~1);
-    const int dim = fdim_s[f];
+    const bool live = recent_wg || f < (__builtin_amdgcn_readfirstlane(nf_r) & ~1);
+    const int dim = recent_wg ? 32 * c + k : fdim_s[f];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int hh = 2 * j + (tid >> 7);
@@ -842,102 +844,92 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     for (int64_t tile = t_begin + wave + W; tile < t_end; tile += W) tile_body(tile, false);
   }
   if (recent_wg) {
-    // ---- recent window (fp16 K and V, no scales): wave w takes 64-position chunks w, w + W,
-    //      ...  Lane t computes the G logits of position t of the chunk from this wave's copy
-    //      of q * sigma' in LDS; the online softmax runs per head on wave reductions; lane
-    //      (n, g) with n < G then accumulates head n's outputs at the dims the value product
-    //      would hold (16 dt + 4 g + r), so the wave merge below is shared.  The lo columns
-    //      stay zero. ----
-    float* qn = reinterpret_cast<float*>(kr);       // [G][128]
-    float* pwf = qn + G * kHeadDim;                 // [G][64]
-    for (int k = lane; k < G * kHeadDim; k += 64) {
-      const int64_t qi = (static_cast<int64_t>(b) * n_q + h * G) * kHeadDim + k;
-      const float qf = q_f32 ? reinterpret_cast<const float*>(qv)[qi]
-                             : __half2float(reinterpret_cast<const __half*>(qv)[qi]);
-      qn[k] = qf * sigma;
-    }
-    wave_sync();
-    float mr[G], lr[G];
+    // ---- recent window: fp16 keys [R][n_kv][128] and values in dim-major 128-slot tiles, no
+    //      scales.  Recent workgroup j takes ring tile j (its first min(128, n_recent - 128 j)
+    //      slots hold window positions; the order of positions does not matter to the
+    //      softmax), on wave 0: the tile's 64 KB of fp16 operands are as much as one compute
+    //      unit reads for a packed split.  Same products as a packed tile, with the operands
+    //      loaded straight from the ring. ----
+    const int64_t j = s - n_packed_splits;
+    const int64_t nv64 = n_recent - 128 * j;
+    if (wave == 0) {
+      const int nv = nv64 < 128 ? static_cast<int>(nv64) : 128;
+      const __half* kt = rk + ((static_cast<int64_t>(b) * R + 128 * j) * n_kv + h) * kHeadDim;
+      const __half* vt = rv + ((bh * (R / 128) + j) * kHeadDim) * 128;
+      f4 dacc[8];
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      mr[hh] = -INFINITY;
-      lr[hh] = 0.0f;
-    }
-    const int64_t n_chunks = (n_recent + 63) / 64;
-    for (int64_t ci = wave; ci < n_chunks; ci += W) {
-      const int64_t c0 = len + ci * 64;                       // first position of the chunk
-      const int nvalid = n_recent - ci * 64 < 64 ? static_cast<int>(n_recent - ci * 64) : 64;
-      const bool valid = lane < nvalid;
-      const int64_t slot = (c0 + (valid ? lane : 0)) % R;
-      const __half* krow = rk + ((static_cast<int64_t>(b) * R + slot) * n_kv + h) * kHeadDim;
-      float lg[G];
+      for (int tg = 0; tg < 8; ++tg) dacc[tg] = f4{0.f, 0.f, 0.f, 0.f};
+      // all of the tile's key operands are loaded at once (one round of memory latency)
+      h8 bk[4][8];
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh) lg[hh] = 0.0f;
-#pragma unroll 2
-      for (int c8 = 0; c8 < kHeadDim / 8; ++c8) {
-        const uint4 raw = *reinterpret_cast<const uint4*>(krow + 8 * c8);
-        __half xh[8];
-        __builtin_memcpy(xh, &raw, 16);
+      for (int c = 0; c < 4; ++c) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = __half2float(xh[e]);
-#pragma unroll
-          for (int hh = 0; hh < G; ++hh) lg[hh] = fmaf(x, qn[hh * kHeadDim + 8 * c8 + e], lg[hh]);
+        for (int tg = 0; tg < 8; ++tg) {
+          const int t = 16 * tg + n < nv ? 16 * tg + n : 0;   // slots past the window: slot 0, masked
+          bk[c][tg] = *reinterpret_cast<const h8*>(kt + static_cast<int64_t>(t) * n_kv * kHeadDim + 32 * c + 8 * g);
         }
       }
-      float al[G];
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        const float x = valid ? lg[hh] : -INFINITY;
-        const float mn = fmaxf(mr[hh], wave_max(x));
-        al[hh] = __builtin_amdgcn_exp2f(mr[hh] - mn);   // 0 on the first chunk
-        const float pp = valid ? __builtin_amdgcn_exp2f(x - mn) : 0.0f;
-        lr[hh] = lr[hh] * al[hh] + wave_sum(pp);
-        mr[hh] = mn;
-        pwf[hh * 64 + lane] = pp;
+      for (int c = 0; c < 4; ++c) {
+        const h8 aq = *reinterpret_cast<const h8*>(&a_s[c][n][8 * g]);
+#pragma unroll
+        for (int tg = 0; tg < 8; ++tg) dacc[tg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq, bk[c][tg], dacc[tg], 0, 0, 0);
       }
-      wave_sync();
-      if (n < G) {
-        float a_n = al[0];
+      // and the value operands, in flight during the softmax
+      // (slots past the window hold zeros or stale values with p = 0: finite either way)
+      h8 av[4][8];
 #pragma unroll
-        for (int hh = 1; hh < G; ++hh) a_n = n == hh ? al[hh] : a_n;
+      for (int c = 0; c < 4; ++c) {
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) oacc[dt] *= a_n;
-        for (int t = 0; t < nvalid; ++t) {
-          const float pt = pwf[n * 64 + t];
-          const __half* vrow = rv + ((static_cast<int64_t>(b) * R + (c0 + t) % R) * n_kv + h) * kHeadDim + 4 * g;
+        for (int dt = 0; dt < 8; ++dt)
+          av[c][dt] = *reinterpret_cast<const h8*>(vt + static_cast<int64_t>(16 * dt + n) * 128 + 32 * g + 8 * c);
+      }
+      float L0[8], L1[8];
+      float mt0 = -INFINITY, mt1 = -INFINITY;
 #pragma unroll
-          for (int dt = 0; dt < 8; ++dt) {
-            const uint2 raw = *reinterpret_cast<const uint2*>(vrow + 16 * dt);
-            __half vh[4];
-            __builtin_memcpy(vh, &raw, 8);
+      for (int tg = 0; tg < 8; ++tg) {
+        const float bias = 16 * tg + n < nv ? 0.0f : -INFINITY;
+        L0[tg] = dacc[tg][0] + dacc[tg][1] + bias;
+        L1[tg] = dacc[tg][2] + dacc[tg][3] + bias;
+        mt0 = fmaxf(mt0, L0[tg]);
+        mt1 = fmaxf(mt1, L1[tg]);
+      }
+      mt0 = row_max16(mt0);
+      mt1 = row_max16(mt1);
+      // first (and only) tile of this wave: m starts at -inf, so no rescale of o or l
+      m0 = mt0;
+      m1 = mt1;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) oacc[dt][r] = fmaf(pt, __half2float(vh[r]), oacc[dt][r]);
-          }
+      for (int tg = 0; tg < 8; ++tg) {
+        const float p0 = __builtin_amdgcn_exp2f(L0[tg] - m0), p1 = __builtin_amdgcn_exp2f(L1[tg] - m1);
+        l0 += p0;
+        l1 += p1;
+        const _Float16 p0h = static_cast<_Float16>(p0), p1h = static_cast<_Float16>(p1);
+        const int t = 16 * tg + n;
+        if (vh0) {
+          pw[h0 * kPS + t] = p0h;
+          pw[(G + h0) * kPS + t] = static_cast<_Float16>(p0 - static_cast<float>(p0h));
+        }
+        if (vh1) {
+          pw[h1 * kPS + t] = p1h;
+          pw[(G + h1) * kPS + t] = static_cast<_Float16>(p1 - static_cast<float>(p1h));
         }
       }
       wave_sync();
-    }
-    // row g's lanes carry heads 2g, 2g + 1: the maxima in every lane, the sums in lane n = 0
-    // (summed over the row below)
-    float m_a = mr[0], m_b = -INFINITY, l_a = lr[0], l_b = 0.0f;
-    if constexpr (G > 1) {
-      m_b = mr[1];
-      l_b = lr[1];
 #pragma unroll
-      for (int hh = 2; hh < G; hh += 2) {
-        if (2 * g == hh) {
-          m_a = mr[hh];
-          m_b = mr[hh + 1];
-          l_a = lr[hh];
-          l_b = lr[hh + 1];
+      for (int c = 0; c < 4; ++c) {
+        h8 bp;
+        if (n < PCOLS) {
+          bp = *reinterpret_cast<const h8*>(&pw[n * kPS + 32 * g + 8 * c]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) bp[e] = static_cast<_Float16>(0.0f);
         }
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[c][dt], bp, oacc[dt], 0, 0, 0);
       }
+      wave_sync();
     }
-    m0 = m_a;
-    m1 = m_b;
-    l0 = n == 0 ? l_a : 0.0f;
-    l1 = n == 0 ? l_b : 0.0f;
   }
 
   // tag base of this call's split partials (read before this workgroup publishes anything)
@@ -1041,7 +1033,8 @@ hipError_t launch_gvw(kvq_cache* c, int layer, const void* q, int q_f32, float s
   const int64_t n_recent = c->len[layer] - plen;
   const int64_t n_tiles = (plen + kVTile - 1) / kVTile;
   const int tps = S > 0 ? static_cast<int>((n_tiles + S - 1) / S) : 0;
-  const int S_all = S + (n_recent > 0 ? 1 : 0);
+  // one ring tile of the window per recent workgroup
+  const int S_all = S + static_cast<int>((n_recent + 127) / 128);
   const __half* rk = n_recent > 0 ? layer_k_recent(c, layer) : nullptr;
   const __half* rv = n_recent > 0 ? layer_v_recent(c, layer) : nullptr;
   const int R = cfg.recent_window;

@@ -8,15 +8,16 @@ hipError_t launch_decode_mfma_g2(kvq_cache*, int, const void*, int, float, float
 hipError_t launch_decode_mfma_g4(kvq_cache*, int, const void*, int, float, float*, int, hipStream_t);
 hipError_t launch_decode_mfma_g8(kvq_cache*, int, const void*, int, float, float*, int, hipStream_t);
 
-int auto_splits_mfma(const kvq_cache* c, int64_t len) {
-  // one workgroup per compute unit over (splits x KV heads x sequences), and at least one
-  // 128-token tile per wave; `len` packed positions (none: no packed split)
+int auto_splits_mfma(const kvq_cache* c, int64_t len, int n_extra) {
+  // one workgroup per compute unit over (splits x KV heads x sequences), counting the n_extra
+  // recent-window workgroups per unit, and at least one 128-token tile per wave; `len` packed
+  // positions (none: no packed split)
   if (len <= 0) return 0;
   const int64_t n_tiles = (len + kVTile - 1) / kVTile;
   const int64_t units = static_cast<int64_t>(c->cfg.batch) * c->cfg.n_kv_heads;
   const int W = decode_waves(c);
   int64_t S = (n_tiles + W - 1) / W;
-  const int64_t want = (256 + units - 1) / units;
+  const int64_t want = (c->n_cu + units - 1) / units - n_extra;
   if (S > want) S = want;
   if (S > c->max_splits) S = c->max_splits;
   if (S < 1) S = 1;

@@ -100,10 +100,11 @@ namespace kvq {
 // return the launch status; arguments are validated by the caller.
 hipError_t launch_alloc(kvq_cache* c, int layer, const void* keys, int dtype, int64_t n_tok,
                         const double* block_weight, hipStream_t stream);
-// Quantizes positions L0 .. L0 + n_new - 1 of every sequence from rows 0 .. n_new - 1 of
-// [batch][in_stride][n_kv][128] K and V inputs into the packed storage.
+// Quantizes positions L0 .. L0 + n_new - 1 of every sequence into the packed storage, from
+// rows 0 .. n_new - 1 of [batch][in_stride][n_kv][128] K and V inputs, or (ring_R > 0) from
+// the recent-window rings of R = ring_R slots (fp16).
 hipError_t launch_quantize(kvq_cache* c, int layer, const void* k, const void* v, int dtype,
-                           int64_t n_new, int64_t in_stride, int64_t L0, hipStream_t stream);
+                           int64_t n_new, int64_t in_stride, int ring_R, int64_t L0, hipStream_t stream);
 hipError_t launch_recent_write(kvq_cache* c, int layer, const void* k, const void* v, int dtype,
                                int64_t in_stride, int64_t row0, int64_t pos0, int64_t count,
                                hipStream_t stream);
@@ -111,7 +112,7 @@ hipError_t launch_decode_mfma(kvq_cache* c, int layer, const void* q, int dtype,
                               float* out, int n_splits, hipStream_t stream);
 hipError_t launch_fidelity(kvq_cache* c, int layer, const void* q, const void* keys, int dtype,
                            float scale, double* mae, double* kl, hipStream_t stream);
-int auto_splits_mfma(const kvq_cache* c, int64_t len);
+int auto_splits_mfma(const kvq_cache* c, int64_t len, int n_extra);
 
 // Launch shape of the decode kernel for a cache: waves per workgroup (8 = two per SIMD, or 4),
 // whether each wave's V tile has an LDS area of its own (copied at tile start; a static array

@@ -47,7 +47,7 @@ __device__ inline float inv_scale(__half s16) {
 
 template <typename T, bool NF>
 __global__ __launch_bounds__(kThreads) void quantize_append(
-    const T* __restrict__ kin, const T* __restrict__ vin, int64_t n_new, int64_t in_stride, int64_t L0, int n_kv,
+    const T* __restrict__ kin, const T* __restrict__ vin, int64_t n_new, int64_t in_stride, int ring_R, int64_t L0, int n_kv,
     int64_t cap, const Plan* __restrict__ plans, const Tables* __restrict__ tab,
     uint32_t* __restrict__ kc, uint32_t* __restrict__ vc, uint16_t* __restrict__ ks,
     uint16_t* __restrict__ vs, int k_words, int v_bits, int n_nf) {
@@ -88,9 +88,24 @@ __global__ __launch_bounds__(kThreads) void quantize_append(
     const int hh = (k / (kHeadDim / kVec * kGroupTok)) % kHeads;
     const int tsr = k / (kHeadDim / kVec * kGroupTok * kHeads);   // 0: K, 1: V
     if (r >= lo && r < hi) {
-      const int64_t src = ((static_cast<int64_t>(b) * in_stride + (g0 + r - L0)) * n_kv + h0 + hh) * kHeadDim + q * kVec;
-      const T* in = tsr ? vin : kin;
-      const uint4 v4 = *reinterpret_cast<const uint4*>(in + src);
+      uint4 v4;
+      if (ring_R == 0) {
+        const int64_t src = ((static_cast<int64_t>(b) * in_stride + (g0 + r - L0)) * n_kv + h0 + hh) * kHeadDim + q * kVec;
+        v4 = *reinterpret_cast<const uint4*>((tsr ? vin : kin) + src);
+      } else {
+        // recent-window rings (fp16): keys [batch][R][n_kv][128], values in dim-major 128-slot
+        // tiles [batch][n_kv][R / 128][128][128]; position p sits in slot p mod R
+        const int64_t slot = (g0 + r) % ring_R;
+        if (tsr == 0) {
+          v4 = *reinterpret_cast<const uint4*>(kin + ((static_cast<int64_t>(b) * ring_R + slot) * n_kv + h0 + hh) * kHeadDim + q * kVec);
+        } else {
+          const T* vt = vin + (((static_cast<int64_t>(b) * n_kv + h0 + hh) * (ring_R / 128) + slot / 128) * kHeadDim + q * kVec) * 128 + slot % 128;
+          T e8[kVec];
+#pragma unroll
+          for (int e = 0; e < kVec; ++e) e8[e] = vt[e * 128];
+          __builtin_memcpy(&v4, e8, 16);
+        }
+      }
       uint32_t* d = &x_s[tsr][hh][r][q * 4];
       d[0] = v4.x;
       d[1] = v4.y;
@@ -219,7 +234,7 @@ __global__ __launch_bounds__(kThreads) void quantize_append(
 }  // namespace
 
 hipError_t launch_quantize(kvq_cache* c, int layer, const void* k, const void* v, int dtype,
-                           int64_t n_new, int64_t in_stride, int64_t L0, hipStream_t stream) {
+                           int64_t n_new, int64_t in_stride, int ring_R, int64_t L0, hipStream_t stream) {
   const kvq_config& cfg = c->cfg;
   const int64_t first = L0 / kGroupTok, last = (L0 + n_new - 1) / kGroupTok;
   dim3 grid(static_cast<unsigned>(last - first + 1), static_cast<unsigned>(cfg.n_kv_heads),
@@ -228,7 +243,7 @@ hipError_t launch_quantize(kvq_cache* c, int layer, const void* k, const void* v
   const Plan* plans = c->plans + static_cast<int64_t>(layer) * cfg.n_kv_heads;
 #define KVQ_LAUNCH_Q(T, NF)                                                                      \
   hipLaunchKernelGGL((quantize_append<T, NF>), grid, dim3(kThreads), 0, stream,                 \
-                     static_cast<const T*>(k), static_cast<const T*>(v), n_new, in_stride, L0,   \
+                     static_cast<const T*>(k), static_cast<const T*>(v), n_new, in_stride, ring_R, L0, \
                      cfg.n_kv_heads, c->cap, plans, c->tables, layer_k_codes(c, layer),          \
                      layer_v_codes(c, layer), layer_k_scales(c, layer), layer_v_scales(c, layer), \
                      c->k_words, cfg.v_bits, c->n_nf_blocks)
@@ -244,9 +259,11 @@ hipError_t launch_quantize(kvq_cache* c, int layer, const void* k, const void* v
 namespace {
 
 // Copies `count` new positions (input rows row0 .. row0 + count - 1 of a [batch][in_stride]
-// [n_kv][128] tensor, positions pos0 ..) into a recent-window ring [batch][R][n_kv][128] fp16
-// at slot position mod R, rounding fp32 inputs to fp16 (nearest even).  One workgroup per
-// (position, sequence); thread i copies element i of every head.
+// [n_kv][128] tensor, positions pos0 ..) into the recent-window rings at slot position mod R,
+// rounding fp32 inputs to fp16 (nearest even): keys as [batch][R][n_kv][128], values in
+// dim-major 128-slot tiles [batch][n_kv][R / 128][128 dims][128 slots] (the value product's
+// operand order).  One workgroup per (position, sequence); thread i copies element i of every
+// head.
 template <typename T>
 __global__ __launch_bounds__(256) void recent_write(const T* __restrict__ kin, const T* __restrict__ vin,
                                                    int64_t in_stride, int64_t row0, int64_t pos0, int n_kv,
@@ -257,8 +274,10 @@ __global__ __launch_bounds__(256) void recent_write(const T* __restrict__ kin, c
   const int64_t src = (static_cast<int64_t>(b) * in_stride + row0 + i) * n_kv * kHeadDim;
   const int64_t dst = (static_cast<int64_t>(b) * R + slot) * n_kv * kHeadDim;
   for (int e = threadIdx.x; e < n_kv * kHeadDim; e += 256) {
+    const int hh = e / kHeadDim, d = e % kHeadDim;
     kr[dst + e] = __float2half_rn(static_cast<float>(kin[src + e]));
-    vr[dst + e] = __float2half_rn(static_cast<float>(vin[src + e]));
+    const int64_t vdst = (((static_cast<int64_t>(b) * n_kv + hh) * (R / 128) + slot / 128) * kHeadDim + d) * 128 + slot % 128;
+    vr[vdst] = __float2half_rn(static_cast<float>(vin[src + e]));
   }
 }
 

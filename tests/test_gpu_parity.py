@@ -137,7 +137,9 @@ def run_case(wname, T, k_bits, v_bits, codec="bgtq", pairing="half", batch=None,
                     assert np.array_equal(vscale[b, h, :P], r["v_s16"].view(np.uint16)), f"V scales b={b} h={h}"
         if recent > 0:
             kr = cache.read(0, kvq.PART_K_RECENT, np.float16).reshape(B, recent, H, 128)
-            vr = cache.read(0, kvq.PART_V_RECENT, np.float16).reshape(B, recent, H, 128)
+            # values: dim-major 128-slot tiles [B][H][R/128][128][128] -> [B][R][H][128]
+            vr = cache.read(0, kvq.PART_V_RECENT, np.float16).reshape(B, H, recent // 128, 128, 128)
+            vr = vr.transpose(0, 2, 4, 1, 3).reshape(B, recent, H, 128)
             pos = np.arange(P, T)
             assert np.array_equal(kr[:, pos % recent].view(np.uint16), Ke[:, P:].astype(np.float16).view(np.uint16))
             assert np.array_equal(vr[:, pos % recent].view(np.uint16), Ve[:, P:].astype(np.float16).view(np.uint16))
