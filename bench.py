@@ -124,6 +124,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen3b_128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="skip the K3V2 / recent-window variants and the fidelity diagnostics "
+                         "(for kernel traces of the step's decode launches alone)")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run one plain copy of known size and one decode launch, then exit "
                          "(for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)")
@@ -213,7 +216,7 @@ def main():
     # window of 1024 positions; decode launches timed like the step
     variants = {}
     k0d = keys0[0]
-    v0d = torch.from_numpy(keep[1]).to(dev) if keep is not None else None
+    v0d = torch.from_numpy(keep[1]).to(dev) if keep is not None and not args.decode_only else None
     if v0d is not None:
         for label, vk, vv, R in (("K3V2", 3, 2, 0), ("K3V3_recent1024", 3, 3, 1024)):
             vc = kvq.Cache(kvq.Config(1, H, Hq, B, T, vk, vv, recent_window=R))
@@ -237,16 +240,18 @@ def main():
         del v0d
 
     # key-fidelity diagnostics of layer 0 (logit MAE and softmax KL against the given keys)
-    fid_reps = 5
-    cache.key_fidelity(0, qs[0], keys0)
-    torch.cuda.synchronize()
-    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    f0.record(stream)
-    for _ in range(fid_reps):
-        mae, kl = cache.key_fidelity(0, qs[0], keys0)
-    f1.record(stream)
-    torch.cuda.synchronize()
-    fid_us = f0.elapsed_time(f1) * 1e3 / fid_reps
+    fid_reps = 0 if args.decode_only else 5
+    fid_us, mae, kl = float("nan"), torch.full((1,), float("nan")), torch.full((1,), float("nan"))
+    if fid_reps:
+        cache.key_fidelity(0, qs[0], keys0)
+        torch.cuda.synchronize()
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        f0.record(stream)
+        for _ in range(fid_reps):
+            mae, kl = cache.key_fidelity(0, qs[0], keys0)
+        f1.record(stream)
+        torch.cuda.synchronize()
+        fid_us = f0.elapsed_time(f1) * 1e3 / fid_reps
     fid_bytes = B * T * H * (128 * 2 + kb * 16 + 2) + B * Hq * 128 * 2
     fid_flops = 2 * 2 * 128 * B * T * Hq          # two fp64 dot products per (position, query head)
     del keys0
@@ -285,7 +290,7 @@ def main():
                           (float(np.mean(app_ms)) * 1e-3) / 1e9, 2),
         },
         "variants": variants,
-        "fidelity": {
+        "fidelity": None if not fid_reps else {
             "layer": 0,
             "us_per_layer": round(fid_us, 2),
             "GB/s": round(fid_bytes / (fid_us * 1e-6) / 1e9, 2),
