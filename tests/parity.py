@@ -36,11 +36,13 @@ def assert_attention_close(gpu, ref, what=""):
 class OracleLayer:
     """Oracle plan, codes, packed words and dequantized cache for one layer."""
 
-    def __init__(self, calib, k_bits, v_bits, codec="bgtq", pairing="half", b_min=0, b_max=8):
+    def __init__(self, calib, k_bits, v_bits, codec="bgtq", pairing="half", b_min=0, b_max=8,
+                 block_weight=None):
         self.k_bits, self.v_bits, self.codec, self.pairing = k_bits, v_bits, codec, pairing
         H = calib.shape[1] if calib is not None else None
         if codec == "bgtq":
-            self.widths, self.g, self.ig, self.m = al.allocate(calib, k_bits, b_min, b_max, pairing)
+            self.widths, self.g, self.ig, self.m = al.allocate(calib, k_bits, b_min, b_max, pairing,
+                                                               block_weight=block_weight)
         else:
             kb = 4 if codec == "nf16" else k_bits
             self.widths = np.full((H, 64), kb, dtype=np.int64)

@@ -9,6 +9,7 @@ within 1e-9 relative + 1e-12 absolute.
 import numpy as np
 import pytest
 
+from oracle import allocation as al
 from oracle import attention as at
 from oracle import fidelity as fd
 from oracle import layout as lay
@@ -32,7 +33,7 @@ def _kvq():
 
 def run_case(wname, T, k_bits, v_bits, codec="bgtq", pairing="half", batch=None, layer=0,
              chunks=None, n_splits=0, noise="gauss", temper=False, check_codes=True, sample_rows=None,
-             b_min=0, b_max=8, fidelity=True, recent=0):
+             b_min=0, b_max=8, fidelity=True, recent=0, query_weighted=False):
     """Quantize T tokens of one layer on the GPU and in the oracle; compare everything.
 
     recent > 0: the last `recent` positions stay in the fp16 window.  A position that was inside
@@ -55,15 +56,23 @@ def run_case(wname, T, k_bits, v_bits, codec="bgtq", pairing="half", batch=None,
     print(f"[{wname} T={T} K{k_bits}V{v_bits} {codec}] inputs generated", flush=True)
     tc = min(T, w.calib_tokens)
     calib = K[:, :tc].reshape(B * tc, H, 128)
+    # query-energy block weights w[h, j] (mean squared norm of block j over the queries of KV
+    # head h's group), an input of the allocation
+    bw = None
+    if query_weighted:
+        qv = Q.astype(np.float64).reshape(B, H, w.group, 128)
+        p0, p1 = al.block_pairs(128, pairing)
+        bw = np.ascontiguousarray(np.mean(qv[..., p0] ** 2 + qv[..., p1] ** 2, axis=(0, 2)))   # [H, 64]
     ol = OracleLayer(calib if codec == "bgtq" else K[:, :1].reshape(B, H, 128), k_bits, v_bits,
-                     codec, pairing, b_min, b_max)
+                     codec, pairing, b_min, b_max, block_weight=bw)
 
     cfg = kvq.Config(n_layers=1, n_kv_heads=H, n_q_heads=Hq, batch=B, max_tokens=T, k_bits=k_bits,
                      v_bits=v_bits, b_min=b_min, b_max=b_max, codec=CODEC[codec],
                      pairing=PAIRING[pairing], recent_window=recent)
     cache = kvq.Cache(cfg)
     dev = torch.device("cuda:0")
-    cache.alloc_bits(0, torch.from_numpy(np.ascontiguousarray(calib)).to(dev) if codec == "bgtq" else None)
+    cache.alloc_bits(0, torch.from_numpy(np.ascontiguousarray(calib)).to(dev) if codec == "bgtq" else None,
+                     block_weight=torch.from_numpy(bw).to(dev) if bw is not None else None)
     bits, gains = cache.get_plan(0)
     assert np.array_equal(bits, ol.widths), "plan widths differ"
     assert np.array_equal(gains.view(np.uint32), ol.g.astype(np.float32).view(np.uint32)), "gains differ"
@@ -242,6 +251,11 @@ def test_recent_window_nf16():
 def test_asymmetric_k3v2_qwen_shape():
     """The paper's K3V2 setting (abstract), no recent window, on the Qwen2.5-3B shape."""
     run_case("qwen3b_128k", 20000, 3, 2, temper=True)
+
+
+def test_query_weighted_allocation():
+    """Block weights w_j = E |q_j|^2 from the decode queries, passed to the allocation."""
+    run_case("llama8b_32k", 2000, 3, 3, query_weighted=True, temper=True)
 
 
 def test_b_min_b_max_limits():
