@@ -60,6 +60,9 @@ typedef enum { KVQ_F16 = 0, KVQ_F32 = 1 } kvq_dtype;
 typedef enum {
   KVQ_CODEC_BGTQ = 0,       /* Block-GTQ: per-block widths from kvq_alloc_bits, per-block gains */
   KVQ_CODEC_UNIFORM = 1,    /* uniform TQ-MSE-style baseline: every block k_bits, no gains */
+  KVQ_CODEC_UNIFORM_ROT = 3, /* uniform baseline on randomly rotated keys: K rows pass through
+                                R = H D / sqrt(128) (Sylvester-Hadamard H, caller signs D, see
+                                kvq_set_rotation) before the uniform quantizer; V as UNIFORM */
   KVQ_CODEC_NF16_B256 = 2   /* NQKV-style: 4-bit 16-level Gaussian quantiles, absmax scale per
                                256 consecutive values of a token's [n_kv_heads*128] vector */
 } kvq_codec;
@@ -168,7 +171,8 @@ kvq_status kvq_get_plan(const kvq_cache* cache, int32_t layer, int8_t* bits, flo
    fp32) while they are among the last R of the sequence; a position is
    quantized, from its fp16 copy, when it leaves the window, so the packed
    storage always covers positions 0 .. len-R-1.
-   Errors: KVQ_EINVAL, KVQ_ESTATE (no plan for the layer), KVQ_ECAPACITY. */
+   Errors: KVQ_EINVAL, KVQ_ESTATE (no plan for the layer, or no rotation signs for the
+   rotated codec), KVQ_ECAPACITY. */
 kvq_status kvq_quantize_append(kvq_cache* cache, int32_t layer, const void* k, const void* v,
                                int32_t dtype, int64_t n_new, kvq_stream stream);
 
@@ -217,6 +221,17 @@ kvq_status kvq_decode_attn_splits(kvq_cache* cache, int32_t layer, const void* q
 kvq_status kvq_key_fidelity(kvq_cache* cache, int32_t layer, const void* q, const void* keys,
                             int32_t dtype, float softmax_scale, double* mae, double* kl,
                             kvq_stream stream);
+
+/* Random signs of the key rotation of one layer (codec KVQ_CODEC_UNIFORM_ROT), after
+   "RoPE-Aware Bit Allocation for KV-Cache Quantization", abstract: the quantizer is built
+   on TQ-MSE, whose quantizer rotates the whole vector at random before scalar
+   quantization.  The stored key input is y = fp32(H (s * k) / sqrt(128)) (the fast
+   Walsh-Hadamard transform in fp64); decode and the fidelity diagnostics rotate the query
+   instead of the keys.  signs: host int8 [n_kv_heads][128], each +1 or -1; the caller draws
+   them.  Must precede the layer's first append.  Synchronizes the device.
+   Errors: KVQ_EINVAL (other codec, null or a value other than +-1), KVQ_ESTATE (the layer
+   already holds tokens). */
+kvq_status kvq_set_rotation(kvq_cache* cache, int32_t layer, const int8_t* signs);
 
 /* Tokens appended so far to `layer` (host bookkeeping; does not synchronize). */
 kvq_status kvq_seq_len(const kvq_cache* cache, int32_t layer, int64_t* len);

@@ -31,7 +31,7 @@ bool config_valid(const kvq_config* c) {
   if (c->n_q_heads % c->n_kv_heads != 0) return false;
   const int G = c->n_q_heads / c->n_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return false;
-  if (c->codec < KVQ_CODEC_BGTQ || c->codec > KVQ_CODEC_NF16_B256) return false;
+  if (c->codec < KVQ_CODEC_BGTQ || c->codec > KVQ_CODEC_UNIFORM_ROT) return false;
   if (c->recent_window < 0 || c->recent_window > kvq::kMaxRecent || c->recent_window % 128) return false;
   if (c->pairing != KVQ_ROPE_HALF && c->pairing != KVQ_ROPE_INTERLEAVED) return false;
   if (c->v_bits < 1 || c->v_bits > kMaxBits) return false;
@@ -51,7 +51,7 @@ bool layer_ok(const kvq_cache* c, int32_t layer) {
 void free_device(kvq_cache* c) {
   void* ptrs[] = {c->k_codes, c->v_codes, c->k_scales, c->v_scales, c->plans,
                   c->tables,  c->part_o,  c->part_l,  c->part_mt, c->energy_scratch, c->split_epochs,
-                  c->fid_part, c->k_recent, c->v_recent};
+                  c->fid_part, c->k_recent, c->v_recent, c->rot_signs};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
 }
@@ -125,9 +125,11 @@ kvq_status kvq_cache_create(const kvq_config* cfg, kvq_cache** out) {
   c->n_nf_blocks = cfg->n_kv_heads * kHeadDim / kvq::kNfBlock;
   c->len = static_cast<int64_t*>(std::calloc(cfg->n_layers, sizeof(int64_t)));
   c->plan_ready = static_cast<uint8_t*>(std::calloc(cfg->n_layers, 1));
-  if (!c->len || !c->plan_ready) {
+  c->rot_ready = static_cast<uint8_t*>(std::calloc(cfg->n_layers, 1));
+  if (!c->len || !c->plan_ready || !c->rot_ready) {
     std::free(c->len);
     std::free(c->plan_ready);
+    std::free(c->rot_ready);
     delete c;
     return KVQ_ENOMEM;
   }
@@ -158,6 +160,8 @@ kvq_status kvq_cache_create(const kvq_config* cfg, kvq_cache** out) {
     if (st == KVQ_OK) st = dev_alloc(reinterpret_cast<void**>(&c->v_recent), c->recent_layer * L, "recent V");
   }
   if (st == KVQ_OK) st = dev_alloc(reinterpret_cast<void**>(&c->plans), sizeof(kvq::Plan) * L * H, "plans");
+  if (st == KVQ_OK && cfg->codec == KVQ_CODEC_UNIFORM_ROT)
+    st = dev_alloc(reinterpret_cast<void**>(&c->rot_signs), L * H * kHeadDim, "rotation signs");
   if (st == KVQ_OK) st = dev_alloc(reinterpret_cast<void**>(&c->tables), sizeof(kvq::Tables), "tables");
   if (st == KVQ_OK)
     st = dev_alloc(reinterpret_cast<void**>(&c->part_o), per_split / (kHeadDim + 2) * kHeadDim * ms, "partials");
@@ -193,6 +197,7 @@ kvq_status kvq_cache_create(const kvq_config* cfg, kvq_cache** out) {
     free_device(c);
     std::free(c->len);
     std::free(c->plan_ready);
+    std::free(c->rot_ready);
     delete c;
     return st;
   }
@@ -206,6 +211,7 @@ void kvq_cache_destroy(kvq_cache* c) {
   free_device(c);
   std::free(c->len);
   std::free(c->plan_ready);
+  std::free(c->rot_ready);
   delete c;
 }
 
@@ -279,6 +285,7 @@ kvq_status kvq_quantize_append(kvq_cache* c, int32_t layer, const void* k, const
     return KVQ_EINVAL;
   }
   if (!c->plan_ready[layer]) return KVQ_ESTATE;
+  if (c->cfg.codec == KVQ_CODEC_UNIFORM_ROT && !c->rot_ready[layer]) return KVQ_ESTATE;
   if (c->len[layer] + n_new > c->cfg.max_tokens) return KVQ_ECAPACITY;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t len = c->len[layer], R = c->cfg.recent_window;
@@ -355,6 +362,18 @@ kvq_status kvq_key_fidelity(kvq_cache* c, int32_t layer, const void* q, const vo
   hipError_t e = kvq::launch_fidelity(c, layer, q, keys, dtype, softmax_scale, mae, kl,
                                       static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "fidelity launch");
+  return KVQ_OK;
+}
+
+kvq_status kvq_set_rotation(kvq_cache* c, int32_t layer, const int8_t* signs) {
+  if (!layer_ok(c, layer) || !signs || c->cfg.codec != KVQ_CODEC_UNIFORM_ROT) return KVQ_EINVAL;
+  const int64_t n = static_cast<int64_t>(c->cfg.n_kv_heads) * kHeadDim;
+  for (int64_t i = 0; i < n; ++i)
+    if (signs[i] != 1 && signs[i] != -1) return KVQ_EINVAL;
+  if (c->len[layer] > 0) return KVQ_ESTATE;
+  hipError_t e = hipMemcpy(c->rot_signs + layer * n, signs, n, hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail(e, "set rotation");
+  c->rot_ready[layer] = 1;
   return KVQ_OK;
 }
 

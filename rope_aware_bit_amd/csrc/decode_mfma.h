@@ -418,7 +418,8 @@ __device__ __attribute__((always_inline)) inline KWin k_windows(const KPar& k, c
 template <int G, int VB, bool NF, int W>
 __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     const void* __restrict__ qv, int q_f32, float sigma, int64_t len, int n_packed_splits,
-    const __half* __restrict__ rk, const __half* __restrict__ rv, int R, int64_t n_recent, int n_kv, int64_t cap,
+    const __half* __restrict__ rk, const __half* __restrict__ rv, int R, int64_t n_recent,
+    const int8_t* __restrict__ rot, int n_kv, int64_t cap,
     int tiles_per_split, const Plan* __restrict__ plans, const Tables* __restrict__ tabg,
     const uint32_t* __restrict__ kc, const uint32_t* __restrict__ vc, const uint16_t* __restrict__ ks,
     const uint16_t* __restrict__ vs, int k_words, int n_nf, int n_splits, int n_mergers, int region_words,
@@ -615,6 +616,29 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     }
   }
   lds_barrier();
+  // rotated keys (randomized Hadamard R = H D / sqrt(128)): <q, R^T y> = <R q, y>, so the
+  // packed splits rotate the scaled query (fast Walsh-Hadamard stages in fp32); the recent
+  // window holds unrotated keys
+  if (rot != nullptr && !recent_wg) {
+    if (setup_wave) {
+      for (int k = tid; k < G * kHeadDim; k += 256)
+        qs_s[k / kHeadDim][k % kHeadDim] *= static_cast<float>(rot[h * kHeadDim + k % kHeadDim]);
+    }
+    lds_barrier();
+    for (int hb = 1; hb < kHeadDim; hb <<= 1) {
+      if (setup_wave) {
+        for (int p = tid; p < G * kHeadDim / 2; p += 256) {
+          const int hh = p / (kHeadDim / 2), jj = p % (kHeadDim / 2);
+          const int i0 = (jj / hb) * 2 * hb + jj % hb, i1 = i0 + hb;
+          const float a = qs_s[hh][i0], bq = qs_s[hh][i1];
+          const float sc = hb == kHeadDim / 2 ? 0.08838834764831845f : 1.0f;   // 1/sqrt(128) at the end
+          qs_s[hh][i0] = (a + bq) * sc;
+          qs_s[hh][i1] = (a - bq) * sc;
+        }
+      }
+      lds_barrier();
+    }
+  }
   if (W == 4 && v_early) dma_v(t0);   // (8 waves: copied after the tile's K rows are staged)
   // query operand of the key product: a_s[c][m][k] = hi (m even) or lo (m odd) fp16 part of
   // q'[m / 2][dim of field 32 c + k]; rows of heads >= G and fields past the stored ones are 0.
@@ -1038,6 +1062,7 @@ hipError_t launch_gvw(kvq_cache* c, int layer, const void* q, int q_f32, float s
   const __half* rk = n_recent > 0 ? layer_k_recent(c, layer) : nullptr;
   const __half* rv = n_recent > 0 ? layer_v_recent(c, layer) : nullptr;
   const int R = cfg.recent_window;
+  const int8_t* rot = cfg.codec == KVQ_CODEC_UNIFORM_ROT ? c->rot_signs + static_cast<int64_t>(layer) * cfg.n_kv_heads * kHeadDim : nullptr;
   dim3 grid(S_all, cfg.n_kv_heads, cfg.batch);
   const size_t dyn = static_cast<size_t>(W) * sh.region_words * sizeof(uint32_t);
   const Plan* plans = c->plans + static_cast<int64_t>(layer) * cfg.n_kv_heads;
@@ -1046,7 +1071,7 @@ hipError_t launch_gvw(kvq_cache* c, int layer, const void* q, int q_f32, float s
   if constexpr (VB == 4) {
     if (nf) {
       hipLaunchKernelGGL((decode_mfma<G, 4, true, W>), grid, dim3(64 * W), dyn, stream, q, q_f32, sigma,
-                         plen, S, rk, rv, R, n_recent, cfg.n_kv_heads, c->cap, tps, plans, c->tables, layer_k_codes(c, layer),
+                         plen, S, rk, rv, R, n_recent, rot, cfg.n_kv_heads, c->cap, tps, plans, c->tables, layer_k_codes(c, layer),
                          layer_v_codes(c, layer), layer_k_scales(c, layer), layer_v_scales(c, layer),
                          c->k_words, c->n_nf_blocks, S_all, mergers, sh.region_words, sh.v_early, sh.v_off,
                          c->part_o, c->part_l, c->part_mt, c->split_epochs, out);
@@ -1054,7 +1079,7 @@ hipError_t launch_gvw(kvq_cache* c, int layer, const void* q, int q_f32, float s
     }
   }
   hipLaunchKernelGGL((decode_mfma<G, VB, false, W>), grid, dim3(64 * W), dyn, stream, q, q_f32, sigma,
-                     plen, S, rk, rv, R, n_recent, cfg.n_kv_heads, c->cap, tps, plans, c->tables, layer_k_codes(c, layer),
+                     plen, S, rk, rv, R, n_recent, rot, cfg.n_kv_heads, c->cap, tps, plans, c->tables, layer_k_codes(c, layer),
                      layer_v_codes(c, layer), layer_k_scales(c, layer), layer_v_scales(c, layer),
                      c->k_words, c->n_nf_blocks, S_all, mergers, sh.region_words, sh.v_early, sh.v_off,
                      c->part_o, c->part_l, c->part_mt, c->split_epochs, out);

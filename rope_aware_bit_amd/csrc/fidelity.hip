@@ -115,7 +115,8 @@ __global__ __launch_bounds__(256, 2) void fidelity_partials(
     const T* __restrict__ q, const T* __restrict__ keys, int64_t len, int n_kv, int64_t cap,
     double sigma, int64_t tok_per_split, const Plan* __restrict__ plans, const Tables* __restrict__ tab,
     const uint32_t* __restrict__ kc, const uint16_t* __restrict__ ks, int k_words, int n_nf, int nf,
-    int64_t plen, const __half* __restrict__ rk, int R, double* __restrict__ part, int S) {
+    int64_t plen, const __half* __restrict__ rk, int R, const int8_t* __restrict__ rot,
+    double* __restrict__ part, int S) {
   constexpr int kVec = 16 / sizeof(T);
   constexpr int kRow = kHeadDim + kVec;            // padded key row (elements)
   const int tid = threadIdx.x;
@@ -126,6 +127,7 @@ __global__ __launch_bounds__(256, 2) void fidelity_partials(
   const int64_t t_end = t_begin + tok_per_split < len ? t_begin + tok_per_split : len;
 
   __shared__ double q_s[kMaxGroup][kHeadDim];
+  __shared__ double qr_s[kMaxGroup][kHeadDim];   // rotated query (packed keys of the rotated codec)
   __shared__ double g_s[kHeadDim];
   __shared__ uint16_t cb_s[kMaxBits + 1][256];
   __shared__ uint8_t fdim_s[kHeadDim], fw_s[kHeadDim];
@@ -152,6 +154,27 @@ __global__ __launch_bounds__(256, 2) void fidelity_partials(
   if (tid == 0) nf_s = P->n_fields;
   __syncthreads();
   const int n_fields = nf_s;
+  // rotated codec: <q, R^T y> = <R q, y> with R q = H (s * q) / sqrt(128), in fp64
+  if (rot != nullptr) {
+    for (int k = tid; k < G * kHeadDim; k += 256)
+      qr_s[k / kHeadDim][k % kHeadDim] = q_s[k / kHeadDim][k % kHeadDim] * static_cast<double>(rot[h * kHeadDim + k % kHeadDim]);
+    __syncthreads();
+    for (int hb = 1; hb < kHeadDim; hb <<= 1) {
+      for (int p = tid; p < G * kHeadDim / 2; p += 256) {
+        const int hh = p / (kHeadDim / 2), jj = p % (kHeadDim / 2);
+        const int i0 = (jj / hb) * 2 * hb + jj % hb, i1 = i0 + hb;
+        const double a = qr_s[hh][i0], bq = qr_s[hh][i1];
+        qr_s[hh][i0] = a + bq;
+        qr_s[hh][i1] = a - bq;
+      }
+      __syncthreads();
+    }
+    const double sq = sqrt(static_cast<double>(kHeadDim));
+    for (int k = tid; k < G * kHeadDim; k += 256) qr_s[k / kHeadDim][k % kHeadDim] /= sq;
+  } else {
+    for (int k = tid; k < G * kHeadDim; k += 256) qr_s[k / kHeadDim][k % kHeadDim] = q_s[k / kHeadDim][k % kHeadDim];
+  }
+  __syncthreads();
 
   Stats st[2];
   stats_init(st[0]);
@@ -229,7 +252,7 @@ __global__ __launch_bounds__(256, 2) void fidelity_partials(
         const double c = static_cast<double>(__half2float(__ushort_as_half(cb_s[w][code])));
         const double kh = (s16 * g_s[dim]) * c;
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) ah[hh] += kh * q_s[hh][dim];
+        for (int hh = 0; hh < G; ++hh) ah[hh] += kh * qr_s[hh][dim];
       }
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
@@ -341,7 +364,9 @@ hipError_t launch_fidelity(kvq_cache* c, int layer, const void* q, const void* k
                      static_cast<const T*>(keys), len, H, c->cap, sigma, per, plans, c->tables,       \
                      layer_k_codes(c, layer), layer_k_scales(c, layer), c->k_words, c->n_nf_blocks,   \
                      nf ? 1 : 0, plen, plen < len ? layer_k_recent(c, layer) : nullptr,       \
-                     c->cfg.recent_window > 0 ? c->cfg.recent_window : 1, c->fid_part, static_cast<int>(S))
+                     c->cfg.recent_window > 0 ? c->cfg.recent_window : 1,                         \
+                     cfg.codec == KVQ_CODEC_UNIFORM_ROT ? c->rot_signs + static_cast<int64_t>(layer) * H * kHeadDim : nullptr, \
+                     c->fid_part, static_cast<int>(S))
 #define KVQ_FID_G(T)                  \
   switch (G) {                        \
     case 1: KVQ_FID(T, 1); break;     \

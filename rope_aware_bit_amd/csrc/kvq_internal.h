@@ -79,6 +79,8 @@ struct kvq_cache {
   __half* k_recent;            // recent-window rings [L][B][R][H][128] fp16 (R > 0)
   __half* v_recent;
   kvq::Plan* plans;            // [L][H]
+  int8_t* rot_signs;           // key-rotation signs [L][H][128] (codec UNIFORM_ROT)
+  uint8_t* rot_ready;          // per layer: signs set
   kvq::Tables* tables;         // device copy
   kvq::Tables host_tables;
   float* part_o;               // split partials [B][H][max_splits][G][128]

@@ -50,7 +50,7 @@ __global__ __launch_bounds__(kThreads) void quantize_append(
     const T* __restrict__ kin, const T* __restrict__ vin, int64_t n_new, int64_t in_stride, int ring_R, int64_t L0, int n_kv,
     int64_t cap, const Plan* __restrict__ plans, const Tables* __restrict__ tab,
     uint32_t* __restrict__ kc, uint32_t* __restrict__ vc, uint16_t* __restrict__ ks,
-    uint16_t* __restrict__ vs, int k_words, int v_bits, int n_nf) {
+    uint16_t* __restrict__ vs, int k_words, int v_bits, int n_nf, const int8_t* __restrict__ rot) {
   constexpr int kVec = 16 / sizeof(T);            // elements per 16-byte load
   constexpr int kRowW = kHeadDim * static_cast<int>(sizeof(T)) / 4 + 1;   // odd: no bank conflicts
   constexpr int kHeads = NF ? 2 : 1;              // heads staged per tensor
@@ -129,6 +129,38 @@ __global__ __launch_bounds__(kThreads) void quantize_append(
   if (tid == 0) nf_s = P->n_fields;
   __syncthreads();
 
+  // ---- 1b. rotated keys (randomized Hadamard): y = fp32(H (s * x) / sqrt(128)), the fast
+  //      Walsh-Hadamard stages in fp64 (exact for fp16 keys), one rounding at the division and
+  //      one to fp32; the K rows below are then read from ky_s ----
+  __shared__ double rw_s[kGroupTok][kHeadDim];
+  __shared__ float ky_s[kGroupTok][kHeadDim];
+  if (rot != nullptr) {   // uniform over the launch
+    const int8_t* sg = rot + h * kHeadDim;
+    for (int e = tid; e < kGroupTok * kHeadDim; e += kThreads) {
+      const int r = e / kHeadDim, i = e % kHeadDim;
+      rw_s[r][i] = static_cast<double>(xval(0, 0, r, i)) * static_cast<double>(sg[i]);
+    }
+    __syncthreads();
+    for (int hb = 1; hb < kHeadDim; hb <<= 1) {
+      for (int p = tid; p < kGroupTok * kHeadDim / 2; p += kThreads) {
+        const int r = p / (kHeadDim / 2), jj = p % (kHeadDim / 2);
+        const int i0 = (jj / hb) * 2 * hb + jj % hb, i1 = i0 + hb;
+        const double a = rw_s[r][i0], b = rw_s[r][i1];
+        rw_s[r][i0] = __dadd_rn(a, b);
+        rw_s[r][i1] = __dsub_rn(a, b);
+      }
+      __syncthreads();
+    }
+    const double sq = __dsqrt_rn(static_cast<double>(kHeadDim));
+    for (int e = tid; e < kGroupTok * kHeadDim; e += kThreads) {
+      const int r = e / kHeadDim, i = e % kHeadDim;
+      ky_s[r][i] = static_cast<float>(__ddiv_rn(rw_s[r][i], sq));
+    }
+    __syncthreads();
+  }
+  // K value i of staged row r of this head (rotated when the codec rotates)
+  auto kval = [&](int r, int i) { return rot != nullptr ? ky_s[r][i] : xval(0, NF ? (h - h0) : 0, r, i); };
+
   // ---- 2. scales: lanes 0..7 K, 8..15 V (one token each, in the quantizer's order) ----
   const int hsel = h - h0;   // this head's staged rows
   if (tid < 2 * kGroupTok) {
@@ -142,7 +174,7 @@ __global__ __launch_bounds__(kThreads) void quantize_append(
     } else {
       double ss = 0.0;
       for (int i = 0; i < kHeadDim; ++i) {
-        const float x = xval(tsr, hsel, r, i);
+        const float x = tsr == 0 ? kval(r, i) : xval(tsr, hsel, r, i);
         const double y = static_cast<double>(tsr == 0 ? __fmul_rn(x, ig_s[i]) : x);
         ss = __dadd_rn(ss, __dmul_rn(y, y));
       }
@@ -175,7 +207,7 @@ __global__ __launch_bounds__(kThreads) void quantize_append(
     const bool kl = live && f < nfld;
     const int i = kl ? fdim_s[f] : 0;
     const int w = kl ? fw_s[f] : 0;
-    const float x = xval(0, hsel, r, i);
+    const float x = kval(r, i);
     const float y = NF ? x : __fmul_rn(x, ig_s[i]);
     u[m] = __fmul_rn(y, isk_s[r]);
     wd[m] = w;
@@ -246,7 +278,8 @@ hipError_t launch_quantize(kvq_cache* c, int layer, const void* k, const void* v
                      static_cast<const T*>(k), static_cast<const T*>(v), n_new, in_stride, ring_R, L0, \
                      cfg.n_kv_heads, c->cap, plans, c->tables, layer_k_codes(c, layer),          \
                      layer_v_codes(c, layer), layer_k_scales(c, layer), layer_v_scales(c, layer), \
-                     c->k_words, cfg.v_bits, c->n_nf_blocks)
+                     c->k_words, cfg.v_bits, c->n_nf_blocks,                                      \
+                     cfg.codec == KVQ_CODEC_UNIFORM_ROT ? c->rot_signs + static_cast<int64_t>(layer) * cfg.n_kv_heads * kHeadDim : nullptr)
   if (dtype == KVQ_F16) {
     if (nf) KVQ_LAUNCH_Q(__half, true); else KVQ_LAUNCH_Q(__half, false);
   } else {

@@ -18,13 +18,13 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so"
 
 KVQ_OK, KVQ_EINVAL, KVQ_ENOMEM, KVQ_ECAPACITY, KVQ_ESTATE, KVQ_EHIP = range(6)
 KVQ_F16, KVQ_F32 = 0, 1
-CODEC_BGTQ, CODEC_UNIFORM, CODEC_NF16_B256 = 0, 1, 2
+CODEC_BGTQ, CODEC_UNIFORM, CODEC_NF16_B256, CODEC_UNIFORM_ROT = 0, 1, 2, 3
 ROPE_HALF, ROPE_INTERLEAVED = 0, 1
 PART_K_CODES, PART_V_CODES, PART_K_SCALES, PART_V_SCALES, PART_K_RECENT, PART_V_RECENT = range(6)
 
 EXPORTED = (
     "kvq_cache_create", "kvq_cache_destroy", "kvq_alloc_bits", "kvq_get_plan",
-    "kvq_quantize_append", "kvq_decode_attn", "kvq_decode_attn_splits", "kvq_key_fidelity", "kvq_seq_len",
+    "kvq_quantize_append", "kvq_decode_attn", "kvq_decode_attn_splits", "kvq_key_fidelity", "kvq_set_rotation", "kvq_seq_len",
     "kvq_layer_info_get", "kvq_read_cache", "kvq_codebook", "kvq_delta",
     "kvq_nf16_codebook", "kvq_status_str", "kvq_last_error",
 )
@@ -70,6 +70,7 @@ def _load() -> ctypes.CDLL:
         "kvq_decode_attn": (I32, [P, I32, P, I32, F32, P, P]),
         "kvq_decode_attn_splits": (I32, [P, I32, P, I32, F32, P, I32, P]),
         "kvq_key_fidelity": (I32, [P, I32, P, P, I32, F32, P, P, P]),
+        "kvq_set_rotation": (I32, [P, I32, P]),
         "kvq_seq_len": (I32, [P, I32, ctypes.POINTER(I64)]),
         "kvq_layer_info_get": (I32, [P, I32, ctypes.POINTER(kvq_layer_info)]),
         "kvq_read_cache": (I32, [P, I32, I32, I64, I64, P]),
@@ -209,6 +210,13 @@ class Cache:
         n = keys.shape[0] if keys is not None else 0
         wp = _ptr(block_weight) if block_weight is not None else None
         _check(lib.kvq_alloc_bits(self._h, layer, kp, dt, n, wp, _stream(stream)), "kvq_alloc_bits")
+
+    def set_rotation(self, layer: int, signs):
+        """Key-rotation signs of `layer` (codec CODEC_UNIFORM_ROT): int8 [n_kv_heads, 128] of +-1."""
+        sg = np.ascontiguousarray(np.asarray(signs, dtype=np.int8))
+        if sg.shape != (self.cfg.n_kv_heads, self.cfg.head_dim):
+            raise ValueError(f"signs must be [n_kv_heads, head_dim], got {sg.shape}")
+        _check(lib.kvq_set_rotation(self._h, layer, sg.ctypes.data), "kvq_set_rotation")
 
     def get_plan(self, layer: int):
         H = self.cfg.n_kv_heads

@@ -11,9 +11,10 @@ from oracle import allocation as al
 from oracle import attention as at
 from oracle import layout as lay
 from oracle import quantize as qz
+from oracle import rotation as rt
 
 PAIRING = {"half": 0, "interleaved": 1}
-CODEC = {"bgtq": 0, "uniform": 1, "nf16": 2}
+CODEC = {"bgtq": 0, "uniform": 1, "nf16": 2, "rot": 3}
 
 ABS_TOL = 2e-3
 REL_L2_TOL = 1e-3
@@ -37,8 +38,9 @@ class OracleLayer:
     """Oracle plan, codes, packed words and dequantized cache for one layer."""
 
     def __init__(self, calib, k_bits, v_bits, codec="bgtq", pairing="half", b_min=0, b_max=8,
-                 block_weight=None):
+                 block_weight=None, signs=None):
         self.k_bits, self.v_bits, self.codec, self.pairing = k_bits, v_bits, codec, pairing
+        self.signs = signs   # key-rotation signs [H, 128] of the rotated codec
         H = calib.shape[1] if calib is not None else None
         if codec == "bgtq":
             self.widths, self.g, self.ig, self.m = al.allocate(calib, k_bits, b_min, b_max, pairing,
@@ -68,7 +70,10 @@ class OracleLayer:
         else:
             wd = al.dim_widths(self.widths[h], 128, self.pairing)
             igd = al.dim_values(self.ig[h], 128, self.pairing)
-            ck, sk, _ = qz.quantize_rows(k_rows, wd, igd)
+            if self.codec == "rot":
+                ck, sk, _ = qz.quantize_rows(rt.rotate_rows_fp32(k_rows, self.signs[h]), wd)
+            else:
+                ck, sk, _ = qz.quantize_rows(k_rows, wd, igd)
             cv, sv, _ = qz.quantize_rows(v_rows, np.full(128, self.v_bits))
             out.update(k_codes=ck, k_s16=sk, v_codes=cv, v_s16=sv)
         dims, ws = self.fields(h)
@@ -84,6 +89,8 @@ class OracleLayer:
         wd = al.dim_widths(self.widths[h], 128, self.pairing)
         gd = al.dim_values(self.g[h], 128, self.pairing)
         kh = at.dequant_k(q_out["k_codes"], q_out["k_s16"], wd, gd)
+        if self.codec == "rot":
+            kh = rt.unrotate(kh, self.signs[h])
         vh = at.dequant_v(q_out["v_codes"], q_out["v_s16"], self.v_bits)
         return kh, vh
 

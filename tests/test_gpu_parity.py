@@ -63,8 +63,10 @@ def run_case(wname, T, k_bits, v_bits, codec="bgtq", pairing="half", batch=None,
         qv = Q.astype(np.float64).reshape(B, H, w.group, 128)
         p0, p1 = al.block_pairs(128, pairing)
         bw = np.ascontiguousarray(np.mean(qv[..., p0] ** 2 + qv[..., p1] ** 2, axis=(0, 2)))   # [H, 64]
+    # the rotated codec's signs are drawn here and passed to both sides
+    signs = np.random.default_rng(7).choice([-1, 1], size=(H, 128)).astype(np.int8) if codec == "rot" else None
     ol = OracleLayer(calib if codec == "bgtq" else K[:, :1].reshape(B, H, 128), k_bits, v_bits,
-                     codec, pairing, b_min, b_max, block_weight=bw)
+                     codec, pairing, b_min, b_max, block_weight=bw, signs=signs)
 
     cfg = kvq.Config(n_layers=1, n_kv_heads=H, n_q_heads=Hq, batch=B, max_tokens=T, k_bits=k_bits,
                      v_bits=v_bits, b_min=b_min, b_max=b_max, codec=CODEC[codec],
@@ -73,6 +75,8 @@ def run_case(wname, T, k_bits, v_bits, codec="bgtq", pairing="half", batch=None,
     dev = torch.device("cuda:0")
     cache.alloc_bits(0, torch.from_numpy(np.ascontiguousarray(calib)).to(dev) if codec == "bgtq" else None,
                      block_weight=torch.from_numpy(bw).to(dev) if bw is not None else None)
+    if signs is not None:
+        cache.set_rotation(0, signs)
     bits, gains = cache.get_plan(0)
     assert np.array_equal(bits, ol.widths), "plan widths differ"
     assert np.array_equal(gains.view(np.uint32), ol.g.astype(np.float32).view(np.uint32)), "gains differ"
@@ -256,6 +260,16 @@ def test_asymmetric_k3v2_qwen_shape():
 def test_query_weighted_allocation():
     """Block weights w_j = E |q_j|^2 from the decode queries, passed to the allocation."""
     run_case("llama8b_32k", 2000, 3, 3, query_weighted=True, temper=True)
+
+
+@pytest.mark.parametrize("kb", [2, 3])
+def test_rotated_uniform_codec(kb):
+    """Uniform quantizer on randomly rotated keys (Hadamard rotation with caller signs)."""
+    run_case("llama8b_32k", 3000, kb, kb, codec="rot", temper=True, chunks=[1000, 1999, 1])
+
+
+def test_rotated_uniform_codec_recent_window():
+    run_case("qwen3b_128k", 5000, 3, 3, codec="rot", chunks=[2048, 2951, 1], recent=256)
 
 
 def test_b_min_b_max_limits():
