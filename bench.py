@@ -218,9 +218,13 @@ def main():
     k0d = keys0[0]
     v0d = torch.from_numpy(keep[1]).to(dev) if keep is not None and not args.decode_only else None
     if v0d is not None:
-        for label, vk, vv, R in (("K3V2", 3, 2, 0), ("K3V3_recent1024", 3, 3, 1024)):
-            vc = kvq.Cache(kvq.Config(1, H, Hq, B, T, vk, vv, recent_window=R))
-            vc.alloc_bits(0, k0d[:chunk])
+        for label, vk, vv, R, codec in (("K3V2", 3, 2, 0, kvq.CODEC_BGTQ),
+                                        ("K3V3_recent1024", 3, 3, 1024, kvq.CODEC_BGTQ),
+                                        ("K3V3_uniform_rotated", 3, 3, 0, kvq.CODEC_UNIFORM_ROT)):
+            vc = kvq.Cache(kvq.Config(1, H, Hq, B, T, vk, vv, recent_window=R, codec=codec))
+            vc.alloc_bits(0, k0d[:chunk] if codec == kvq.CODEC_BGTQ else None)
+            if codec == kvq.CODEC_UNIFORM_ROT:
+                vc.set_rotation(0, np.random.default_rng(11).choice([-1, 1], size=(H, 128)).astype(np.int8))
             vc.quantize_append(0, k0d[None], v0d[None])
             vo = torch.empty(B, Hq, 128, dtype=torch.float32, device=dev)
             for _ in range(5):
@@ -234,7 +238,8 @@ def main():
             torch.cuda.synchronize()
             us = a0.elapsed_time(a1) * 1e3 / 50
             vbytes = B * H * ((T - R) * ((vk + vv) * 128 / 8 + 4) + R * 512) + B * Hq * 128 * 6 + H * PLAN_BYTES_PER_HEAD
-            variants[label] = {"k_bits": vk, "v_bits": vv, "recent_window": R, "us_per_launch": round(us, 2),
+            variants[label] = {"k_bits": vk, "v_bits": vv, "recent_window": R, "codec": int(codec),
+                               "us_per_launch": round(us, 2),
                                "GB/s": round(vbytes / (us * 1e-6) / 1e9, 2)}
             vc.close()
         del v0d

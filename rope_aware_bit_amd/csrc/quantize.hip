@@ -45,7 +45,7 @@ __device__ inline float inv_scale(__half s16) {
   return s == 0.0f ? 0.0f : __fdiv_rn(1.0f, s);
 }
 
-template <typename T, bool NF>
+template <typename T, bool NF, bool ROT>
 __global__ __launch_bounds__(kThreads) void quantize_append(
     const T* __restrict__ kin, const T* __restrict__ vin, int64_t n_new, int64_t in_stride, int ring_R, int64_t L0, int n_kv,
     int64_t cap, const Plan* __restrict__ plans, const Tables* __restrict__ tab,
@@ -132,9 +132,10 @@ __global__ __launch_bounds__(kThreads) void quantize_append(
   // ---- 1b. rotated keys (randomized Hadamard): y = fp32(H (s * x) / sqrt(128)), the fast
   //      Walsh-Hadamard stages in fp64 (exact for fp16 keys), one rounding at the division and
   //      one to fp32; the K rows below are then read from ky_s ----
-  __shared__ double rw_s[kGroupTok][kHeadDim];
-  __shared__ float ky_s[kGroupTok][kHeadDim];
-  if (rot != nullptr) {   // uniform over the launch
+  // (only the rotating instantiation carries these buffers)
+  __shared__ double rw_s[ROT ? kGroupTok : 1][ROT ? kHeadDim : 1];
+  __shared__ float ky_s[ROT ? kGroupTok : 1][ROT ? kHeadDim : 1];
+  if constexpr (ROT) {
     const int8_t* sg = rot + h * kHeadDim;
     for (int e = tid; e < kGroupTok * kHeadDim; e += kThreads) {
       const int r = e / kHeadDim, i = e % kHeadDim;
@@ -159,7 +160,10 @@ __global__ __launch_bounds__(kThreads) void quantize_append(
     __syncthreads();
   }
   // K value i of staged row r of this head (rotated when the codec rotates)
-  auto kval = [&](int r, int i) { return rot != nullptr ? ky_s[r][i] : xval(0, NF ? (h - h0) : 0, r, i); };
+  auto kval = [&](int r, int i) {
+    if constexpr (ROT) return ky_s[r][i];
+    else return xval(0, NF ? (h - h0) : 0, r, i);
+  };
 
   // ---- 2. scales: lanes 0..7 K, 8..15 V (one token each, in the quantizer's order) ----
   const int hsel = h - h0;   // this head's staged rows
@@ -272,18 +276,19 @@ hipError_t launch_quantize(kvq_cache* c, int layer, const void* k, const void* v
   dim3 grid(static_cast<unsigned>(last - first + 1), static_cast<unsigned>(cfg.n_kv_heads),
             static_cast<unsigned>(cfg.batch));
   const bool nf = cfg.codec == KVQ_CODEC_NF16_B256;
+  const bool rotk = cfg.codec == KVQ_CODEC_UNIFORM_ROT;
   const Plan* plans = c->plans + static_cast<int64_t>(layer) * cfg.n_kv_heads;
-#define KVQ_LAUNCH_Q(T, NF)                                                                      \
-  hipLaunchKernelGGL((quantize_append<T, NF>), grid, dim3(kThreads), 0, stream,                 \
+#define KVQ_LAUNCH_Q(T, NF, ROT)                                                                 \
+  hipLaunchKernelGGL((quantize_append<T, NF, ROT>), grid, dim3(kThreads), 0, stream,            \
                      static_cast<const T*>(k), static_cast<const T*>(v), n_new, in_stride, ring_R, L0, \
                      cfg.n_kv_heads, c->cap, plans, c->tables, layer_k_codes(c, layer),          \
                      layer_v_codes(c, layer), layer_k_scales(c, layer), layer_v_scales(c, layer), \
                      c->k_words, cfg.v_bits, c->n_nf_blocks,                                      \
                      cfg.codec == KVQ_CODEC_UNIFORM_ROT ? c->rot_signs + static_cast<int64_t>(layer) * cfg.n_kv_heads * kHeadDim : nullptr)
   if (dtype == KVQ_F16) {
-    if (nf) KVQ_LAUNCH_Q(__half, true); else KVQ_LAUNCH_Q(__half, false);
+    if (nf) KVQ_LAUNCH_Q(__half, true, false); else if (rotk) KVQ_LAUNCH_Q(__half, false, true); else KVQ_LAUNCH_Q(__half, false, false);
   } else {
-    if (nf) KVQ_LAUNCH_Q(float, true); else KVQ_LAUNCH_Q(float, false);
+    if (nf) KVQ_LAUNCH_Q(float, true, false); else if (rotk) KVQ_LAUNCH_Q(float, false, true); else KVQ_LAUNCH_Q(float, false, false);
   }
 #undef KVQ_LAUNCH_Q
   return hipGetLastError();
