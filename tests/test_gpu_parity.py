@@ -33,7 +33,7 @@ def _kvq():
 
 def run_case(wname, T, k_bits, v_bits, codec="bgtq", pairing="half", batch=None, layer=0,
              chunks=None, n_splits=0, noise="gauss", temper=False, check_codes=True, sample_rows=None,
-             b_min=0, b_max=8, fidelity=True, recent=0, query_weighted=False):
+             b_min=0, b_max=8, fidelity=True, recent=0, query_weighted=False, zero_blocks=()):
     """Quantize T tokens of one layer on the GPU and in the oracle; compare everything.
 
     recent > 0: the last `recent` positions stay in the fp16 window.  A position that was inside
@@ -51,6 +51,12 @@ def run_case(wname, T, k_bits, v_bits, codec="bgtq", pairing="half", batch=None,
         vs.append(v)
         qs.append(gen_query(w, layer, T, seq=b, noise=noise, pairing=pairing))
     K = np.stack(ks)            # [B, T, H, d]
+    if zero_blocks:
+        # degenerate blocks: both coordinates zero in every key (zero energy, zero gain)
+        p0, p1 = al.block_pairs(128, pairing)
+        for j in zero_blocks:
+            K[..., p0[j]] = 0
+            K[..., p1[j]] = 0
     V = np.stack(vs)
     Q = np.stack(qs)            # [B, Hq, d]
     print(f"[{wname} T={T} K{k_bits}V{v_bits} {codec}] inputs generated", flush=True)
@@ -270,6 +276,15 @@ def test_rotated_uniform_codec(kb):
 
 def test_rotated_uniform_codec_recent_window():
     run_case("qwen3b_128k", 5000, 3, 3, codec="rot", chunks=[2048, 2951, 1], recent=256)
+
+
+def test_zero_energy_blocks():
+    """Blocks that are zero in every key get zero energy, no bits and a zero gain."""
+    run_case("llama8b_32k", 1500, 3, 3, zero_blocks=(0, 5, 63), temper=True)
+
+
+def test_largest_recent_window():
+    run_case("qwen3b_128k", 6000, 3, 3, chunks=[2048, 3951, 1], recent=4096)
 
 
 def test_b_min_b_max_limits():
