@@ -802,16 +802,17 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
       const float p0 = __builtin_amdgcn_exp2f(L0[tg] - mn0), p1 = __builtin_amdgcn_exp2f(L1[tg] - mn1);
       l0 += p0;
       l1 += p1;
-      const float q0 = p0 * sv, q1 = p1 * sv;
-      const _Float16 q0h = static_cast<_Float16>(q0), q1h = static_cast<_Float16>(q1);
+      // weight p s^V as fp16 hi + lo: hi = fp16(p s^V), lo = fp16(p s^V - hi) with the product
+      // kept exact inside one fused operation (one mixed-precision instruction each)
+      const _Float16 q0h = static_cast<_Float16>(p0 * sv), q1h = static_cast<_Float16>(p1 * sv);
       const int t = 16 * tg + n;
       if (vh0) {
         pw[h0 * kPS + t] = q0h;
-        pw[(G + h0) * kPS + t] = static_cast<_Float16>(q0 - static_cast<float>(q0h));
+        pw[(G + h0) * kPS + t] = static_cast<_Float16>(__builtin_fmaf(p0, sv, -static_cast<float>(q0h)));
       }
       if (vh1) {
         pw[h1 * kPS + t] = q1h;
-        pw[(G + h1) * kPS + t] = static_cast<_Float16>(q1 - static_cast<float>(q1h));
+        pw[(G + h1) * kPS + t] = static_cast<_Float16>(__builtin_fmaf(p1, sv, -static_cast<float>(q1h)));
       }
     }
     if (n == 0) {
