@@ -176,10 +176,15 @@ __global__ __launch_bounds__(kThreads) void quantize_append(
         for (int i = 0; i < kHeadDim; ++i) a = fmaxf(a, fabsf(xval(tsr, hh, r, i)));
       s16 = __float2half_rn(a);
     } else {
+      // one code path for K and V lanes (no branch per element), so the LDS reads of a batch
+      // are issued together and only the fp64 sum is a dependent chain
       double ss = 0.0;
+      const float* krot = nullptr;
+      if constexpr (ROT) krot = &ky_s[r][0];
+#pragma unroll 16
       for (int i = 0; i < kHeadDim; ++i) {
-        const float x = tsr == 0 ? kval(r, i) : xval(tsr, hsel, r, i);
-        const double y = static_cast<double>(tsr == 0 ? __fmul_rn(x, ig_s[i]) : x);
+        const float x = (ROT && tsr == 0) ? krot[i] : xval(tsr, hsel, r, i);
+        const double y = static_cast<double>(__fmul_rn(x, tsr == 0 ? ig_s[i] : 1.0f));
         ss = __dadd_rn(ss, __dmul_rn(y, y));
       }
       s16 = __float2half_rn(static_cast<float>(__dsqrt_rn(ss / static_cast<double>(kHeadDim))));
