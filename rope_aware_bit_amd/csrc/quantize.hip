@@ -203,54 +203,64 @@ __global__ __launch_bounds__(kThreads) void quantize_append(
   }
   __syncthreads();
 
-  // ---- 3. codes: element e = tid + 256 m is K (field e / 8, token e % 8) and V (dim e / 8,
-  //      token e % 8); the eight searches of a thread advance in lock step ----
+  // ---- 3. codes.  K: wave w takes the plan's fields 32 w .. 32 w + 31 (fields are in plan
+  //      order, widest first), lane l fields 32 w + l / 8 + 8 m and token l % 8, so the wave's
+  //      searches need only as many steps as its first field's width.  V: element e = tid +
+  //      256 m is dim e / 8, token e % 8 (v_bits steps).  The four searches of a thread of each
+  //      kind advance in lock step. ----
   const int nfld = nf_s;
+  const int wv = tid >> 6, ln = tid & 63;
   uint32_t pos[2 * kEl], tb[2 * kEl];
-  int wd[2 * kEl];
+  int wd[2 * kEl], fk[kEl];
   float u[2 * kEl];
 #pragma unroll
   for (int m = 0; m < kEl; ++m) {
-    const int e = tid + kThreads * m, f = e / kGroupTok, r = e % kGroupTok;
-    const bool live = r >= lo && r < hi;
-    const bool kl = live && f < nfld;
+    const int f = 32 * wv + (ln >> 3) + 8 * m, r = ln & 7;   // K element
+    const bool kl = r >= lo && r < hi && f < nfld;
     const int i = kl ? fdim_s[f] : 0;
     const int w = kl ? fw_s[f] : 0;
     const float x = kval(r, i);
     const float y = NF ? x : __fmul_rn(x, ig_s[i]);
     u[m] = __fmul_rn(y, isk_s[r]);
     wd[m] = w;
+    fk[m] = f;
     tb[m] = static_cast<uint32_t>(w) * 256u;
     pos[m] = 0u;
-    u[kEl + m] = __fmul_rn(xval(1, hsel, r, f), isv_s[r]);   // V: dim f
-    wd[kEl + m] = live ? vb : 0;
+    const int e = tid + kThreads * m, fv = e / kGroupTok, rv = e % kGroupTok;   // V element
+    const bool vl = rv >= lo && rv < hi;
+    u[kEl + m] = __fmul_rn(xval(1, hsel, rv, fv), isv_s[rv]);
+    wd[kEl + m] = vl ? vb : 0;
     tb[kEl + m] = static_cast<uint32_t>(vb) * 256u;
     pos[kEl + m] = 0u;
   }
-  const int steps = nfld > 0 && fw_s[0] > vb ? fw_s[0] : vb;   // plan order: widest field first
-  for (int st = 0; st < steps; ++st) {
+  auto search = [&](int m0, int steps) {
+    for (int st = 0; st < steps; ++st) {
 #pragma unroll
-    for (int m = 0; m < 2 * kEl; ++m) {
-      const int sh = wd[m] - 1 - st;
-      const uint32_t step = sh >= 0 ? 1u << sh : 0u;
-      const float bdv = bd_s[tb[m] + pos[m] + (step ? step : 1u) - 1u];
-      pos[m] += (step != 0u && bdv < u[m]) ? step : 0u;
+      for (int m = m0; m < m0 + kEl; ++m) {
+        const int sh = wd[m] - 1 - st;
+        const uint32_t step = sh >= 0 ? 1u << sh : 0u;
+        const float bdv = bd_s[tb[m] + pos[m] + (step ? step : 1u) - 1u];
+        pos[m] += (step != 0u && bdv < u[m]) ? step : 0u;
+      }
     }
-  }
+  };
+  search(0, 32 * wv < nfld ? fw_s[32 * wv] : 0);   // wave-uniform: the widest field of the wave
+  search(kEl, vb);
 #pragma unroll
   for (int m = 0; m < kEl; ++m) {
-    const int e = tid + kThreads * m, f = e / kGroupTok, r = e % kGroupTok;
     if (wd[m] > 0) {   // K code into its row word(s)
+      const int f = fk[m], r = ln & 7;
       const int off = foff_s[f], w = wd[m];
       const int word = off >> 5, sh = off & 31;
       atomicOr(&krow_s[r * k_words + word], pos[m] << sh);
       if (sh + w > 32) atomicOr(&krow_s[r * k_words + word + 1], pos[m] >> (32 - sh));
     }
     if (wd[kEl + m] > 0) {   // V code into its segment word(s)
-      const int bit = (eb + r) * vb - 32 * vw0, word = bit >> 5, sh = bit & 31;
+      const int e = tid + kThreads * m, fv = e / kGroupTok, rv = e % kGroupTok;
+      const int bit = (eb + rv) * vb - 32 * vw0, word = bit >> 5, sh = bit & 31;
       const uint32_t code = pos[kEl + m];
-      atomicOr(&vw_s[f][word], code << sh);
-      if (sh + vb > 32) atomicOr(&vw_s[f][word + 1], code >> (32 - sh));
+      atomicOr(&vw_s[fv][word], code << sh);
+      if (sh + vb > 32) atomicOr(&vw_s[fv][word + 1], code >> (32 - sh));
     }
   }
   __syncthreads();
