@@ -141,6 +141,7 @@ def main():
 
     from rope_aware_bit_amd import kvq
     from synth import WORKLOADS
+    from synth import gen_query as gen_query_np
     from synth.torch_gen import TorchLayerGen
 
     w = WORKLOADS[args.workload]
@@ -243,6 +244,35 @@ def main():
                                "GB/s": round(vbytes / (us * 1e-6) / 1e9, 2)}
             vc.close()
         del v0d
+
+    # batched decode at the Llama-3.1-8B shape of the batch-64 workload (64 x 8192 tokens,
+    # 8 KV / 32 query heads, K4V4): one layer, every sequence holding the same synthetic data
+    if not args.decode_only:
+        wb = WORKLOADS["llama8b_b64"]
+        gb = TorchLayerGen(wb, dev)
+        kb0, vb0 = gb.layer(0)
+        bc = kvq.Cache(kvq.Config(1, wb.n_kv, wb.n_q, wb.batch, wb.T, 4, 4))
+        bc.alloc_bits(0, kb0[:wb.calib_tokens])
+        bc.quantize_append(0, kb0[None].expand(wb.batch, -1, -1, -1).contiguous(),
+                           vb0[None].expand(wb.batch, -1, -1, -1).contiguous())
+        del kb0, vb0
+        qb = torch.from_numpy(np.stack([np.asarray(gen_query_np(wb, 0, wb.T, seq=i)) for i in range(wb.batch)])).to(dev)
+        ob = torch.empty(wb.batch, wb.n_q, 128, dtype=torch.float32, device=dev)
+        for _ in range(5):
+            bc.decode_attn(0, qb, out=ob)
+        torch.cuda.synchronize()
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        for _ in range(20):
+            bc.decode_attn(0, qb, out=ob)
+        a1.record(stream)
+        torch.cuda.synchronize()
+        us = a0.elapsed_time(a1) * 1e3 / 20
+        bbytes = wb.batch * wb.n_kv * wb.T * (8 * 16 + 4) + wb.batch * wb.n_q * 128 * 6 + wb.n_kv * PLAN_BYTES_PER_HEAD
+        variants["llama8b_b64_K4V4"] = {"batch": wb.batch, "context": wb.T, "us_per_launch": round(us, 2),
+                                        "GB/s": round(bbytes / (us * 1e-6) / 1e9, 2),
+                                        "frac_of_hbm_peak": round(bbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        bc.close()
 
     # key-fidelity diagnostics of layer 0 (logit MAE and softmax KL against the given keys)
     fid_reps = 0 if args.decode_only else 5
