@@ -91,6 +91,9 @@ typedef struct {
                             packed cache; 0 = none.  The paper's own results use none (RoPE-
                             aware bit allocation page, abstract: "without an fp16 recent-key
                             buffer"); the leaderboard's "Buffer Setting" is this option. */
+  int32_t per_sequence_plans; /* 0: one plan per (layer, KV head), shared by the batch; 1: one
+                            plan per (layer, sequence, KV head), each from that sequence's own
+                            calibration keys (see kvq_alloc_bits) */
 } kvq_config;
 
 /* Layout facts of one layer's packed storage, for parity dumps (see kvq_read_cache). */
@@ -139,10 +142,12 @@ void kvq_cache_destroy(kvq_cache* cache);
    alone, then integer widths are handed out one step at a time to the block
    whose marginal gain is largest).
    keys:   [n_tok][n_kv_heads][128] post-RoPE calibration keys (dtype), n_tok >= 1,
-           16-byte aligned.
+           16-byte aligned; with per_sequence_plans, [batch][n_tok][n_kv_heads][128]
+           (n_tok keys of every sequence, each sequence's plans from its own keys).
            May be NULL for the UNIFORM and NF16 codecs, whose plans are fixed.
-   block_weight: NULL, or a device fp64 array [n_kv_heads][64] of per-block
-           weights multiplying the energy score before the greedy.
+   block_weight: NULL, or a device fp64 array [n_kv_heads][64] ([batch][n_kv_heads][64]
+           with per_sequence_plans) of per-block weights multiplying the energy score
+           before the greedy.
    Computes m_j = sum over tokens of the block's squared norm / (2 n_tok) in fp64
    (terms summed in token order inside 256-token chunks, then chunk totals in
    order), widths b_j in [b_min, b_max] with sum_j 2 b_j = 128 k_bits by
@@ -154,8 +159,9 @@ kvq_status kvq_alloc_bits(kvq_cache* cache, int32_t layer, const void* keys, int
                           int64_t n_tok, const double* block_weight, kvq_stream stream);
 
 /* Copy one layer's plan to host memory.  Synchronizes the device.
-   bits:  host int8 [n_kv_heads][64] per-block widths (required).
-   gains: host fp32 [n_kv_heads][64] per-block gains g_j (nullable).
+   bits:  host int8 [n_kv_heads][64] per-block widths (required); with
+          per_sequence_plans [batch][n_kv_heads][64].
+   gains: host fp32, same shape as bits: per-block gains g_j (nullable).
    Errors: KVQ_EINVAL, KVQ_ESTATE (no plan yet), KVQ_EHIP. */
 kvq_status kvq_get_plan(const kvq_cache* cache, int32_t layer, int8_t* bits, float* gains);
 

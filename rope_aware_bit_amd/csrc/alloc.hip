@@ -4,6 +4,9 @@
 // frequency block of each (layer, KV head) gets an energy score computed from
 // keys alone; integer widths are then raised greedily by marginal gain.
 //
+// With per-sequence plans every sequence's calibration keys give a plan of their own: the
+// kernels below run once per (sequence, KV head) instead of once per KV head.
+//
 // Kernel 1 (energy_chunks): one workgroup per (256-token chunk, KV head).  The
 // chunk's keys of that head are first copied into LDS with coalesced loads (one
 // round of memory latency); lane j then sums block j's squared norm over the
@@ -45,6 +48,8 @@ __global__ __launch_bounds__(256) void energy_chunks(const T* __restrict__ keys,
   const int tid = threadIdx.x, j = tid;
   const int h = blockIdx.y;
   const int64_t c = blockIdx.x;
+  const int64_t u = static_cast<int64_t>(blockIdx.z) * n_kv + h;   // (sequence, head) unit
+  keys += static_cast<int64_t>(blockIdx.z) * n_tok * n_kv * kHeadDim;
   const int p0 = pairing == KVQ_ROPE_HALF ? j : 2 * j;
   const int p1 = pairing == KVQ_ROPE_HALF ? j + kBlocks : 2 * j + 1;
   __shared__ T x_s[kEnergyTok][kHeadDim + 16 / sizeof(T)];   // padded rows
@@ -70,7 +75,7 @@ __global__ __launch_bounds__(256) void energy_chunks(const T* __restrict__ keys,
     }
     __syncthreads();
   }
-  if (j < kBlocks) scratch[(static_cast<int64_t>(h) * n_chunks + c) * kBlocks + j] = acc;
+  if (j < kBlocks) scratch[(u * n_chunks + c) * kBlocks + j] = acc;
 }
 
 __global__ __launch_bounds__(512) void greedy_plan(const double* __restrict__ scratch, int64_t n_chunks,
@@ -80,6 +85,7 @@ __global__ __launch_bounds__(512) void greedy_plan(const double* __restrict__ sc
                                                    Plan* __restrict__ plans) {
   const int tid = threadIdx.x;
   const int h = blockIdx.x;
+  const int64_t u = static_cast<int64_t>(blockIdx.y) * gridDim.x + h;   // (sequence, head) unit
   __shared__ double m_s[kBlocks];
   __shared__ int w_s[kBlocks];
   __shared__ double cand_s[kBlocks * kMaxBits];   // candidate gains, then sorted
@@ -95,7 +101,7 @@ __global__ __launch_bounds__(512) void greedy_plan(const double* __restrict__ sc
     if (bgtq) {
       double S = 0.0;
       for (int64_t c = 0; c < n_chunks; ++c)
-        S = __dadd_rn(S, scratch[(static_cast<int64_t>(h) * n_chunks + c) * kBlocks + j]);
+        S = __dadd_rn(S, scratch[(u * n_chunks + c) * kBlocks + j]);
       m = __ddiv_rn(S, 2.0 * static_cast<double>(n_tok));
     }
     m_s[j] = m;
@@ -108,7 +114,7 @@ __global__ __launch_bounds__(512) void greedy_plan(const double* __restrict__ sc
     const int j = tid >> 3, b = tid & 7;
     const double m = m_s[j];
     // equal scores make the greedy hand out a uniform width (UNIFORM and NF16 plans)
-    const double sj = bgtq ? (weight ? __dmul_rn(m, weight[h * kBlocks + j]) : m) : 1.0;
+    const double sj = bgtq ? (weight ? __dmul_rn(m, weight[u * kBlocks + j]) : m) : 1.0;
     cand_s[tid] = (b >= b_min && b < b_max) ? __dmul_rn(sj, static_cast<double>(tab->delta[b])) : -INFINITY;
     cid_s[tid] = tid;
   }
@@ -177,7 +183,7 @@ __global__ __launch_bounds__(512) void greedy_plan(const double* __restrict__ sc
   }
   const int p0 = pairing == KVQ_ROPE_HALF ? j : 2 * j;
   const int p1 = pairing == KVQ_ROPE_HALF ? j + kBlocks : 2 * j + 1;
-  Plan* P = plans + h;
+  Plan* P = plans + u;
   // fields past n_fields are zero: every lane first clears two slots, then writes its own
   if (act) {
     P->fdim[2 * j] = P->fdim[2 * j + 1] = 0;
@@ -214,7 +220,7 @@ hipError_t launch_alloc(kvq_cache* c, int layer, const void* keys, int dtype, in
   const bool bgtq = cfg.codec == KVQ_CODEC_BGTQ;
   const int64_t n_chunks = bgtq ? (n_tok + kEnergyChunk - 1) / kEnergyChunk : 0;
   if (bgtq) {
-    dim3 grid(static_cast<unsigned>(n_chunks), static_cast<unsigned>(H));
+    dim3 grid(static_cast<unsigned>(n_chunks), static_cast<unsigned>(H), static_cast<unsigned>(c->n_plan));
     if (dtype == KVQ_F16)
       hipLaunchKernelGGL(energy_chunks<__half>, grid, dim3(256), 0, stream,
                          static_cast<const __half*>(keys), n_tok, H, cfg.pairing, c->energy_scratch,
@@ -229,9 +235,9 @@ hipError_t launch_alloc(kvq_cache* c, int layer, const void* keys, int dtype, in
   const int k_bits = cfg.codec == KVQ_CODEC_NF16_B256 ? 4 : cfg.k_bits;
   const int b_min = bgtq ? cfg.b_min : 0;
   const int b_max = bgtq ? cfg.b_max : kMaxBits;
-  hipLaunchKernelGGL(greedy_plan, dim3(H), dim3(kBlocks * kMaxBits), 0, stream, c->energy_scratch, n_chunks, n_tok,
+  hipLaunchKernelGGL(greedy_plan, dim3(H, c->n_plan), dim3(kBlocks * kMaxBits), 0, stream, c->energy_scratch, n_chunks, n_tok,
                      block_weight, k_bits, b_min, b_max, cfg.codec, cfg.pairing, c->tables,
-                     c->plans + static_cast<int64_t>(layer) * H);
+                     c->plans + static_cast<int64_t>(layer) * c->n_plan * H);
   return hipGetLastError();
 }
 

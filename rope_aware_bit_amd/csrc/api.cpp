@@ -34,6 +34,7 @@ bool config_valid(const kvq_config* c) {
   if (c->codec < KVQ_CODEC_BGTQ || c->codec > KVQ_CODEC_UNIFORM_ROT) return false;
   if (c->recent_window < 0 || c->recent_window > kvq::kMaxRecent || c->recent_window % 128) return false;
   if (c->pairing != KVQ_ROPE_HALF && c->pairing != KVQ_ROPE_INTERLEAVED) return false;
+  if (c->per_sequence_plans != 0 && c->per_sequence_plans != 1) return false;
   if (c->v_bits < 1 || c->v_bits > kMaxBits) return false;
   if (c->b_min < 0 || c->b_max > kMaxBits || c->b_min > c->b_max) return false;
   if (c->k_bits < 1 || c->k_bits < c->b_min || c->k_bits > c->b_max) return false;
@@ -118,6 +119,7 @@ kvq_status kvq_cache_create(const kvq_config* cfg, kvq_cache** out) {
   std::memset(static_cast<void*>(c), 0, sizeof(kvq_cache));
   c->cfg = *cfg;
   c->group = cfg->n_q_heads / cfg->n_kv_heads;
+  c->n_plan = cfg->per_sequence_plans ? cfg->batch : 1;
   c->cap = (cfg->max_tokens + kVTile - 1) / kVTile * kVTile;
   const bool nf = cfg->codec == KVQ_CODEC_NF16_B256;
   c->k_words = 4 * (nf ? 4 : cfg->k_bits);
@@ -159,7 +161,7 @@ kvq_status kvq_cache_create(const kvq_config* cfg, kvq_cache** out) {
     st = dev_alloc(reinterpret_cast<void**>(&c->k_recent), c->recent_layer * L, "recent K");
     if (st == KVQ_OK) st = dev_alloc(reinterpret_cast<void**>(&c->v_recent), c->recent_layer * L, "recent V");
   }
-  if (st == KVQ_OK) st = dev_alloc(reinterpret_cast<void**>(&c->plans), sizeof(kvq::Plan) * L * H, "plans");
+  if (st == KVQ_OK) st = dev_alloc(reinterpret_cast<void**>(&c->plans), sizeof(kvq::Plan) * L * c->n_plan * H, "plans");
   if (st == KVQ_OK && cfg->codec == KVQ_CODEC_UNIFORM_ROT)
     st = dev_alloc(reinterpret_cast<void**>(&c->rot_signs), L * H * kHeadDim, "rotation signs");
   if (st == KVQ_OK) st = dev_alloc(reinterpret_cast<void**>(&c->tables), sizeof(kvq::Tables), "tables");
@@ -187,7 +189,7 @@ kvq_status kvq_cache_create(const kvq_config* cfg, kvq_cache** out) {
         hipMemset(c->v_scales, 0, c->v_scales_layer * L),
         c->k_recent ? hipMemset(c->k_recent, 0, c->recent_layer * L) : hipSuccess,
         c->v_recent ? hipMemset(c->v_recent, 0, c->recent_layer * L) : hipSuccess,
-        hipMemset(c->plans, 0, sizeof(kvq::Plan) * L * H),
+        hipMemset(c->plans, 0, sizeof(kvq::Plan) * L * c->n_plan * H),
         hipMemcpy(c->tables, &c->host_tables, sizeof(kvq::Tables), hipMemcpyHostToDevice),
         hipDeviceSynchronize()};
     for (hipError_t x : es)
@@ -225,7 +227,7 @@ kvq_status kvq_alloc_bits(kvq_cache* c, int32_t layer, const void* keys, int32_t
     g_last_error = "alloc_bits: keys must be 16-byte aligned";
     return KVQ_EINVAL;
   }
-  if (bgtq && n_tok > (int64_t(1) << 31)) return KVQ_EINVAL;
+  if (bgtq && n_tok * c->n_plan > (int64_t(1) << 31)) return KVQ_EINVAL;
   if (c->len[layer] > 0) return KVQ_ESTATE;
   if (bgtq) {
     const int64_t n_chunks = (n_tok + kvq::kEnergyChunk - 1) / kvq::kEnergyChunk;
@@ -240,7 +242,7 @@ kvq_status kvq_alloc_bits(kvq_cache* c, int32_t layer, const void* keys, int32_t
         c->energy_scratch_chunks = 0;
       }
       kvq_status st = dev_alloc(reinterpret_cast<void**>(&c->energy_scratch),
-                                sizeof(double) * n_chunks * c->cfg.n_kv_heads * kBlocks, "energy scratch");
+                                sizeof(double) * n_chunks * c->n_plan * c->cfg.n_kv_heads * kBlocks, "energy scratch");
       if (st != KVQ_OK) return st;
       c->energy_scratch_chunks = n_chunks;
     }
@@ -255,7 +257,7 @@ kvq_status kvq_alloc_bits(kvq_cache* c, int32_t layer, const void* keys, int32_t
 kvq_status kvq_get_plan(const kvq_cache* c, int32_t layer, int8_t* bits, float* gains) {
   if (!layer_ok(c, layer) || !bits) return KVQ_EINVAL;
   if (!c->plan_ready[layer]) return KVQ_ESTATE;
-  const int H = c->cfg.n_kv_heads;
+  const int H = c->n_plan * c->cfg.n_kv_heads;   // (sequence,) head units of the layer
   hipError_t e = hipDeviceSynchronize();
   if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
   for (int h = 0; h < H; ++h) {

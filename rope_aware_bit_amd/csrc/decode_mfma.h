@@ -420,7 +420,7 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     const void* __restrict__ qv, int q_f32, float sigma, int64_t len, int n_packed_splits,
     const __half* __restrict__ rk, const __half* __restrict__ rv, int R, int64_t n_recent,
     const int8_t* __restrict__ rot, int n_kv, int64_t cap,
-    int tiles_per_split, const Plan* __restrict__ plans, const Tables* __restrict__ tabg,
+    int tiles_per_split, const Plan* __restrict__ plans, int plan_bs, const Tables* __restrict__ tabg,
     const uint32_t* __restrict__ kc, const uint32_t* __restrict__ vc, const uint16_t* __restrict__ ks,
     const uint16_t* __restrict__ vs, int k_words, int n_nf, int n_splits, int n_mergers, int region_words,
     int v_early, int v_off, float* __restrict__ part_o, float* __restrict__ part_l,
@@ -468,7 +468,7 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   const int64_t n_tiles = (len + kVTile - 1) / kVTile;
   const int64_t t_begin = recent_wg ? n_tiles : static_cast<int64_t>(s) * tiles_per_split;
   const int64_t t_end = recent_wg ? n_tiles : (t_begin + tiles_per_split < n_tiles ? t_begin + tiles_per_split : n_tiles);
-  const Plan* P = plans + h;
+  const Plan* P = plans + static_cast<int64_t>(b) * plan_bs + h;   // plan of (sequence, head)
 
   // ---- set-up loads first (small and shared by every workgroup), then the first tile's.
   //      Every load is unconditional (clamped indices; waves 4..7 repeat those of waves 0..3
@@ -1066,13 +1066,14 @@ hipError_t launch_gvw(kvq_cache* c, int layer, const void* q, int q_f32, float s
   const int8_t* rot = cfg.codec == KVQ_CODEC_UNIFORM_ROT ? c->rot_signs + static_cast<int64_t>(layer) * cfg.n_kv_heads * kHeadDim : nullptr;
   dim3 grid(S_all, cfg.n_kv_heads, cfg.batch);
   const size_t dyn = static_cast<size_t>(W) * sh.region_words * sizeof(uint32_t);
-  const Plan* plans = c->plans + static_cast<int64_t>(layer) * cfg.n_kv_heads;
+  const Plan* plans = c->plans + static_cast<int64_t>(layer) * c->n_plan * cfg.n_kv_heads;
+  const int plan_bs = c->n_plan > 1 ? cfg.n_kv_heads : 0;
   const bool nf = cfg.codec == KVQ_CODEC_NF16_B256;
   const int mergers = decode_split_mergers(S_all, static_cast<int64_t>(cfg.batch) * cfg.n_kv_heads, c->n_cu);
   if constexpr (VB == 4) {
     if (nf) {
       hipLaunchKernelGGL((decode_mfma<G, 4, true, W>), grid, dim3(64 * W), dyn, stream, q, q_f32, sigma,
-                         plen, S, rk, rv, R, n_recent, rot, cfg.n_kv_heads, c->cap, tps, plans, c->tables, layer_k_codes(c, layer),
+                         plen, S, rk, rv, R, n_recent, rot, cfg.n_kv_heads, c->cap, tps, plans, plan_bs, c->tables, layer_k_codes(c, layer),
                          layer_v_codes(c, layer), layer_k_scales(c, layer), layer_v_scales(c, layer),
                          c->k_words, c->n_nf_blocks, S_all, mergers, sh.region_words, sh.v_early, sh.v_off,
                          c->part_o, c->part_l, c->part_mt, c->split_epochs, out);
@@ -1080,7 +1081,7 @@ hipError_t launch_gvw(kvq_cache* c, int layer, const void* q, int q_f32, float s
     }
   }
   hipLaunchKernelGGL((decode_mfma<G, VB, false, W>), grid, dim3(64 * W), dyn, stream, q, q_f32, sigma,
-                     plen, S, rk, rv, R, n_recent, rot, cfg.n_kv_heads, c->cap, tps, plans, c->tables, layer_k_codes(c, layer),
+                     plen, S, rk, rv, R, n_recent, rot, cfg.n_kv_heads, c->cap, tps, plans, plan_bs, c->tables, layer_k_codes(c, layer),
                      layer_v_codes(c, layer), layer_k_scales(c, layer), layer_v_scales(c, layer),
                      c->k_words, c->n_nf_blocks, S_all, mergers, sh.region_words, sh.v_early, sh.v_off,
                      c->part_o, c->part_l, c->part_mt, c->split_epochs, out);

@@ -113,7 +113,7 @@ __device__ inline Stats stats_shfl_xor(const Stats& s, int mask) {
 template <typename T, int G>
 __global__ __launch_bounds__(256, 2) void fidelity_partials(
     const T* __restrict__ q, const T* __restrict__ keys, int64_t len, int n_kv, int64_t cap,
-    double sigma, int64_t tok_per_split, const Plan* __restrict__ plans, const Tables* __restrict__ tab,
+    double sigma, int64_t tok_per_split, const Plan* __restrict__ plans, int plan_bs, const Tables* __restrict__ tab,
     const uint32_t* __restrict__ kc, const uint16_t* __restrict__ ks, int k_words, int n_nf, int nf,
     int64_t plen, const __half* __restrict__ rk, int R, const int8_t* __restrict__ rot,
     double* __restrict__ part, int S) {
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(256, 2) void fidelity_partials(
   __shared__ double sc_s[kFidTok];
   __shared__ int nf_s;
 
-  const Plan* P = plans + h;
+  const Plan* P = plans + static_cast<int64_t>(b) * plan_bs + h;   // plan of (sequence, head)
   for (int k = tid; k < G * kHeadDim; k += 256)
     q_s[k / kHeadDim][k % kHeadDim] = to_d(q[(static_cast<int64_t>(b) * n_kv * G + h * G) * kHeadDim + k]);
   for (int k = tid; k < (kMaxBits + 1) * 256; k += 256) {
@@ -357,11 +357,12 @@ hipError_t launch_fidelity(kvq_cache* c, int layer, const void* q, const void* k
   S = (len + per - 1) / per;
   const double sigma = scale > 0.0f ? static_cast<double>(scale) : 1.0 / std::sqrt(static_cast<double>(kHeadDim));
   const bool nf = cfg.codec == KVQ_CODEC_NF16_B256;
-  const Plan* plans = c->plans + static_cast<int64_t>(layer) * H;
+  const Plan* plans = c->plans + static_cast<int64_t>(layer) * c->n_plan * H;
+  const int plan_bs = c->n_plan > 1 ? H : 0;
   dim3 grid(static_cast<unsigned>(S), static_cast<unsigned>(H), static_cast<unsigned>(B));
 #define KVQ_FID(T, GG)                                                                              \
   hipLaunchKernelGGL((fidelity_partials<T, GG>), grid, dim3(256), 0, stream, static_cast<const T*>(q), \
-                     static_cast<const T*>(keys), len, H, c->cap, sigma, per, plans, c->tables,       \
+                     static_cast<const T*>(keys), len, H, c->cap, sigma, per, plans, plan_bs, c->tables, \
                      layer_k_codes(c, layer), layer_k_scales(c, layer), c->k_words, c->n_nf_blocks,   \
                      nf ? 1 : 0, plen, plen < len ? layer_k_recent(c, layer) : nullptr,       \
                      c->cfg.recent_window > 0 ? c->cfg.recent_window : 1,                         \

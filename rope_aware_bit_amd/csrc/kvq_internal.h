@@ -78,7 +78,8 @@ struct kvq_cache {
   uint16_t* v_scales;
   __half* k_recent;            // recent-window rings [L][B][R][H][128] fp16 (R > 0)
   __half* v_recent;
-  kvq::Plan* plans;            // [L][H]
+  kvq::Plan* plans;            // [L][n_plan][H]
+  int n_plan;                  // plans per (layer, KV head): batch with per-sequence plans, else 1
   int8_t* rot_signs;           // key-rotation signs [L][H][128] (codec UNIFORM_ROT)
   uint8_t* rot_ready;          // per layer: signs set
   kvq::Tables* tables;         // device copy

@@ -48,7 +48,7 @@ __device__ inline float inv_scale(__half s16) {
 template <typename T, bool NF, bool ROT>
 __global__ __launch_bounds__(kThreads) void quantize_append(
     const T* __restrict__ kin, const T* __restrict__ vin, int64_t n_new, int64_t in_stride, int ring_R, int64_t L0, int n_kv,
-    int64_t cap, const Plan* __restrict__ plans, const Tables* __restrict__ tab,
+    int64_t cap, const Plan* __restrict__ plans, int plan_bs, const Tables* __restrict__ tab,
     uint32_t* __restrict__ kc, uint32_t* __restrict__ vc, uint16_t* __restrict__ ks,
     uint16_t* __restrict__ vs, int k_words, int v_bits, int n_nf, const int8_t* __restrict__ rot) {
   constexpr int kVec = 16 / sizeof(T);            // elements per 16-byte load
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(kThreads) void quantize_append(
       d[3] = v4.w;
     }
   }
-  const Plan* P = plans + h;
+  const Plan* P = plans + static_cast<int64_t>(b) * plan_bs + h;   // plan of (sequence, head)
   for (int k = tid; k < (kMaxBits + 1) * 256; k += kThreads) {
     const int bb = k >> 8, e = k & 255;
     bd_s[k] = NF ? (bb == 4 && e < 16 ? tab->nf_bd[e] : INFINITY) : tab->bd[bb][e];
@@ -292,11 +292,12 @@ hipError_t launch_quantize(kvq_cache* c, int layer, const void* k, const void* v
             static_cast<unsigned>(cfg.batch));
   const bool nf = cfg.codec == KVQ_CODEC_NF16_B256;
   const bool rotk = cfg.codec == KVQ_CODEC_UNIFORM_ROT;
-  const Plan* plans = c->plans + static_cast<int64_t>(layer) * cfg.n_kv_heads;
+  const Plan* plans = c->plans + static_cast<int64_t>(layer) * c->n_plan * cfg.n_kv_heads;
+  const int plan_bs = c->n_plan > 1 ? cfg.n_kv_heads : 0;
 #define KVQ_LAUNCH_Q(T, NF, ROT)                                                                 \
   hipLaunchKernelGGL((quantize_append<T, NF, ROT>), grid, dim3(kThreads), 0, stream,            \
                      static_cast<const T*>(k), static_cast<const T*>(v), n_new, in_stride, ring_R, L0, \
-                     cfg.n_kv_heads, c->cap, plans, c->tables, layer_k_codes(c, layer),          \
+                     cfg.n_kv_heads, c->cap, plans, plan_bs, c->tables, layer_k_codes(c, layer), \
                      layer_v_codes(c, layer), layer_k_scales(c, layer), layer_v_scales(c, layer), \
                      c->k_words, cfg.v_bits, c->n_nf_blocks,                                      \
                      cfg.codec == KVQ_CODEC_UNIFORM_ROT ? c->rot_signs + static_cast<int64_t>(layer) * cfg.n_kv_heads * kHeadDim : nullptr)

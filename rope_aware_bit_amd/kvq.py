@@ -42,7 +42,7 @@ class kvq_config(ctypes.Structure):
         ("head_dim", ctypes.c_int32), ("batch", ctypes.c_int32), ("max_tokens", ctypes.c_int64),
         ("k_bits", ctypes.c_int32), ("v_bits", ctypes.c_int32), ("b_min", ctypes.c_int32),
         ("b_max", ctypes.c_int32), ("codec", ctypes.c_int32), ("pairing", ctypes.c_int32),
-        ("recent_window", ctypes.c_int32),
+        ("recent_window", ctypes.c_int32), ("per_sequence_plans", ctypes.c_int32),
     ]
 
 
@@ -163,11 +163,12 @@ class Config:
     codec: int = CODEC_BGTQ
     pairing: int = ROPE_HALF
     recent_window: int = 0
+    per_sequence_plans: int = 0
 
     def to_c(self) -> kvq_config:
         return kvq_config(self.n_layers, self.n_kv_heads, self.n_q_heads, self.head_dim, self.batch,
                           self.max_tokens, self.k_bits, self.v_bits, self.b_min, self.b_max,
-                          self.codec, self.pairing, self.recent_window)
+                          self.codec, self.pairing, self.recent_window, self.per_sequence_plans)
 
 
 def create_status(cfg: Config) -> int:
@@ -205,9 +206,18 @@ class Cache:
         return self._h
 
     def alloc_bits(self, layer: int, keys=None, block_weight=None, stream=None):
+        """keys: [n_tok, n_kv_heads, head_dim], or [batch, n_tok, n_kv_heads, head_dim] with
+        per-sequence plans; block_weight: fp64 [(batch,) n_kv_heads, 64] or None."""
+        per_seq = bool(self.cfg.per_sequence_plans)
+        if keys is not None:
+            lead = (self.cfg.batch,) if per_seq else ()
+            if keys.dim() != len(lead) + 3 or tuple(keys.shape[:len(lead)]) != lead \
+                    or tuple(keys.shape[-2:]) != (self.cfg.n_kv_heads, self.cfg.head_dim):
+                raise ValueError(f"keys must be [{'batch, ' if per_seq else ''}n_tok, n_kv_heads, head_dim], "
+                                 f"got {tuple(keys.shape)}")
         kp = _ptr(keys) if keys is not None else None
         dt = _dtype_code(keys) if keys is not None else KVQ_F16
-        n = keys.shape[0] if keys is not None else 0
+        n = keys.shape[-3] if keys is not None else 0
         wp = _ptr(block_weight) if block_weight is not None else None
         _check(lib.kvq_alloc_bits(self._h, layer, kp, dt, n, wp, _stream(stream)), "kvq_alloc_bits")
 
@@ -219,9 +229,9 @@ class Cache:
         _check(lib.kvq_set_rotation(self._h, layer, sg.ctypes.data), "kvq_set_rotation")
 
     def get_plan(self, layer: int):
-        H = self.cfg.n_kv_heads
-        bits = np.zeros((H, 64), dtype=np.int8)
-        gains = np.zeros((H, 64), dtype=np.float32)
+        shape = ((self.cfg.batch,) if self.cfg.per_sequence_plans else ()) + (self.cfg.n_kv_heads, 64)
+        bits = np.zeros(shape, dtype=np.int8)
+        gains = np.zeros(shape, dtype=np.float32)
         _check(lib.kvq_get_plan(self._h, layer, bits.ctypes.data, gains.ctypes.data), "kvq_get_plan")
         return bits.astype(np.int64), gains
 

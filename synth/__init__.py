@@ -10,6 +10,7 @@ from .workloads import (  # noqa: F401
     rope_frequencies,
     apply_rope,
     block_sigmas,
+    seq_block_sigmas,
     gen_layer,
     gen_query,
     to_input_dtype,

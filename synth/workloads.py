@@ -98,6 +98,21 @@ def block_sigmas(w: Workload, layer: int) -> np.ndarray:
     return sig
 
 
+def seq_block_sigmas(w: Workload, layer: int, seq: int) -> np.ndarray:
+    """Block deviations of one sequence in a batch whose sequences differ in kind: sequence 0
+    has the layer's own (block_sigmas); sequence s > 0 an independent draw of the same law."""
+    if seq == 0:
+        return block_sigmas(w, layer)
+    nb = w.head_dim // 2
+    sig = np.exp(_rng(w, _S_SIGMA, layer, seq).standard_normal((w.n_kv, nb)))
+    if w.n_outliers:
+        r = _rng(w, _S_OUTLIER, layer, seq)
+        for h in range(w.n_kv):
+            idx = r.choice(nb, size=w.n_outliers, replace=False)
+            sig[h, idx] *= w.outlier_mult
+    return sig
+
+
 def rope_frequencies(head_dim: int, theta: float) -> np.ndarray:
     j = np.arange(head_dim // 2, dtype=np.float64)
     return theta ** (-2.0 * j / head_dim)

@@ -69,6 +69,8 @@ BAD = [
     dict(codec=2, n_kv_heads=1, n_q_heads=1),  # NF16 needs n_kv*128 % 256 == 0
     dict(recent_window=-1),
     dict(recent_window=4097),
+    dict(recent_window=100),            # not a multiple of 128
+    dict(per_sequence_plans=2),
 ]
 
 

@@ -14,7 +14,7 @@ from oracle import attention as at
 from oracle import fidelity as fd
 from oracle import layout as lay
 from oracle import window as wn
-from synth import WORKLOADS, gen_layer, gen_query
+from synth import WORKLOADS, gen_layer, gen_query, seq_block_sigmas
 from tests.parity import CODEC, PAIRING, OracleLayer, assert_attention_close, errors
 
 pytestmark = pytest.mark.gpu
@@ -33,12 +33,16 @@ def _kvq():
 
 def run_case(wname, T, k_bits, v_bits, codec="bgtq", pairing="half", batch=None, layer=0,
              chunks=None, n_splits=0, noise="gauss", temper=False, check_codes=True, sample_rows=None,
-             b_min=0, b_max=8, fidelity=True, recent=0, query_weighted=False, zero_blocks=()):
+             b_min=0, b_max=8, fidelity=True, recent=0, query_weighted=False, zero_blocks=(),
+             per_seq=False):
     """Quantize T tokens of one layer on the GPU and in the oracle; compare everything.
 
     recent > 0: the last `recent` positions stay in the fp16 window.  A position that was inside
     the window at the end of its append went through fp16 (fp32 inputs are rounded), and the
-    packed storage holds positions 0 .. T - recent - 1."""
+    packed storage holds positions 0 .. T - recent - 1.
+
+    per_seq: every sequence draws its own block profile and gets plans of its own from its own
+    calibration keys (and its own query-energy weights)."""
     torch = _torch()
     kvq = _kvq()
     w = WORKLOADS[wname]
@@ -46,10 +50,11 @@ def run_case(wname, T, k_bits, v_bits, codec="bgtq", pairing="half", batch=None,
     H, Hq = w.n_kv, w.n_q
     ks, vs, qs = [], [], []
     for b in range(B):
-        k, v = gen_layer(w, layer, 0, T, seq=b, noise=noise, pairing=pairing)
+        sig = seq_block_sigmas(w, layer, b) if per_seq else None
+        k, v = gen_layer(w, layer, 0, T, seq=b, noise=noise, pairing=pairing, sigmas=sig)
         ks.append(k)
         vs.append(v)
-        qs.append(gen_query(w, layer, T, seq=b, noise=noise, pairing=pairing))
+        qs.append(gen_query(w, layer, T, seq=b, noise=noise, pairing=pairing, sigmas=sig))
     K = np.stack(ks)            # [B, T, H, d]
     if zero_blocks:
         # degenerate blocks: both coordinates zero in every key (zero energy, zero gain)
@@ -61,22 +66,32 @@ def run_case(wname, T, k_bits, v_bits, codec="bgtq", pairing="half", batch=None,
     Q = np.stack(qs)            # [B, Hq, d]
     print(f"[{wname} T={T} K{k_bits}V{v_bits} {codec}] inputs generated", flush=True)
     tc = min(T, w.calib_tokens)
-    calib = K[:, :tc].reshape(B * tc, H, 128)
+    # calibration keys: the first tc positions of every sequence, pooled (one plan per KV head)
+    # or per sequence ([B, tc, H, 128], one plan per (sequence, KV head))
+    calib = np.ascontiguousarray(K[:, :tc]) if per_seq else K[:, :tc].reshape(B * tc, H, 128)
     # query-energy block weights w[h, j] (mean squared norm of block j over the queries of KV
-    # head h's group), an input of the allocation
+    # head h's group, and over the batch unless plans are per sequence), an input of the allocation
     bw = None
     if query_weighted:
         qv = Q.astype(np.float64).reshape(B, H, w.group, 128)
         p0, p1 = al.block_pairs(128, pairing)
-        bw = np.ascontiguousarray(np.mean(qv[..., p0] ** 2 + qv[..., p1] ** 2, axis=(0, 2)))   # [H, 64]
+        e = qv[..., p0] ** 2 + qv[..., p1] ** 2
+        bw = np.ascontiguousarray(np.mean(e, axis=2) if per_seq else np.mean(e, axis=(0, 2)))   # [(B,) H, 64]
     # the rotated codec's signs are drawn here and passed to both sides
     signs = np.random.default_rng(7).choice([-1, 1], size=(H, 128)).astype(np.int8) if codec == "rot" else None
-    ol = OracleLayer(calib if codec == "bgtq" else K[:, :1].reshape(B, H, 128), k_bits, v_bits,
-                     codec, pairing, b_min, b_max, block_weight=bw, signs=signs)
+    if per_seq:
+        ols = [OracleLayer(calib[b] if codec == "bgtq" else K[b, :1], k_bits, v_bits, codec, pairing,
+                           b_min, b_max, block_weight=None if bw is None else bw[b], signs=signs)
+               for b in range(B)]
+        # the sequences' plans must really differ, or the case would not test the indexing
+        assert B == 1 or any(not np.array_equal(ols[0].widths, o.widths) for o in ols[1:])
+    else:
+        ols = [OracleLayer(calib if codec == "bgtq" else K[:, :1].reshape(B, H, 128), k_bits, v_bits,
+                           codec, pairing, b_min, b_max, block_weight=bw, signs=signs)] * B
 
     cfg = kvq.Config(n_layers=1, n_kv_heads=H, n_q_heads=Hq, batch=B, max_tokens=T, k_bits=k_bits,
                      v_bits=v_bits, b_min=b_min, b_max=b_max, codec=CODEC[codec],
-                     pairing=PAIRING[pairing], recent_window=recent)
+                     pairing=PAIRING[pairing], recent_window=recent, per_sequence_plans=int(per_seq))
     cache = kvq.Cache(cfg)
     dev = torch.device("cuda:0")
     cache.alloc_bits(0, torch.from_numpy(np.ascontiguousarray(calib)).to(dev) if codec == "bgtq" else None,
@@ -84,8 +99,10 @@ def run_case(wname, T, k_bits, v_bits, codec="bgtq", pairing="half", batch=None,
     if signs is not None:
         cache.set_rotation(0, signs)
     bits, gains = cache.get_plan(0)
-    assert np.array_equal(bits, ol.widths), "plan widths differ"
-    assert np.array_equal(gains.view(np.uint32), ol.g.astype(np.float32).view(np.uint32)), "gains differ"
+    want_w = np.stack([o.widths for o in ols]) if per_seq else ols[0].widths
+    want_g = np.stack([o.g for o in ols]) if per_seq else ols[0].g
+    assert np.array_equal(bits, want_w), "plan widths differ"
+    assert np.array_equal(gains.view(np.uint32), want_g.astype(np.float32).view(np.uint32)), "gains differ"
 
     bounds = [0, T] if chunks is None else [0, *np.cumsum(chunks).tolist()]
     assert bounds[-1] == T
@@ -103,6 +120,7 @@ def run_case(wname, T, k_bits, v_bits, codec="bgtq", pairing="half", batch=None,
     refs = []
     for b in range(B):
         kh_all, vh_all, qo = [], [], []
+        ol = ols[b]
         for h in range(H):
             kh = np.zeros((0, 128))
             vh = np.zeros((0, 128))
@@ -272,6 +290,18 @@ def test_query_weighted_allocation():
 def test_rotated_uniform_codec(kb):
     """Uniform quantizer on randomly rotated keys (Hadamard rotation with caller signs)."""
     run_case("llama8b_32k", 3000, kb, kb, codec="rot", temper=True, chunks=[1000, 1999, 1])
+
+
+def test_per_sequence_plans():
+    """One plan per (sequence, KV head), each sequence with its own block profile."""
+    run_case("llama8b_b64", 1500, 4, 4, batch=4, per_seq=True, temper=True, chunks=[700, 799, 1])
+
+
+def test_per_sequence_plans_weighted_with_window():
+    """Per-sequence plans with per-sequence query weights, a recent window and K3V3 (8 waves)."""
+    run_case("qwen3b_128k", 3000, 3, 3, batch=3, per_seq=True, query_weighted=True, recent=512,
+             chunks=[2048, 951, 1], temper=True)
+    run_case("qwen3b_128k", 2500, 2, 2, batch=2, per_seq=True, n_splits=3, pairing="interleaved")
 
 
 def test_rotated_uniform_codec_recent_window():
