@@ -63,8 +63,16 @@ typedef enum {
   KVQ_CODEC_UNIFORM_ROT = 3, /* uniform baseline on randomly rotated keys: K rows pass through
                                 R = H D / sqrt(128) (Sylvester-Hadamard H, caller signs D, see
                                 kvq_set_rotation) before the uniform quantizer; V as UNIFORM */
-  KVQ_CODEC_NF16_B256 = 2   /* NQKV-style: 4-bit 16-level Gaussian quantiles, absmax scale per
+  KVQ_CODEC_NF16_B256 = 2,  /* NQKV-style: 4-bit 16-level Gaussian quantiles, absmax scale per
                                256 consecutive values of a token's [n_kv_heads*128] vector */
+  KVQ_CODEC_KIVI = 4        /* KIVI-style asymmetric integers (the leaderboard's third method; NQKV
+                               review, ablation table: keys per channel, values per token): a key
+                               group is one channel over a 128-position tile, a value group is one
+                               position's 128 channels; per group lo = fp16(min), s = fp16(fp32(
+                               fp32(fp16(max) - lo) / (2^b - 1))), code = clamp(rint(fp32(fp32(x - lo)
+                               * fp32(1/s))), 0, 2^b - 1), reconstruction fp16(lo + s * code).  Key
+                               tiles are quantized once complete: the positions after the last
+                               whole tile (and the window, if any) stay in fp16 */
 } kvq_codec;
 
 typedef enum {
@@ -88,9 +96,9 @@ typedef struct {
   int32_t pairing;     /* kvq_pairing */
   int32_t recent_window; /* R in [0, 4096], a multiple of 128: the most recent min(len, R) tokens of each
                             sequence and layer are kept in fp16 (K and V) instead of the
-                            packed cache; 0 = none.  The paper's own results use none (RoPE-
-                            aware bit allocation page, abstract: "without an fp16 recent-key
-                            buffer"); the leaderboard's "Buffer Setting" is this option. */
+                            packed cache; 0 = none.  The paper reports its results with no such
+                            fp16 buffer of recent keys (RoPE-aware bit allocation page,
+                            abstract); the leaderboard's buffer-setting column is this option. */
   int32_t per_sequence_plans; /* 0: one plan per (layer, KV head), shared by the batch; 1: one
                             plan per (layer, sequence, KV head), each from that sequence's own
                             calibration keys (see kvq_alloc_bits) */
@@ -110,15 +118,19 @@ typedef struct {
                               of that dim for tile tokens 32g .. 32g+31, LSB first (token 32g+e at bit
                               e*v_bits), stored at index ((dim/16)*4 + g)*16 + dim%16 */
   int64_t k_scales_bytes;  /* fp16 K scales: BGTQ/UNIFORM [batch][n_kv][capacity];
-                              NF16 [batch][capacity][n_kv*128/256] */
-  int64_t v_scales_bytes;  /* fp16 V scales, same shapes as K scales */
+                              NF16 [batch][capacity][n_kv*128/256];
+                              KIVI [batch][n_kv][capacity/128][64 blocks][s(p0), s(p1), lo(p0), lo(p1)] */
+  int64_t v_scales_bytes;  /* fp16 V scales, same shapes as K scales;
+                              KIVI [batch][n_kv][capacity/128][2][128]: the tile's s, then its lo */
   int32_t plan_ready;      /* 1 once kvq_alloc_bits has run for this layer */
   int32_t recent_window;   /* R of the config */
-  int64_t packed_len;      /* positions held by the packed storage: max(0, len - R); positions
-                              packed_len .. len-1 are in the recent window */
-  int64_t recent_bytes;    /* bytes of one layer's recent-window K (or V) ring, fp16, position p in
-                              slot p mod R: K [batch][R][n_kv][128]; V in dim-major 128-slot tiles
-                              [batch][n_kv][R/128][128 dims][128 slots] */
+  int64_t packed_len;      /* positions held by the packed storage: max(0, len - R) (KIVI: rounded
+                              down to a multiple of 128); positions packed_len .. len-1 are in the
+                              recent window */
+  int64_t recent_bytes;    /* bytes of one layer's recent-window K (or V) ring of ring_slots slots,
+                              fp16, position p in slot p mod ring_slots: K [batch][ring_slots][n_kv][128];
+                              V in dim-major 128-slot tiles [batch][n_kv][ring_slots/128][128 dims][128 slots] */
+  int32_t ring_slots;      /* R, or R + 128 for KIVI (whose window also holds the last partial tile) */
 } kvq_layer_info;
 
 typedef enum {

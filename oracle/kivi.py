@@ -1,9 +1,9 @@
 """KIVI-style asymmetric integer codec (oracle; test infrastructure only).
 
 The leaderboard (KV Cache Quantization on WikiText-2 prompt 2048-token (train)) compares
-Block-GTQ and TQ-MSE with KIVI, whose title on the NQKV review's reference list names it
-"streaming asymmetric quantization"; the review's ablation table (KVQuant row) gives the
-split that method family uses: keys quantized per channel, values per token.  The pages
+Block-GTQ and TQ-MSE with KIVI, which the NQKV review's reference list describes as a
+streaming, asymmetric quantizer; the review's ablation table (KVQuant row) gives the split
+that method family uses: keys quantized per channel, values per token.  The pages
 give no formulas.  Readings (the plainest asymmetric min/max integer quantizer):
 
   For a group of values x (fp32 as given; fp16 inputs are exact) and a width b,

@@ -1,7 +1,7 @@
 """Randomized Hadamard rotation of key rows (oracle; test infrastructure only).
 
-RoPE-Aware Bit Allocation for KV-Cache Quantization, abstract: the allocator is
-"built on TurboQuant-MSE (TQ-MSE)".  TurboQuant's quantizer first applies a random
+RoPE-Aware Bit Allocation for KV-Cache Quantization, abstract: the allocator sits on
+top of TurboQuant-MSE (TQ-MSE).  TurboQuant's quantizer first applies a random
 orthogonal rotation to the whole vector, so that every coordinate follows nearly
 the same law, and then quantizes each coordinate with one scalar codebook.  The
 pages do not describe the rotation.  Reading (the flat-vector uniform baseline):

@@ -1,12 +1,11 @@
 """The fp16 recent window (oracle; test infrastructure only).
 
-RoPE-Aware Bit Allocation for KV-Cache Quantization, abstract: the paper's results
-are stated "without an fp16 recent-key buffer", i.e. a variant in which the most
-recent tokens are held in fp16 rather than in the low-bit cache; the leaderboard
-(KV Cache Quantization on WikiText-2 prompt 2048-token (train)) lists this as its
-"Buffer Setting".  The pages do not describe the buffer.  Readings:
+RoPE-Aware Bit Allocation for KV-Cache Quantization, abstract: the paper reports its
+results with no fp16 buffer of recent keys, which names the variant where the most recent
+tokens are held in fp16 rather than in the low-bit cache; the leaderboard (KV Cache
+Quantization on WikiText-2 prompt 2048-token (train)) has a buffer-setting column for it.  The pages do not describe the buffer.  Readings:
   * after every append, the last min(len, R) positions of the sequence are held as
-    fp16 copies of their K and V rows (both, as "recent tokens");
+    fp16 copies of their K and V rows (both: the buffer is read as one of recent tokens);
   * a position is quantized when it leaves the window, from its fp16 copy; a
     position that is already outside the window when it is appended is quantized
     from the input as given;
