@@ -221,7 +221,8 @@ def main():
     if v0d is not None:
         for label, vk, vv, R, codec in (("K3V2", 3, 2, 0, kvq.CODEC_BGTQ),
                                         ("K3V3_recent1024", 3, 3, 1024, kvq.CODEC_BGTQ),
-                                        ("K3V3_uniform_rotated", 3, 3, 0, kvq.CODEC_UNIFORM_ROT)):
+                                        ("K3V3_uniform_rotated", 3, 3, 0, kvq.CODEC_UNIFORM_ROT),
+                                        ("K3V3_kivi", 3, 3, 0, kvq.CODEC_KIVI)):
             vc = kvq.Cache(kvq.Config(1, H, Hq, B, T, vk, vv, recent_window=R, codec=codec))
             vc.alloc_bits(0, k0d[:chunk] if codec == kvq.CODEC_BGTQ else None)
             if codec == kvq.CODEC_UNIFORM_ROT:
@@ -238,7 +239,11 @@ def main():
             a1.record(stream)
             torch.cuda.synchronize()
             us = a0.elapsed_time(a1) * 1e3 / 50
-            vbytes = B * H * ((T - R) * ((vk + vv) * 128 / 8 + 4) + R * 512) + B * Hq * 128 * 6 + H * PLAN_BYTES_PER_HEAD
+            # packed positions (KIVI: whole 128-position tiles) with 4 B of scales each (KIVI: 8 B,
+            # 2 fp16 per channel per tile and 2 per position), the rest fp16 K and V
+            P = vc.layer_info(0).packed_len
+            par = 8 if codec == kvq.CODEC_KIVI else 4
+            vbytes = B * H * (P * ((vk + vv) * 128 / 8 + par) + (T - P) * 512) + B * Hq * 128 * 6 + H * PLAN_BYTES_PER_HEAD
             variants[label] = {"k_bits": vk, "v_bits": vv, "recent_window": R, "codec": int(codec),
                                "us_per_launch": round(us, 2),
                                "GB/s": round(vbytes / (us * 1e-6) / 1e9, 2)}

@@ -31,13 +31,14 @@ bool config_valid(const kvq_config* c) {
   if (c->n_q_heads % c->n_kv_heads != 0) return false;
   const int G = c->n_q_heads / c->n_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return false;
-  if (c->codec < KVQ_CODEC_BGTQ || c->codec > KVQ_CODEC_UNIFORM_ROT) return false;
+  if (c->codec < KVQ_CODEC_BGTQ || c->codec > KVQ_CODEC_KIVI) return false;
   if (c->recent_window < 0 || c->recent_window > kvq::kMaxRecent || c->recent_window % 128) return false;
   if (c->pairing != KVQ_ROPE_HALF && c->pairing != KVQ_ROPE_INTERLEAVED) return false;
   if (c->per_sequence_plans != 0 && c->per_sequence_plans != 1) return false;
   if (c->v_bits < 1 || c->v_bits > kMaxBits) return false;
   if (c->b_min < 0 || c->b_max > kMaxBits || c->b_min > c->b_max) return false;
   if (c->k_bits < 1 || c->k_bits < c->b_min || c->k_bits > c->b_max) return false;
+  if (c->codec == KVQ_CODEC_KIVI && (c->k_bits > 4 || c->v_bits > 4)) return false;
   if (c->codec == KVQ_CODEC_NF16_B256) {
     if (c->k_bits != 4 || c->v_bits != 4) return false;
     if ((c->n_kv_heads * kHeadDim) % kvq::kNfBlock != 0) return false;
@@ -120,6 +121,10 @@ kvq_status kvq_cache_create(const kvq_config* cfg, kvq_cache** out) {
   c->cfg = *cfg;
   c->group = cfg->n_q_heads / cfg->n_kv_heads;
   c->n_plan = cfg->per_sequence_plans ? cfg->batch : 1;
+  // KIVI packs whole 128-position key tiles: its fp16 ring also holds the last partial tile
+  const bool kivi = cfg->codec == KVQ_CODEC_KIVI;
+  c->ring = cfg->recent_window + (kivi ? kVTile : 0);
+  c->pack_group = kivi ? kVTile : 1;
   c->cap = (cfg->max_tokens + kVTile - 1) / kVTile * kVTile;
   const bool nf = cfg->codec == KVQ_CODEC_NF16_B256;
   c->k_words = 4 * (nf ? 4 : cfg->k_bits);
@@ -140,9 +145,10 @@ kvq_status kvq_cache_create(const kvq_config* cfg, kvq_cache** out) {
   const int64_t B = cfg->batch, H = cfg->n_kv_heads, L = cfg->n_layers, cap = c->cap;
   c->k_codes_layer = B * H * cap * c->k_words * 4;
   c->v_codes_layer = B * H * cap * c->v_words * 4;  // (cap/128) tiles * 128 dims * v_words words
-  c->k_scales_layer = nf ? B * cap * c->n_nf_blocks * 2 : B * H * cap * 2;
+  // KIVI: 2 fp16 per channel per 128-position tile (K), 2 fp16 per position (V)
+  c->k_scales_layer = nf ? B * cap * c->n_nf_blocks * 2 : B * H * cap * (kivi ? 4 : 2);
   c->v_scales_layer = c->k_scales_layer;
-  c->recent_layer = B * cfg->recent_window * H * kHeadDim * 2;
+  c->recent_layer = B * c->ring * H * kHeadDim * 2;
   // split partials: at most 256 splits per (sequence, head), at most 256 MiB of partials
   int64_t per_split = B * H * c->group * (kHeadDim + 2) * 4;
   int64_t ms = (int64_t(256) << 20) / per_split;
@@ -292,7 +298,16 @@ kvq_status kvq_quantize_append(kvq_cache* c, int32_t layer, const void* k, const
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t len = c->len[layer], R = c->cfg.recent_window;
   hipError_t e = hipSuccess;
-  if (R == 0) {
+  if (c->cfg.codec == KVQ_CODEC_KIVI) {
+    // whole key tiles [p_old, p_new) are quantized, each position from its fp16 copy in the
+    // ring (positions before len) or from the input; new positions after p_new go to the ring
+    // (after the quantization: they may reuse the slots it reads)
+    const int64_t p_old = kvq::packed_len_at(c, len), p_new = kvq::packed_len_at(c, len + n_new);
+    if (p_new > p_old) e = kvq::launch_kivi_quantize(c, layer, k, v, dtype, n_new, p_old, p_new - p_old, len, s);
+    const int64_t w0 = p_new > len ? p_new : len;
+    if (e == hipSuccess && w0 < len + n_new)
+      e = kvq::launch_recent_write(c, layer, k, v, dtype, n_new, w0 - len, w0, len + n_new - w0, s);
+  } else if (R == 0) {
     e = kvq::launch_quantize(c, layer, k, v, dtype, n_new, n_new, 0, len, s);
   } else {
     // positions [p_old, p_new) leave the window for the packed storage: first those already
@@ -399,6 +414,7 @@ kvq_status kvq_layer_info_get(const kvq_cache* c, int32_t layer, kvq_layer_info*
   info->recent_window = c->cfg.recent_window;
   info->packed_len = kvq::packed_len(c, layer);
   info->recent_bytes = c->recent_layer;
+  info->ring_slots = c->ring;
   return KVQ_OK;
 }
 

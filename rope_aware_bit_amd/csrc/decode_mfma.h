@@ -40,6 +40,20 @@ namespace kvq {
 namespace mfma {
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+// fp16x2 a * b + c with one rounding per half (the asymmetric integer codec's reconstruction
+// lo + s * code of two values at once)
+__device__ inline uint32_t fma_h2(uint32_t a, uint32_t b, uint32_t c) {
+  h2 x, y, z;
+  __builtin_memcpy(&x, &a, 4);
+  __builtin_memcpy(&y, &b, 4);
+  __builtin_memcpy(&z, &c, 4);
+  const h2 r = __builtin_elementwise_fma(x, y, z);
+  uint32_t o;
+  __builtin_memcpy(&o, &r, 4);
+  return o;
+}
 typedef __attribute__((address_space(3))) void* lds_ptr;
 typedef __attribute__((address_space(1))) void* glb_ptr;
 typedef float f4 __attribute__((ext_vector_type(4)));
@@ -415,7 +429,7 @@ __device__ __attribute__((always_inline)) inline KWin k_windows(const KPar& k, c
 // Decode kernel.  W waves per workgroup (one or two per SIMD).  Every wave owns a region of
 // `region_words` LDS words that holds, in turn, its staged K tile, its softmax weights and its
 // share of the wave merge (and, during set-up, wave 0's region holds the scaled query).
-template <int G, int VB, bool NF, int W>
+template <int G, int VB, bool NF, int W, bool KV>
 __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     const void* __restrict__ qv, int q_f32, float sigma, int64_t len, int n_packed_splits,
     const __half* __restrict__ rk, const __half* __restrict__ rv, int R, int64_t n_recent,
@@ -460,6 +474,13 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   } else {
     vbuf = kr + v_off;
   }
+  // asymmetric integer codec: the wave's tile parameters, [0, 64) key block j (s pair, lo
+  // pair), [64, 128) value positions (s of the 128 positions, then their lo)
+  uint2* kvp = nullptr;
+  if constexpr (KV) {
+    __shared__ __attribute__((aligned(16))) uint2 kvp_s[W][2 * kBlocks];
+    kvp = kvp_s[wave];
+  }
   float (*qs_s)[kHeadDim] = reinterpret_cast<float (*)[kHeadDim]>(dyn_s);   // set-up only
 
   // `len` packed positions in 128-token tiles; workgroups from n_packed_splits on read the
@@ -476,7 +497,7 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   //      one round of memory latency. ----
   const bool setup_wave = __builtin_amdgcn_readfirstlane(wave) < 4;
   const int st = tid & 255;   // set-up thread
-  const uint8_t* gimg = tabg->lds_image[NF ? 1 : 0];
+  const uint8_t* gimg = tabg->lds_image[KV ? 2 : NF ? 1 : 0];
   const uint4 timg = reinterpret_cast<const uint4*>(gimg)[st < kLdsTableBytes / 16 ? st : kLdsTableBytes / 16 - 1];
   uint32_t qraw[QPT];
   float gr[QPT];
@@ -515,7 +536,15 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     }
   };
   uint32_t skr[8], svr[8];   // fp16 bits of the scales of tokens 16 tg + n
+  uint2 kpr, vpr;            // asymmetric integer codec: this lane's 8 bytes of each tile parameter set
   auto load_scales = [&](int64_t tile) {
+    if constexpr (KV) {
+      // [tile][64 blocks][s(p0), s(p1), lo(p0), lo(p1)] and [tile][2][128]: 512 bytes each
+      const int64_t tb = (bh * (cap / kVTile) + tile) * kBlocks + lane;
+      kpr = reinterpret_cast<const uint2*>(ks)[tb];
+      vpr = reinterpret_cast<const uint2*>(vs)[tb];
+      return;
+    }
 #pragma unroll
     for (int tg = 0; tg < 8; ++tg) {
       const int64_t t = tile * kVTile + 16 * tg + n;
@@ -532,6 +561,7 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   // two per register for the rest of the tile
   uint32_t skp[4], svp[4];
   auto pack_scales = [&]() {
+    if constexpr (KV) return;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       skp[j] = (skr[2 * j] & 0xFFFFu) | (skr[2 * j + 1] << 16);
@@ -702,6 +732,10 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     }
     kr[k_words * kKS + lane] = kr[k_words * kKS + 64 + lane] = 0u;
     pack_scales();
+    if constexpr (KV) {
+      kvp[lane] = kpr;
+      kvp[kBlocks + lane] = vpr;
+    }
     wave_sync();
     // 8 waves: the V tile is copied now, when no other load of this wave is in flight, and
     // arrives during the key product
@@ -758,15 +792,32 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     };
     // per chunk: parameters, then the first half's row windows; the second half's windows are
     // read before the first half's lookups
+    // asymmetric integer codec: the lookups give the codes as fp16 integers; each pair becomes
+    // fp16(lo + s * code) with its block's parameters (pair p of chunk c is plan rank
+    // 16 c + 8 (p >> 1) + 2 g + (p & 1), which is block index for the codec's uniform plan)
+    auto k_dequant = [&](const uint2 (&sm)[4], uint32_t (&u)[4][4]) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) u[t][p] = fma_h2(u[t][p], sm[p].x, sm[p].y);
+      }
+    };
 #pragma unroll 1
     for (int c = 0; c < 4; ++c) {
       const KPar P = k_params(c, g, n, kp_s, a_s);
       const KWin W0 = k_windows(P, kr, 0);
       const KWin W1 = k_windows(P, kr, 1);
+      uint2 sm[4];
+      if constexpr (KV) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) sm[p] = kvp[16 * c + 8 * (p >> 1) + 2 * g + (p & 1)];
+      }
       uint32_t u[4][4];
       k_lookups(P, W0, c, u);
+      if constexpr (KV) k_dequant(sm, u);
       k_products(P, u, 0);
       k_lookups(P, W1, c, u);
+      if constexpr (KV) k_dequant(sm, u);
       k_products(P, u, 1);
     }
     wave_sync();   // the key rows are read; the area takes the softmax weights (and V) next
@@ -779,7 +830,7 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
 #pragma unroll
     for (int tg = 0; tg < 8; ++tg) {
       const float bias = 16 * tg + n < rem ? 0.0f : -INFINITY;
-      const float sk = scale_of(skp, tg);
+      const float sk = KV ? 1.0f : scale_of(skp, tg);
       L0[tg] = fmaf(dacc[tg][0] + dacc[tg][1], sk, bias);
       L1[tg] = fmaf(dacc[tg][2] + dacc[tg][3], sk, bias);
       mt0 = fmaxf(mt0, L0[tg]);
@@ -798,7 +849,7 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
 #pragma unroll
     for (int tg = 0; tg < 8; ++tg) {
       // tokens past the sequence end have p = 0; their stored scales are finite (zero-filled)
-      const float sv = scale_of(svp, tg);
+      const float sv = KV ? 1.0f : scale_of(svp, tg);
       const float p0 = __builtin_amdgcn_exp2f(L0[tg] - mn0), p1 = __builtin_amdgcn_exp2f(L1[tg] - mn1);
       l0 += p0;
       l1 += p1;
@@ -842,6 +893,13 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
+      // asymmetric integer codec: s and lo pairs of this lane's tokens 32 g + 8 c + 2 e, +1
+      uint4 vsc, vlo;
+      if constexpr (KV) {
+        const uint32_t* vp = reinterpret_cast<const uint32_t*>(kvp + kBlocks);
+        vsc = *reinterpret_cast<const uint4*>(vp + 16 * g + 4 * c);
+        vlo = *reinterpret_cast<const uint4*>(vp + kBlocks + 16 * g + 4 * c);
+      }
       h8 bp;
       if (n < PCOLS) {
         bp = *reinterpret_cast<const h8*>(&pw[n * kPS + 32 * g + 8 * c]);
@@ -854,6 +912,12 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
         uint32_t pr[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) pr[e] = v_pair<VB>(&vseg[dt][1], 8 * c + 2 * e, tab_s, lb);
+        if constexpr (KV) {
+          pr[0] = fma_h2(pr[0], vsc.x, vlo.x);
+          pr[1] = fma_h2(pr[1], vsc.y, vlo.y);
+          pr[2] = fma_h2(pr[2], vsc.z, vlo.z);
+          pr[3] = fma_h2(pr[3], vsc.w, vlo.w);
+        }
         h8 av;
         __builtin_memcpy(&av, pr, 16);
         oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bp, oacc[dt], 0, 0, 0);
@@ -877,10 +941,14 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     //      loaded straight from the ring. ----
     const int64_t j = s - n_packed_splits;
     const int64_t nv64 = n_recent - 128 * j;
+    // window positions len .. len + n_recent - 1 sit in slots p mod R; the j-th 128 of them
+    // fill ring tile (len / 128 + j) mod (R / 128) from its first slot on (len is a multiple of
+    // 128, or the window is full and every tile is)
+    const int64_t jt = ((len >> 7) + j) % (R >> 7);
     if (wave == 0) {
       const int nv = nv64 < 128 ? static_cast<int>(nv64) : 128;
-      const __half* kt = rk + ((static_cast<int64_t>(b) * R + 128 * j) * n_kv + h) * kHeadDim;
-      const __half* vt = rv + ((bh * (R / 128) + j) * kHeadDim) * 128;
+      const __half* kt = rk + ((static_cast<int64_t>(b) * R + 128 * jt) * n_kv + h) * kHeadDim;
+      const __half* vt = rv + ((bh * (R / 128) + jt) * kHeadDim) * 128;
       f4 dacc[8];
 #pragma unroll
       for (int tg = 0; tg < 8; ++tg) dacc[tg] = f4{0.f, 0.f, 0.f, 0.f};
@@ -1062,29 +1130,33 @@ hipError_t launch_gvw(kvq_cache* c, int layer, const void* q, int q_f32, float s
   const int S_all = S + static_cast<int>((n_recent + 127) / 128);
   const __half* rk = n_recent > 0 ? layer_k_recent(c, layer) : nullptr;
   const __half* rv = n_recent > 0 ? layer_v_recent(c, layer) : nullptr;
-  const int R = cfg.recent_window;
+  const int R = c->ring;
   const int8_t* rot = cfg.codec == KVQ_CODEC_UNIFORM_ROT ? c->rot_signs + static_cast<int64_t>(layer) * cfg.n_kv_heads * kHeadDim : nullptr;
   dim3 grid(S_all, cfg.n_kv_heads, cfg.batch);
   const size_t dyn = static_cast<size_t>(W) * sh.region_words * sizeof(uint32_t);
   const Plan* plans = c->plans + static_cast<int64_t>(layer) * c->n_plan * cfg.n_kv_heads;
   const int plan_bs = c->n_plan > 1 ? cfg.n_kv_heads : 0;
-  const bool nf = cfg.codec == KVQ_CODEC_NF16_B256;
   const int mergers = decode_split_mergers(S_all, static_cast<int64_t>(cfg.batch) * cfg.n_kv_heads, c->n_cu);
+#define KVQ_LAUNCH_DEC(NF, KV)                                                                         \
+  hipLaunchKernelGGL((decode_mfma<G, VB, NF, W, KV>), grid, dim3(64 * W), dyn, stream, q, q_f32, sigma,   \
+                     plen, S, rk, rv, R, n_recent, rot, cfg.n_kv_heads, c->cap, tps, plans, plan_bs,        \
+                     c->tables, layer_k_codes(c, layer), layer_v_codes(c, layer), layer_k_scales(c, layer), \
+                     layer_v_scales(c, layer), c->k_words, c->n_nf_blocks, S_all, mergers, sh.region_words,  \
+                     sh.v_early, sh.v_off, c->part_o, c->part_l, c->part_mt, c->split_epochs, out)
   if constexpr (VB == 4) {
-    if (nf) {
-      hipLaunchKernelGGL((decode_mfma<G, 4, true, W>), grid, dim3(64 * W), dyn, stream, q, q_f32, sigma,
-                         plen, S, rk, rv, R, n_recent, rot, cfg.n_kv_heads, c->cap, tps, plans, plan_bs, c->tables, layer_k_codes(c, layer),
-                         layer_v_codes(c, layer), layer_k_scales(c, layer), layer_v_scales(c, layer),
-                         c->k_words, c->n_nf_blocks, S_all, mergers, sh.region_words, sh.v_early, sh.v_off,
-                         c->part_o, c->part_l, c->part_mt, c->split_epochs, out);
+    if (cfg.codec == KVQ_CODEC_NF16_B256) {
+      KVQ_LAUNCH_DEC(true, false);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((decode_mfma<G, VB, false, W>), grid, dim3(64 * W), dyn, stream, q, q_f32, sigma,
-                     plen, S, rk, rv, R, n_recent, rot, cfg.n_kv_heads, c->cap, tps, plans, plan_bs, c->tables, layer_k_codes(c, layer),
-                     layer_v_codes(c, layer), layer_k_scales(c, layer), layer_v_scales(c, layer),
-                     c->k_words, c->n_nf_blocks, S_all, mergers, sh.region_words, sh.v_early, sh.v_off,
-                     c->part_o, c->part_l, c->part_mt, c->split_epochs, out);
+  if constexpr (VB <= 4) {
+    if (cfg.codec == KVQ_CODEC_KIVI) {
+      KVQ_LAUNCH_DEC(false, true);
+      return hipGetLastError();
+    }
+  }
+  KVQ_LAUNCH_DEC(false, false);
+#undef KVQ_LAUNCH_DEC
   return hipGetLastError();
 }
 

@@ -115,6 +115,7 @@ __global__ __launch_bounds__(256, 2) void fidelity_partials(
     const T* __restrict__ q, const T* __restrict__ keys, int64_t len, int n_kv, int64_t cap,
     double sigma, int64_t tok_per_split, const Plan* __restrict__ plans, int plan_bs, const Tables* __restrict__ tab,
     const uint32_t* __restrict__ kc, const uint16_t* __restrict__ ks, int k_words, int n_nf, int nf,
+    int kivi, int pairing,
     int64_t plen, const __half* __restrict__ rk, int R, const int8_t* __restrict__ rot,
     double* __restrict__ part, int S) {
   constexpr int kVec = 16 / sizeof(T);
@@ -136,6 +137,7 @@ __global__ __launch_bounds__(256, 2) void fidelity_partials(
   __shared__ uint32_t kr_s[kFidTok][4 * kMaxBits + 1];
   __shared__ __attribute__((aligned(16))) __half xr_s[kFidTok][kHeadDim + 8];   // recent-window rows
   __shared__ double sc_s[kFidTok];
+  __shared__ __half ksc_s[kHeadDim], klo_s[kHeadDim];   // asymmetric integer codec: the tile's channel parameters
   __shared__ int nf_s;
 
   const Plan* P = plans + static_cast<int64_t>(b) * plan_bs + h;   // plan of (sequence, head)
@@ -200,7 +202,15 @@ __global__ __launch_bounds__(256, 2) void fidelity_partials(
             *reinterpret_cast<const uint4*>(rk + ((static_cast<int64_t>(b) * R + slot) * n_kv + h) * kHeadDim + 8 * c);
       }
     }
-    if (tid < nr && r0 + tid < plen) {
+    if (kivi && tid < kHeadDim && r0 < plen) {
+      // [tile][block j][s(p0), s(p1), lo(p0), lo(p1)]; the round lies inside one 128-position tile
+      const int j = pairing == KVQ_ROPE_HALF ? tid % kBlocks : tid / 2;
+      const int co = pairing == KVQ_ROPE_HALF ? tid / kBlocks : tid % 2;
+      const uint16_t* kp = ks + ((bh * (cap / kVTile) + r0 / kVTile) * kBlocks + j) * 4;
+      ksc_s[tid] = __ushort_as_half(kp[co]);
+      klo_s[tid] = __ushort_as_half(kp[2 + co]);
+    }
+    if (!kivi && tid < nr && r0 + tid < plen) {
       const uint16_t sb = nf ? ks[(static_cast<int64_t>(b) * cap + r0 + tid) * n_nf + h / 2] : ks[bh * cap + r0 + tid];
       sc_s[tid] = static_cast<double>(__half2float(__ushort_as_half(sb)));
     }
@@ -250,7 +260,9 @@ __global__ __launch_bounds__(256, 2) void fidelity_partials(
                              (static_cast<uint64_t>(kr_s[t][(off >> 5) + 1]) << 32);
         const uint32_t code = static_cast<uint32_t>(two >> (off & 31)) & ((1u << w) - 1u);
         const double c = static_cast<double>(__half2float(__ushort_as_half(cb_s[w][code])));
-        const double kh = (s16 * g_s[dim]) * c;
+        // asymmetric integer codec: fp16(lo + s * code) with one rounding
+        const double kh = kivi ? static_cast<double>(__half2float(__hfma(ksc_s[dim], __float2half_rn(static_cast<float>(code)), klo_s[dim])))
+                               : (s16 * g_s[dim]) * c;
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) ah[hh] += kh * qr_s[hh][dim];
       }
@@ -364,8 +376,8 @@ hipError_t launch_fidelity(kvq_cache* c, int layer, const void* q, const void* k
   hipLaunchKernelGGL((fidelity_partials<T, GG>), grid, dim3(256), 0, stream, static_cast<const T*>(q), \
                      static_cast<const T*>(keys), len, H, c->cap, sigma, per, plans, plan_bs, c->tables, \
                      layer_k_codes(c, layer), layer_k_scales(c, layer), c->k_words, c->n_nf_blocks,   \
-                     nf ? 1 : 0, plen, plen < len ? layer_k_recent(c, layer) : nullptr,       \
-                     c->cfg.recent_window > 0 ? c->cfg.recent_window : 1,                         \
+                     nf ? 1 : 0, cfg.codec == KVQ_CODEC_KIVI ? 1 : 0, cfg.pairing, plen, plen < len ? layer_k_recent(c, layer) : nullptr,       \
+                     c->ring > 0 ? c->ring : 1,                                                   \
                      cfg.codec == KVQ_CODEC_UNIFORM_ROT ? c->rot_signs + static_cast<int64_t>(layer) * H * kHeadDim : nullptr, \
                      c->fid_part, static_cast<int>(S))
 #define KVQ_FID_G(T)                  \

@@ -37,8 +37,9 @@ struct Tables {
   uint16_t nf_cb[16];                // fp16 levels of the 16-level Gaussian-quantile codebook
   float nf_bd[16];                   // 15 boundaries; [15] = +inf
   // decode lookup tables in their LDS layout: [0] Lloyd-Max codebooks, [1] the same with
-  // the width-4 tables holding the 16-level Gaussian-quantile codebook
-  alignas(16) uint8_t lds_image[2][kLdsTableBytes];
+  // the width-4 tables holding the 16-level Gaussian-quantile codebook, [2] the integers
+  // 0 .. 2^b - 1 as fp16 (codes of the asymmetric integer codec)
+  alignas(16) uint8_t lds_image[3][kLdsTableBytes];
 };
 
 // Per-(layer, KV head) plan written by the allocation kernel.
@@ -76,8 +77,10 @@ struct kvq_cache {
   uint32_t* v_codes;           // [L][B][H][cap/128][128][v_words]
   uint16_t* k_scales;          // BGTQ/UNI [L][B][H][cap]; NF16 [L][B][cap][nnf]
   uint16_t* v_scales;
-  __half* k_recent;            // recent-window rings [L][B][R][H][128] fp16 (R > 0)
+  __half* k_recent;            // recent-window rings [L][B][ring][H][128] fp16 (ring > 0)
   __half* v_recent;
+  int ring;                    // ring slots: R, or R + 128 for KIVI (its last partial key tile)
+  int pack_group;              // positions are packed in whole groups of this many (KIVI: 128)
   kvq::Plan* plans;            // [L][n_plan][H]
   int n_plan;                  // plans per (layer, KV head): batch with per-sequence plans, else 1
   int8_t* rot_signs;           // key-rotation signs [L][H][128] (codec UNIFORM_ROT)
@@ -108,6 +111,12 @@ hipError_t launch_alloc(kvq_cache* c, int layer, const void* keys, int dtype, in
 // the recent-window rings of R = ring_R slots (fp16).
 hipError_t launch_quantize(kvq_cache* c, int layer, const void* k, const void* v, int dtype,
                            int64_t n_new, int64_t in_stride, int ring_R, int64_t L0, hipStream_t stream);
+// KIVI: quantizes the n_pos positions from p0 (whole 128-position tiles) of every sequence;
+// position p < len_old comes from its fp16 copy in the ring, others from input row p - len_old
+// of [batch][in_stride][n_kv][128] K and V.
+hipError_t launch_kivi_quantize(kvq_cache* c, int layer, const void* k, const void* v, int dtype,
+                                int64_t in_stride, int64_t p0, int64_t n_pos, int64_t len_old,
+                                hipStream_t stream);
 hipError_t launch_recent_write(kvq_cache* c, int layer, const void* k, const void* v, int dtype,
                                int64_t in_stride, int64_t row0, int64_t pos0, int64_t count,
                                hipStream_t stream);
@@ -136,11 +145,13 @@ inline DecodeShape decode_shape(const kvq_cache* c) {
   if (kpart < G * 192) kpart = G * 192;   // recent window: q * sigma' and one chunk's weights
   kpart = (kpart + 3) & ~3;
   const int vwords = 512 * vb;
+  // asymmetric integer codec: 1 KB of tile parameters per wave
+  const int kvx = c->cfg.codec == KVQ_CODEC_KIVI ? 1024 : 0;
   {
-    const int stat = kStaticBase + 16 * 8 * G + 64 * G + 4 * 8 * vwords;
+    const int stat = kStaticBase + 16 * 8 * G + 64 * G + 4 * 8 * vwords + 8 * kvx;
     if (stat + 4 * 8 * kpart <= kLds) return {8, 1, kpart, 0};
   }
-  const int stat = kStaticBase + 16 * 4 * G + 64 * G;
+  const int stat = kStaticBase + 16 * 4 * G + 64 * G + 4 * kvx;
   if (stat + 4 * 4 * (kpart + vwords) <= kLds) return {4, 1, kpart + vwords, kpart};
   int late = ((G * kPS + 3) & ~3) + vwords;
   if (late < kpart) late = kpart;
@@ -175,10 +186,12 @@ inline __half* layer_v_recent(kvq_cache* c, int layer) {
   return reinterpret_cast<__half*>(reinterpret_cast<char*>(c->v_recent) + c->recent_layer * layer);
 }
 // Positions of `layer` held by the packed storage (the rest are in the recent window).
-inline int64_t packed_len(const kvq_cache* c, int layer) {
-  const int64_t len = c->len[layer], R = c->cfg.recent_window;
-  return len > R ? len - R : 0;
+inline int64_t packed_len_at(const kvq_cache* c, int64_t len) {
+  const int64_t R = c->cfg.recent_window;
+  const int64_t p = len > R ? len - R : 0;
+  return p / c->pack_group * c->pack_group;
 }
+inline int64_t packed_len(const kvq_cache* c, int layer) { return packed_len_at(c, c->len[layer]); }
 inline uint16_t* layer_v_scales(kvq_cache* c, int layer) {
   return reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(c->v_scales) + c->v_scales_layer * layer);
 }

@@ -345,11 +345,11 @@ hipError_t launch_recent_write(kvq_cache* c, int layer, const void* k, const voi
   if (dtype == KVQ_F16)
     hipLaunchKernelGGL(recent_write<__half>, grid, dim3(256), 0, stream, static_cast<const __half*>(k),
                        static_cast<const __half*>(v), in_stride, row0, pos0, cfg.n_kv_heads,
-                       cfg.recent_window, layer_k_recent(c, layer), layer_v_recent(c, layer));
+                       c->ring, layer_k_recent(c, layer), layer_v_recent(c, layer));
   else
     hipLaunchKernelGGL(recent_write<float>, grid, dim3(256), 0, stream, static_cast<const float*>(k),
                        static_cast<const float*>(v), in_stride, row0, pos0, cfg.n_kv_heads,
-                       cfg.recent_window, layer_k_recent(c, layer), layer_v_recent(c, layer));
+                       c->ring, layer_k_recent(c, layer), layer_v_recent(c, layer));
   return hipGetLastError();
 }
 

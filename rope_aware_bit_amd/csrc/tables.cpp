@@ -184,10 +184,12 @@ void build_tables(Tables* t) {
   for (int k = 0; k < 15; ++k) t->nf_bd[k] = static_cast<float>(0.5 * (lv[k] + lv[k + 1]));
   t->nf_bd[15] = inf;
 
-  for (int img = 0; img < 2; ++img) {
+  uint16_t ints[256];   // fp16 bit patterns of the integers 0 .. 255
+  for (int k = 0; k < 256; ++k) ints[k] = half_bits(static_cast<double>(k));
+  for (int img = 0; img < 3; ++img) {
     uint8_t* out = t->lds_image[img];
     for (int w = 1; w <= kMaxBits; ++w) {
-      const uint16_t* cb = (img == 1 && w == 4) ? t->nf_cb : t->cb[w];
+      const uint16_t* cb = img == 2 ? ints : (img == 1 && w == 4) ? t->nf_cb : t->cb[w];
       for (int c = 0; c < (1 << w); ++c)
         std::memcpy(out + single_table_base(w) + 2 * c, &cb[c], 2);
       if (w <= 4) {

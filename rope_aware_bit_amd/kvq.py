@@ -18,7 +18,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so"
 
 KVQ_OK, KVQ_EINVAL, KVQ_ENOMEM, KVQ_ECAPACITY, KVQ_ESTATE, KVQ_EHIP = range(6)
 KVQ_F16, KVQ_F32 = 0, 1
-CODEC_BGTQ, CODEC_UNIFORM, CODEC_NF16_B256, CODEC_UNIFORM_ROT = 0, 1, 2, 3
+CODEC_BGTQ, CODEC_UNIFORM, CODEC_NF16_B256, CODEC_UNIFORM_ROT, CODEC_KIVI = 0, 1, 2, 3, 4
 ROPE_HALF, ROPE_INTERLEAVED = 0, 1
 PART_K_CODES, PART_V_CODES, PART_K_SCALES, PART_V_SCALES, PART_K_RECENT, PART_V_RECENT = range(6)
 
@@ -53,6 +53,7 @@ class kvq_layer_info(ctypes.Structure):
         ("v_codes_bytes", ctypes.c_int64), ("k_scales_bytes", ctypes.c_int64),
         ("v_scales_bytes", ctypes.c_int64), ("plan_ready", ctypes.c_int32),
         ("recent_window", ctypes.c_int32), ("packed_len", ctypes.c_int64), ("recent_bytes", ctypes.c_int64),
+        ("ring_slots", ctypes.c_int32),
     ]
 
 

@@ -9,12 +9,13 @@ import numpy as np
 
 from oracle import allocation as al
 from oracle import attention as at
+from oracle import kivi as kv
 from oracle import layout as lay
 from oracle import quantize as qz
 from oracle import rotation as rt
 
 PAIRING = {"half": 0, "interleaved": 1}
-CODEC = {"bgtq": 0, "uniform": 1, "nf16": 2, "rot": 3}
+CODEC = {"bgtq": 0, "uniform": 1, "nf16": 2, "rot": 3, "kivi": 4}
 
 ABS_TOL = 2e-3
 REL_L2_TOL = 1e-3
@@ -67,6 +68,13 @@ class OracleLayer:
             out["k_scale_blocks"], out["v_scale_blocks"] = sk, sv
             out["k_s16"] = sk[:, h // 2]
             out["v_s16"] = sv[:, h // 2]
+        elif self.codec == "kivi":
+            # keys per channel over whole 128-position tiles, values per position
+            ck, sk, lk = kv.quantize_k(k_rows, self.k_bits)
+            cv, sv, lv = kv.quantize_v(v_rows, self.v_bits)
+            out.update(k_codes=ck, k_s16=sk, k_lo16=lk, v_codes=cv, v_s16=sv, v_lo16=lv)
+            out["k_params"] = kv.k_params_layout(sk, lk, self.pairing)
+            out["v_params"] = kv.v_params_layout(sv, lv)
         else:
             wd = al.dim_widths(self.widths[h], 128, self.pairing)
             igd = al.dim_values(self.ig[h], 128, self.pairing)
@@ -82,6 +90,9 @@ class OracleLayer:
         return out
 
     def dequant(self, q_out, h):
+        if self.codec == "kivi":
+            return (kv.dequant_k(q_out["k_codes"], q_out["k_s16"], q_out["k_lo16"]),
+                    kv.dequant_v(q_out["v_codes"], q_out["v_s16"], q_out["v_lo16"]))
         if self.codec == "nf16":
             lv = at.dequant_nf16(q_out["k_codes"], q_out["k_s16"][:, None], block=128)
             vv = at.dequant_nf16(q_out["v_codes"], q_out["v_s16"][:, None], block=128)

@@ -71,6 +71,9 @@ BAD = [
     dict(recent_window=4097),
     dict(recent_window=100),            # not a multiple of 128
     dict(per_sequence_plans=2),
+    dict(codec=4, k_bits=5, b_max=8),   # KIVI codes are at most 4 bits
+    dict(codec=4, v_bits=6),
+    dict(codec=5),
 ]
 
 

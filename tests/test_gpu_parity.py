@@ -106,10 +106,11 @@ def run_case(wname, T, k_bits, v_bits, codec="bgtq", pairing="half", batch=None,
 
     bounds = [0, T] if chunks is None else [0, *np.cumsum(chunks).tolist()]
     assert bounds[-1] == T
-    P = wn.packed_len(T, recent)                          # packed positions
+    grp = 128 if codec == "kivi" else 1                   # KIVI packs whole key tiles only
+    P = wn.packed_len(T, recent, grp)                     # packed positions
     # the rows each position is stored from (fp16 copies where it went through the window)
-    Ke = np.stack([wn.stored_rows(K[b], bounds, recent) for b in range(B)])
-    Ve = np.stack([wn.stored_rows(V[b], bounds, recent) for b in range(B)])
+    Ke = np.stack([wn.stored_rows(K[b], bounds, recent, grp) for b in range(B)])
+    Ve = np.stack([wn.stored_rows(V[b], bounds, recent, grp) for b in range(B)])
     Kt = torch.from_numpy(K).to(dev)
     Vt = torch.from_numpy(V).to(dev)
     for a, z in zip(bounds[:-1], bounds[1:]):
@@ -152,6 +153,9 @@ def run_case(wname, T, k_bits, v_bits, codec="bgtq", pairing="half", batch=None,
         if codec == "nf16":
             kscale = kscale.reshape(B, cap, -1)
             vscale = vscale.reshape(B, cap, -1)
+        elif codec == "kivi":
+            kscale = kscale.reshape(B, H, cap // 128, 64, 4)
+            vscale = vscale.reshape(B, H, cap // 128, 2, 128)
         else:
             kscale = kscale.reshape(B, H, cap)
             vscale = vscale.reshape(B, H, cap)
@@ -169,17 +173,22 @@ def run_case(wname, T, k_bits, v_bits, codec="bgtq", pairing="half", batch=None,
                 if codec == "nf16":
                     assert np.array_equal(kscale[b, :P], r["k_scale_blocks"].view(np.uint16))
                     assert np.array_equal(vscale[b, :P], r["v_scale_blocks"].view(np.uint16))
+                elif codec == "kivi":
+                    assert np.array_equal(kscale[b, h, :nt], r["k_params"].view(np.uint16)), f"K params b={b} h={h}"
+                    assert np.array_equal(vscale[b, h, :nt], r["v_params"].view(np.uint16)), f"V params b={b} h={h}"
                 else:
                     assert np.array_equal(kscale[b, h, :P], r["k_s16"].view(np.uint16)), f"K scales b={b} h={h}"
                     assert np.array_equal(vscale[b, h, :P], r["v_s16"].view(np.uint16)), f"V scales b={b} h={h}"
-        if recent > 0:
-            kr = cache.read(0, kvq.PART_K_RECENT, np.float16).reshape(B, recent, H, 128)
-            # values: dim-major 128-slot tiles [B][H][R/128][128][128] -> [B][R][H][128]
-            vr = cache.read(0, kvq.PART_V_RECENT, np.float16).reshape(B, H, recent // 128, 128, 128)
-            vr = vr.transpose(0, 2, 4, 1, 3).reshape(B, recent, H, 128)
+        ring = info.ring_slots          # R, or R + 128 with KIVI
+        assert ring == recent + (128 if codec == "kivi" else 0)
+        if ring > 0:
+            kr = cache.read(0, kvq.PART_K_RECENT, np.float16).reshape(B, ring, H, 128)
+            # values: dim-major 128-slot tiles [B][H][ring/128][128][128] -> [B][ring][H][128]
+            vr = cache.read(0, kvq.PART_V_RECENT, np.float16).reshape(B, H, ring // 128, 128, 128)
+            vr = vr.transpose(0, 2, 4, 1, 3).reshape(B, ring, H, 128)
             pos = np.arange(P, T)
-            assert np.array_equal(kr[:, pos % recent].view(np.uint16), Ke[:, P:].astype(np.float16).view(np.uint16))
-            assert np.array_equal(vr[:, pos % recent].view(np.uint16), Ve[:, P:].astype(np.float16).view(np.uint16))
+            assert np.array_equal(kr[:, pos % ring].view(np.uint16), Ke[:, P:].astype(np.float16).view(np.uint16))
+            assert np.array_equal(vr[:, pos % ring].view(np.uint16), Ve[:, P:].astype(np.float16).view(np.uint16))
 
     Qt = torch.from_numpy(Q).to(dev)
     out = cache.decode_attn(0, Qt, scale=sigma, n_splits=n_splits)
@@ -304,6 +313,22 @@ def test_per_sequence_plans_weighted_with_window():
     run_case("qwen3b_128k", 2500, 2, 2, batch=2, per_seq=True, n_splits=3, pairing="interleaved")
 
 
+@pytest.mark.parametrize("kb,vb", [(2, 2), (3, 3), (4, 4), (4, 2)])
+def test_kivi_codec(kb, vb):
+    """KIVI-style asymmetric integers: whole key tiles from ring and input, the last partial
+    tile in fp16."""
+    run_case("llama8b_32k", 3000, kb, vb, codec="kivi", temper=True, chunks=[1000, 1999, 1])
+
+
+def test_kivi_codec_window_and_tile_boundaries():
+    """A recent window on top (ring of R + 128 slots), appends ending on and off tile
+    boundaries, a context of exactly whole tiles, fp32 inputs, interleaved pairs."""
+    run_case("qwen3b_128k", 5000, 3, 3, codec="kivi", chunks=[2048, 2951, 1], recent=256, temper=True)
+    run_case("qwen3b_128k", 1024, 2, 2, codec="kivi", chunks=[128, 640, 256], n_splits=3)
+    run_case("qwen3b_128k", 300, 3, 3, codec="kivi", chunks=[100, 27, 1, 172], recent=128)
+    run_case("tiny", 1000, 4, 4, codec="kivi", chunks=[127, 1, 500, 372], pairing="interleaved")
+
+
 def test_rotated_uniform_codec_recent_window():
     run_case("qwen3b_128k", 5000, 3, 3, codec="rot", chunks=[2048, 2951, 1], recent=256)
 
@@ -392,6 +417,13 @@ def test_headline_layer_full_size():
     rng = np.random.default_rng(0)
     rows = np.sort(rng.choice(131072, 4096, replace=False))
     run_case("qwen3b_128k", 131072, 3, 3, layer=5, sample_rows=rows)
+
+
+def test_kivi_codec_full_size():
+    """The KIVI-style codec at the headline shape (131072 positions, K3V3): 1024 key tiles."""
+    rng = np.random.default_rng(1)
+    rows = np.sort(rng.choice(131072, 4096, replace=False))
+    run_case("qwen3b_128k", 131072, 3, 3, codec="kivi", layer=5, sample_rows=rows)
 
 
 @pytest.mark.timeout(600)
