@@ -222,10 +222,12 @@ def main():
         for label, vk, vv, R, codec in (("K3V2", 3, 2, 0, kvq.CODEC_BGTQ),
                                         ("K3V3_recent1024", 3, 3, 1024, kvq.CODEC_BGTQ),
                                         ("K3V3_uniform_rotated", 3, 3, 0, kvq.CODEC_UNIFORM_ROT),
-                                        ("K3V3_kivi", 3, 3, 0, kvq.CODEC_KIVI)):
+                                        ("K3V3_kivi", 3, 3, 0, kvq.CODEC_KIVI),
+                                        ("K3V3_bgtq_group_rotated", 3, 3, 0, kvq.CODEC_BGTQ_ROT)):
             vc = kvq.Cache(kvq.Config(1, H, Hq, B, T, vk, vv, recent_window=R, codec=codec))
-            vc.alloc_bits(0, k0d[:chunk] if codec == kvq.CODEC_BGTQ else None)
-            if codec == kvq.CODEC_UNIFORM_ROT:
+            allocates = codec in (kvq.CODEC_BGTQ, kvq.CODEC_BGTQ_ROT)
+            vc.alloc_bits(0, k0d[:chunk] if allocates else None)
+            if codec in (kvq.CODEC_UNIFORM_ROT, kvq.CODEC_BGTQ_ROT):
                 vc.set_rotation(0, np.random.default_rng(11).choice([-1, 1], size=(H, 128)).astype(np.int8))
             vc.quantize_append(0, k0d[None], v0d[None])
             vo = torch.empty(B, Hq, 128, dtype=torch.float32, device=dev)

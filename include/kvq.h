@@ -65,6 +65,11 @@ typedef enum {
                                 kvq_set_rotation) before the uniform quantizer; V as UNIFORM */
   KVQ_CODEC_NF16_B256 = 2,  /* NQKV-style: 4-bit 16-level Gaussian quantiles, absmax scale per
                                256 consecutive values of a token's [n_kv_heads*128] vector */
+  KVQ_CODEC_BGTQ_ROT = 5,   /* Block-GTQ with rotations inside equal-width groups: in plan field order
+                               each run of equal-width fields is cut into power-of-two chunks (largest
+                               first) and every chunk of m fields rotated by H_m D / sqrt(m) (caller
+                               signs D per dim, see kvq_set_rotation) after the gain normalisation;
+                               decode rotates g * q instead; V as BGTQ */
   KVQ_CODEC_KIVI = 4        /* KIVI-style asymmetric integers (the leaderboard's third method; NQKV
                                review, ablation table: keys per channel, values per token): a key
                                group is one channel over a 128-position tile, a value group is one
@@ -240,13 +245,15 @@ kvq_status kvq_key_fidelity(kvq_cache* cache, int32_t layer, const void* q, cons
                             int32_t dtype, float softmax_scale, double* mae, double* kl,
                             kvq_stream stream);
 
-/* Random signs of the key rotation of one layer (codec KVQ_CODEC_UNIFORM_ROT), after
-   "RoPE-Aware Bit Allocation for KV-Cache Quantization", abstract: the quantizer is built
-   on TQ-MSE, whose quantizer rotates the whole vector at random before scalar
-   quantization.  The stored key input is y = fp32(H (s * k) / sqrt(128)) (the fast
-   Walsh-Hadamard transform in fp64); decode and the fidelity diagnostics rotate the query
-   instead of the keys.  signs: host int8 [n_kv_heads][128], each +1 or -1; the caller draws
-   them.  Must precede the layer's first append.  Synchronizes the device.
+/* Random signs of the key rotation of one layer (codecs KVQ_CODEC_UNIFORM_ROT and
+   KVQ_CODEC_BGTQ_ROT), after RoPE-Aware Bit Allocation for KV-Cache Quantization,
+   abstract: the quantizer sits on top of TQ-MSE, whose quantizer rotates the whole vector
+   at random before scalar quantization.  UNIFORM_ROT stores y = fp32(H (s * k) / sqrt(128))
+   (the fast Walsh-Hadamard transform in fp64); BGTQ_ROT rotates the gain-normalised key
+   fp32(k * ig) chunk by chunk inside its equal-width groups (see the codec).  Decode and the
+   fidelity diagnostics rotate the query instead of the keys.  signs: host int8
+   [n_kv_heads][128] indexed by dim, each +1 or -1; the caller draws them.  Must precede the
+   layer's first append.  Synchronizes the device.
    Errors: KVQ_EINVAL (other codec, null or a value other than +-1), KVQ_ESTATE (the layer
    already holds tokens). */
 kvq_status kvq_set_rotation(kvq_cache* cache, int32_t layer, const int8_t* signs);

@@ -1,4 +1,4 @@
-"""Randomized Hadamard rotation of key rows (oracle; test infrastructure only).
+"""Randomized Hadamard rotations of key rows (oracle; test infrastructure only).
 
 RoPE-Aware Bit Allocation for KV-Cache Quantization, abstract: the allocator sits on
 top of TurboQuant-MSE (TQ-MSE).  TurboQuant's quantizer first applies a random
@@ -50,3 +50,54 @@ def unrotate(y: np.ndarray, signs: np.ndarray) -> np.ndarray:
     """R^T y = s * (H y) / sqrt(d), fp64."""
     d = y.shape[-1]
     return np.asarray(signs, dtype=np.float64) * fwht(y) / np.sqrt(float(d))
+
+
+# ---- Block-GTQ with rotations inside equal-width groups -------------------------------------
+# The allocation hands every RoPE block a width; a rotation that mixed blocks of different
+# widths would undo it.  Reading (the "rotating within equal-width groups" variant of the
+# TQ-MSE element): in the plan's field order (blocks by width descending, then index; p0 then
+# p1) the fields of each width form one contiguous run.  Each run of n fields is cut into
+# power-of-two chunks, largest first (its binary decomposition), and each chunk of m fields
+# with dims d_0 .. d_{m-1} is rotated by H_m D / sqrt(m): y_{d_k} = sum_l H_m[k, l] s_{d_l}
+# v_{d_l} / sqrt(m), with the caller's signs s indexed by dim.  The rotated input is the
+# gain-normalised key v = fp32(x * ig); the stored input is fp32 of that rotation (fp64
+# butterflies stage by stage, then the division by sqrt(m)).  Decode uses
+# <q, g * R^T y_hat> = <R (g * q), y_hat>; width-0 blocks are not stored and not rotated.
+
+
+def group_chunks(fwidths: np.ndarray):
+    """Chunks (start, size) of the stored fields (widths in plan order, all > 0)."""
+    out = []
+    f, n = 0, len(fwidths)
+    while f < n:
+        e = f
+        while e < n and fwidths[e] == fwidths[f]:
+            e += 1
+        run = e - f
+        s = f
+        for bit in range(7, -1, -1):
+            if run & (1 << bit):
+                out.append((s, 1 << bit))
+                s += 1 << bit
+        f = e
+    return out
+
+
+def rotate_in_groups(v: np.ndarray, signs: np.ndarray, fdims: np.ndarray, fwidths: np.ndarray) -> np.ndarray:
+    """R v for rows v [N, 128] (dim layout), fp64; dims of width-0 blocks are passed through."""
+    out = np.array(v, dtype=np.float64, copy=True)
+    sg = np.asarray(signs, dtype=np.float64)
+    for s, m in group_chunks(fwidths):
+        d = np.asarray(fdims[s:s + m])
+        out[:, d] = fwht(out[:, d] * sg[d]) / np.sqrt(float(m))
+    return out
+
+
+def unrotate_in_groups(y: np.ndarray, signs: np.ndarray, fdims: np.ndarray, fwidths: np.ndarray) -> np.ndarray:
+    """R^T y (R is orthogonal: each chunk's inverse is D H_m / sqrt(m)), fp64."""
+    out = np.array(y, dtype=np.float64, copy=True)
+    sg = np.asarray(signs, dtype=np.float64)
+    for s, m in group_chunks(fwidths):
+        d = np.asarray(fdims[s:s + m])
+        out[:, d] = fwht(out[:, d]) / np.sqrt(float(m)) * sg[d]
+    return out

@@ -94,7 +94,7 @@ __global__ __launch_bounds__(512) void greedy_plan(const double* __restrict__ sc
   __shared__ double mbar_s;
   __shared__ int nf_s;
 
-  const bool bgtq = codec == KVQ_CODEC_BGTQ;
+  const bool bgtq = codec_allocates(codec);
   if (tid < kBlocks) {
     const int j = tid;
     double m = 0.0;
@@ -172,20 +172,25 @@ __global__ __launch_bounds__(512) void greedy_plan(const double* __restrict__ sc
     }
   }
 
-  // rank in plan order and bit offset of the block's first field
-  int rank = 0, off = 0;
+  // rank in plan order and bit offset of the block's first field; the blocks of equal width
+  // form the run of fields [2 n_wider, 2 (n_wider + n_equal)) in plan order
+  int rank = 0, off = 0, n_wider = 0, n_equal = 0;
   for (int k = 0; k < kBlocks; ++k) {
     const int wk = w_s[k];
     if (wk > b || (wk == b && k < j)) {
       ++rank;
       off += 2 * wk;
     }
+    n_wider += wk > b ? 1 : 0;
+    n_equal += wk == b ? 1 : 0;
   }
   const int p0 = pairing == KVQ_ROPE_HALF ? j : 2 * j;
   const int p1 = pairing == KVQ_ROPE_HALF ? j + kBlocks : 2 * j + 1;
   Plan* P = plans + u;
   // fields past n_fields are zero: every lane first clears two slots, then writes its own
   if (act) {
+    P->cstart[2 * j] = P->cstart[2 * j + 1] = 0;
+    P->csize[2 * j] = P->csize[2 * j + 1] = 0;
     P->fdim[2 * j] = P->fdim[2 * j + 1] = 0;
     P->fwidth[2 * j] = P->fwidth[2 * j + 1] = 0;
     P->foff[2 * j] = P->foff[2 * j + 1] = 0;
@@ -200,6 +205,22 @@ __global__ __launch_bounds__(512) void greedy_plan(const double* __restrict__ sc
     P->foff[2 * rank] = static_cast<uint16_t>(off);
     P->foff[2 * rank + 1] = static_cast<uint16_t>(off + b);
     P->pdesc[rank] = static_cast<uint32_t>(off) | (static_cast<uint32_t>(b) << 16);
+    // rotation chunks: the run's power-of-two pieces, largest first
+    for (int e = 0; e < 2; ++e) {
+      const int f = 2 * rank + e;
+      int start = 2 * n_wider, o = f - start, n = 2 * n_equal;
+      for (int bit = 7; bit >= 0; --bit) {
+        const int m = 1 << bit;
+        if (!(n & m)) continue;
+        if (o < m) {
+          P->cstart[f] = static_cast<uint8_t>(start);
+          P->csize[f] = static_cast<uint8_t>(m);
+          break;
+        }
+        o -= m;
+        start += m;
+      }
+    }
   }
   P->g[p0] = P->g[p1] = g;
   P->ig[p0] = P->ig[p1] = ig;
@@ -217,7 +238,7 @@ hipError_t launch_alloc(kvq_cache* c, int layer, const void* keys, int dtype, in
                         const double* block_weight, hipStream_t stream) {
   const kvq_config& cfg = c->cfg;
   const int H = cfg.n_kv_heads;
-  const bool bgtq = cfg.codec == KVQ_CODEC_BGTQ;
+  const bool bgtq = codec_allocates(cfg.codec);
   const int64_t n_chunks = bgtq ? (n_tok + kEnergyChunk - 1) / kEnergyChunk : 0;
   if (bgtq) {
     dim3 grid(static_cast<unsigned>(n_chunks), static_cast<unsigned>(H), static_cast<unsigned>(c->n_plan));

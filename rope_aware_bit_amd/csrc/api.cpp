@@ -31,7 +31,7 @@ bool config_valid(const kvq_config* c) {
   if (c->n_q_heads % c->n_kv_heads != 0) return false;
   const int G = c->n_q_heads / c->n_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return false;
-  if (c->codec < KVQ_CODEC_BGTQ || c->codec > KVQ_CODEC_KIVI) return false;
+  if (c->codec < KVQ_CODEC_BGTQ || c->codec > KVQ_CODEC_BGTQ_ROT) return false;
   if (c->recent_window < 0 || c->recent_window > kvq::kMaxRecent || c->recent_window % 128) return false;
   if (c->pairing != KVQ_ROPE_HALF && c->pairing != KVQ_ROPE_INTERLEAVED) return false;
   if (c->per_sequence_plans != 0 && c->per_sequence_plans != 1) return false;
@@ -168,7 +168,7 @@ kvq_status kvq_cache_create(const kvq_config* cfg, kvq_cache** out) {
     if (st == KVQ_OK) st = dev_alloc(reinterpret_cast<void**>(&c->v_recent), c->recent_layer * L, "recent V");
   }
   if (st == KVQ_OK) st = dev_alloc(reinterpret_cast<void**>(&c->plans), sizeof(kvq::Plan) * L * c->n_plan * H, "plans");
-  if (st == KVQ_OK && cfg->codec == KVQ_CODEC_UNIFORM_ROT)
+  if (st == KVQ_OK && kvq::codec_rotates(cfg->codec))
     st = dev_alloc(reinterpret_cast<void**>(&c->rot_signs), L * H * kHeadDim, "rotation signs");
   if (st == KVQ_OK) st = dev_alloc(reinterpret_cast<void**>(&c->tables), sizeof(kvq::Tables), "tables");
   if (st == KVQ_OK)
@@ -227,7 +227,7 @@ kvq_status kvq_alloc_bits(kvq_cache* c, int32_t layer, const void* keys, int32_t
                           int64_t n_tok, const double* block_weight, kvq_stream stream) {
   if (!layer_ok(c, layer)) return KVQ_EINVAL;
   if (dtype != KVQ_F16 && dtype != KVQ_F32) return KVQ_EINVAL;
-  const bool bgtq = c->cfg.codec == KVQ_CODEC_BGTQ;
+  const bool bgtq = kvq::codec_allocates(c->cfg.codec);
   if (bgtq && (!keys || n_tok < 1)) return KVQ_EINVAL;
   if (bgtq && reinterpret_cast<uintptr_t>(keys) % 16) {
     g_last_error = "alloc_bits: keys must be 16-byte aligned";
@@ -293,7 +293,7 @@ kvq_status kvq_quantize_append(kvq_cache* c, int32_t layer, const void* k, const
     return KVQ_EINVAL;
   }
   if (!c->plan_ready[layer]) return KVQ_ESTATE;
-  if (c->cfg.codec == KVQ_CODEC_UNIFORM_ROT && !c->rot_ready[layer]) return KVQ_ESTATE;
+  if (kvq::codec_rotates(c->cfg.codec) && !c->rot_ready[layer]) return KVQ_ESTATE;
   if (c->len[layer] + n_new > c->cfg.max_tokens) return KVQ_ECAPACITY;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t len = c->len[layer], R = c->cfg.recent_window;
@@ -383,7 +383,7 @@ kvq_status kvq_key_fidelity(kvq_cache* c, int32_t layer, const void* q, const vo
 }
 
 kvq_status kvq_set_rotation(kvq_cache* c, int32_t layer, const int8_t* signs) {
-  if (!layer_ok(c, layer) || !signs || c->cfg.codec != KVQ_CODEC_UNIFORM_ROT) return KVQ_EINVAL;
+  if (!layer_ok(c, layer) || !signs || !kvq::codec_rotates(c->cfg.codec)) return KVQ_EINVAL;
   const int64_t n = static_cast<int64_t>(c->cfg.n_kv_heads) * kHeadDim;
   for (int64_t i = 0; i < n; ++i)
     if (signs[i] != 1 && signs[i] != -1) return KVQ_EINVAL;

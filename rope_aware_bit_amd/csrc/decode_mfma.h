@@ -433,7 +433,7 @@ template <int G, int VB, bool NF, int W, bool KV>
 __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     const void* __restrict__ qv, int q_f32, float sigma, int64_t len, int n_packed_splits,
     const __half* __restrict__ rk, const __half* __restrict__ rv, int R, int64_t n_recent,
-    const int8_t* __restrict__ rot, int n_kv, int64_t cap,
+    const int8_t* __restrict__ rot, int rot_groups, int n_kv, int64_t cap,
     int tiles_per_split, const Plan* __restrict__ plans, int plan_bs, const Tables* __restrict__ tabg,
     const uint32_t* __restrict__ kc, const uint32_t* __restrict__ vc, const uint16_t* __restrict__ ks,
     const uint16_t* __restrict__ vs, int k_words, int n_nf, int n_splits, int n_mergers, int region_words,
@@ -649,7 +649,46 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   // rotated keys (randomized Hadamard R = H D / sqrt(128)): <q, R^T y> = <R q, y>, so the
   // packed splits rotate the scaled query (fast Walsh-Hadamard stages in fp32); the recent
   // window holds unrotated keys
-  if (rot != nullptr && !recent_wg) {
+  if (rot != nullptr && !recent_wg && rot_groups) {
+    // rotation inside equal-width groups: <q, g * R^T y> = <R (g * q), y>.  In plan field
+    // order, chunk (start, m) of each equal-width run gets the signs, the butterflies of
+    // H_m (stage h pairs fields f, f + h with (f - start) & h == 0) and 1/sqrt(m), in fp32,
+    // on the gain-scaled query held by dim
+    uint8_t* gcs = reinterpret_cast<uint8_t*>(dyn_s + G * kHeadDim);   // [0]: start, [128]: size
+    const int nfs = __builtin_amdgcn_readfirstlane(nf_r);
+    if (setup_wave) {
+      if (tid < kHeadDim) {
+        gcs[tid] = P->cstart[tid];
+        gcs[kHeadDim + tid] = P->csize[tid];
+      }
+      for (int k = tid; k < G * kHeadDim; k += 256) {
+        const int f = k % kHeadDim;
+        if (f < nfs) qs_s[k / kHeadDim][fdim_s[f]] *= static_cast<float>(rot[h * kHeadDim + fdim_s[f]]);
+      }
+    }
+    lds_barrier();
+    for (int hb = 1; hb < kHeadDim; hb <<= 1) {
+      if (setup_wave) {
+        for (int k = tid; k < G * kHeadDim; k += 256) {
+          const int hh = k / kHeadDim, f = k % kHeadDim;
+          if (hb < gcs[kHeadDim + f] && ((f - gcs[f]) & hb) == 0) {
+            const int d0 = fdim_s[f], d1 = fdim_s[f + hb];
+            const float a = qs_s[hh][d0], bq = qs_s[hh][d1];
+            qs_s[hh][d0] = a + bq;
+            qs_s[hh][d1] = a - bq;
+          }
+        }
+      }
+      lds_barrier();
+    }
+    if (setup_wave) {
+      for (int k = tid; k < G * kHeadDim; k += 256) {
+        const int f = k % kHeadDim;
+        if (f < nfs) qs_s[k / kHeadDim][fdim_s[f]] *= 1.0f / sqrtf(static_cast<float>(gcs[kHeadDim + f]));
+      }
+    }
+    lds_barrier();
+  } else if (rot != nullptr && !recent_wg) {
     if (setup_wave) {
       for (int k = tid; k < G * kHeadDim; k += 256)
         qs_s[k / kHeadDim][k % kHeadDim] *= static_cast<float>(rot[h * kHeadDim + k % kHeadDim]);
@@ -1131,7 +1170,8 @@ hipError_t launch_gvw(kvq_cache* c, int layer, const void* q, int q_f32, float s
   const __half* rk = n_recent > 0 ? layer_k_recent(c, layer) : nullptr;
   const __half* rv = n_recent > 0 ? layer_v_recent(c, layer) : nullptr;
   const int R = c->ring;
-  const int8_t* rot = cfg.codec == KVQ_CODEC_UNIFORM_ROT ? c->rot_signs + static_cast<int64_t>(layer) * cfg.n_kv_heads * kHeadDim : nullptr;
+  const int8_t* rot = codec_rotates(cfg.codec) ? c->rot_signs + static_cast<int64_t>(layer) * cfg.n_kv_heads * kHeadDim : nullptr;
+  const int rot_groups = cfg.codec == KVQ_CODEC_BGTQ_ROT ? 1 : 0;
   dim3 grid(S_all, cfg.n_kv_heads, cfg.batch);
   const size_t dyn = static_cast<size_t>(W) * sh.region_words * sizeof(uint32_t);
   const Plan* plans = c->plans + static_cast<int64_t>(layer) * c->n_plan * cfg.n_kv_heads;
@@ -1139,7 +1179,7 @@ hipError_t launch_gvw(kvq_cache* c, int layer, const void* q, int q_f32, float s
   const int mergers = decode_split_mergers(S_all, static_cast<int64_t>(cfg.batch) * cfg.n_kv_heads, c->n_cu);
 #define KVQ_LAUNCH_DEC(NF, KV)                                                                         \
   hipLaunchKernelGGL((decode_mfma<G, VB, NF, W, KV>), grid, dim3(64 * W), dyn, stream, q, q_f32, sigma,   \
-                     plen, S, rk, rv, R, n_recent, rot, cfg.n_kv_heads, c->cap, tps, plans, plan_bs,        \
+                     plen, S, rk, rv, R, n_recent, rot, rot_groups, cfg.n_kv_heads, c->cap, tps, plans, plan_bs, \
                      c->tables, layer_k_codes(c, layer), layer_v_codes(c, layer), layer_k_scales(c, layer), \
                      layer_v_scales(c, layer), c->k_words, c->n_nf_blocks, S_all, mergers, sh.region_words,  \
                      sh.v_early, sh.v_off, c->part_o, c->part_l, c->part_mt, c->split_epochs, out)

@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256, 2) void fidelity_partials(
     const T* __restrict__ q, const T* __restrict__ keys, int64_t len, int n_kv, int64_t cap,
     double sigma, int64_t tok_per_split, const Plan* __restrict__ plans, int plan_bs, const Tables* __restrict__ tab,
     const uint32_t* __restrict__ kc, const uint16_t* __restrict__ ks, int k_words, int n_nf, int nf,
-    int kivi, int pairing,
+    int kivi, int pairing, int rot_groups,
     int64_t plen, const __half* __restrict__ rk, int R, const int8_t* __restrict__ rot,
     double* __restrict__ part, int S) {
   constexpr int kVec = 16 / sizeof(T);
@@ -156,8 +156,44 @@ __global__ __launch_bounds__(256, 2) void fidelity_partials(
   if (tid == 0) nf_s = P->n_fields;
   __syncthreads();
   const int n_fields = nf_s;
-  // rotated codec: <q, R^T y> = <R q, y> with R q = H (s * q) / sqrt(128), in fp64
-  if (rot != nullptr) {
+  // rotated codecs: <q, R^T y> = <R q, y>.  Inside equal-width groups (fp64): R (g * q), chunk
+  // by chunk in plan field order (signs, butterflies, 1/sqrt(m)); the gains are then inside
+  // the rotated query
+  if (rot != nullptr && rot_groups) {
+    __shared__ uint8_t cst_s[kHeadDim], csz_s[kHeadDim];
+    if (tid < kHeadDim) {
+      cst_s[tid] = P->cstart[tid];
+      csz_s[tid] = P->csize[tid];
+    }
+    for (int k = tid; k < G * kHeadDim; k += 256) {
+      const int d = k % kHeadDim;
+      qr_s[k / kHeadDim][d] = q_s[k / kHeadDim][d] * g_s[d];
+    }
+    __syncthreads();
+    for (int k = tid; k < G * kHeadDim; k += 256) {
+      const int f = k % kHeadDim;
+      if (f < n_fields) qr_s[k / kHeadDim][fdim_s[f]] *= static_cast<double>(rot[h * kHeadDim + fdim_s[f]]);
+    }
+    __syncthreads();
+    for (int hb = 1; hb < kHeadDim; hb <<= 1) {
+      for (int k = tid; k < G * kHeadDim; k += 256) {
+        const int hh = k / kHeadDim, f = k % kHeadDim;
+        if (hb < csz_s[f] && ((f - cst_s[f]) & hb) == 0) {
+          const int d0 = fdim_s[f], d1 = fdim_s[f + hb];
+          const double a = qr_s[hh][d0], bq = qr_s[hh][d1];
+          qr_s[hh][d0] = a + bq;
+          qr_s[hh][d1] = a - bq;
+        }
+      }
+      __syncthreads();
+    }
+    for (int k = tid; k < G * kHeadDim; k += 256) {
+      const int f = k % kHeadDim;
+      if (f < n_fields) qr_s[k / kHeadDim][fdim_s[f]] /= sqrt(static_cast<double>(csz_s[f]));
+    }
+    __syncthreads();
+    if (tid < kHeadDim) g_s[tid] = 1.0;
+  } else if (rot != nullptr) {
     for (int k = tid; k < G * kHeadDim; k += 256)
       qr_s[k / kHeadDim][k % kHeadDim] = q_s[k / kHeadDim][k % kHeadDim] * static_cast<double>(rot[h * kHeadDim + k % kHeadDim]);
     __syncthreads();
@@ -376,9 +412,10 @@ hipError_t launch_fidelity(kvq_cache* c, int layer, const void* q, const void* k
   hipLaunchKernelGGL((fidelity_partials<T, GG>), grid, dim3(256), 0, stream, static_cast<const T*>(q), \
                      static_cast<const T*>(keys), len, H, c->cap, sigma, per, plans, plan_bs, c->tables, \
                      layer_k_codes(c, layer), layer_k_scales(c, layer), c->k_words, c->n_nf_blocks,   \
-                     nf ? 1 : 0, cfg.codec == KVQ_CODEC_KIVI ? 1 : 0, cfg.pairing, plen, plen < len ? layer_k_recent(c, layer) : nullptr,       \
+                     nf ? 1 : 0, cfg.codec == KVQ_CODEC_KIVI ? 1 : 0, cfg.pairing,                  \
+                     cfg.codec == KVQ_CODEC_BGTQ_ROT ? 1 : 0, plen, plen < len ? layer_k_recent(c, layer) : nullptr,       \
                      c->ring > 0 ? c->ring : 1,                                                   \
-                     cfg.codec == KVQ_CODEC_UNIFORM_ROT ? c->rot_signs + static_cast<int64_t>(layer) * H * kHeadDim : nullptr, \
+                     codec_rotates(cfg.codec) ? c->rot_signs + static_cast<int64_t>(layer) * H * kHeadDim : nullptr, \
                      c->fid_part, static_cast<int>(S))
 #define KVQ_FID_G(T)                  \
   switch (G) {                        \

@@ -52,9 +52,15 @@ struct alignas(16) Plan {
   uint8_t dwidth[kHeadDim];          // width of dim i
   int8_t bwidth[kBlocks];            // width of block j
   uint32_t pdesc[kBlocks];           // stored block (pair) r in plan order: bit offset | width << 16
+  uint8_t cstart[kHeadDim];          // field f's rotation chunk (power-of-two piece of its
+  uint8_t csize[kHeadDim];           //   equal-width run): first field and size; 0 past n_fields
   int32_t n_fields;                  // stored fields (2 x blocks with width > 0)
   int32_t pad[3];
 };
+
+// Codecs whose K widths come from the allocation, and codecs that rotate keys.
+__host__ __device__ inline bool codec_allocates(int codec) { return codec == KVQ_CODEC_BGTQ || codec == KVQ_CODEC_BGTQ_ROT; }
+__host__ __device__ inline bool codec_rotates(int codec) { return codec == KVQ_CODEC_UNIFORM_ROT || codec == KVQ_CODEC_BGTQ_ROT; }
 
 // Host-side tables builder (independent implementation of the codebook definitions).
 void build_tables(Tables* t);
@@ -83,7 +89,7 @@ struct kvq_cache {
   int pack_group;              // positions are packed in whole groups of this many (KIVI: 128)
   kvq::Plan* plans;            // [L][n_plan][H]
   int n_plan;                  // plans per (layer, KV head): batch with per-sequence plans, else 1
-  int8_t* rot_signs;           // key-rotation signs [L][H][128] (codec UNIFORM_ROT)
+  int8_t* rot_signs;           // key-rotation signs [L][H][128] (codecs UNIFORM_ROT, BGTQ_ROT)
   uint8_t* rot_ready;          // per layer: signs set
   kvq::Tables* tables;         // device copy
   kvq::Tables host_tables;

@@ -45,7 +45,8 @@ __device__ inline float inv_scale(__half s16) {
   return s == 0.0f ? 0.0f : __fdiv_rn(1.0f, s);
 }
 
-template <typename T, bool NF, bool ROT>
+// RM: key rotation, 0 none, 1 the whole row (uniform codec), 2 inside equal-width groups
+template <typename T, bool NF, int RM>
 __global__ __launch_bounds__(kThreads) void quantize_append(
     const T* __restrict__ kin, const T* __restrict__ vin, int64_t n_new, int64_t in_stride, int ring_R, int64_t L0, int n_kv,
     int64_t cap, const Plan* __restrict__ plans, int plan_bs, const Tables* __restrict__ tab,
@@ -125,6 +126,16 @@ __global__ __launch_bounds__(kThreads) void quantize_append(
     foff_s[tid] = P->foff[tid];
     vw_s[tid][0] = vw_s[tid][1] = vw_s[tid][2] = vw_s[tid][3] = 0u;
   }
+  // rotation inside equal-width groups: field f's chunk, and each dim's chunk size (0: the
+  // dim's block is not stored)
+  __shared__ uint8_t cst_s[RM == 2 ? kHeadDim : 1], csz_s[RM == 2 ? kHeadDim : 1], dsz_s[RM == 2 ? kHeadDim : 1];
+  if constexpr (RM == 2) {
+    if (tid < kHeadDim) {
+      cst_s[tid] = P->cstart[tid];
+      csz_s[tid] = P->csize[tid];
+      dsz_s[tid] = 0;
+    }
+  }
   for (int k = tid; k < kGroupTok * k_words; k += kThreads) krow_s[k] = 0u;
   if (tid == 0) nf_s = P->n_fields;
   __syncthreads();
@@ -133,9 +144,43 @@ __global__ __launch_bounds__(kThreads) void quantize_append(
   //      Walsh-Hadamard stages in fp64 (exact for fp16 keys), one rounding at the division and
   //      one to fp32; the K rows below are then read from ky_s ----
   // (only the rotating instantiation carries these buffers)
-  __shared__ double rw_s[ROT ? kGroupTok : 1][ROT ? kHeadDim : 1];
-  __shared__ float ky_s[ROT ? kGroupTok : 1][ROT ? kHeadDim : 1];
-  if constexpr (ROT) {
+  __shared__ double rw_s[RM ? kGroupTok : 1][RM ? kHeadDim : 1];
+  __shared__ float ky_s[RM ? kGroupTok : 1][RM ? kHeadDim : 1];
+  if constexpr (RM == 2) {
+    // gain-normalised rows v = fp32(x * ig), signs on the stored dims, then in plan field
+    // order the butterflies of each power-of-two chunk of an equal-width run (stage h pairs
+    // fields f, f + h with (f - chunk start) & h == 0), fp64, and the division by sqrt(m)
+    const int8_t* sg = rot + h * kHeadDim;
+    if (tid < nf_s) dsz_s[fdim_s[tid]] = csz_s[tid];
+    __syncthreads();
+    for (int e = tid; e < kGroupTok * kHeadDim; e += kThreads) {
+      const int r = e / kHeadDim, i = e % kHeadDim;
+      const double v = static_cast<double>(__fmul_rn(xval(0, 0, r, i), ig_s[i]));
+      rw_s[r][i] = dsz_s[i] ? v * static_cast<double>(sg[i]) : v;
+    }
+    __syncthreads();
+    for (int hb = 1; hb < kHeadDim; hb <<= 1) {
+      for (int e = tid; e < kGroupTok * kHeadDim; e += kThreads) {
+        const int r = e / kHeadDim, f = e % kHeadDim;
+        if (hb < csz_s[f] && ((f - cst_s[f]) & hb) == 0) {
+          const int d0 = fdim_s[f], d1 = fdim_s[f + hb];
+          const double a = rw_s[r][d0], b = rw_s[r][d1];
+          rw_s[r][d0] = __dadd_rn(a, b);
+          rw_s[r][d1] = __dsub_rn(a, b);
+        }
+      }
+      __syncthreads();
+    }
+    for (int e = tid; e < kGroupTok * kHeadDim; e += kThreads) {
+      const int r = e / kHeadDim, i = e % kHeadDim;
+      const int m = dsz_s[i];
+      ky_s[r][i] = m ? static_cast<float>(__ddiv_rn(rw_s[r][i], __dsqrt_rn(static_cast<double>(m))))
+                     : static_cast<float>(rw_s[r][i]);
+    }
+    if (tid < kHeadDim) ig_s[tid] = 1.0f;   // the gains are inside the rotated rows now
+    __syncthreads();
+  }
+  if constexpr (RM == 1) {
     const int8_t* sg = rot + h * kHeadDim;
     for (int e = tid; e < kGroupTok * kHeadDim; e += kThreads) {
       const int r = e / kHeadDim, i = e % kHeadDim;
@@ -161,7 +206,7 @@ __global__ __launch_bounds__(kThreads) void quantize_append(
   }
   // K value i of staged row r of this head (rotated when the codec rotates)
   auto kval = [&](int r, int i) {
-    if constexpr (ROT) return ky_s[r][i];
+    if constexpr (RM != 0) return ky_s[r][i];
     else return xval(0, NF ? (h - h0) : 0, r, i);
   };
 
@@ -180,10 +225,10 @@ __global__ __launch_bounds__(kThreads) void quantize_append(
       // are issued together and only the fp64 sum is a dependent chain
       double ss = 0.0;
       const float* krot = nullptr;
-      if constexpr (ROT) krot = &ky_s[r][0];
+      if constexpr (RM != 0) krot = &ky_s[r][0];
 #pragma unroll 16
       for (int i = 0; i < kHeadDim; ++i) {
-        const float x = (ROT && tsr == 0) ? krot[i] : xval(tsr, hsel, r, i);
+        const float x = (RM != 0 && tsr == 0) ? krot[i] : xval(tsr, hsel, r, i);
         const double y = static_cast<double>(__fmul_rn(x, tsr == 0 ? ig_s[i] : 1.0f));
         ss = __dadd_rn(ss, __dmul_rn(y, y));
       }
@@ -291,20 +336,26 @@ hipError_t launch_quantize(kvq_cache* c, int layer, const void* k, const void* v
   dim3 grid(static_cast<unsigned>(last - first + 1), static_cast<unsigned>(cfg.n_kv_heads),
             static_cast<unsigned>(cfg.batch));
   const bool nf = cfg.codec == KVQ_CODEC_NF16_B256;
-  const bool rotk = cfg.codec == KVQ_CODEC_UNIFORM_ROT;
+  const int rm = cfg.codec == KVQ_CODEC_UNIFORM_ROT ? 1 : cfg.codec == KVQ_CODEC_BGTQ_ROT ? 2 : 0;
   const Plan* plans = c->plans + static_cast<int64_t>(layer) * c->n_plan * cfg.n_kv_heads;
   const int plan_bs = c->n_plan > 1 ? cfg.n_kv_heads : 0;
-#define KVQ_LAUNCH_Q(T, NF, ROT)                                                                 \
-  hipLaunchKernelGGL((quantize_append<T, NF, ROT>), grid, dim3(kThreads), 0, stream,            \
+#define KVQ_LAUNCH_Q(T, NF, RM)                                                                  \
+  hipLaunchKernelGGL((quantize_append<T, NF, RM>), grid, dim3(kThreads), 0, stream,             \
                      static_cast<const T*>(k), static_cast<const T*>(v), n_new, in_stride, ring_R, L0, \
                      cfg.n_kv_heads, c->cap, plans, plan_bs, c->tables, layer_k_codes(c, layer), \
                      layer_v_codes(c, layer), layer_k_scales(c, layer), layer_v_scales(c, layer), \
                      c->k_words, cfg.v_bits, c->n_nf_blocks,                                      \
-                     cfg.codec == KVQ_CODEC_UNIFORM_ROT ? c->rot_signs + static_cast<int64_t>(layer) * cfg.n_kv_heads * kHeadDim : nullptr)
+                     rm ? c->rot_signs + static_cast<int64_t>(layer) * cfg.n_kv_heads * kHeadDim : nullptr)
   if (dtype == KVQ_F16) {
-    if (nf) KVQ_LAUNCH_Q(__half, true, false); else if (rotk) KVQ_LAUNCH_Q(__half, false, true); else KVQ_LAUNCH_Q(__half, false, false);
+    if (nf) KVQ_LAUNCH_Q(__half, true, 0);
+    else if (rm == 1) KVQ_LAUNCH_Q(__half, false, 1);
+    else if (rm == 2) KVQ_LAUNCH_Q(__half, false, 2);
+    else KVQ_LAUNCH_Q(__half, false, 0);
   } else {
-    if (nf) KVQ_LAUNCH_Q(float, true, false); else if (rotk) KVQ_LAUNCH_Q(float, false, true); else KVQ_LAUNCH_Q(float, false, false);
+    if (nf) KVQ_LAUNCH_Q(float, true, 0);
+    else if (rm == 1) KVQ_LAUNCH_Q(float, false, 1);
+    else if (rm == 2) KVQ_LAUNCH_Q(float, false, 2);
+    else KVQ_LAUNCH_Q(float, false, 0);
   }
 #undef KVQ_LAUNCH_Q
   return hipGetLastError();

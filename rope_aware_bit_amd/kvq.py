@@ -18,7 +18,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so"
 
 KVQ_OK, KVQ_EINVAL, KVQ_ENOMEM, KVQ_ECAPACITY, KVQ_ESTATE, KVQ_EHIP = range(6)
 KVQ_F16, KVQ_F32 = 0, 1
-CODEC_BGTQ, CODEC_UNIFORM, CODEC_NF16_B256, CODEC_UNIFORM_ROT, CODEC_KIVI = 0, 1, 2, 3, 4
+CODEC_BGTQ, CODEC_UNIFORM, CODEC_NF16_B256, CODEC_UNIFORM_ROT, CODEC_KIVI, CODEC_BGTQ_ROT = 0, 1, 2, 3, 4, 5
 ROPE_HALF, ROPE_INTERLEAVED = 0, 1
 PART_K_CODES, PART_V_CODES, PART_K_SCALES, PART_V_SCALES, PART_K_RECENT, PART_V_RECENT = range(6)
 
@@ -223,7 +223,8 @@ class Cache:
         _check(lib.kvq_alloc_bits(self._h, layer, kp, dt, n, wp, _stream(stream)), "kvq_alloc_bits")
 
     def set_rotation(self, layer: int, signs):
-        """Key-rotation signs of `layer` (codec CODEC_UNIFORM_ROT): int8 [n_kv_heads, 128] of +-1."""
+        """Key-rotation signs of `layer` (codecs CODEC_UNIFORM_ROT, CODEC_BGTQ_ROT): int8
+        [n_kv_heads, 128] of +-1, indexed by dim."""
         sg = np.ascontiguousarray(np.asarray(signs, dtype=np.int8))
         if sg.shape != (self.cfg.n_kv_heads, self.cfg.head_dim):
             raise ValueError(f"signs must be [n_kv_heads, head_dim], got {sg.shape}")

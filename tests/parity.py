@@ -15,7 +15,7 @@ from oracle import quantize as qz
 from oracle import rotation as rt
 
 PAIRING = {"half": 0, "interleaved": 1}
-CODEC = {"bgtq": 0, "uniform": 1, "nf16": 2, "rot": 3, "kivi": 4}
+CODEC = {"bgtq": 0, "uniform": 1, "nf16": 2, "rot": 3, "kivi": 4, "bgtq_rot": 5}
 
 ABS_TOL = 2e-3
 REL_L2_TOL = 1e-3
@@ -43,7 +43,7 @@ class OracleLayer:
         self.k_bits, self.v_bits, self.codec, self.pairing = k_bits, v_bits, codec, pairing
         self.signs = signs   # key-rotation signs [H, 128] of the rotated codec
         H = calib.shape[1] if calib is not None else None
-        if codec == "bgtq":
+        if codec in ("bgtq", "bgtq_rot"):
             self.widths, self.g, self.ig, self.m = al.allocate(calib, k_bits, b_min, b_max, pairing,
                                                                block_weight=block_weight)
         else:
@@ -80,6 +80,13 @@ class OracleLayer:
             igd = al.dim_values(self.ig[h], 128, self.pairing)
             if self.codec == "rot":
                 ck, sk, _ = qz.quantize_rows(rt.rotate_rows_fp32(k_rows, self.signs[h]), wd)
+            elif self.codec == "bgtq_rot":
+                # gain-normalised rows, rotated inside the equal-width groups, then quantized
+                # with unit gains
+                y32 = (np.asarray(k_rows).astype(np.float32) * igd.astype(np.float32)[None, :]).astype(np.float32)
+                dims, ws = self.fields(h)
+                yr = rt.rotate_in_groups(y32.astype(np.float64), self.signs[h], dims, ws).astype(np.float32)
+                ck, sk, _ = qz.quantize_rows(yr, wd)
             else:
                 ck, sk, _ = qz.quantize_rows(k_rows, wd, igd)
             cv, sv, _ = qz.quantize_rows(v_rows, np.full(128, self.v_bits))
@@ -99,7 +106,12 @@ class OracleLayer:
             return lv, vv
         wd = al.dim_widths(self.widths[h], 128, self.pairing)
         gd = al.dim_values(self.g[h], 128, self.pairing)
-        kh = at.dequant_k(q_out["k_codes"], q_out["k_s16"], wd, gd)
+        if self.codec == "bgtq_rot":
+            dims, ws = self.fields(h)
+            kh = at.dequant_k(q_out["k_codes"], q_out["k_s16"], wd, np.ones(128, np.float32))
+            kh = rt.unrotate_in_groups(kh, self.signs[h], dims, ws) * gd.astype(np.float64)[None, :]
+        else:
+            kh = at.dequant_k(q_out["k_codes"], q_out["k_s16"], wd, gd)
         if self.codec == "rot":
             kh = rt.unrotate(kh, self.signs[h])
         vh = at.dequant_v(q_out["v_codes"], q_out["v_s16"], self.v_bits)

@@ -73,7 +73,7 @@ BAD = [
     dict(per_sequence_plans=2),
     dict(codec=4, k_bits=5, b_max=8),   # KIVI codes are at most 4 bits
     dict(codec=4, v_bits=6),
-    dict(codec=5),
+    dict(codec=6),
 ]
 
 

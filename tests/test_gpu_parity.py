@@ -78,15 +78,17 @@ def run_case(wname, T, k_bits, v_bits, codec="bgtq", pairing="half", batch=None,
         e = qv[..., p0] ** 2 + qv[..., p1] ** 2
         bw = np.ascontiguousarray(np.mean(e, axis=2) if per_seq else np.mean(e, axis=(0, 2)))   # [(B,) H, 64]
     # the rotated codec's signs are drawn here and passed to both sides
-    signs = np.random.default_rng(7).choice([-1, 1], size=(H, 128)).astype(np.int8) if codec == "rot" else None
+    signs = (np.random.default_rng(7).choice([-1, 1], size=(H, 128)).astype(np.int8)
+             if codec in ("rot", "bgtq_rot") else None)
+    alloc = codec in ("bgtq", "bgtq_rot")     # widths from the allocation (calibration keys)
     if per_seq:
-        ols = [OracleLayer(calib[b] if codec == "bgtq" else K[b, :1], k_bits, v_bits, codec, pairing,
+        ols = [OracleLayer(calib[b] if alloc else K[b, :1], k_bits, v_bits, codec, pairing,
                            b_min, b_max, block_weight=None if bw is None else bw[b], signs=signs)
                for b in range(B)]
         # the sequences' plans must really differ, or the case would not test the indexing
         assert B == 1 or any(not np.array_equal(ols[0].widths, o.widths) for o in ols[1:])
     else:
-        ols = [OracleLayer(calib if codec == "bgtq" else K[:, :1].reshape(B, H, 128), k_bits, v_bits,
+        ols = [OracleLayer(calib if alloc else K[:, :1].reshape(B, H, 128), k_bits, v_bits,
                            codec, pairing, b_min, b_max, block_weight=bw, signs=signs)] * B
 
     cfg = kvq.Config(n_layers=1, n_kv_heads=H, n_q_heads=Hq, batch=B, max_tokens=T, k_bits=k_bits,
@@ -94,7 +96,7 @@ def run_case(wname, T, k_bits, v_bits, codec="bgtq", pairing="half", batch=None,
                      pairing=PAIRING[pairing], recent_window=recent, per_sequence_plans=int(per_seq))
     cache = kvq.Cache(cfg)
     dev = torch.device("cuda:0")
-    cache.alloc_bits(0, torch.from_numpy(np.ascontiguousarray(calib)).to(dev) if codec == "bgtq" else None,
+    cache.alloc_bits(0, torch.from_numpy(np.ascontiguousarray(calib)).to(dev) if alloc else None,
                      block_weight=torch.from_numpy(bw).to(dev) if bw is not None else None)
     if signs is not None:
         cache.set_rotation(0, signs)
@@ -327,6 +329,19 @@ def test_kivi_codec_window_and_tile_boundaries():
     run_case("qwen3b_128k", 1024, 2, 2, codec="kivi", chunks=[128, 640, 256], n_splits=3)
     run_case("qwen3b_128k", 300, 3, 3, codec="kivi", chunks=[100, 27, 1, 172], recent=128)
     run_case("tiny", 1000, 4, 4, codec="kivi", chunks=[127, 1, 500, 372], pairing="interleaved")
+
+
+@pytest.mark.parametrize("kb,noise", [(2, "gauss"), (3, "t5"), (4, "gauss")])
+def test_bgtq_group_rotation(kb, noise):
+    """Block-GTQ with rotations inside equal-width groups: codes bit-exact, decode and
+    fidelity to the usual bars."""
+    run_case("llama8b_32k", 3000, kb, kb, codec="bgtq_rot", temper=True, chunks=[1000, 1999, 1], noise=noise)
+
+
+def test_bgtq_group_rotation_window_and_limits():
+    run_case("qwen3b_128k", 5000, 3, 3, codec="bgtq_rot", chunks=[2048, 2951, 1], recent=256, temper=True)
+    run_case("qwen3b_128k", 2000, 3, 3, codec="bgtq_rot", b_min=2, b_max=4, pairing="interleaved", n_splits=2)
+    run_case("tiny", 1000, 4, 4, codec="bgtq_rot", zero_blocks=(1, 2))
 
 
 def test_rotated_uniform_codec_recent_window():

@@ -88,3 +88,69 @@ def test_block_allocation_beats_rotated_uniform_on_logit_mae(bits):
     mae_b, _ = fd.logit_fidelity(q, kt, np.stack(kb))
     mae_r, _ = fd.logit_fidelity(q, kt, np.stack(kr))
     assert mae_b.mean() < mae_r.mean(), (mae_b.mean(), mae_r.mean())
+
+
+# ---- rotations inside equal-width groups ---------------------------------------------------
+
+def test_group_chunks_hand_example():
+    w = np.array([5, 5, 4, 4, 4, 4, 4, 4, 3, 3, 3, 3, 3, 3, 3, 3, 3, 3, 3, 3, 3, 3, 2, 2])
+    # runs: 2 fives, 6 fours (4 + 2), 14 threes (8 + 4 + 2), 2 twos
+    assert rt.group_chunks(w) == [(0, 2), (2, 4), (6, 2), (8, 8), (16, 4), (20, 2), (22, 2)]
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_group_chunks_partition_runs_in_binary_order(seed):
+    rng = np.random.default_rng(seed)
+    w = np.sort(rng.integers(1, 9, size=64))[::-1].repeat(2)     # a plan: pairs, widest first
+    ch = rt.group_chunks(w)
+    assert [s for s, _ in ch] == list(np.cumsum([0] + [m for _, m in ch])[:-1])
+    assert sum(m for _, m in ch) == len(w)
+    for s, m in ch:
+        assert m & (m - 1) == 0 and len(set(w[s:s + m])) == 1
+    for width in set(w.tolist()):
+        sizes = [m for s, m in ch if w[s] == width]
+        assert sizes == sorted(sizes, reverse=True) and sum(sizes) == int((w == width).sum())
+        assert len(sizes) == bin(sum(sizes)).count("1")
+
+
+def _plan(seed):
+    rng = np.random.default_rng(seed)
+    K = rng.standard_normal((256, 1, 128)) * np.exp(rng.standard_normal(128))
+    widths, _, _, _ = al.allocate(K, 3)
+    dims, ws = al.field_order(widths[0], 128, "half")
+    return widths[0], dims, ws
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_group_rotation_matrix_structure(seed):
+    """R is orthogonal, never mixes dims of different widths, and each chunk is the Sylvester
+    Hadamard matrix with the signs, over sqrt(m), in field order."""
+    widths, dims, ws = _plan(seed)
+    s = np.random.default_rng(50 + seed).choice([-1.0, 1.0], size=128)
+    R = rt.rotate_in_groups(np.eye(128), s, dims, ws).T       # column j = R e_j
+    stored = np.zeros(128, bool)
+    stored[dims] = True
+    Rs = R[np.ix_(stored, stored)]
+    assert np.allclose(Rs @ Rs.T, np.eye(stored.sum()), atol=1e-14)
+    wd = al.dim_widths(widths, 128, "half")
+    nz = np.abs(R) > 0
+    assert not np.any(nz & (wd[:, None] != wd[None, :]))
+    for st, m in rt.group_chunks(ws):
+        d = dims[st:st + m]
+        assert np.allclose(R[np.ix_(d, d)], linalg.hadamard(m) * s[d][None, :] / np.sqrt(m), atol=1e-15)
+    # width-0 dims pass through
+    for i in np.flatnonzero(~stored):
+        assert R[i, i] == 1.0 and np.count_nonzero(R[:, i]) == 1
+
+
+def test_group_rotation_inverts_and_keeps_group_energy():
+    widths, dims, ws = _plan(7)
+    rng = np.random.default_rng(8)
+    s = rng.choice([-1.0, 1.0], size=128)
+    x = rng.standard_normal((9, 128))
+    y = rt.rotate_in_groups(x, s, dims, ws)
+    assert np.allclose(rt.unrotate_in_groups(y, s, dims, ws), x, atol=1e-13)
+    wd = al.dim_widths(widths, 128, "half")
+    for width in set(wd.tolist()):
+        g = wd == width
+        assert np.allclose((y[:, g] ** 2).sum(1), (x[:, g] ** 2).sum(1), rtol=1e-13)
