@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 PLAN_BYTES_PER_HEAD = 1024   # field dims/widths/offsets and gains read by each decode launch
+APPEND_STEPS = 24               # new positions of the append-and-attend steps (2 warm-up + 22 timed)
 CPU_SAMPLE_S = 10.0          # lower bound on the host time spent timing the oracle
 DECODE_SOURCES = ["decode_mfma.h", "decode_mfma.hip", "decode_mfma_g1.hip", "decode_mfma_g2.hip",
                   "decode_mfma_g4.hip", "decode_mfma_g8.hip", "kvq_internal.h"]
@@ -151,7 +152,8 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
 
-    cache = kvq.Cache(kvq.Config(L, H, Hq, B, T, kb, vb))
+    # capacity for the T cached positions plus the new ones of the append-and-attend steps
+    cache = kvq.Cache(kvq.Config(L, H, Hq, B, T + APPEND_STEPS, kb, vb))
     gen = TorchLayerGen(w, dev)
     chunk = min(w.calib_tokens, T)
     app_ms = []
@@ -298,6 +300,33 @@ def main():
     fid_flops = 2 * 2 * 128 * B * T * Hq          # two fp64 dot products per (position, query head)
     del keys0
 
+    # the decode step as a model runs it: every layer first appends the new position's K and V
+    # (one quantize_append of one position per sequence), then attends over the cache holding it
+    step_app = None
+    if not args.decode_only:
+        g = torch.Generator(device=dev).manual_seed(5)
+        new_kv = [(torch.randn(B, 1, H, 128, device=dev, generator=g).half(),
+                   torch.randn(B, 1, H, 128, device=dev, generator=g).half()) for _ in range(L)]
+
+        def step_with_append():
+            for layer in range(L):
+                cache.quantize_append(layer, new_kv[layer][0], new_kv[layer][1])
+                cache.decode_attn(layer, qs[layer], out=outs[layer])
+
+        n_warm, n_timed = 2, APPEND_STEPS - 2
+        for _ in range(n_warm):
+            step_with_append()
+        torch.cuda.synchronize()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        for _ in range(n_timed):
+            step_with_append()
+        s1.record(stream)
+        torch.cuda.synchronize()
+        ms_app = s0.elapsed_time(s1) / n_timed
+        step_app = {"ms_per_step": round(ms_app, 5), "tokens_per_s": round(B / (ms_app * 1e-3), 2),
+                    "steps": n_timed, "append_us_per_layer": round((ms_app - ms_step) * 1e3 / L, 2)}
+
     # average decode-launch duration: the timed region holds only decode launches on this stream
     launch_us = ms_step * 1e3 / L
 
@@ -331,6 +360,7 @@ def main():
             "GB/s": round((B * H * chunk * (2 * 128 * 2 + (kb + vb) * 16 + 4)) /
                           (float(np.mean(app_ms)) * 1e-3) / 1e9, 2),
         },
+        "decode_step_with_append": step_app,
         "variants": variants,
         "fidelity": None if not fid_reps else {
             "layer": 0,
