@@ -86,7 +86,7 @@ def run_case(wname, T, k_bits, v_bits, codec="bgtq", pairing="half", batch=None,
                            b_min, b_max, block_weight=None if bw is None else bw[b], signs=signs)
                for b in range(B)]
         # the sequences' plans must really differ, or the case would not test the indexing
-        assert B == 1 or any(not np.array_equal(ols[0].widths, o.widths) for o in ols[1:])
+        assert B == 1 or not alloc or any(not np.array_equal(ols[0].widths, o.widths) for o in ols[1:])
     else:
         ols = [OracleLayer(calib if alloc else K[:, :1].reshape(B, H, 128), k_bits, v_bits,
                            codec, pairing, b_min, b_max, block_weight=bw, signs=signs)] * B
@@ -342,6 +342,14 @@ def test_bgtq_group_rotation_window_and_limits():
     run_case("qwen3b_128k", 5000, 3, 3, codec="bgtq_rot", chunks=[2048, 2951, 1], recent=256, temper=True)
     run_case("qwen3b_128k", 2000, 3, 3, codec="bgtq_rot", b_min=2, b_max=4, pairing="interleaved", n_splits=2)
     run_case("tiny", 1000, 4, 4, codec="bgtq_rot", zero_blocks=(1, 2))
+
+
+def test_codec_combinations():
+    """Per-sequence plans under the group rotation; the KIVI-style codec over a batch with a
+    window; the group rotation with fp32 inputs over several appends."""
+    run_case("llama8b_b64", 1500, 3, 3, codec="bgtq_rot", batch=3, per_seq=True, chunks=[1000, 499, 1], temper=True)
+    run_case("llama8b_b64", 1000, 2, 4, codec="kivi", batch=3, per_seq=True, chunks=[300, 700], recent=128)
+    run_case("tiny", 1000, 3, 3, codec="bgtq_rot", chunks=[1, 126, 873])
 
 
 def test_rotated_uniform_codec_recent_window():
