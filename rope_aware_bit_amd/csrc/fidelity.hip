@@ -13,12 +13,15 @@
 //
 // Kernel 1 (fidelity_partials): one 256-lane workgroup per (split, KV head, sequence).  It
 // stages 64 positions at a time (the given keys with 16-byte loads, the packed rows, the
-// scales).  Four lanes share a position: each takes a quarter of the dims (given row) and of
-// the fields (stored row) for all G heads, in fp64, and the quarters are summed across the
-// four lanes.  Lane quarter q then keeps running statistics of heads q and q + 4: sum
-// |a - a^|, and for each distribution a running maximum M, the sum Z = sum e^(x - M) and
-// (for a) W = sum e^(a - M_a) (a - a^).  The lanes' statistics are merged within each wave,
-// then across the four waves, and the split's six numbers per head are stored.
+// scales).  Wave w takes positions 16 w .. 16 w + 15 of a round and forms both sets of logits
+// as fp64 16x16x4 matrix products (positions x dims times dims x query heads, 32 steps of 4
+// dims): each lane supplies one element of the position operand per step (a given key value,
+// or a stored one decoded from its packed field, its codebook entry and scales) and one of the
+// query operand.  The lane holding column h then keeps running statistics of head h over its
+// four positions per round: sum |a - a^|, and for each distribution a running maximum M, the
+// sum Z = sum e^(x - M) and (for a) W = sum e^(a - M_a) (a - a^).  The lanes' statistics are
+// merged within each wave, then across the four waves, and the split's six numbers per head
+// are stored.
 // Kernel 2 (fidelity_merge): one wave per (sequence, query head) merges the splits and
 // writes mae = sum |a - a^| / T and kl = W / Z_a - M_a - ln Z_a + M_b + ln Z_b.
 #include <hip/hip_fp16.h>
@@ -31,6 +34,7 @@ namespace kvq {
 namespace {
 
 constexpr int kFidTok = 64;       // positions staged per round
+typedef double d4 __attribute__((ext_vector_type(4)));
 constexpr int kFidStats = 6;      // sum|d|, M_a, Z_a, W_a, M_b, Z_b
 
 template <typename T>
@@ -121,7 +125,7 @@ __global__ __launch_bounds__(256, 2) void fidelity_partials(
   constexpr int kVec = 16 / sizeof(T);
   constexpr int kRow = kHeadDim + kVec;            // padded key row (elements)
   const int tid = threadIdx.x;
-  const int t = tid >> 2, quarter = tid & 3;   // position of the round, quarter of the row
+  const int wave = tid >> 6, mi = tid & 15, kq = (tid & 63) >> 4;   // MFMA row / column, k slot
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int64_t bh = static_cast<int64_t>(b) * n_kv + h;
   const int64_t t_begin = s * tok_per_split;
@@ -147,7 +151,11 @@ __global__ __launch_bounds__(256, 2) void fidelity_partials(
     const int w = k >> 8, c = k & 255;
     cb_s[w][c] = nf ? (w == 4 && c < 16 ? tab->nf_cb[c] : 0) : (w >= 1 ? tab->cb[w][c] : 0);
   }
+  __shared__ uint16_t dfo_s[kHeadDim];   // bit offset of dim d's field in the packed row
+  __shared__ uint8_t dfw_s[kHeadDim];    // its width (0: the dim is not stored)
   if (tid < kHeadDim) {
+    dfw_s[tid] = 0;
+    dfo_s[tid] = 0;
     g_s[tid] = nf ? 1.0 : static_cast<double>(P->g[tid]);
     fdim_s[tid] = P->fdim[tid];
     fw_s[tid] = P->fwidth[tid];
@@ -156,6 +164,10 @@ __global__ __launch_bounds__(256, 2) void fidelity_partials(
   if (tid == 0) nf_s = P->n_fields;
   __syncthreads();
   const int n_fields = nf_s;
+  if (tid < n_fields) {
+    dfw_s[fdim_s[tid]] = fw_s[tid];
+    dfo_s[fdim_s[tid]] = foff_s[tid];
+  }
   // rotated codecs: <q, R^T y> = <R q, y>.  Inside equal-width groups (fp64): R (g * q), chunk
   // by chunk in plan field order (signs, butterflies, 1/sqrt(m)); the gains are then inside
   // the rotated query
@@ -214,9 +226,18 @@ __global__ __launch_bounds__(256, 2) void fidelity_partials(
   }
   __syncthreads();
 
-  Stats st[2];
-  stats_init(st[0]);
-  stats_init(st[1]);
+  Stats st;   // head mi's statistics over this lane's positions
+  stats_init(st);
+  // which rows of the product this lane's four results belong to: one product of the row
+  // numbers (A[i][0] = i + 1) with ones (B[0][j] = 1) tells, whatever the register layout
+  int prow[4];
+  {
+    const d4 z = {0.0, 0.0, 0.0, 0.0};
+    const d4 pr = __builtin_amdgcn_mfma_f64_16x16x4f64(kq == 0 ? static_cast<double>(mi + 1) : 0.0,
+                                                       kq == 0 ? 1.0 : 0.0, z, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) prow[r] = static_cast<int>(pr[r]) - 1;
+  }
   for (int64_t r0 = t_begin; r0 < t_end; r0 += kFidTok) {
     const int nr = t_end - r0 < kFidTok ? static_cast<int>(t_end - r0) : kFidTok;
     // stage the given keys (16-byte pieces), the packed rows and the scales
@@ -252,100 +273,70 @@ __global__ __launch_bounds__(256, 2) void fidelity_partials(
     }
     if (tid < kFidTok) kr_s[tid][k_words] = 0u;   // zero word after the row (fields read two words)
     __syncthreads();
-    if (t < nr) {
-      // lane (t, quarter): dims 32 quarter .. + 31 of the given row and fields 32 quarter ..
-      // + 31 of the stored row, for all G heads; the four quarters are then summed
-      double a[G], ah[G];
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) a[hh] = ah[hh] = 0.0;
-      constexpr int kPer = 32 / kVec;   // 16-byte pieces per quarter row
-#pragma unroll 1
-      for (int cc = 0; cc < kPer; ++cc) {
-        const int c = quarter * kPer + (cc + quarter) % kPer;   // rotated: fewer bank conflicts
-        const uint4 raw = *reinterpret_cast<const uint4*>(&x_s[t][c * kVec]);
-        T xv[kVec];
-        __builtin_memcpy(xv, &raw, 16);
-#pragma unroll
-        for (int e = 0; e < kVec; ++e) {
-          const double x = to_d(xv[e]);
-#pragma unroll
-          for (int hh = 0; hh < G; ++hh) a[hh] += x * q_s[hh][c * kVec + e];
-        }
-      }
-      if (r0 + t >= plen) {
-        // recent window: the stored key is the fp16 copy (dims of this quarter)
-#pragma unroll 1
-        for (int c = 4 * quarter; c < 4 * quarter + 4; ++c) {
-          const uint4 raw = *reinterpret_cast<const uint4*>(&xr_s[t][8 * c]);
-          __half xv[8];
-          __builtin_memcpy(xv, &raw, 16);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const double x = static_cast<double>(__half2float(xv[e]));
-#pragma unroll
-            for (int hh = 0; hh < G; ++hh) ah[hh] += x * q_s[hh][8 * c + e];
+    // wave w: positions 16 w .. 16 w + 15 of the round as fp64 16x16x4 products, rows =
+    // positions, columns = query heads (G of 16 used), 4 dims per step:
+    //   a = <x_t, q_h> (given keys), a_hat = <k_hat_t, q'_h> (stored keys; q' = q rotated,
+    //   with the gains inside for the group rotation), plus <window row, q_h> for recent rows
+    // lane l gives A[l % 16][l / 16] and B[l / 16][l % 16] and holds D[prow[r]][l % 16]
+    {
+      const int tl = 16 * wave + mi;                   // this lane's A row (staged position)
+      const bool valid = tl < nr;
+      const bool packed = valid && r0 + tl < plen;
+      const bool ring = valid && r0 + tl >= plen;
+      const bool any_packed = r0 + 16 * wave < plen && 16 * wave < nr;
+      const bool any_ring = r0 + 16 * wave + 15 >= plen && 16 * wave < nr;
+      const double s16 = packed ? sc_s[tl] : 0.0;
+      d4 da = {0.0, 0.0, 0.0, 0.0}, db = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+      for (int kk = 0; kk < kHeadDim / 4; ++kk) {
+        const int d = 4 * kk + kq;
+        const double bq = mi < G ? q_s[mi][d] : 0.0;
+        const double ag = valid ? to_d(x_s[tl][d]) : 0.0;
+        da = __builtin_amdgcn_mfma_f64_16x16x4f64(ag, bq, da, 0, 0, 0);
+        if (any_packed) {
+          double ap = 0.0;
+          const int w = dfw_s[d];
+          if (packed && w > 0) {
+            const int off = dfo_s[d];
+            const uint64_t two = static_cast<uint64_t>(kr_s[tl][off >> 5]) |
+                                 (static_cast<uint64_t>(kr_s[tl][(off >> 5) + 1]) << 32);
+            const uint32_t code = static_cast<uint32_t>(two >> (off & 31)) & ((1u << w) - 1u);
+            // asymmetric integer codec: fp16(lo + s * code) with one rounding
+            ap = kivi ? static_cast<double>(__half2float(__hfma(ksc_s[d], __float2half_rn(static_cast<float>(code)), klo_s[d])))
+                      : (s16 * g_s[d]) * static_cast<double>(__half2float(__ushort_as_half(cb_s[w][code])));
           }
+          const double br = mi < G ? qr_s[mi][d] : 0.0;
+          db = __builtin_amdgcn_mfma_f64_16x16x4f64(ap, br, db, 0, 0, 0);
+        }
+        if (any_ring) {
+          // recent window: the stored key is the fp16 copy, against the plain query
+          const double ar = ring ? static_cast<double>(__half2float(xr_s[tl][d])) : 0.0;
+          db = __builtin_amdgcn_mfma_f64_16x16x4f64(ar, bq, db, 0, 0, 0);
         }
       }
-      const double s16 = sc_s[t];
-      const int f_end = r0 + t >= plen ? 0 : n_fields < 32 * quarter + 32 ? n_fields : 32 * quarter + 32;
-#pragma unroll 2
-      for (int f = 32 * quarter; f < f_end; ++f) {
-        const int off = foff_s[f], w = fw_s[f], dim = fdim_s[f];
-        const uint64_t two = static_cast<uint64_t>(kr_s[t][off >> 5]) |
-                             (static_cast<uint64_t>(kr_s[t][(off >> 5) + 1]) << 32);
-        const uint32_t code = static_cast<uint32_t>(two >> (off & 31)) & ((1u << w) - 1u);
-        const double c = static_cast<double>(__half2float(__ushort_as_half(cb_s[w][code])));
-        // asymmetric integer codec: fp16(lo + s * code) with one rounding
-        const double kh = kivi ? static_cast<double>(__half2float(__hfma(ksc_s[dim], __float2half_rn(static_cast<float>(code)), klo_s[dim])))
-                               : (s16 * g_s[dim]) * c;
+      if (mi < G) {
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) ah[hh] += kh * qr_s[hh][dim];
-      }
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        a[hh] += __shfl_xor(a[hh], 1);
-        a[hh] += __shfl_xor(a[hh], 2);
-        ah[hh] += __shfl_xor(ah[hh], 1);
-        ah[hh] += __shfl_xor(ah[hh], 2);
-      }
-      // lane (t, quarter) keeps the statistics of heads quarter and quarter + 4
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int hl = quarter + 4 * j;
-        if (hl >= G) continue;
-        double av = a[0], bv = ah[0];
-#pragma unroll
-        for (int hh = 1; hh < G; ++hh) {
-          if (hh == hl) {
-            av = a[hh];
-            bv = ah[hh];
-          }
+        for (int r = 0; r < 4; ++r) {
+          if (16 * wave + prow[r] < nr) stats_add(st, sigma * da[r], sigma * db[r]);
         }
-        stats_add(st[j], sigma * av, sigma * bv);
       }
     }
     __syncthreads();
   }
-  // merge the wave's positions (lanes of one quarter), then the four waves through LDS
+  // merge the lanes of one head (l % 16) in the wave, then the four waves through LDS
   __shared__ double wst_s[4][kMaxGroup][kFidStats];
-  const int wave = tid >> 6;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    for (int m = 4; m <= 32; m <<= 1) {
-      const Stats o = stats_shfl_xor(st[j], m);
-      stats_merge(st[j], o);
-    }
-    const int hl = quarter + 4 * j;
-    if ((tid & 63) < 4 && hl < G) {
-      double* d = wst_s[wave][hl];
-      d[0] = st[j].abs_sum;
-      d[1] = st[j].ma;
-      d[2] = st[j].za;
-      d[3] = st[j].wa;
-      d[4] = st[j].mb;
-      d[5] = st[j].zb;
-    }
+  for (int m = 16; m <= 32; m <<= 1) {
+    const Stats o = stats_shfl_xor(st, m);
+    stats_merge(st, o);
+  }
+  if (kq == 0 && mi < G) {
+    double* d = wst_s[wave][mi];
+    d[0] = st.abs_sum;
+    d[1] = st.ma;
+    d[2] = st.za;
+    d[3] = st.wa;
+    d[4] = st.mb;
+    d[5] = st.zb;
   }
   __syncthreads();
   if (tid < G) {
