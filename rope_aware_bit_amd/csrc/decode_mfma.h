@@ -521,6 +521,14 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   // CB_8[st] and CB_7[st % 128]
   const uint32_t cb8 = reinterpret_cast<const uint16_t*>(gimg + single_table_base(8))[st];
   const uint32_t cb7 = reinterpret_cast<const uint16_t*>(gimg + single_table_base(7))[st & 127];
+  // rotation inside equal-width groups: the chunk (start | size << 8) of field st % 128 and the
+  // sign of dim st % 128
+  uint32_t rg_chunk = 0u;
+  float rg_sign = 1.0f;
+  if (rot_groups && rot != nullptr) {
+    rg_chunk = static_cast<uint32_t>(P->cstart[st & 127]) | (static_cast<uint32_t>(P->csize[st & 127]) << 8);
+    rg_sign = static_cast<float>(rot[h * kHeadDim + (st & 127)]);
+  }
 
   // K rows of tokens lane and lane + 64 (first 16 words), scales of tokens 16 tg + n, V segments
   uint4 ka[4], kb2[4];
@@ -654,24 +662,19 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     // order, chunk (start, m) of each equal-width run gets the signs, the butterflies of
     // H_m (stage h pairs fields f, f + h with (f - start) & h == 0) and 1/sqrt(m), in fp32,
     // on the gain-scaled query held by dim
-    uint8_t* gcs = reinterpret_cast<uint8_t*>(dyn_s + G * kHeadDim);   // [0]: start, [128]: size
+    // (set-up thread t handles dim t % 128 for the signs and field t % 128 for the chunks; the
+    // signs of dims whose blocks are not stored are applied too, and never read)
     const int nfs = __builtin_amdgcn_readfirstlane(nf_r);
+    const int c_start = static_cast<int>(rg_chunk & 0xFFu), c_size = static_cast<int>(rg_chunk >> 8);
     if (setup_wave) {
-      if (tid < kHeadDim) {
-        gcs[tid] = P->cstart[tid];
-        gcs[kHeadDim + tid] = P->csize[tid];
-      }
-      for (int k = tid; k < G * kHeadDim; k += 256) {
-        const int f = k % kHeadDim;
-        if (f < nfs) qs_s[k / kHeadDim][fdim_s[f]] *= static_cast<float>(rot[h * kHeadDim + fdim_s[f]]);
-      }
+      for (int k = tid; k < G * kHeadDim; k += 256) qs_s[k / kHeadDim][k % kHeadDim] *= rg_sign;
     }
     lds_barrier();
     for (int hb = 1; hb < kHeadDim; hb <<= 1) {
       if (setup_wave) {
         for (int k = tid; k < G * kHeadDim; k += 256) {
           const int hh = k / kHeadDim, f = k % kHeadDim;
-          if (hb < gcs[kHeadDim + f] && ((f - gcs[f]) & hb) == 0) {
+          if (hb < c_size && ((f - c_start) & hb) == 0) {
             const int d0 = fdim_s[f], d1 = fdim_s[f + hb];
             const float a = qs_s[hh][d0], bq = qs_s[hh][d1];
             qs_s[hh][d0] = a + bq;
@@ -684,7 +687,7 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     if (setup_wave) {
       for (int k = tid; k < G * kHeadDim; k += 256) {
         const int f = k % kHeadDim;
-        if (f < nfs) qs_s[k / kHeadDim][fdim_s[f]] *= 1.0f / sqrtf(static_cast<float>(gcs[kHeadDim + f]));
+        if (f < nfs) qs_s[k / kHeadDim][fdim_s[f]] *= 1.0f / sqrtf(static_cast<float>(c_size));
       }
     }
     lds_barrier();
