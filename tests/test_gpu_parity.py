@@ -434,6 +434,49 @@ def test_error_states():
     cache.close()
 
 
+def test_codec_error_states():
+    """Rotation signs: required before the first append, only +-1, only for rotating codecs,
+    not after an append.  KIVI below one tile: everything in fp16, decode still works."""
+    torch = _torch()
+    kvq = _kvq()
+    dev = torch.device("cuda:0")
+    x = torch.randn(1, 200, 2, 128, device=dev).half()
+    q = torch.randn(1, 16, 128, device=dev).half()
+    rc = kvq.Cache(kvq.Config(1, 2, 16, 1, 300, 3, 3, codec=kvq.CODEC_BGTQ_ROT))
+    rc.alloc_bits(0, x[0, :64].contiguous())
+    with pytest.raises(kvq.KvqError) as e:
+        rc.quantize_append(0, x, x)                           # no signs yet
+    assert e.value.status == kvq.KVQ_ESTATE
+    bad = np.ones((2, 128), np.int8)
+    bad[1, 7] = 2
+    with pytest.raises(kvq.KvqError) as e:
+        rc.set_rotation(0, bad)
+    assert e.value.status == kvq.KVQ_EINVAL
+    rc.set_rotation(0, np.ones((2, 128), np.int8))
+    rc.quantize_append(0, x, x)
+    with pytest.raises(kvq.KvqError) as e:
+        rc.set_rotation(0, np.ones((2, 128), np.int8))         # after an append
+    assert e.value.status == kvq.KVQ_ESTATE
+    assert torch.isfinite(rc.decode_attn(0, q)).all()
+    rc.close()
+    bc = kvq.Cache(kvq.Config(1, 2, 16, 1, 300, 3, 3))
+    with pytest.raises(kvq.KvqError) as e:
+        bc.set_rotation(0, np.ones((2, 128), np.int8))         # codec does not rotate
+    assert e.value.status == kvq.KVQ_EINVAL
+    bc.close()
+    pc = kvq.Cache(kvq.Config(1, 2, 16, 2, 300, 3, 3, per_sequence_plans=1))
+    with pytest.raises(ValueError):
+        pc.alloc_bits(0, x[0, :64].contiguous())             # needs [batch, n_tok, heads, dim]
+    pc.close()
+    kc = kvq.Cache(kvq.Config(1, 2, 16, 1, 300, 2, 2, codec=kvq.CODEC_KIVI))
+    kc.alloc_bits(0)
+    kc.quantize_append(0, x[:, :100].contiguous(), x[:, :100].contiguous())
+    info = kc.layer_info(0)
+    assert info.packed_len == 0 and info.ring_slots == 128 and info.len == 100
+    assert torch.isfinite(kc.decode_attn(0, q)).all()
+    kc.close()
+
+
 def test_headline_layer_full_size():
     """Qwen2.5-3B-shaped layer at 131072 tokens, K3V3: sampled K rows, all V tiles and
     scales bit-exact; decode (auto split count, as benchmarked) vs fp64 oracle."""
