@@ -79,11 +79,15 @@ def cpu_baseline(k0, v0, q0, calib, kb, vb, n_layers, bytes_per_step):
     from tests.parity import OracleLayer
 
     H = k0.shape[1]
-    ol = OracleLayer(calib, kb, vb)
-    packed = []
-    for h in range(H):                      # quantize + pack (not timed: that is the append)
-        r = ol.quantize_head(k0[:, h], v0[:, h], h)
-        packed.append((r["k_words"], r["k_s16"], lay.pack_v_tiles(r["v_codes"], vb), r["v_s16"]))
+    with threadpool_limits(limits=1):
+        t_a = time.perf_counter()
+        ol = OracleLayer(calib, kb, vb)         # allocation from the calibration keys
+        t_q = time.perf_counter()
+        packed = []
+        for h in range(H):                      # quantize + pack every position (the appends)
+            r = ol.quantize_head(k0[:, h], v0[:, h], h)
+            packed.append((r["k_words"], r["k_s16"], lay.pack_v_tiles(r["v_codes"], vb), r["v_s16"]))
+        t_e = time.perf_counter()
     T = k0.shape[0]
 
     def one_layer():
@@ -112,6 +116,8 @@ def cpu_baseline(k0, v0, q0, calib, kb, vb, n_layers, bytes_per_step):
         "tokens_per_s": round(1.0 / step_s, 5),
         "cores": 1,
         "kind": "oracle",
+        "alloc_s_per_layer": round(t_q - t_a, 3),
+        "quantize_s_per_layer": round(t_e - t_q, 3),
         "sample": f"layer 0 of {n_layers} ({H} KV heads x {T} tokens), decoded {reps} times: unpack + "
                   f"fp64 dequantize + fp64 attention took {dt:.2f} s per layer; scaled x{n_layers} "
                   f"to one step",
@@ -214,6 +220,14 @@ def main():
     ms_step = ev0.elapsed_time(ev1) / args.steps
     for o in outs:
         assert torch.isfinite(o).all()
+    # spread of single steps (a second pass, each step between its own events)
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, z in step_ev:
+        a.record(stream)
+        step()
+        z.record(stream)
+    torch.cuda.synchronize()
+    step_ms = np.array([a.elapsed_time(z) for a, z in step_ev])
 
     # variants on layer 0's data (one layer each): the asymmetric K3V2 budget, and an fp16 recent
     # window of 1024 positions; decode launches timed like the step
@@ -340,6 +354,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        "ms_per_step_p10_p50_p90": [round(float(np.percentile(step_ms, p)), 5) for p in (10, 50, 90)],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
