@@ -148,6 +148,7 @@ def main():
 
     from rope_aware_bit_amd import kvq
     from synth import WORKLOADS
+    from synth import gen_layer as gen_layer_np
     from synth import gen_query as gen_query_np
     from synth.torch_gen import TorchLayerGen
 
@@ -297,6 +298,49 @@ def main():
                                         "frac_of_hbm_peak": round(bbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
         bc.close()
 
+    # quality side-report: each codec on one Llama-3.1-8B-shaped layer (8 KV / 32 query heads,
+    # 8192 positions, Gaussian and Student-t(5) noise): logit MAE and softmax KL of the stored
+    # keys (the library's diagnostics) and the decode output's relative L2 error against fp64
+    # attention over the unquantized keys and values (torch, fp64)
+    quality = None
+    if not args.decode_only:
+        quality = {}
+        wq = WORKLOADS["llama8b_32k"]
+        Tq, Hk, Hqq = 8192, wq.n_kv, wq.n_q
+        codecs = (("bgtq_K3V3", kvq.CODEC_BGTQ, 3), ("uniform_K3V3", kvq.CODEC_UNIFORM, 3),
+                  ("uniform_rotated_K3V3", kvq.CODEC_UNIFORM_ROT, 3),
+                  ("bgtq_group_rotated_K3V3", kvq.CODEC_BGTQ_ROT, 3), ("kivi_K3V3", kvq.CODEC_KIVI, 3),
+                  ("bgtq_K4V4", kvq.CODEC_BGTQ, 4), ("nf16_K4V4", kvq.CODEC_NF16_B256, 4))
+        for noise in ("gauss", "t5"):
+            kq_np, vq_np = gen_layer_np(wq, 0, 0, Tq, noise=noise)
+            qq_np = gen_query_np(wq, 0, Tq, noise=noise)
+            kq = torch.from_numpy(kq_np).to(dev)[None].contiguous()
+            vq = torch.from_numpy(vq_np).to(dev)[None].contiguous()
+            qq = torch.from_numpy(qq_np).to(dev)[None].contiguous()
+            k64, v64, q64 = kq[0].double(), vq[0].double(), qq[0].double()
+            ref = torch.empty(Hqq, 128, dtype=torch.float64, device=dev)
+            for hq in range(Hqq):
+                lg = (k64[:, hq // wq.group].contiguous() @ q64[hq]) / float(np.sqrt(128.0))
+                ref[hq] = torch.softmax(lg, dim=0) @ v64[:, hq // wq.group].contiguous()
+            rows = {}
+            for label, codec, bits in codecs:
+                qc = kvq.Cache(kvq.Config(1, Hk, Hqq, 1, Tq, bits, bits, codec=codec))
+                qc.alloc_bits(0, kq[0, :wq.calib_tokens].contiguous()
+                              if codec in (kvq.CODEC_BGTQ, kvq.CODEC_BGTQ_ROT) else None)
+                if codec in (kvq.CODEC_UNIFORM_ROT, kvq.CODEC_BGTQ_ROT):
+                    qc.set_rotation(0, np.random.default_rng(11).choice([-1, 1], size=(Hk, 128)).astype(np.int8))
+                qc.quantize_append(0, kq, vq)
+                o = qc.decode_attn(0, qq)
+                mae_q, kl_q = qc.key_fidelity(0, qq, kq)
+                torch.cuda.synchronize()
+                err = float(torch.linalg.norm(o[0].double() - ref) / torch.linalg.norm(ref))
+                rows[label] = {"logit_mae": round(float(mae_q.mean()), 5),
+                               "softmax_kl": float(f"{float(kl_q.mean()):.5g}"),
+                               "out_rel_l2": float(f"{err:.4g}")}
+                qc.close()
+            quality[noise] = rows
+            del kq, vq, qq, k64, v64, q64, ref
+
     # key-fidelity diagnostics of layer 0 (logit MAE and softmax KL against the given keys)
     fid_reps = 0 if args.decode_only else 5
     fid_us, mae, kl = float("nan"), torch.full((1,), float("nan")), torch.full((1,), float("nan"))
@@ -376,6 +420,7 @@ def main():
                           (float(np.mean(app_ms)) * 1e-3) / 1e9, 2),
         },
         "decode_step_with_append": step_app,
+        "quality": None if quality is None else {"workload": "llama8b_32k layer 0, 8192 positions", **quality},
         "variants": variants,
         "fidelity": None if not fid_reps else {
             "layer": 0,
