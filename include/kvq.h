@@ -188,14 +188,18 @@ kvq_status kvq_get_plan(const kvq_cache* cache, int32_t layer, int8_t* bits, flo
           16-byte aligned.
    n_new = 0 is a no-op.  Row quantizer, in IEEE fp32/fp64 with no fused ops:
    y = x * ig_j; s = fp16(fp32(sqrt(sum y^2 / 128))); u = y * fp32(1/s);
-   code = number of codebook boundaries below u.  NF16: s = fp16(absmax) per
-   256 values, u = x * fp32(1/s).
+   code = number of codebook boundaries below u (the sum of squares in dim order).
+   NF16: s = fp16(absmax) per 256 values, u = x * fp32(1/s).  Rotating codecs
+   quantize the rotated rows (see kvq_codec); KIVI quantizes whole 128-position
+   key tiles (see kvq_codec) and keeps the positions after the last whole tile in
+   fp16.
    With a recent window R > 0, positions stay in fp16 (rounded once if given in
    fp32) while they are among the last R of the sequence; a position is
    quantized, from its fp16 copy, when it leaves the window, so the packed
-   storage always covers positions 0 .. len-R-1.
-   Errors: KVQ_EINVAL, KVQ_ESTATE (no plan for the layer, or no rotation signs for the
-   rotated codec), KVQ_ECAPACITY. */
+   storage always covers positions 0 .. len-R-1 (KIVI: rounded down to a
+   multiple of 128).
+   Errors: KVQ_EINVAL, KVQ_ESTATE (no plan for the layer, or no rotation signs for a
+   rotating codec), KVQ_ECAPACITY. */
 kvq_status kvq_quantize_append(kvq_cache* cache, int32_t layer, const void* k, const void* v,
                                int32_t dtype, int64_t n_new, kvq_stream stream);
 
