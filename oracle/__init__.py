@@ -25,9 +25,17 @@ quantize    per-row scale, codebook lookup; the per-256-value absmax codec.
 layout      bit packing of K rows and dim-major V tiles, and unpacking.
 attention   dequantization, fp64 GQA decode attention, RoPE block identity,
             compression arithmetic.
+fidelity    logit MAE and softmax KL of stored keys against the given ones.
+window      which positions pass through the fp16 recent window; packed length
+            (also in whole 128-position groups).
+rotation    randomized Hadamard rotations: of the whole row, and inside the
+            plan's equal-width groups.
+kivi        the KIVI-style asymmetric integer codec (keys per channel over
+            128-position tiles, values per position) and its parameter layout.
 
 Every function is pinned by a ``-m "not gpu"`` test against something other
 than itself (closed forms, textbook values, library routines, brute force or
 invariants); see tests/test_oracle_*.py.
 """
 from . import codebooks, allocation, quantize, layout, attention  # noqa: F401
+from . import fidelity, window, rotation, kivi  # noqa: F401
