@@ -32,10 +32,13 @@ rotation    randomized Hadamard rotations: of the whole row, and inside the
             plan's equal-width groups.
 kivi        the KIVI-style asymmetric integer codec (keys per channel over
             128-position tiles, values per position) and its parameter layout.
+codecs      each codec of the cache as one chain of the steps above, per KV head
+            (Block-GTQ keys and values, rotated uniform, group-rotated Block-GTQ,
+            the 256-value absmax codec's per-head slices).
 
 Every function is pinned by a ``-m "not gpu"`` test against something other
 than itself (closed forms, textbook values, library routines, brute force or
 invariants); see tests/test_oracle_*.py.
 """
 from . import codebooks, allocation, quantize, layout, attention  # noqa: F401
-from . import fidelity, window, rotation, kivi  # noqa: F401
+from . import fidelity, window, rotation, kivi, codecs  # noqa: F401

@@ -8,11 +8,9 @@ from __future__ import annotations
 import numpy as np
 
 from oracle import allocation as al
-from oracle import attention as at
+from oracle import codecs as cd
 from oracle import kivi as kv
 from oracle import layout as lay
-from oracle import quantize as qz
-from oracle import rotation as rt
 
 PAIRING = {"half": 0, "interleaved": 1}
 CODEC = {"bgtq": 0, "uniform": 1, "nf16": 2, "rot": 3, "kivi": 4, "bgtq_rot": 5}
@@ -60,14 +58,13 @@ class OracleLayer:
         """Quantize rows of head h: k_rows, v_rows [N, 128].  For nf16, *_tok_all are the
         tokens' full [N, H*128] vectors.  Returns dict of codes, scales, words."""
         out = {}
+        wid, pr = self.widths[h], self.pairing
         if self.codec == "nf16":
-            ck, sk, _ = qz.quantize_nf16(k_tok_all)
-            cv, sv, _ = qz.quantize_nf16(v_tok_all)
-            out["k_codes"] = ck[:, h * 128:(h + 1) * 128]
-            out["v_codes"] = cv[:, h * 128:(h + 1) * 128]
+            ck, sk = cd.quantize_nf16_tokens(k_tok_all)
+            cv, sv = cd.quantize_nf16_tokens(v_tok_all)
+            out["k_codes"], out["k_s16"] = cd.nf16_head_slice(ck, sk, h)
+            out["v_codes"], out["v_s16"] = cd.nf16_head_slice(cv, sv, h)
             out["k_scale_blocks"], out["v_scale_blocks"] = sk, sv
-            out["k_s16"] = sk[:, h // 2]
-            out["v_s16"] = sv[:, h // 2]
         elif self.codec == "kivi":
             # keys per channel over whole 128-position tiles, values per position
             ck, sk, lk = kv.quantize_k(k_rows, self.k_bits)
@@ -76,20 +73,13 @@ class OracleLayer:
             out["k_params"] = kv.k_params_layout(sk, lk, self.pairing)
             out["v_params"] = kv.v_params_layout(sv, lv)
         else:
-            wd = al.dim_widths(self.widths[h], 128, self.pairing)
-            igd = al.dim_values(self.ig[h], 128, self.pairing)
             if self.codec == "rot":
-                ck, sk, _ = qz.quantize_rows(rt.rotate_rows_fp32(k_rows, self.signs[h]), wd)
+                ck, sk = cd.quantize_rotated_uniform(k_rows, self.k_bits, self.signs[h])
             elif self.codec == "bgtq_rot":
-                # gain-normalised rows, rotated inside the equal-width groups, then quantized
-                # with unit gains
-                y32 = (np.asarray(k_rows).astype(np.float32) * igd.astype(np.float32)[None, :]).astype(np.float32)
-                dims, ws = self.fields(h)
-                yr = rt.rotate_in_groups(y32.astype(np.float64), self.signs[h], dims, ws).astype(np.float32)
-                ck, sk, _ = qz.quantize_rows(yr, wd)
+                ck, sk = cd.quantize_bgtq_group_rotated(k_rows, wid, self.ig[h], self.signs[h], pr)
             else:
-                ck, sk, _ = qz.quantize_rows(k_rows, wd, igd)
-            cv, sv, _ = qz.quantize_rows(v_rows, np.full(128, self.v_bits))
+                ck, sk = cd.quantize_bgtq_keys(k_rows, wid, self.ig[h], pr)
+            cv, sv = cd.quantize_values(v_rows, self.v_bits)
             out.update(k_codes=ck, k_s16=sk, v_codes=cv, v_s16=sv)
         dims, ws = self.fields(h)
         kb = 4 if self.codec == "nf16" else self.k_bits
@@ -97,36 +87,19 @@ class OracleLayer:
         return out
 
     def dequant(self, q_out, h):
+        wid, pr = self.widths[h], self.pairing
         if self.codec == "kivi":
             return (kv.dequant_k(q_out["k_codes"], q_out["k_s16"], q_out["k_lo16"]),
                     kv.dequant_v(q_out["v_codes"], q_out["v_s16"], q_out["v_lo16"]))
         if self.codec == "nf16":
-            lv = at.dequant_nf16(q_out["k_codes"], q_out["k_s16"][:, None], block=128)
-            vv = at.dequant_nf16(q_out["v_codes"], q_out["v_s16"][:, None], block=128)
-            return lv, vv
-        wd = al.dim_widths(self.widths[h], 128, self.pairing)
-        gd = al.dim_values(self.g[h], 128, self.pairing)
+            return (cd.dequant_nf16_head(q_out["k_codes"], q_out["k_s16"]),
+                    cd.dequant_nf16_head(q_out["v_codes"], q_out["v_s16"]))
         if self.codec == "bgtq_rot":
-            dims, ws = self.fields(h)
-            kh = at.dequant_k(q_out["k_codes"], q_out["k_s16"], wd, np.ones(128, np.float32))
-            kh = rt.unrotate_in_groups(kh, self.signs[h], dims, ws) * gd.astype(np.float64)[None, :]
+            kh = cd.dequant_bgtq_group_rotated(q_out["k_codes"], q_out["k_s16"], wid, self.g[h],
+                                               self.signs[h], pr)
+        elif self.codec == "rot":
+            kh = cd.dequant_rotated_uniform(q_out["k_codes"], q_out["k_s16"], self.k_bits, self.signs[h])
         else:
-            kh = at.dequant_k(q_out["k_codes"], q_out["k_s16"], wd, gd)
-        if self.codec == "rot":
-            kh = rt.unrotate(kh, self.signs[h])
-        vh = at.dequant_v(q_out["v_codes"], q_out["v_s16"], self.v_bits)
+            kh = cd.dequant_bgtq_keys(q_out["k_codes"], q_out["k_s16"], wid, self.g[h], pr)
+        vh = cd.dequant_values(q_out["v_codes"], q_out["v_s16"], self.v_bits)
         return kh, vh
-
-
-def flips_excused(gpu_codes, ref_codes, u, width_dim, bounds_of):
-    """Count code mismatches and check each lies within 1 ulp of a boundary of the oracle's u."""
-    bad = np.argwhere(gpu_codes != ref_codes)
-    excused = 0
-    for r, i in bad:
-        w = int(width_dim[i])
-        bd = bounds_of(w)
-        uu = np.float32(u[r, i])
-        ulp = np.spacing(np.abs(uu))
-        if np.min(np.abs(bd.astype(np.float64) - float(uu))) <= float(ulp):
-            excused += 1
-    return len(bad), excused
