@@ -147,8 +147,17 @@ typedef enum {
   KVQ_PART_V_RECENT = 5
 } kvq_part;
 
-/* Create a cache for cfg and allocate its full capacity on the current device.
-   Validates cfg before touching the GPU (KVQ_EINVAL).  *out is set only on KVQ_OK. */
+/* Create a cache for cfg and allocate its full capacity on the current device: the packed store
+   of codebook indices plus scales that the NQKV review describes ("What carries the argument"),
+   filled append-only ("Assumptions", third item), with one plan per layer and KV head as in
+   "RoPE-Aware Bit Allocation for KV-Cache Quantization", abstract (allocation per layer and KV
+   head).  Every device buffer any later call needs is allocated here; no other call allocates
+   device memory except kvq_alloc_bits, which grows its energy scratch to the largest
+   calibration seen.
+   Validates cfg before touching the GPU (KVQ_EINVAL).  *out is set only on KVQ_OK; the caller
+   owns the cache and frees it with kvq_cache_destroy.
+   Environment: KVQ_MERGE_POLL_LIMIT (integer, 0 .. 4194304, read here) bounds how long a decode
+   split merger waits for the partials of the other splits; a test hook (see kvq_cache_status). */
 kvq_status kvq_cache_create(const kvq_config* cfg, kvq_cache** out);
 
 /* Free everything the cache owns; NULL is ignored.  Synchronizes the device. */
@@ -175,7 +184,9 @@ void kvq_cache_destroy(kvq_cache* cache);
 kvq_status kvq_alloc_bits(kvq_cache* cache, int32_t layer, const void* keys, int32_t dtype,
                           int64_t n_tok, const double* block_weight, kvq_stream stream);
 
-/* Copy one layer's plan to host memory.  Synchronizes the device.
+/* Copy one layer's plan to host memory: the integer widths the greedy allocation handed to each
+   RoPE block and the per-block gains ("RoPE-Aware Bit Allocation for KV-Cache Quantization",
+   abstract: widths per layer and KV head under the bit budget).  Synchronizes the device.
    bits:  host int8 [n_kv_heads][64] per-block widths (required); with
           per_sequence_plans [batch][n_kv_heads][64].
    gains: host fp32, same shape as bits: per-block gains g_j (nullable).
@@ -183,7 +194,11 @@ kvq_status kvq_alloc_bits(kvq_cache* cache, int32_t layer, const void* keys, int
 kvq_status kvq_get_plan(const kvq_cache* cache, int32_t layer, int8_t* bits, float* gains);
 
 /* Quantize and append n_new tokens to every sequence of one layer
-   (per-token scale, codebook lookup and bit-packing; append-only).
+   (per-token scale, codebook lookup and bit-packing; append-only).  The quantizer is the
+   TQ-MSE-style scalar codebook quantizer at the layer's per-block widths ("RoPE-Aware Bit
+   Allocation for KV-Cache Quantization", abstract: built on TQ-MSE, matched K/V budgets), or the
+   NQKV review's 16-level Gaussian-quantile codebook with one absmax scale per 256 values ("What
+   carries the argument"); tokens are encoded once, when appended ("Assumptions", third item).
    k, v:  [batch][n_new][n_kv_heads][128] post-RoPE keys and values (dtype),
           16-byte aligned.
    n_new = 0 is a no-op.  Row quantizer, in IEEE fp32/fp64 with no fused ops:
@@ -204,8 +219,9 @@ kvq_status kvq_quantize_append(kvq_cache* cache, int32_t layer, const void* k, c
                                int32_t dtype, int64_t n_new, kvq_stream stream);
 
 /* Grouped-query decode attention of one query per sequence against the packed
-   cache of one layer: logits sigma * <q_h, x_hat^K> over every appended token,
-   softmax, weighted sum of x_hat^V; KV head of query head h is h / group.
+   cache of one layer ("RoPE-Aware Bit Allocation for KV-Cache Quantization", abstract: decoding
+   reads the packed K3V3 cache directly at 128K context): logits sigma * <q_h, x_hat^K> over every
+   appended token, softmax, weighted sum of x_hat^V; KV head of query head h is h / group.
    q:     [batch][n_q_heads][128] (dtype), 4-byte aligned.
    softmax_scale: sigma; <= 0 selects 1/sqrt(128).
    out:   [batch][n_q_heads][128] fp32 device buffer, 16-byte aligned.
@@ -213,8 +229,12 @@ kvq_status kvq_quantize_append(kvq_cache* cache, int32_t layer, const void* k, c
    window (x_hat = the fp16 values) and the others from the packed storage.
    The context is split into chunks processed in parallel, each producing a
    partial (max, sum, weighted sum); the last chunks of each (sequence, KV head)
-   to finish combine them in fixed order.  Decode calls on one cache must not
-   overlap in time (they share the partial buffers).
+   to finish combine them in fixed order (with as many (sequence, KV head) units as
+   the device has compute units, a second kernel on the same stream combines them).
+   A combining workgroup waits a bounded time for the other chunks; if it gives up it
+   writes NaN over its outputs and sets the cache's device error word, reported by
+   kvq_cache_status.  Decode calls on one cache must not overlap in time (they share the
+   partial buffers).
    Errors: KVQ_EINVAL (also a misaligned q or out), KVQ_ESTATE (layer empty or
    without plan). */
 kvq_status kvq_decode_attn(kvq_cache* cache, int32_t layer, const void* q, int32_t dtype,
@@ -261,6 +281,57 @@ kvq_status kvq_key_fidelity(kvq_cache* cache, int32_t layer, const void* q, cons
    Errors: KVQ_EINVAL (other codec, null or a value other than +-1), KVQ_ESTATE (the layer
    already holds tokens). */
 kvq_status kvq_set_rotation(kvq_cache* cache, int32_t layer, const int8_t* signs);
+
+/* Device-side status of the cache.  Synchronizes the device, then returns KVQ_EHIP (with the
+   text in kvq_last_error) if a decode split merge gave up waiting since the last call of this
+   function, else KVQ_OK.  After such a give-up every merged decode output is NaN until this call,
+   which also clears the word and the merge bookkeeping (the cache's data are unaffected).
+   Errors: KVQ_EINVAL (null cache), KVQ_EHIP (also a runtime error of the synchronization). */
+kvq_status kvq_cache_status(kvq_cache* cache);
+
+/* Read-only device view of one layer's packed storage and plans, for callers that read the
+   packed cache in place (indices plus scales, as the NQKV review's cache holds them: "What
+   carries the argument"; decode reads the packed cache directly: "RoPE-Aware Bit Allocation
+   for KV-Cache Quantization", abstract).  No copy and no synchronization: the pointers address
+   the cache's own memory, stay valid until kvq_cache_destroy, and see later appends of the
+   layer (len and packed_len are those at the time of the call).  The caller must not write
+   through them.  Layouts are those of kvq_layer_info; strides are in elements of each part:
+     k_codes   uint32 [batch][n_kv][capacity][k_row_words]; strides (sequence, head, token)
+     v_codes   uint32 [batch][n_kv][capacity/128][512][v_bits]; strides (sequence, head, tile)
+     k_scales, v_scales  fp16 bit patterns; strides (sequence, head, token) for BGTQ, UNIFORM and
+               the rotating codecs, (sequence, token, 256-value block) for NF16_B256, (sequence,
+               head, 128-position tile: 256 halves) for KIVI
+     k_recent, v_recent  fp16 rings of the recent window (NULL without one)
+     plans     n_plans records of plan_bytes bytes, [n_kv] or [batch][n_kv] with per-sequence
+               plans; at byte KVQ_PLAN_OFF_GAIN 128 fp32 gains by dim, KVQ_PLAN_OFF_FIELD_DIM 128
+               uint8 dims in plan (field) order, KVQ_PLAN_OFF_FIELD_WIDTH their uint8 widths,
+               KVQ_PLAN_OFF_BLOCK_WIDTH 64 int8 block widths, KVQ_PLAN_OFF_N_FIELDS the int32
+               count of stored fields.
+   Errors: KVQ_EINVAL (null cache or view, bad layer). */
+#define KVQ_PLAN_BYTES 2256
+#define KVQ_PLAN_OFF_GAIN 0
+#define KVQ_PLAN_OFF_FIELD_DIM 1280
+#define KVQ_PLAN_OFF_FIELD_WIDTH 1408
+#define KVQ_PLAN_OFF_BLOCK_WIDTH 1664
+#define KVQ_PLAN_OFF_N_FIELDS 2240
+typedef struct {
+  const uint32_t* k_codes;
+  int64_t k_codes_strides[3];
+  const uint32_t* v_codes;
+  int64_t v_codes_strides[3];
+  const uint16_t* k_scales;
+  const uint16_t* v_scales;
+  int64_t scale_strides[3];
+  const uint16_t* k_recent;
+  const uint16_t* v_recent;
+  const void* plans;
+  int32_t n_plans;
+  int32_t plan_bytes;
+  int64_t capacity;
+  int64_t len;
+  int64_t packed_len;
+} kvq_view;
+kvq_status kvq_cache_view(const kvq_cache* cache, int32_t layer, kvq_view* view);
 
 /* Tokens appended so far to `layer` (host bookkeeping; does not synchronize). */
 kvq_status kvq_seq_len(const kvq_cache* cache, int32_t layer, int64_t* len);

@@ -1,6 +1,7 @@
 // Host side of the libkvq C ABI: validation, cache memory, bookkeeping, launches.
 #include <hip/hip_runtime.h>
 
+#include <cstddef>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -53,7 +54,7 @@ bool layer_ok(const kvq_cache* c, int32_t layer) {
 void free_device(kvq_cache* c) {
   void* ptrs[] = {c->k_codes, c->v_codes, c->k_scales, c->v_scales, c->plans,
                   c->tables,  c->part_o,  c->part_l,  c->part_mt, c->energy_scratch, c->split_epochs,
-                  c->fid_part, c->k_recent, c->v_recent, c->rot_signs};
+                  c->fid_part, c->k_recent, c->v_recent, c->rot_signs, c->dev_status};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
 }
@@ -179,6 +180,13 @@ kvq_status kvq_cache_create(const kvq_config* cfg, kvq_cache** out) {
     st = dev_alloc(reinterpret_cast<void**>(&c->part_mt), per_split / (kHeadDim + 2) * 2 * ms, "partials");
   if (st == KVQ_OK)
     st = dev_alloc(reinterpret_cast<void**>(&c->split_epochs), sizeof(unsigned) * B * H, "split tags");
+  if (st == KVQ_OK) st = dev_alloc(reinterpret_cast<void**>(&c->dev_status), sizeof(unsigned), "status word");
+  // bound on a split merger's wait (a test hook: a small bound makes the wait give up at once)
+  c->merge_polls = kvq::kMaxMergePolls;
+  if (const char* ev = std::getenv("KVQ_MERGE_POLL_LIMIT")) {
+    const long v = std::strtol(ev, nullptr, 10);
+    if (v >= 0 && v <= kvq::kMaxMergePolls) c->merge_polls = static_cast<int>(v);
+  }
   // fidelity diagnostics: about four workgroups per compute unit over the (sequence, KV head)
   // units, six fp64 statistics per query head and split
   c->fid_max_splits = static_cast<int>((4LL * c->n_cu + B * H - 1) / (B * H));
@@ -188,6 +196,7 @@ kvq_status kvq_cache_create(const kvq_config* cfg, kvq_cache** out) {
   if (st == KVQ_OK) {
     const hipError_t es[] = {
         hipMemset(c->split_epochs, 0, sizeof(unsigned) * B * H),
+        hipMemset(c->dev_status, 0, sizeof(unsigned)),
         hipMemset(c->part_mt, 0, per_split / (kHeadDim + 2) * 2 * ms),
         hipMemset(c->k_codes, 0, c->k_codes_layer * L),
         hipMemset(c->v_codes, 0, c->v_codes_layer * L),
@@ -347,12 +356,10 @@ kvq_status kvq_decode_attn_splits(kvq_cache* c, int32_t layer, const void* q, in
   const int S = plen == 0 ? 0 : n_splits > 0 ? n_splits : kvq::auto_splits_mfma(c, plen, n_rwg);
   const int S_all = S + n_rwg;
   if (S_all > c->max_splits) return KVQ_EINVAL;
-  const int64_t units = static_cast<int64_t>(c->cfg.batch) * c->cfg.n_kv_heads;
-  if (S_all > 1 && kvq::decode_split_mergers(S_all, units, c->n_cu) == 0) {
-    g_last_error = "decode: more split units than compute units can merge; use one split";
-    return KVQ_EINVAL;
-  }
-  hipError_t e = kvq::launch_decode_mfma(c, layer, q, dtype, softmax_scale, out, S,
+  // (with as many (sequence, KV head) units as compute units the splits are merged by a
+  // second kernel instead of in the decode kernel)
+  const kvq::DecodeScratch ws{c->part_o, c->part_l, c->part_mt, c->split_epochs, c->dev_status, c->merge_polls};
+  hipError_t e = kvq::launch_decode_mfma(c, layer, q, dtype, softmax_scale, out, S, ws,
                                          static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return KVQ_OK;
@@ -391,6 +398,75 @@ kvq_status kvq_set_rotation(kvq_cache* c, int32_t layer, const int8_t* signs) {
   hipError_t e = hipMemcpy(c->rot_signs + layer * n, signs, n, hipMemcpyHostToDevice);
   if (e != hipSuccess) return hip_fail(e, "set rotation");
   c->rot_ready[layer] = 1;
+  return KVQ_OK;
+}
+
+kvq_status kvq_cache_status(kvq_cache* c) {
+  if (!c) return KVQ_EINVAL;
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+  unsigned word = 0;
+  e = hipMemcpy(&word, c->dev_status, sizeof(word), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "status read");
+  if (word == 0) return KVQ_OK;
+  // nothing is in flight: clear the word, the split maxima words and the tag bases, so the
+  // next decode starts from a clean state
+  const int64_t units = static_cast<int64_t>(c->cfg.batch) * c->cfg.n_kv_heads;
+  const hipError_t es[] = {hipMemset(c->dev_status, 0, sizeof(unsigned)),
+                           hipMemset(c->part_mt, 0, sizeof(uint64_t) * units * c->group * c->max_splits),
+                           hipMemset(c->split_epochs, 0, sizeof(unsigned) * units), hipDeviceSynchronize()};
+  for (hipError_t x : es)
+    if (x != hipSuccess) return hip_fail(x, "status reset");
+  g_last_error = "decode: a split merge gave up waiting for the partials of other splits; the outputs it "
+                 "covered (and those of later merged decodes until this call) were written as NaN";
+  return KVQ_EHIP;
+}
+
+static_assert(sizeof(kvq::Plan) == KVQ_PLAN_BYTES, "plan record size");
+static_assert(offsetof(kvq::Plan, g) == KVQ_PLAN_OFF_GAIN, "plan gains");
+static_assert(offsetof(kvq::Plan, fdim) == KVQ_PLAN_OFF_FIELD_DIM, "plan field dims");
+static_assert(offsetof(kvq::Plan, fwidth) == KVQ_PLAN_OFF_FIELD_WIDTH, "plan field widths");
+static_assert(offsetof(kvq::Plan, bwidth) == KVQ_PLAN_OFF_BLOCK_WIDTH, "plan block widths");
+static_assert(offsetof(kvq::Plan, n_fields) == KVQ_PLAN_OFF_N_FIELDS, "plan field count");
+
+kvq_status kvq_cache_view(const kvq_cache* c, int32_t layer, kvq_view* v) {
+  if (!layer_ok(c, layer) || !v) return KVQ_EINVAL;
+  kvq_cache* m = const_cast<kvq_cache*>(c);
+  const int64_t H = c->cfg.n_kv_heads, cap = c->cap;
+  std::memset(v, 0, sizeof(*v));
+  v->k_codes = kvq::layer_k_codes(m, layer);
+  v->k_codes_strides[0] = H * cap * c->k_words;
+  v->k_codes_strides[1] = cap * c->k_words;
+  v->k_codes_strides[2] = c->k_words;
+  v->v_codes = kvq::layer_v_codes(m, layer);
+  v->v_codes_strides[0] = H * cap * c->v_words;
+  v->v_codes_strides[1] = cap * c->v_words;
+  v->v_codes_strides[2] = kVTile * c->v_words;
+  v->k_scales = kvq::layer_k_scales(m, layer);
+  v->v_scales = kvq::layer_v_scales(m, layer);
+  if (c->cfg.codec == KVQ_CODEC_NF16_B256) {
+    v->scale_strides[0] = cap * c->n_nf_blocks;
+    v->scale_strides[1] = c->n_nf_blocks;
+    v->scale_strides[2] = 1;
+  } else if (c->cfg.codec == KVQ_CODEC_KIVI) {
+    v->scale_strides[0] = H * (cap / kVTile) * 256;
+    v->scale_strides[1] = (cap / kVTile) * 256;
+    v->scale_strides[2] = 256;
+  } else {
+    v->scale_strides[0] = H * cap;
+    v->scale_strides[1] = cap;
+    v->scale_strides[2] = 1;
+  }
+  if (c->recent_layer > 0) {
+    v->k_recent = reinterpret_cast<const uint16_t*>(kvq::layer_k_recent(m, layer));
+    v->v_recent = reinterpret_cast<const uint16_t*>(kvq::layer_v_recent(m, layer));
+  }
+  v->plans = c->plans + static_cast<int64_t>(layer) * c->n_plan * H;
+  v->n_plans = static_cast<int32_t>(c->n_plan * H);
+  v->plan_bytes = static_cast<int32_t>(sizeof(kvq::Plan));
+  v->capacity = cap;
+  v->len = c->len[layer];
+  v->packed_len = kvq::packed_len(c, layer);
   return KVQ_OK;
 }
 

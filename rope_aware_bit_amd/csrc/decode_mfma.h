@@ -58,7 +58,6 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 typedef __attribute__((address_space(1))) void* glb_ptr;
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-constexpr int kMaxPolls = 1 << 22;  // bound on a merger's wait for the other splits
 constexpr int kCohAux = 16;         // buffer-load cache policy sc1: coherent at device scope
 constexpr int kRawBuffer = 0x00020000;   // buffer descriptor word 3: raw 32-bit data
 constexpr int kKS = 144;          // LDS row stride (words) of a staged K tile: 128 tokens + 16
@@ -274,16 +273,26 @@ __device__ inline uint32_t v_pair(const uint32_t* S, int e, const char* tab, uin
 // m* = max_e m_e and w_e = 2^(m_e - m*), out = sum_e w_e o_e / sum_e w_e l_e.  `bump`, if
 // not null, receives `want` once every split is seen (the next call's tag base).  `smem`
 // holds nh S + 4 NT + nh floats (+3 alignment; nh = heads covered); S <= 256.
+//
+// The wait is bounded by `max_polls`.  A merger that gives up, or that finds the sticky error
+// word `status` already set (an earlier merge of this cache gave up; its partial words may be
+// stale), writes NaN over its slice and sets bit 0 of `status`; the tag base is then not
+// advanced.  The host clears the word, the maxima words and the tag bases after a device-wide
+// synchronization (kvq_cache_status).
 template <int G, int NT>
 __device__ __attribute__((always_inline)) inline void merge_slice(
     const float* __restrict__ src_o, const float* __restrict__ src_l, const uint64_t* __restrict__ src_mt,
-    unsigned want, unsigned* bump, int S, int first, int count, float* smem, int tid,
-    float* __restrict__ dst) {
+    unsigned want, unsigned* bump, unsigned* status, int max_polls, int S, int first, int count,
+    float* smem, int tid, float* __restrict__ dst) {
   constexpr int kPre = 8;
+  __shared__ unsigned merge_fail;
   const int hd0 = first / kHeadDim;
   const int nh = count > kHeadDim ? count / kHeadDim : 1;
   float* wv = smem;                               // [nh][S] weights
   const int wave = tid >> 6, lane = tid & 63;
+  const unsigned sticky = __hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) merge_fail = sticky;
+  __syncthreads();
   for (int hh = wave; hh < nh; hh += NT / 64) {
     const uint64_t* mt = src_mt + hd0 + hh;
     float mr[4];
@@ -293,7 +302,8 @@ __device__ __attribute__((always_inline)) inline void merge_slice(
       ok[k] = lane + 64 * k >= S;
       mr[k] = -INFINITY;
     }
-    for (int polls = 0; polls < kMaxPolls; ++polls) {
+    bool seen_all = false;
+    for (int polls = sticky ? max_polls : 0; polls < max_polls; ++polls) {
       bool mine = true;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -307,8 +317,15 @@ __device__ __attribute__((always_inline)) inline void merge_slice(
           }
         }
       }
-      if (__ballot(!mine) == 0ull) break;
+      if (__ballot(!mine) == 0ull) {
+        seen_all = true;
+        break;
+      }
       __builtin_amdgcn_s_sleep(1);
+    }
+    if (!seen_all) {
+      if (lane == 0) merge_fail = 1u;
+      continue;
     }
     if (hh == 0 && lane == 0 && bump) __hip_atomic_store(bump, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const float m = wave_max(fmaxf(fmaxf(mr[0], mr[1]), fmaxf(mr[2], mr[3])));
@@ -319,6 +336,11 @@ __device__ __attribute__((always_inline)) inline void merge_slice(
     }
   }
   __syncthreads();
+  if (merge_fail) {
+    for (int i = tid; i < count; i += NT) dst[first + i] = __builtin_nanf("");
+    if (tid == 0) __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   // outputs in groups of four (one 16-byte load per split and group)
   const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
@@ -438,7 +460,8 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     const uint32_t* __restrict__ kc, const uint32_t* __restrict__ vc, const uint16_t* __restrict__ ks,
     const uint16_t* __restrict__ vs, int k_words, int n_nf, int n_splits, int n_mergers, int region_words,
     int v_early, int v_off, float* __restrict__ part_o, float* __restrict__ part_l,
-    uint64_t* __restrict__ part_mt, unsigned* __restrict__ epochs, float* __restrict__ out) {
+    uint64_t* __restrict__ part_mt, unsigned* __restrict__ epochs, unsigned* status, int max_polls,
+    float* __restrict__ out) {
   constexpr int NT = 64 * W;
   constexpr bool kPipe = W == 4;                      // one wave per SIMD: prefetch and pipeline
   constexpr int PCOLS = 2 * G;                        // P columns: hi of heads 0..G-1, then lo
@@ -1155,13 +1178,32 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   if (rank < 0) return;
   const int count = G * kHeadDim / n_mergers;
   merge_slice<G, NT>(part_o + bh * n_splits * G * kHeadDim, part_l + bh * n_splits * G,
-                     part_mt + bh * n_splits * G, tag, rank == 0 ? epochs + bh : nullptr, n_splits,
-                     rank * count, count, reinterpret_cast<float*>(dyn_s), tid, out + out_base);
+                     part_mt + bh * n_splits * G, tag, rank == 0 ? epochs + bh : nullptr, status, max_polls,
+                     n_splits, rank * count, count, reinterpret_cast<float*>(dyn_s), tid, out + out_base);
+}
+
+// Merge of the split partials by a kernel of its own, for launches whose mergers would not fit
+// beside the splits they wait for (as many (sequence, KV head) units as compute units): the
+// decode kernel only publishes partials, and this kernel, enqueued after it on the same stream,
+// merges each unit's splits in one workgroup.  Every tag is then already published; the tag
+// base is the one the decode kernel read, advanced here.
+template <int G>
+__global__ __launch_bounds__(256) void decode_merge(
+    const float* __restrict__ part_o, const float* __restrict__ part_l, const uint64_t* __restrict__ part_mt,
+    unsigned* __restrict__ epochs, unsigned* status, int max_polls, int n_splits, int n_kv,
+    float* __restrict__ out) {
+  extern __shared__ __attribute__((aligned(16))) float msm[];
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int64_t bh = static_cast<int64_t>(b) * n_kv + h;
+  const unsigned want = __hip_atomic_load(epochs + bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+  merge_slice<G, 256>(part_o + bh * n_splits * G * kHeadDim, part_l + bh * n_splits * G, part_mt + bh * n_splits * G,
+                      want, epochs + bh, status, max_polls, n_splits, 0, G * kHeadDim, msm, threadIdx.x,
+                      out + bh * G * kHeadDim);
 }
 
 template <int G, int VB, int W>
 hipError_t launch_gvw(kvq_cache* c, int layer, const void* q, int q_f32, float sigma, float* out,
-                      int S, const DecodeShape& sh, hipStream_t stream) {
+                      int S, const DecodeShape& sh, const DecodeScratch& ws, hipStream_t stream) {
   const kvq_config& cfg = c->cfg;
   // S packed splits over the packed positions, plus one workgroup for the recent window
   const int64_t plen = packed_len(c, layer);
@@ -1185,48 +1227,55 @@ hipError_t launch_gvw(kvq_cache* c, int layer, const void* q, int q_f32, float s
                      plen, S, rk, rv, R, n_recent, rot, rot_groups, cfg.n_kv_heads, c->cap, tps, plans, plan_bs, \
                      c->tables, layer_k_codes(c, layer), layer_v_codes(c, layer), layer_k_scales(c, layer), \
                      layer_v_scales(c, layer), c->k_words, c->n_nf_blocks, S_all, mergers, sh.region_words,  \
-                     sh.v_early, sh.v_off, c->part_o, c->part_l, c->part_mt, c->split_epochs, out)
+                     sh.v_early, sh.v_off, ws.o, ws.l, ws.mt, ws.epochs, ws.status, ws.max_polls, out)
+  bool launched = false;
   if constexpr (VB == 4) {
     if (cfg.codec == KVQ_CODEC_NF16_B256) {
       KVQ_LAUNCH_DEC(true, false);
-      return hipGetLastError();
+      launched = true;
     }
   }
   if constexpr (VB <= 4) {
-    if (cfg.codec == KVQ_CODEC_KIVI) {
+    if (!launched && cfg.codec == KVQ_CODEC_KIVI) {
       KVQ_LAUNCH_DEC(false, true);
-      return hipGetLastError();
+      launched = true;
     }
   }
-  KVQ_LAUNCH_DEC(false, false);
+  if (!launched) KVQ_LAUNCH_DEC(false, false);
 #undef KVQ_LAUNCH_DEC
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || S_all <= 1 || mergers > 0) return e;
+  // no room for in-kernel mergers: merge in a kernel of its own
+  const size_t msm = sizeof(float) * ((static_cast<size_t>(G) * S_all + 3) / 4 * 4 + 4 * 256 + G);
+  hipLaunchKernelGGL((decode_merge<G>), dim3(cfg.n_kv_heads, cfg.batch), dim3(256), msm, stream, ws.o, ws.l, ws.mt,
+                     ws.epochs, ws.status, ws.max_polls, S_all, cfg.n_kv_heads, out);
   return hipGetLastError();
 }
 
 template <int G, int VB>
 hipError_t launch_gv(kvq_cache* c, int layer, const void* q, int q_f32, float sigma, float* out,
-                     int S, hipStream_t stream) {
+                     int S, const DecodeScratch& ws, hipStream_t stream) {
   const DecodeShape sh = decode_shape(c);
   if constexpr (VB <= 4) {   // wider V tiles never leave room for 8 waves
-    if (sh.waves == 8) return launch_gvw<G, VB, 8>(c, layer, q, q_f32, sigma, out, S, sh, stream);
+    if (sh.waves == 8) return launch_gvw<G, VB, 8>(c, layer, q, q_f32, sigma, out, S, sh, ws, stream);
   }
   if (sh.waves != 4) return hipErrorInvalidConfiguration;
-  return launch_gvw<G, VB, 4>(c, layer, q, q_f32, sigma, out, S, sh, stream);
+  return launch_gvw<G, VB, 4>(c, layer, q, q_f32, sigma, out, S, sh, ws, stream);
 }
 
 template <int G>
 hipError_t launch_group(kvq_cache* c, int layer, const void* q, int q_f32, float sigma, float* out,
-                        int S, hipStream_t stream) {
+                        int S, const DecodeScratch& ws, hipStream_t stream) {
   const int vb = c->cfg.codec == KVQ_CODEC_NF16_B256 ? 4 : c->cfg.v_bits;
   switch (vb) {
-    case 1: return launch_gv<G, 1>(c, layer, q, q_f32, sigma, out, S, stream);
-    case 2: return launch_gv<G, 2>(c, layer, q, q_f32, sigma, out, S, stream);
-    case 3: return launch_gv<G, 3>(c, layer, q, q_f32, sigma, out, S, stream);
-    case 4: return launch_gv<G, 4>(c, layer, q, q_f32, sigma, out, S, stream);
-    case 5: return launch_gv<G, 5>(c, layer, q, q_f32, sigma, out, S, stream);
-    case 6: return launch_gv<G, 6>(c, layer, q, q_f32, sigma, out, S, stream);
-    case 7: return launch_gv<G, 7>(c, layer, q, q_f32, sigma, out, S, stream);
-    default: return launch_gv<G, 8>(c, layer, q, q_f32, sigma, out, S, stream);
+    case 1: return launch_gv<G, 1>(c, layer, q, q_f32, sigma, out, S, ws, stream);
+    case 2: return launch_gv<G, 2>(c, layer, q, q_f32, sigma, out, S, ws, stream);
+    case 3: return launch_gv<G, 3>(c, layer, q, q_f32, sigma, out, S, ws, stream);
+    case 4: return launch_gv<G, 4>(c, layer, q, q_f32, sigma, out, S, ws, stream);
+    case 5: return launch_gv<G, 5>(c, layer, q, q_f32, sigma, out, S, ws, stream);
+    case 6: return launch_gv<G, 6>(c, layer, q, q_f32, sigma, out, S, ws, stream);
+    case 7: return launch_gv<G, 7>(c, layer, q, q_f32, sigma, out, S, ws, stream);
+    default: return launch_gv<G, 8>(c, layer, q, q_f32, sigma, out, S, ws, stream);
   }
 }
 

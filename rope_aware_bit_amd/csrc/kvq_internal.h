@@ -17,6 +17,7 @@ constexpr int kEnergyChunk = 256;    // tokens per sequential energy partial sum
 constexpr int kMaxGroup = 8;         // query heads per KV head supported
 constexpr int kNfBlock = 256;        // values per absmax block of the NF16 codec
 constexpr int kMaxRecent = 4096;     // largest recent window (tokens)
+constexpr int kMaxMergePolls = 1 << 22;   // default bound on a split merger's wait for partials
 
 // Byte layout of the decode lookup tables that every decode workgroup copies into LDS.
 // Pair tables (widths 1..4) hold fp16x2 (CB[c0], CB[c1]) at index c0 | c1 << w; single
@@ -97,6 +98,8 @@ struct kvq_cache {
   float* part_l;               // split softmax sums [B][H][max_splits][G]
   uint64_t* part_mt;           // split maxima | publication tag << 32 [B][H][max_splits][G]
   unsigned* split_epochs;      // [B][H] tag base of the next call's split partials
+  unsigned* dev_status;        // sticky device error word (bit 0: a split merge gave up waiting)
+  int merge_polls;             // bound on a merger's polls (KVQ_MERGE_POLL_LIMIT, else kMaxMergePolls)
   int max_splits;
   double* energy_scratch;      // [H][n_chunks][64]
   double* fid_part;            // fidelity split statistics [B][n_q][fid_max_splits][6]
@@ -126,8 +129,19 @@ hipError_t launch_kivi_quantize(kvq_cache* c, int layer, const void* k, const vo
 hipError_t launch_recent_write(kvq_cache* c, int layer, const void* k, const void* v, int dtype,
                                int64_t in_stride, int64_t row0, int64_t pos0, int64_t count,
                                hipStream_t stream);
+// Split partials and merge bookkeeping of one decode call: outputs [units][S][G][128], sums
+// [units][S][G], maxima | tag << 32 [units][S][G], one tag base per unit, the sticky error word
+// and the bound on a merger's polls.  The cache's own buffers, or a caller's.
+struct DecodeScratch {
+  float* o;
+  float* l;
+  uint64_t* mt;
+  unsigned* epochs;
+  unsigned* status;
+  int max_polls;
+};
 hipError_t launch_decode_mfma(kvq_cache* c, int layer, const void* q, int dtype, float scale,
-                              float* out, int n_splits, hipStream_t stream);
+                              float* out, int n_splits, const DecodeScratch& ws, hipStream_t stream);
 hipError_t launch_fidelity(kvq_cache* c, int layer, const void* q, const void* keys, int dtype,
                            float scale, double* mae, double* kl, hipStream_t stream);
 int auto_splits_mfma(const kvq_cache* c, int64_t len, int n_extra);

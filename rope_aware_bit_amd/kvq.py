@@ -26,8 +26,11 @@ EXPORTED = (
     "kvq_cache_create", "kvq_cache_destroy", "kvq_alloc_bits", "kvq_get_plan",
     "kvq_quantize_append", "kvq_decode_attn", "kvq_decode_attn_splits", "kvq_key_fidelity", "kvq_set_rotation", "kvq_seq_len",
     "kvq_layer_info_get", "kvq_read_cache", "kvq_codebook", "kvq_delta",
-    "kvq_nf16_codebook", "kvq_status_str", "kvq_last_error",
+    "kvq_nf16_codebook", "kvq_status_str", "kvq_last_error", "kvq_cache_status", "kvq_cache_view",
 )
+
+PLAN_BYTES, PLAN_OFF_GAIN, PLAN_OFF_FIELD_DIM, PLAN_OFF_FIELD_WIDTH = 2256, 0, 1280, 1408
+PLAN_OFF_BLOCK_WIDTH, PLAN_OFF_N_FIELDS = 1664, 2240
 
 
 class KvqError(RuntimeError):
@@ -57,6 +60,17 @@ class kvq_layer_info(ctypes.Structure):
     ]
 
 
+class kvq_view(ctypes.Structure):
+    _fields_ = [
+        ("k_codes", ctypes.c_void_p), ("k_codes_strides", ctypes.c_int64 * 3),
+        ("v_codes", ctypes.c_void_p), ("v_codes_strides", ctypes.c_int64 * 3),
+        ("k_scales", ctypes.c_void_p), ("v_scales", ctypes.c_void_p), ("scale_strides", ctypes.c_int64 * 3),
+        ("k_recent", ctypes.c_void_p), ("v_recent", ctypes.c_void_p), ("plans", ctypes.c_void_p),
+        ("n_plans", ctypes.c_int32), ("plan_bytes", ctypes.c_int32), ("capacity", ctypes.c_int64),
+        ("len", ctypes.c_int64), ("packed_len", ctypes.c_int64),
+    ]
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(_LIB_PATH):
         raise ImportError(f"libkvq.so not built at {_LIB_PATH}; run __graft_entry__.build()")
@@ -80,6 +94,8 @@ def _load() -> ctypes.CDLL:
         "kvq_nf16_codebook": (I32, [P, P]),
         "kvq_status_str": (ctypes.c_char_p, [I32]),
         "kvq_last_error": (ctypes.c_char_p, []),
+        "kvq_cache_status": (I32, [P]),
+        "kvq_cache_view": (I32, [P, I32, ctypes.POINTER(kvq_view)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -219,7 +235,15 @@ class Cache:
         kp = _ptr(keys) if keys is not None else None
         dt = _dtype_code(keys) if keys is not None else KVQ_F16
         n = keys.shape[-3] if keys is not None else 0
-        wp = _ptr(block_weight) if block_weight is not None else None
+        wp = None
+        if block_weight is not None:
+            import torch
+            want = lead + (self.cfg.n_kv_heads, 64) if keys is not None else \
+                ((self.cfg.batch,) if per_seq else ()) + (self.cfg.n_kv_heads, 64)
+            if block_weight.dtype != torch.float64 or tuple(block_weight.shape) != want:
+                raise ValueError(f"block_weight must be float64 of shape {want}, got "
+                                 f"{block_weight.dtype} {tuple(block_weight.shape)}")
+            wp = _ptr(block_weight)
         _check(lib.kvq_alloc_bits(self._h, layer, kp, dt, n, wp, _stream(stream)), "kvq_alloc_bits")
 
     def set_rotation(self, layer: int, signs):
@@ -276,6 +300,17 @@ class Cache:
         _check(lib.kvq_key_fidelity(self._h, layer, _ptr(q), _ptr(keys), _dtype_code(q), float(scale),
                                     _ptr(mae), _ptr(kl), _stream(stream)), "kvq_key_fidelity")
         return mae, kl
+
+    def status(self):
+        """Raise KvqError if a decode split merge of this cache gave up since the last check
+        (kvq_cache_status; synchronizes the device and clears the error)."""
+        _check(lib.kvq_cache_status(self._h), "kvq_cache_status")
+
+    def view(self, layer: int) -> kvq_view:
+        """Read-only device pointers and strides of one layer's storage and plans (no copy)."""
+        v = kvq_view()
+        _check(lib.kvq_cache_view(self._h, layer, ctypes.byref(v)), "kvq_cache_view")
+        return v
 
     def seq_len(self, layer: int) -> int:
         n = ctypes.c_int64()

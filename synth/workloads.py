@@ -68,6 +68,10 @@ WORKLOADS = {
     # batched decode, Llama-3.1-8B KV shape, 64 x 8192, K4V4
     "llama8b_b64": Workload(4, "llama8b_b64", 1, 8, 32, 64, 8192, 5.0e5, "f16",
                             ((4, 4),), 2, 10.0, 2048),
+    # two query heads per KV head (a grouped-query ratio the library accepts that none of the
+    # workloads above has), same key recipe, for parity only
+    "gqa2_8k": Workload(5, "gqa2_8k", 1, 4, 8, 1, 8192, 1.0e6, "f16",
+                        ((3, 3),), 2, 10.0, 2048),
 }
 
 

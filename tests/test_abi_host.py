@@ -96,6 +96,9 @@ def test_null_handles_and_status_strings():
     n = ctypes.c_int64()
     assert L.kvq_seq_len(None, 0, ctypes.byref(n)) == kvq.KVQ_EINVAL
     assert L.kvq_read_cache(None, 0, 0, 0, 0, None) == kvq.KVQ_EINVAL
+    assert L.kvq_cache_status(None) == kvq.KVQ_EINVAL
+    v = kvq.kvq_view()
+    assert L.kvq_cache_view(None, 0, ctypes.byref(v)) == kvq.KVQ_EINVAL
     L.kvq_cache_destroy(None)
     for s, name in enumerate(["KVQ_OK", "KVQ_EINVAL", "KVQ_ENOMEM", "KVQ_ECAPACITY", "KVQ_ESTATE", "KVQ_EHIP"]):
         assert L.kvq_status_str(s).decode() == name
