@@ -247,6 +247,21 @@ kvq_status kvq_decode_attn_splits(kvq_cache* cache, int32_t layer, const void* q
                                   float softmax_scale, float* out, int32_t n_splits,
                                   kvq_stream stream);
 
+/* As kvq_decode_attn (automatic split count), for callers that cannot allocate: code under
+   HIP graph or stream capture, tight serving loops, harnesses that forbid allocation.  It makes
+   no allocation of any kind: the split partials, maxima words and tag bases live in a fixed
+   8 MiB device array of the library (one per device, held until the process ends; its address is
+   looked up once per device on the first call there), not in the cache's buffers.  Each call
+   first clears the words it merges on (a small kernel, no memset), so nothing of an earlier call
+   is ever read.  Results are those of kvq_decode_attn on the same cache.  The cache's device
+   error word reports a merge that gave up, as for kvq_decode_attn (see kvq_cache_status).
+   Every call on a device shares that device's array: calls that overlap in time on one device
+   race, whatever their caches.
+   Errors: as kvq_decode_attn; KVQ_EINVAL also when the call needs more than 8 MiB of split
+   scratch (batch * n_kv_heads * splits * group * 524 bytes; kvq_last_error has the figure). */
+kvq_status kvq_decode_attn_noalloc(kvq_cache* cache, int32_t layer, const void* q, int32_t dtype,
+                                   float softmax_scale, float* out, kvq_stream stream);
+
 /* Key-cache fidelity diagnostics of `layer`: how well the stored keys preserve the
    attention logits, after "RoPE-Aware Bit Allocation for KV-Cache Quantization",
    abstract (per-layer query-key logit mean absolute error, keys only) and

@@ -72,6 +72,10 @@ kvq_status dev_alloc(void** p, size_t bytes, const char* what) {
 
 }  // namespace
 
+namespace kvq {
+void set_last_error(const std::string& what) { g_last_error = what; }
+}  // namespace kvq
+
 extern "C" {
 
 const char* kvq_status_str(kvq_status s) {

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <string>
+
 #include "../../include/kvq.h"
 
 namespace kvq {
@@ -110,6 +112,9 @@ struct kvq_cache {
 };
 
 namespace kvq {
+
+// Records the text kvq_last_error() returns to this thread.
+void set_last_error(const std::string& what);
 
 // Kernel launchers (defined in the .hip sources).  All enqueue on `stream` and
 // return the launch status; arguments are validated by the caller.

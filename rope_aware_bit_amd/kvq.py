@@ -27,6 +27,7 @@ EXPORTED = (
     "kvq_quantize_append", "kvq_decode_attn", "kvq_decode_attn_splits", "kvq_key_fidelity", "kvq_set_rotation", "kvq_seq_len",
     "kvq_layer_info_get", "kvq_read_cache", "kvq_codebook", "kvq_delta",
     "kvq_nf16_codebook", "kvq_status_str", "kvq_last_error", "kvq_cache_status", "kvq_cache_view",
+    "kvq_decode_attn_noalloc",
 )
 
 PLAN_BYTES, PLAN_OFF_GAIN, PLAN_OFF_FIELD_DIM, PLAN_OFF_FIELD_WIDTH = 2256, 0, 1280, 1408
@@ -96,6 +97,7 @@ def _load() -> ctypes.CDLL:
         "kvq_last_error": (ctypes.c_char_p, []),
         "kvq_cache_status": (I32, [P]),
         "kvq_cache_view": (I32, [P, I32, ctypes.POINTER(kvq_view)]),
+        "kvq_decode_attn_noalloc": (I32, [P, I32, P, I32, F32, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -280,6 +282,20 @@ class Cache:
             raise ValueError("out must be fp32 with q's shape")
         _check(lib.kvq_decode_attn_splits(self._h, layer, _ptr(q), _dtype_code(q), float(scale),
                                           _ptr(out), int(n_splits), _stream(stream)), "kvq_decode_attn")
+        return out
+
+    def decode_attn_noalloc(self, layer: int, q, out, scale: float = 0.0, stream=None):
+        """kvq_decode_attn_noalloc: as decode_attn (automatic splits) into the caller's `out`,
+        with no allocation anywhere (split scratch in the library's fixed device array)."""
+        import torch
+        if q.dim() != 3 or tuple(q.shape) != (self.cfg.batch, self.cfg.n_q_heads, self.cfg.head_dim):
+            raise ValueError(f"q must be [batch, n_q_heads, head_dim], got {tuple(q.shape)}")
+        if out.dtype != torch.float32 or tuple(out.shape) != tuple(q.shape):
+            raise ValueError("out must be fp32 with q's shape")
+        st = lib.kvq_decode_attn_noalloc(self._h, layer, _ptr(q), _dtype_code(q), float(scale), _ptr(out),
+                                         _stream(stream))
+        if st != KVQ_OK:
+            raise KvqError(st, "kvq_decode_attn_noalloc", lib.kvq_last_error().decode())
         return out
 
     def key_fidelity(self, layer: int, q, keys, scale: float = 0.0, stream=None):
