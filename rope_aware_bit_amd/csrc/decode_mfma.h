@@ -68,16 +68,17 @@ constexpr int kAS = 40;           // LDS row stride (halves) of the query operan
 // Random lookups into the larger tables would collide in LDS banks, so they are replicated:
 // the width-4 pair table 16 times (entry p of copy k at (p << 6) + 4 k, lane l reads copy
 // l % 16) and the width-3 pair table 32 times (entry p of copy k at (p << 7) + 4 k, lane l
-// reads copy l % 32).  Widths 5..8 use single tables (one fp16 in the low half of a 32-bit
-// slot, the high half zero), built per workgroup when the plan uses them: widths 5 and 6
+// reads copy l % 32).  Widths 6..8 use single tables (one fp16 in the low half of a 32-bit
+// slot, the high half zero), built per workgroup when the plan uses them: width 6
 // replicated 32 times the same way, widths 7 and 8 once (few blocks are that wide); a pair
-// costs two lookups in the same table.  The prebuilt image holds the pair tables of widths 1..4
-// and the fp16 single tables of widths 1..8.  Every base is a multiple of its table's extent,
-// so an entry address is "(p << shift) | copy offset | base".
+// costs two lookups in the same table.  Width 5 has a pair table of its own (1024 fp16 pairs,
+// not replicated), so its pairs cost one lookup.  The prebuilt image holds the pair tables of
+// widths 1..4 and the fp16 single tables of widths 1..8.  Every base is a multiple of its
+// table's extent, so an entry address is "(p << shift) | copy offset | base".
 constexpr int kRep4Base = 0;           // 16 KB
 constexpr int kRep3Base = 16384;       // 8 KB
 constexpr int kSing6Base = 24576;      // 8 KB
-constexpr int kSing5Base = 32768;      // 4 KB
+constexpr int kPair5Base = 32768;      // 4 KB
 constexpr int kImageBase = 36864;      // 2.5 KB
 constexpr int kSing7Base = 39424;      // 512 B
 constexpr int kSing8Base = 39936;      // 1 KB
@@ -95,8 +96,8 @@ __host__ __device__ constexpr int slot_field(int c, int k) {
 // Key-product parameters of one (chunk c, lane group g): its four pairs, held in LDS as 24 words
 //   [0..3]  table base of pair p (with the part of the lane's replica offset fixed by g)
 //   [4..7]  mask applied to 4 n (the rest of the replica offset; 0 for single tables)
-//   [8..11] extract width (2 w for pair tables; w for widths 5..8, whose first field is
-//           looked up here)
+//   [8..11] extract width (2 w for pair tables, widths up to 5; w for widths 6..8, whose
+//           first field is looked up here)
 //   [12..15] left shift of the extracted code (2 single copy, 6 sixteen copies, 32: 7)
 //   [16..19] bit shift of window A (pairs 0, 1) and B (pairs 2, 3); bit offset of pairs 1, 3
 //   [20..21] byte offset of the first word of windows A and B in a staged K tile
@@ -114,19 +115,21 @@ __device__ inline void write_pair_params(uint32_t* kp, int r, uint32_t desc) {
     base = kRep3Base | (64u * (g & 1));   // lane & 31 = n + 16 (g & 1)
     mask = 0x3Cu;
     shift = 7u;
-  } else if (w == 5u || w == 6u) {
-    base = (w == 5u ? kSing5Base : kSing6Base) | (64u * (g & 1));
+  } else if (w == 6u) {
+    base = kSing6Base | (64u * (g & 1));
     mask = 0x3Cu;
     shift = 7u;
   } else if (w >= 7u) {
     base = w == 7u ? kSing7Base : kSing8Base;
+  } else if (w == 5u) {
+    base = kPair5Base;
   } else {
     base = kImageBase + static_cast<uint32_t>(pair_table_base(static_cast<int>(w)));
   }
   uint32_t* blk = kp + (4 * c + g) * kParamWords;
   blk[p] = base;
   blk[4 + p] = mask;
-  blk[8 + p] = w <= 4u ? 2u * w : w;
+  blk[8 + p] = w <= 5u ? 2u * w : w;
   blk[12 + p] = shift;
   reinterpret_cast<uint8_t*>(blk + 22)[p] = static_cast<uint8_t>(w);
   if ((p & 1) == 0) {
@@ -380,16 +383,39 @@ __device__ __attribute__((always_inline)) inline void merge_slice(
         if (e < S) add(wv[hh * S + e], ov[k]);
     }
     for (; e < S; e += R) add(wv[hh * S + e], ld_coh4(ro, 4u * static_cast<uint32_t>(e * G * kHeadDim + oi)));
-    red[tid] = acc;
-    __syncthreads();
-    if (tid < P4) {
-      float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int r = 0; r < R; ++r) {
-        const float4 t = red[tid + P4 * r];
-        o.x += t.x; o.y += t.y; o.z += t.z; o.w += t.w;
+    if (P4 < 64) {
+      // the R threads of a group sit at lanes j4 + P4 k of each wave: sum them across lanes
+      // first, then the waves' sums through LDS
+      for (int off = P4; off < 64; off <<= 1) {
+        acc.x += __shfl_xor(acc.x, off);
+        acc.y += __shfl_xor(acc.y, off);
+        acc.z += __shfl_xor(acc.z, off);
+        acc.w += __shfl_xor(acc.w, off);
       }
-      const float inv = 1.0f / Ls[hh];
-      *reinterpret_cast<float4*>(dst + oi) = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+      if (lane < P4) red[wave * P4 + lane] = acc;
+      __syncthreads();
+      if (tid < P4) {
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int r = 0; r < NT / 64; ++r) {
+          const float4 t = red[tid + P4 * r];
+          o.x += t.x; o.y += t.y; o.z += t.z; o.w += t.w;
+        }
+        const float inv = 1.0f / Ls[hh];
+        *reinterpret_cast<float4*>(dst + oi) = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+      }
+    } else {
+      red[tid] = acc;
+      __syncthreads();
+      if (tid < P4) {
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int r = 0; r < R; ++r) {
+          const float4 t = red[tid + P4 * r];
+          o.x += t.x; o.y += t.y; o.z += t.z; o.w += t.w;
+        }
+        const float inv = 1.0f / Ls[hh];
+        *reinterpret_cast<float4*>(dst + oi) = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+      }
     }
     __syncthreads();
   }
@@ -509,6 +535,10 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   // `len` packed positions in 128-token tiles; workgroups from n_packed_splits on read the
   // n_recent positions of the recent window instead (one 128-slot ring tile per wave)
   const bool recent_wg = s >= n_packed_splits;
+  // tag base of this call's split partials: read first (its round trip overlaps the set-up);
+  // only a merger of this same call advances it, after every split has published, so every
+  // workgroup of the call reads the same value
+  const unsigned epoch = __hip_atomic_load(epochs + bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int64_t n_tiles = (len + kVTile - 1) / kVTile;
   const int64_t t_begin = recent_wg ? n_tiles : static_cast<int64_t>(s) * tiles_per_split;
   const int64_t t_end = recent_wg ? n_tiles : (t_begin + tiles_per_split < n_tiles ? t_begin + tiles_per_split : n_tiles);
@@ -521,36 +551,50 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   const bool setup_wave = __builtin_amdgcn_readfirstlane(wave) < 4;
   const int st = tid & 255;   // set-up thread
   const uint8_t* gimg = tabg->lds_image[KV ? 2 : NF ? 1 : 0];
-  const uint4 timg = reinterpret_cast<const uint4*>(gimg)[st < kLdsTableBytes / 16 ? st : kLdsTableBytes / 16 - 1];
+  const uint16_t* gimg16 = reinterpret_cast<const uint16_t*>(gimg);
+  uint4 timg = make_uint4(0u, 0u, 0u, 0u);
   uint32_t qraw[QPT];
   float gr[QPT];
-#pragma unroll
-  for (int j = 0; j < QPT; ++j) {
-    const int k = st + 256 * j < G * kHeadDim ? st + 256 * j : G * kHeadDim - 1;
-    const int64_t qi = (static_cast<int64_t>(b) * n_q + h * G) * kHeadDim + k;
-    // fp32: the element; fp16: the aligned 32-bit word holding it (q is 4-byte aligned)
-    const int64_t byte = q_f32 ? 4 * qi : (2 * qi) & ~static_cast<int64_t>(3);
-    qraw[j] = *reinterpret_cast<const uint32_t*>(static_cast<const char*>(qv) + byte);
-    gr[j] = P->g[k % kHeadDim];
-  }
-  const uint32_t fd_r = P->fdim[st & (kHeadDim - 1)];
-  const uint32_t pd_r = P->pdesc[lane];   // descriptor of pair `lane`
-  const int nf_r = P->n_fields;
-  // sources of the per-workgroup pair tables (see below)
-  const uint32_t rep4v = reinterpret_cast<const uint32_t*>(gimg + pair_table_base(4))[st];
-  const uint32_t rep3v = reinterpret_cast<const uint32_t*>(gimg + pair_table_base(3))[st & 63];
-  // rows 0..31: CB_5[st]; rows 32..95: CB_6[st - 32] (higher threads read a valid entry, unused)
-  const uint32_t cb56 = reinterpret_cast<const uint16_t*>(gimg + single_table_base(st < 32 ? 5 : 6))[st < 32 ? st : (st - 32) & 63];
-  // CB_8[st] and CB_7[st % 128]
-  const uint32_t cb8 = reinterpret_cast<const uint16_t*>(gimg + single_table_base(8))[st];
-  const uint32_t cb7 = reinterpret_cast<const uint16_t*>(gimg + single_table_base(7))[st & 127];
+  uint32_t fd_r = 0u, pd_r = 0u, rep4v = 0u, rep3v = 0u, cb6 = 0u, cb8 = 0u, cb7 = 0u, cb5lo = 0u;
+  uint32_t cb5hi[4] = {0u, 0u, 0u, 0u};
+  int nf_r = 0;
   // rotation inside equal-width groups: the chunk (start | size << 8) of field st % 128 and the
   // sign of dim st % 128
   uint32_t rg_chunk = 0u;
   float rg_sign = 1.0f;
-  if (rot_groups && rot != nullptr) {
-    rg_chunk = static_cast<uint32_t>(P->cstart[st & 127]) | (static_cast<uint32_t>(P->csize[st & 127]) << 8);
-    rg_sign = static_cast<float>(rot[h * kHeadDim + (st & 127)]);
+#pragma unroll
+  for (int j = 0; j < QPT; ++j) {
+    qraw[j] = 0u;
+    gr[j] = 0.0f;
+  }
+  if (setup_wave) {   // (with 8 waves, waves 4..7 load nothing of the set-up)
+    timg = reinterpret_cast<const uint4*>(gimg)[st < kLdsTableBytes / 16 ? st : kLdsTableBytes / 16 - 1];
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) {
+      const int k = st + 256 * j < G * kHeadDim ? st + 256 * j : G * kHeadDim - 1;
+      const int64_t qi = (static_cast<int64_t>(b) * n_q + h * G) * kHeadDim + k;
+      // fp32: the element; fp16: the aligned 32-bit word holding it (q is 4-byte aligned)
+      const int64_t byte = q_f32 ? 4 * qi : (2 * qi) & ~static_cast<int64_t>(3);
+      qraw[j] = *reinterpret_cast<const uint32_t*>(static_cast<const char*>(qv) + byte);
+      gr[j] = P->g[k % kHeadDim];
+    }
+    fd_r = P->fdim[st & (kHeadDim - 1)];
+    pd_r = P->pdesc[lane];   // descriptor of pair `lane`
+    nf_r = P->n_fields;
+    // sources of the per-workgroup tables (see below)
+    rep4v = reinterpret_cast<const uint32_t*>(gimg + pair_table_base(4))[st];
+    rep3v = reinterpret_cast<const uint32_t*>(gimg + pair_table_base(3))[st & 63];
+    cb6 = gimg16[single_table_base(6) / 2 + (st & 63)];
+    cb8 = gimg16[single_table_base(8) / 2 + st];
+    cb7 = gimg16[single_table_base(7) / 2 + (st & 127)];
+    // width-5 pair entries st + 256 i: CB_5[st % 32] and CB_5[st / 32 + 8 i]
+    cb5lo = gimg16[single_table_base(5) / 2 + (st & 31)];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cb5hi[i] = gimg16[single_table_base(5) / 2 + (st >> 5) + 8 * i];
+    if (rot_groups && rot != nullptr) {
+      rg_chunk = static_cast<uint32_t>(P->cstart[st & 127]) | (static_cast<uint32_t>(P->csize[st & 127]) << 8);
+      rg_sign = static_cast<float>(rot[h * kHeadDim + (st & 127)]);
+    }
   }
 
   // K rows of tokens lane and lane + 64 (first 16 words), scales of tokens 16 tg + n, V segments
@@ -621,8 +665,13 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   // its own reads the split's last tile and discards it); its V tile is copied once the
   // set-up data has been used, so waiting for the set-up loads never waits for it
   const int64_t t0 = t_begin + wave < t_end ? t_begin + wave : (t_end > 0 ? t_end - 1 : 0);
-  load_k(t0);
-  load_scales(t0);
+  // with 8 waves, the older four (one per SIMD) ask for their tiles first; the younger four
+  // ask once the set-up has landed
+  const bool late_tile = W == 8 && !setup_wave;
+  if (!late_tile) {
+    load_k(t0);
+    load_scales(t0);
+  }
 
   // ---- set-up: tables, scaled query, field dims and pair descriptors into LDS ----
   if (setup_wave) {
@@ -657,17 +706,24 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
         }
       }
     }
-    // single tables of widths 5..8 when the plan stores such blocks: for widths 5 and 6,
-    // thread t < 96 writes the 32 copies of one entry; for widths 7 and 8, thread t writes
-    // CB_8[t] and (t < 128) CB_7[t]
+    // tables of widths 5..8 when the plan stores such blocks: the width-5 pair table (thread t
+    // writes entries t + 256 i), 32 copies of the width-6 single table (thread t < 64 writes
+    // the copies of entry t), and for widths 7 and 8 thread t writes CB_8[t] and (t < 128)
+    // CB_7[t].  Pairs of 6 bits or more take two single lookups in the key product.
     const uint32_t pw = pd_r >> 16;
-    const uint64_t wide = __ballot(pw >= 5u);
-    const uint64_t w56 = __ballot(pw == 5u || pw == 6u);
+    const uint64_t wide = __ballot(pw >= 6u);
+    const uint64_t w5 = __ballot(pw == 5u);
+    const uint64_t w6 = __ballot(pw == 6u);
     const uint64_t w78 = __ballot(pw >= 7u);
     if (tid == 0) wide_s = wide;
-    if (w56 && tid < 96) {
-      const uint4 v = make_uint4(cb56, cb56, cb56, cb56);
-      char* row = tab_s + (tid < 32 ? kSing5Base + (tid << 7) : kSing6Base + ((tid - 32) << 7));
+    if (w5) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<uint32_t*>(tab_s + kPair5Base + 4 * (tid + 256 * i)) = cb5lo | (cb5hi[i] << 16);
+    }
+    if (w6 && tid < 64) {
+      const uint4 v = make_uint4(cb6, cb6, cb6, cb6);
+      char* row = tab_s + kSing6Base + (tid << 7);
 #pragma unroll
       for (int j = 0; j < 8; ++j) *reinterpret_cast<uint4*>(row + 16 * ((j + tid) & 7)) = v;
     }
@@ -677,6 +733,10 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     }
   }
   lds_barrier();
+  if (late_tile) {
+    load_k(t0);
+    load_scales(t0);
+  }
   // rotated keys (randomized Hadamard R = H D / sqrt(128)): <q, R^T y> = <R q, y>, so the
   // packed splits rotate the scaled query (fast Walsh-Hadamard stages in fp32); the recent
   // window holds unrotated keys
@@ -754,7 +814,7 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   }
   const uint32_t lb = (lane & 31u) << 2;   // this lane's replica offset
   lds_barrier();
-  const uint64_t uses_wide = wide_s;       // pairs (plan ranks) with blocks of 5..8 bits
+  const uint64_t uses_wide = wide_s;       // pairs (plan ranks) with blocks of 6..8 bits
 
   // ---- per-wave state: lane (n, g) keeps heads 2g, 2g + 1 ----
   const int h0 = 2 * g, h1 = 2 * g + 1;
@@ -828,14 +888,17 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
         u[t][3] = lds_u32(tab_s, (__builtin_amdgcn_ubfe(xb[t], P.rel3, P.bw[3]) << P.ps[3]) | P.pb[3]);
       }
       if ((uses_wide >> (16 * c)) & 0xFFFFull) {
-        // blocks of 5..8 bits, without branches per pair: the first field was looked up above;
+        // blocks of 6..8 bits, without branches per lane: the first field was looked up above;
         // the second comes from the same single table (same shift and base) into the high
-        // half.  Lanes whose pair is narrower read a placeholder and keep their value.
+        // half.  Lanes whose pair is narrower read a placeholder and keep their value.  Pair
+        // position p of the chunk holds ranks 16 c + 8 (p / 2) + (p % 2) + 2 g: positions with
+        // no such pair in any lane group are skipped.
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
+          if (!((uses_wide >> (16 * c + 8 * (p >> 1) + (p & 1))) & 0x55ull)) continue;
           const uint32_t w = (P.wid >> (8 * p)) & 0xFFu;
           const uint32_t rel = (p & 1) ? (p == 1 ? P.rel1 : P.rel3) : 0u;
-          const bool wide = w >= 5u;
+          const bool wide = w >= 6u;
           uint32_t v[4];
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
@@ -1090,8 +1153,6 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     }
   }
 
-  // tag base of this call's split partials (read before this workgroup publishes anything)
-  const unsigned epoch = __hip_atomic_load(epochs + bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // ---- merge the W waves of this workgroup: each wave adds its lo columns (n + G) into its
   //      hi columns (n) and writes them, with its (m, l), to LDS; after one barrier every
