@@ -327,11 +327,161 @@ __global__ __launch_bounds__(kThreads) void quantize_append(
   }
 }
 
+// A few new positions (a decode step's), one workgroup per (KV head, sequence): the same row
+// quantizer as quantize_append, arranged for latency.  Every load of the call (rows, plan,
+// boundary tables) is issued in one round; the squares y_i^2 of all rows are formed in parallel
+// (exact in fp64), so the scale lane of each row only runs the sum's dependent chain; every
+// thread then quantizes one (position, element) at a time; K rows are stored whole and V codes
+// OR-ed into their segment words in HBM.  No fp16 window, no rotation, not the 256-value codec.
+constexpr int kSmallMax = 4;   // positions per call handled this way
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void quantize_small(
+    const T* __restrict__ kin, const T* __restrict__ vin, int n_new, int64_t L0, int n_kv, int64_t cap,
+    const Plan* __restrict__ plans, int plan_bs, const Tables* __restrict__ tab, uint32_t* __restrict__ kc,
+    uint32_t* __restrict__ vc, uint16_t* __restrict__ ks, uint16_t* __restrict__ vs, int k_words, int v_bits) {
+  constexpr int kVec = 16 / sizeof(T);                       // elements per 16-byte load
+  constexpr int kRowVec = kHeadDim / kVec;                   // 16-byte pieces per row
+  constexpr int kBd4 = (kMaxBits + 1) * 256 / 4;             // boundary table in 16-byte pieces
+  const int tid = threadIdx.x;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const Plan* P = plans + static_cast<int64_t>(b) * plan_bs + h;
+
+  __shared__ __attribute__((aligned(16))) float bd_s[(kMaxBits + 1) * 256];
+  __shared__ __attribute__((aligned(16))) T x_s[2][kSmallMax][kHeadDim];      // [K, V][position][dim]
+  __shared__ __attribute__((aligned(16))) double sq_s[2 * kSmallMax][kHeadDim];
+  __shared__ float ig_s[kHeadDim];
+  __shared__ uint8_t fdim_s[kHeadDim], fw_s[kHeadDim];
+  __shared__ uint16_t foff_s[kHeadDim];
+  __shared__ float is_s[2 * kSmallMax];
+  __shared__ uint32_t krow_s[kSmallMax * 4 * kMaxBits];
+
+  // ---- one round of loads: boundary tables, rows, plan ----
+  uint4 bdv[(kBd4 + kThreads - 1) / kThreads];
+#pragma unroll
+  for (int j = 0; j < (kBd4 + kThreads - 1) / kThreads; ++j) {
+    const int q = tid + kThreads * j;
+    bdv[j] = reinterpret_cast<const uint4*>(&tab->bd[0][0])[q < kBd4 ? q : kBd4 - 1];
+  }
+  // row piece tid: tensor tid / (kSmallMax kRowVec), position, 16-byte piece
+  const int rt = tid / (kSmallMax * kRowVec), rp = (tid / kRowVec) % kSmallMax, rq = tid % kRowVec;
+  const bool rl = rt < 2 && rp < n_new;
+  uint4 xv = make_uint4(0u, 0u, 0u, 0u);
+  if (rl) {
+    const T* src = (rt ? vin : kin) + ((static_cast<int64_t>(b) * n_new + rp) * n_kv + h) * kHeadDim + rq * kVec;
+    xv = *reinterpret_cast<const uint4*>(src);
+  }
+  float igv = 1.0f;
+  uint32_t fdv = 0u, fwv = 0u, fov = 0u;
+  if (tid < kHeadDim) {
+    igv = P->ig[tid];
+    fdv = P->fdim[tid];
+    fwv = P->fwidth[tid];
+    fov = P->foff[tid];
+  }
+  const int nfld = P->n_fields;
+#pragma unroll
+  for (int j = 0; j < (kBd4 + kThreads - 1) / kThreads; ++j) {
+    const int q = tid + kThreads * j;
+    if (q < kBd4) reinterpret_cast<uint4*>(bd_s)[q] = bdv[j];
+  }
+  if (rl) *reinterpret_cast<uint4*>(&x_s[rt][rp][rq * kVec]) = xv;
+  if (tid < kHeadDim) {
+    ig_s[tid] = igv;
+    fdim_s[tid] = static_cast<uint8_t>(fdv);
+    fw_s[tid] = static_cast<uint8_t>(fwv);
+    foff_s[tid] = static_cast<uint16_t>(fov);
+  }
+  for (int k = tid; k < kSmallMax * k_words; k += kThreads) krow_s[k] = 0u;
+  __syncthreads();
+
+  // ---- squares y_i^2 in fp64 (exact), all rows at once: y = x * ig for K, x for V ----
+  for (int e = tid; e < 2 * n_new * kHeadDim; e += kThreads) {
+    const int c = e / kHeadDim, i = e % kHeadDim;           // chain c: K of position c, or V of c - n_new
+    const int t = c < n_new ? 0 : 1, p = c < n_new ? c : c - n_new;
+    const float x = to_f(x_s[t][p][i]);
+    const double y = static_cast<double>(t == 0 ? __fmul_rn(x, ig_s[i]) : x);
+    sq_s[c][i] = __dmul_rn(y, y);
+  }
+  __syncthreads();
+  // ---- scales: the sum of squares in dim order, one lane per row ----
+  if (tid < 2 * n_new) {
+    const int c = tid, t = c < n_new ? 0 : 1, p = c < n_new ? c : c - n_new;
+    double ss = 0.0;
+#pragma unroll 16
+    for (int i = 0; i < kHeadDim; ++i) ss = __dadd_rn(ss, sq_s[c][i]);
+    const __half s16 = __float2half_rn(static_cast<float>(__dsqrt_rn(ss / static_cast<double>(kHeadDim))));
+    is_s[c] = inv_scale(s16);
+    (t == 0 ? ks : vs)[(static_cast<int64_t>(b) * n_kv + h) * cap + L0 + p] = __half_as_ushort(s16);
+  }
+  __syncthreads();
+
+  // ---- codes: element e = (position, K field or V dim); binary search over the width's
+  //      boundaries (a u on a boundary takes the lower code) ----
+  for (int e = tid; e < 2 * n_new * kHeadDim; e += kThreads) {
+    const int c = e / kHeadDim, j = e % kHeadDim;
+    const bool key = c < n_new;
+    const int p = key ? c : c - n_new;
+    int w;
+    float u;
+    if (key) {
+      if (j >= nfld) continue;
+      const int i = fdim_s[j];
+      w = fw_s[j];
+      u = __fmul_rn(__fmul_rn(to_f(x_s[0][p][i]), ig_s[i]), is_s[c]);
+    } else {
+      w = v_bits;
+      u = __fmul_rn(to_f(x_s[1][p][j]), is_s[c]);
+    }
+    uint32_t code = 0u;
+    const float* bw = bd_s + 256 * w;
+    for (int sh = w - 1; sh >= 0; --sh) {
+      const uint32_t step = 1u << sh;
+      code += bw[code + step - 1u] < u ? step : 0u;
+    }
+    if (key) {
+      const int off = foff_s[j], word = off >> 5, sb = off & 31;
+      atomicOr(&krow_s[p * k_words + word], code << sb);
+      if (sb + w > 32) atomicOr(&krow_s[p * k_words + word + 1], code >> (32 - sb));
+    } else {
+      const int64_t pos = L0 + p;
+      const int gq = static_cast<int>((pos % kVTile) / 32), bit = static_cast<int>(pos % 32) * w;
+      uint32_t* seg = vc + ((static_cast<int64_t>(b) * n_kv + h) * (cap / kVTile) + pos / kVTile) * kVTile * 4 * w +
+                      static_cast<int64_t>(((j / 16) * 4 + gq) * 16 + j % 16) * w;
+      const int word = bit >> 5, sb = bit & 31;
+      if (code) {
+        atomicOr(seg + word, code << sb);
+        if (sb + w > 32 && (code >> (32 - sb))) atomicOr(seg + word + 1, code >> (32 - sb));
+      }
+    }
+  }
+  __syncthreads();
+  uint32_t* dst = kc + ((static_cast<int64_t>(b) * n_kv + h) * cap + L0) * k_words;
+  for (int k = tid; k < n_new * k_words; k += kThreads) dst[k] = krow_s[k];
+}
+
 }  // namespace
 
 hipError_t launch_quantize(kvq_cache* c, int layer, const void* k, const void* v, int dtype,
                            int64_t n_new, int64_t in_stride, int ring_R, int64_t L0, hipStream_t stream) {
   const kvq_config& cfg = c->cfg;
+  if (n_new <= kSmallMax && ring_R == 0 && in_stride == n_new &&
+      (cfg.codec == KVQ_CODEC_BGTQ || cfg.codec == KVQ_CODEC_UNIFORM)) {
+    const Plan* plans = c->plans + static_cast<int64_t>(layer) * c->n_plan * cfg.n_kv_heads;
+    const int plan_bs = c->n_plan > 1 ? cfg.n_kv_heads : 0;
+    dim3 grid(static_cast<unsigned>(cfg.n_kv_heads), static_cast<unsigned>(cfg.batch));
+    if (dtype == KVQ_F16)
+      hipLaunchKernelGGL(quantize_small<__half>, grid, dim3(kThreads), 0, stream, static_cast<const __half*>(k),
+                         static_cast<const __half*>(v), static_cast<int>(n_new), L0, cfg.n_kv_heads, c->cap, plans,
+                         plan_bs, c->tables, layer_k_codes(c, layer), layer_v_codes(c, layer),
+                         layer_k_scales(c, layer), layer_v_scales(c, layer), c->k_words, cfg.v_bits);
+    else
+      hipLaunchKernelGGL(quantize_small<float>, grid, dim3(kThreads), 0, stream, static_cast<const float*>(k),
+                         static_cast<const float*>(v), static_cast<int>(n_new), L0, cfg.n_kv_heads, c->cap, plans,
+                         plan_bs, c->tables, layer_k_codes(c, layer), layer_v_codes(c, layer),
+                         layer_k_scales(c, layer), layer_v_scales(c, layer), c->k_words, cfg.v_bits);
+    return hipGetLastError();
+  }
   const int64_t first = L0 / kGroupTok, last = (L0 + n_new - 1) / kGroupTok;
   dim3 grid(static_cast<unsigned>(last - first + 1), static_cast<unsigned>(cfg.n_kv_heads),
             static_cast<unsigned>(cfg.batch));

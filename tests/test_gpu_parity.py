@@ -278,6 +278,16 @@ def test_bgtq_batched_t5():
     run_case("llama8b_b64", 2048, 4, 4, batch=4, noise="t5", temper=True)
 
 
+def test_decode_step_appends():
+    """Decode-sized appends (one to four positions per call, the latency path) after a prefill,
+    crossing 32-position V segments and 128-position tiles; fp32 and fp16 inputs, per-sequence
+    plans, the uniform codec; codes bit-exact and decode to the usual bar."""
+    run_case("tiny", 400, 3, 3, chunks=[300] + [1] * 50 + [2, 3, 4] * 5 + [5])
+    run_case("llama8b_b64", 600, 4, 3, batch=3, per_seq=True, chunks=[500] + [1] * 30 + [3] * 10 + [4] * 10,
+             temper=True)
+    run_case("llama8b_32k", 700, 2, 2, codec="uniform", chunks=[600] + [1] * 100)
+
+
 def test_recent_window_ragged_appends():
     """fp16 recent window of 256 positions: evictions from the ring (with wrap), positions
     that arrive already outside the window, fp32 inputs rounded to fp16 in the window."""
