@@ -360,6 +360,18 @@ kvq_status kvq_layer_info_get(const kvq_cache* cache, int32_t layer, kvq_layer_i
 kvq_status kvq_read_cache(const kvq_cache* cache, int32_t layer, int32_t part, int64_t offset,
                           int64_t nbytes, void* dst);
 
+/* Measurement aid, not a step of the method: one launch that reads nbytes of device memory
+   once (16-byte loads, n_blocks workgroups of 256 threads, grid-stride) and writes nothing but,
+   in practice never, one word of `sink` per workgroup.  Timing it over buffers of one decode
+   launch's size gives the per-launch HBM read ceiling the decode kernel's effective rate is
+   set against (the decode is bound by reading the packed cache: RoPE-Aware Bit Allocation for
+   KV-Cache Quantization, abstract, serving from the packed cache).
+   src: device, 16-byte aligned; nbytes a positive multiple of 16; sink: device uint32
+   [n_blocks], caller-owned.  Errors: KVQ_EINVAL (bad pointer, size or n_blocks outside
+   [1, 65536]), KVQ_EHIP. */
+kvq_status kvq_probe_stream_read(const void* src, int64_t nbytes, int32_t n_blocks, uint32_t* sink,
+                                 kvq_stream stream);
+
 /* Host copies of the library's own constant tables (no GPU needed).
    kvq_codebook: bits in [1, 8]; centroids: 2^bits fp16 bit patterns;
                  boundaries: 2^bits - 1 fp32 values (either pointer nullable).

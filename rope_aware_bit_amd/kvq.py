@@ -27,7 +27,7 @@ EXPORTED = (
     "kvq_quantize_append", "kvq_decode_attn", "kvq_decode_attn_splits", "kvq_key_fidelity", "kvq_set_rotation", "kvq_seq_len",
     "kvq_layer_info_get", "kvq_read_cache", "kvq_codebook", "kvq_delta",
     "kvq_nf16_codebook", "kvq_status_str", "kvq_last_error", "kvq_cache_status", "kvq_cache_view",
-    "kvq_decode_attn_noalloc",
+    "kvq_decode_attn_noalloc", "kvq_probe_stream_read",
 )
 
 PLAN_BYTES, PLAN_OFF_GAIN, PLAN_OFF_FIELD_DIM, PLAN_OFF_FIELD_WIDTH = 2256, 0, 1280, 1408
@@ -98,6 +98,7 @@ def _load() -> ctypes.CDLL:
         "kvq_cache_status": (I32, [P]),
         "kvq_cache_view": (I32, [P, I32, ctypes.POINTER(kvq_view)]),
         "kvq_decode_attn_noalloc": (I32, [P, I32, P, I32, F32, P, P]),
+        "kvq_probe_stream_read": (I32, [P, I64, I32, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -163,6 +164,12 @@ def nf16_codebook():
     bd = np.zeros(15, dtype=np.float32)
     _check(lib.kvq_nf16_codebook(lv.ctypes.data, bd.ctypes.data), "kvq_nf16_codebook")
     return lv.view(np.float16), bd
+
+
+def probe_stream_read(src, n_blocks: int, sink, stream=None):
+    """One streaming-read launch over the bytes of the GPU tensor `src` (a measurement aid)."""
+    _check(lib.kvq_probe_stream_read(_ptr(src), src.numel() * src.element_size(), int(n_blocks), _ptr(sink),
+                                     _stream(stream)), "kvq_probe_stream_read")
 
 
 # ---- cache -----------------------------------------------------------------------------------
