@@ -22,9 +22,10 @@ Beside the headline (skipped with --decode-only): the 524288-token K2V2 step
 uniform codec (12 copies cycled so the 256 MB last-level cache holds none),
 batched decode at 64 x 8192 for Block-GTQ and the 256-value absmax codec,
 codec variants of the headline layer, append rates from back-to-back launches,
-the decode step with each layer first appending the new position, the key
-fidelity diagnostics, and a quality side-report (logit MAE, softmax KL, output
-error) at the default and a tempered softmax scale.
+the decode step with each layer first appending the new position (one fused
+launch per layer, and as two calls), the key fidelity diagnostics, and a
+quality side-report (logit MAE, softmax KL, output error) at the default and a
+tempered softmax scale.
 
 The CPU baseline times the fp64 oracle's decode (unpack, dequantize,
 attention) of layer 0, repeated for at least 10 s of host time on one thread,
@@ -49,7 +50,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 PLAN_BYTES_PER_HEAD = 1024   # field dims/widths/offsets and gains read by each decode launch
-APPEND_STEPS = 24               # new positions of the append-and-attend steps (2 warm-up + 22 timed)
+APPEND_STEPS = 24               # new positions per append-and-attend variant (2 warm-up + 22 timed)
 SINGLE_APPENDS = 200            # one-position appends timed back to back
 CPU_SAMPLE_S = 10.0          # lower bound on the host time spent timing the oracle
 DECODE_SOURCES = ["decode_mfma.h", "decode_mfma.hip", "decode_mfma_g1.hip", "decode_mfma_g2.hip",
@@ -423,7 +424,7 @@ def main():
     timer = Timer(torch, stream)
 
     # capacity for the T cached positions plus the new ones of the append-and-attend steps
-    cache = kvq.Cache(kvq.Config(L, H, Hq, B, T + APPEND_STEPS, kb, vb))
+    cache = kvq.Cache(kvq.Config(L, H, Hq, B, T + 2 * APPEND_STEPS, kb, vb))
     gen = TorchLayerGen(w, dev)
     chunk = min(w.calib_tokens, T)
     keep = None
@@ -546,22 +547,35 @@ def main():
     del keys0
 
     # the decode step as a model runs it: every layer first appends the new position's K and V
-    # (one quantize_append of one position per sequence), then attends over the cache holding it
+    # (one position per sequence), then attends over the cache holding it.  decode_step does both
+    # in one launch; the second figure is the two calls (quantize_append, then decode_attn)
     step_app = None
     if not args.decode_only:
         g = torch.Generator(device=dev).manual_seed(5)
         new_kv = [(torch.randn(B, 1, H, 128, device=dev, generator=g).half(),
                    torch.randn(B, 1, H, 128, device=dev, generator=g).half()) for _ in range(L)]
 
-        def step_with_append():
+        def step_fused():
+            for layer in range(L):
+                cache.decode_step(layer, new_kv[layer][0][:, 0], new_kv[layer][1][:, 0], qs[layer], out=outs[layer])
+
+        def step_two_calls():
             for layer in range(L):
                 cache.quantize_append(layer, new_kv[layer][0], new_kv[layer][1])
                 cache.decode_attn(layer, qs[layer], out=outs[layer])
 
-        ms_app = timer.ms(step_with_append, APPEND_STEPS - 2, warm=2)
+        ms_app = timer.ms(step_fused, APPEND_STEPS - 2, warm=2)
+        # attention alone over the grown cache (T + 24 positions: one more, nearly empty, tile
+        # per head than the headline's T), the append's cost at equal length
+        ms_same = timer.ms(step, APPEND_STEPS - 2, warm=2)
+        ms_two = timer.ms(step_two_calls, APPEND_STEPS - 2, warm=2)
         step_app = {"ms_per_step": round(ms_app, 5), "tokens_per_s": round(B / (ms_app * 1e-3), 2),
                     "steps": APPEND_STEPS - 2, "vs_attention_only": round(ms_app / ms_step, 3),
-                    "append_us_per_layer": round((ms_app - ms_step) * 1e3 / L, 2)}
+                    "attention_only_same_len_ms": round(ms_same, 5),
+                    "vs_attention_only_same_len": round(ms_app / ms_same, 3),
+                    "append_us_per_layer": round((ms_app - ms_same) * 1e3 / L, 2),
+                    "two_calls": {"ms_per_step": round(ms_two, 5), "vs_attention_only": round(ms_two / ms_step, 3),
+                                  "append_us_per_layer": round((ms_two - ms_same) * 1e3 / L, 2)}}
 
     # average decode-launch duration: the timed region holds only decode launches on this stream
     launch_us = ms_step * 1e3 / L

@@ -247,6 +247,23 @@ kvq_status kvq_decode_attn_splits(kvq_cache* cache, int32_t layer, const void* q
                                   float softmax_scale, float* out, int32_t n_splits,
                                   kvq_stream stream);
 
+/* One decode step of a layer: appends one new position to every sequence and then attends
+   with q over all positions, the new one included ("RoPE-Aware Bit Allocation for KV-Cache
+   Quantization", abstract: decoding reads the packed cache directly; Pith review of NQKV,
+   "Assumptions & free parameters", third item: the cache is encoded append-only, so a new
+   position is quantized once, on arrival).
+   k_new, v_new: [batch][n_kv_heads][128] (dtype), 16-byte aligned; q and out as for
+   kvq_decode_attn; one dtype for all three inputs.
+   Codes, scales and output are those of kvq_quantize_append(..., n_new = 1) followed by
+   kvq_decode_attn.  For the Block-GTQ and uniform codecs without a recent window this is one
+   launch: the workgroup that reads the new position's tile quantizes it, stores it, and
+   uses it from its own copy; other codecs and recent windows run the two calls.
+   Errors: those of the two calls (KVQ_EINVAL, KVQ_ESTATE, KVQ_ECAPACITY); on an error
+   nothing is appended. */
+kvq_status kvq_decode_step(kvq_cache* cache, int32_t layer, const void* k_new, const void* v_new,
+                           const void* q, int32_t dtype, float softmax_scale, float* out,
+                           kvq_stream stream);
+
 /* As kvq_decode_attn (automatic split count), for callers that cannot allocate: code under
    HIP graph or stream capture, tight serving loops, harnesses that forbid allocation.  It makes
    no allocation of any kind: the split partials, maxima words and tag bases live in a fixed

@@ -364,8 +364,47 @@ kvq_status kvq_decode_attn_splits(kvq_cache* c, int32_t layer, const void* q, in
   // second kernel instead of in the decode kernel)
   const kvq::DecodeScratch ws{c->part_o, c->part_l, c->part_mt, c->split_epochs, c->dev_status, c->merge_polls};
   hipError_t e = kvq::launch_decode_mfma(c, layer, q, dtype, softmax_scale, out, S, ws,
-                                         static_cast<hipStream_t>(stream));
+                                         kvq::DecodeAppend{nullptr, nullptr, -1}, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return KVQ_OK;
+}
+
+kvq_status kvq_decode_step(kvq_cache* c, int32_t layer, const void* k_new, const void* v_new, const void* q,
+                           int32_t dtype, float softmax_scale, float* out, kvq_stream stream) {
+  if (!layer_ok(c, layer) || !k_new || !v_new || !q || !out) return KVQ_EINVAL;
+  if (dtype != KVQ_F16 && dtype != KVQ_F32) return KVQ_EINVAL;
+  const kvq_config& cfg = c->cfg;
+  if (!((cfg.codec == KVQ_CODEC_BGTQ || cfg.codec == KVQ_CODEC_UNIFORM) && cfg.recent_window == 0)) {
+    // the other codecs and the recent window: the append, then the attention
+    const kvq_status st = kvq_quantize_append(c, layer, k_new, v_new, dtype, 1, stream);
+    if (st != KVQ_OK) return st;
+    return kvq_decode_attn(c, layer, q, dtype, softmax_scale, out, stream);
+  }
+  if (reinterpret_cast<uintptr_t>(k_new) % 16 || reinterpret_cast<uintptr_t>(v_new) % 16) {
+    g_last_error = "decode_step: k_new and v_new must be 16-byte aligned";
+    return KVQ_EINVAL;
+  }
+  if (reinterpret_cast<uintptr_t>(q) % 4 || reinterpret_cast<uintptr_t>(out) % 16) {
+    g_last_error = "decode_step: q must be 4-byte and out 16-byte aligned";
+    return KVQ_EINVAL;
+  }
+  if (!(softmax_scale == softmax_scale)) return KVQ_EINVAL;  // NaN
+  if (!c->plan_ready[layer]) return KVQ_ESTATE;
+  if (c->len[layer] + 1 > cfg.max_tokens) return KVQ_ECAPACITY;
+  const int64_t pos = c->len[layer];
+  c->len[layer] = pos + 1;
+  const int S = kvq::auto_splits_mfma(c, kvq::packed_len(c, layer), 0);
+  if (S > c->max_splits) {
+    c->len[layer] = pos;
+    return KVQ_EINVAL;
+  }
+  const kvq::DecodeScratch ws{c->part_o, c->part_l, c->part_mt, c->split_epochs, c->dev_status, c->merge_polls};
+  const hipError_t e = kvq::launch_decode_mfma(c, layer, q, dtype, softmax_scale, out, S, ws,
+                                               kvq::DecodeAppend{k_new, v_new, pos}, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    c->len[layer] = pos;
+    return hip_fail(e, "decode step launch");
+  }
   return KVQ_OK;
 }
 

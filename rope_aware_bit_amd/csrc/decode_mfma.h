@@ -477,7 +477,7 @@ __device__ __attribute__((always_inline)) inline KWin k_windows(const KPar& k, c
 // Decode kernel.  W waves per workgroup (one or two per SIMD).  Every wave owns a region of
 // `region_words` LDS words that holds, in turn, its staged K tile, its softmax weights and its
 // share of the wave merge (and, during set-up, wave 0's region holds the scaled query).
-template <int G, int VB, bool NF, int W, bool KV>
+template <int G, int VB, bool NF, int W, bool KV, bool APP>
 __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     const void* __restrict__ qv, int q_f32, float sigma, int64_t len, int n_packed_splits,
     const __half* __restrict__ rk, const __half* __restrict__ rv, int R, int64_t n_recent,
@@ -487,7 +487,8 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     const uint16_t* __restrict__ vs, int k_words, int n_nf, int n_splits, int n_mergers, int region_words,
     int v_early, int v_off, float* __restrict__ part_o, float* __restrict__ part_l,
     uint64_t* __restrict__ part_mt, unsigned* __restrict__ epochs, unsigned* status, int max_polls,
-    float* __restrict__ out) {
+    const void* __restrict__ app_k, const void* __restrict__ app_v, int64_t app_pos, uint32_t* app_kc,
+    uint32_t* app_vc, uint16_t* app_ks, uint16_t* app_vs, float* __restrict__ out) {
   constexpr int NT = 64 * W;
   constexpr bool kPipe = W == 4;                      // one wave per SIMD: prefetch and pipeline
   constexpr int PCOLS = 2 * G;                        // P columns: hi of heads 0..G-1, then lo
@@ -511,6 +512,13 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   __shared__ float alpha_s[W][G];
   __shared__ float ms_s[G];
   __shared__ uint64_t wide_s;
+  // fused append: the new position's key row, value codes, scales (fp16 bits) and inverse
+  // scales, and its gain-normalised rows (keys) / rows (values) in fp32
+  __shared__ uint32_t app_kw[32];
+  __shared__ uint8_t app_vcode[kHeadDim];
+  __shared__ uint32_t app_s16[2];
+  __shared__ float app_is[2];
+  __shared__ float app_y[2][kHeadDim];
   extern __shared__ __attribute__((aligned(16))) uint32_t dyn_s[];   // [W][region_words]
   uint32_t* kr = dyn_s + wave * region_words;                         // [k_words + 1][kKS]
   _Float16* pw = reinterpret_cast<_Float16*>(kr);                     // [PCOLS][kPS], after keys
@@ -595,6 +603,47 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
       rg_chunk = static_cast<uint32_t>(P->cstart[st & 127]) | (static_cast<uint32_t>(P->csize[st & 127]) << 8);
       rg_sign = static_cast<float>(rot[h * kHeadDim + (st & 127)]);
     }
+  }
+
+  // ---- fused append of one new position app_pos (a decode step): rows [batch][n_kv][128] in
+  //      q's precision.  The workgroup whose tiles hold app_pos quantizes that position with the
+  //      row quantizer of the append (codes and scales identical to it), stores it in HBM and
+  //      puts the same codes and scales into its own copy of the tile, so nothing waits for the
+  //      stores.  Four waves aw0 .. aw0 + 3 do it (with 8 waves the younger four, idle during
+  //      the set-up): waves aw0 and aw0 + 1 form the key and value rows and their scales, then
+  //      each of the 256 threads quantizes one key field or value dim. ----
+  const int64_t app_tile = app_pos >= 0 ? app_pos / kVTile : -1;
+  const bool app_wg = APP && !NF && !KV && app_pos >= 0 && !recent_wg && t_begin <= app_tile && app_tile < t_end;
+  // (in the tile loop: the tile to patch, -1 for none, and the position's index in it)
+  const int app_t32 = app_wg ? static_cast<int>(app_tile) : -1;
+  const int app_tau = static_cast<int>(app_pos & (kVTile - 1));
+  constexpr int aw0 = W - 4;
+  const int awave = __builtin_amdgcn_readfirstlane(wave) - aw0;   // 0 .. 3 on the append waves
+  const bool app_wave = app_wg && awave >= 0;
+  const int at = tid - 64 * aw0;
+  float ax0 = 0.0f, ax1 = 0.0f, ag0 = 1.0f, ag1 = 1.0f;
+  uint32_t a_fw = 0u, a_fo = 0u, a_fd = 0u;
+  int a_nf = 0;
+  if (app_wave) {
+    if (awave < 2) {
+      const int64_t e = bh * kHeadDim + lane;
+      const void* src = awave ? app_v : app_k;
+      if (q_f32) {
+        ax0 = static_cast<const float*>(src)[e];
+        ax1 = static_cast<const float*>(src)[e + 64];
+      } else {
+        ax0 = __half2float(static_cast<const __half*>(src)[e]);
+        ax1 = __half2float(static_cast<const __half*>(src)[e + 64]);
+      }
+      if (awave == 0) {
+        ag0 = P->ig[lane];
+        ag1 = P->ig[lane + 64];
+      }
+    }
+    a_fw = P->fwidth[at & 127];
+    a_fo = P->foff[at & 127];
+    a_fd = P->fdim[at & 127];
+    a_nf = P->n_fields;
   }
 
   // K rows of tokens lane and lane + 64 (first 16 words), scales of tokens 16 tg + n, V segments
@@ -732,6 +781,26 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
       if (tid < 128) *reinterpret_cast<uint32_t*>(tab_s + kSing7Base + 4 * tid) = cb7;
     }
   }
+  if (app_wave && awave < 2) {
+    // key row y = x * ig_i (fp32), value row x; scale = fp16(fp32(sqrt(sum y_i^2 / 128))) with
+    // the fp64 sum taken in dim order, inverse scale fp32(1 / scale) (0 for a zero scale)
+    app_y[awave][lane] = awave ? ax0 : __fmul_rn(ax0, ag0);
+    app_y[awave][lane + 64] = awave ? ax1 : __fmul_rn(ax1, ag1);
+    if (awave == 0 && lane < 32) app_kw[lane] = 0u;
+    wave_sync();
+    if (lane == 0) {
+      double ss = 0.0;
+#pragma unroll 16
+      for (int i = 0; i < kHeadDim; ++i) {
+        const double y = static_cast<double>(app_y[awave][i]);
+        ss = __dadd_rn(ss, __dmul_rn(y, y));
+      }
+      const __half s16 = __float2half_rn(static_cast<float>(__dsqrt_rn(ss / static_cast<double>(kHeadDim))));
+      const float sf = __half2float(s16);
+      app_s16[awave] = __half_as_ushort(s16);
+      app_is[awave] = sf == 0.0f ? 0.0f : __fdiv_rn(1.0f, sf);
+    }
+  }
   lds_barrier();
   if (late_tile) {
     load_k(t0);
@@ -812,9 +881,54 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
       a_s[c][2 * hh + 1][k] = static_cast<_Float16>(qq - static_cast<float>(hi));
     }
   }
+  if (app_wave) {
+    // codes: thread at < 128 key field at, thread at >= 128 value dim at - 128; u = y * is, and
+    // the code is the number of boundaries below u, the boundary between centroids k and k + 1
+    // being their midpoint (exact in fp32 for fp16 centroids)
+    const bool key = at < 128;
+    const int w = key ? static_cast<int>(a_fw) : VB;
+    if (!key || at < a_nf) {
+      const float u = __fmul_rn(key ? app_y[0][a_fd] : app_y[1][at - 128], app_is[key ? 0 : 1]);
+      const _Float16* cbw = reinterpret_cast<const _Float16*>(tab_s + kImageBase + single_table_base(w));
+      uint32_t code = 0u;
+      for (int sh = w - 1; sh >= 0; --sh) {
+        const uint32_t step = 1u << sh, k = code + step - 1u;
+        const float bk = __fmul_rn(0.5f, __fadd_rn(static_cast<float>(cbw[k]), static_cast<float>(cbw[k + 1])));
+        code += bk < u ? step : 0u;
+      }
+      if (key) {
+        const uint32_t wd = a_fo >> 5, sb = a_fo & 31u;
+        atomicOr(&app_kw[wd], code << sb);
+        if (sb + w > 32u) atomicOr(&app_kw[wd + 1], code >> (32u - sb));
+      } else {
+        app_vcode[at - 128] = static_cast<uint8_t>(code);
+      }
+    }
+  }
   const uint32_t lb = (lane & 31u) << 2;   // this lane's replica offset
   lds_barrier();
   const uint64_t uses_wide = wide_s;       // pairs (plan ranks) with blocks of 6..8 bits
+  // the new position into HBM: its key row whole, its value codes OR-ed into their segment words
+  // (the position's bits are still zero there), its scales.  Issued by each append wave once it
+  // has waited for its own tile's loads (after the value tile copy), so that no wait of the tile
+  // loop also waits for these stores.
+  auto app_store = [&]() __attribute__((always_inline)) {
+    if (!app_wave) return;
+    if (at < k_words) app_kc[(bh * cap + app_pos) * k_words + at] = app_kw[at];
+    const uint32_t a_vcode = at >= 128 ? static_cast<uint32_t>(app_vcode[at - 128]) : 0u;
+    if (a_vcode != 0u) {
+      const int j = at - 128, gq = app_tau >> 5;
+      const uint32_t bit = static_cast<uint32_t>(app_tau & 31) * VB, wd = bit >> 5, sb = bit & 31u;
+      uint32_t* seg = app_vc + (bh * (cap / kVTile) + app_t32) * (kVTile * KWV) +
+                      ((((j >> 4) << 2) + gq) * 16 + (j & 15)) * VB;
+      atomicOr(seg + wd, a_vcode << sb);
+      if (sb + VB > 32u && (a_vcode >> (32u - sb))) atomicOr(seg + wd + 1, a_vcode >> (32u - sb));
+    }
+    if (at == 0) {
+      app_ks[bh * cap + app_pos] = static_cast<uint16_t>(app_s16[0]);
+      app_vs[bh * cap + app_pos] = static_cast<uint16_t>(app_s16[1]);
+    }
+  };
 
   // ---- per-wave state: lane (n, g) keeps heads 2g, 2g + 1 ----
   const int h0 = 2 * g, h1 = 2 * g + 1;
@@ -856,6 +970,20 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
       dst[64] = x1.x; dst[kKS + 64] = x1.y; dst[2 * kKS + 64] = x1.z; dst[3 * kKS + 64] = x1.w;
     }
     kr[k_words * kKS + lane] = kr[k_words * kKS + 64 + lane] = 0u;
+    if (APP && static_cast<int>(tile) == app_t32) {   // the appended position: row and scales from above
+      const int tau = app_tau;
+      if (lane < k_words) kr[lane * kKS + tau] = app_kw[lane];
+      // (selected by masks, not by conditional writes, which the compiler would merge into one
+      // write at a variable index and so move the scale registers to memory)
+      const uint32_t hit = n == (tau & 15) ? 0xFFFFFFFFu : 0u;
+      const uint32_t nk = app_s16[0], nv = app_s16[1];
+#pragma unroll
+      for (int tg = 0; tg < 8; ++tg) {
+        const uint32_t m = tg == (tau >> 4) ? hit : 0u;
+        skr[tg] = (skr[tg] & ~m) | (nk & m);
+        svr[tg] = (svr[tg] & ~m) | (nv & m);
+      }
+    }
     pack_scales();
     if constexpr (KV) {
       kvp[lane] = kpr;
@@ -1012,6 +1140,22 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     // -- values: O^T[dim][col] += V^T[dim][tok] P^T[tok][col] over 4 chunks of 32 tokens --
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the V tile copy has landed
     wave_sync();
+    if (APP && static_cast<int>(tile) == app_t32) {   // the appended position's value codes into the copy
+      const int tau = app_tau;
+      const int bit = (tau & 31) * VB, wd = bit >> 5, sb = bit & 31;
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int j = lane + 64 * jj;
+        const uint32_t code = app_vcode[j];
+        uint32_t* seg = vbuf + ((((j >> 4) << 2) + (tau >> 5)) * 16 + (j & 15)) * VB;
+        seg[wd] |= code << sb;
+        if (sb + VB > 32) seg[wd + 1] |= code >> (32 - sb);
+      }
+      wave_sync();
+    }
+    if constexpr (APP) {
+      if (first) app_store();
+    }
     uint32_t vseg[8][VB + 2];
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
@@ -1059,6 +1203,8 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   if (t_begin + wave < t_end) {
     tile_body(t_begin + wave, true);
     for (int64_t tile = t_begin + wave + W; tile < t_end; tile += W) tile_body(tile, false);
+  } else if constexpr (APP) {
+    app_store();
   }
   if (recent_wg) {
     // ---- recent window: fp16 keys [R][n_kv][128] and values in dim-major 128-slot tiles, no
@@ -1264,7 +1410,8 @@ __global__ __launch_bounds__(256) void decode_merge(
 
 template <int G, int VB, int W>
 hipError_t launch_gvw(kvq_cache* c, int layer, const void* q, int q_f32, float sigma, float* out,
-                      int S, const DecodeShape& sh, const DecodeScratch& ws, hipStream_t stream) {
+                      int S, const DecodeShape& sh, const DecodeScratch& ws, const DecodeAppend& app,
+                      hipStream_t stream) {
   const kvq_config& cfg = c->cfg;
   // S packed splits over the packed positions, plus one workgroup for the recent window
   const int64_t plen = packed_len(c, layer);
@@ -1283,26 +1430,30 @@ hipError_t launch_gvw(kvq_cache* c, int layer, const void* q, int q_f32, float s
   const Plan* plans = c->plans + static_cast<int64_t>(layer) * c->n_plan * cfg.n_kv_heads;
   const int plan_bs = c->n_plan > 1 ? cfg.n_kv_heads : 0;
   const int mergers = decode_split_mergers(S_all, static_cast<int64_t>(cfg.batch) * cfg.n_kv_heads, c->n_cu);
-#define KVQ_LAUNCH_DEC(NF, KV)                                                                         \
-  hipLaunchKernelGGL((decode_mfma<G, VB, NF, W, KV>), grid, dim3(64 * W), dyn, stream, q, q_f32, sigma,   \
+#define KVQ_LAUNCH_DEC(NF, KV, APP)                                                                    \
+  hipLaunchKernelGGL((decode_mfma<G, VB, NF, W, KV, APP>), grid, dim3(64 * W), dyn, stream, q, q_f32, sigma, \
                      plen, S, rk, rv, R, n_recent, rot, rot_groups, cfg.n_kv_heads, c->cap, tps, plans, plan_bs, \
                      c->tables, layer_k_codes(c, layer), layer_v_codes(c, layer), layer_k_scales(c, layer), \
                      layer_v_scales(c, layer), c->k_words, c->n_nf_blocks, S_all, mergers, sh.region_words,  \
-                     sh.v_early, sh.v_off, ws.o, ws.l, ws.mt, ws.epochs, ws.status, ws.max_polls, out)
+                     sh.v_early, sh.v_off, ws.o, ws.l, ws.mt, ws.epochs, ws.status, ws.max_polls, app.k, app.v,   \
+                     app.pos, layer_k_codes(c, layer), layer_v_codes(c, layer), layer_k_scales(c, layer),         \
+                     layer_v_scales(c, layer), out)
   bool launched = false;
   if constexpr (VB == 4) {
     if (cfg.codec == KVQ_CODEC_NF16_B256) {
-      KVQ_LAUNCH_DEC(true, false);
+      KVQ_LAUNCH_DEC(true, false, false);
       launched = true;
     }
   }
   if constexpr (VB <= 4) {
     if (!launched && cfg.codec == KVQ_CODEC_KIVI) {
-      KVQ_LAUNCH_DEC(false, true);
+      KVQ_LAUNCH_DEC(false, true, false);
       launched = true;
     }
   }
-  if (!launched) KVQ_LAUNCH_DEC(false, false);
+  // a decode step's append (Block-GTQ / uniform codecs only) runs in an instantiation of its own
+  if (!launched && app.pos >= 0) KVQ_LAUNCH_DEC(false, false, true);
+  else if (!launched) KVQ_LAUNCH_DEC(false, false, false);
 #undef KVQ_LAUNCH_DEC
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S_all <= 1 || mergers > 0) return e;
@@ -1315,28 +1466,28 @@ hipError_t launch_gvw(kvq_cache* c, int layer, const void* q, int q_f32, float s
 
 template <int G, int VB>
 hipError_t launch_gv(kvq_cache* c, int layer, const void* q, int q_f32, float sigma, float* out,
-                     int S, const DecodeScratch& ws, hipStream_t stream) {
+                     int S, const DecodeScratch& ws, const DecodeAppend& app, hipStream_t stream) {
   const DecodeShape sh = decode_shape(c);
   if constexpr (VB <= 4) {   // wider V tiles never leave room for 8 waves
-    if (sh.waves == 8) return launch_gvw<G, VB, 8>(c, layer, q, q_f32, sigma, out, S, sh, ws, stream);
+    if (sh.waves == 8) return launch_gvw<G, VB, 8>(c, layer, q, q_f32, sigma, out, S, sh, ws, app, stream);
   }
   if (sh.waves != 4) return hipErrorInvalidConfiguration;
-  return launch_gvw<G, VB, 4>(c, layer, q, q_f32, sigma, out, S, sh, ws, stream);
+  return launch_gvw<G, VB, 4>(c, layer, q, q_f32, sigma, out, S, sh, ws, app, stream);
 }
 
 template <int G>
 hipError_t launch_group(kvq_cache* c, int layer, const void* q, int q_f32, float sigma, float* out,
-                        int S, const DecodeScratch& ws, hipStream_t stream) {
+                        int S, const DecodeScratch& ws, const DecodeAppend& app, hipStream_t stream) {
   const int vb = c->cfg.codec == KVQ_CODEC_NF16_B256 ? 4 : c->cfg.v_bits;
   switch (vb) {
-    case 1: return launch_gv<G, 1>(c, layer, q, q_f32, sigma, out, S, ws, stream);
-    case 2: return launch_gv<G, 2>(c, layer, q, q_f32, sigma, out, S, ws, stream);
-    case 3: return launch_gv<G, 3>(c, layer, q, q_f32, sigma, out, S, ws, stream);
-    case 4: return launch_gv<G, 4>(c, layer, q, q_f32, sigma, out, S, ws, stream);
-    case 5: return launch_gv<G, 5>(c, layer, q, q_f32, sigma, out, S, ws, stream);
-    case 6: return launch_gv<G, 6>(c, layer, q, q_f32, sigma, out, S, ws, stream);
-    case 7: return launch_gv<G, 7>(c, layer, q, q_f32, sigma, out, S, ws, stream);
-    default: return launch_gv<G, 8>(c, layer, q, q_f32, sigma, out, S, ws, stream);
+    case 1: return launch_gv<G, 1>(c, layer, q, q_f32, sigma, out, S, ws, app, stream);
+    case 2: return launch_gv<G, 2>(c, layer, q, q_f32, sigma, out, S, ws, app, stream);
+    case 3: return launch_gv<G, 3>(c, layer, q, q_f32, sigma, out, S, ws, app, stream);
+    case 4: return launch_gv<G, 4>(c, layer, q, q_f32, sigma, out, S, ws, app, stream);
+    case 5: return launch_gv<G, 5>(c, layer, q, q_f32, sigma, out, S, ws, app, stream);
+    case 6: return launch_gv<G, 6>(c, layer, q, q_f32, sigma, out, S, ws, app, stream);
+    case 7: return launch_gv<G, 7>(c, layer, q, q_f32, sigma, out, S, ws, app, stream);
+    default: return launch_gv<G, 8>(c, layer, q, q_f32, sigma, out, S, ws, app, stream);
   }
 }
 

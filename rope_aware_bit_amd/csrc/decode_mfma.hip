@@ -4,13 +4,13 @@
 namespace kvq {
 
 hipError_t launch_decode_mfma_g1(kvq_cache*, int, const void*, int, float, float*, int, const DecodeScratch&,
-                                 hipStream_t);
+                                 const DecodeAppend&, hipStream_t);
 hipError_t launch_decode_mfma_g2(kvq_cache*, int, const void*, int, float, float*, int, const DecodeScratch&,
-                                 hipStream_t);
+                                 const DecodeAppend&, hipStream_t);
 hipError_t launch_decode_mfma_g4(kvq_cache*, int, const void*, int, float, float*, int, const DecodeScratch&,
-                                 hipStream_t);
+                                 const DecodeAppend&, hipStream_t);
 hipError_t launch_decode_mfma_g8(kvq_cache*, int, const void*, int, float, float*, int, const DecodeScratch&,
-                                 hipStream_t);
+                                 const DecodeAppend&, hipStream_t);
 
 int auto_splits_mfma(const kvq_cache* c, int64_t len, int n_extra) {
   // one workgroup per compute unit over (splits x KV heads x sequences), counting the n_extra
@@ -31,15 +31,16 @@ int auto_splits_mfma(const kvq_cache* c, int64_t len, int n_extra) {
 }
 
 hipError_t launch_decode_mfma(kvq_cache* c, int layer, const void* q, int dtype, float scale,
-                              float* out, int n_splits, const DecodeScratch& ws, hipStream_t stream) {
+                              float* out, int n_splits, const DecodeScratch& ws, const DecodeAppend& app,
+                              hipStream_t stream) {
   const float kLog2e = 1.4426950408889634f;
   const float sigma = (scale > 0.0f ? scale : 0.08838834764831845f) * kLog2e;
   const int q_f32 = dtype == KVQ_F32;
   switch (c->group) {
-    case 1: return launch_decode_mfma_g1(c, layer, q, q_f32, sigma, out, n_splits, ws, stream);
-    case 2: return launch_decode_mfma_g2(c, layer, q, q_f32, sigma, out, n_splits, ws, stream);
-    case 4: return launch_decode_mfma_g4(c, layer, q, q_f32, sigma, out, n_splits, ws, stream);
-    default: return launch_decode_mfma_g8(c, layer, q, q_f32, sigma, out, n_splits, ws, stream);
+    case 1: return launch_decode_mfma_g1(c, layer, q, q_f32, sigma, out, n_splits, ws, app, stream);
+    case 2: return launch_decode_mfma_g2(c, layer, q, q_f32, sigma, out, n_splits, ws, app, stream);
+    case 4: return launch_decode_mfma_g4(c, layer, q, q_f32, sigma, out, n_splits, ws, app, stream);
+    default: return launch_decode_mfma_g8(c, layer, q, q_f32, sigma, out, n_splits, ws, app, stream);
   }
 }
 

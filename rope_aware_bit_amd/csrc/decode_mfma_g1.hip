@@ -3,7 +3,8 @@
 
 namespace kvq {
 hipError_t launch_decode_mfma_g1(kvq_cache* c, int layer, const void* q, int q_f32, float sigma,
-                                 float* out, int S, const DecodeScratch& ws, hipStream_t stream) {
-  return mfma::launch_group<1>(c, layer, q, q_f32, sigma, out, S, ws, stream);
+                                 float* out, int S, const DecodeScratch& ws, const DecodeAppend& app,
+                                 hipStream_t stream) {
+  return mfma::launch_group<1>(c, layer, q, q_f32, sigma, out, S, ws, app, stream);
 }
 }  // namespace kvq

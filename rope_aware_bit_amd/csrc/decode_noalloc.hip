@@ -98,7 +98,8 @@ kvq_status kvq_decode_attn_noalloc(kvq_cache* c, int32_t layer, const void* q, i
   }
   if (e == hipSuccess) {
     const kvq::DecodeScratch ws{so, sl, smt, sep, c->dev_status, c->merge_polls};
-    e = kvq::launch_decode_mfma(c, layer, q, dtype, softmax_scale, out, S, ws, s);
+    e = kvq::launch_decode_mfma(c, layer, q, dtype, softmax_scale, out, S, ws,
+                                 kvq::DecodeAppend{nullptr, nullptr, -1}, s);
   }
   if (e != hipSuccess) {
     kvq::set_last_error(std::string("decode_attn_noalloc launch: ") + hipGetErrorString(e));

@@ -145,8 +145,18 @@ struct DecodeScratch {
   unsigned* status;
   int max_polls;
 };
+// A decode step's new position, appended by the decode launch itself: rows k and v
+// [batch][n_kv][128] in the query's precision, quantized into position pos (pos < 0: none).
+// Only for codecs without rotation, not the 256-value or asymmetric integer codecs, and no
+// recent window.
+struct DecodeAppend {
+  const void* k;
+  const void* v;
+  int64_t pos;
+};
 hipError_t launch_decode_mfma(kvq_cache* c, int layer, const void* q, int dtype, float scale,
-                              float* out, int n_splits, const DecodeScratch& ws, hipStream_t stream);
+                              float* out, int n_splits, const DecodeScratch& ws, const DecodeAppend& app,
+                              hipStream_t stream);
 hipError_t launch_fidelity(kvq_cache* c, int layer, const void* q, const void* keys, int dtype,
                            float scale, double* mae, double* kl, hipStream_t stream);
 int auto_splits_mfma(const kvq_cache* c, int64_t len, int n_extra);
@@ -160,7 +170,14 @@ struct DecodeShape {
 };
 inline DecodeShape decode_shape(const kvq_cache* c) {
   constexpr int kKS = 144, kPS = 136, kOS = 10, kLds = 163840;
-  constexpr int kStaticBase = 40960 + 4 * 16 * 40 * 2 + 128 + 64 * 4 + 16 * 24 * 4 + 64;
+  // tables, query operand, field dims, pair descriptors, pair parameters, small words
+  constexpr int kStaticBase0 = 40960 + 4 * 16 * 40 * 2 + 128 + 64 * 4 + 16 * 24 * 4 + 64;
+  // caches whose decode step may append inside the decode launch reserve that instantiation's
+  // row image (1 KB rows + 128 B key row + 128 B value codes + scales), so both launches of
+  // such a cache have the same shape
+  const bool fusable = (c->cfg.codec == KVQ_CODEC_BGTQ || c->cfg.codec == KVQ_CODEC_UNIFORM) &&
+                       c->cfg.recent_window == 0;
+  const int kStaticBase = kStaticBase0 + (fusable ? 1024 + 128 + 128 + 16 : 0);
   const int G = c->group;
   const int vb = c->cfg.codec == KVQ_CODEC_NF16_B256 ? 4 : c->cfg.v_bits;
   int kpart = (c->k_words + 1) * kKS;

@@ -27,7 +27,7 @@ EXPORTED = (
     "kvq_quantize_append", "kvq_decode_attn", "kvq_decode_attn_splits", "kvq_key_fidelity", "kvq_set_rotation", "kvq_seq_len",
     "kvq_layer_info_get", "kvq_read_cache", "kvq_codebook", "kvq_delta",
     "kvq_nf16_codebook", "kvq_status_str", "kvq_last_error", "kvq_cache_status", "kvq_cache_view",
-    "kvq_decode_attn_noalloc", "kvq_probe_stream_read",
+    "kvq_decode_attn_noalloc", "kvq_probe_stream_read", "kvq_decode_step",
 )
 
 PLAN_BYTES, PLAN_OFF_GAIN, PLAN_OFF_FIELD_DIM, PLAN_OFF_FIELD_WIDTH = 2256, 0, 1280, 1408
@@ -99,6 +99,7 @@ def _load() -> ctypes.CDLL:
         "kvq_cache_view": (I32, [P, I32, ctypes.POINTER(kvq_view)]),
         "kvq_decode_attn_noalloc": (I32, [P, I32, P, I32, F32, P, P]),
         "kvq_probe_stream_read": (I32, [P, I64, I32, P, P]),
+        "kvq_decode_step": (I32, [P, I32, P, P, P, I32, F32, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -289,6 +290,26 @@ class Cache:
             raise ValueError("out must be fp32 with q's shape")
         _check(lib.kvq_decode_attn_splits(self._h, layer, _ptr(q), _dtype_code(q), float(scale),
                                           _ptr(out), int(n_splits), _stream(stream)), "kvq_decode_attn")
+        return out
+
+    def decode_step(self, layer: int, k_new, v_new, q, out=None, scale: float = 0.0, stream=None):
+        """kvq_decode_step: append one position (k_new, v_new [batch, n_kv_heads, head_dim]) to
+        every sequence of `layer`, then attend with q over all positions (one launch where the
+        codec allows it)."""
+        import torch
+        B, H, d = self.cfg.batch, self.cfg.n_kv_heads, self.cfg.head_dim
+        for name, t in (("k_new", k_new), ("v_new", v_new)):
+            if t.dim() != 3 or tuple(t.shape) != (B, H, d) or t.dtype != q.dtype or not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous [batch, n_kv_heads, head_dim] in q's dtype, "
+                                 f"got {tuple(t.shape)} {t.dtype}")
+        if q.dim() != 3 or tuple(q.shape) != (B, self.cfg.n_q_heads, d):
+            raise ValueError(f"q must be [batch, n_q_heads, head_dim], got {tuple(q.shape)}")
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        if out.dtype != torch.float32 or tuple(out.shape) != tuple(q.shape):
+            raise ValueError("out must be fp32 with q's shape")
+        _check(lib.kvq_decode_step(self._h, layer, _ptr(k_new), _ptr(v_new), _ptr(q), _dtype_code(q),
+                                   float(scale), _ptr(out), _stream(stream)), "kvq_decode_step")
         return out
 
     def decode_attn_noalloc(self, layer: int, q, out, scale: float = 0.0, stream=None):

@@ -40,6 +40,20 @@ def test_library_tables_equal_oracle_tables():
     assert np.array_equal(bd.view(np.uint32), cbk.nf16_boundaries().view(np.uint32))
 
 
+def test_boundaries_are_fp32_midpoints_of_fp16_centroids():
+    # the decode step's in-kernel quantizer forms boundary k as 0.5 * (CB[k] + CB[k+1]) in fp32
+    # from the fp16 centroids; that is the library's boundary table bit for bit, because the sum
+    # of two neighbouring fp16 centroids is exact in fp32
+    from rope_aware_bit_amd import kvq
+    for b in range(1, 9):
+        cb, bd = kvq.codebook(b)
+        c = cb.astype(np.float32)
+        mid = np.float32(0.5) * (c[:-1] + c[1:])
+        assert np.array_equal(mid.view(np.uint32), bd[:len(mid)].view(np.uint32)), b
+        exact = (cb[:-1].astype(np.float64) + cb[1:].astype(np.float64)) / 2
+        assert np.array_equal(mid.astype(np.float64), exact), b
+
+
 def test_codebook_bad_bits():
     from rope_aware_bit_amd import kvq
     for b in (0, 9, -1):

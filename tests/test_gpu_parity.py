@@ -49,7 +49,7 @@ def _gen_batch(w, layer, T, B, noise, pairing, per_seq):
 def run_case(wname, T, k_bits, v_bits, codec="bgtq", pairing="half", batch=None, layer=0,
              chunks=None, n_splits=0, noise="gauss", temper=False, check_codes=True, sample_rows=None,
              b_min=0, b_max=8, fidelity=True, recent=0, query_weighted=False, zero_blocks=(),
-             per_seq=False, sample_seqs=None):
+             per_seq=False, sample_seqs=None, steps=0):
     """Quantize T tokens of one layer on the GPU and in the oracle; compare everything.
 
     recent > 0: the last `recent` positions stay in the fp16 window.  A position that was inside
@@ -60,7 +60,11 @@ def run_case(wname, T, k_bits, v_bits, codec="bgtq", pairing="half", batch=None,
     calibration keys (and its own query-energy weights).
 
     sample_seqs: the GPU runs the whole batch; the oracle quantizes, and the comparisons cover,
-    only these sequences (the plan is still compared in full)."""
+    only these sequences (the plan is still compared in full).
+
+    steps > 0: the last `steps` positions arrive one at a time through decode_step (append, then
+    attend), on this cache and, as append + decode_attn, on a twin cache: every step's output
+    and, at the end, every stored byte must be equal between the two."""
     torch = _torch()
     kvq = _kvq()
     w = WORKLOADS[wname]
@@ -117,8 +121,10 @@ def run_case(wname, T, k_bits, v_bits, codec="bgtq", pairing="half", batch=None,
     assert np.array_equal(bits, want_w), "plan widths differ"
     assert np.array_equal(gains.view(np.uint32), want_g.astype(np.float32).view(np.uint32)), "gains differ"
 
-    bounds = [0, T] if chunks is None else [0, *np.cumsum(chunks).tolist()]
-    assert bounds[-1] == T
+    T0 = T - steps
+    bounds = [0, T0] if chunks is None else [0, *np.cumsum(chunks).tolist()]
+    assert bounds[-1] == T0
+    bounds += list(range(T0 + 1, T + 1))
     grp = 128 if codec == "kivi" else 1                   # KIVI packs whole key tiles only
     P = wn.packed_len(T, recent, grp)                     # packed positions
     # the rows each position is stored from (fp16 copies where it went through the window)
@@ -126,8 +132,37 @@ def run_case(wname, T, k_bits, v_bits, codec="bgtq", pairing="half", batch=None,
     Ve = {b: wn.stored_rows(V[b], bounds, recent, grp) for b in seqs}
     Kt = torch.from_numpy(K).to(dev)
     Vt = torch.from_numpy(V).to(dev)
+    twin = None
+    if steps:
+        twin = kvq.Cache(cfg)
+        twin.alloc_bits(0, torch.from_numpy(np.ascontiguousarray(calib)).to(dev) if alloc else None,
+                        block_weight=torch.from_numpy(bw).to(dev) if bw is not None else None)
+        if signs is not None:
+            twin.set_rotation(0, signs)
     for a, z in zip(bounds[:-1], bounds[1:]):
+        if a >= T0:
+            break
         cache.quantize_append(0, Kt[:, a:z].contiguous(), Vt[:, a:z].contiguous())
+        if twin is not None:
+            twin.quantize_append(0, Kt[:, a:z].contiguous(), Vt[:, a:z].contiguous())
+    if steps:
+        Qd = torch.from_numpy(Q).to(dev)
+        for st in range(steps):
+            p = T0 + st
+            qs = torch.roll(Qd, st, dims=1).contiguous()   # a different query for every step
+            got_s = cache.decode_step(0, Kt[:, p].contiguous(), Vt[:, p].contiguous(), qs)
+            twin.quantize_append(0, Kt[:, p:p + 1].contiguous(), Vt[:, p:p + 1].contiguous())
+            want_s = twin.decode_attn(0, qs)
+            torch.cuda.synchronize()
+            assert torch.equal(got_s, want_s), f"decode_step output differs from append + decode at position {p}"
+        for part, dt in ((kvq.PART_K_CODES, np.uint32), (kvq.PART_V_CODES, np.uint32),
+                         (kvq.PART_K_SCALES, np.uint16), (kvq.PART_V_SCALES, np.uint16)):
+            assert np.array_equal(cache.read(0, part, dt), twin.read(0, part, dt)), f"decode_step storage differs: part {part}"
+        if recent:
+            for part in (kvq.PART_K_RECENT, kvq.PART_V_RECENT):
+                assert np.array_equal(cache.read(0, part, np.uint16), twin.read(0, part, np.uint16))
+        twin.close()
+        print(f"[{wname} T={T}] {steps} decode steps equal to append + decode", flush=True)
     assert cache.seq_len(0) == T
 
     sigma = 0.0
@@ -286,6 +321,28 @@ def test_decode_step_appends():
     run_case("llama8b_b64", 600, 4, 3, batch=3, per_seq=True, chunks=[500] + [1] * 30 + [3] * 10 + [4] * 10,
              temper=True)
     run_case("llama8b_32k", 700, 2, 2, codec="uniform", chunks=[600] + [1] * 100)
+
+
+def test_decode_step_fused_append():
+    """decode_step (the new position quantized inside the decode launch) against append +
+    decode_attn: outputs of every step and all stored bytes equal, then codes and the final
+    decode against the oracle.  Steps cross 32-position V segments and 128-position tiles; one
+    query head per KV head (fp32), 8 (two waves per SIMD), 4 with per-sequence plans, the uniform
+    codec, value widths 2 and 5 (codes straddling words), and the paths that fall back to two
+    calls (recent window, 256-value codec)."""
+    run_case("tiny", 300, 3, 3, chunks=[100, 26], steps=174)
+    run_case("qwen3b_128k", 2100, 3, 3, chunks=[2040], steps=60, temper=True)
+    run_case("llama8b_b64", 700, 4, 3, batch=3, per_seq=True, chunks=[630], steps=70, temper=True)
+    run_case("llama8b_32k", 400, 2, 2, codec="uniform", chunks=[380], steps=20)
+    run_case("llama8b_32k", 300, 3, 5, chunks=[250], steps=50, temper=True)
+    run_case("tiny", 400, 3, 3, chunks=[300], steps=100, recent=128)
+    run_case("llama8b_32k", 600, 4, 4, codec="nf16", chunks=[590], steps=10)
+
+
+def test_decode_step_fused_append_full_size():
+    """The headline layer (Qwen2.5-3B shape, K3V3) grown to 131072 positions by decode steps
+    from 131000: the fused launch at the bench's full size and split count."""
+    run_case("qwen3b_128k", 131072, 3, 3, layer=5, chunks=[2048, 128952], steps=72)
 
 
 def test_recent_window_ragged_appends():
