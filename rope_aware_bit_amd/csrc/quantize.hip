@@ -327,6 +327,173 @@ __global__ __launch_bounds__(kThreads) void quantize_append(
   }
 }
 
+// Many new positions (a prefill), for the codecs without rotation or absmax blocks, from the
+// caller's rows: the same row quantizer as quantize_append, one workgroup per 32 consecutive
+// positions (one V segment) of one (sequence, KV head).  Thread t takes key field t / 2 and
+// value dim t / 2 for the 16 positions 16 (t % 2) .. 16 (t % 2) + 15, so the field's plan entries
+// are read once.  One wave runs the 64 scale sums (32 key and 32 value rows, one lane each) while
+// the others read their rows.  The searches take one step size per step for a whole wave (the
+// widest field of the wave, or the value width): a narrower field's boundaries are followed in
+// the table by +inf, which no value exceeds, so the extra steps leave its code unchanged.  A
+// segment whose 32 positions are all new is stored with plain stores (no other position shares
+// its words); the first and last segments of a call are OR-ed in.
+constexpr int kBulkTok = 32;
+constexpr int kBulkHalf = kBulkTok / 2;
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void quantize_bulk(
+    const T* __restrict__ kin, const T* __restrict__ vin, int64_t n_new, int64_t in_stride, int64_t L0, int n_kv,
+    int64_t cap, const Plan* __restrict__ plans, int plan_bs, const Tables* __restrict__ tab,
+    uint32_t* __restrict__ kc, uint32_t* __restrict__ vc, uint16_t* __restrict__ ks,
+    uint16_t* __restrict__ vs, int k_words, int v_bits) {
+  constexpr int kVec = 16 / sizeof(T);
+  constexpr int kRowW = kHeadDim * static_cast<int>(sizeof(T)) / 4 + 1;   // odd: no bank conflicts
+  constexpr int kBd4 = (kMaxBits + 1) * 256 / 4;
+  const int tid = threadIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int64_t g0 = (L0 / kBulkTok + blockIdx.x) * kBulkTok;   // first position of the segment
+  const int lo = static_cast<int>(L0 > g0 ? L0 - g0 : 0);
+  const int hi = static_cast<int>(L0 + n_new - g0 < kBulkTok ? L0 + n_new - g0 : kBulkTok);
+  const int vb = v_bits;
+
+  __shared__ uint32_t x_s[2][kBulkTok][kRowW];   // [K, V][position] rows of T
+  auto xval = [&](int tsr, int r, int i) { return to_f(reinterpret_cast<const T*>(&x_s[tsr][r][0])[i]); };
+  __shared__ __attribute__((aligned(16))) float bd_s[(kMaxBits + 1) * 256];
+  __shared__ float ig_s[kHeadDim];
+  __shared__ uint8_t fdim_s[kHeadDim], fw_s[kHeadDim];
+  __shared__ uint16_t foff_s[kHeadDim];
+  __shared__ __attribute__((aligned(16))) uint32_t krow_s[kBulkTok * 4 * kMaxBits];
+  __shared__ uint32_t vw_s[kHeadDim][kMaxBits];  // the segment's words, per dim
+  __shared__ __attribute__((aligned(16))) float isk_s[kBulkTok];
+  __shared__ __attribute__((aligned(16))) float isv_s[kBulkTok];
+  __shared__ int nf_s;
+
+  // ---- 1. stage rows, boundaries and plan; clear the word images ----
+  for (int k = tid; k < 2 * kBulkTok * (kHeadDim / kVec); k += kThreads) {
+    const int q = k % (kHeadDim / kVec), r = (k / (kHeadDim / kVec)) % kBulkTok, tsr = k / (kHeadDim / kVec * kBulkTok);
+    if (r >= lo && r < hi) {
+      const int64_t src = ((static_cast<int64_t>(b) * in_stride + (g0 + r - L0)) * n_kv + h) * kHeadDim + q * kVec;
+      const uint4 v4 = *reinterpret_cast<const uint4*>((tsr ? vin : kin) + src);
+      uint32_t* d = &x_s[tsr][r][q * 4];
+      d[0] = v4.x;
+      d[1] = v4.y;
+      d[2] = v4.z;
+      d[3] = v4.w;
+    }
+  }
+  for (int q = tid; q < kBd4; q += kThreads)
+    reinterpret_cast<uint4*>(bd_s)[q] = reinterpret_cast<const uint4*>(&tab->bd[0][0])[q];
+  const Plan* P = plans + static_cast<int64_t>(b) * plan_bs + h;
+  if (tid < kHeadDim) {
+    ig_s[tid] = P->ig[tid];
+    fdim_s[tid] = P->fdim[tid];
+    fw_s[tid] = P->fwidth[tid];
+    foff_s[tid] = P->foff[tid];
+  }
+  for (int k = tid; k < kBulkTok * k_words; k += kThreads) krow_s[k] = 0u;
+  for (int k = tid; k < kHeadDim * kMaxBits; k += kThreads) vw_s[k / kMaxBits][k % kMaxBits] = 0u;
+  if (tid == 0) nf_s = P->n_fields;
+  __syncthreads();
+
+  // ---- 2. scales (wave 0: lane l < 32 key row l, lane 32 + l value row l, the quantizer's
+  //      order); the other waves meanwhile read their 16 key and 16 value elements ----
+  const int wv = tid >> 6;
+  const int f = tid >> 1, hf = tid & 1;   // key field f / value dim f, positions 16 hf ..
+  const int r0 = kBulkHalf * hf;
+  const int nfld = nf_s;
+  const bool kfield = f < nfld;
+  const int kdim = kfield ? fdim_s[f] : 0;
+  const int kw = kfield ? fw_s[f] : 0;
+  const float kig = ig_s[kdim];
+  float uk[kBulkHalf], uv[kBulkHalf];
+  auto gather = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < kBulkHalf; ++j) {
+      uk[j] = __fmul_rn(xval(0, r0 + j, kdim), kig);   // y = x * ig
+      uv[j] = xval(1, r0 + j, f);
+    }
+  };
+  if (wv != 0) gather();
+  if (wv == 0) {
+    const int tsr = tid / kBulkTok, r = tid % kBulkTok;
+    double ss = 0.0;
+#pragma unroll 16
+    for (int i = 0; i < kHeadDim; ++i) {
+      const double y = static_cast<double>(__fmul_rn(xval(tsr, r, i), tsr == 0 ? ig_s[i] : 1.0f));
+      ss = __dadd_rn(ss, __dmul_rn(y, y));
+    }
+    const __half s16 = __float2half_rn(static_cast<float>(__dsqrt_rn(ss / static_cast<double>(kHeadDim))));
+    (tsr == 0 ? isk_s : isv_s)[r] = inv_scale(s16);
+    if (r >= lo && r < hi) (tsr == 0 ? ks : vs)[(static_cast<int64_t>(b) * n_kv + h) * cap + g0 + r] = __half_as_ushort(s16);
+  }
+  __syncthreads();
+  if (wv == 0) gather();
+
+  // ---- 3. codes: u = y * is; count of boundaries below u by a search of S steps ----
+  uint32_t pk[kBulkHalf], pv[kBulkHalf];
+#pragma unroll
+  for (int j = 0; j < kBulkHalf; j += 4) {
+    const float4 ik = *reinterpret_cast<const float4*>(&isk_s[r0 + j]);
+    const float4 iv = *reinterpret_cast<const float4*>(&isv_s[r0 + j]);
+    uk[j] = __fmul_rn(uk[j], ik.x); uk[j + 1] = __fmul_rn(uk[j + 1], ik.y);
+    uk[j + 2] = __fmul_rn(uk[j + 2], ik.z); uk[j + 3] = __fmul_rn(uk[j + 3], ik.w);
+    uv[j] = __fmul_rn(uv[j], iv.x); uv[j + 1] = __fmul_rn(uv[j + 1], iv.y);
+    uv[j + 2] = __fmul_rn(uv[j + 2], iv.z); uv[j + 3] = __fmul_rn(uv[j + 3], iv.w);
+  }
+  auto search = [&](const float (&u)[kBulkHalf], uint32_t (&pos)[kBulkHalf], uint32_t tb, int steps) {
+#pragma unroll
+    for (int j = 0; j < kBulkHalf; ++j) pos[j] = 0u;
+    for (int st = steps - 1; st >= 0; --st) {
+      const uint32_t step = 1u << st, base = tb + step - 1u;
+#pragma unroll
+      for (int j = 0; j < kBulkHalf; ++j) {
+        const float bdv = bd_s[base + pos[j]];
+        pos[j] = bdv < u[j] ? pos[j] + step : pos[j];
+      }
+    }
+  };
+  const int ksteps = 32 * wv < nfld ? fw_s[32 * wv] : 0;   // wave-uniform: the wave's widest field
+  search(uk, pk, static_cast<uint32_t>(kw) * 256u, ksteps);
+  search(uv, pv, static_cast<uint32_t>(vb) * 256u, vb);
+  if (kfield) {
+    const int word = foff_s[f] >> 5, sh = foff_s[f] & 31;
+#pragma unroll
+    for (int j = 0; j < kBulkHalf; ++j) {
+      const int r = r0 + j;
+      if (r < lo || r >= hi) continue;
+      atomicOr(&krow_s[r * k_words + word], pk[j] << sh);
+      if (sh + kw > 32) atomicOr(&krow_s[r * k_words + word + 1], pk[j] >> (32 - sh));
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kBulkHalf; ++j) {
+    const int r = r0 + j;
+    if (r < lo || r >= hi) continue;
+    const int bit = r * vb, word = bit >> 5, sh = bit & 31;
+    atomicOr(&vw_s[f][word], pv[j] << sh);
+    if (sh + vb > 32) atomicOr(&vw_s[f][word + 1], pv[j] >> (32 - sh));
+  }
+  __syncthreads();
+
+  // ---- 4. stores ----
+  {
+    uint32_t* dst = kc + ((static_cast<int64_t>(b) * n_kv + h) * cap + g0) * k_words;
+    for (int k = tid + lo * k_words; k < hi * k_words; k += kThreads) dst[k] = krow_s[k];
+  }
+  {
+    const int gq = static_cast<int>((g0 % kVTile) / kBulkTok);
+    uint32_t* tile_dst = vc + ((static_cast<int64_t>(b) * n_kv + h) * (cap / kVTile) + g0 / kVTile) * kVTile * 4 * vb;
+    const bool whole = lo == 0 && hi == kBulkTok;
+    for (int k = tid; k < kHeadDim * vb; k += kThreads) {
+      const int i = k / vb, w = k % vb;
+      const uint32_t bits = vw_s[i][w];
+      uint32_t* d = tile_dst + static_cast<int64_t>(((i / 16) * 4 + gq) * 16 + i % 16) * vb + w;
+      if (whole) *d = bits;
+      else if (bits) atomicOr(d, bits);
+    }
+  }
+}
+
 // A few new positions (a decode step's), one workgroup per (KV head, sequence): the same row
 // quantizer as quantize_append, arranged for latency.  Every load of the call (rows, plan,
 // boundary tables) is issued in one round; the squares y_i^2 of all rows are formed in parallel
@@ -480,6 +647,22 @@ hipError_t launch_quantize(kvq_cache* c, int layer, const void* k, const void* v
                          static_cast<const float*>(v), static_cast<int>(n_new), L0, cfg.n_kv_heads, c->cap, plans,
                          plan_bs, c->tables, layer_k_codes(c, layer), layer_v_codes(c, layer),
                          layer_k_scales(c, layer), layer_v_scales(c, layer), c->k_words, cfg.v_bits);
+    return hipGetLastError();
+  }
+  if (n_new >= kBulkTok && ring_R == 0 && (cfg.codec == KVQ_CODEC_BGTQ || cfg.codec == KVQ_CODEC_UNIFORM)) {
+    const Plan* plans = c->plans + static_cast<int64_t>(layer) * c->n_plan * cfg.n_kv_heads;
+    const int plan_bs = c->n_plan > 1 ? cfg.n_kv_heads : 0;
+    const int64_t first = L0 / kBulkTok, last = (L0 + n_new - 1) / kBulkTok;
+    dim3 grid(static_cast<unsigned>(last - first + 1), static_cast<unsigned>(cfg.n_kv_heads),
+              static_cast<unsigned>(cfg.batch));
+#define KVQ_LAUNCH_BULK(T)                                                                            \
+  hipLaunchKernelGGL(quantize_bulk<T>, grid, dim3(kThreads), 0, stream, static_cast<const T*>(k),         \
+                     static_cast<const T*>(v), n_new, in_stride, L0, cfg.n_kv_heads, c->cap, plans, plan_bs, \
+                     c->tables, layer_k_codes(c, layer), layer_v_codes(c, layer), layer_k_scales(c, layer), \
+                     layer_v_scales(c, layer), c->k_words, cfg.v_bits)
+    if (dtype == KVQ_F16) KVQ_LAUNCH_BULK(__half);
+    else KVQ_LAUNCH_BULK(float);
+#undef KVQ_LAUNCH_BULK
     return hipGetLastError();
   }
   const int64_t first = L0 / kGroupTok, last = (L0 + n_new - 1) / kGroupTok;

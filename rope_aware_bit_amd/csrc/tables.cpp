@@ -159,7 +159,7 @@ void build_tables(Tables* t) {
       t->cb[b][n + k] = h;
       t->cb[b][n - 1 - k] = h | 0x8000;
     }
-    for (int k = 0; k < L; ++k) t->bd[b][k] = inf;
+    for (int k = 0; k < 256; ++k) t->bd[b][k] = inf;   // +inf after the 2^b - 1 boundaries
     t->bd[b][n - 1] = 0.0f;
     for (int k = 0; k + 1 < n; ++k) {
       float m = static_cast<float>(0.5 * (hpos[k] + hpos[k + 1]));  // exact midpoint, one rounding
