@@ -329,32 +329,38 @@ __global__ __launch_bounds__(kThreads) void quantize_append(
 
 // Many new positions (a prefill), for the codecs without rotation or absmax blocks, from the
 // caller's rows: the same row quantizer as quantize_append, one workgroup per 32 consecutive
-// positions (one V segment) of one (sequence, KV head).  Thread t takes key field t / 2 and
-// value dim t / 2 for the 16 positions 16 (t % 2) .. 16 (t % 2) + 15, so the field's plan entries
-// are read once.  One wave runs the 64 scale sums (32 key and 32 value rows, one lane each) while
-// the others read their rows.  The searches take one step size per step for a whole wave (the
-// widest field of the wave, or the value width): a narrower field's boundaries are followed in
-// the table by +inf, which no value exceeds, so the extra steps leave its code unchanged.  A
-// segment whose 32 positions are all new is stored with plain stores (no other position shares
-// its words); the first and last segments of a call are OR-ed in.
+// positions (one V segment) of one (sequence, KV head).
+//   - One wave runs the 64 scale sums (32 key and 32 value rows, one lane each, dim order).
+//   - Keys: thread t quantizes fields 16 (t / 32) .. + 15 of position t % 32, so the 32 lanes
+//     that share a field hold 32 different rows and OR into 32 different row words (the LDS row
+//     image has an odd stride: no two lanes of a field share a bank).
+//   - Values: thread t quantizes dim t / 2 at the 16 positions 16 (t % 2) .. + 15, packs their
+//     codes into words in registers and ORs a handful of words into the segment image.
+//   - The searches take one step size per step for a whole wave (the widest field of the wave,
+//     or the value width): a narrower field's boundaries are followed by +inf in the table,
+//     which no value exceeds, so the extra steps leave its code unchanged.
+//   - A segment whose 32 positions are all new is stored with plain stores (no other position
+//     shares its words); the first and last segments of a call are OR-ed in.
 constexpr int kBulkTok = 32;
 constexpr int kBulkHalf = kBulkTok / 2;
 
-template <typename T>
+template <typename T, int VB>
 __global__ __launch_bounds__(kThreads) void quantize_bulk(
     const T* __restrict__ kin, const T* __restrict__ vin, int64_t n_new, int64_t in_stride, int64_t L0, int n_kv,
     int64_t cap, const Plan* __restrict__ plans, int plan_bs, const Tables* __restrict__ tab,
     uint32_t* __restrict__ kc, uint32_t* __restrict__ vc, uint16_t* __restrict__ ks,
-    uint16_t* __restrict__ vs, int k_words, int v_bits) {
+    uint16_t* __restrict__ vs, int k_words) {
   constexpr int kVec = 16 / sizeof(T);
   constexpr int kRowW = kHeadDim * static_cast<int>(sizeof(T)) / 4 + 1;   // odd: no bank conflicts
   constexpr int kBd4 = (kMaxBits + 1) * 256 / 4;
+  constexpr int kVW = kMaxBits + 1;               // odd stride of the segment image rows
+  constexpr int kLW = (kBulkHalf * VB + 31) / 32; // words of one thread's 16 value codes
   const int tid = threadIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
   const int64_t g0 = (L0 / kBulkTok + blockIdx.x) * kBulkTok;   // first position of the segment
   const int lo = static_cast<int>(L0 > g0 ? L0 - g0 : 0);
   const int hi = static_cast<int>(L0 + n_new - g0 < kBulkTok ? L0 + n_new - g0 : kBulkTok);
-  const int vb = v_bits;
+  const int ks_stride = k_words | 1;               // odd stride of the K row image
 
   __shared__ uint32_t x_s[2][kBulkTok][kRowW];   // [K, V][position] rows of T
   auto xval = [&](int tsr, int r, int i) { return to_f(reinterpret_cast<const T*>(&x_s[tsr][r][0])[i]); };
@@ -362,8 +368,8 @@ __global__ __launch_bounds__(kThreads) void quantize_bulk(
   __shared__ float ig_s[kHeadDim];
   __shared__ uint8_t fdim_s[kHeadDim], fw_s[kHeadDim];
   __shared__ uint16_t foff_s[kHeadDim];
-  __shared__ __attribute__((aligned(16))) uint32_t krow_s[kBulkTok * 4 * kMaxBits];
-  __shared__ uint32_t vw_s[kHeadDim][kMaxBits];  // the segment's words, per dim
+  __shared__ uint32_t krow_s[kBulkTok * (4 * kMaxBits + 1)];
+  __shared__ uint32_t vw_s[kHeadDim * kVW];       // the segment's words, per dim
   __shared__ __attribute__((aligned(16))) float isk_s[kBulkTok];
   __shared__ __attribute__((aligned(16))) float isv_s[kBulkTok];
   __shared__ int nf_s;
@@ -390,27 +396,25 @@ __global__ __launch_bounds__(kThreads) void quantize_bulk(
     fw_s[tid] = P->fwidth[tid];
     foff_s[tid] = P->foff[tid];
   }
-  for (int k = tid; k < kBulkTok * k_words; k += kThreads) krow_s[k] = 0u;
-  for (int k = tid; k < kHeadDim * kMaxBits; k += kThreads) vw_s[k / kMaxBits][k % kMaxBits] = 0u;
+  for (int k = tid; k < kBulkTok * ks_stride; k += kThreads) krow_s[k] = 0u;
+  for (int k = tid; k < kHeadDim * kVW; k += kThreads) vw_s[k] = 0u;
   if (tid == 0) nf_s = P->n_fields;
   __syncthreads();
 
   // ---- 2. scales (wave 0: lane l < 32 key row l, lane 32 + l value row l, the quantizer's
-  //      order); the other waves meanwhile read their 16 key and 16 value elements ----
+  //      order); the other waves meanwhile read their elements ----
   const int wv = tid >> 6;
-  const int f = tid >> 1, hf = tid & 1;   // key field f / value dim f, positions 16 hf ..
-  const int r0 = kBulkHalf * hf;
   const int nfld = nf_s;
-  const bool kfield = f < nfld;
-  const int kdim = kfield ? fdim_s[f] : 0;
-  const int kw = kfield ? fw_s[f] : 0;
-  const float kig = ig_s[kdim];
+  const int kr_ = tid & 31, fg = tid >> 5;        // key: position kr_, fields 16 fg .. 16 fg + 15
+  const int vd = tid >> 1, r0 = kBulkHalf * (tid & 1);   // value: dim vd, positions r0 ..
   float uk[kBulkHalf], uv[kBulkHalf];
   auto gather = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < kBulkHalf; ++j) {
-      uk[j] = __fmul_rn(xval(0, r0 + j, kdim), kig);   // y = x * ig
-      uv[j] = xval(1, r0 + j, f);
+      const int f = kBulkHalf * fg + j;
+      const int d = fdim_s[f];
+      uk[j] = __fmul_rn(xval(0, kr_, d), ig_s[d]);   // y = x * ig
+      uv[j] = xval(1, r0 + j, vd);
     }
   };
   if (wv != 0) gather();
@@ -429,65 +433,97 @@ __global__ __launch_bounds__(kThreads) void quantize_bulk(
   __syncthreads();
   if (wv == 0) gather();
 
-  // ---- 3. codes: u = y * is; count of boundaries below u by a search of S steps ----
-  uint32_t pk[kBulkHalf], pv[kBulkHalf];
+  // ---- 3. codes: u = y * is; the count of boundaries below u by a search of S steps ----
+  {
+    const float isk = isk_s[kr_];
 #pragma unroll
-  for (int j = 0; j < kBulkHalf; j += 4) {
-    const float4 ik = *reinterpret_cast<const float4*>(&isk_s[r0 + j]);
-    const float4 iv = *reinterpret_cast<const float4*>(&isv_s[r0 + j]);
-    uk[j] = __fmul_rn(uk[j], ik.x); uk[j + 1] = __fmul_rn(uk[j + 1], ik.y);
-    uk[j + 2] = __fmul_rn(uk[j + 2], ik.z); uk[j + 3] = __fmul_rn(uk[j + 3], ik.w);
-    uv[j] = __fmul_rn(uv[j], iv.x); uv[j + 1] = __fmul_rn(uv[j + 1], iv.y);
-    uv[j + 2] = __fmul_rn(uv[j + 2], iv.z); uv[j + 3] = __fmul_rn(uv[j + 3], iv.w);
-  }
-  auto search = [&](const float (&u)[kBulkHalf], uint32_t (&pos)[kBulkHalf], uint32_t tb, int steps) {
+    for (int j = 0; j < kBulkHalf; ++j) uk[j] = __fmul_rn(uk[j], isk);
 #pragma unroll
-    for (int j = 0; j < kBulkHalf; ++j) pos[j] = 0u;
-    for (int st = steps - 1; st >= 0; --st) {
-      const uint32_t step = 1u << st, base = tb + step - 1u;
-#pragma unroll
-      for (int j = 0; j < kBulkHalf; ++j) {
-        const float bdv = bd_s[base + pos[j]];
-        pos[j] = bdv < u[j] ? pos[j] + step : pos[j];
-      }
-    }
-  };
-  const int ksteps = 32 * wv < nfld ? fw_s[32 * wv] : 0;   // wave-uniform: the wave's widest field
-  search(uk, pk, static_cast<uint32_t>(kw) * 256u, ksteps);
-  search(uv, pv, static_cast<uint32_t>(vb) * 256u, vb);
-  if (kfield) {
-    const int word = foff_s[f] >> 5, sh = foff_s[f] & 31;
-#pragma unroll
-    for (int j = 0; j < kBulkHalf; ++j) {
-      const int r = r0 + j;
-      if (r < lo || r >= hi) continue;
-      atomicOr(&krow_s[r * k_words + word], pk[j] << sh);
-      if (sh + kw > 32) atomicOr(&krow_s[r * k_words + word + 1], pk[j] >> (32 - sh));
+    for (int j = 0; j < kBulkHalf; j += 4) {
+      const float4 iv = *reinterpret_cast<const float4*>(&isv_s[r0 + j]);
+      uv[j] = __fmul_rn(uv[j], iv.x);
+      uv[j + 1] = __fmul_rn(uv[j + 1], iv.y);
+      uv[j + 2] = __fmul_rn(uv[j + 2], iv.z);
+      uv[j + 3] = __fmul_rn(uv[j + 3], iv.w);
     }
   }
+  uint32_t pk[kBulkHalf], pv[kBulkHalf], tbk[kBulkHalf];
 #pragma unroll
   for (int j = 0; j < kBulkHalf; ++j) {
-    const int r = r0 + j;
-    if (r < lo || r >= hi) continue;
-    const int bit = r * vb, word = bit >> 5, sh = bit & 31;
-    atomicOr(&vw_s[f][word], pv[j] << sh);
-    if (sh + vb > 32) atomicOr(&vw_s[f][word + 1], pv[j] >> (32 - sh));
+    tbk[j] = static_cast<uint32_t>(fw_s[kBulkHalf * fg + j]) * 256u;
+    pk[j] = 0u;
+    pv[j] = 0u;
+  }
+  // wave-uniform step counts: the wave's widest field (fields are widest first) and the value width
+  const int ksteps = __builtin_amdgcn_readfirstlane(32 * wv < nfld ? fw_s[32 * wv] : 0);
+  for (int st = ksteps - 1; st >= 0; --st) {
+    const uint32_t step = 1u << st;
+#pragma unroll
+    for (int j = 0; j < kBulkHalf; ++j) {
+      const float bdv = bd_s[tbk[j] + step - 1u + pk[j]];
+      pk[j] = bdv < uk[j] ? pk[j] + step : pk[j];
+    }
+  }
+#pragma unroll
+  for (int st = VB - 1; st >= 0; --st) {
+    const uint32_t step = 1u << st;
+#pragma unroll
+    for (int j = 0; j < kBulkHalf; ++j) {
+      const float bdv = bd_s[VB * 256 + step - 1u + pv[j]];
+      pv[j] = bdv < uv[j] ? pv[j] + step : pv[j];
+    }
+  }
+  // key codes into the row image (position kr_, lanes of one field on distinct rows)
+  if (kr_ >= lo && kr_ < hi) {
+#pragma unroll
+    for (int j = 0; j < kBulkHalf; ++j) {
+      const int f = kBulkHalf * fg + j;
+      if (f >= nfld) break;
+      const int off = foff_s[f], w = fw_s[f], word = off >> 5, sh = off & 31;
+      atomicOr(&krow_s[kr_ * ks_stride + word], pk[j] << sh);
+      if (sh + w > 32) atomicOr(&krow_s[kr_ * ks_stride + word + 1], pk[j] >> (32 - sh));
+    }
+  }
+  // value codes: this thread's 16 positions of dim vd as a bit string in registers, then OR-ed
+  // into the segment image at bit 16 VB (t % 2) (positions outside [lo, hi) contribute 0)
+  {
+    uint32_t lw[kLW + 1];
+#pragma unroll
+    for (int i = 0; i <= kLW; ++i) lw[i] = 0u;
+#pragma unroll
+    for (int j = 0; j < kBulkHalf; ++j) {
+      const uint32_t code = (r0 + j >= lo && r0 + j < hi) ? pv[j] : 0u;
+      const int bit = j * VB, word = bit >> 5, sh = bit & 31;
+      lw[word] |= code << sh;
+      if (sh + VB > 32) lw[word + 1] |= code >> (32 - sh);
+    }
+    const int base = r0 * VB, bw = base >> 5, bs = base & 31;
+    uint32_t* row = vw_s + vd * kVW;
+#pragma unroll
+    for (int i = 0; i < kLW; ++i) {
+      if (lw[i] == 0u) continue;
+      atomicOr(&row[bw + i], lw[i] << bs);
+      if (bs != 0 && (lw[i] >> (32 - bs)) != 0u) atomicOr(&row[bw + i + 1], lw[i] >> (32 - bs));
+    }
   }
   __syncthreads();
 
   // ---- 4. stores ----
   {
     uint32_t* dst = kc + ((static_cast<int64_t>(b) * n_kv + h) * cap + g0) * k_words;
-    for (int k = tid + lo * k_words; k < hi * k_words; k += kThreads) dst[k] = krow_s[k];
+    for (int k = tid + lo * k_words; k < hi * k_words; k += kThreads) {
+      const int r = k / k_words;
+      dst[k] = krow_s[r * ks_stride + (k - r * k_words)];
+    }
   }
   {
     const int gq = static_cast<int>((g0 % kVTile) / kBulkTok);
-    uint32_t* tile_dst = vc + ((static_cast<int64_t>(b) * n_kv + h) * (cap / kVTile) + g0 / kVTile) * kVTile * 4 * vb;
+    uint32_t* tile_dst = vc + ((static_cast<int64_t>(b) * n_kv + h) * (cap / kVTile) + g0 / kVTile) * kVTile * 4 * VB;
     const bool whole = lo == 0 && hi == kBulkTok;
-    for (int k = tid; k < kHeadDim * vb; k += kThreads) {
-      const int i = k / vb, w = k % vb;
-      const uint32_t bits = vw_s[i][w];
-      uint32_t* d = tile_dst + static_cast<int64_t>(((i / 16) * 4 + gq) * 16 + i % 16) * vb + w;
+    for (int k = tid; k < kHeadDim * VB; k += kThreads) {
+      const int i = k / VB, w = k % VB;
+      const uint32_t bits = vw_s[i * kVW + w];
+      uint32_t* d = tile_dst + static_cast<int64_t>(((i / 16) * 4 + gq) * 16 + i % 16) * VB + w;
       if (whole) *d = bits;
       else if (bits) atomicOr(d, bits);
     }
@@ -655,13 +691,28 @@ hipError_t launch_quantize(kvq_cache* c, int layer, const void* k, const void* v
     const int64_t first = L0 / kBulkTok, last = (L0 + n_new - 1) / kBulkTok;
     dim3 grid(static_cast<unsigned>(last - first + 1), static_cast<unsigned>(cfg.n_kv_heads),
               static_cast<unsigned>(cfg.batch));
-#define KVQ_LAUNCH_BULK(T)                                                                            \
-  hipLaunchKernelGGL(quantize_bulk<T>, grid, dim3(kThreads), 0, stream, static_cast<const T*>(k),         \
+#define KVQ_LAUNCH_BULK(T, VB)                                                                        \
+  hipLaunchKernelGGL((quantize_bulk<T, VB>), grid, dim3(kThreads), 0, stream, static_cast<const T*>(k),    \
                      static_cast<const T*>(v), n_new, in_stride, L0, cfg.n_kv_heads, c->cap, plans, plan_bs, \
                      c->tables, layer_k_codes(c, layer), layer_v_codes(c, layer), layer_k_scales(c, layer), \
-                     layer_v_scales(c, layer), c->k_words, cfg.v_bits)
-    if (dtype == KVQ_F16) KVQ_LAUNCH_BULK(__half);
-    else KVQ_LAUNCH_BULK(float);
+                     layer_v_scales(c, layer), c->k_words)
+#define KVQ_LAUNCH_BULK_T(T)                  \
+  switch (cfg.v_bits) {                       \
+    case 1: KVQ_LAUNCH_BULK(T, 1); break;     \
+    case 2: KVQ_LAUNCH_BULK(T, 2); break;     \
+    case 3: KVQ_LAUNCH_BULK(T, 3); break;     \
+    case 4: KVQ_LAUNCH_BULK(T, 4); break;     \
+    case 5: KVQ_LAUNCH_BULK(T, 5); break;     \
+    case 6: KVQ_LAUNCH_BULK(T, 6); break;     \
+    case 7: KVQ_LAUNCH_BULK(T, 7); break;     \
+    default: KVQ_LAUNCH_BULK(T, 8); break;    \
+  }
+    if (dtype == KVQ_F16) {
+      KVQ_LAUNCH_BULK_T(__half);
+    } else {
+      KVQ_LAUNCH_BULK_T(float);
+    }
+#undef KVQ_LAUNCH_BULK_T
 #undef KVQ_LAUNCH_BULK
     return hipGetLastError();
   }
