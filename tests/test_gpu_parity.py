@@ -514,6 +514,113 @@ def test_error_states():
     cache.close()
 
 
+def _boundary_rows(bits, rng):
+    """fp32 rows whose scale is exactly 1 (so u = x) and which hold every boundary of the width,
+    and the fp32 numbers just above and below it: ties take the lower code."""
+    from oracle import codebooks as cbk
+    from oracle import quantize as qz
+    bd = cbk.boundaries(bits)[: 2 ** bits - 1].astype(np.float32)
+    probes = np.concatenate([bd, np.nextafter(bd, np.float32(np.inf)), np.nextafter(bd, np.float32(-np.inf)),
+                             np.float32([0.0, -0.0])])
+    probes = probes[rng.permutation(len(probes))]
+    rows, i = [], 0
+    while i < len(probes):
+        row = np.zeros(128, np.float32)
+        n = 0
+        while i < len(probes) and n < 100 and float(np.sum(row[:n].astype(np.float64) ** 2) + probes[i] ** 2) < 90.0:
+            row[n] = probes[i]
+            n += 1
+            i += 1
+        energy = float(np.sum(row[:n].astype(np.float64) ** 2))
+        row[n:] = np.float32(np.sqrt((128.0 - energy) / (128 - n)))
+        row = row[rng.permutation(128)]
+        # the oracle's scale of the row must be exactly 1 (then u = x exactly)
+        s16, _ = qz.row_scale(row[None])
+        assert s16[0] == np.float16(1.0), s16
+        rows.append(row)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("kb,vb", [(2, 8), (3, 3), (8, 5), (5, 1)])
+def test_codes_on_boundaries(kb, vb):
+    """Values exactly on a boundary, and one fp32 step on either side, in rows of scale 1 (the
+    uniform codec, fp32 input): codes bit-exact against the oracle through the many-position
+    append, the few-position append and the decode step."""
+    torch = _torch()
+    kvq = _kvq()
+    rng = np.random.default_rng(11 + kb + 10 * vb)
+    Kr = _boundary_rows(kb, rng)
+    Vr = _boundary_rows(vb, rng)
+    N = max(len(Kr), len(Vr)) + 40
+    pad = lambda x: np.concatenate([x, x[rng.integers(0, len(x), N - len(x))]])   # noqa: E731
+    Kr, Vr = pad(Kr), pad(Vr)
+    dev = torch.device("cuda:0")
+    cache = kvq.Cache(kvq.Config(n_layers=1, n_kv_heads=1, n_q_heads=1, batch=1, max_tokens=N, k_bits=kb,
+                                 v_bits=vb, codec=CODEC["uniform"]))
+    cache.alloc_bits(0, None)
+    Kt = torch.from_numpy(Kr[None, :, None]).to(dev)   # [1, N, 1, 128] fp32
+    Vt = torch.from_numpy(Vr[None, :, None]).to(dev)
+    q = torch.zeros(1, 1, 128, dtype=torch.float32, device=dev)
+    n_bulk = N - 12
+    cache.quantize_append(0, Kt[:, :n_bulk].contiguous(), Vt[:, :n_bulk].contiguous())
+    for p in range(n_bulk, N - 6):
+        cache.quantize_append(0, Kt[:, p:p + 1].contiguous(), Vt[:, p:p + 1].contiguous())
+    for p in range(N - 6, N):
+        cache.decode_step(0, Kt[:, p].contiguous(), Vt[:, p].contiguous(), q)
+    torch.cuda.synchronize()
+    ol = OracleLayer(np.zeros((1, 1, 128)), kb, vb, "uniform")
+    r = ol.quantize_head(Kr.astype(np.float32), Vr.astype(np.float32), 0)
+    assert np.all(r["k_s16"].view(np.uint16) == 0x3C00) and np.all(r["v_s16"].view(np.uint16) == 0x3C00)
+    info = cache.layer_info(0)
+    kw = cache.read(0, kvq.PART_K_CODES, np.uint32).reshape(info.capacity, info.k_row_words)[:N]
+    vw = cache.read(0, kvq.PART_V_CODES, np.uint32).reshape(info.capacity // 128, 512, vb)[:(N + 127) // 128]
+    assert np.array_equal(kw, r["k_words"]), "K words differ"
+    assert np.array_equal(vw, lay.pack_v_tiles(r["v_codes"], vb)), "V tiles differ"
+    cache.close()
+
+
+def test_decode_step_error_states():
+    """kvq_decode_step validates like the two calls it stands for and appends nothing on an error:
+    no plan, a full cache, misaligned rows or output, a NaN scale, a bad layer."""
+    torch = _torch()
+    kvq = _kvq()
+    dev = torch.device("cuda:0")
+    cache = kvq.Cache(kvq.Config(1, 2, 16, 1, 130, 3, 3))
+    q = torch.randn(1, 16, 128, device=dev).half()
+    row = torch.randn(1, 2, 128, device=dev).half()
+    with pytest.raises(kvq.KvqError) as e:
+        cache.decode_step(0, row, row, q)                      # no plan yet
+    assert e.value.status == kvq.KVQ_ESTATE
+    cache.alloc_bits(0, torch.randn(64, 2, 128, device=dev).half())
+    out = cache.decode_step(0, row, row, q)                    # the first position, one launch
+    assert cache.seq_len(0) == 1 and torch.isfinite(out).all()
+    raw = torch.zeros(2 * 128 + 8, dtype=torch.float16, device=dev)
+    h = cache.handle
+    assert kvq.lib.kvq_decode_step(h, 0, raw.data_ptr() + 2, row.data_ptr(), q.data_ptr(), kvq.KVQ_F16, 0.0,
+                                   out.data_ptr(), None) == kvq.KVQ_EINVAL            # misaligned k_new
+    assert kvq.lib.kvq_decode_step(h, 0, row.data_ptr(), row.data_ptr(), q.data_ptr(), kvq.KVQ_F16, 0.0,
+                                   out.data_ptr() + 4, None) == kvq.KVQ_EINVAL        # misaligned out
+    assert kvq.lib.kvq_decode_step(h, 0, row.data_ptr(), row.data_ptr(), q.data_ptr(), kvq.KVQ_F16,
+                                   float("nan"), out.data_ptr(), None) == kvq.KVQ_EINVAL
+    assert kvq.lib.kvq_decode_step(h, 3, row.data_ptr(), row.data_ptr(), q.data_ptr(), kvq.KVQ_F16, 0.0,
+                                   out.data_ptr(), None) == kvq.KVQ_EINVAL            # bad layer
+    assert kvq.lib.kvq_decode_step(h, 0, None, row.data_ptr(), q.data_ptr(), kvq.KVQ_F16, 0.0,
+                                   out.data_ptr(), None) == kvq.KVQ_EINVAL
+    assert cache.seq_len(0) == 1                                # nothing appended by the failures
+    for _ in range(129):
+        cache.decode_step(0, row, row, q)
+    assert cache.seq_len(0) == 130
+    with pytest.raises(kvq.KvqError) as e:
+        cache.decode_step(0, row, row, q)                      # full
+    assert e.value.status == kvq.KVQ_ECAPACITY
+    assert cache.seq_len(0) == 130
+    with pytest.raises(ValueError):
+        cache.decode_step(0, row.float(), row, q)               # dtype differs from q's
+    torch.cuda.synchronize()
+    assert torch.isfinite(cache.decode_attn(0, q)).all()
+    cache.close()
+
+
 def test_codec_error_states():
     """Rotation signs: required before the first append, only +-1, only for rotating codecs,
     not after an append.  KIVI below one tile: everything in fp16, decode still works."""
