@@ -337,6 +337,13 @@ def test_decode_step_fused_append():
     run_case("llama8b_32k", 300, 3, 5, chunks=[250], steps=50, temper=True)
     run_case("tiny", 400, 3, 3, chunks=[300], steps=100, recent=128)
     run_case("llama8b_32k", 600, 4, 4, codec="nf16", chunks=[590], steps=10)
+    run_case("gqa2_8k", 700, 3, 3, chunks=[650], steps=50, temper=True)   # two query heads per KV head
+
+
+def test_decode_step_fused_append_separate_merge():
+    """32 sequences x 8 KV heads = 256 (sequence, head) units: the decode step's launch is followed by
+    the separate merge kernel."""
+    run_case("llama8b_b64", 400, 3, 3, batch=32, chunks=[380], steps=20, sample_seqs=(0, 17, 31))
 
 
 def test_decode_step_fused_append_full_size():
