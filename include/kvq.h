@@ -258,8 +258,8 @@ kvq_status kvq_decode_attn_splits(kvq_cache* cache, int32_t layer, const void* q
    kvq_decode_attn.  For the Block-GTQ and uniform codecs without a recent window this is one
    launch: the workgroup that reads the new position's tile quantizes it, stores it, and
    uses it from its own copy; other codecs and recent windows run the two calls.
-   Errors: those of the two calls (KVQ_EINVAL, KVQ_ESTATE, KVQ_ECAPACITY); on an error
-   nothing is appended. */
+   Errors: those of the two calls (KVQ_EINVAL, KVQ_ESTATE, KVQ_ECAPACITY), all checked before
+   anything is enqueued, so a rejected call appends nothing; KVQ_EHIP if a launch fails. */
 kvq_status kvq_decode_step(kvq_cache* cache, int32_t layer, const void* k_new, const void* v_new,
                            const void* q, int32_t dtype, float softmax_scale, float* out,
                            kvq_stream stream);

@@ -373,13 +373,7 @@ kvq_status kvq_decode_step(kvq_cache* c, int32_t layer, const void* k_new, const
                            int32_t dtype, float softmax_scale, float* out, kvq_stream stream) {
   if (!layer_ok(c, layer) || !k_new || !v_new || !q || !out) return KVQ_EINVAL;
   if (dtype != KVQ_F16 && dtype != KVQ_F32) return KVQ_EINVAL;
-  const kvq_config& cfg = c->cfg;
-  if (!((cfg.codec == KVQ_CODEC_BGTQ || cfg.codec == KVQ_CODEC_UNIFORM) && cfg.recent_window == 0)) {
-    // the other codecs and the recent window: the append, then the attention
-    const kvq_status st = kvq_quantize_append(c, layer, k_new, v_new, dtype, 1, stream);
-    if (st != KVQ_OK) return st;
-    return kvq_decode_attn(c, layer, q, dtype, softmax_scale, out, stream);
-  }
+  // every check of both calls comes first, so that a rejected call appends nothing
   if (reinterpret_cast<uintptr_t>(k_new) % 16 || reinterpret_cast<uintptr_t>(v_new) % 16) {
     g_last_error = "decode_step: k_new and v_new must be 16-byte aligned";
     return KVQ_EINVAL;
@@ -390,7 +384,15 @@ kvq_status kvq_decode_step(kvq_cache* c, int32_t layer, const void* k_new, const
   }
   if (!(softmax_scale == softmax_scale)) return KVQ_EINVAL;  // NaN
   if (!c->plan_ready[layer]) return KVQ_ESTATE;
+  const kvq_config& cfg = c->cfg;
+  if (kvq::codec_rotates(cfg.codec) && !c->rot_ready[layer]) return KVQ_ESTATE;
   if (c->len[layer] + 1 > cfg.max_tokens) return KVQ_ECAPACITY;
+  if (!((cfg.codec == KVQ_CODEC_BGTQ || cfg.codec == KVQ_CODEC_UNIFORM) && cfg.recent_window == 0)) {
+    // the other codecs and the recent window: the append, then the attention
+    const kvq_status st = kvq_quantize_append(c, layer, k_new, v_new, dtype, 1, stream);
+    if (st != KVQ_OK) return st;
+    return kvq_decode_attn(c, layer, q, dtype, softmax_scale, out, stream);
+  }
   const int64_t pos = c->len[layer];
   c->len[layer] = pos + 1;
   const int S = kvq::auto_splits_mfma(c, kvq::packed_len(c, layer), 0);
