@@ -6,7 +6,9 @@ heads, 16 query heads, head_dim 128, 131072 cached tokens per layer, batch 1,
 Block-GTQ K3V3 packed cache.  Synthetic RoPE'd Gaussian keys with per-block
 log-normal deviations (2 outlier blocks per head at 10x) and Gaussian values
 are drawn on the GPU; each layer is calibrated on its first 2048 tokens,
-then all tokens are appended.
+then all but the last 24 tokens are appended at once, and the last 24 by
+decode steps (kvq_decode_step: the append and the attention in one launch per
+layer), timed as `decode_step_with_append`.
 
 A step = one kvq_decode_attn call per layer (36 launches, one query each),
 inputs resident in HBM.  `value` is the step's algorithmic bytes over its time
@@ -423,16 +425,21 @@ def main():
     stream = torch.cuda.current_stream()
     timer = Timer(torch, stream)
 
-    # capacity for the T cached positions plus the new ones of the append-and-attend steps
+    # capacity for the T cached positions plus the new ones of the append-and-attend steps past T
     cache = kvq.Cache(kvq.Config(L, H, Hq, B, T + 2 * APPEND_STEPS, kb, vb))
     gen = TorchLayerGen(w, dev)
     chunk = min(w.calib_tokens, T)
     keep = None
     t_setup = time.perf_counter()
+    # every layer holds T positions: the first T - APPEND_STEPS appended at once, the last
+    # APPEND_STEPS by decode steps (below, timed), each appending one position and attending
+    n_pre = T if args.traffic_probe else T - APPEND_STEPS
+    tails = []
     for layer in range(1 if args.traffic_probe else L):
         k, v = gen.layer(layer)
         cache.alloc_bits(layer, k[:chunk])
-        cache.quantize_append(layer, k[None], v[None])
+        cache.quantize_append(layer, k[None, :n_pre].contiguous(), v[None, :n_pre].contiguous())
+        tails.append((k[n_pre:].contiguous(), v[n_pre:].contiguous()))
         torch.cuda.synchronize()
         if layer == 0:
             keep = (k.cpu().numpy(), v.cpu().numpy(), k[:chunk].cpu().numpy())
@@ -460,6 +467,21 @@ def main():
 
     bytes_launch = decode_bytes(B, H, Hq, T, kb, vb)
     bytes_step = bytes_launch * L
+
+    # the decode step as a model runs it, over the last APPEND_STEPS positions (T - 23 .. T): every
+    # layer appends the new position's K and V and attends over the cache holding it, in one launch
+    # (kvq_decode_step); 2 warm-up steps, the rest timed
+    pos = [0]
+
+    def step_fused_tail():
+        i = pos[0]
+        for layer in range(L):
+            cache.decode_step(layer, tails[layer][0][i][None], tails[layer][1][i][None], qs[layer], out=outs[layer])
+        pos[0] += 1
+
+    ms_app_tail = timer.ms(step_fused_tail, APPEND_STEPS - 2, warm=2)
+    assert pos[0] == APPEND_STEPS and cache.seq_len(0) == T
+    del tails
 
     def step():
         for layer in range(L):
@@ -564,17 +586,20 @@ def main():
                 cache.quantize_append(layer, new_kv[layer][0], new_kv[layer][1])
                 cache.decode_attn(layer, qs[layer], out=outs[layer])
 
+        # past T (T + 1 .. T + 24 positions: one more, nearly empty, tile per head than at T): the
+        # same fused step, attention alone at that length, and the two calls
         ms_app = timer.ms(step_fused, APPEND_STEPS - 2, warm=2)
-        # attention alone over the grown cache (T + 24 positions: one more, nearly empty, tile
-        # per head than the headline's T), the append's cost at equal length
         ms_same = timer.ms(step, APPEND_STEPS - 2, warm=2)
         ms_two = timer.ms(step_two_calls, APPEND_STEPS - 2, warm=2)
-        step_app = {"ms_per_step": round(ms_app, 5), "tokens_per_s": round(B / (ms_app * 1e-3), 2),
-                    "steps": APPEND_STEPS - 2, "vs_attention_only": round(ms_app / ms_step, 3),
-                    "attention_only_same_len_ms": round(ms_same, 5),
-                    "vs_attention_only_same_len": round(ms_app / ms_same, 3),
-                    "append_us_per_layer": round((ms_app - ms_same) * 1e3 / L, 2),
-                    "two_calls": {"ms_per_step": round(ms_two, 5), "vs_attention_only": round(ms_two / ms_step, 3),
+        step_app = {"positions": f"{T - APPEND_STEPS + 1}..{T}", "ms_per_step": round(ms_app_tail, 5),
+                    "tokens_per_s": round(B / (ms_app_tail * 1e-3), 2), "steps": APPEND_STEPS - 2,
+                    "vs_attention_only": round(ms_app_tail / ms_step, 3),
+                    "append_us_per_layer": round((ms_app_tail - ms_step) * 1e3 / L, 2),
+                    "past_T": {"positions": f"{T + 1}..{T + APPEND_STEPS}", "ms_per_step": round(ms_app, 5),
+                               "attention_only_same_len_ms": round(ms_same, 5),
+                               "vs_attention_only_same_len": round(ms_app / ms_same, 3)},
+                    "two_calls": {"positions": f"{T + APPEND_STEPS + 1}..{T + 2 * APPEND_STEPS}",
+                                  "ms_per_step": round(ms_two, 5), "vs_attention_only": round(ms_two / ms_step, 3),
                                   "append_us_per_layer": round((ms_two - ms_same) * 1e3 / L, 2)}}
 
     # average decode-launch duration: the timed region holds only decode launches on this stream
