@@ -477,7 +477,7 @@ __device__ __attribute__((always_inline)) inline KWin k_windows(const KPar& k, c
 // Decode kernel.  W waves per workgroup (one or two per SIMD).  Every wave owns a region of
 // `region_words` LDS words that holds, in turn, its staged K tile, its softmax weights and its
 // share of the wave merge (and, during set-up, wave 0's region holds the scaled query).
-template <int G, int VB, bool NF, int W, bool KV, bool APP>
+template <int G, int VB, bool NF, int W, bool KV, bool APP, bool LV>
 __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     const void* __restrict__ qv, int q_f32, float sigma, int64_t len, int n_packed_splits,
     const __half* __restrict__ rk, const __half* __restrict__ rv, int R, int64_t n_recent,
@@ -491,6 +491,9 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     uint32_t* app_vc, uint16_t* app_ks, uint16_t* app_vs, float* __restrict__ out) {
   constexpr int NT = 64 * W;
   constexpr bool kPipe = W == 4;                      // one wave per SIMD: prefetch and pipeline
+  // 8 waves with a static V tile area each, copied at tile start (else: the V tile shares the
+  // wave's region, copied after the key product, LV with 8 waves or 4 waves without v_early)
+  constexpr bool kStaticV = W == 8 && !LV;
   constexpr int PCOLS = 2 * G;                        // P columns: hi of heads 0..G-1, then lo
   constexpr int KWV = 4 * VB;                         // words per dim per V tile
   constexpr int QPT = (G * kHeadDim + 255) / 256;     // query values per set-up thread
@@ -525,7 +528,7 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   // [512][VB] V tile, written by global-to-LDS loads.  With 8 waves it is an LDS object of its
   // own, so the compiler need not wait for those loads before reading the K tile.
   uint32_t* vbuf;
-  if constexpr (W == 8) {
+  if constexpr (kStaticV) {
     __shared__ __attribute__((aligned(16))) uint32_t vbuf_s[W][kVTile * 4 * VB];
     vbuf = vbuf_s[wave];
   } else {
@@ -701,10 +704,10 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     const uint32_t* vt = vc + (bh * (cap / kVTile) + tile) * (kVTile * KWV);
     // 8 waves: every load of this wave has been consumed by now; saying so keeps the compiler
     // from waiting later (for loads it would believe in flight, and so for the copy)
-    if constexpr (W == 8) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    if constexpr (kStaticV) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 #pragma unroll
     for (int i = 0; i < 2 * VB; ++i) {
-      if constexpr (W == 8)
+      if constexpr (kStaticV)
         dma16(vt + 256 * i + 4 * lane, vbuf + 256 * i);
       else
         __builtin_amdgcn_global_load_lds((glb_ptr)(vt + 256 * i + 4 * lane), (lds_ptr)(vbuf + 256 * i), 16, 0, 0);
@@ -992,7 +995,7 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     wave_sync();
     // 8 waves: the V tile is copied now, when no other load of this wave is in flight, and
     // arrives during the key product
-    if constexpr (W == 8) dma_v(tile);
+    if constexpr (kStaticV) dma_v(tile);
     if constexpr (kPipe) {
       if (next < t_end) load_k(next);
     }
@@ -1077,7 +1080,7 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
       k_products(P, u, 1);
     }
     wave_sync();   // the key rows are read; the area takes the softmax weights (and V) next
-    if (W == 4 && !v_early) dma_v(tile);
+    if (!kStaticV && !v_early) dma_v(tile);
 
     // -- online softmax: lane (n, g) holds heads 2g and 2g + 1 of tokens 16 tg + n --
     float L0[8], L1[8];
@@ -1430,14 +1433,27 @@ hipError_t launch_gvw(kvq_cache* c, int layer, const void* q, int q_f32, float s
   const Plan* plans = c->plans + static_cast<int64_t>(layer) * c->n_plan * cfg.n_kv_heads;
   const int plan_bs = c->n_plan > 1 ? cfg.n_kv_heads : 0;
   const int mergers = decode_split_mergers(S_all, static_cast<int64_t>(cfg.batch) * cfg.n_kv_heads, c->n_cu);
-#define KVQ_LAUNCH_DEC(NF, KV, APP)                                                                    \
-  hipLaunchKernelGGL((decode_mfma<G, VB, NF, W, KV, APP>), grid, dim3(64 * W), dyn, stream, q, q_f32, sigma, \
+#define KVQ_LAUNCH_DEC_(NF, KV, APP, LV)                                                               \
+  hipLaunchKernelGGL((decode_mfma<G, VB, NF, W, KV, APP, LV>), grid, dim3(64 * W), dyn, stream, q, q_f32, sigma, \
                      plen, S, rk, rv, R, n_recent, rot, rot_groups, cfg.n_kv_heads, c->cap, tps, plans, plan_bs, \
                      c->tables, layer_k_codes(c, layer), layer_v_codes(c, layer), layer_k_scales(c, layer), \
                      layer_v_scales(c, layer), c->k_words, c->n_nf_blocks, S_all, mergers, sh.region_words,  \
                      sh.v_early, sh.v_off, ws.o, ws.l, ws.mt, ws.epochs, ws.status, ws.max_polls, app.k, app.v,   \
                      app.pos, layer_k_codes(c, layer), layer_v_codes(c, layer), layer_k_scales(c, layer),         \
                      layer_v_scales(c, layer), out)
+  // 8 waves: a static V tile area per wave (v_early) or the V tile in the wave's region (LV)
+#define KVQ_LAUNCH_DEC(NF, KV, APP)                                        \
+  do {                                                                     \
+    if constexpr (W == 8) {                                                \
+      if (!sh.v_early) {                                                   \
+        KVQ_LAUNCH_DEC_(NF, KV, APP, true);                                \
+      } else {                                                             \
+        if constexpr (VB <= 4) KVQ_LAUNCH_DEC_(NF, KV, APP, false);        \
+      }                                                                    \
+    } else {                                                               \
+      KVQ_LAUNCH_DEC_(NF, KV, APP, false);                                 \
+    }                                                                      \
+  } while (0)
   bool launched = false;
   if constexpr (VB == 4) {
     if (cfg.codec == KVQ_CODEC_NF16_B256) {
@@ -1455,6 +1471,7 @@ hipError_t launch_gvw(kvq_cache* c, int layer, const void* q, int q_f32, float s
   if (!launched && app.pos >= 0) KVQ_LAUNCH_DEC(false, false, true);
   else if (!launched) KVQ_LAUNCH_DEC(false, false, false);
 #undef KVQ_LAUNCH_DEC
+#undef KVQ_LAUNCH_DEC_
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S_all <= 1 || mergers > 0) return e;
   // no room for in-kernel mergers: merge in a kernel of its own
@@ -1468,9 +1485,7 @@ template <int G, int VB>
 hipError_t launch_gv(kvq_cache* c, int layer, const void* q, int q_f32, float sigma, float* out,
                      int S, const DecodeScratch& ws, const DecodeAppend& app, hipStream_t stream) {
   const DecodeShape sh = decode_shape(c);
-  if constexpr (VB <= 4) {   // wider V tiles never leave room for 8 waves
-    if (sh.waves == 8) return launch_gvw<G, VB, 8>(c, layer, q, q_f32, sigma, out, S, sh, ws, app, stream);
-  }
+  if (sh.waves == 8) return launch_gvw<G, VB, 8>(c, layer, q, q_f32, sigma, out, S, sh, ws, app, stream);
   if (sh.waves != 4) return hipErrorInvalidConfiguration;
   return launch_gvw<G, VB, 4>(c, layer, q, q_f32, sigma, out, S, sh, ws, app, stream);
 }

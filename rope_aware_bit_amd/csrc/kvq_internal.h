@@ -164,7 +164,7 @@ int auto_splits_mfma(const kvq_cache* c, int64_t len, int n_extra);
 // Launch shape of the decode kernel for a cache: waves per workgroup (8 = two per SIMD, or 4),
 // whether each wave's V tile has an LDS area of its own (copied at tile start; a static array
 // with 8 waves) or reuses the K area after the key product, the dynamic LDS words of each
-// wave's region and the V area's offset in it (4 waves).
+// wave's region and the V area's offset in it.
 struct DecodeShape {
   int waves, v_early, region_words, v_off;
 };
@@ -189,9 +189,16 @@ inline DecodeShape decode_shape(const kvq_cache* c) {
   const int vwords = 512 * vb;
   // asymmetric integer codec: 1 KB of tile parameters per wave
   const int kvx = c->cfg.codec == KVQ_CODEC_KIVI ? 1024 : 0;
-  {
+  if (vb <= 4) {   // 8 waves, each with a static V tile area copied at tile start
     const int stat = kStaticBase + 16 * 8 * G + 64 * G + 4 * 8 * vwords + 8 * kvx;
     if (stat + 4 * 8 * kpart <= kLds) return {8, 1, kpart, 0};
+  }
+  {   // 8 waves, each V tile copied into its wave's region (after the softmax weights) once the
+      // key product is done
+    int late = ((G * kPS + 3) & ~3) + vwords;
+    if (late < kpart) late = kpart;
+    const int stat = kStaticBase + 16 * 8 * G + 64 * G + 8 * kvx;
+    if (stat + 4 * 8 * late <= kLds) return {8, 0, late, (G * kPS + 3) & ~3};
   }
   const int stat = kStaticBase + 16 * 4 * G + 64 * G + 4 * kvx;
   if (stat + 4 * 4 * (kpart + vwords) <= kLds) return {4, 1, kpart + vwords, kpart};
