@@ -1429,7 +1429,12 @@ hipError_t launch_gvw(kvq_cache* c, int layer, const void* q, int q_f32, float s
   const int8_t* rot = codec_rotates(cfg.codec) ? c->rot_signs + static_cast<int64_t>(layer) * cfg.n_kv_heads * kHeadDim : nullptr;
   const int rot_groups = cfg.codec == KVQ_CODEC_BGTQ_ROT ? 1 : 0;
   dim3 grid(S_all, cfg.n_kv_heads, cfg.batch);
-  const size_t dyn = static_cast<size_t>(W) * sh.region_words * sizeof(uint32_t);
+  // 8 waves: the V tile in the wave's region when no wave has more than one tile (the static V
+  // areas only pay when a wave's next tile can be copied during its key product)
+  const bool lv = W == 8 && sh.lv_region > 0 && (!sh.v_early || tps <= W);
+  const int region_words = lv ? sh.lv_region : sh.region_words;
+  const int v_early = lv ? 0 : sh.v_early, v_off = lv ? sh.lv_off : sh.v_off;
+  const size_t dyn = static_cast<size_t>(W) * region_words * sizeof(uint32_t);
   const Plan* plans = c->plans + static_cast<int64_t>(layer) * c->n_plan * cfg.n_kv_heads;
   const int plan_bs = c->n_plan > 1 ? cfg.n_kv_heads : 0;
   const int mergers = decode_split_mergers(S_all, static_cast<int64_t>(cfg.batch) * cfg.n_kv_heads, c->n_cu);
@@ -1437,15 +1442,15 @@ hipError_t launch_gvw(kvq_cache* c, int layer, const void* q, int q_f32, float s
   hipLaunchKernelGGL((decode_mfma<G, VB, NF, W, KV, APP, LV>), grid, dim3(64 * W), dyn, stream, q, q_f32, sigma, \
                      plen, S, rk, rv, R, n_recent, rot, rot_groups, cfg.n_kv_heads, c->cap, tps, plans, plan_bs, \
                      c->tables, layer_k_codes(c, layer), layer_v_codes(c, layer), layer_k_scales(c, layer), \
-                     layer_v_scales(c, layer), c->k_words, c->n_nf_blocks, S_all, mergers, sh.region_words,  \
-                     sh.v_early, sh.v_off, ws.o, ws.l, ws.mt, ws.epochs, ws.status, ws.max_polls, app.k, app.v,   \
+                     layer_v_scales(c, layer), c->k_words, c->n_nf_blocks, S_all, mergers, region_words,     \
+                     v_early, v_off, ws.o, ws.l, ws.mt, ws.epochs, ws.status, ws.max_polls, app.k, app.v,        \
                      app.pos, layer_k_codes(c, layer), layer_v_codes(c, layer), layer_k_scales(c, layer),         \
                      layer_v_scales(c, layer), out)
   // 8 waves: a static V tile area per wave (v_early) or the V tile in the wave's region (LV)
 #define KVQ_LAUNCH_DEC(NF, KV, APP)                                        \
   do {                                                                     \
     if constexpr (W == 8) {                                                \
-      if (!sh.v_early) {                                                   \
+      if (lv) {                                                            \
         KVQ_LAUNCH_DEC_(NF, KV, APP, true);                                \
       } else {                                                             \
         if constexpr (VB <= 4) KVQ_LAUNCH_DEC_(NF, KV, APP, false);        \

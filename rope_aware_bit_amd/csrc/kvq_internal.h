@@ -167,6 +167,11 @@ int auto_splits_mfma(const kvq_cache* c, int64_t len, int n_extra);
 // wave's region and the V area's offset in it.
 struct DecodeShape {
   int waves, v_early, region_words, v_off;
+  // 8 waves: the region and V offset when each V tile is copied into the wave's region after the
+  // key product (0 when that does not fit).  Launches of at most one tile per wave use it; the
+  // static V areas (v_early) serve launches of several tiles per wave, whose copies then overlap
+  // the key products
+  int lv_region, lv_off;
 };
 inline DecodeShape decode_shape(const kvq_cache* c) {
   constexpr int kKS = 144, kPS = 136, kOS = 10, kLds = 163840;
@@ -189,22 +194,20 @@ inline DecodeShape decode_shape(const kvq_cache* c) {
   const int vwords = 512 * vb;
   // asymmetric integer codec: 1 KB of tile parameters per wave
   const int kvx = c->cfg.codec == KVQ_CODEC_KIVI ? 1024 : 0;
-  if (vb <= 4) {   // 8 waves, each with a static V tile area copied at tile start
-    const int stat = kStaticBase + 16 * 8 * G + 64 * G + 4 * 8 * vwords + 8 * kvx;
-    if (stat + 4 * 8 * kpart <= kLds) return {8, 1, kpart, 0};
-  }
-  {   // 8 waves, each V tile copied into its wave's region (after the softmax weights) once the
-      // key product is done
-    int late = ((G * kPS + 3) & ~3) + vwords;
-    if (late < kpart) late = kpart;
-    const int stat = kStaticBase + 16 * 8 * G + 64 * G + 8 * kvx;
-    if (stat + 4 * 8 * late <= kLds) return {8, 0, late, (G * kPS + 3) & ~3};
-  }
-  const int stat = kStaticBase + 16 * 4 * G + 64 * G + 4 * kvx;
-  if (stat + 4 * 4 * (kpart + vwords) <= kLds) return {4, 1, kpart + vwords, kpart};
+  // 8 waves, each V tile copied into its wave's region (after the softmax weights) once the key
+  // product is done
   int late = ((G * kPS + 3) & ~3) + vwords;
   if (late < kpart) late = kpart;
-  return {4, 0, late, (G * kPS + 3) & ~3};
+  const bool lv_ok = kStaticBase + 16 * 8 * G + 64 * G + 8 * kvx + 4 * 8 * late <= kLds;
+  const int lv_region = lv_ok ? late : 0, lv_off = (G * kPS + 3) & ~3;
+  if (vb <= 4) {   // 8 waves, each with a static V tile area copied at tile start
+    const int stat = kStaticBase + 16 * 8 * G + 64 * G + 4 * 8 * vwords + 8 * kvx;
+    if (stat + 4 * 8 * kpart <= kLds) return {8, 1, kpart, 0, lv_region, lv_off};
+  }
+  if (lv_ok) return {8, 0, late, lv_off, lv_region, lv_off};
+  const int stat = kStaticBase + 16 * 4 * G + 64 * G + 4 * kvx;
+  if (stat + 4 * 4 * (kpart + vwords) <= kLds) return {4, 1, kpart + vwords, kpart, 0, 0};
+  return {4, 0, late, lv_off, 0, 0};
 }
 inline int decode_waves(const kvq_cache* c) { return decode_shape(c).waves; }
 
