@@ -57,13 +57,20 @@ __global__ __launch_bounds__(256) void energy_chunks(const T* __restrict__ keys,
   double acc = 0.0;
   for (int64_t s0 = c * kEnergyChunk; s0 < (c + 1) * kEnergyChunk && s0 < n_tok; s0 += kEnergyTok) {
     const int64_t ns = n_tok - s0 < kEnergyTok ? n_tok - s0 : kEnergyTok;
-    // stage: thread t copies 16-byte pieces t, t + 256, ... of the stage's rows
-    for (int k = tid; k < kEnergyTok * kHeadDim / kVec; k += 256) {
-      const int r = k / (kHeadDim / kVec), q = k % (kHeadDim / kVec);
-      if (r < ns) {
-        const uint4 v = *reinterpret_cast<const uint4*>(keys + ((s0 + r) * n_kv + h) * kHeadDim + q * kVec);
-        *reinterpret_cast<uint4*>(&x_s[r][q * kVec]) = v;
-      }
+    // stage: thread t copies 16-byte pieces t, t + 256, ... of the stage's rows, all loads
+    // issued before the first store (rows past the stage's end repeat its last row, unused)
+    constexpr int kIt = kEnergyTok * kHeadDim / kVec / 256;
+    uint4 v[kIt];
+#pragma unroll
+    for (int i = 0; i < kIt; ++i) {
+      const int k = tid + 256 * i, r = k / (kHeadDim / kVec), q = k % (kHeadDim / kVec);
+      const int64_t rc = r < ns ? r : ns - 1;
+      v[i] = *reinterpret_cast<const uint4*>(keys + ((s0 + rc) * n_kv + h) * kHeadDim + q * kVec);
+    }
+#pragma unroll
+    for (int i = 0; i < kIt; ++i) {
+      const int k = tid + 256 * i, r = k / (kHeadDim / kVec), q = k % (kHeadDim / kVec);
+      *reinterpret_cast<uint4*>(&x_s[r][q * kVec]) = v[i];
     }
     __syncthreads();
     if (j < kBlocks) {

@@ -240,16 +240,40 @@ __global__ __launch_bounds__(256, 2) void fidelity_partials(
   }
   for (int64_t r0 = t_begin; r0 < t_end; r0 += kFidTok) {
     const int nr = t_end - r0 < kFidTok ? static_cast<int>(t_end - r0) : kFidTok;
-    // stage the given keys (16-byte pieces), the packed rows and the scales
-    for (int k = tid; k < nr * (kHeadDim / kVec); k += 256) {
-      const int r = k / (kHeadDim / kVec), c = k % (kHeadDim / kVec);
-      const int64_t src = ((static_cast<int64_t>(b) * len + r0 + r) * n_kv + h) * kHeadDim + c * kVec;
-      *reinterpret_cast<uint4*>(&x_s[r][c * kVec]) = *reinterpret_cast<const uint4*>(keys + src);
+    // stage the given keys (16-byte pieces), the packed rows and the scales: the loads of the
+    // keys and rows are all issued first (indices clamped to the round; the packed words of
+    // window positions are zero, within capacity, and never read), then the scales, then the
+    // stores, so the round waits for memory once
+    constexpr int kXIt = kFidTok * (kHeadDim / kVec) / 256;
+    constexpr int kKIt = kFidTok * 4 * kMaxBits / 256;
+    uint4 xv[kXIt];
+    uint32_t kw[kKIt];
+#pragma unroll
+    for (int i = 0; i < kXIt; ++i) {
+      const int k = tid + 256 * i, r = k / (kHeadDim / kVec), c = k % (kHeadDim / kVec);
+      const int rc = r < nr ? r : nr - 1;
+      xv[i] = *reinterpret_cast<const uint4*>(keys + ((static_cast<int64_t>(b) * len + r0 + rc) * n_kv + h) * kHeadDim + c * kVec);
+    }
+    const int nkw = nr * k_words;
+#pragma unroll
+    for (int i = 0; i < kKIt; ++i) {
+      const int k = tid + 256 * i;
+      kw[i] = kc[(bh * cap + r0) * k_words + (k < nkw ? k : nkw - 1)];
+    }
+    if (!kivi && tid < nr && r0 + tid < plen) {
+      const uint16_t sb = nf ? ks[(static_cast<int64_t>(b) * cap + r0 + tid) * n_nf + h / 2] : ks[bh * cap + r0 + tid];
+      sc_s[tid] = static_cast<double>(__half2float(__ushort_as_half(sb)));
+    }
+#pragma unroll
+    for (int i = 0; i < kXIt; ++i) {
+      const int k = tid + 256 * i, r = k / (kHeadDim / kVec), c = k % (kHeadDim / kVec);
+      *reinterpret_cast<uint4*>(&x_s[r][c * kVec]) = xv[i];
     }
     // stored rows: packed below plen, fp16 ring copies (slot p mod R) from plen on
-    for (int k = tid; k < nr * k_words; k += 256) {
-      const int r = k / k_words, c = k % k_words;
-      if (r0 + r < plen) kr_s[r][c] = kc[(bh * cap + r0 + r) * k_words + c];
+#pragma unroll
+    for (int i = 0; i < kKIt; ++i) {
+      const int k = tid + 256 * i, kk = k < nkw ? k : nkw - 1;
+      kr_s[kk / k_words][kk % k_words] = kw[i];
     }
     for (int k = tid; k < nr * (kHeadDim / 8); k += 256) {
       const int r = k / (kHeadDim / 8), c = k % (kHeadDim / 8);
@@ -266,10 +290,6 @@ __global__ __launch_bounds__(256, 2) void fidelity_partials(
       const uint16_t* kp = ks + ((bh * (cap / kVTile) + r0 / kVTile) * kBlocks + j) * 4;
       ksc_s[tid] = __ushort_as_half(kp[co]);
       klo_s[tid] = __ushort_as_half(kp[2 + co]);
-    }
-    if (!kivi && tid < nr && r0 + tid < plen) {
-      const uint16_t sb = nf ? ks[(static_cast<int64_t>(b) * cap + r0 + tid) * n_nf + h / 2] : ks[bh * cap + r0 + tid];
-      sc_s[tid] = static_cast<double>(__half2float(__ushort_as_half(sb)));
     }
     if (tid < kFidTok) kr_s[tid][k_words] = 0u;   // zero word after the row (fields read two words)
     __syncthreads();

@@ -82,22 +82,32 @@ __global__ __launch_bounds__(kT) void kivi_quantize(
   const Plan* P = plans + static_cast<int64_t>(b) * plan_bs + h;
   if (tid < kHeadDim) fdim_s[tid] = P->fdim[tid];
 
-  // position r of the tile: ring slot (already appended) or input row
+  // position r of the tile: ring slot (already appended) or input row.  Thread t takes
+  // channel t % 128 of rows t / 128 + 2 i, sixteen rows at a time with all sixteen loads
+  // issued before the first store
   auto load_tile = [&](const T* in, const __half* rg, bool values) {
+    constexpr int kU = 16;
     const int d = tid & (kHeadDim - 1);
-    for (int r = tid >> 7; r < kVTile; r += 2) {
-      const int64_t p = pos0 + r;
-      float x;
-      if (p < len_old) {
-        const int64_t slot = p % ring;
-        const int64_t off = values
-            ? (((bh * (ring / kVTile) + slot / kVTile) * kHeadDim + d) * kVTile + slot % kVTile)
-            : (((static_cast<int64_t>(b) * ring + slot) * n_kv + h) * kHeadDim + d);
-        x = __half2float(rg[off]);
-      } else {
-        x = as_f(in[((static_cast<int64_t>(b) * in_stride + (p - len_old)) * n_kv + h) * kHeadDim + d]);
+    for (int r0 = tid >> 7; r0 < kVTile; r0 += 2 * kU) {
+      // (raw loads first, conversions after, so no conversion waits between the loads)
+      __half hv[kU];
+      T tv[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int64_t p = pos0 + r0 + 2 * u;
+        if (p < len_old) {
+          const int64_t slot = p % ring;
+          const int64_t off = values
+              ? (((bh * (ring / kVTile) + slot / kVTile) * kHeadDim + d) * kVTile + slot % kVTile)
+              : (((static_cast<int64_t>(b) * ring + slot) * n_kv + h) * kHeadDim + d);
+          hv[u] = rg[off];
+        } else {
+          tv[u] = in[((static_cast<int64_t>(b) * in_stride + (p - len_old)) * n_kv + h) * kHeadDim + d];
+        }
       }
-      x_s[r][d] = x;
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+        x_s[r0 + 2 * u][d] = pos0 + r0 + 2 * u < len_old ? __half2float(hv[u]) : as_f(tv[u]);
     }
   };
 

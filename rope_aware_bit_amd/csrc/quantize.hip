@@ -72,7 +72,7 @@ __global__ __launch_bounds__(kThreads) void quantize_append(
   auto xval = [&](int tsr, int hh, int r, int i) {
     return to_f(reinterpret_cast<const T*>(&x_s[tsr][hh][r][0])[i]);
   };
-  __shared__ float bd_s[(kMaxBits + 1) * 256];
+  __shared__ __attribute__((aligned(16))) float bd_s[(kMaxBits + 1) * 256];
   __shared__ float ig_s[kHeadDim];
   __shared__ uint8_t fdim_s[kHeadDim], fw_s[kHeadDim];
   __shared__ uint16_t foff_s[kHeadDim];
@@ -81,63 +81,107 @@ __global__ __launch_bounds__(kThreads) void quantize_append(
   __shared__ float isk_s[kGroupTok], isv_s[kGroupTok];
   __shared__ int nf_s;
 
-  // ---- 1. stage rows, tables and plan; clear the word images ----
+  // ---- 1. every load of the workgroup first (rows, tables, plan: one round of memory
+  //      latency; nothing loaded is used before all are issued), then the LDS images.  Rows
+  //      outside [lo, hi) read the nearest row inside (their images are never used). ----
   const int h0 = NF ? (h & ~1) : h;   // first head of the staged block
-  for (int k = tid; k < 2 * kHeads * kGroupTok * (kHeadDim / kVec); k += kThreads) {
-    const int q = k % (kHeadDim / kVec);
-    const int r = (k / (kHeadDim / kVec)) % kGroupTok;
-    const int hh = (k / (kHeadDim / kVec * kGroupTok)) % kHeads;
-    const int tsr = k / (kHeadDim / kVec * kGroupTok * kHeads);   // 0: K, 1: V
-    if (r >= lo && r < hi) {
-      uint4 v4;
-      if (ring_R == 0) {
-        const int64_t src = ((static_cast<int64_t>(b) * in_stride + (g0 + r - L0)) * n_kv + h0 + hh) * kHeadDim + q * kVec;
-        v4 = *reinterpret_cast<const uint4*>((tsr ? vin : kin) + src);
-      } else {
-        // recent-window rings (fp16): keys [batch][R][n_kv][128], values in dim-major 128-slot
-        // tiles [batch][n_kv][R / 128][128][128]; position p sits in slot p mod R
-        const int64_t slot = (g0 + r) % ring_R;
-        if (tsr == 0) {
-          v4 = *reinterpret_cast<const uint4*>(kin + ((static_cast<int64_t>(b) * ring_R + slot) * n_kv + h0 + hh) * kHeadDim + q * kVec);
-        } else {
-          const T* vt = vin + (((static_cast<int64_t>(b) * n_kv + h0 + hh) * (ring_R / 128) + slot / 128) * kHeadDim + q * kVec) * 128 + slot % 128;
-          T e8[kVec];
+  constexpr int kPieces = kHeadDim / kVec;                                 // 16-byte pieces per row
+  constexpr int kRowIt = 2 * kHeads * kGroupTok * kPieces / kThreads;      // pieces per thread
+  constexpr int kBd4 = (kMaxBits + 1) * 256 / 4;
+  constexpr int kBdIt = (kBd4 + kThreads - 1) / kThreads;
+  uint4 xr[kRowIt];
 #pragma unroll
-          for (int e = 0; e < kVec; ++e) e8[e] = vt[e * 128];
-          __builtin_memcpy(&v4, e8, 16);
-        }
+  for (int it = 0; it < kRowIt; ++it) {
+    const int k = tid + kThreads * it;
+    const int q = k % kPieces;
+    const int r = (k / kPieces) % kGroupTok;
+    const int hh = (k / (kPieces * kGroupTok)) % kHeads;
+    const int tsr = k / (kPieces * kGroupTok * kHeads);   // 0: K, 1: V
+    const int rc = r < lo ? lo : r >= hi ? hi - 1 : r;
+    if (ring_R == 0) {
+      const int64_t src = ((static_cast<int64_t>(b) * in_stride + (g0 + rc - L0)) * n_kv + h0 + hh) * kHeadDim + q * kVec;
+      xr[it] = *reinterpret_cast<const uint4*>((tsr ? vin : kin) + src);
+    } else {
+      // recent-window rings (fp16): keys [batch][R][n_kv][128], values in dim-major 128-slot
+      // tiles [batch][n_kv][R / 128][128][128]; position p sits in slot p mod R
+      const int64_t slot = (g0 + rc) % ring_R;
+      if (tsr == 0) {
+        xr[it] = *reinterpret_cast<const uint4*>(kin + ((static_cast<int64_t>(b) * ring_R + slot) * n_kv + h0 + hh) * kHeadDim + q * kVec);
+      } else {
+        const T* vt = vin + (((static_cast<int64_t>(b) * n_kv + h0 + hh) * (ring_R / 128) + slot / 128) * kHeadDim + q * kVec) * 128 + slot % 128;
+        T e8[kVec];
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) e8[e] = vt[e * 128];
+        __builtin_memcpy(&xr[it], e8, 16);
       }
-      uint32_t* d = &x_s[tsr][hh][r][q * 4];
-      d[0] = v4.x;
-      d[1] = v4.y;
-      d[2] = v4.z;
-      d[3] = v4.w;
+    }
+  }
+  uint4 bdr[NF ? 1 : kBdIt];
+  float nfb = 0.0f;
+  if constexpr (NF) {
+    nfb = tab->nf_bd[tid & 15];
+  } else {
+#pragma unroll
+    for (int j = 0; j < kBdIt; ++j) {
+      const int q = tid + kThreads * j;
+      bdr[j] = reinterpret_cast<const uint4*>(&tab->bd[0][0])[q < kBd4 ? q : kBd4 - 1];
     }
   }
   const Plan* P = plans + static_cast<int64_t>(b) * plan_bs + h;   // plan of (sequence, head)
-  for (int k = tid; k < (kMaxBits + 1) * 256; k += kThreads) {
-    const int bb = k >> 8, e = k & 255;
-    bd_s[k] = NF ? (bb == 4 && e < 16 ? tab->nf_bd[e] : INFINITY) : tab->bd[bb][e];
+  const int pi = tid & (kHeadDim - 1);
+  const float igv = P->ig[pi];
+  const uint32_t fdv = P->fdim[pi], fwv = P->fwidth[pi], fov = P->foff[pi];
+  uint32_t cstv = 0u, cszv = 0u;
+  if constexpr (RM == 2) {
+    cstv = P->cstart[pi];
+    cszv = P->csize[pi];
   }
-  if (tid < kHeadDim) {
-    ig_s[tid] = P->ig[tid];
-    fdim_s[tid] = P->fdim[tid];
-    fw_s[tid] = P->fwidth[tid];
-    foff_s[tid] = P->foff[tid];
-    vw_s[tid][0] = vw_s[tid][1] = vw_s[tid][2] = vw_s[tid][3] = 0u;
+  const int nfv = P->n_fields;
+#pragma unroll
+  for (int it = 0; it < kRowIt; ++it) {
+    const int k = tid + kThreads * it;
+    const int q = k % kPieces;
+    const int r = (k / kPieces) % kGroupTok;
+    const int hh = (k / (kPieces * kGroupTok)) % kHeads;
+    const int tsr = k / (kPieces * kGroupTok * kHeads);
+    uint32_t* d = &x_s[tsr][hh][r][q * 4];
+    d[0] = xr[it].x;
+    d[1] = xr[it].y;
+    d[2] = xr[it].z;
+    d[3] = xr[it].w;
   }
+  // (the table stores are unconditional: threads past it rewrite its last piece with the same
+  // value, so the compiler has no reason to move their loads down to a conditional store)
+  if constexpr (NF) {
+#pragma unroll
+    for (int j = 0; j < (kMaxBits + 1); ++j) {
+      const int k = tid + kThreads * j, bb = k >> 8, e = k & 255;
+      bd_s[k] = bb == 4 && e < 16 ? nfb : INFINITY;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kBdIt; ++j) {
+      const int q = tid + kThreads * j;
+      reinterpret_cast<uint4*>(bd_s)[q < kBd4 ? q : kBd4 - 1] = bdr[j];
+    }
+  }
+  // (the plan's entries are written by both halves of the workgroup, with the same values, so
+  // that their loads are not moved down to a conditional store either)
+  ig_s[pi] = igv;
+  fdim_s[pi] = static_cast<uint8_t>(fdv);
+  fw_s[pi] = static_cast<uint8_t>(fwv);
+  foff_s[pi] = static_cast<uint16_t>(fov);
+  if (tid < kHeadDim) vw_s[tid][0] = vw_s[tid][1] = vw_s[tid][2] = vw_s[tid][3] = 0u;
   // rotation inside equal-width groups: field f's chunk, and each dim's chunk size (0: the
   // dim's block is not stored)
   __shared__ uint8_t cst_s[RM == 2 ? kHeadDim : 1], csz_s[RM == 2 ? kHeadDim : 1], dsz_s[RM == 2 ? kHeadDim : 1];
   if constexpr (RM == 2) {
-    if (tid < kHeadDim) {
-      cst_s[tid] = P->cstart[tid];
-      csz_s[tid] = P->csize[tid];
-      dsz_s[tid] = 0;
-    }
+    cst_s[pi] = static_cast<uint8_t>(cstv);
+    csz_s[pi] = static_cast<uint8_t>(cszv);
+    if (tid < kHeadDim) dsz_s[tid] = 0;
   }
   for (int k = tid; k < kGroupTok * k_words; k += kThreads) krow_s[k] = 0u;
-  if (tid == 0) nf_s = P->n_fields;
+  if (tid == 0) nf_s = nfv;
   __syncthreads();
 
   // ---- 1b. rotated keys (randomized Hadamard): y = fp32(H (s * x) / sqrt(128)), the fast
@@ -374,31 +418,57 @@ __global__ __launch_bounds__(kThreads) void quantize_bulk(
   __shared__ __attribute__((aligned(16))) float isv_s[kBulkTok];
   __shared__ int nf_s;
 
-  // ---- 1. stage rows, boundaries and plan; clear the word images ----
-  for (int k = tid; k < 2 * kBulkTok * (kHeadDim / kVec); k += kThreads) {
-    const int q = k % (kHeadDim / kVec), r = (k / (kHeadDim / kVec)) % kBulkTok, tsr = k / (kHeadDim / kVec * kBulkTok);
-    if (r >= lo && r < hi) {
-      const int64_t src = ((static_cast<int64_t>(b) * in_stride + (g0 + r - L0)) * n_kv + h) * kHeadDim + q * kVec;
-      const uint4 v4 = *reinterpret_cast<const uint4*>((tsr ? vin : kin) + src);
-      uint32_t* d = &x_s[tsr][r][q * 4];
-      d[0] = v4.x;
-      d[1] = v4.y;
-      d[2] = v4.z;
-      d[3] = v4.w;
-    }
+  // ---- 1. every load of the workgroup first (rows, boundaries, plan: one round of memory
+  //      latency; nothing loaded is used before all are issued), then the LDS images.  Rows
+  //      outside [lo, hi) read the nearest row inside (their images are never used). ----
+  constexpr int kPieces = kHeadDim / kVec;                     // 16-byte pieces per row
+  constexpr int kRowIt = 2 * kBulkTok * kPieces / kThreads;    // pieces per thread
+  constexpr int kBdIt = (kBd4 + kThreads - 1) / kThreads;
+  uint4 xr[kRowIt], bdr[kBdIt];
+#pragma unroll
+  for (int i = 0; i < kRowIt; ++i) {
+    const int k = tid + kThreads * i;
+    const int q = k % kPieces, r = (k / kPieces) % kBulkTok, tsr = k / (kPieces * kBulkTok);
+    const int rc = r < lo ? lo : r >= hi ? hi - 1 : r;
+    const int64_t src = ((static_cast<int64_t>(b) * in_stride + (g0 + rc - L0)) * n_kv + h) * kHeadDim + q * kVec;
+    xr[i] = *reinterpret_cast<const uint4*>((tsr ? vin : kin) + src);
   }
-  for (int q = tid; q < kBd4; q += kThreads)
-    reinterpret_cast<uint4*>(bd_s)[q] = reinterpret_cast<const uint4*>(&tab->bd[0][0])[q];
+#pragma unroll
+  for (int j = 0; j < kBdIt; ++j) {
+    const int q = tid + kThreads * j;
+    bdr[j] = reinterpret_cast<const uint4*>(&tab->bd[0][0])[q < kBd4 ? q : kBd4 - 1];
+  }
   const Plan* P = plans + static_cast<int64_t>(b) * plan_bs + h;
-  if (tid < kHeadDim) {
-    ig_s[tid] = P->ig[tid];
-    fdim_s[tid] = P->fdim[tid];
-    fw_s[tid] = P->fwidth[tid];
-    foff_s[tid] = P->foff[tid];
-  }
+  const int pi = tid & (kHeadDim - 1);
+  const float igv = P->ig[pi];
+  const uint32_t fdv = P->fdim[pi], fwv = P->fwidth[pi], fov = P->foff[pi];
+  const int nfv = P->n_fields;
   for (int k = tid; k < kBulkTok * ks_stride; k += kThreads) krow_s[k] = 0u;
   for (int k = tid; k < kHeadDim * kVW; k += kThreads) vw_s[k] = 0u;
-  if (tid == 0) nf_s = P->n_fields;
+#pragma unroll
+  for (int i = 0; i < kRowIt; ++i) {
+    const int k = tid + kThreads * i;
+    const int q = k % kPieces, r = (k / kPieces) % kBulkTok, tsr = k / (kPieces * kBulkTok);
+    uint32_t* d = &x_s[tsr][r][q * 4];
+    d[0] = xr[i].x;
+    d[1] = xr[i].y;
+    d[2] = xr[i].z;
+    d[3] = xr[i].w;
+  }
+  // (unconditional: threads past the table rewrite its last piece with the same value, so the
+  // compiler has no reason to move their loads down to a conditional store)
+#pragma unroll
+  for (int j = 0; j < kBdIt; ++j) {
+    const int q = tid + kThreads * j;
+    reinterpret_cast<uint4*>(bd_s)[q < kBd4 ? q : kBd4 - 1] = bdr[j];
+  }
+  if (tid < kHeadDim) {
+    ig_s[tid] = igv;
+    fdim_s[tid] = static_cast<uint8_t>(fdv);
+    fw_s[tid] = static_cast<uint8_t>(fwv);
+    foff_s[tid] = static_cast<uint16_t>(fov);
+  }
+  if (tid == 0) nf_s = nfv;
   __syncthreads();
 
   // ---- 2. scales (wave 0: lane l < 32 key row l, lane 32 + l value row l, the quantizer's
@@ -447,31 +517,41 @@ __global__ __launch_bounds__(kThreads) void quantize_bulk(
       uv[j + 3] = __fmul_rn(uv[j + 3], iv.w);
     }
   }
-  uint32_t pk[kBulkHalf], pv[kBulkHalf], tbk[kBulkHalf];
+  // search state as byte addresses into the boundary table: row w (1 KB) plus 4 x code, so that
+  // with the steps unrolled each probe is one LDS read at a constant offset from it
+  const char* bdb = reinterpret_cast<const char*>(bd_s);
+  uint32_t pk[kBulkHalf], pv[kBulkHalf];
 #pragma unroll
   for (int j = 0; j < kBulkHalf; ++j) {
-    tbk[j] = static_cast<uint32_t>(fw_s[kBulkHalf * fg + j]) * 256u;
-    pk[j] = 0u;
-    pv[j] = 0u;
+    pk[j] = static_cast<uint32_t>(fw_s[kBulkHalf * fg + j]) * 1024u;
+    pv[j] = static_cast<uint32_t>(VB) * 1024u;
   }
   // wave-uniform step counts: the wave's widest field (fields are widest first) and the value width
   const int ksteps = __builtin_amdgcn_readfirstlane(32 * wv < nfld ? fw_s[32 * wv] : 0);
-  for (int st = ksteps - 1; st >= 0; --st) {
-    const uint32_t step = 1u << st;
+#pragma unroll
+  for (int st = kMaxBits - 1; st >= 0; --st) {
+    if (st >= ksteps) continue;
+    constexpr uint32_t one = 1u;
+    const uint32_t step4 = (one << st) * 4u;
 #pragma unroll
     for (int j = 0; j < kBulkHalf; ++j) {
-      const float bdv = bd_s[tbk[j] + step - 1u + pk[j]];
-      pk[j] = bdv < uk[j] ? pk[j] + step : pk[j];
+      const float bdv = *reinterpret_cast<const float*>(bdb + pk[j] + (step4 - 4u));
+      pk[j] = bdv < uk[j] ? pk[j] + step4 : pk[j];
     }
   }
 #pragma unroll
   for (int st = VB - 1; st >= 0; --st) {
-    const uint32_t step = 1u << st;
+    const uint32_t step4 = (1u << st) * 4u;
 #pragma unroll
     for (int j = 0; j < kBulkHalf; ++j) {
-      const float bdv = bd_s[VB * 256 + step - 1u + pv[j]];
-      pv[j] = bdv < uv[j] ? pv[j] + step : pv[j];
+      const float bdv = *reinterpret_cast<const float*>(bdb + pv[j] + (step4 - 4u));
+      pv[j] = bdv < uv[j] ? pv[j] + step4 : pv[j];
     }
+  }
+#pragma unroll
+  for (int j = 0; j < kBulkHalf; ++j) {   // back to codes
+    pk[j] = (pk[j] >> 2) & 255u;
+    pv[j] = (pv[j] >> 2) & 255u;
   }
   // key codes into the row image (position kr_, lanes of one field on distinct rows)
   if (kr_ >= lo && kr_ < hi) {
