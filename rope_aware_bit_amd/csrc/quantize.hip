@@ -490,11 +490,20 @@ __global__ __launch_bounds__(kThreads) void quantize_bulk(
   if (wv != 0) gather();
   if (wv == 0) {
     const int tsr = tid / kBulkTok, r = tid % kBulkTok;
+    const float gsel = tsr == 0 ? 1.0f : 0.0f;   // (keys: times ig_i; values: times 1)
     double ss = 0.0;
-#pragma unroll 16
-    for (int i = 0; i < kHeadDim; ++i) {
-      const double y = static_cast<double>(__fmul_rn(xval(tsr, r, i), tsr == 0 ? ig_s[i] : 1.0f));
-      ss = __dadd_rn(ss, __dmul_rn(y, y));
+    // sixteen squares at a time (exact in fp64, independent), then their sum in dim order: only
+    // the additions form the dependent chain
+    for (int i0 = 0; i0 < kHeadDim; i0 += 16) {
+      double sq[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const float gi = gsel != 0.0f ? ig_s[i0 + u] : 1.0f;
+        const double y = static_cast<double>(__fmul_rn(xval(tsr, r, i0 + u), gi));
+        sq[u] = __dmul_rn(y, y);
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) ss = __dadd_rn(ss, sq[u]);
     }
     const __half s16 = __float2half_rn(static_cast<float>(__dsqrt_rn(ss / static_cast<double>(kHeadDim))));
     (tsr == 0 ? isk_s : isv_s)[r] = inv_scale(s16);
