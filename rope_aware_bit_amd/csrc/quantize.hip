@@ -409,7 +409,9 @@ __global__ __launch_bounds__(kThreads) void quantize_bulk(
   __shared__ uint32_t x_s[2][kBulkTok][kRowW];   // [K, V][position] rows of T
   auto xval = [&](int tsr, int r, int i) { return to_f(reinterpret_cast<const T*>(&x_s[tsr][r][0])[i]); };
   __shared__ __attribute__((aligned(16))) float bd_s[(kMaxBits + 1) * 256];
-  __shared__ float ig_s[kHeadDim];
+  // gains of the key rows (ig) and of the value rows (1), indexed by tensor
+  __shared__ __attribute__((aligned(16))) float g2_s[2][kHeadDim];
+  float* ig_s = g2_s[0];
   __shared__ uint8_t fdim_s[kHeadDim], fw_s[kHeadDim];
   __shared__ uint16_t foff_s[kHeadDim];
   __shared__ uint32_t krow_s[kBulkTok * (4 * kMaxBits + 1)];
@@ -463,7 +465,8 @@ __global__ __launch_bounds__(kThreads) void quantize_bulk(
     reinterpret_cast<uint4*>(bd_s)[q < kBd4 ? q : kBd4 - 1] = bdr[j];
   }
   if (tid < kHeadDim) {
-    ig_s[tid] = igv;
+    g2_s[0][tid] = igv;
+    g2_s[1][tid] = 1.0f;
     fdim_s[tid] = static_cast<uint8_t>(fdv);
     fw_s[tid] = static_cast<uint8_t>(fwv);
     foff_s[tid] = static_cast<uint16_t>(fov);
@@ -490,17 +493,32 @@ __global__ __launch_bounds__(kThreads) void quantize_bulk(
   if (wv != 0) gather();
   if (wv == 0) {
     const int tsr = tid / kBulkTok, r = tid % kBulkTok;
-    const float gsel = tsr == 0 ? 1.0f : 0.0f;   // (keys: times ig_i; values: times 1)
+    const float* gp = g2_s[tsr];   // keys: y = x * ig_i; values: y = x * 1
     double ss = 0.0;
     // sixteen squares at a time (exact in fp64, independent), then their sum in dim order: only
     // the additions form the dependent chain
     for (int i0 = 0; i0 < kHeadDim; i0 += 16) {
       double sq[16];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const float gi = gsel != 0.0f ? ig_s[i0 + u] : 1.0f;
-        const double y = static_cast<double>(__fmul_rn(xval(tsr, r, i0 + u), gi));
-        sq[u] = __dmul_rn(y, y);
+      for (int u = 0; u < 16; u += 4) {
+        const float4 g4 = *reinterpret_cast<const float4*>(gp + i0 + u);
+        const float gv[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+        for (int e = 0; e < 4; e += 2) {
+          float x0, x1;
+          if constexpr (sizeof(T) == 2) {   // one 32-bit word holds the fp16 pair i, i + 1
+            const uint32_t w = x_s[tsr][r][(i0 + u + e) >> 1];
+            x0 = __half2float(__ushort_as_half(static_cast<uint16_t>(w & 0xFFFFu)));
+            x1 = __half2float(__ushort_as_half(static_cast<uint16_t>(w >> 16)));
+          } else {
+            x0 = __uint_as_float(x_s[tsr][r][i0 + u + e]);
+            x1 = __uint_as_float(x_s[tsr][r][i0 + u + e + 1]);
+          }
+          const double y0 = static_cast<double>(__fmul_rn(x0, gv[e]));
+          const double y1 = static_cast<double>(__fmul_rn(x1, gv[e + 1]));
+          sq[u + e] = __dmul_rn(y0, y0);
+          sq[u + e + 1] = __dmul_rn(y1, y1);
+        }
       }
 #pragma unroll
       for (int u = 0; u < 16; ++u) ss = __dadd_rn(ss, sq[u]);
