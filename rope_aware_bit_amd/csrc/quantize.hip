@@ -495,10 +495,10 @@ __global__ __launch_bounds__(kThreads) void quantize_bulk(
     const int tsr = tid / kBulkTok, r = tid % kBulkTok;
     const float* gp = g2_s[tsr];   // keys: y = x * ig_i; values: y = x * 1
     double ss = 0.0;
-    // sixteen squares at a time (exact in fp64, independent), then their sum in dim order: only
-    // the additions form the dependent chain
+    // the sum in dim order; each square y_i^2 is exact in fp64 (a product of two fp32 values), so
+    // one fused multiply-add ss + y_i * y_i rounds exactly as the addition of the square does
     for (int i0 = 0; i0 < kHeadDim; i0 += 16) {
-      double sq[16];
+      double yd[16];
 #pragma unroll
       for (int u = 0; u < 16; u += 4) {
         const float4 g4 = *reinterpret_cast<const float4*>(gp + i0 + u);
@@ -514,14 +514,12 @@ __global__ __launch_bounds__(kThreads) void quantize_bulk(
             x0 = __uint_as_float(x_s[tsr][r][i0 + u + e]);
             x1 = __uint_as_float(x_s[tsr][r][i0 + u + e + 1]);
           }
-          const double y0 = static_cast<double>(__fmul_rn(x0, gv[e]));
-          const double y1 = static_cast<double>(__fmul_rn(x1, gv[e + 1]));
-          sq[u + e] = __dmul_rn(y0, y0);
-          sq[u + e + 1] = __dmul_rn(y1, y1);
+          yd[u + e] = static_cast<double>(__fmul_rn(x0, gv[e]));
+          yd[u + e + 1] = static_cast<double>(__fmul_rn(x1, gv[e + 1]));
         }
       }
 #pragma unroll
-      for (int u = 0; u < 16; ++u) ss = __dadd_rn(ss, sq[u]);
+      for (int u = 0; u < 16; ++u) ss = __fma_rn(yd[u], yd[u], ss);
     }
     const __half s16 = __float2half_rn(static_cast<float>(__dsqrt_rn(ss / static_cast<double>(kHeadDim))));
     (tsr == 0 ? isk_s : isv_s)[r] = inv_scale(s16);
