@@ -608,45 +608,43 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     }
   }
 
-  // ---- fused append of one new position app_pos (a decode step): rows [batch][n_kv][128] in
-  //      q's precision.  The workgroup whose tiles hold app_pos quantizes that position with the
-  //      row quantizer of the append (codes and scales identical to it), stores it in HBM and
-  //      puts the same codes and scales into its own copy of the tile, so nothing waits for the
-  //      stores.  Four waves aw0 .. aw0 + 3 do it (with 8 waves the younger four, idle during
-  //      the set-up): waves aw0 and aw0 + 1 form the key and value rows and their scales, then
-  //      each of the 256 threads quantizes one key field or value dim. ----
+  // The sequence's last tile is taken by wave 0 of its split, the oldest wave, which finishes its
+  // tiles first (slot s of a split is tiles t_begin + s, + W, ...; wave w takes slot
+  // (w + last - t_begin) mod W there, slot w elsewhere).
+  const int64_t last_tile = n_tiles - 1;
+  const int wslot = __builtin_amdgcn_readfirstlane(
+      !recent_wg && t_begin <= last_tile && last_tile < t_end
+          ? static_cast<int>((static_cast<int64_t>(wave) + last_tile - t_begin) & (W - 1))
+          : wave);
+
+  // ---- fused append of one new position app_pos (a decode step; it is the sequence's last
+  //      position): rows [batch][n_kv][128] in q's precision.  The workgroup whose tiles hold
+  //      app_pos quantizes that position with the row quantizer of the append (codes and scales
+  //      identical to it), stores it in HBM and puts the same codes and scales into its own copy
+  //      of the tile, so nothing waits for the stores.  Wave 0, which holds that tile, does all of
+  //      it after the set-up, so no other wave waits for it; its rows are loaded with the set-up. ----
   const int64_t app_tile = app_pos >= 0 ? app_pos / kVTile : -1;
   const bool app_wg = APP && !NF && !KV && app_pos >= 0 && !recent_wg && t_begin <= app_tile && app_tile < t_end;
   // (in the tile loop: the tile to patch, -1 for none, and the position's index in it)
   const int app_t32 = app_wg ? static_cast<int>(app_tile) : -1;
   const int app_tau = static_cast<int>(app_pos & (kVTile - 1));
-  constexpr int aw0 = W - 4;
-  const int awave = __builtin_amdgcn_readfirstlane(wave) - aw0;   // 0 .. 3 on the append waves
-  const bool app_wave = app_wg && awave >= 0;
-  const int at = tid - 64 * aw0;
-  float ax0 = 0.0f, ax1 = 0.0f, ag0 = 1.0f, ag1 = 1.0f;
-  uint32_t a_fw = 0u, a_fo = 0u, a_fd = 0u;
-  int a_nf = 0;
-  if (app_wave) {
-    if (awave < 2) {
-      const int64_t e = bh * kHeadDim + lane;
-      const void* src = awave ? app_v : app_k;
-      if (q_f32) {
-        ax0 = static_cast<const float*>(src)[e];
-        ax1 = static_cast<const float*>(src)[e + 64];
-      } else {
-        ax0 = __half2float(static_cast<const __half*>(src)[e]);
-        ax1 = __half2float(static_cast<const __half*>(src)[e + 64]);
-      }
-      if (awave == 0) {
-        ag0 = P->ig[lane];
-        ag1 = P->ig[lane + 64];
-      }
+  const bool app_w0 = app_wg && __builtin_amdgcn_readfirstlane(wave) == 0;
+  float ax0 = 0.0f, ax1 = 0.0f, bx0 = 0.0f, bx1 = 0.0f, ag0 = 1.0f, ag1 = 1.0f;
+  if (app_w0) {   // key and value dims lane and lane + 64, and their inverse gains
+    const int64_t e = bh * kHeadDim + lane;
+    if (q_f32) {
+      ax0 = static_cast<const float*>(app_k)[e];
+      ax1 = static_cast<const float*>(app_k)[e + 64];
+      bx0 = static_cast<const float*>(app_v)[e];
+      bx1 = static_cast<const float*>(app_v)[e + 64];
+    } else {
+      ax0 = __half2float(static_cast<const __half*>(app_k)[e]);
+      ax1 = __half2float(static_cast<const __half*>(app_k)[e + 64]);
+      bx0 = __half2float(static_cast<const __half*>(app_v)[e]);
+      bx1 = __half2float(static_cast<const __half*>(app_v)[e + 64]);
     }
-    a_fw = P->fwidth[at & 127];
-    a_fo = P->foff[at & 127];
-    a_fd = P->fdim[at & 127];
-    a_nf = P->n_fields;
+    ag0 = P->ig[lane];
+    ag1 = P->ig[lane + 64];
   }
 
   // K rows of tokens lane and lane + 64 (first 16 words), scales of tokens 16 tg + n, V segments
@@ -716,7 +714,7 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   // the first tile's K rows and scales are loaded unconditionally (a wave without a tile of
   // its own reads the split's last tile and discards it); its V tile is copied once the
   // set-up data has been used, so waiting for the set-up loads never waits for it
-  const int64_t t0 = t_begin + wave < t_end ? t_begin + wave : (t_end > 0 ? t_end - 1 : 0);
+  const int64_t t0 = t_begin + wslot < t_end ? t_begin + wslot : (t_end > 0 ? t_end - 1 : 0);
   // with 8 waves, the older four (one per SIMD) ask for their tiles first; the younger four
   // ask once the set-up has landed
   const bool late_tile = W == 8 && !setup_wave;
@@ -782,26 +780,6 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     if (w78) {
       *reinterpret_cast<uint32_t*>(tab_s + kSing8Base + 4 * tid) = cb8;
       if (tid < 128) *reinterpret_cast<uint32_t*>(tab_s + kSing7Base + 4 * tid) = cb7;
-    }
-  }
-  if (app_wave && awave < 2) {
-    // key row y = x * ig_i (fp32), value row x; scale = fp16(fp32(sqrt(sum y_i^2 / 128))) with
-    // the fp64 sum taken in dim order, inverse scale fp32(1 / scale) (0 for a zero scale)
-    app_y[awave][lane] = awave ? ax0 : __fmul_rn(ax0, ag0);
-    app_y[awave][lane + 64] = awave ? ax1 : __fmul_rn(ax1, ag1);
-    if (awave == 0 && lane < 32) app_kw[lane] = 0u;
-    wave_sync();
-    if (lane == 0) {
-      double ss = 0.0;
-#pragma unroll 16
-      for (int i = 0; i < kHeadDim; ++i) {
-        const double y = static_cast<double>(app_y[awave][i]);
-        ss = __dadd_rn(ss, __dmul_rn(y, y));
-      }
-      const __half s16 = __float2half_rn(static_cast<float>(__dsqrt_rn(ss / static_cast<double>(kHeadDim))));
-      const float sf = __half2float(s16);
-      app_s16[awave] = __half_as_ushort(s16);
-      app_is[awave] = sf == 0.0f ? 0.0f : __fdiv_rn(1.0f, sf);
     }
   }
   lds_barrier();
@@ -884,50 +862,90 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
       a_s[c][2 * hh + 1][k] = static_cast<_Float16>(qq - static_cast<float>(hi));
     }
   }
-  if (app_wave) {
-    // codes: thread at < 128 key field at, thread at >= 128 value dim at - 128; u = y * is, and
-    // the code is the number of boundaries below u, the boundary between centroids k and k + 1
-    // being their midpoint (exact in fp32 for fp16 centroids)
-    const bool key = at < 128;
-    const int w = key ? static_cast<int>(a_fw) : VB;
-    if (!key || at < a_nf) {
-      const float u = __fmul_rn(key ? app_y[0][a_fd] : app_y[1][at - 128], app_is[key ? 0 : 1]);
-      const _Float16* cbw = reinterpret_cast<const _Float16*>(tab_s + kImageBase + single_table_base(w));
+  const uint32_t lb = (lane & 31u) << 2;   // this lane's replica offset
+  lds_barrier();
+  const uint64_t uses_wide = wide_s;       // pairs (plan ranks) with blocks of 6..8 bits
+  // wave 0 of the appending workgroup: the new position's key row y = x * ig_i (fp32) and value
+  // row x into LDS; lanes 0 and 1 take the key and the value scale, fp16(fp32(sqrt(sum y_i^2 /
+  // 128))) with the fp64 sum in dim order (y_i^2 is exact in fp64, so each fused multiply-add
+  // rounds as the addition of the square), and the inverse scale fp32(1 / scale) (0 for a zero
+  // scale); then lane l codes key fields l, l + 64 and value dims l, l + 64: u = y * is, and the
+  // code is the number of boundaries below u, the boundary between centroids k and k + 1 being
+  // their midpoint (exact in fp32 for fp16 centroids).  Field f is coordinate f % 2 of plan pair
+  // f / 2 (offset | width << 16): at the pair's offset, plus its width for the second.
+  auto app_quantize = [&]() __attribute__((always_inline)) {
+    app_y[0][lane] = __fmul_rn(ax0, ag0);
+    app_y[0][lane + 64] = __fmul_rn(ax1, ag1);
+    app_y[1][lane] = bx0;
+    app_y[1][lane + 64] = bx1;
+    if (lane < 32) app_kw[lane] = 0u;
+    wave_sync();
+    if (lane < 2) {
+      const float* yr = app_y[lane];
+      double ss = 0.0;
+#pragma unroll 16
+      for (int i = 0; i < kHeadDim; ++i) {
+        const double y = static_cast<double>(yr[i]);
+        ss = __fma_rn(y, y, ss);
+      }
+      const __half s16 = __float2half_rn(static_cast<float>(__dsqrt_rn(ss / static_cast<double>(kHeadDim))));
+      const float sf = __half2float(s16);
+      app_s16[lane] = __half_as_ushort(s16);
+      app_is[lane] = sf == 0.0f ? 0.0f : __fdiv_rn(1.0f, sf);
+    }
+    wave_sync();
+    const int nfs = __builtin_amdgcn_readfirstlane(nf_r);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool key = e < 2;
+      const int idx = lane + 64 * (e & 1);
+      if (key && idx >= nfs) continue;
+      uint32_t w = VB, off = 0u;
+      int dim = idx;
+      if (key) {
+        const uint32_t pd = pd_s[idx >> 1];
+        w = pd >> 16;
+        off = (pd & 0xFFFFu) + (idx & 1 ? w : 0u);
+        dim = fdim_s[idx];
+      }
+      const float u = __fmul_rn(app_y[key ? 0 : 1][dim], app_is[key ? 0 : 1]);
+      const _Float16* cbw = reinterpret_cast<const _Float16*>(tab_s + kImageBase + single_table_base(static_cast<int>(w)));
       uint32_t code = 0u;
-      for (int sh = w - 1; sh >= 0; --sh) {
+      for (int sh = static_cast<int>(w) - 1; sh >= 0; --sh) {
         const uint32_t step = 1u << sh, k = code + step - 1u;
         const float bk = __fmul_rn(0.5f, __fadd_rn(static_cast<float>(cbw[k]), static_cast<float>(cbw[k + 1])));
         code += bk < u ? step : 0u;
       }
       if (key) {
-        const uint32_t wd = a_fo >> 5, sb = a_fo & 31u;
+        const uint32_t wd = off >> 5, sb = off & 31u;
         atomicOr(&app_kw[wd], code << sb);
         if (sb + w > 32u) atomicOr(&app_kw[wd + 1], code >> (32u - sb));
       } else {
-        app_vcode[at - 128] = static_cast<uint8_t>(code);
+        app_vcode[idx] = static_cast<uint8_t>(code);
       }
     }
-  }
-  const uint32_t lb = (lane & 31u) << 2;   // this lane's replica offset
-  lds_barrier();
-  const uint64_t uses_wide = wide_s;       // pairs (plan ranks) with blocks of 6..8 bits
-  // the new position into HBM: its key row whole, its value codes OR-ed into their segment words
-  // (the position's bits are still zero there), its scales.  Issued by each append wave once it
-  // has waited for its own tile's loads (after the value tile copy), so that no wait of the tile
-  // loop also waits for these stores.
+    wave_sync();
+  };
+  if (app_w0) app_quantize();
+  // the new position into HBM (wave 0, once its tile's value copy has landed, so that no wait of
+  // the tile loop also waits for these stores): its key row whole, its value codes OR-ed into
+  // their segment words (the position's bits are still zero there), its scales
   auto app_store = [&]() __attribute__((always_inline)) {
-    if (!app_wave) return;
-    if (at < k_words) app_kc[(bh * cap + app_pos) * k_words + at] = app_kw[at];
-    const uint32_t a_vcode = at >= 128 ? static_cast<uint32_t>(app_vcode[at - 128]) : 0u;
-    if (a_vcode != 0u) {
-      const int j = at - 128, gq = app_tau >> 5;
-      const uint32_t bit = static_cast<uint32_t>(app_tau & 31) * VB, wd = bit >> 5, sb = bit & 31u;
-      uint32_t* seg = app_vc + (bh * (cap / kVTile) + app_t32) * (kVTile * KWV) +
-                      ((((j >> 4) << 2) + gq) * 16 + (j & 15)) * VB;
-      atomicOr(seg + wd, a_vcode << sb);
-      if (sb + VB > 32u && (a_vcode >> (32u - sb))) atomicOr(seg + wd + 1, a_vcode >> (32u - sb));
+    if (lane < k_words) app_kc[(bh * cap + app_pos) * k_words + lane] = app_kw[lane];
+    const int gq = app_tau >> 5;
+    const uint32_t bit = static_cast<uint32_t>(app_tau & 31) * VB, wd = bit >> 5, sb = bit & 31u;
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int j = lane + 64 * jj;
+      const uint32_t a_vcode = app_vcode[j];
+      if (a_vcode != 0u) {
+        uint32_t* seg = app_vc + (bh * (cap / kVTile) + app_t32) * (kVTile * KWV) +
+                        ((((j >> 4) << 2) + gq) * 16 + (j & 15)) * VB;
+        atomicOr(seg + wd, a_vcode << sb);
+        if (sb + VB > 32u && (a_vcode >> (32u - sb))) atomicOr(seg + wd + 1, a_vcode >> (32u - sb));
+      }
     }
-    if (at == 0) {
+    if (lane == 0) {
       app_ks[bh * cap + app_pos] = static_cast<uint16_t>(app_s16[0]);
       app_vs[bh * cap + app_pos] = static_cast<uint16_t>(app_s16[1]);
     }
@@ -1156,9 +1174,7 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
       }
       wave_sync();
     }
-    if constexpr (APP) {
-      if (first) app_store();
-    }
+    if (APP && static_cast<int>(tile) == app_t32) app_store();
     uint32_t vseg[8][VB + 2];
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
@@ -1203,11 +1219,9 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
       if (v_early && next < t_end) dma_v(next);
     }
   };
-  if (t_begin + wave < t_end) {
-    tile_body(t_begin + wave, true);
-    for (int64_t tile = t_begin + wave + W; tile < t_end; tile += W) tile_body(tile, false);
-  } else if constexpr (APP) {
-    app_store();
+  if (t_begin + wslot < t_end) {
+    tile_body(t_begin + wslot, true);
+    for (int64_t tile = t_begin + wslot + W; tile < t_end; tile += W) tile_body(tile, false);
   }
   if (recent_wg) {
     // ---- recent window: fp16 keys [R][n_kv][128] and values in dim-major 128-slot tiles, no
