@@ -397,7 +397,7 @@ __global__ __launch_bounds__(kThreads) void quantize_bulk(
   constexpr int kVec = 16 / sizeof(T);
   constexpr int kRowW = kHeadDim * static_cast<int>(sizeof(T)) / 4 + 1;   // odd: no bank conflicts
   constexpr int kBd4 = (kMaxBits + 1) * 256 / 4;
-  constexpr int kVW = kMaxBits + 1;               // odd stride of the segment image rows
+  constexpr int kVW = VB | 1;                     // odd stride of the segment image rows (>= VB words)
   constexpr int kLW = (kBulkHalf * VB + 31) / 32; // words of one thread's 16 value codes
   const int tid = threadIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
@@ -414,7 +414,9 @@ __global__ __launch_bounds__(kThreads) void quantize_bulk(
   float* ig_s = g2_s[0];
   __shared__ uint8_t fdim_s[kHeadDim], fw_s[kHeadDim];
   __shared__ uint16_t foff_s[kHeadDim];
-  __shared__ uint32_t krow_s[kBulkTok * (4 * kMaxBits + 1)];
+  // the K row image, 32 rows of k_words | 1 words, in dynamic LDS sized by the launch (so that
+  // narrow rows leave room for a fifth workgroup per compute unit)
+  extern __shared__ uint32_t krow_s[];
   __shared__ uint32_t vw_s[kHeadDim * kVW];       // the segment's words, per dim
   __shared__ __attribute__((aligned(16))) float isk_s[kBulkTok];
   __shared__ __attribute__((aligned(16))) float isv_s[kBulkTok];
@@ -796,8 +798,9 @@ hipError_t launch_quantize(kvq_cache* c, int layer, const void* k, const void* v
     const int64_t first = L0 / kBulkTok, last = (L0 + n_new - 1) / kBulkTok;
     dim3 grid(static_cast<unsigned>(last - first + 1), static_cast<unsigned>(cfg.n_kv_heads),
               static_cast<unsigned>(cfg.batch));
+    const size_t krow_bytes = static_cast<size_t>(kBulkTok) * (c->k_words | 1) * sizeof(uint32_t);
 #define KVQ_LAUNCH_BULK(T, VB)                                                                        \
-  hipLaunchKernelGGL((quantize_bulk<T, VB>), grid, dim3(kThreads), 0, stream, static_cast<const T*>(k),    \
+  hipLaunchKernelGGL((quantize_bulk<T, VB>), grid, dim3(kThreads), krow_bytes, stream, static_cast<const T*>(k), \
                      static_cast<const T*>(v), n_new, in_stride, L0, cfg.n_kv_heads, c->cap, plans, plan_bs, \
                      c->tables, layer_k_codes(c, layer), layer_v_codes(c, layer), layer_k_scales(c, layer), \
                      layer_v_scales(c, layer), c->k_words)
