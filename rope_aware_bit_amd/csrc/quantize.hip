@@ -256,14 +256,29 @@ __global__ __launch_bounds__(kThreads) void quantize_append(
 
   // ---- 2. scales: lanes 0..7 K, 8..15 V (one token each, in the quantizer's order) ----
   const int hsel = h - h0;   // this head's staged rows
+  // 256-value absmax codec: the absolute maximum of each staged (tensor, token) block by all
+  // threads, 16 lanes per block with 16 values each, then across those lanes (a maximum does not
+  // depend on the order in which it is taken)
+  __shared__ float amax_s[NF ? 2 * kGroupTok : 1];
+  if constexpr (NF) {
+    const int blk = tid >> 4, sub = tid & 15;   // block tensor * 8 + token
+    const int tsr = blk / kGroupTok, r = blk % kGroupTok;
+    float a = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int v = sub + 16 * u;                // value v: head v / 128, dim v % 128
+      a = fmaxf(a, fabsf(xval(tsr, v >> 7, r, v & (kHeadDim - 1))));
+    }
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off));
+    if (sub == 0) amax_s[blk] = a;
+    __syncthreads();
+  }
   if (tid < 2 * kGroupTok) {
     const int tsr = tid / kGroupTok, r = tid % kGroupTok;
     __half s16 = __float2half_rn(0.0f);
     if (NF) {
-      float a = 0.0f;
-      for (int hh = 0; hh < kHeads; ++hh)
-        for (int i = 0; i < kHeadDim; ++i) a = fmaxf(a, fabsf(xval(tsr, hh, r, i)));
-      s16 = __float2half_rn(a);
+      s16 = __float2half_rn(amax_s[tid]);
     } else {
       // one code path for K and V lanes (no branch per element), so the LDS reads of a batch
       // are issued together and only the fp64 sum is a dependent chain
