@@ -340,6 +340,14 @@ def test_decode_step_fused_append():
     run_case("gqa2_8k", 700, 3, 3, chunks=[650], steps=50, temper=True)   # two query heads per KV head
 
 
+def test_decode_step_from_empty_cache():
+    """Every position through decode_step, from an empty cache: the first launches have one
+    split and one partly filled tile (the appended position is its last), then the splits grow
+    past the first tiles; outputs and stored bytes equal to append + decode_attn at every step."""
+    run_case("tiny", 200, 3, 3, steps=200)
+    run_case("qwen3b_128k", 300, 3, 3, steps=300, temper=True)
+
+
 def test_decode_step_fused_append_separate_merge():
     """32 sequences x 8 KV heads = 256 (sequence, head) units: the decode step's launch is followed by
     the separate merge kernel."""
