@@ -136,6 +136,8 @@ __global__ __launch_bounds__(kThreads) void quantize_append(
     cstv = P->cstart[pi];
     cszv = P->csize[pi];
   }
+  float sgv = 1.0f;   // rotating codecs: the sign of dim pi
+  if constexpr (RM != 0) sgv = static_cast<float>(rot[h * kHeadDim + pi]);
   const int nfv = P->n_fields;
 #pragma unroll
   for (int it = 0; it < kRowIt; ++it) {
@@ -175,6 +177,8 @@ __global__ __launch_bounds__(kThreads) void quantize_append(
   // rotation inside equal-width groups: field f's chunk, and each dim's chunk size (0: the
   // dim's block is not stored)
   __shared__ uint8_t cst_s[RM == 2 ? kHeadDim : 1], csz_s[RM == 2 ? kHeadDim : 1], dsz_s[RM == 2 ? kHeadDim : 1];
+  __shared__ float sg_s[RM ? kHeadDim : 1];
+  if constexpr (RM != 0) sg_s[pi] = sgv;
   if constexpr (RM == 2) {
     cst_s[pi] = static_cast<uint8_t>(cstv);
     csz_s[pi] = static_cast<uint8_t>(cszv);
@@ -194,13 +198,12 @@ __global__ __launch_bounds__(kThreads) void quantize_append(
     // gain-normalised rows v = fp32(x * ig), signs on the stored dims, then in plan field
     // order the butterflies of each power-of-two chunk of an equal-width run (stage h pairs
     // fields f, f + h with (f - chunk start) & h == 0), fp64, and the division by sqrt(m)
-    const int8_t* sg = rot + h * kHeadDim;
     if (tid < nf_s) dsz_s[fdim_s[tid]] = csz_s[tid];
     __syncthreads();
     for (int e = tid; e < kGroupTok * kHeadDim; e += kThreads) {
       const int r = e / kHeadDim, i = e % kHeadDim;
       const double v = static_cast<double>(__fmul_rn(xval(0, 0, r, i), ig_s[i]));
-      rw_s[r][i] = dsz_s[i] ? v * static_cast<double>(sg[i]) : v;
+      rw_s[r][i] = dsz_s[i] ? v * static_cast<double>(sg_s[i]) : v;
     }
     __syncthreads();
     for (int hb = 1; hb < kHeadDim; hb <<= 1) {
@@ -225,10 +228,9 @@ __global__ __launch_bounds__(kThreads) void quantize_append(
     __syncthreads();
   }
   if constexpr (RM == 1) {
-    const int8_t* sg = rot + h * kHeadDim;
     for (int e = tid; e < kGroupTok * kHeadDim; e += kThreads) {
       const int r = e / kHeadDim, i = e % kHeadDim;
-      rw_s[r][i] = static_cast<double>(xval(0, 0, r, i)) * static_cast<double>(sg[i]);
+      rw_s[r][i] = static_cast<double>(xval(0, 0, r, i)) * static_cast<double>(sg_s[i]);
     }
     __syncthreads();
     for (int hb = 1; hb < kHeadDim; hb <<= 1) {
