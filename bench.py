@@ -54,6 +54,7 @@ HBM_PEAK_GBS = 8000.0
 PLAN_BYTES_PER_HEAD = 1024   # field dims/widths/offsets and gains read by each decode launch
 APPEND_STEPS = 24               # new positions per append-and-attend variant (2 warm-up + 22 timed)
 SINGLE_APPENDS = 200            # one-position appends timed back to back
+BULK_CACHES = 4                 # layers whose 98304-position appends are timed back to back
 CPU_SAMPLE_S = 10.0          # lower bound on the host time spent timing the oracle
 DECODE_SOURCES = ["decode_mfma.h", "decode_mfma.hip", "decode_mfma_g1.hip", "decode_mfma_g2.hip",
                   "decode_mfma_g4.hip", "decode_mfma_g8.hip", "kvq_internal.h"]
@@ -290,9 +291,10 @@ def batched_decode(torch, kvq, timer, dev, WORKLOADS, TorchLayerGen, gen_query_n
 
 
 def append_rates(torch, kvq, timer, dev, WORKLOADS, TorchLayerGen, kb, vb):
-    """Kernel-side append rates of the headline shape (2 KV heads, K3V3): back-to-back appends of
-    2048 positions, one append of the rest of a 131072-token layer, and back-to-back one-position
-    appends (the decode step's)."""
+    """Kernel-side append rates of the headline shape (2 KV heads, K3V3), each from back-to-back
+    launches: appends of 2048 positions, appends of the rest of a 131072-token layer (one per
+    layer of BULK_CACHES layers, after their first 32768 positions), and one-position appends
+    (the decode step's)."""
     w = WORKLOADS["qwen3b_128k"]
     H, T = w.n_kv, w.T
     gen = TorchLayerGen(w, dev)
@@ -316,13 +318,24 @@ def append_rates(torch, kvq, timer, dev, WORKLOADS, TorchLayerGen, kb, vb):
                          "appends": n_chunks}
     rest = T - n_chunks * 2048
     kr, vr = k[None, n_chunks * 2048:].contiguous(), v[None, n_chunks * 2048:].contiguous()
+    c.quantize_append(0, kr, vr)
+    # the same append on further layers, back to back (each layer first holds 32768 positions)
+    bc = kvq.Cache(kvq.Config(BULK_CACHES, H, w.n_q, 1, T, kb, vb))
+    k0, v0 = k[None, :n_chunks * 2048].contiguous(), v[None, :n_chunks * 2048].contiguous()
+    for layer in range(BULK_CACHES):
+        bc.alloc_bits(layer, k[:w.calib_tokens])
+        bc.quantize_append(layer, k0, v0)
     torch.cuda.synchronize()
     a.record(timer.stream)
-    c.quantize_append(0, kr, vr)
+    for layer in range(BULK_CACHES):
+        bc.quantize_append(layer, kr, vr)
     z.record(timer.stream)
     torch.cuda.synchronize()
-    us = a.elapsed_time(z) * 1e3
-    res["bulk"] = {"positions": rest, "us": round(us, 2), "GB/s": round(rest * per_pos / (us * 1e-6) / 1e9, 2),
+    us = a.elapsed_time(z) * 1e3 / BULK_CACHES
+    assert all(bc.seq_len(layer) == T for layer in range(BULK_CACHES))
+    bc.close()
+    res["bulk"] = {"positions": rest, "us": round(us, 2), "appends": BULK_CACHES,
+                   "GB/s": round(rest * per_pos / (us * 1e-6) / 1e9, 2),
                    "frac_of_hbm_peak": round(rest * per_pos / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
     g = torch.Generator(device=dev).manual_seed(3)
     ones = [(torch.randn(1, 1, H, 128, device=dev, generator=g).half(),
