@@ -35,7 +35,7 @@ __host__ __device__ constexpr int single_table_base(int w) { return kLdsTableByt
 // Constant tables, built on the host at cache creation and copied to the device.
 struct Tables {
   uint16_t cb[kMaxBits + 1][256];    // fp16 bit patterns of CB_b[k], b = 1..8 (row 0 unused)
-  float bd[kMaxBits + 1][256];       // fp32 boundaries beta_b[k], k < 2^b - 1; +inf after them (row 0: 0)
+  float bd[kMaxBits + 1][256];       // fp32 boundaries beta_b[k], k < 2^b - 1; +inf after them (row 0: all +inf)
   float delta[kMaxBits];             // greedy gain delta(b) = c(b) - c(b+1), fp32
   uint16_t nf_cb[16];                // fp16 levels of the 16-level Gaussian-quantile codebook
   float nf_bd[16];                   // 15 boundaries; [15] = +inf

@@ -597,15 +597,17 @@ __global__ __launch_bounds__(kThreads) void quantize_bulk(
     pk[j] = (pk[j] >> 2) & 255u;
     pv[j] = (pv[j] >> 2) & 255u;
   }
-  // key codes into the row image (position kr_, lanes of one field on distinct rows)
-  if (kr_ >= lo && kr_ < hi) {
+  // key codes into the row image (position kr_, lanes of one field on distinct rows), without
+  // branches: fields past the stored ones have width 0, offset 0 and code 0 (they OR nothing),
+  // and rows outside [lo, hi) are never stored
+  {
+    uint32_t* row = krow_s + kr_ * ks_stride;
 #pragma unroll
     for (int j = 0; j < kBulkHalf; ++j) {
       const int f = kBulkHalf * fg + j;
-      if (f >= nfld) break;
       const int off = foff_s[f], w = fw_s[f], word = off >> 5, sh = off & 31;
-      atomicOr(&krow_s[kr_ * ks_stride + word], pk[j] << sh);
-      if (sh + w > 32) atomicOr(&krow_s[kr_ * ks_stride + word + 1], pk[j] >> (32 - sh));
+      atomicOr(&row[word], pk[j] << sh);
+      if (sh + w > 32) atomicOr(&row[word + 1], pk[j] >> (32 - sh));
     }
   }
   // value codes: this thread's 16 positions of dim vd as a bit string in registers, then OR-ed

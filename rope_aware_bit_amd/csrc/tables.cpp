@@ -149,6 +149,7 @@ void build_tables(Tables* t) {
   const float inf = std::numeric_limits<float>::infinity();
   double c[kMaxBits + 1];
   c[0] = 1.0;
+  for (int k = 0; k < 256; ++k) t->bd[0][k] = inf;   // width 0: no boundary, every search stays at code 0
   for (int b = 1; b <= kMaxBits; ++b) {
     const int n = 1 << (b - 1), L = 1 << b;
     std::vector<double> cpos = lloyd_max_positive(n);
