@@ -431,8 +431,8 @@ __global__ __launch_bounds__(kThreads) void quantize_bulk(
   float* ig_s = g2_s[0];
   __shared__ uint8_t fdim_s[kHeadDim], fw_s[kHeadDim];
   __shared__ uint16_t foff_s[kHeadDim];
-  // the K row image, 32 rows of k_words | 1 words, in dynamic LDS sized by the launch (so that
-  // narrow rows leave room for a fifth workgroup per compute unit)
+  // the K row image, 32 rows of k_words | 1 words and a spare word, in dynamic LDS sized by the
+  // launch (so that narrow rows leave room for a fifth workgroup per compute unit)
   extern __shared__ uint32_t krow_s[];
   __shared__ uint32_t vw_s[kHeadDim * kVW];       // the segment's words, per dim
   __shared__ __attribute__((aligned(16))) float isk_s[kBulkTok];
@@ -464,7 +464,7 @@ __global__ __launch_bounds__(kThreads) void quantize_bulk(
   const float igv = P->ig[pi];
   const uint32_t fdv = P->fdim[pi], fwv = P->fwidth[pi], fov = P->foff[pi];
   const int nfv = P->n_fields;
-  for (int k = tid; k < kBulkTok * ks_stride; k += kThreads) krow_s[k] = 0u;
+  for (int k = tid; k < kBulkTok * ks_stride + 1; k += kThreads) krow_s[k] = 0u;
   for (int k = tid; k < kHeadDim * kVW; k += kThreads) vw_s[k] = 0u;
 #pragma unroll
   for (int i = 0; i < kRowIt; ++i) {
@@ -599,15 +599,17 @@ __global__ __launch_bounds__(kThreads) void quantize_bulk(
   }
   // key codes into the row image (position kr_, lanes of one field on distinct rows), without
   // branches: fields past the stored ones have width 0, offset 0 and code 0 (they OR nothing),
-  // and rows outside [lo, hi) are never stored
+  // rows outside [lo, hi) are never stored, and a field's bits are OR-ed into its word and the
+  // next (zero when it does not straddle; the image has a spare word after its last row)
   {
     uint32_t* row = krow_s + kr_ * ks_stride;
 #pragma unroll
     for (int j = 0; j < kBulkHalf; ++j) {
       const int f = kBulkHalf * fg + j;
-      const int off = foff_s[f], w = fw_s[f], word = off >> 5, sh = off & 31;
-      atomicOr(&row[word], pk[j] << sh);
-      if (sh + w > 32) atomicOr(&row[word + 1], pk[j] >> (32 - sh));
+      const int off = foff_s[f];
+      const uint64_t bits = static_cast<uint64_t>(pk[j]) << (off & 31);
+      atomicOr(&row[off >> 5], static_cast<uint32_t>(bits));
+      atomicOr(&row[(off >> 5) + 1], static_cast<uint32_t>(bits >> 32));
     }
   }
   // value codes: this thread's 16 positions of dim vd as a bit string in registers, then OR-ed
@@ -817,7 +819,7 @@ hipError_t launch_quantize(kvq_cache* c, int layer, const void* k, const void* v
     const int64_t first = L0 / kBulkTok, last = (L0 + n_new - 1) / kBulkTok;
     dim3 grid(static_cast<unsigned>(last - first + 1), static_cast<unsigned>(cfg.n_kv_heads),
               static_cast<unsigned>(cfg.batch));
-    const size_t krow_bytes = static_cast<size_t>(kBulkTok) * (c->k_words | 1) * sizeof(uint32_t);
+    const size_t krow_bytes = (static_cast<size_t>(kBulkTok) * (c->k_words | 1) + 1) * sizeof(uint32_t);
 #define KVQ_LAUNCH_BULK(T, VB)                                                                        \
   hipLaunchKernelGGL((quantize_bulk<T, VB>), grid, dim3(kThreads), krow_bytes, stream, static_cast<const T*>(k), \
                      static_cast<const T*>(v), n_new, in_stride, L0, cfg.n_kv_heads, c->cap, plans, plan_bs, \
