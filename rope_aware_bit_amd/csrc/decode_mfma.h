@@ -494,6 +494,12 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   // 8 waves with a static V tile area each, copied at tile start (else: the V tile shares the
   // wave's region, copied after the key product, LV with 8 waves or 4 waves without v_early)
   constexpr bool kStaticV = W == 8 && !LV;
+  // late V with at most 4-bit values, attention only: each lane loads its own V words straight
+  // into registers after the key product (the tile is stored in the value product's operand
+  // order, so a lane's 8 x VB words are its own); no LDS copy, the region's V area stays
+  // unused.  (The fused-append instantiation keeps the LDS copy: with the V words in registers
+  // its append code no longer fits the register budget.)
+  constexpr bool kRegV = LV && VB <= 4 && !kPipe && !APP;
   constexpr int PCOLS = 2 * G;                        // P columns: hi of heads 0..G-1, then lo
   constexpr int KWV = 4 * VB;                         // words per dim per V tile
   constexpr int QPT = (G * kHeadDim + 255) / 256;     // query values per set-up thread
@@ -658,6 +664,18 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     for (int k = 0; k < 4; ++k) {
       ka[k] = krow0[k < last ? k : last];
       kb2[k] = krow1[k < last ? k : last];
+    }
+  };
+  uint32_t vreg[8][kRegV ? VB : 1];   // lane's words of the 8 16-dim slices (dims 16 dt + n % 16,
+                                     // tokens 32 ((lane / 16) % 4) .. + 31 of the tile)
+  auto load_v = [&](int64_t tile) {
+    if constexpr (kRegV) {
+      const uint32_t* vt = vc + (bh * (cap / kVTile) + tile) * (kVTile * KWV) + lane * VB;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+#pragma unroll
+        for (int k = 0; k < VB; ++k) vreg[dt][k] = vt[dt * 64 * VB + k];
+      }
     }
   };
   uint32_t skr[8], svr[8];   // fp16 bits of the scales of tokens 16 tg + n
@@ -1098,7 +1116,8 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
       k_products(P, u, 1);
     }
     wave_sync();   // the key rows are read; the area takes the softmax weights (and V) next
-    if (!kStaticV && !v_early) dma_v(tile);
+    if constexpr (kRegV) load_v(tile);   // the V words land in registers during the softmax
+    else if (!kStaticV && !v_early) dma_v(tile);
 
     // -- online softmax: lane (n, g) holds heads 2g and 2g + 1 of tokens 16 tg + n --
     float L0[8], L1[8];
@@ -1159,7 +1178,7 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
       for (int dt = 0; dt < 8; ++dt) oacc[dt] *= al;
     }
     // -- values: O^T[dim][col] += V^T[dim][tok] P^T[tok][col] over 4 chunks of 32 tokens --
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the V tile copy has landed
+    if constexpr (!kRegV) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the V tile copy has landed
     wave_sync();
     if (APP && static_cast<int>(tile) == app_t32) {   // the appended position's value codes into the copy
       const int tau = app_tau;
@@ -1180,7 +1199,7 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     for (int dt = 0; dt < 8; ++dt) {
       vseg[dt][0] = vseg[dt][VB + 1] = 0u;
 #pragma unroll
-      for (int k = 0; k < VB; ++k) vseg[dt][k + 1] = vbuf[(dt * 64 + lane) * VB + k];
+      for (int k = 0; k < VB; ++k) vseg[dt][k + 1] = kRegV ? vreg[dt][kRegV ? k : 0] : vbuf[(dt * 64 + lane) * VB + k];
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
