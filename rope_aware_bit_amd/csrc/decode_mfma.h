@@ -494,12 +494,13 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   // 8 waves with a static V tile area each, copied at tile start (else: the V tile shares the
   // wave's region, copied after the key product, LV with 8 waves or 4 waves without v_early)
   constexpr bool kStaticV = W == 8 && !LV;
-  // late V with at most 4-bit values, attention only: each lane loads its own V words straight
-  // into registers after the key product (the tile is stored in the value product's operand
-  // order, so a lane's 8 x VB words are its own); no LDS copy, the region's V area stays
-  // unused.  (The fused-append instantiation keeps the LDS copy: with the V words in registers
-  // its append code no longer fits the register budget.)
-  constexpr bool kRegV = LV && VB <= 4 && !kPipe && !APP;
+  // 8 waves, at most 4-bit values, attention only: each lane loads its own V words straight into
+  // registers (the tile is stored in the value product's operand order, so a lane's 8 x VB
+  // words are its own), after the key product (late V) or once the tile's K rows are staged
+  // (static V areas, several tiles per wave); no LDS copy, the LDS V areas stay unused.  (The
+  // fused-append instantiation keeps the LDS copy: with the V words in registers its append
+  // code no longer fits the register budget.)
+  constexpr bool kRegV = (LV || kStaticV) && VB <= 4 && !kPipe && !APP;
   constexpr int PCOLS = 2 * G;                        // P columns: hi of heads 0..G-1, then lo
   constexpr int KWV = 4 * VB;                         // words per dim per V tile
   constexpr int QPT = (G * kHeadDim + 255) / 256;     // query values per set-up thread
@@ -534,7 +535,7 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
   // [512][VB] V tile, written by global-to-LDS loads.  With 8 waves it is an LDS object of its
   // own, so the compiler need not wait for those loads before reading the K tile.
   uint32_t* vbuf;
-  if constexpr (kStaticV) {
+  if constexpr (kStaticV && !kRegV) {
     __shared__ __attribute__((aligned(16))) uint32_t vbuf_s[W][kVTile * 4 * VB];
     vbuf = vbuf_s[wave];
   } else {
@@ -1031,7 +1032,10 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
     wave_sync();
     // 8 waves: the V tile is copied now, when no other load of this wave is in flight, and
     // arrives during the key product
-    if constexpr (kStaticV) dma_v(tile);
+    if constexpr (kStaticV) {
+      if constexpr (kRegV) load_v(tile);
+      else dma_v(tile);
+    }
     if constexpr (kPipe) {
       if (next < t_end) load_k(next);
     }
@@ -1116,7 +1120,7 @@ __global__ __launch_bounds__(64 * W, W / 4) void decode_mfma(
       k_products(P, u, 1);
     }
     wave_sync();   // the key rows are read; the area takes the softmax weights (and V) next
-    if constexpr (kRegV) load_v(tile);   // the V words land in registers during the softmax
+    if constexpr (kRegV && LV) load_v(tile);   // the V words land in registers during the softmax
     else if (!kStaticV && !v_early) dma_v(tile);
 
     // -- online softmax: lane (n, g) holds heads 2g and 2g + 1 of tokens 16 tg + n --
