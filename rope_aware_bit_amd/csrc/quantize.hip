@@ -638,11 +638,11 @@ __global__ __launch_bounds__(kThreads) void quantize_bulk(
 
   // ---- 4. stores ----
   {
+    // half-wave per row (k_words <= 32): rows 2 w + (lane / 32), + 8, ...; no division
     uint32_t* dst = kc + ((static_cast<int64_t>(b) * n_kv + h) * cap + g0) * k_words;
-    for (int k = tid + lo * k_words; k < hi * k_words; k += kThreads) {
-      const int r = k / k_words;
-      dst[k] = krow_s[r * ks_stride + (k - r * k_words)];
-    }
+    const int wl = tid & 31;
+    for (int r = (tid >> 5); r < kBulkTok; r += kThreads / 32)
+      if (r >= lo && r < hi && wl < k_words) dst[r * k_words + wl] = krow_s[r * ks_stride + wl];
   }
   {
     const int gq = static_cast<int>((g0 % kVTile) / kBulkTok);
