@@ -417,6 +417,17 @@ def test_kivi_codec(kb, vb):
     run_case("llama8b_32k", 3000, kb, vb, codec="kivi", temper=True, chunks=[1000, 1999, 1])
 
 
+def test_several_tiles_per_wave():
+    """Launches whose waves walk several 128-position tiles (few splits over many tiles): each
+    later tile's K rows, scales and V words are loaded inside the tile loop.  Block-GTQ with a
+    window and a one-position last append, the KIVI-style codec, the 256-value codec at four
+    query heads per KV head over a batch, and one split per head (no merge) with a ragged last
+    tile."""
+    run_case("qwen3b_128k", 6000, 3, 3, chunks=[2048, 3951, 1], n_splits=2, recent=256, temper=True)
+    run_case("qwen3b_128k", 5000, 3, 3, codec="kivi", chunks=[2048, 2952], n_splits=2)
+    run_case("llama8b_b64", 3000, 4, 4, codec="nf16", batch=2, n_splits=1, temper=True)
+    run_case("llama8b_32k", 4000, 2, 2, n_splits=1)
+
 def test_kivi_codec_window_and_tile_boundaries():
     """A recent window on top (ring of R + 128 slots), appends ending on and off tile
     boundaries, a context of exactly whole tiles, fp32 inputs, interleaved pairs."""
