@@ -212,11 +212,11 @@ inline DecodeShape decode_shape(const kvq_cache* c) {
 inline int decode_waves(const kvq_cache* c) { return decode_shape(c).waves; }
 
 // Workgroups that merge the S splits of one (sequence, KV head) in the decode kernel: a power
-// of two, at most 16 and at most S, small enough that the waiting mergers of all units occupy
+// of two, at most 32 and at most S, small enough that the waiting mergers of all units occupy
 // fewer than all compute units (units x K < CUs), so the splits they wait for can always be
 // scheduled.  0: no such count (the call is rejected).
 inline int decode_split_mergers(int S, int64_t units, int n_cu) {
-  int k = 16;
+  int k = 32;
   while (k > 1 && (k > S || units * k >= n_cu)) k >>= 1;
   return units * k < n_cu ? k : 0;
 }
