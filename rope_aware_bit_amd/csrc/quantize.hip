@@ -390,12 +390,13 @@ __global__ __launch_bounds__(kThreads) void quantize_append(
 
 // Many new positions (a prefill), for the codecs without rotation or absmax blocks, from the
 // caller's rows: the same row quantizer as quantize_append, one workgroup per 32 consecutive
-// positions (one V segment) of one (sequence, KV head).
+// positions (one V segment) of one (sequence, KV head), 8 waves.
 //   - One wave runs the 64 scale sums (32 key and 32 value rows, one lane each, dim order).
-//   - Keys: thread t quantizes fields 16 (t / 32) .. + 15 of position t % 32, so the 32 lanes
+//   - Keys: thread t quantizes fields 8 (t / 32) .. + 7 of position t % 32, so the 32 lanes
 //     that share a field hold 32 different rows and OR into 32 different row words (the LDS row
-//     image has an odd stride: no two lanes of a field share a bank).
-//   - Values: thread t quantizes dim t / 2 at the 16 positions 16 (t % 2) .. + 15, packs their
+//     image has an odd stride: no two lanes of a field share a bank); wave w holds fields
+//     16 w .. 16 w + 15.
+//   - Values: thread t quantizes dim t / 4 at the 8 positions 8 (t % 4) .. + 7, packs their
 //     codes into words in registers and ORs a handful of words into the segment image.
 //   - The searches take one step size per step for a whole wave (the widest field of the wave,
 //     or the value width): a narrower field's boundaries are followed by +inf in the table,
@@ -403,10 +404,10 @@ __global__ __launch_bounds__(kThreads) void quantize_append(
 //   - A segment whose 32 positions are all new is stored with plain stores (no other position
 //     shares its words); the first and last segments of a call are OR-ed in.
 constexpr int kBulkTok = 32;
-constexpr int kBulkHalf = kBulkTok / 2;
+constexpr int kBulkThreads = 512;   // 8 waves per workgroup
 
 template <typename T, int VB>
-__global__ __launch_bounds__(kThreads) void quantize_bulk(
+__global__ __launch_bounds__(kBulkThreads) void quantize_bulk(
     const T* __restrict__ kin, const T* __restrict__ vin, int64_t n_new, int64_t in_stride, int64_t L0, int n_kv,
     int64_t cap, const Plan* __restrict__ plans, int plan_bs, const Tables* __restrict__ tab,
     uint32_t* __restrict__ kc, uint32_t* __restrict__ vc, uint16_t* __restrict__ ks,
@@ -415,7 +416,10 @@ __global__ __launch_bounds__(kThreads) void quantize_bulk(
   constexpr int kRowW = kHeadDim * static_cast<int>(sizeof(T)) / 4 + 1;   // odd: no bank conflicts
   constexpr int kBd4 = (kMaxBits + 1) * 256 / 4;
   constexpr int kVW = VB | 1;                     // odd stride of the segment image rows (>= VB words)
-  constexpr int kLW = (kBulkHalf * VB + 31) / 32; // words of one thread's 16 value codes
+  constexpr int kBT = kBulkThreads;
+  constexpr int kE = kBulkTok * kHeadDim / kBT;   // key (and value) elements per thread: 8
+  constexpr int kVPer = kBulkTok / kE;             // threads per value dim: 4
+  constexpr int kLW = (kE * VB + 31) / 32;         // words of one thread's value codes
   const int tid = threadIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
   const int64_t g0 = (L0 / kBulkTok + blockIdx.x) * kBulkTok;   // first position of the segment
@@ -443,12 +447,12 @@ __global__ __launch_bounds__(kThreads) void quantize_bulk(
   //      latency; nothing loaded is used before all are issued), then the LDS images.  Rows
   //      outside [lo, hi) read the nearest row inside (their images are never used). ----
   constexpr int kPieces = kHeadDim / kVec;                     // 16-byte pieces per row
-  constexpr int kRowIt = 2 * kBulkTok * kPieces / kThreads;    // pieces per thread
-  constexpr int kBdIt = (kBd4 + kThreads - 1) / kThreads;
+  constexpr int kRowIt = 2 * kBulkTok * kPieces / kBT;    // pieces per thread
+  constexpr int kBdIt = (kBd4 + kBT - 1) / kBT;
   uint4 xr[kRowIt], bdr[kBdIt];
 #pragma unroll
   for (int i = 0; i < kRowIt; ++i) {
-    const int k = tid + kThreads * i;
+    const int k = tid + kBT * i;
     const int q = k % kPieces, r = (k / kPieces) % kBulkTok, tsr = k / (kPieces * kBulkTok);
     const int rc = r < lo ? lo : r >= hi ? hi - 1 : r;
     const int64_t src = ((static_cast<int64_t>(b) * in_stride + (g0 + rc - L0)) * n_kv + h) * kHeadDim + q * kVec;
@@ -456,7 +460,7 @@ __global__ __launch_bounds__(kThreads) void quantize_bulk(
   }
 #pragma unroll
   for (int j = 0; j < kBdIt; ++j) {
-    const int q = tid + kThreads * j;
+    const int q = tid + kBT * j;
     bdr[j] = reinterpret_cast<const uint4*>(&tab->bd[0][0])[q < kBd4 ? q : kBd4 - 1];
   }
   const Plan* P = plans + static_cast<int64_t>(b) * plan_bs + h;
@@ -464,11 +468,11 @@ __global__ __launch_bounds__(kThreads) void quantize_bulk(
   const float igv = P->ig[pi];
   const uint32_t fdv = P->fdim[pi], fwv = P->fwidth[pi], fov = P->foff[pi];
   const int nfv = P->n_fields;
-  for (int k = tid; k < kBulkTok * ks_stride + 1; k += kThreads) krow_s[k] = 0u;
-  for (int k = tid; k < kHeadDim * kVW; k += kThreads) vw_s[k] = 0u;
+  for (int k = tid; k < kBulkTok * ks_stride + 1; k += kBT) krow_s[k] = 0u;
+  for (int k = tid; k < kHeadDim * kVW; k += kBT) vw_s[k] = 0u;
 #pragma unroll
   for (int i = 0; i < kRowIt; ++i) {
-    const int k = tid + kThreads * i;
+    const int k = tid + kBT * i;
     const int q = k % kPieces, r = (k / kPieces) % kBulkTok, tsr = k / (kPieces * kBulkTok);
     uint32_t* d = &x_s[tsr][r][q * 4];
     d[0] = xr[i].x;
@@ -480,7 +484,7 @@ __global__ __launch_bounds__(kThreads) void quantize_bulk(
   // compiler has no reason to move their loads down to a conditional store)
 #pragma unroll
   for (int j = 0; j < kBdIt; ++j) {
-    const int q = tid + kThreads * j;
+    const int q = tid + kBT * j;
     reinterpret_cast<uint4*>(bd_s)[q < kBd4 ? q : kBd4 - 1] = bdr[j];
   }
   if (tid < kHeadDim) {
@@ -497,13 +501,13 @@ __global__ __launch_bounds__(kThreads) void quantize_bulk(
   //      order); the other waves meanwhile read their elements ----
   const int wv = tid >> 6;
   const int nfld = nf_s;
-  const int kr_ = tid & 31, fg = tid >> 5;        // key: position kr_, fields 16 fg .. 16 fg + 15
-  const int vd = tid >> 1, r0 = kBulkHalf * (tid & 1);   // value: dim vd, positions r0 ..
-  float uk[kBulkHalf], uv[kBulkHalf];
+  const int kr_ = tid & 31, fg = tid >> 5;        // key: position kr_, fields kE fg .. kE fg + kE - 1
+  const int vd = tid / kVPer, r0 = kE * (tid % kVPer);   // value: dim vd, positions r0 .. r0 + kE - 1
+  float uk[kE], uv[kE];
   auto gather = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < kBulkHalf; ++j) {
-      const int f = kBulkHalf * fg + j;
+    for (int j = 0; j < kE; ++j) {
+      const int f = kE * fg + j;
       const int d = fdim_s[f];
       uk[j] = __fmul_rn(xval(0, kr_, d), ig_s[d]);   // y = x * ig
       uv[j] = xval(1, r0 + j, vd);
@@ -551,9 +555,9 @@ __global__ __launch_bounds__(kThreads) void quantize_bulk(
   {
     const float isk = isk_s[kr_];
 #pragma unroll
-    for (int j = 0; j < kBulkHalf; ++j) uk[j] = __fmul_rn(uk[j], isk);
+    for (int j = 0; j < kE; ++j) uk[j] = __fmul_rn(uk[j], isk);
 #pragma unroll
-    for (int j = 0; j < kBulkHalf; j += 4) {
+    for (int j = 0; j < kE; j += 4) {
       const float4 iv = *reinterpret_cast<const float4*>(&isv_s[r0 + j]);
       uv[j] = __fmul_rn(uv[j], iv.x);
       uv[j + 1] = __fmul_rn(uv[j + 1], iv.y);
@@ -564,21 +568,21 @@ __global__ __launch_bounds__(kThreads) void quantize_bulk(
   // search state as byte addresses into the boundary table: row w (1 KB) plus 4 x code, so that
   // with the steps unrolled each probe is one LDS read at a constant offset from it
   const char* bdb = reinterpret_cast<const char*>(bd_s);
-  uint32_t pk[kBulkHalf], pv[kBulkHalf];
+  uint32_t pk[kE], pv[kE];
 #pragma unroll
-  for (int j = 0; j < kBulkHalf; ++j) {
-    pk[j] = static_cast<uint32_t>(fw_s[kBulkHalf * fg + j]) * 1024u;
+  for (int j = 0; j < kE; ++j) {
+    pk[j] = static_cast<uint32_t>(fw_s[kE * fg + j]) * 1024u;
     pv[j] = static_cast<uint32_t>(VB) * 1024u;
   }
   // wave-uniform step counts: the wave's widest field (fields are widest first) and the value width
-  const int ksteps = __builtin_amdgcn_readfirstlane(32 * wv < nfld ? fw_s[32 * wv] : 0);
+  const int ksteps = __builtin_amdgcn_readfirstlane(2 * kE * wv < nfld ? fw_s[2 * kE * wv] : 0);
 #pragma unroll
   for (int st = kMaxBits - 1; st >= 0; --st) {
     if (st >= ksteps) continue;
     constexpr uint32_t one = 1u;
     const uint32_t step4 = (one << st) * 4u;
 #pragma unroll
-    for (int j = 0; j < kBulkHalf; ++j) {
+    for (int j = 0; j < kE; ++j) {
       const float bdv = *reinterpret_cast<const float*>(bdb + pk[j] + (step4 - 4u));
       pk[j] = bdv < uk[j] ? pk[j] + step4 : pk[j];
     }
@@ -587,13 +591,13 @@ __global__ __launch_bounds__(kThreads) void quantize_bulk(
   for (int st = VB - 1; st >= 0; --st) {
     const uint32_t step4 = (1u << st) * 4u;
 #pragma unroll
-    for (int j = 0; j < kBulkHalf; ++j) {
+    for (int j = 0; j < kE; ++j) {
       const float bdv = *reinterpret_cast<const float*>(bdb + pv[j] + (step4 - 4u));
       pv[j] = bdv < uv[j] ? pv[j] + step4 : pv[j];
     }
   }
 #pragma unroll
-  for (int j = 0; j < kBulkHalf; ++j) {   // back to codes
+  for (int j = 0; j < kE; ++j) {   // back to codes
     pk[j] = (pk[j] >> 2) & 255u;
     pv[j] = (pv[j] >> 2) & 255u;
   }
@@ -604,22 +608,22 @@ __global__ __launch_bounds__(kThreads) void quantize_bulk(
   {
     uint32_t* row = krow_s + kr_ * ks_stride;
 #pragma unroll
-    for (int j = 0; j < kBulkHalf; ++j) {
-      const int f = kBulkHalf * fg + j;
+    for (int j = 0; j < kE; ++j) {
+      const int f = kE * fg + j;
       const int off = foff_s[f];
       const uint64_t bits = static_cast<uint64_t>(pk[j]) << (off & 31);
       atomicOr(&row[off >> 5], static_cast<uint32_t>(bits));
       atomicOr(&row[(off >> 5) + 1], static_cast<uint32_t>(bits >> 32));
     }
   }
-  // value codes: this thread's 16 positions of dim vd as a bit string in registers, then OR-ed
-  // into the segment image at bit 16 VB (t % 2) (positions outside [lo, hi) contribute 0)
+  // value codes: this thread's kE positions of dim vd as a bit string in registers, then OR-ed
+  // into the segment image at bit r0 VB (positions outside [lo, hi) contribute 0)
   {
     uint32_t lw[kLW + 1];
 #pragma unroll
     for (int i = 0; i <= kLW; ++i) lw[i] = 0u;
 #pragma unroll
-    for (int j = 0; j < kBulkHalf; ++j) {
+    for (int j = 0; j < kE; ++j) {
       const uint32_t code = (r0 + j >= lo && r0 + j < hi) ? pv[j] : 0u;
       const int bit = j * VB, word = bit >> 5, sh = bit & 31;
       lw[word] |= code << sh;
@@ -641,14 +645,14 @@ __global__ __launch_bounds__(kThreads) void quantize_bulk(
     // half-wave per row (k_words <= 32): rows 2 w + (lane / 32), + 8, ...; no division
     uint32_t* dst = kc + ((static_cast<int64_t>(b) * n_kv + h) * cap + g0) * k_words;
     const int wl = tid & 31;
-    for (int r = (tid >> 5); r < kBulkTok; r += kThreads / 32)
+    for (int r = (tid >> 5); r < kBulkTok; r += kBT / 32)
       if (r >= lo && r < hi && wl < k_words) dst[r * k_words + wl] = krow_s[r * ks_stride + wl];
   }
   {
     const int gq = static_cast<int>((g0 % kVTile) / kBulkTok);
     uint32_t* tile_dst = vc + ((static_cast<int64_t>(b) * n_kv + h) * (cap / kVTile) + g0 / kVTile) * kVTile * 4 * VB;
     const bool whole = lo == 0 && hi == kBulkTok;
-    for (int k = tid; k < kHeadDim * VB; k += kThreads) {
+    for (int k = tid; k < kHeadDim * VB; k += kBT) {
       const int i = k / VB, w = k % VB;
       const uint32_t bits = vw_s[i * kVW + w];
       uint32_t* d = tile_dst + static_cast<int64_t>(((i / 16) * 4 + gq) * 16 + i % 16) * VB + w;
@@ -821,7 +825,7 @@ hipError_t launch_quantize(kvq_cache* c, int layer, const void* k, const void* v
               static_cast<unsigned>(cfg.batch));
     const size_t krow_bytes = (static_cast<size_t>(kBulkTok) * (c->k_words | 1) + 1) * sizeof(uint32_t);
 #define KVQ_LAUNCH_BULK(T, VB)                                                                        \
-  hipLaunchKernelGGL((quantize_bulk<T, VB>), grid, dim3(kThreads), krow_bytes, stream, static_cast<const T*>(k), \
+  hipLaunchKernelGGL((quantize_bulk<T, VB>), grid, dim3(kBulkThreads), krow_bytes, stream, static_cast<const T*>(k), \
                      static_cast<const T*>(v), n_new, in_stride, L0, cfg.n_kv_heads, c->cap, plans, plan_bs, \
                      c->tables, layer_k_codes(c, layer), layer_v_codes(c, layer), layer_k_scales(c, layer), \
                      layer_v_scales(c, layer), c->k_words)
