@@ -294,12 +294,19 @@ def append_rates(torch, kvq, timer, dev, WORKLOADS, TorchLayerGen, kb, vb):
     """Kernel-side append rates of the headline shape (2 KV heads, K3V3), each from back-to-back
     launches: appends of 2048 positions, appends of the rest of a 131072-token layer (one per
     layer of BULK_CACHES layers, after their first 32768 positions), and one-position appends
-    (the decode step's)."""
+    (the decode step's).  The small appends are queued behind a spin kernel, so their time is
+    the GPU's, not the host's per-call overhead."""
     w = WORKLOADS["qwen3b_128k"]
     H, T = w.n_kv, w.T
     gen = TorchLayerGen(w, dev)
     k, v = gen.layer(0)
     per_pos = H * (2 * 128 * 2 + (kb + vb) * 16 + 4)      # fp16 K and V in, packed rows and scales out
+
+    def hold_gpu():
+        # a spin kernel of several ms ahead of the timed launches, so that the host has enqueued
+        # them all before the GPU reaches the first: small appends then run back to back on the
+        # GPU instead of waiting for the host's per-call overhead
+        torch.cuda._sleep(20_000_000)
     res = {}
     n_chunks = 16
     c = kvq.Cache(kvq.Config(1, H, w.n_q, 1, T + SINGLE_APPENDS + 8, kb, vb))
@@ -308,6 +315,7 @@ def append_rates(torch, kvq, timer, dev, WORKLOADS, TorchLayerGen, kb, vb):
               for i in range(n_chunks)]
     torch.cuda.synchronize()
     a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    hold_gpu()
     a.record(timer.stream)
     for kc_, vc_ in chunks:
         c.quantize_append(0, kc_, vc_)
@@ -341,6 +349,7 @@ def append_rates(torch, kvq, timer, dev, WORKLOADS, TorchLayerGen, kb, vb):
     ones = [(torch.randn(1, 1, H, 128, device=dev, generator=g).half(),
              torch.randn(1, 1, H, 128, device=dev, generator=g).half()) for _ in range(SINGLE_APPENDS)]
     torch.cuda.synchronize()
+    hold_gpu()
     a.record(timer.stream)
     for kk, vv in ones:
         c.quantize_append(0, kk, vv)
