@@ -306,7 +306,8 @@ def append_rates(torch, kvq, timer, dev, WORKLOADS, TorchLayerGen, kb, vb):
         # a spin kernel of several ms ahead of the timed launches, so that the host has enqueued
         # them all before the GPU reaches the first: small appends then run back to back on the
         # GPU instead of waiting for the host's per-call overhead
-        torch.cuda._sleep(20_000_000)
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(20_000_000)
     res = {}
     n_chunks = 16
     c = kvq.Cache(kvq.Config(1, H, w.n_q, 1, T + SINGLE_APPENDS + 8, kb, vb))
