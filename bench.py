@@ -24,6 +24,7 @@ Beside the headline (skipped with --decode-only): the 524288-token K2V2 step
 uniform codec (12 copies cycled so the 256 MB last-level cache holds none),
 batched decode at 64 x 8192 for Block-GTQ and the 256-value absmax codec,
 codec variants of the headline layer, append rates from back-to-back launches,
+the single-head 1024-position fp32 K4V4 decode (latency-bound, in us),
 the decode step with each layer first appending the new position (one fused
 launch per layer, and as two calls), the key fidelity diagnostics, and a
 quality side-report (logit MAE, softmax KL, output error) at the default and a
@@ -259,6 +260,40 @@ def llama_layer_budgets(torch, kvq, timer, dev, WORKLOADS, TorchLayerGen):
                                          "bytes_per_launch": int(byts)}
             c.close()
     return {"workload": f"one layer, {H} KV / {Hq} query heads, {T} tokens, batch 1 ({n_copies} copies cycled)", **res}
+
+
+def tiny_decode(torch, kvq, timer, dev, WORKLOADS, TorchLayerGen):
+    """The single-head case (one KV head, one query head, 1024 positions, fp32 keys, values and
+    query, K4V4): its 135 KB take 0.02 us at the HBM peak, so the launch is latency-bound and is
+    reported in us.  Back-to-back launches queued behind a spin kernel, so the time is the GPU's,
+    not the host's per-call overhead."""
+    w = WORKLOADS["tiny"]
+    kb, vb = w.budgets[0]
+    gen = TorchLayerGen(w, dev)
+    k, v = gen.layer(0, dtype=torch.float32)
+    q = gen.query(0, dtype=torch.float32)[None].contiguous()
+    out = torch.empty(1, w.n_q, 128, dtype=torch.float32, device=dev)
+    c = kvq.Cache(kvq.Config(1, w.n_kv, w.n_q, 1, w.T, kb, vb))
+    c.alloc_bits(0, k[:w.calib_tokens])
+    c.quantize_append(0, k[None], v[None])
+    n = 200
+    for _ in range(5):
+        c.decode_attn(0, q, out=out)
+    torch.cuda.synchronize()
+    a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(20_000_000)
+    a.record(timer.stream)
+    for _ in range(n):
+        c.decode_attn(0, q, out=out)
+    z.record(timer.stream)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    us = a.elapsed_time(z) * 1e3 / n
+    c.close()
+    return {"workload": f"{w.n_kv} KV / {w.n_q} query head, {w.T} positions, batch 1, fp32 inputs, K{kb}V{vb}",
+            "us_per_launch": round(us, 2), "launches": n,
+            "bytes_per_launch": int(decode_bytes(1, w.n_kv, w.n_q, w.T, kb, vb))}
 
 
 def batched_decode(torch, kvq, timer, dev, WORKLOADS, TorchLayerGen, gen_query_np, np):
@@ -573,6 +608,8 @@ def main():
         log("budgets done")
         extra["append"] = append_rates(torch, kvq, timer, dev, WORKLOADS, TorchLayerGen, kb, vb)
         log("append done")
+        extra["tiny_decode"] = tiny_decode(torch, kvq, timer, dev, WORKLOADS, TorchLayerGen)
+        log("tiny done")
         extra["quality"] = quality_report(torch, kvq, dev, WORKLOADS, gen_layer_np, gen_query_np, np)
         log("quality done")
 
